@@ -1,0 +1,68 @@
+"""FP4 main-KV codec: E2M1 values with one E4M3 scale per 16 channels.
+
+Follows [atlas] section 3.2 (FP4 main KV paragraph: E2M1, one E4M3 scale per
+16 channels), [newsaint] section 4 (FP4 main KV, dequantised just before
+attention) and the FP4Quantizer of [newsaint] section 8 (per-group absolute
+maximum, scale = amax / 6 clamped to the E4M3 maximum 448, nearest E2M1
+level), on the 512-wide latent shared across heads ([stamatios], "CSA2:
+compressão em três dimensões").
+
+Readings where the pages are silent or differ (each also listed in the design
+notes):
+* the scale is rounded to E4M3 with round-to-nearest-even after the 448 clamp
+  (the quantiser on the page keeps it unrounded; a stored E4M3 scale must be
+  rounded, and the plainest rounding is RNE);
+* the E2M1 ratio |x|/s is rounded to nearest with ties to the even code (the
+  page's argmin picks the smaller level on a tie);
+* the sign bit is the sign of x, so a small negative value stores -0 (0x8);
+  a group whose scale rounds to 0 stores all codes 0x0;
+* two codes per byte, the even channel in the low nibble; the 32 scale bytes
+  are stored apart from the 256 code bytes.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .formats import E2M1_LEVELS, bf16_to_f64, e2m1_encode_rne, e4m3_decode, e4m3_encode_rne
+
+GROUP = 16          # channels per E4M3 scale
+D_LATENT = 512
+BYTES_CODES = D_LATENT // 2        # 256 code bytes per entry
+BYTES_SCALES = D_LATENT // GROUP   # 32 scale bytes per entry
+
+
+def encode_kv(latent_bits: np.ndarray):
+    """Encode bf16 latent rows [n, 512] (uint16 bit patterns) to
+    (codes uint8 [n, 256], scales uint8 [n, 32])."""
+    lb = np.asarray(latent_bits).astype(np.uint16)
+    n = lb.shape[0]
+    if lb.shape != (n, D_LATENT):
+        raise ValueError("latent must be [n, 512]")
+    x = bf16_to_f64(lb).reshape(n, BYTES_SCALES, GROUP)
+    neg = ((lb >> 15) & 1).astype(np.uint8).reshape(n, BYTES_SCALES, GROUP)
+    amax = np.abs(x).max(axis=-1)                              # [n, 32]
+    t = np.minimum(amax / 6.0, 448.0)
+    scale_code = e4m3_encode_rne(t)                            # [n, 32]
+    s = e4m3_decode(scale_code)
+    zero = s == 0.0
+    ratio = np.abs(x) / np.where(zero, 1.0, s)[..., None]
+    mag = e2m1_encode_rne(ratio)                               # [n, 32, 16]
+    code = (neg << 3) | mag
+    code = np.where(zero[..., None], 0, code).astype(np.uint8)
+    code = code.reshape(n, D_LATENT)
+    packed = (code[:, 0::2] | (code[:, 1::2] << 4)).astype(np.uint8)
+    return packed, scale_code
+
+
+def decode_kv(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """(codes [n, 256], scales [n, 32]) -> float64 latent [n, 512]:
+    value = (-1)^sign * E2M1 level * E4M3 scale (exact in float64)."""
+    c = np.asarray(codes).astype(np.uint8)
+    n = c.shape[0]
+    nib = np.empty((n, D_LATENT), dtype=np.uint8)
+    nib[:, 0::2] = c & 0xF
+    nib[:, 1::2] = c >> 4
+    sgn = np.where(nib >> 3, -1.0, 1.0)
+    lev = E2M1_LEVELS[nib & 7]
+    s = np.repeat(e4m3_decode(np.asarray(scales)), GROUP, axis=1)
+    return sgn * lev * s
