@@ -1,0 +1,293 @@
+"""CSA2 decode path on AMD MI355X (gfx950): Python binding of libcsa2.so.
+
+Argument marshalling only: every step of the path runs in the library's HIP
+kernels (see include/csa2.h for the contracts).  torch supplies device memory
+and the current HIP stream.  There is no CPU fallback: if the library is not
+built, or the device is not gfx950, every call raises.
+
+    encode_kv      FP4 main-KV encode (E2M1 + one E4M3 scale per 16 channels)
+    index_full     Full-mode indexer: scores, block-of-8 maxima, Top-P pool
+    index_reindex  Reindex inside the pool: Top-K positions
+    attend         sparse FP4 + sliding-window attention, one softmax
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+from typing import Optional, Tuple
+
+import torch
+
+__all__ = ["Dims", "Batch", "Csa2Error", "lib", "lib_path", "encode_kv", "index_full",
+           "index_reindex", "attend", "workspace_full", "workspace_reindex",
+           "workspace_attend", "abi_version"]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+lib_path = os.path.join(_PKG, "libcsa2.so")
+
+
+class Csa2Error(RuntimeError):
+    pass
+
+
+class _Dims(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in
+                ("n_heads", "d_latent", "d_rope", "idx_heads", "idx_dim", "block",
+                 "pool_blocks", "topk", "swa")]
+
+
+class _Queries(ctypes.Structure):
+    _fields_ = [("n_q", ctypes.c_int32), ("tokens_per_seq", ctypes.c_int32),
+                ("max_visible", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("seq_base", ctypes.c_void_p), ("n_visible", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libcsa2.so from the package directory (raises if it is missing)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(lib_path):
+            raise Csa2Error(f"{lib_path} is not built; run __graft_entry__.build() "
+                            "or python -m compressed_sparse_attention_decode_amd._build")
+        L = ctypes.CDLL(lib_path)
+        P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+        PD, PQ = ctypes.POINTER(_Dims), ctypes.POINTER(_Queries)
+        sig = {
+            "csa2_abi_version": (I32, []),
+            "csa2_status_string": (ctypes.c_char_p, [I32]),
+            "csa2_last_error": (ctypes.c_char_p, []),
+            "csa2_encode_kv": (I32, [I64, P, P, P, P, P, P, P]),
+            "csa2_index_full_workspace_size": (I32, [PD, PQ, ctypes.POINTER(SZ)]),
+            "csa2_index_full": (I32, [PD, PQ, P, P, P, P, P, P, I64, P, SZ, P]),
+            "csa2_index_reindex_workspace_size": (I32, [PD, PQ, ctypes.POINTER(SZ)]),
+            "csa2_index_reindex": (I32, [PD, PQ, P, P, P, P, P, P, P, P, P, SZ, P]),
+            "csa2_attend_workspace_size": (I32, [PD, PQ, ctypes.POINTER(SZ)]),
+            "csa2_attend": (I32, [PD, PQ, P, P, ctypes.c_float, P, P, P, P, P, P, P, P, P, P, SZ, P]),
+        }
+        for name, (res, args) in sig.items():
+            f = getattr(L, name)
+            f.restype, f.argtypes = res, args
+        _lib = L
+    return _lib
+
+
+def abi_version() -> int:
+    return lib().csa2_abi_version()
+
+
+def _check(st: int):
+    if st != 0:
+        L = lib()
+        raise Csa2Error(f"{L.csa2_status_string(st).decode()}: {L.csa2_last_error().decode()}")
+
+
+@dataclasses.dataclass(frozen=True)
+class Dims:
+    n_heads: int
+    idx_heads: int
+    idx_dim: int
+    pool_blocks: int
+    topk: int
+    swa: int = 128
+    d_latent: int = 512
+    d_rope: int = 64
+    block: int = 8
+
+    def c(self) -> _Dims:
+        return _Dims(self.n_heads, self.d_latent, self.d_rope, self.idx_heads, self.idx_dim,
+                     self.block, self.pool_blocks, self.topk, self.swa)
+
+
+@dataclasses.dataclass
+class Batch:
+    """Decode queries: device int64 seq_base [n_q], int32 n_visible [n_q]."""
+    seq_base: torch.Tensor
+    n_visible: torch.Tensor
+    max_visible: int
+    tokens_per_seq: int = 1
+
+    @property
+    def n_q(self) -> int:
+        return self.n_visible.numel()
+
+    def c(self) -> _Queries:
+        if self.seq_base.dtype != torch.int64 or self.n_visible.dtype != torch.int32:
+            raise TypeError("seq_base must be int64 and n_visible int32")
+        _dev(self.seq_base, self.n_visible)
+        return _Queries(self.n_q, self.tokens_per_seq, self.max_visible, 0,
+                        self.seq_base.data_ptr(), self.n_visible.data_ptr())
+
+
+def _dev(*ts):
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise TypeError("CSA2 tensors must live on the GPU")
+        if not t.is_contiguous():
+            raise TypeError("CSA2 tensors must be contiguous")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _ws_size(fn, dims: Dims, b: Batch) -> int:
+    n = ctypes.c_size_t(0)
+    d, q = dims.c(), b.c()
+    _check(fn(ctypes.byref(d), ctypes.byref(q), ctypes.byref(n)))
+    return n.value
+
+
+def workspace_full(dims: Dims, b: Batch) -> int:
+    return _ws_size(lib().csa2_index_full_workspace_size, dims, b)
+
+
+def workspace_reindex(dims: Dims, b: Batch) -> int:
+    return _ws_size(lib().csa2_index_reindex_workspace_size, dims, b)
+
+
+def workspace_attend(dims: Dims, b: Batch) -> int:
+    return _ws_size(lib().csa2_attend_workspace_size, dims, b)
+
+
+def _workspace(nbytes: int, device, ws: Optional[torch.Tensor]) -> Optional[torch.Tensor]:
+    if nbytes == 0:
+        return ws
+    if ws is None or ws.numel() * ws.element_size() < nbytes:
+        ws = torch.empty(nbytes + 256, dtype=torch.uint8, device=device)
+    return ws
+
+
+def _ws_ptr(ws: Optional[torch.Tensor]):
+    if ws is None:
+        return None, 0
+    p = ws.data_ptr()
+    off = (-p) % 256
+    return p + off, ws.numel() * ws.element_size() - off
+
+
+def encode_kv(latent: torch.Tensor, rope: torch.Tensor, kv_codes: torch.Tensor,
+              kv_scales: torch.Tensor, kv_rope: torch.Tensor,
+              dst_row: Optional[torch.Tensor] = None) -> None:
+    """Encode bf16 latent [n, 512] (+ rope [n, 64]) into the FP4 cache planes
+    kv_codes uint8 [rows, 256], kv_scales uint8 [rows, 32], kv_rope bf16
+    [rows, 64] at rows dst_row (int64 [n]) or 0..n-1."""
+    _dev(latent, rope, kv_codes, kv_scales, kv_rope, dst_row)
+    if latent.dtype != torch.bfloat16 or rope.dtype != torch.bfloat16 or kv_rope.dtype != torch.bfloat16:
+        raise TypeError("latent, rope and kv_rope must be bfloat16")
+    n = latent.shape[0]
+    if latent.shape != (n, 512) or rope.shape != (n, 64):
+        raise ValueError("latent must be [n, 512] and rope [n, 64]")
+    rows = kv_codes.shape[0]
+    if kv_codes.shape != (rows, 256) or kv_scales.shape != (rows, 32) or kv_rope.shape != (rows, 64):
+        raise ValueError("cache planes must be [rows, 256] / [rows, 32] / [rows, 64]")
+    if dst_row is None and n > rows:
+        raise ValueError("more entries than cache rows")
+    if dst_row is not None and (dst_row.dtype != torch.int64 or dst_row.shape != (n,)):
+        raise ValueError("dst_row must be int64 [n]")
+    _check(lib().csa2_encode_kv(n, latent.data_ptr(), rope.data_ptr(), _ptr(dst_row), kv_codes.data_ptr(),
+                                kv_scales.data_ptr(), kv_rope.data_ptr(), _stream(latent.device)))
+
+
+def index_full(dims: Dims, b: Batch, idx_q: torch.Tensor, idx_w: torch.Tensor, idx_k: torch.Tensor,
+               pool_blocks: Optional[torch.Tensor] = None, pool_count: Optional[torch.Tensor] = None,
+               block_scores: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None
+               ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Full-mode indexer. idx_q fp8 [n_q, H_i, d_i], idx_w f32 [n_q, H_i],
+    idx_k fp8 [rows, d_i].  Returns (pool_blocks int32 [n_q, P], pool_count)."""
+    dev = idx_k.device
+    _dev(idx_q, idx_w, idx_k, pool_blocks, pool_count, block_scores)
+    n_q = b.n_q
+    if idx_q.dtype != torch.float8_e4m3fn or idx_k.dtype != torch.float8_e4m3fn:
+        raise TypeError("idx_q and idx_k must be float8_e4m3fn")
+    if idx_q.shape != (n_q, dims.idx_heads, dims.idx_dim) or idx_w.shape != (n_q, dims.idx_heads):
+        raise ValueError("idx_q / idx_w shape mismatch")
+    if idx_w.dtype != torch.float32 or idx_k.shape[1] != dims.idx_dim:
+        raise ValueError("idx_w must be float32 and idx_k [rows, d_i]")
+    if pool_blocks is None:
+        pool_blocks = torch.empty(n_q, dims.pool_blocks, dtype=torch.int32, device=dev)
+    if pool_count is None:
+        pool_count = torch.empty(n_q, dtype=torch.int32, device=dev)
+    ld = 0
+    if block_scores is not None:
+        if block_scores.dtype != torch.float32 or block_scores.dim() != 2 or block_scores.shape[0] != n_q:
+            raise ValueError("block_scores must be float32 [n_q, ld]")
+        ld = block_scores.shape[1]
+    ws = _workspace(workspace_full(dims, b), dev, ws)
+    wp, wn = _ws_ptr(ws)
+    d, q = dims.c(), b.c()
+    _check(lib().csa2_index_full(ctypes.byref(d), ctypes.byref(q), idx_q.data_ptr(), idx_w.data_ptr(),
+                                 idx_k.data_ptr(), pool_blocks.data_ptr(), pool_count.data_ptr(),
+                                 _ptr(block_scores), ld, wp, wn, _stream(dev)))
+    return pool_blocks, pool_count
+
+
+def index_reindex(dims: Dims, b: Batch, idx_q: torch.Tensor, idx_w: torch.Tensor, idx_k: torch.Tensor,
+                  pool_blocks: torch.Tensor, pool_count: torch.Tensor,
+                  topk_pos: Optional[torch.Tensor] = None, topk_count: Optional[torch.Tensor] = None,
+                  topk_scores: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None
+                  ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Reindex inside the pool. Returns (topk_pos int32 [n_q, K], topk_count)."""
+    dev = idx_k.device
+    _dev(idx_q, idx_w, idx_k, pool_blocks, pool_count, topk_pos, topk_count, topk_scores)
+    n_q = b.n_q
+    if idx_q.dtype != torch.float8_e4m3fn or idx_k.dtype != torch.float8_e4m3fn:
+        raise TypeError("idx_q and idx_k must be float8_e4m3fn")
+    if idx_q.shape != (n_q, dims.idx_heads, dims.idx_dim) or idx_w.shape != (n_q, dims.idx_heads):
+        raise ValueError("idx_q / idx_w shape mismatch")
+    if pool_blocks.shape != (n_q, dims.pool_blocks) or pool_count.shape != (n_q,):
+        raise ValueError("pool shape mismatch")
+    if topk_pos is None:
+        topk_pos = torch.empty(n_q, dims.topk, dtype=torch.int32, device=dev)
+    if topk_count is None:
+        topk_count = torch.empty(n_q, dtype=torch.int32, device=dev)
+    if topk_scores is not None and topk_scores.shape != (n_q, dims.topk):
+        raise ValueError("topk_scores must be float32 [n_q, K]")
+    ws = _workspace(workspace_reindex(dims, b), dev, ws)
+    wp, wn = _ws_ptr(ws)
+    d, q = dims.c(), b.c()
+    _check(lib().csa2_index_reindex(ctypes.byref(d), ctypes.byref(q), idx_q.data_ptr(), idx_w.data_ptr(),
+                                    idx_k.data_ptr(), pool_blocks.data_ptr(), pool_count.data_ptr(),
+                                    topk_pos.data_ptr(), topk_count.data_ptr(), _ptr(topk_scores),
+                                    wp, wn, _stream(dev)))
+    return topk_pos, topk_count
+
+
+def attend(dims: Dims, b: Batch, q_lat: torch.Tensor, q_rope: torch.Tensor, softmax_scale: float,
+           kv_codes: torch.Tensor, kv_scales: torch.Tensor, kv_rope: torch.Tensor,
+           topk_pos: torch.Tensor, topk_count: torch.Tensor, swa_kv: torch.Tensor, swa_base: torch.Tensor,
+           out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+           ws: Optional[torch.Tensor] = None, want_lse: bool = True) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Sparse FP4 + window attention. Returns (out f32 [n_q, H, 512], lse)."""
+    dev = q_lat.device
+    _dev(q_lat, q_rope, kv_codes, kv_scales, kv_rope, topk_pos, topk_count, swa_kv, swa_base, out, lse)
+    n_q, H = b.n_q, dims.n_heads
+    if q_lat.shape != (n_q, H, 512) or q_rope.shape != (n_q, H, 64):
+        raise ValueError("q_lat / q_rope shape mismatch")
+    if q_lat.dtype != torch.bfloat16 or q_rope.dtype != torch.bfloat16 or swa_kv.dtype != torch.bfloat16:
+        raise TypeError("q_lat, q_rope and swa_kv must be bfloat16")
+    if topk_pos.shape != (n_q, dims.topk) or swa_base.dtype != torch.int64 or swa_base.shape != (n_q,):
+        raise ValueError("topk_pos / swa_base shape mismatch")
+    if swa_kv.dim() != 2 or swa_kv.shape[1] != 576:
+        raise ValueError("swa_kv must be [rows, 576]")
+    if out is None:
+        out = torch.empty(n_q, H, 512, dtype=torch.float32, device=dev)
+    if lse is None and want_lse:
+        lse = torch.empty(n_q, H, dtype=torch.float32, device=dev)
+    ws = _workspace(workspace_attend(dims, b), dev, ws)
+    wp, wn = _ws_ptr(ws)
+    d, q = dims.c(), b.c()
+    _check(lib().csa2_attend(ctypes.byref(d), ctypes.byref(q), q_lat.data_ptr(), q_rope.data_ptr(),
+                             float(softmax_scale), kv_codes.data_ptr(), kv_scales.data_ptr(), kv_rope.data_ptr(),
+                             topk_pos.data_ptr(), topk_count.data_ptr(), swa_kv.data_ptr(), swa_base.data_ptr(),
+                             out.data_ptr(), _ptr(lse), wp, wn, _stream(dev)))
+    return out, lse

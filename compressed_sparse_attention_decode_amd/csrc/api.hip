@@ -1,0 +1,304 @@
+// C ABI of the CSA2 decode-path library: argument checks, workspace layout and
+// kernel launches.  Declarations and contracts are in include/csa2.h.
+#include <mutex>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/csa2.h"
+#include "internal.h"
+
+using namespace csa2;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+csa2_status fail(csa2_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+csa2_status hip_fail(hipError_t e, const char* what) {
+  return fail(CSA2_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// gfx950 check, once per device.
+csa2_status check_device() {
+  static std::mutex mu;
+  static int known[64] = {0};        // 0 unknown, 1 ok, 2 unsupported
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= 64) return fail(CSA2_ERR_UNSUPPORTED, "device id %d out of range", dev);
+  std::lock_guard<std::mutex> lk(mu);
+  if (known[dev] == 0) {
+    hipDeviceProp_t p;
+    e = hipGetDeviceProperties(&p, dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDeviceProperties");
+    known[dev] = strncmp(p.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+  }
+  if (known[dev] != 1) return fail(CSA2_ERR_UNSUPPORTED, "device %d is not gfx950", dev);
+  return CSA2_OK;
+}
+
+csa2_status check_dims(const csa2_dims* d) {
+  if (!d) return fail(CSA2_ERR_INVALID_ARG, "dims is NULL");
+  if (d->d_latent != 512) return fail(CSA2_ERR_INVALID_ARG, "d_latent must be 512 (got %d)", d->d_latent);
+  if (d->d_rope != 64) return fail(CSA2_ERR_INVALID_ARG, "d_rope must be 64 (got %d)", d->d_rope);
+  if (d->block != 8) return fail(CSA2_ERR_INVALID_ARG, "block must be 8 (got %d)", d->block);
+  if (d->n_heads < 16 || d->n_heads > 128 || d->n_heads % 16)
+    return fail(CSA2_ERR_INVALID_ARG, "n_heads must be a multiple of 16 in [16, 128] (got %d)", d->n_heads);
+  if (d->idx_heads < 1 || d->idx_heads > 64)
+    return fail(CSA2_ERR_INVALID_ARG, "idx_heads must be in [1, 64] (got %d)", d->idx_heads);
+  if (d->idx_dim != 64 && d->idx_dim != 128)
+    return fail(CSA2_ERR_INVALID_ARG, "idx_dim must be 64 or 128 (got %d)", d->idx_dim);
+  if (d->pool_blocks < 1 || d->pool_blocks > 2048)
+    return fail(CSA2_ERR_INVALID_ARG, "pool_blocks must be in [1, 2048] (got %d)", d->pool_blocks);
+  if (d->topk < 1 || d->topk > 2048 || d->topk > 8 * d->pool_blocks)
+    return fail(CSA2_ERR_INVALID_ARG, "topk must be in [1, min(2048, 8*pool_blocks)] (got %d)", d->topk);
+  if (d->swa < 0 || d->swa > 1024) return fail(CSA2_ERR_INVALID_ARG, "swa must be in [0, 1024] (got %d)", d->swa);
+  return CSA2_OK;
+}
+
+csa2_status check_queries(const csa2_queries* q) {
+  if (!q) return fail(CSA2_ERR_INVALID_ARG, "queries is NULL");
+  if (q->n_q < 1) return fail(CSA2_ERR_INVALID_ARG, "n_q must be >= 1 (got %d)", q->n_q);
+  if (q->n_q > (1 << 20)) return fail(CSA2_ERR_INVALID_ARG, "n_q must be <= 2^20 (got %d)", q->n_q);
+  if (q->tokens_per_seq < 1 || q->tokens_per_seq > 4 || q->n_q % q->tokens_per_seq)
+    return fail(CSA2_ERR_INVALID_ARG, "tokens_per_seq must be 1..4 and divide n_q (got %d)", q->tokens_per_seq);
+  if (q->max_visible < 0 || q->max_visible > kMaxVisible)
+    return fail(CSA2_ERR_INVALID_ARG, "max_visible must be in [0, 2^21] (got %d)", q->max_visible);
+  if (q->reserved != 0) return fail(CSA2_ERR_INVALID_ARG, "reserved must be 0");
+  if (!q->seq_base || !q->n_visible) return fail(CSA2_ERR_INVALID_ARG, "seq_base / n_visible is NULL");
+  return CSA2_OK;
+}
+
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+int64_t max_blocks(const csa2_dims* d, const csa2_queries* q) {
+  const int64_t c = q->max_visible > d->swa ? q->max_visible - d->swa : 0;
+  return (c + 7) / 8;
+}
+
+// index_full workspace: [hist n_q x 4096 u32][block scores n_q x ldb f32]
+int64_t full_ldb(const csa2_dims* d, const csa2_queries* q) {
+  const int64_t nb = max_blocks(d, q);
+  return ((nb > 0 ? nb : 1) + 63) / 64 * 64;
+}
+
+size_t full_ws(const csa2_dims* d, const csa2_queries* q) {
+  return align256((size_t)q->n_q * kHistBins * 4) + align256((size_t)q->n_q * full_ldb(d, q) * 4);
+}
+
+size_t reindex_ws(const csa2_dims* d, const csa2_queries* q) {
+  return align256((size_t)q->n_q * d->pool_blocks * 8 * 4);
+}
+
+struct AttendPlan { int nw, hg, splits, split_entries; };
+
+AttendPlan attend_plan(const csa2_dims* d, const csa2_queries* q) {
+  AttendPlan p;
+  p.nw = attend_waves(d->n_heads);
+  p.hg = d->n_heads / (16 * p.nw);
+  const int emax = d->topk + d->swa;
+  const int tiles = (emax + kAttendTile - 1) / kAttendTile;
+  // aim for >= 2 workgroups per CU overall, but keep >= 4 tiles per split
+  int want = (512 + q->n_q * p.hg - 1) / (q->n_q * p.hg);
+  int maxs = (tiles + 3) / 4;
+  if (maxs < 1) maxs = 1;
+  int s = want < 1 ? 1 : (want > maxs ? maxs : want);
+  const int tps = (tiles + s - 1) / s;
+  p.split_entries = tps * kAttendTile;
+  p.splits = (emax + p.split_entries - 1) / p.split_entries;
+  if (p.splits < 1) p.splits = 1;
+  return p;
+}
+
+size_t attend_ws(const csa2_dims* d, const csa2_queries* q) {
+  const AttendPlan p = attend_plan(d, q);
+  if (p.splits == 1) return 0;
+  const size_t rows = (size_t)q->n_q * p.splits * d->n_heads;
+  return align256(rows * 512 * 4) + align256(rows * 2 * 4);
+}
+
+csa2_status check_ws(void* ws, size_t have, size_t need) {
+  if (need == 0) return CSA2_OK;
+  if (!ws) return fail(CSA2_ERR_WORKSPACE, "workspace is NULL (need %zu bytes)", need);
+  if (((uintptr_t)ws) & 255) return fail(CSA2_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  if (have < need) return fail(CSA2_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", have, need);
+  return CSA2_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t csa2_abi_version(void) { return CSA2_ABI_VERSION; }
+
+const char* csa2_status_string(csa2_status s) {
+  switch (s) {
+    case CSA2_OK: return "ok";
+    case CSA2_ERR_INVALID_ARG: return "invalid argument";
+    case CSA2_ERR_UNSUPPORTED: return "unsupported device";
+    case CSA2_ERR_WORKSPACE: return "workspace missing or too small";
+    case CSA2_ERR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+const char* csa2_last_error(void) { return g_err; }
+
+csa2_status csa2_encode_kv(int64_t n, const uint16_t* latent, const uint16_t* rope, const int64_t* dst_row,
+                           uint8_t* kv_codes, uint8_t* kv_scales, uint16_t* kv_rope, void* stream) {
+  if (n < 0) return fail(CSA2_ERR_INVALID_ARG, "n must be >= 0 (got %lld)", (long long)n);
+  if (n > ((int64_t)1 << 36)) return fail(CSA2_ERR_INVALID_ARG, "n too large");
+  if (n == 0) return CSA2_OK;
+  if (!latent || !rope || !kv_codes || !kv_scales || !kv_rope)
+    return fail(CSA2_ERR_INVALID_ARG, "required pointer is NULL");
+  if (((uintptr_t)latent | (uintptr_t)rope | (uintptr_t)kv_rope) & 15)
+    return fail(CSA2_ERR_INVALID_ARG, "latent, rope and kv_rope must be 16-byte aligned");
+  if ((uintptr_t)kv_codes & 7) return fail(CSA2_ERR_INVALID_ARG, "kv_codes must be 8-byte aligned");
+  csa2_status st = check_device();
+  if (st) return st;
+  hipError_t e = launch_encode(n, latent, rope, dst_row, kv_codes, kv_scales, kv_rope, (hipStream_t)stream);
+  return e == hipSuccess ? CSA2_OK : hip_fail(e, "encode launch");
+}
+
+csa2_status csa2_index_full_workspace_size(const csa2_dims* d, const csa2_queries* q, size_t* bytes) {
+  csa2_status st = check_dims(d);
+  if (st) return st;
+  if ((st = check_queries(q))) return st;
+  if (!bytes) return fail(CSA2_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = full_ws(d, q);
+  return CSA2_OK;
+}
+
+csa2_status csa2_index_full(const csa2_dims* d, const csa2_queries* q, const uint8_t* idx_q, const float* idx_w,
+                            const uint8_t* idx_k, int32_t* pool_blocks, int32_t* pool_count, float* block_scores,
+                            int64_t ld_block_scores, void* ws, size_t ws_bytes, void* stream) {
+  csa2_status st = check_dims(d);
+  if (st) return st;
+  if ((st = check_queries(q))) return st;
+  if (!idx_q || !idx_w || !idx_k || !pool_blocks || !pool_count)
+    return fail(CSA2_ERR_INVALID_ARG, "required pointer is NULL");
+  if (((uintptr_t)idx_q | (uintptr_t)idx_k) & 15) return fail(CSA2_ERR_INVALID_ARG, "idx_q and idx_k must be 16-byte aligned");
+  const int64_t nb = max_blocks(d, q);
+  if (block_scores && ld_block_scores < nb)
+    return fail(CSA2_ERR_INVALID_ARG, "ld_block_scores %lld < %lld blocks", (long long)ld_block_scores, (long long)nb);
+  if ((st = check_ws(ws, ws_bytes, full_ws(d, q)))) return st;
+  if ((st = check_device())) return st;
+  hipStream_t s = (hipStream_t)stream;
+  uint32_t* hist = (uint32_t*)ws;
+  float* bs_ws = (float*)((char*)ws + align256((size_t)q->n_q * kHistBins * 4));
+
+  ScanArgs sa;
+  sa.idx_q = idx_q; sa.idx_w = idx_w; sa.idx_k = idx_k;
+  sa.seq_base = q->seq_base; sa.n_visible = q->n_visible;
+  sa.n_q = q->n_q; sa.hi = d->idx_heads; sa.d = d->idx_dim; sa.swa = d->swa; sa.g = q->tokens_per_seq;
+  const int64_t cmax = nb * 8;
+  sa.tiles = (int)((cmax + kScanTile - 1) / kScanTile);
+  sa.bscore = block_scores ? block_scores : bs_ws;
+  sa.ld = block_scores ? ld_block_scores : full_ldb(d, q);
+  sa.hist = hist;
+
+  hipError_t e = launch_fill_u32(hist, (size_t)q->n_q * kHistBins, 0u, s);
+  if (e != hipSuccess) return hip_fail(e, "histogram clear");
+  if ((e = launch_scan(sa, s)) != hipSuccess) return hip_fail(e, "scan launch");
+
+  PoolArgs pa;
+  pa.bscore = sa.bscore; pa.ld = sa.ld; pa.hist = hist; pa.n_visible = q->n_visible;
+  pa.n_q = q->n_q; pa.swa = d->swa; pa.pool = d->pool_blocks;
+  pa.pool_blocks = pool_blocks; pa.pool_count = pool_count;
+  if ((e = launch_pool_select(pa, s)) != hipSuccess) return hip_fail(e, "pool select launch");
+  return CSA2_OK;
+}
+
+csa2_status csa2_index_reindex_workspace_size(const csa2_dims* d, const csa2_queries* q, size_t* bytes) {
+  csa2_status st = check_dims(d);
+  if (st) return st;
+  if ((st = check_queries(q))) return st;
+  if (!bytes) return fail(CSA2_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = reindex_ws(d, q);
+  return CSA2_OK;
+}
+
+csa2_status csa2_index_reindex(const csa2_dims* d, const csa2_queries* q, const uint8_t* idx_q, const float* idx_w,
+                               const uint8_t* idx_k, const int32_t* pool_blocks, const int32_t* pool_count,
+                               int32_t* topk_pos, int32_t* topk_count, float* topk_scores, void* ws,
+                               size_t ws_bytes, void* stream) {
+  csa2_status st = check_dims(d);
+  if (st) return st;
+  if ((st = check_queries(q))) return st;
+  if (!idx_q || !idx_w || !idx_k || !pool_blocks || !pool_count || !topk_pos || !topk_count)
+    return fail(CSA2_ERR_INVALID_ARG, "required pointer is NULL");
+  if (((uintptr_t)idx_q | (uintptr_t)idx_k) & 15) return fail(CSA2_ERR_INVALID_ARG, "idx_q and idx_k must be 16-byte aligned");
+  if ((st = check_ws(ws, ws_bytes, reindex_ws(d, q)))) return st;
+  if ((st = check_device())) return st;
+  ReindexArgs ra;
+  ra.idx_q = idx_q; ra.idx_w = idx_w; ra.idx_k = idx_k;
+  ra.seq_base = q->seq_base; ra.n_visible = q->n_visible;
+  ra.pool_blocks = pool_blocks; ra.pool_count = pool_count;
+  ra.n_q = q->n_q; ra.hi = d->idx_heads; ra.d = d->idx_dim; ra.swa = d->swa;
+  ra.pool = d->pool_blocks; ra.topk = d->topk;
+  ra.split = kReindexSplit;
+  if (ra.split > (d->pool_blocks + 1) / 2) ra.split = (d->pool_blocks + 1) / 2;
+  if (ra.split < 1) ra.split = 1;
+  ra.scores = (float*)ws;
+  ra.topk_pos = topk_pos; ra.topk_count = topk_count; ra.topk_scores = topk_scores;
+  hipError_t e = launch_reindex(ra, (hipStream_t)stream);
+  return e == hipSuccess ? CSA2_OK : hip_fail(e, "reindex launch");
+}
+
+csa2_status csa2_attend_workspace_size(const csa2_dims* d, const csa2_queries* q, size_t* bytes) {
+  csa2_status st = check_dims(d);
+  if (st) return st;
+  if ((st = check_queries(q))) return st;
+  if (!bytes) return fail(CSA2_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = attend_ws(d, q);
+  return CSA2_OK;
+}
+
+csa2_status csa2_attend(const csa2_dims* d, const csa2_queries* q, const uint16_t* q_lat, const uint16_t* q_rope,
+                        float softmax_scale, const uint8_t* kv_codes, const uint8_t* kv_scales,
+                        const uint16_t* kv_rope, const int32_t* topk_pos, const int32_t* topk_count,
+                        const uint16_t* swa_kv, const int64_t* swa_base, float* out, float* lse, void* ws,
+                        size_t ws_bytes, void* stream) {
+  csa2_status st = check_dims(d);
+  if (st) return st;
+  if ((st = check_queries(q))) return st;
+  if (!q_lat || !q_rope || !kv_codes || !kv_scales || !kv_rope || !topk_pos || !topk_count || !swa_base || !out)
+    return fail(CSA2_ERR_INVALID_ARG, "required pointer is NULL");
+  if (!swa_kv && d->swa > 0) return fail(CSA2_ERR_INVALID_ARG, "swa_kv is NULL");
+  if (!(softmax_scale == softmax_scale) || softmax_scale > 3.0e38f || softmax_scale < -3.0e38f)
+    return fail(CSA2_ERR_INVALID_ARG, "softmax_scale must be finite");
+  if (((uintptr_t)q_lat | (uintptr_t)q_rope | (uintptr_t)kv_rope | (uintptr_t)swa_kv | (uintptr_t)out) & 15)
+    return fail(CSA2_ERR_INVALID_ARG, "q_lat, q_rope, kv_rope, swa_kv and out must be 16-byte aligned");
+  if ((uintptr_t)kv_codes & 7) return fail(CSA2_ERR_INVALID_ARG, "kv_codes must be 8-byte aligned");
+  if ((st = check_ws(ws, ws_bytes, attend_ws(d, q)))) return st;
+  if ((st = check_device())) return st;
+  const AttendPlan p = attend_plan(d, q);
+  AttendArgs aa;
+  aa.q_lat = q_lat; aa.q_rope = q_rope; aa.scale_log2 = softmax_scale * 1.4426950408889634f;
+  aa.kv_codes = kv_codes; aa.kv_scales = kv_scales; aa.kv_rope = kv_rope;
+  aa.topk_pos = topk_pos; aa.topk_count = topk_count; aa.swa_kv = swa_kv; aa.swa_base = swa_base;
+  aa.seq_base = q->seq_base; aa.n_visible = q->n_visible;
+  aa.n_q = q->n_q; aa.heads = d->n_heads; aa.topk = d->topk; aa.swa = d->swa;
+  aa.head_groups = p.hg; aa.splits = p.splits; aa.split_entries = p.split_entries;
+  aa.out = out; aa.lse = lse;
+  if (p.splits > 1) {
+    const size_t rows = (size_t)q->n_q * p.splits * d->n_heads;
+    aa.part_o = (float*)ws;
+    aa.part_ml = (float*)((char*)ws + align256(rows * 512 * 4));
+  } else {
+    aa.part_o = nullptr;
+    aa.part_ml = nullptr;
+  }
+  hipError_t e = launch_attend(aa, (hipStream_t)stream);
+  return e == hipSuccess ? CSA2_OK : hip_fail(e, "attend launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,105 @@
+// Device-side helpers shared by the CSA2 kernels (gfx950 / CDNA4).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "internal.h"
+
+namespace csa2 {
+
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
+typedef unsigned v2u __attribute__((ext_vector_type(2)));
+
+constexpr int kLatent = 512;           // latent width shared across heads
+constexpr int kRope = 64;              // bf16 RoPE key width
+constexpr int kKeyDim = kLatent + kRope;
+constexpr int kGroup = 16;             // channels per E4M3 scale
+constexpr int kCodeBytes = kLatent / 2;
+constexpr int kScaleBytes = kLatent / kGroup;
+constexpr int kBlock = 8;              // indexer block
+constexpr int kWave = 64;
+
+// Order-preserving map float -> uint32 (larger float -> larger key); -0 and
+// +0 map to the same key so equal scores tie exactly.
+__device__ __forceinline__ uint32_t order_key(float x) {
+  uint32_t u = __float_as_uint(x);
+  if (u == 0x80000000u) u = 0;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float key_float(uint32_t k) {
+  uint32_t u = (k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k;
+  return __uint_as_float(u);
+}
+
+// Raw buffer resource over [base, base + bytes): loads past the end return 0.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ v4u buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+
+// Four OCP E4M3FN bytes -> four f16 (exact: every E4M3 value is an f16).
+__device__ __forceinline__ void fp8x4_to_f16(uint32_t x, _Float16* o) {
+  v2h lo = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x, 1.0f, false);
+  v2h hi = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x, 1.0f, true);
+  o[0] = lo[0]; o[1] = lo[1]; o[2] = hi[0]; o[3] = hi[1];
+}
+
+// Eight E4M3 bytes (two dwords) -> one v8h MFMA operand.
+__device__ __forceinline__ v8h fp8x8_to_v8h(uint32_t a, uint32_t b) {
+  v2h p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(a, 1.0f, false);
+  v2h p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(a, 1.0f, true);
+  v2h p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b, 1.0f, false);
+  v2h p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b, 1.0f, true);
+  v8h r;
+  r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
+  r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
+  return r;
+}
+
+__device__ __forceinline__ float bf16_to_float(uint16_t b) {
+  return __uint_as_float((uint32_t)b << 16);
+}
+
+// E4M3FN byte -> float (scale decode; NaN codes are not produced by encode).
+__device__ __forceinline__ float e4m3_to_float(uint32_t c) {
+  uint32_t e = (c >> 3) & 15, m = c & 7;
+  float v = e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0.001953125f;
+  return (c & 0x80) ? -v : v;
+}
+
+// Block-wide exclusive scan of one uint32 per thread (blockDim.x = NT, a
+// multiple of 64).  `sh` needs NT/64 + 1 words.  Returns the exclusive prefix;
+// *total receives the block sum.  Contains __syncthreads().
+template <int NT>
+__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* sh, uint32_t* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint32_t x = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    uint32_t y = __shfl_up(x, d, 64);
+    if (lane >= d) x += y;
+  }
+  if (lane == 63) sh[wave] = x;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t acc = 0;
+    for (int w = 0; w < NT / 64; ++w) { uint32_t t = sh[w]; sh[w] = acc; acc += t; }
+    sh[NT / 64] = acc;
+  }
+  __syncthreads();
+  uint32_t r = sh[wave] + x - v;
+  *total = sh[NT / 64];
+  __syncthreads();
+  return r;
+}
+
+}  // namespace csa2

@@ -1,0 +1,107 @@
+// FP4 main-KV encode: E2M1 codes with one E4M3 scale per 16 latent channels.
+//
+// Follows "DeepSeek-V4.1-Flash 梗概" §3.2 (FP4 main KV: E2M1 with one E4M3
+// scale per 16 channels) and the FP4Quantizer of section 8 of the newsaint.id
+// page "DeepSeek-V4.1-Flash 2026: Arsitektur ... CSA2, FP4 KV Caching ..."
+// (scale = group amax / 6 clamped to 448, nearest E2M1 level).  The scale is
+// rounded to E4M3 with round-to-nearest-even, E2M1 ties go to the even code.
+//
+// One thread per 16-channel group: 32 bytes of bf16 in, 8 code bytes and one
+// scale byte out.  A 256-thread block covers 8 entries; the bf16 reads and the
+// code writes are contiguous across the block.  HBM-bound (1,576 bytes moved
+// per entry, about 4 ALU ops per byte).
+#include "common.h"
+#include "internal.h"
+
+namespace csa2 {
+namespace {
+
+// RNE of t in [0, 448] to an E4M3FN code (0x00..0x7E).
+__device__ __forceinline__ uint32_t e4m3_rne(float t) {
+  if (t < 0.015625f) {                       // below 2^-6: subnormal grid 2^-9
+    return (uint32_t)__builtin_rintf(t * 512.0f);   // 8 -> 0x08 = 2^-6, still right
+  }
+  uint32_t u = __float_as_uint(t);
+  u += 0x7FFFFu + ((u >> 20) & 1u);          // round mantissa to 3 bits, ties to even
+  return (u >> 20) - (120u << 3);
+}
+
+__global__ __launch_bounds__(256) void k_encode(int64_t n, const uint16_t* __restrict__ latent,
+                                                const uint16_t* __restrict__ rope,
+                                                const int64_t* __restrict__ dst_row,
+                                                uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
+                                                uint16_t* __restrict__ rope_out) {
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t e = gid >> 5;
+  const int g = (int)(gid & 31);
+  if (e >= n) return;
+  const int64_t row = dst_row ? dst_row[e] : e;
+
+  const v4u* src = reinterpret_cast<const v4u*>(latent + e * kLatent + g * kGroup);
+  v4u a = src[0], b = src[1];
+  uint32_t w[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+
+  // group maximum of |x| on the bit patterns (finite bf16 magnitudes order as integers)
+  uint32_t amax = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    amax = max(amax, w[i] & 0x7FFFu);
+    amax = max(amax, (w[i] >> 16) & 0x7FFFu);
+  }
+  const float t = fminf(__uint_as_float(amax << 16) / 6.0f, 448.0f);
+  const uint32_t S = e4m3_rne(t);
+  const float s = e4m3_to_float(S);
+
+  uint32_t lo = 0, hi = 0;
+  if (s != 0.0f) {
+    const float t025 = 0.25f * s, t075 = 0.75f * s, t125 = 1.25f * s, t175 = 1.75f * s;
+    const float t250 = 2.5f * s, t350 = 3.5f * s, t500 = 5.0f * s;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const uint32_t bits = (w[i >> 1] >> ((i & 1) * 16)) & 0xFFFFu;
+      const float ax = __uint_as_float((bits & 0x7FFFu) << 16);
+      // nearest E2M1 level, ties to the even code: strict at ties whose lower
+      // neighbour is even, inclusive where the upper neighbour is even.
+      uint32_t m = (ax > t025) + (ax >= t075) + (ax > t125) + (ax >= t175) +
+                   (ax > t250) + (ax >= t350) + (ax > t500);
+      const uint32_t code = ((bits >> 12) & 8u) | m;
+      if (i < 8) lo |= code << (4 * i);
+      else hi |= code << (4 * (i - 8));
+    }
+  }
+  v2u packed = {lo, hi};
+  *reinterpret_cast<v2u*>(codes + row * kCodeBytes + g * 8) = packed;
+  scales[row * kScaleBytes + g] = (uint8_t)S;
+  if (g < 8) {
+    const v4u* rs = reinterpret_cast<const v4u*>(rope + e * kRope + g * 8);
+    *reinterpret_cast<v4u*>(rope_out + row * kRope + g * 8) = rs[0];
+  }
+}
+
+__global__ void k_fill_u32(uint32_t* p, size_t n, uint32_t v) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+    p[i] = v;
+}
+
+}  // namespace
+
+hipError_t launch_encode(int64_t n, const uint16_t* latent, const uint16_t* rope,
+                         const int64_t* dst_row, uint8_t* codes, uint8_t* scales,
+                         uint16_t* rope_out, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  const int64_t threads = n * 32;
+  const int64_t blocks = (threads + 255) / 256;
+  hipLaunchKernelGGL(k_encode, dim3((unsigned)blocks), dim3(256), 0, s, n, latent, rope, dst_row,
+                     codes, scales, rope_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_u32(uint32_t* p, size_t n, uint32_t v, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  size_t blocks = (n + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(k_fill_u32, dim3((unsigned)blocks), dim3(256), 0, s, p, n, v);
+  return hipGetLastError();
+}
+
+}  // namespace csa2

@@ -1,0 +1,91 @@
+// Launchers shared between the host dispatch and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace csa2 {
+
+struct ScanArgs {
+  const uint8_t* idx_q;      // [n_q, Hi, d]
+  const float* idx_w;        // [n_q, Hi]
+  const uint8_t* idx_k;      // [rows, d]
+  const int64_t* seq_base;   // [n_q]
+  const int32_t* n_visible;  // [n_q]
+  int n_q, hi, d, swa, g;    // g: queries per sequence
+  int tiles;                 // position tiles per query
+  float* bscore;             // [n_q, ld]
+  int64_t ld;
+  uint32_t* hist;            // [n_q, kHistBins]
+};
+
+struct PoolArgs {
+  const float* bscore;
+  int64_t ld;
+  const uint32_t* hist;
+  const int32_t* n_visible;
+  int n_q, swa, pool;
+  int32_t* pool_blocks;      // [n_q, pool]
+  int32_t* pool_count;
+};
+
+struct ReindexArgs {
+  const uint8_t* idx_q;
+  const float* idx_w;
+  const uint8_t* idx_k;
+  const int64_t* seq_base;
+  const int32_t* n_visible;
+  const int32_t* pool_blocks;
+  const int32_t* pool_count;
+  int n_q, hi, d, swa, pool, topk;
+  int split;                 // workgroups per query in the scoring kernel
+  float* scores;             // workspace [n_q, 8 * pool]
+  int32_t* topk_pos;
+  int32_t* topk_count;
+  float* topk_scores;        // optional
+};
+
+struct AttendArgs {
+  const uint16_t* q_lat;     // [n_q, H, 512]
+  const uint16_t* q_rope;    // [n_q, H, 64]
+  float scale_log2;          // softmax_scale * log2(e)
+  const uint8_t* kv_codes;
+  const uint8_t* kv_scales;
+  const uint16_t* kv_rope;
+  const int32_t* topk_pos;
+  const int32_t* topk_count;
+  const uint16_t* swa_kv;
+  const int64_t* swa_base;
+  const int64_t* seq_base;
+  const int32_t* n_visible;
+  int n_q, heads, topk, swa;
+  int head_groups;           // workgroups across heads per query
+  int splits;                // workgroups across entries per query
+  int split_entries;         // entries per split (multiple of the tile)
+  float* out;                // [n_q, H, 512]
+  float* lse;                // optional [n_q, H]
+  float* part_o;             // [n_q, splits, H, 512] when splits > 1
+  float* part_ml;            // [n_q, splits, H, 2]
+};
+
+hipError_t launch_encode(int64_t n, const uint16_t* latent, const uint16_t* rope,
+                         const int64_t* dst_row, uint8_t* codes, uint8_t* scales,
+                         uint16_t* rope_out, hipStream_t s);
+hipError_t launch_fill_u32(uint32_t* p, size_t n, uint32_t v, hipStream_t s);
+hipError_t launch_scan(const ScanArgs& a, hipStream_t s);
+hipError_t launch_pool_select(const PoolArgs& a, hipStream_t s);
+hipError_t launch_reindex(const ReindexArgs& a, hipStream_t s);
+hipError_t launch_attend(const AttendArgs& a, hipStream_t s);
+int attend_waves(int heads);   // waves (16 heads each) per attention workgroup
+
+// Tiling constants the host needs for grids and workspace sizes.
+constexpr int kHistShift = 20;         // coarse histogram: top 12 bits of a key
+constexpr int kHistBins = 1 << (32 - kHistShift);
+constexpr int kScanTile = 2048;        // positions per scan workgroup
+constexpr int kAttendTile = 32;        // entries per attention tile
+constexpr int kReindexSplit = 16;      // scoring workgroups per query
+constexpr int kMaxVisible = 1 << 21;   // bound of n_visible
+constexpr int kMaxBlocks = kMaxVisible / 8;
+
+}  // namespace csa2

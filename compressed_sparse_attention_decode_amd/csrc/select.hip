@@ -1,0 +1,232 @@
+// Top-P block pool selection (Full mode, second half).
+//
+// Follows "DeepSeek-V4.1-Flash 梗概" §3.2 (hierarchical sparse indexer: the
+// Full layer keeps the Top-2048 blocks of 8 as the candidate pool).  Order is
+// (block score descending, block id ascending); the pool is written in
+// ascending block order.
+//
+// One 1024-thread workgroup per query:
+//  1. the scan's coarse histogram (top 12 bits of the order-preserving key)
+//     gives the bin b* holding the P-th best block; blocks in higher bins are
+//     selected outright;
+//  2. one pass over the block scores marks those blocks in an LDS bitmap and
+//     appends the blocks of bin b* to an LDS candidate list (wave ballots);
+//  3. an exact radix select over the low 20 key bits of the candidates finds
+//     the threshold key T and how many blocks equal to T are still needed;
+//     a candidate list that overflows LDS is re-read from global memory;
+//  4. ordered compaction of the bitmap writes ascending block ids, admitting
+//     blocks equal to T in ascending order (ties to the lower id).
+#include "common.h"
+#include "internal.h"
+
+namespace csa2 {
+namespace {
+
+constexpr int kSelThreads = 1024;
+constexpr int kCandCap = 8192;
+constexpr int kMaxWords = kMaxBlocks / 32;
+
+__device__ __forceinline__ uint32_t lane_prefix(uint64_t mask) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+// Wave 0 finds, in a histogram of `nbins` (<= 256) counts, the bin where the
+// count from the top reaches `need`.  Writes {bin, count strictly above} to out.
+__device__ void find_crossing(const uint32_t* hist, int nbins, uint32_t need, uint32_t* out) {
+  const int lane = threadIdx.x & 63;
+  if (threadIdx.x >= 64) return;
+  const int per = (nbins + 63) / 64;
+  // lane handles bins from the top: [nbins - (lane+1)*per, nbins - lane*per)
+  uint32_t local = 0;
+  for (int k = 0; k < per; ++k) {
+    const int b = nbins - 1 - (lane * per + k);
+    if (b >= 0) local += hist[b];
+  }
+  uint32_t x = local;
+  for (int d = 1; d < 64; d <<= 1) {
+    const uint32_t y = __shfl_up(x, d, 64);
+    if (lane >= d) x += y;
+  }
+  uint32_t above = x - local;
+  if (above < need && need <= x) {
+    for (int k = 0; k < per; ++k) {
+      const int b = nbins - 1 - (lane * per + k);
+      if (b < 0) break;
+      const uint32_t cnt = hist[b];
+      if (above + cnt >= need) {
+        out[0] = (uint32_t)b;
+        out[1] = above;
+        break;
+      }
+      above += cnt;
+    }
+  }
+}
+
+__global__ __launch_bounds__(kSelThreads) void k_pool_select(PoolArgs a) {
+  __shared__ uint32_t s_hist[kHistBins];
+  __shared__ uint32_t s_sel[kMaxWords];
+  __shared__ uint32_t s_tie[kMaxWords];
+  __shared__ uint32_t s_ckey[kCandCap];
+  __shared__ int32_t s_cj[kCandCap];
+  __shared__ uint32_t s_scan[kSelThreads / 64 + 1];
+  __shared__ uint32_t s_misc[4];
+  __shared__ uint32_t s_ccount;
+
+  const int q = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = a.n_visible[q];
+  const int c = max(0, n - a.swa);
+  const int nb = (c + 7) >> 3;
+  const int P = a.pool;
+  int32_t* out = a.pool_blocks + (int64_t)q * P;
+  if (nb <= P) {
+    for (int j = tid; j < P; j += kSelThreads) out[j] = j < nb ? j : -1;
+    if (tid == 0) a.pool_count[q] = nb;
+    return;
+  }
+  const float* bs = a.bscore + (int64_t)q * a.ld;
+  const uint32_t* gh = a.hist + (int64_t)q * kHistBins;
+
+  // 1. bin b* of the P-th best block (4 bins per thread, from the top)
+  constexpr int kPer = kHistBins / kSelThreads;
+  uint32_t local = 0, cnt[kPer];
+  for (int k = 0; k < kPer; ++k) {
+    cnt[k] = gh[kHistBins - 1 - (tid * kPer + k)];
+    local += cnt[k];
+  }
+  uint32_t total;
+  uint32_t above = block_exclusive_scan<kSelThreads>(local, s_scan, &total);
+  if (above < (uint32_t)P && (uint32_t)P <= above + local) {
+    for (int k = 0; k < kPer; ++k) {
+      if (above + cnt[k] >= (uint32_t)P) {
+        s_misc[0] = kHistBins - 1 - (tid * kPer + k);
+        s_misc[1] = above;
+        break;
+      }
+      above += cnt[k];
+    }
+  }
+  const int nw = (nb + 31) >> 5;
+  for (int w = tid; w < nw; w += kSelThreads) { s_sel[w] = 0; s_tie[w] = 0; }
+  if (tid == 0) s_ccount = 0;
+  __syncthreads();
+  const uint32_t bstar = s_misc[0];
+  uint32_t need = (uint32_t)P - s_misc[1];
+
+  // 2. mark blocks above b*, collect the blocks of bin b*
+  for (int base = 0; base < nb; base += kSelThreads) {
+    const int jb = base + tid;
+    const uint32_t key = jb < nb ? order_key(bs[jb]) : 0u;
+    const uint32_t bin = key >> kHistShift;
+    const bool hi = jb < nb && bin > bstar;
+    const bool cand = jb < nb && bin == bstar;
+    const uint64_t mhi = __ballot(hi);
+    const uint64_t mc = __ballot(cand);
+    if (lane == 0) {
+      const int w0 = (base + wave * 64) >> 5;
+      s_sel[w0] = (uint32_t)mhi;
+      s_sel[w0 + 1] = (uint32_t)(mhi >> 32);
+    }
+    uint32_t slot0 = 0;
+    if (lane == 0 && mc) slot0 = atomicAdd(&s_ccount, (uint32_t)__popcll(mc));
+    slot0 = __shfl(slot0, 0, 64);
+    if (cand) {
+      const uint32_t slot = slot0 + lane_prefix(mc);
+      if (slot < kCandCap) { s_ckey[slot] = key; s_cj[slot] = jb; }
+    }
+  }
+  __syncthreads();
+  const uint32_t C = s_ccount;
+  const bool in_lds = C <= (uint32_t)kCandCap;
+
+  // 3. radix select of the need-th largest key inside bin b* (bits 19..0)
+  uint32_t prefix = bstar << kHistShift;
+  int fixed = 32 - kHistShift;
+  const int widths[3] = {8, 8, 4};
+  for (int ps = 0; ps < 3; ++ps) {
+    const int wdt = widths[ps];
+    const int sh = 32 - fixed - wdt;
+    for (int i = tid; i < 256; i += kSelThreads) s_hist[i] = 0;
+    __syncthreads();
+    const uint32_t hmask = ~0u << (32 - fixed);
+    if (in_lds) {
+      for (uint32_t i = tid; i < C; i += kSelThreads) {
+        const uint32_t key = s_ckey[i];
+        if ((key & hmask) == prefix) atomicAdd(&s_hist[(key >> sh) & ((1u << wdt) - 1)], 1u);
+      }
+    } else {
+      for (int jb = tid; jb < nb; jb += kSelThreads) {
+        const uint32_t key = order_key(bs[jb]);
+        if ((key & hmask) == prefix) atomicAdd(&s_hist[(key >> sh) & ((1u << wdt) - 1)], 1u);
+      }
+    }
+    __syncthreads();
+    find_crossing(s_hist, 1 << wdt, need, s_misc + 2);
+    __syncthreads();
+    prefix |= s_misc[2] << sh;
+    need -= s_misc[3];
+    fixed += wdt;
+    __syncthreads();
+  }
+  const uint32_t T = prefix;
+  const uint32_t need_eq = need;
+
+  // mark candidates above T (selected) and equal to T (tie bits)
+  if (in_lds) {
+    for (uint32_t i = tid; i < C; i += kSelThreads) {
+      const uint32_t key = s_ckey[i];
+      const int jb = s_cj[i];
+      if (key > T) atomicOr(&s_sel[jb >> 5], 1u << (jb & 31));
+      else if (key == T) atomicOr(&s_tie[jb >> 5], 1u << (jb & 31));
+    }
+  } else {
+    for (int jb = tid; jb < nb; jb += kSelThreads) {
+      const uint32_t key = order_key(bs[jb]);
+      if ((key >> kHistShift) != bstar) continue;
+      if (key > T) atomicOr(&s_sel[jb >> 5], 1u << (jb & 31));
+      else if (key == T) atomicOr(&s_tie[jb >> 5], 1u << (jb & 31));
+    }
+  }
+  __syncthreads();
+
+  // 4. ordered compaction; ties admitted in ascending block order
+  const int wpt = (nw + kSelThreads - 1) / kSelThreads;
+  const int w_lo = min(nw, tid * wpt), w_hi = min(nw, w_lo + wpt);
+  uint32_t ties = 0;
+  for (int w = w_lo; w < w_hi; ++w) ties += __popc(s_tie[w]);
+  uint32_t tie_before = block_exclusive_scan<kSelThreads>(ties, s_scan, &total);
+  uint32_t sel_local = 0;
+  for (int w = w_lo; w < w_hi; ++w) {
+    uint32_t t = s_tie[w], acc = 0;
+    while (t && tie_before < need_eq) {
+      const uint32_t bit = t & (0u - t);
+      acc |= bit;
+      t ^= bit;
+      ++tie_before;
+    }
+    const uint32_t fin = s_sel[w] | acc;
+    s_sel[w] = fin;
+    sel_local += __popc(fin);
+  }
+  uint32_t out_before = block_exclusive_scan<kSelThreads>(sel_local, s_scan, &total);
+  for (int w = w_lo; w < w_hi; ++w) {
+    uint32_t fin = s_sel[w];
+    while (fin) {
+      const int b = __ffs(fin) - 1;
+      fin &= fin - 1;
+      if (out_before < (uint32_t)P) out[out_before] = w * 32 + b;
+      ++out_before;
+    }
+  }
+  if (tid == 0) a.pool_count[q] = P;
+}
+
+}  // namespace
+
+hipError_t launch_pool_select(const PoolArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(k_pool_select, dim3(a.n_q), dim3(kSelThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace csa2

@@ -1,0 +1,215 @@
+/*
+ * csa2.h -- C ABI of the CSA2 decode-path library for AMD Instinct MI355X
+ * (gfx950): FP4 main-KV encode, Full-mode hierarchical indexer, Reindex, and
+ * joint sparse + sliding-window attention.
+ *
+ * Sources (web pages about DeepSeek-V4.1-Flash):
+ *   [atlas]     "DeepSeek-V4.1-Flash 梗概" (deepseek-mechanism-atlas), §3.2
+ *               Compressed Sparse Attention 2: the Full / Reindex / Reuse mode
+ *               table, the heterogeneous-KV figure, the hierarchical sparse
+ *               indexer paragraph and the FP4 main-KV paragraph.
+ *   [newsaint]  "DeepSeek-V4.1-Flash 2026: Arsitektur Causal Encoder-Decoder
+ *               (CED), Compressed Sparse Attention 2 (CSA2), FP4 KV Caching,
+ *               dan SWA Bounded Replay untuk 1M Context Window", §3 (indexer),
+ *               §4 (FP4 main KV), §8 (FP4Quantizer, HierarchicalSparseIndexer).
+ *   [stamatios] "DeepSeek-V4.1 Flash comprime cache KV para 890 bytes por
+ *               token", "CSA2: compressão em três dimensões" (512-wide latent
+ *               shared across heads; Full / Reindex / Reuse).
+ *
+ * Conventions for every call
+ *   - Every array pointer is DEVICE memory owned by the caller.  The library
+ *     never allocates or frees device memory; scratch comes from a caller
+ *     workspace whose size the matching *_workspace_size call returns.
+ *   - Calls validate their host-side arguments synchronously, then enqueue
+ *     kernels on `stream` (a hipStream_t; NULL is the null stream) and return
+ *     without waiting.  Outputs are ready when the stream reaches that point.
+ *   - Per-query device data (seq_base, n_visible, swa_base, pool and top-k
+ *     lists) are preconditions: they are not checked on the device.  Rows a
+ *     query reads must exist in the caller's buffers.
+ *   - bf16 arrays are passed as uint16_t bit patterns; fp8 arrays as uint8_t
+ *     OCP E4M3FN bytes (maximum 448, the MI355X FP8 format).
+ *   - Non-finite inputs give undefined (but memory-safe) results.
+ *   - Calls on different streams may run concurrently if their workspaces
+ *     and outputs do not overlap.  The library keeps no mutable state except
+ *     a per-device architecture check done once.
+ *   - On error the call enqueues nothing and returns a status;
+ *     csa2_last_error() gives a message for the calling thread.
+ */
+#ifndef CSA2_H
+#define CSA2_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CSA2_ABI_VERSION 1
+
+typedef enum csa2_status {
+  CSA2_OK = 0,
+  CSA2_ERR_INVALID_ARG = 1,  /* null required pointer, bad size or dimension */
+  CSA2_ERR_UNSUPPORTED = 2,  /* current device is not gfx950 */
+  CSA2_ERR_WORKSPACE = 3,    /* workspace missing, too small or misaligned */
+  CSA2_ERR_HIP = 4           /* a HIP runtime call or kernel launch failed */
+} csa2_status;
+
+/* Problem dimensions.  Supported values:
+ *   n_heads      H    main attention heads, a multiple of 16, 16..128
+ *   d_latent          512 (the latent shared across heads; [stamatios])
+ *   d_rope            64  (the bf16 RoPE key part)
+ *   idx_heads    H_i  indexer heads, 1..64
+ *   idx_dim      d_i  indexer key / query width, 64 or 128
+ *   block             8   (indexer block size; [atlas] §3.2)
+ *   pool_blocks  P    blocks kept by the Full indexer, 1..2048
+ *                     ([atlas] §3.2: Top-2048 blocks, about 16,384 positions)
+ *   topk         K    positions kept by Reindex, 1..min(8*P, 2048)
+ *                     ([atlas] §3.2: Top-512 inside the pool)
+ *   swa          W    sliding-window rows, 0..1024 */
+typedef struct csa2_dims {
+  int32_t n_heads;
+  int32_t d_latent;
+  int32_t d_rope;
+  int32_t idx_heads;
+  int32_t idx_dim;
+  int32_t block;
+  int32_t pool_blocks;
+  int32_t topk;
+  int32_t swa;
+} csa2_dims;
+
+/* A batch of decode queries.
+ *   n_q             number of queries (>= 1).
+ *   tokens_per_seq  g in 1..4: queries g*i .. g*i+g-1 belong to one
+ *                   sequence (consecutive causal query tokens, e.g. a
+ *                   speculative-verify step) and MUST share seq_base; the
+ *                   Full scan then reads that sequence's keys once for all g.
+ *                   n_q must be a multiple of g.
+ *   max_visible     host-side upper bound of every n_visible[i], at most
+ *                   2^21; used only to size launch grids.
+ *   seq_base        device int64 [n_q]: cache row of position 0 of the
+ *                   query's sequence.  Position p lives at row seq_base + p
+ *                   in idx_k, kv_codes, kv_scales and kv_rope.
+ *   n_visible       device int32 [n_q]: the query sees positions [0, n).
+ * A query's sparse candidates are positions [0, c), c = max(0, n - W); the
+ * window is [c, n) ([atlas] §3.2 heterogeneous KV: the indexer and Top-K
+ * serve only the sparse branch). */
+typedef struct csa2_queries {
+  int32_t n_q;
+  int32_t tokens_per_seq;
+  int32_t max_visible;
+  int32_t reserved;          /* must be 0 */
+  const int64_t* seq_base;
+  const int32_t* n_visible;
+} csa2_queries;
+
+/* ABI version of the loaded library (CSA2_ABI_VERSION). */
+int32_t csa2_abi_version(void);
+
+/* Static text for a status code. */
+const char* csa2_status_string(csa2_status status);
+
+/* Message describing the last error returned on the calling thread. */
+const char* csa2_last_error(void);
+
+/* FP4 main-KV encode ([atlas] §3.2 FP4 main KV; [newsaint] §4 and §8
+ * FP4Quantizer).  For each of n entries and each group of 16 latent channels:
+ *   amax = max |x|,  S = E4M3(round-to-nearest-even(min(amax / 6, 448))),
+ *   s = value of S;  code_i = sign(x_i) << 3 | E2M1(|x_i| / s), the nearest
+ *   E2M1 level with ties to the even code, saturating at 6;  s == 0 gives
+ *   all codes 0.  Byte 8g+k of an entry's codes holds channel 16g+2k in the
+ *   low nibble and 16g+2k+1 in the high nibble; scale byte g holds S.
+ * The RoPE part is copied unchanged.
+ *   latent   bf16 [n, 512]        rope      bf16 [n, 64]
+ *   dst_row  int64 [n] destination rows, or NULL for rows 0..n-1
+ *   kv_codes uint8 [rows, 256]    kv_scales uint8 [rows, 32]
+ *   kv_rope  bf16 [rows, 64]
+ * n == 0 is a no-op.  Errors: CSA2_ERR_INVALID_ARG for n < 0 or a null
+ * pointer (dst_row excepted). */
+csa2_status csa2_encode_kv(int64_t n, const uint16_t* latent, const uint16_t* rope,
+                           const int64_t* dst_row, uint8_t* kv_codes, uint8_t* kv_scales,
+                           uint16_t* kv_rope, void* stream);
+
+/* Workspace bytes for csa2_index_full (256-byte aligned start required). */
+csa2_status csa2_index_full_workspace_size(const csa2_dims* dims, const csa2_queries* q,
+                                           size_t* bytes);
+
+/* Full-mode hierarchical indexer ([atlas] §3.2 hierarchical sparse indexer
+ * and mode table; [newsaint] §3).  For every query:
+ *   s_p = sum_h w_h * max(0, q_h . k_p)  for p in [0, c)   (fp8 x fp8, fp32)
+ *   b_j = max of s_p over p in [8j, min(8j+8, c)),  j < nb = ceil(c / 8)
+ *   pool = the min(P, nb) blocks with the largest b_j, ties to the lower j,
+ *          written in ascending block order.
+ *   idx_q       fp8 [n_q, H_i, d_i]      idx_w  float [n_q, H_i]
+ *   idx_k       fp8 [rows, d_i]  (one key per position, shared by heads)
+ *   pool_blocks int32 [n_q, P]  ascending block ids, -1 after pool_count
+ *   pool_count  int32 [n_q]
+ *   block_scores  optional float [n_q, ld_block_scores] (NULL to skip):
+ *               b_j for j < nb; entries at j >= nb are left untouched;
+ *               ld_block_scores >= ceil((max_visible - W) / 8).
+ *   ws, ws_bytes  workspace of csa2_index_full_workspace_size bytes.
+ * Queries with n <= W get pool_count = 0. */
+csa2_status csa2_index_full(const csa2_dims* dims, const csa2_queries* q,
+                            const uint8_t* idx_q, const float* idx_w, const uint8_t* idx_k,
+                            int32_t* pool_blocks, int32_t* pool_count,
+                            float* block_scores, int64_t ld_block_scores,
+                            void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace bytes for csa2_index_reindex. */
+csa2_status csa2_index_reindex_workspace_size(const csa2_dims* dims, const csa2_queries* q,
+                                              size_t* bytes);
+
+/* Reindex inside the pool ([atlas] §3.2: Reindex re-scores with this
+ * layer's indexer query over the pool only and keeps the Top-K; [newsaint]
+ * §3 constant-size search domain; §8 gathers only the pool's keys).
+ * Candidates R = union over pool blocks j of [8j, min(8j+8, c)); scores as
+ * in csa2_index_full with this call's (idx_q, idx_w); keeps the
+ * min(K, |R|) best by (score desc, position asc), ascending positions.
+ *   pool_blocks, pool_count  as produced by csa2_index_full (ascending)
+ *   topk_pos    int32 [n_q, K]  ascending positions, -1 after topk_count
+ *   topk_count  int32 [n_q]
+ *   topk_scores optional float [n_q, K] (NULL to skip): the score of each
+ *               kept position, same order as topk_pos. */
+csa2_status csa2_index_reindex(const csa2_dims* dims, const csa2_queries* q,
+                               const uint8_t* idx_q, const float* idx_w, const uint8_t* idx_k,
+                               const int32_t* pool_blocks, const int32_t* pool_count,
+                               int32_t* topk_pos, int32_t* topk_count, float* topk_scores,
+                               void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace bytes for csa2_attend. */
+csa2_status csa2_attend_workspace_size(const csa2_dims* dims, const csa2_queries* q,
+                                       size_t* bytes);
+
+/* Core attention, MLA-absorbed, over the kept FP4 entries and the window
+ * ([atlas] §3.2 heterogeneous KV: one main Q attends the sparse main-KV
+ * branch and the uncompressed window branch, merged; mode table: Reuse
+ * layers call this with a new Q and the inherited index set; [newsaint] §4:
+ * FP4 is dequantised just before attention).  Entries of a query:
+ *   sparse  j in topk_pos[0 .. topk_count): key = [deq(codes, scales) (512)
+ *           || kv_rope (64)], value = deq latent (512);
+ *   window  positions [c, n) read from swa_kv rows swa_base .. swa_base+n-c-1:
+ *           key = the row's 576 bf16 values, value = its first 512.
+ *   l_j = softmax_scale * (q_lat . key[:512] + q_rope . key[512:]);
+ *   out_h = sum_j softmax(l)_j value_j  (one softmax over all entries),
+ *   lse_h = log sum_j exp(l_j).  A query with no entries gets out = 0 and
+ *   lse = -inf.
+ *   q_lat  bf16 [n_q, H, 512]     q_rope bf16 [n_q, H, 64]
+ *   kv_codes, kv_scales, kv_rope  as written by csa2_encode_kv
+ *   topk_pos, topk_count          as produced by csa2_index_reindex
+ *   swa_kv bf16 [swa_rows, 576]   swa_base int64 [n_q] (device)
+ *   out    float [n_q, H, 512]    lse float [n_q, H] or NULL
+ * Window values are converted to fp16 for the value product: |v| must stay
+ * below 65504. */
+csa2_status csa2_attend(const csa2_dims* dims, const csa2_queries* q,
+                        const uint16_t* q_lat, const uint16_t* q_rope, float softmax_scale,
+                        const uint8_t* kv_codes, const uint8_t* kv_scales, const uint16_t* kv_rope,
+                        const int32_t* topk_pos, const int32_t* topk_count,
+                        const uint16_t* swa_kv, const int64_t* swa_base,
+                        float* out, float* lse, void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CSA2_H */

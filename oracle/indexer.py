@@ -79,6 +79,8 @@ def reindex(q_codes, w, k_codes_all, pool, c: int, K: int):
 
     k_codes_all: the query's key rows indexed by position (at least c rows).
     Returns (ascending positions int64, scores of all pool positions, R)."""
+    if len(k_codes_all) < c:
+        raise ValueError("key rows must cover every candidate position")
     R = pool_positions(pool, c)
     s = index_scores(q_codes, w, np.asarray(k_codes_all)[R]) if len(R) else np.zeros(0)
     keep = np.sort(R[rank_order(s)[: min(K, len(R))]])
@@ -89,6 +91,8 @@ def index_full(q_codes, w, k_codes_all, n: int, W: int, P: int):
     """Full mode: scores over every candidate, block maxima, Top-P blocks.
     Returns (pool ascending int64, block scores float64, position scores)."""
     c = candidates(n, W)
+    if len(k_codes_all) < c:
+        raise ValueError("key rows must cover every candidate position")
     s = index_scores(q_codes, w, np.asarray(k_codes_all)[:c]) if c else np.zeros(0)
     b = block_scores(s)
     return select_pool(b, P), b, s

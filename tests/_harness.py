@@ -1,0 +1,195 @@
+"""Shared set-up for the GPU parity tests and the benchmark's checks.
+
+GPU side: caches and queries generated on the device by `workloads` and run
+through the HIP library.  Oracle side: the same seeded inputs regenerated on
+the CPU for one sampled query at a time and run through `oracle`.  Nothing
+produced by the HIP library is ever handed to the oracle; oracle outputs may be
+fed to the library (e.g. an oracle pool into Reindex) to test one stage alone.
+"""
+from __future__ import annotations
+
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import workloads as wl  # noqa: E402
+import oracle  # noqa: E402
+
+SEL_BAND = 1e-5      # index sets may differ only within this relative score gap
+SCORE_TOL = 1e-3     # indexer scores
+ATTN_TOL = 2e-3      # attention: max|d| / max|ref| per (query, head) row
+
+
+def have_gpu() -> bool:
+    return torch.cuda.is_available()
+
+
+def lib():
+    """The HIP binding; on a GPU machine a missing library is an error, not a skip."""
+    if not have_gpu():
+        pytest.skip("no GPU")
+    import compressed_sparse_attention_decode_amd as csa2
+    csa2.lib()
+    return csa2
+
+
+def u8(t: torch.Tensor) -> np.ndarray:
+    return t.detach().cpu().contiguous().view(torch.uint8).numpy()
+
+
+def u16(t: torch.Tensor) -> np.ndarray:
+    return t.detach().cpu().contiguous().view(torch.int16).numpy().astype(np.uint16)
+
+
+class GpuCase:
+    """Caches, window rows and query batch of a workload on the GPU."""
+
+    def __init__(self, w: wl.Workload, device="cuda", chunk_rows: int = 1 << 18, encode: bool = True):
+        csa2 = lib()
+        self.csa2 = csa2
+        self.w, self.dev = w, device
+        self.lay = lay = wl.layout(w)
+        d = w.dims
+        self.dims = csa2.Dims(n_heads=d.n_heads, idx_heads=d.idx_heads, idx_dim=d.idx_dim,
+                              pool_blocks=d.pool_blocks, topk=d.topk, swa=d.swa)
+        rows = max(lay.rows, 1)
+        self.idx_k = torch.empty(rows, d.idx_dim, dtype=torch.float8_e4m3fn, device=device)
+        self.codes = torch.empty(rows, 256, dtype=torch.uint8, device=device)
+        self.scales = torch.empty(rows, 32, dtype=torch.uint8, device=device)
+        self.kv_rope = torch.empty(rows, 64, dtype=torch.bfloat16, device=device)
+        for r0 in range(0, lay.rows, chunk_rows):
+            n = min(chunk_rows, lay.rows - r0)
+            self.idx_k[r0:r0 + n] = wl.idx_keys(w, r0, n, device)
+            if encode:
+                csa2.encode_kv(wl.latent(w, r0, n, device), wl.rope(w, r0, n, device),
+                               self.codes[r0:r0 + n], self.scales[r0:r0 + n], self.kv_rope[r0:r0 + n])
+        parts = [wl.swa_rows(w, lay, s, device) for s in range(len(lay.ctx))]
+        self.swa_kv = torch.cat(parts) if parts else torch.zeros(1, 576, dtype=torch.bfloat16, device=device)
+        if self.swa_kv.shape[0] == 0:
+            self.swa_kv = torch.zeros(1, 576, dtype=torch.bfloat16, device=device)
+        self.batch = csa2.Batch(
+            seq_base=torch.tensor(lay.q_seq_base, dtype=torch.int64, device=device),
+            n_visible=torch.tensor(lay.q_visible, dtype=torch.int32, device=device),
+            max_visible=max(lay.q_visible) if lay.q_visible else 0,
+            tokens_per_seq=w.tokens_per_seq)
+        self.swa_base = torch.tensor(lay.q_swa_base, dtype=torch.int64, device=device)
+        torch.cuda.synchronize()
+
+    def iq(self, layer: int):
+        n = self.w.n_q
+        return (wl.idx_query(self.w, layer, 0, n, self.dev), wl.idx_weight(self.w, layer, 0, n, self.dev))
+
+    def mq(self, layer: int):
+        n = self.w.n_q
+        return wl.q_latent(self.w, layer, 0, n, self.dev), wl.q_rope(self.w, layer, 0, n, self.dev)
+
+    def full(self, layer=0, block_scores=False):
+        q, w = self.iq(layer)
+        bs = None
+        if block_scores:
+            nb = max(1, -(-(self.batch.max_visible - self.w.dims.swa) // 8))
+            bs = torch.full((self.w.n_q, nb), float("nan"), dtype=torch.float32, device=self.dev)
+        pool, cnt = self.csa2.index_full(self.dims, self.batch, q, w, self.idx_k, block_scores=bs)
+        return pool, cnt, bs
+
+    def reindex(self, layer, pool, cnt, scores=False):
+        q, w = self.iq(layer)
+        ts = torch.empty(self.w.n_q, self.w.dims.topk, dtype=torch.float32, device=self.dev) if scores else None
+        tk, tc = self.csa2.index_reindex(self.dims, self.batch, q, w, self.idx_k, pool, cnt, topk_scores=ts)
+        return tk, tc, ts
+
+    def attend(self, layer, tk, tc):
+        ql, qr = self.mq(layer)
+        return self.csa2.attend(self.dims, self.batch, ql, qr, 1.0, self.codes, self.scales, self.kv_rope,
+                                tk, tc, self.swa_kv, self.swa_base)
+
+
+class OracleQuery:
+    """The oracle's view of one query of a workload (all inputs regenerated on
+    the CPU from the seeded generator)."""
+
+    def __init__(self, w: wl.Workload, lay: wl.Layout, qi: int, keys=None):
+        self.w, self.lay, self.qi = w, lay, qi
+        d = w.dims
+        self.n = lay.q_visible[qi]
+        self.base = lay.q_seq_base[qi]
+        self.c = oracle.candidates(self.n, d.swa)
+        seq = qi // w.tokens_per_seq
+        if keys is None:
+            keys = u8(wl.idx_keys(w, self.base, max(lay.seq_rows[seq], 1)))
+        assert len(keys) >= self.c
+        self.keys = keys
+
+    def iq(self, layer):
+        return (u8(wl.idx_query(self.w, layer, self.qi, 1)[0]),
+                wl.idx_weight(self.w, layer, self.qi, 1)[0].numpy())
+
+    def full(self, layer=0):
+        q, wt = self.iq(layer)
+        return oracle.index_full(q, wt, self.keys, self.n, self.w.dims.swa, self.w.dims.pool_blocks)
+
+    def reindex(self, layer, pool):
+        q, wt = self.iq(layer)
+        return oracle.reindex(q, wt, self.keys, pool, self.c, self.w.dims.topk)
+
+    def scores_at(self, layer, pos):
+        q, wt = self.iq(layer)
+        pos = np.asarray(pos, dtype=np.int64)
+        return oracle.index_scores(q, wt, self.keys[pos]) if len(pos) else np.zeros(0)
+
+    def attention(self, layer, keep, scale=1.0):
+        w = self.w
+        rows = self.base + np.asarray(keep, dtype=np.int64)
+        lat = u16(wl.latent_at(w, rows)) if len(rows) else np.zeros((0, 512), np.uint16)
+        rp = u16(wl.rope_at(w, rows)) if len(rows) else np.zeros((0, 64), np.uint16)
+        codes, scales = oracle.encode_kv(lat) if len(rows) else (np.zeros((0, 256), np.uint8), np.zeros((0, 32), np.uint8))
+        win = self.base + np.arange(self.c, self.n, dtype=np.int64)
+        swa = np.concatenate([u16(wl.latent_at(w, win)), u16(wl.rope_at(w, win))], axis=1) \
+            if len(win) else np.zeros((0, 576), np.uint16)
+        keys = oracle.gather_entries(codes, scales, rp, swa)
+        ql = u16(wl.q_latent(w, layer, self.qi, 1)[0])
+        qr = u16(wl.q_rope(w, layer, self.qi, 1)[0])
+        return oracle.attend(ql, qr, scale, keys)
+
+
+def check_set(got, ref, scores_of, label=""):
+    """Index sets: equal size; each element of the symmetric difference has an
+    oracle score within SEL_BAND (relative) of the oracle's k-th score.
+    `scores_of(idx_array)` returns oracle scores; ref is ordered by rank
+    through `kth`."""
+    got = np.asarray(got, dtype=np.int64)
+    ref = np.asarray(ref, dtype=np.int64)
+    assert len(got) == len(ref), f"{label}: size {len(got)} != {len(ref)}"
+    assert np.all(np.diff(got) > 0), f"{label}: output not strictly ascending"
+    diff = np.setxor1d(got, ref)
+    if len(diff) == 0:
+        return 0
+    ref_scores = scores_of(ref)
+    kth = ref_scores.min()
+    d_scores = scores_of(diff)
+    gap = np.abs(d_scores - kth)
+    bad = gap > SEL_BAND * max(abs(kth), 1e-30)
+    assert not bad.any(), (f"{label}: {bad.sum()} of {len(diff)} differing indices outside the tie band; "
+                           f"k-th score {kth!r}, worst {d_scores[bad][:5]!r}")
+    return len(diff)
+
+
+def check_attention(out, lse, ref_out, ref_lse, label=""):
+    out = np.asarray(out, dtype=np.float64)
+    err = np.abs(out - ref_out).max(axis=-1)
+    den = np.abs(ref_out).max(axis=-1)
+    rel = err / np.maximum(den, 1e-30)
+    assert np.all(rel <= ATTN_TOL), f"{label}: attention rel err {rel.max():.3e} > {ATTN_TOL}"
+    if lse is not None:
+        lse = np.asarray(lse, dtype=np.float64)
+        fin = np.isfinite(ref_lse)
+        assert np.array_equal(np.isfinite(lse), fin), f"{label}: lse finiteness differs"
+        assert np.allclose(lse[fin], ref_lse[fin], rtol=1e-4, atol=1e-4), f"{label}: lse mismatch"
+    return float(rel.max()) if rel.size else 0.0

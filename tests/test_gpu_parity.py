@@ -1,0 +1,249 @@
+"""GPU parity: the HIP library against the oracle on the same seeded inputs.
+
+Bars: FP4 bytes bit-exact; index sets equal except within a 1e-5 relative
+score band around the k-th score (ties to the lower index); indexer scores
+within 1e-3 relative; attention within 2e-3 of max|ref| per (query, head).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as wl
+from tests._harness import (GpuCase, OracleQuery, check_attention, check_set, lib, u8, u16,
+                            SCORE_TOL)
+
+pytestmark = pytest.mark.gpu
+
+BIG = wl.Dims(n_heads=64, idx_heads=64, idx_dim=128, pool_blocks=256, topk=512)
+
+
+def small(idx, dims, ctx_list, g=1, name="small"):
+    ns = len(ctx_list)
+    return wl.Workload(idx, name, dims, n_seq=ns, ctx=(0, 0), tokens_per_seq=g, ctx_list=tuple(ctx_list))
+
+
+# several scan tiles (2048 positions) with ragged tails, several queries
+CASES = {
+    "tiny_c0": wl.workload(0),
+    "ragged_b3": small(101, BIG, [20005, 9000 + 3, 4099]),
+    "ragged_g4": small(102, BIG, [6001, 12345], g=4),
+    "d64_h8": small(103, wl.Dims(n_heads=16, idx_heads=8, idx_dim=64, pool_blocks=64, topk=128), [7777, 300]),
+    "h_odd": small(104, wl.Dims(n_heads=32, idx_heads=40, idx_dim=128, pool_blocks=100, topk=300, swa=64), [5000, 2001]),
+    "edge_short": small(105, wl.Dims(n_heads=16, idx_heads=16, idx_dim=128, pool_blocks=4, topk=16),
+                        [0, 1, 100, 128, 129, 136, 137, 160]),
+    "w0_h128": small(106, wl.Dims(n_heads=128, idx_heads=1, idx_dim=128, pool_blocks=32, topk=64, swa=0), [3000]),
+    "max_pk": small(107, wl.Dims(n_heads=64, idx_heads=64, idx_dim=128, pool_blocks=2048, topk=2048, swa=1024),
+                    [40000, 17000]),
+}
+
+
+@pytest.fixture(scope="module", params=list(CASES))
+def case(request):
+    w = CASES[request.param]
+    return request.param, GpuCase(w), wl.layout(w)
+
+
+def _oq(w, lay, keys_cache, qi):
+    s = lay.q_seq_base[qi]
+    oq = OracleQuery(w, lay, qi, keys_cache.get(s))
+    keys_cache.setdefault(s, oq.keys)
+    return oq
+
+
+def test_encode_bit_exact_generated():
+    csa2 = lib()
+    w = wl.workload(4)
+    n = 4096 + 37
+    lat, rp = wl.fresh_latent(w, 0, 0, n, "cuda"), wl.fresh_rope(w, 0, 0, n, "cuda")
+    rows = 3 * n
+    perm = torch.randperm(rows, generator=torch.Generator().manual_seed(5))[:n].to("cuda")
+    codes = torch.zeros(rows, 256, dtype=torch.uint8, device="cuda")
+    scales = torch.zeros(rows, 32, dtype=torch.uint8, device="cuda")
+    kr = torch.zeros(rows, 64, dtype=torch.bfloat16, device="cuda")
+    csa2.encode_kv(lat, rp, codes, scales, kr, dst_row=perm)
+    torch.cuda.synchronize()
+    rc, rs = oracle.encode_kv(u16(wl.fresh_latent(w, 0, 0, n)))
+    p = perm.cpu().numpy()
+    assert np.array_equal(u8(codes)[p], rc)
+    assert np.array_equal(u8(scales)[p], rs)
+    assert np.array_equal(u16(kr)[p], u16(wl.fresh_rope(w, 0, 0, n)))
+    untouched = np.setdiff1d(np.arange(rows), p)
+    assert not u8(codes)[untouched].any()
+
+
+def _exhaustive_groups():
+    """Groups [6s, x1..x15] for every positive finite E4M3 scale s and every
+    finite bf16 x with |x| <= 6s, plus degenerate groups."""
+    b = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    v = oracle.bf16_to_f64(b)
+    fin = np.isfinite(v)
+    b, v = b[fin], v[fin]
+    groups = []
+    for sc in range(1, 0x7F):
+        s = float(oracle.e4m3_decode(sc))
+        xb = b[np.abs(v) <= 6 * s]
+        ng = -(-len(xb) // 15)
+        flat = np.zeros(ng * 15, np.uint16)
+        flat[:len(xb)] = xb
+        g = np.zeros((ng, 16), np.uint16)
+        g[:, 0] = (np.array([6 * s], np.float32).view(np.uint32) >> 16).astype(np.uint16)
+        g[:, 1:] = flat.reshape(ng, 15)
+        groups.append(g)
+    def bf(x):
+        return (np.array(x, np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    deg = np.zeros((6, 16), np.uint16)
+    deg[1, :2] = bf([-1e-6, 1e-6])                       # scale rounds to 0
+    deg[2, :2] = bf([-1.0, -0.01])                       # -0 code for small negatives
+    deg[3, :2] = bf([1e4, -3000.0])                      # scale clamps at 448, saturates
+    deg[4, :3] = bf([6.375, 1.0625, -0.03125])           # scale tie 1.0625 -> 1.0
+    deg[5, :] = bf(np.linspace(-2688, 2688, 16))
+    groups.append(deg)
+    allg = np.concatenate(groups)
+    rows = -(-len(allg) // 32)
+    out = np.zeros((rows * 32, 16), np.uint16)
+    out[:len(allg)] = allg
+    return out.reshape(rows, 512)
+
+
+def test_encode_exhaustive_scales_and_values():
+    csa2 = lib()
+    lat = _exhaustive_groups()
+    n = lat.shape[0]
+    rc, rs = oracle.encode_kv(lat)
+    t = torch.from_numpy(lat.astype(np.int16)).view(torch.bfloat16).to("cuda")
+    rp = torch.zeros(n, 64, dtype=torch.bfloat16, device="cuda")
+    codes = torch.empty(n, 256, dtype=torch.uint8, device="cuda")
+    scales = torch.empty(n, 32, dtype=torch.uint8, device="cuda")
+    kr = torch.empty(n, 64, dtype=torch.bfloat16, device="cuda")
+    csa2.encode_kv(t, rp, codes, scales, kr)
+    torch.cuda.synchronize()
+    assert np.array_equal(u8(scales), rs)
+    bad = np.argwhere(u8(codes) != rc)
+    assert len(bad) == 0, f"{len(bad)} code bytes differ, first rows {bad[:5]}"
+
+
+def test_full_index(case):
+    name, g, lay = case
+    w = g.w
+    pool, cnt, bs = g.full(0, block_scores=True)
+    torch.cuda.synchronize()
+    pool, cnt, bs = pool.cpu().numpy(), cnt.cpu().numpy(), bs.cpu().numpy()
+    kc = {}
+    for qi in range(w.n_q):
+        oq = _oq(w, lay, kc, qi)
+        rpool, rb, _ = oq.full(0)
+        nb = len(rb)
+        assert cnt[qi] == len(rpool), f"{name} q{qi}: pool count {cnt[qi]} != {len(rpool)}"
+        assert np.all(pool[qi, cnt[qi]:] == -1)
+        if nb:
+            got_b = bs[qi, :nb].astype(np.float64)
+            tol = SCORE_TOL * np.maximum(np.abs(rb), 1e-3 * np.abs(rb).max())
+            assert np.all(np.abs(got_b - rb) <= tol), f"{name} q{qi}: block scores off by {np.abs(got_b - rb).max()}"
+        check_set(pool[qi, :cnt[qi]], rpool, lambda j: rb[j], f"{name} q{qi} pool")
+
+
+def test_reindex_on_oracle_pool(case):
+    name, g, lay = case
+    w = g.w
+    kc = {}
+    P = w.dims.pool_blocks
+    pools = np.full((w.n_q, P), -1, np.int32)
+    cnts = np.zeros(w.n_q, np.int32)
+    oqs = []
+    for qi in range(w.n_q):
+        oq = _oq(w, lay, kc, qi)
+        rpool, _, _ = oq.full(0)
+        pools[qi, :len(rpool)] = rpool
+        cnts[qi] = len(rpool)
+        oqs.append((oq, rpool))
+    layer = 1 if w.reindex_layers > 1 else 0
+    tk, tc, ts = g.reindex(layer, torch.from_numpy(pools).cuda(), torch.from_numpy(cnts).cuda(), scores=True)
+    torch.cuda.synchronize()
+    tk, tc, ts = tk.cpu().numpy(), tc.cpu().numpy(), ts.cpu().numpy()
+    for qi, (oq, rpool) in enumerate(oqs):
+        keep, s, R = oq.reindex(layer, rpool)
+        assert tc[qi] == len(keep), f"{name} q{qi}: topk count {tc[qi]} != {len(keep)}"
+        got = tk[qi, :tc[qi]]
+        assert np.all(tk[qi, tc[qi]:] == -1)
+        assert set(got.tolist()) <= set(R.tolist()), f"{name} q{qi}: selection outside the pool"
+        check_set(got, keep, lambda p: oq.scores_at(layer, p), f"{name} q{qi} topk")
+        if tc[qi]:
+            ref = oq.scores_at(layer, got)
+            assert np.allclose(ts[qi, :tc[qi]], ref, rtol=SCORE_TOL, atol=1e-6 * np.abs(ref).max())
+
+
+def test_attention_on_oracle_topk(case):
+    name, g, lay = case
+    w = g.w
+    K = w.dims.topk
+    kc = {}
+    tks = np.full((w.n_q, K), -1, np.int32)
+    tcs = np.zeros(w.n_q, np.int32)
+    refs = []
+    layer = 1 if w.reindex_layers > 1 else 0
+    for qi in range(w.n_q):
+        oq = _oq(w, lay, kc, qi)
+        rpool, _, _ = oq.full(0)
+        keep, _, _ = oq.reindex(layer, rpool)
+        tks[qi, :len(keep)] = keep
+        tcs[qi] = len(keep)
+        refs.append(oq.attention(layer, keep))
+    out, lse = g.attend(layer, torch.from_numpy(tks).cuda(), torch.from_numpy(tcs).cuda())
+    torch.cuda.synchronize()
+    out, lse = out.cpu().numpy(), lse.cpu().numpy()
+    for qi in range(w.n_q):
+        check_attention(out[qi], lse[qi], refs[qi][0], refs[qi][1], f"{name} q{qi}")
+
+
+def test_pipeline_end_to_end_and_deterministic(case):
+    name, g, lay = case
+    w = g.w
+    runs = []
+    for _ in range(2):
+        pool, cnt, _ = g.full(0)
+        layer = 1 if w.reindex_layers > 1 else 0
+        tk, tc, _ = g.reindex(layer, pool, cnt)
+        out, lse = g.attend(layer, tk, tc)
+        torch.cuda.synchronize()
+        runs.append([t.cpu().clone() for t in (pool, cnt, tk, tc, out, lse)])
+    for a, b in zip(*runs):
+        assert torch.equal(a.view(torch.uint8) if a.dtype == torch.float32 else a,
+                           b.view(torch.uint8) if b.dtype == torch.float32 else b), f"{name}: run-to-run difference"
+    pool, cnt, tk, tc, out, lse = [t.numpy() for t in runs[0]]
+    kc = {}
+    for qi in range(w.n_q):
+        oq = _oq(w, lay, kc, qi)
+        rpool, rb, _ = oq.full(0)
+        check_set(pool[qi, :cnt[qi]], rpool, lambda j: rb[j], f"{name} q{qi} pool")
+        if not np.array_equal(pool[qi, :cnt[qi]], rpool):
+            continue
+        keep, _, _ = oq.reindex(layer, rpool)
+        check_set(tk[qi, :tc[qi]], keep, lambda p: oq.scores_at(layer, p), f"{name} q{qi} topk")
+        if np.array_equal(tk[qi, :tc[qi]], keep):
+            ro, rl = oq.attention(layer, keep)
+            check_attention(out[qi], lse[qi], ro, rl, f"{name} q{qi}")
+
+
+def test_ties_lower_position_wins():
+    """Duplicated keys give equal scores: the lower positions must be kept."""
+    csa2 = lib()
+    dims = wl.Dims(n_heads=16, idx_heads=16, idx_dim=128, pool_blocks=4, topk=20)
+    w = small(110, dims, [3000])
+    g = GpuCase(w)
+    lay = wl.layout(w)
+    oq = OracleQuery(w, lay, 0)
+    # copy the best block's keys over several other blocks (all < c)
+    pool0, b0, s0 = oq.full(0)
+    best = int(np.argmax(b0))
+    src = oq.keys[best * 8:(best + 1) * 8].copy()
+    for j in [3, 40, 41, 200, 301]:
+        oq.keys[j * 8:(j + 1) * 8] = src
+        g.idx_k[j * 8:(j + 1) * 8] = torch.from_numpy(src).view(torch.float8_e4m3fn).cuda()
+    rpool, rb, _ = oq.full(0)
+    pool, cnt, _ = g.full(0)
+    tk, tc, _ = g.reindex(0, pool, cnt)
+    torch.cuda.synchronize()
+    assert np.array_equal(pool.cpu().numpy()[0, :cnt.item()], rpool)
+    keep, _, _ = oq.reindex(0, rpool)
+    assert np.array_equal(tk.cpu().numpy()[0, :tc.item()], keep)

@@ -36,6 +36,7 @@ __all__ = [
     "Dims", "Workload", "WORKLOADS", "workload", "Layout", "layout",
     "idx_keys", "latent", "rope", "idx_query", "idx_weight", "q_latent",
     "q_rope", "fresh_latent", "fresh_rope", "swa_rows", "mix64_reference",
+    "latent_at", "rope_at",
 ]
 
 _MASK64 = (1 << 64) - 1
@@ -109,6 +110,12 @@ def _normal(kind: str, seed: int, start: int, count: int, device) -> torch.Tenso
     return _table(kind, device)[idx]
 
 
+def _normal_at(kind: str, seed: int, idx: torch.Tensor) -> torch.Tensor:
+    """Values at arbitrary flat element indices (int64 tensor)."""
+    z = _mix64((idx + 1) * _s64(_GAMMA) + _s64(seed))
+    return _table(kind, idx.device)[_srl(z, 64 - _TABLE_BITS)]
+
+
 def _uniform01(seed: int, start: int, count: int, device) -> torch.Tensor:
     v = _srl(_bits(seed, start, count, device), 40)
     return v.to(torch.float32) * (1.0 / (1 << 24))
@@ -144,6 +151,7 @@ class Workload:
     reindex_layers: int = 1       # Reindex+Attend layers after the Full scan
     fresh_q_per_layer: bool = False  # True: every Reindex layer draws new Q
     fresh_encode: int = 0         # entries encoded by each step
+    ctx_list: Optional[Tuple[int, ...]] = None   # explicit contexts (tests)
 
     @property
     def key(self) -> int:
@@ -203,7 +211,9 @@ def layout(w: Workload, n_seq: Optional[int] = None) -> Layout:
     """Row layout; `n_seq` keeps only the first sequences (same values)."""
     ns = w.n_seq if n_seq is None else n_seq
     lo, hi = w.ctx
-    if lo == hi:
+    if w.ctx_list is not None:
+        ctx = list(w.ctx_list)
+    elif lo == hi:
         ctx = [lo] * w.n_seq
     else:
         ctx = _uniform_int(_stream_seed(w.key, "ctx"), lo, hi, w.n_seq)
@@ -250,6 +260,20 @@ def rope(w: Workload, row0: int, nrows: int, device="cpu") -> torch.Tensor:
     d = w.dims.d_rope
     s = _stream_seed(w.key, "rope")
     return _normal("bf16", s, row0 * d, nrows * d, device).view(nrows, d)
+
+
+def _rows_at(rows, width: int, device) -> torch.Tensor:
+    r = torch.as_tensor(rows, dtype=torch.int64, device=device).reshape(-1, 1)
+    return r * width + torch.arange(width, dtype=torch.int64, device=device)
+
+
+def latent_at(w: Workload, rows, device="cpu") -> torch.Tensor:
+    """latent() at arbitrary cache rows (int64 sequence) -> bf16 [len, 512]."""
+    return _normal_at("bf16", _stream_seed(w.key, "lat"), _rows_at(rows, w.dims.d_latent, device))
+
+
+def rope_at(w: Workload, rows, device="cpu") -> torch.Tensor:
+    return _normal_at("bf16", _stream_seed(w.key, "rope"), _rows_at(rows, w.dims.d_rope, device))
 
 
 def idx_query(w: Workload, layer: int, q0: int, nq: int, device="cpu") -> torch.Tensor:
