@@ -20,8 +20,9 @@ from typing import Optional, Tuple
 import torch
 
 __all__ = ["Dims", "Batch", "Csa2Error", "lib", "lib_path", "encode_kv", "index_full",
+           "index_scan", "index_pool", "n_blocks",
            "index_reindex", "attend", "workspace_full", "workspace_reindex",
-           "workspace_attend", "abi_version"]
+           "workspace_attend", "abi_version", "Call"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 lib_path = os.path.join(_PKG, "libcsa2.so")
@@ -61,6 +62,8 @@ def lib() -> ctypes.CDLL:
             "csa2_status_string": (ctypes.c_char_p, [I32]),
             "csa2_last_error": (ctypes.c_char_p, []),
             "csa2_encode_kv": (I32, [I64, P, P, P, P, P, P, P]),
+            "csa2_index_scan": (I32, [PD, PQ, P, P, P, P, I64, P]),
+            "csa2_index_pool": (I32, [PD, PQ, P, I64, P, P, P]),
             "csa2_index_full_workspace_size": (I32, [PD, PQ, ctypes.POINTER(SZ)]),
             "csa2_index_full": (I32, [PD, PQ, P, P, P, P, P, P, I64, P, SZ, P]),
             "csa2_index_reindex_workspace_size": (I32, [PD, PQ, ctypes.POINTER(SZ)]),
@@ -77,6 +80,27 @@ def lib() -> ctypes.CDLL:
 
 def abi_version() -> int:
     return lib().csa2_abi_version()
+
+
+class Call:
+    """A library call with its arguments marshalled once: calling it re-issues
+    the same launch on the same stream (for serving loops and benchmarks that
+    reuse buffers).  Keeps the ctypes structs it points to alive."""
+
+    def __init__(self, fn, args, keep=()):
+        self._fn, self._args, self._keep = fn, args, keep
+
+    def __call__(self) -> None:
+        st = self._fn(*self._args)
+        if st != 0:
+            _check(st)
+
+
+def _issue(fn, args, keep, prepare: bool):
+    if prepare:
+        return Call(fn, args, keep)
+    _check(fn(*args))
+    return None
 
 
 def _check(st: int):
@@ -177,7 +201,7 @@ def _ws_ptr(ws: Optional[torch.Tensor]):
 
 def encode_kv(latent: torch.Tensor, rope: torch.Tensor, kv_codes: torch.Tensor,
               kv_scales: torch.Tensor, kv_rope: torch.Tensor,
-              dst_row: Optional[torch.Tensor] = None) -> None:
+              dst_row: Optional[torch.Tensor] = None, prepare: bool = False):
     """Encode bf16 latent [n, 512] (+ rope [n, 64]) into the FP4 cache planes
     kv_codes uint8 [rows, 256], kv_scales uint8 [rows, 32], kv_rope bf16
     [rows, 64] at rows dst_row (int64 [n]) or 0..n-1."""
@@ -194,8 +218,9 @@ def encode_kv(latent: torch.Tensor, rope: torch.Tensor, kv_codes: torch.Tensor,
         raise ValueError("more entries than cache rows")
     if dst_row is not None and (dst_row.dtype != torch.int64 or dst_row.shape != (n,)):
         raise ValueError("dst_row must be int64 [n]")
-    _check(lib().csa2_encode_kv(n, latent.data_ptr(), rope.data_ptr(), _ptr(dst_row), kv_codes.data_ptr(),
-                                kv_scales.data_ptr(), kv_rope.data_ptr(), _stream(latent.device)))
+    args = (n, latent.data_ptr(), rope.data_ptr(), _ptr(dst_row), kv_codes.data_ptr(),
+            kv_scales.data_ptr(), kv_rope.data_ptr(), _stream(latent.device))
+    return _issue(lib().csa2_encode_kv, args, (), prepare)
 
 
 def index_full(dims: Dims, b: Batch, idx_q: torch.Tensor, idx_w: torch.Tensor, idx_k: torch.Tensor,
@@ -231,11 +256,62 @@ def index_full(dims: Dims, b: Batch, idx_q: torch.Tensor, idx_w: torch.Tensor, i
     return pool_blocks, pool_count
 
 
+def n_blocks(dims: Dims, b: Batch) -> int:
+    """Block-score row length needed by index_scan: ceil((max_visible - W) / 8)."""
+    return max(0, -(-(b.max_visible - dims.swa) // 8))
+
+
+def _check_idx(dims: Dims, b: Batch, idx_q, idx_w, idx_k):
+    n_q = b.n_q
+    if idx_q.dtype != torch.float8_e4m3fn or idx_k.dtype != torch.float8_e4m3fn:
+        raise TypeError("idx_q and idx_k must be float8_e4m3fn")
+    if idx_q.shape != (n_q, dims.idx_heads, dims.idx_dim) or idx_w.shape != (n_q, dims.idx_heads):
+        raise ValueError("idx_q / idx_w shape mismatch")
+    if idx_w.dtype != torch.float32 or idx_k.dim() != 2 or idx_k.shape[1] != dims.idx_dim:
+        raise ValueError("idx_w must be float32 and idx_k [rows, d_i]")
+
+
+def index_scan(dims: Dims, b: Batch, idx_q: torch.Tensor, idx_w: torch.Tensor, idx_k: torch.Tensor,
+               block_scores: Optional[torch.Tensor] = None, prepare: bool = False):
+    """Full-mode scan: block scores float32 [n_q, ld] (b_j for j < nb)."""
+    dev = idx_k.device
+    _dev(idx_q, idx_w, idx_k, block_scores)
+    _check_idx(dims, b, idx_q, idx_w, idx_k)
+    if block_scores is None:
+        block_scores = torch.empty(b.n_q, max(1, n_blocks(dims, b)), dtype=torch.float32, device=dev)
+    if block_scores.dtype != torch.float32 or block_scores.dim() != 2 or block_scores.shape[0] != b.n_q:
+        raise ValueError("block_scores must be float32 [n_q, ld]")
+    d, q = dims.c(), b.c()
+    args = (ctypes.byref(d), ctypes.byref(q), idx_q.data_ptr(), idx_w.data_ptr(),
+            idx_k.data_ptr(), block_scores.data_ptr(), block_scores.shape[1], _stream(dev))
+    call = _issue(lib().csa2_index_scan, args, (d, q), prepare)
+    return call if prepare else block_scores
+
+
+def index_pool(dims: Dims, b: Batch, block_scores: torch.Tensor,
+               pool_blocks: Optional[torch.Tensor] = None, pool_count: Optional[torch.Tensor] = None,
+               prepare: bool = False):
+    """Top-P block pool from index_scan's block scores."""
+    dev = block_scores.device
+    _dev(block_scores, pool_blocks, pool_count)
+    if block_scores.dtype != torch.float32 or block_scores.dim() != 2 or block_scores.shape[0] != b.n_q:
+        raise ValueError("block_scores must be float32 [n_q, ld]")
+    if pool_blocks is None:
+        pool_blocks = torch.empty(b.n_q, dims.pool_blocks, dtype=torch.int32, device=dev)
+    if pool_count is None:
+        pool_count = torch.empty(b.n_q, dtype=torch.int32, device=dev)
+    d, q = dims.c(), b.c()
+    args = (ctypes.byref(d), ctypes.byref(q), block_scores.data_ptr(), block_scores.shape[1],
+            pool_blocks.data_ptr(), pool_count.data_ptr(), _stream(dev))
+    call = _issue(lib().csa2_index_pool, args, (d, q), prepare)
+    return call if prepare else (pool_blocks, pool_count)
+
+
 def index_reindex(dims: Dims, b: Batch, idx_q: torch.Tensor, idx_w: torch.Tensor, idx_k: torch.Tensor,
                   pool_blocks: torch.Tensor, pool_count: torch.Tensor,
                   topk_pos: Optional[torch.Tensor] = None, topk_count: Optional[torch.Tensor] = None,
-                  topk_scores: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None
-                  ) -> Tuple[torch.Tensor, torch.Tensor]:
+                  topk_scores: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None,
+                  prepare: bool = False):
     """Reindex inside the pool. Returns (topk_pos int32 [n_q, K], topk_count)."""
     dev = idx_k.device
     _dev(idx_q, idx_w, idx_k, pool_blocks, pool_count, topk_pos, topk_count, topk_scores)
@@ -255,18 +331,18 @@ def index_reindex(dims: Dims, b: Batch, idx_q: torch.Tensor, idx_w: torch.Tensor
     ws = _workspace(workspace_reindex(dims, b), dev, ws)
     wp, wn = _ws_ptr(ws)
     d, q = dims.c(), b.c()
-    _check(lib().csa2_index_reindex(ctypes.byref(d), ctypes.byref(q), idx_q.data_ptr(), idx_w.data_ptr(),
-                                    idx_k.data_ptr(), pool_blocks.data_ptr(), pool_count.data_ptr(),
-                                    topk_pos.data_ptr(), topk_count.data_ptr(), _ptr(topk_scores),
-                                    wp, wn, _stream(dev)))
-    return topk_pos, topk_count
+    args = (ctypes.byref(d), ctypes.byref(q), idx_q.data_ptr(), idx_w.data_ptr(),
+            idx_k.data_ptr(), pool_blocks.data_ptr(), pool_count.data_ptr(),
+            topk_pos.data_ptr(), topk_count.data_ptr(), _ptr(topk_scores), wp, wn, _stream(dev))
+    call = _issue(lib().csa2_index_reindex, args, (d, q, ws), prepare)
+    return call if prepare else (topk_pos, topk_count)
 
 
 def attend(dims: Dims, b: Batch, q_lat: torch.Tensor, q_rope: torch.Tensor, softmax_scale: float,
            kv_codes: torch.Tensor, kv_scales: torch.Tensor, kv_rope: torch.Tensor,
            topk_pos: torch.Tensor, topk_count: torch.Tensor, swa_kv: torch.Tensor, swa_base: torch.Tensor,
            out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-           ws: Optional[torch.Tensor] = None, want_lse: bool = True) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+           ws: Optional[torch.Tensor] = None, want_lse: bool = True, prepare: bool = False):
     """Sparse FP4 + window attention. Returns (out f32 [n_q, H, 512], lse)."""
     dev = q_lat.device
     _dev(q_lat, q_rope, kv_codes, kv_scales, kv_rope, topk_pos, topk_count, swa_kv, swa_base, out, lse)
@@ -286,8 +362,9 @@ def attend(dims: Dims, b: Batch, q_lat: torch.Tensor, q_rope: torch.Tensor, soft
     ws = _workspace(workspace_attend(dims, b), dev, ws)
     wp, wn = _ws_ptr(ws)
     d, q = dims.c(), b.c()
-    _check(lib().csa2_attend(ctypes.byref(d), ctypes.byref(q), q_lat.data_ptr(), q_rope.data_ptr(),
-                             float(softmax_scale), kv_codes.data_ptr(), kv_scales.data_ptr(), kv_rope.data_ptr(),
-                             topk_pos.data_ptr(), topk_count.data_ptr(), swa_kv.data_ptr(), swa_base.data_ptr(),
-                             out.data_ptr(), _ptr(lse), wp, wn, _stream(dev)))
-    return out, lse
+    args = (ctypes.byref(d), ctypes.byref(q), q_lat.data_ptr(), q_rope.data_ptr(),
+            float(softmax_scale), kv_codes.data_ptr(), kv_scales.data_ptr(), kv_rope.data_ptr(),
+            topk_pos.data_ptr(), topk_count.data_ptr(), swa_kv.data_ptr(), swa_base.data_ptr(),
+            out.data_ptr(), _ptr(lse), wp, wn, _stream(dev))
+    call = _issue(lib().csa2_attend, args, (d, q, ws), prepare)
+    return call if prepare else (out, lse)

@@ -11,6 +11,12 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libcsa2.so")
 SOURCES = ["api.hip", "encode.hip", "scan.hip", "select.hip", "reindex.hip", "attend.hip"]
+# The indexer contractions keep their MFMA accumulators in VGPRs (the epilogue
+# reads every result with VALU ops; AGPR results would each need a
+# v_accvgpr_read first) and assume finite scores (non-finite inputs are
+# undefined by the ABI), so max(x, 0) needs no NaN canonicalisation.
+EXTRA = {"scan.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-fno-honor-nans"],
+         "reindex.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-fno-honor-nans"]}
 
 # No fast-math: the FP4 encoder needs the correctly rounded fp32 division.
 # Packed fp32 instructions are disabled for every device compile.
@@ -39,7 +45,7 @@ def build(verbose: bool = False) -> str:
     jobs = []
     for s in SOURCES:
         o = os.path.join(obj_dir, s.replace(".hip", ".o"))
-        jobs.append((s, [cc, *FLAGS, "-c", os.path.join(CSRC, s), "-o", o], o))
+        jobs.append((s, [cc, *FLAGS, *EXTRA.get(s, []), "-c", os.path.join(CSRC, s), "-o", o], o))
     with cf.ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:
         results = list(ex.map(lambda j: (j[0], *_run(j[1])), jobs))
     failed = [(s, out) for s, rc, out in results if rc != 0]

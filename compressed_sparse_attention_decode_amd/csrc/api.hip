@@ -1,6 +1,7 @@
 // C ABI of the CSA2 decode-path library: argument checks, workspace layout and
 // kernel launches.  Declarations and contracts are in include/csa2.h.
 #include <mutex>
+#include <stdlib.h>
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
@@ -84,14 +85,14 @@ int64_t max_blocks(const csa2_dims* d, const csa2_queries* q) {
   return (c + 7) / 8;
 }
 
-// index_full workspace: [hist n_q x 4096 u32][block scores n_q x ldb f32]
+// index_full workspace: block scores n_q x ldb f32 (when the caller passes none)
 int64_t full_ldb(const csa2_dims* d, const csa2_queries* q) {
   const int64_t nb = max_blocks(d, q);
   return ((nb > 0 ? nb : 1) + 63) / 64 * 64;
 }
 
 size_t full_ws(const csa2_dims* d, const csa2_queries* q) {
-  return align256((size_t)q->n_q * kHistBins * 4) + align256((size_t)q->n_q * full_ldb(d, q) * 4);
+  return align256((size_t)q->n_q * full_ldb(d, q) * 4);
 }
 
 size_t reindex_ws(const csa2_dims* d, const csa2_queries* q) {
@@ -106,11 +107,11 @@ AttendPlan attend_plan(const csa2_dims* d, const csa2_queries* q) {
   p.hg = d->n_heads / (16 * p.nw);
   const int emax = d->topk + d->swa;
   const int tiles = (emax + kAttendTile - 1) / kAttendTile;
-  // aim for >= 2 workgroups per CU overall, but keep >= 4 tiles per split
-  int want = (512 + q->n_q * p.hg - 1) / (q->n_q * p.hg);
-  int maxs = (tiles + 3) / 4;
-  if (maxs < 1) maxs = 1;
-  int s = want < 1 ? 1 : (want > maxs ? maxs : want);
+  // spread a small batch over more workgroups (splits of the entry list);
+  // each extra split costs one fp32 partial output (H x 512) per query
+  int want = (160 + q->n_q * p.hg - 1) / (q->n_q * p.hg);
+  if (const char* env = getenv("CSA2_ATTEND_SPLITS")) want = atoi(env);
+  int s = want < 1 ? 1 : (want > tiles ? tiles : want);
   const int tps = (tiles + s - 1) / s;
   p.split_entries = tps * kAttendTile;
   p.splits = (emax + p.split_entries - 1) / p.split_entries;
@@ -177,6 +178,53 @@ csa2_status csa2_index_full_workspace_size(const csa2_dims* d, const csa2_querie
   return CSA2_OK;
 }
 
+csa2_status csa2_index_scan(const csa2_dims* d, const csa2_queries* q, const uint8_t* idx_q, const float* idx_w,
+                            const uint8_t* idx_k, float* block_scores, int64_t ld_block_scores, void* stream) {
+  csa2_status st = check_dims(d);
+  if (st) return st;
+  if ((st = check_queries(q))) return st;
+  if (!idx_q || !idx_w || !idx_k || !block_scores) return fail(CSA2_ERR_INVALID_ARG, "required pointer is NULL");
+  if (((uintptr_t)idx_q | (uintptr_t)idx_k) & 15) return fail(CSA2_ERR_INVALID_ARG, "idx_q and idx_k must be 16-byte aligned");
+  const int64_t nb = max_blocks(d, q);
+  if (ld_block_scores < nb)
+    return fail(CSA2_ERR_INVALID_ARG, "ld_block_scores %lld < %lld blocks", (long long)ld_block_scores, (long long)nb);
+  if ((st = check_device())) return st;
+  ScanArgs sa;
+  sa.idx_q = idx_q; sa.idx_w = idx_w; sa.idx_k = idx_k;
+  sa.seq_base = q->seq_base; sa.n_visible = q->n_visible;
+  sa.n_q = q->n_q; sa.hi = d->idx_heads; sa.d = d->idx_dim; sa.swa = d->swa; sa.g = q->tokens_per_seq;
+  int tile = kScanTile, pf = kScanPrefetch;
+  if (const char* env = getenv("CSA2_SCAN_TILE")) tile = atoi(env);
+  if (const char* env = getenv("CSA2_SCAN_PREFETCH")) pf = atoi(env);
+  if (tile < 64 || tile % 64 || tile > 4096) tile = kScanTile;
+  if (pf != 4 && pf != 6 && pf != 8) pf = kScanPrefetch;
+  sa.tile_pos = tile;
+  sa.prefetch = pf;
+  sa.tiles = (int)((nb * 8 + tile - 1) / tile);
+  sa.bscore = block_scores;
+  sa.ld = ld_block_scores;
+  hipError_t e = launch_scan(sa, (hipStream_t)stream);
+  return e == hipSuccess ? CSA2_OK : hip_fail(e, "scan launch");
+}
+
+csa2_status csa2_index_pool(const csa2_dims* d, const csa2_queries* q, const float* block_scores,
+                            int64_t ld_block_scores, int32_t* pool_blocks, int32_t* pool_count, void* stream) {
+  csa2_status st = check_dims(d);
+  if (st) return st;
+  if ((st = check_queries(q))) return st;
+  if (!block_scores || !pool_blocks || !pool_count) return fail(CSA2_ERR_INVALID_ARG, "required pointer is NULL");
+  const int64_t nb = max_blocks(d, q);
+  if (ld_block_scores < nb)
+    return fail(CSA2_ERR_INVALID_ARG, "ld_block_scores %lld < %lld blocks", (long long)ld_block_scores, (long long)nb);
+  if ((st = check_device())) return st;
+  PoolArgs pa;
+  pa.bscore = block_scores; pa.ld = ld_block_scores; pa.n_visible = q->n_visible;
+  pa.n_q = q->n_q; pa.swa = d->swa; pa.pool = d->pool_blocks;
+  pa.pool_blocks = pool_blocks; pa.pool_count = pool_count;
+  hipError_t e = launch_pool_select(pa, (hipStream_t)stream);
+  return e == hipSuccess ? CSA2_OK : hip_fail(e, "pool select launch");
+}
+
 csa2_status csa2_index_full(const csa2_dims* d, const csa2_queries* q, const uint8_t* idx_q, const float* idx_w,
                             const uint8_t* idx_k, int32_t* pool_blocks, int32_t* pool_count, float* block_scores,
                             int64_t ld_block_scores, void* ws, size_t ws_bytes, void* stream) {
@@ -185,36 +233,15 @@ csa2_status csa2_index_full(const csa2_dims* d, const csa2_queries* q, const uin
   if ((st = check_queries(q))) return st;
   if (!idx_q || !idx_w || !idx_k || !pool_blocks || !pool_count)
     return fail(CSA2_ERR_INVALID_ARG, "required pointer is NULL");
-  if (((uintptr_t)idx_q | (uintptr_t)idx_k) & 15) return fail(CSA2_ERR_INVALID_ARG, "idx_q and idx_k must be 16-byte aligned");
-  const int64_t nb = max_blocks(d, q);
-  if (block_scores && ld_block_scores < nb)
-    return fail(CSA2_ERR_INVALID_ARG, "ld_block_scores %lld < %lld blocks", (long long)ld_block_scores, (long long)nb);
-  if ((st = check_ws(ws, ws_bytes, full_ws(d, q)))) return st;
-  if ((st = check_device())) return st;
-  hipStream_t s = (hipStream_t)stream;
-  uint32_t* hist = (uint32_t*)ws;
-  float* bs_ws = (float*)((char*)ws + align256((size_t)q->n_q * kHistBins * 4));
-
-  ScanArgs sa;
-  sa.idx_q = idx_q; sa.idx_w = idx_w; sa.idx_k = idx_k;
-  sa.seq_base = q->seq_base; sa.n_visible = q->n_visible;
-  sa.n_q = q->n_q; sa.hi = d->idx_heads; sa.d = d->idx_dim; sa.swa = d->swa; sa.g = q->tokens_per_seq;
-  const int64_t cmax = nb * 8;
-  sa.tiles = (int)((cmax + kScanTile - 1) / kScanTile);
-  sa.bscore = block_scores ? block_scores : bs_ws;
-  sa.ld = block_scores ? ld_block_scores : full_ldb(d, q);
-  sa.hist = hist;
-
-  hipError_t e = launch_fill_u32(hist, (size_t)q->n_q * kHistBins, 0u, s);
-  if (e != hipSuccess) return hip_fail(e, "histogram clear");
-  if ((e = launch_scan(sa, s)) != hipSuccess) return hip_fail(e, "scan launch");
-
-  PoolArgs pa;
-  pa.bscore = sa.bscore; pa.ld = sa.ld; pa.hist = hist; pa.n_visible = q->n_visible;
-  pa.n_q = q->n_q; pa.swa = d->swa; pa.pool = d->pool_blocks;
-  pa.pool_blocks = pool_blocks; pa.pool_count = pool_count;
-  if ((e = launch_pool_select(pa, s)) != hipSuccess) return hip_fail(e, "pool select launch");
-  return CSA2_OK;
+  float* bs = block_scores;
+  int64_t ld = ld_block_scores;
+  if (!bs) {
+    if ((st = check_ws(ws, ws_bytes, full_ws(d, q)))) return st;
+    bs = (float*)ws;
+    ld = full_ldb(d, q);
+  }
+  if ((st = csa2_index_scan(d, q, idx_q, idx_w, idx_k, bs, ld, stream))) return st;
+  return csa2_index_pool(d, q, bs, ld, pool_blocks, pool_count, stream);
 }
 
 csa2_status csa2_index_reindex_workspace_size(const csa2_dims* d, const csa2_queries* q, size_t* bytes) {

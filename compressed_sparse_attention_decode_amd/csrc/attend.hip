@@ -10,16 +10,19 @@
 //
 // Mapping (gfx950): a workgroup = one query x up to 64 heads (one wave per 16
 // heads) x one split of the entry list.  Entries stream in tiles of 32:
-//  * the workgroup gathers the tile's rows (FP4 codes + E4M3 scales + rope,
-//    or window rows), dequantises on load (exact in bf16 and f16) and stores
-//    two LDS images: keys row-major in bf16 (for Q.K) and values transposed
-//    in f16 (for P.V);
-//  * Q.K^T: v_mfma_f32_16x16x32_bf16 with the tile as A (rows = entries) and
+//  * the split's cache rows are resolved into LDS once; per tile the
+//    workgroup gathers the rows (FP4 codes + E4M3 scales + rope, or window
+//    rows), dequantises on load and stores one row-major f16 image (FP4 x E4M3
+//    values are exact in f16; bf16 window / rope / query values are exact in
+//    f16 inside its normal range, the reason for the |x| < 65504 bound);
+//  * Q.K^T: v_mfma_f32_16x16x32_f16 with the tile as A (rows = entries) and
 //    the wave's 16 query heads as B (held in registers), giving S^T whose lane
 //    layout is exactly the A layout P.V needs, so P never leaves registers;
 //  * online softmax in the exp2 domain, P rounded to f16 (bf16 would cost
-//    about 2^-9 relative per weight), P.V with v_mfma_f32_16x16x32_f16 into
-//    32 accumulator tiles (16 heads x 512 dims);
+//    about 2^-9 relative per weight); P.V with v_mfma_f32_16x16x32_f16 whose
+//    value operand is read from the same row-major image with the gfx950 LDS
+//    transpose read (ds_read_b64_tr_b16), into 32 accumulator tiles
+//    (16 heads x 512 dims);
 //  * with several splits per query, unnormalised partials (o, m, l) are
 //    merged by k_attend_combine with a log-sum-exp rescale.
 #include "common.h"
@@ -29,8 +32,11 @@ namespace csa2 {
 namespace {
 
 constexpr int kTile = kAttendTile;        // 32 entries
-constexpr int kKLS = kKeyDim + 8;         // bf16 row stride of the key image
-constexpr int kVTS = kTile + 4;           // f16 row stride of the value image
+constexpr int kKS = kKeyDim + 8;          // f16 row stride of the tile image
+constexpr int kMaxSplit = 2048 + 1024;    // entries of one split (topk + swa bounds)
+
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4s lds_v4s;
 
 __device__ __forceinline__ float e2m1_value(uint32_t nib) {
   const uint32_t m = nib & 7u;
@@ -38,11 +44,20 @@ __device__ __forceinline__ float e2m1_value(uint32_t nib) {
   return (nib & 8u) ? -v : v;
 }
 
+__device__ __forceinline__ uint32_t pack_h2(float x, float y) {
+  const _Float16 a = (_Float16)x, b = (_Float16)y;
+  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+
+__device__ __forceinline__ uint32_t bf16x2_to_h2(uint32_t w) {
+  return pack_h2(__uint_as_float(w << 16), __uint_as_float(w & 0xFFFF0000u));
+}
+
 template <int NW>
 __global__ __launch_bounds__(64 * NW) void k_attend(AttendArgs a) {
   constexpr int NT = 64 * NW;
-  __shared__ __attribute__((aligned(16))) uint16_t s_k[kTile * kKLS];     // bf16 keys
-  __shared__ __attribute__((aligned(16))) _Float16 s_v[kLatent * kVTS];   // f16 values^T
+  __shared__ __attribute__((aligned(16))) _Float16 s_k[kTile * kKS];
+  __shared__ int64_t s_row[kMaxSplit];     // cache row (>= 0) or -1 - window row
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int gq = lane >> 4, col = lane & 15;
@@ -63,8 +78,11 @@ __global__ __launch_bounds__(64 * NW) void k_attend(AttendArgs a) {
   const int64_t swa_base = a.swa_base[q];
   const int32_t* tk = a.topk_pos + (int64_t)q * a.topk;
 
-  // query fragments: B operand, lane = head (col), k-slots = dims 32ks + 8gq + j
-  v8bf qf[kKeyDim / 32];
+  for (int e = e_begin + tid; e < e_end; e += NT)
+    s_row[e - e_begin] = e < Es ? seq_base + tk[e] : -1 - (swa_base + (e - Es));
+
+  // query fragments (f16): B operand, lane = head (col), k-slots = dims 32ks + 8gq + j
+  v8h qf[kKeyDim / 32];
   {
     const int h = head0 + col;
 #pragma unroll
@@ -72,8 +90,9 @@ __global__ __launch_bounds__(64 * NW) void k_attend(AttendArgs a) {
       const int d = ks * 32 + gq * 8;
       const uint16_t* src = d < kLatent ? a.q_lat + ((int64_t)q * H + h) * kLatent + d
                                         : a.q_rope + ((int64_t)q * H + h) * kRope + (d - kLatent);
-      v4u raw = *reinterpret_cast<const v4u*>(src);
-      qf[ks] = __builtin_bit_cast(v8bf, raw);
+      const v4u raw = *reinterpret_cast<const v4u*>(src);
+      const v4u hv = {bf16x2_to_h2(raw[0]), bf16x2_to_h2(raw[1]), bf16x2_to_h2(raw[2]), bf16x2_to_h2(raw[3])};
+      qf[ks] = __builtin_bit_cast(v8h, hv);
     }
   }
 
@@ -85,49 +104,44 @@ __global__ __launch_bounds__(64 * NW) void k_attend(AttendArgs a) {
   for (int e0 = e_begin; e0 < e_end; e0 += kTile) {
     const int ne = min(kTile, e_end - e0);
     __syncthreads();
-    // ---- gather + dequantise the tile into LDS
+    // ---- gather + dequantise the tile into the f16 image
     for (int it = tid; it < kTile * 32; it += NT) {
-      const int e = it >> 5, grp = it & 31, ge = e0 + e;
-      uint32_t kw[8] = {0, 0, 0, 0, 0, 0, 0, 0};     // 16 bf16
-      _Float16 vh[16];
-#pragma unroll
-      for (int k = 0; k < 16; ++k) vh[k] = (_Float16)0.0f;
+      const int e = it >> 5, grp = it & 31;
+      v4u w0 = {0, 0, 0, 0}, w1 = {0, 0, 0, 0};
       if (e < ne) {
-        if (ge < Es) {
-          const int64_t row = seq_base + tk[ge];
+        const int64_t row = s_row[e0 - e_begin + e];
+        if (row >= 0) {
           const v2u cw = *reinterpret_cast<const v2u*>(a.kv_codes + row * kCodeBytes + grp * 8);
           const float s = e4m3_to_float(a.kv_scales[row * kScaleBytes + grp]);
+          uint32_t hv[8];
 #pragma unroll
-          for (int k = 0; k < 16; ++k) {
-            const uint32_t nib = (cw[k >> 3] >> (4 * (k & 7))) & 15u;
-            const float v = e2m1_value(nib) * s;            // exact
-            vh[k] = (_Float16)v;
-            kw[k >> 1] |= (__float_as_uint(v) >> 16) << (16 * (k & 1));
+          for (int k = 0; k < 8; ++k) {
+            const uint32_t byte = (cw[k >> 2] >> (8 * (k & 3))) & 0xFFu;
+            hv[k] = pack_h2(e2m1_value(byte & 15u) * s, e2m1_value(byte >> 4) * s);   // exact
           }
+          w0 = v4u{hv[0], hv[1], hv[2], hv[3]};
+          w1 = v4u{hv[4], hv[5], hv[6], hv[7]};
         } else {
-          const int64_t row = swa_base + (ge - Es);
-          const v4u* src = reinterpret_cast<const v4u*>(a.swa_kv + row * kKeyDim + grp * 16);
+          const v4u* src = reinterpret_cast<const v4u*>(a.swa_kv + (-1 - row) * kKeyDim + grp * 16);
           const v4u x0 = src[0], x1 = src[1];
-          kw[0] = x0[0]; kw[1] = x0[1]; kw[2] = x0[2]; kw[3] = x0[3];
-          kw[4] = x1[0]; kw[5] = x1[1]; kw[6] = x1[2]; kw[7] = x1[3];
-#pragma unroll
-          for (int k = 0; k < 16; ++k) vh[k] = (_Float16)bf16_to_float((kw[k >> 1] >> (16 * (k & 1))) & 0xFFFFu);
+          w0 = v4u{bf16x2_to_h2(x0[0]), bf16x2_to_h2(x0[1]), bf16x2_to_h2(x0[2]), bf16x2_to_h2(x0[3])};
+          w1 = v4u{bf16x2_to_h2(x1[0]), bf16x2_to_h2(x1[1]), bf16x2_to_h2(x1[2]), bf16x2_to_h2(x1[3])};
         }
       }
-      v4u* dk = reinterpret_cast<v4u*>(s_k + e * kKLS + grp * 16);
-      dk[0] = v4u{kw[0], kw[1], kw[2], kw[3]};
-      dk[1] = v4u{kw[4], kw[5], kw[6], kw[7]};
-#pragma unroll
-      for (int k = 0; k < 16; ++k) s_v[(grp * 16 + k) * kVTS + e] = vh[k];
+      v4u* dk = reinterpret_cast<v4u*>(s_k + e * kKS + grp * 16);
+      dk[0] = w0;
+      dk[1] = w1;
     }
     for (int it = tid; it < kTile * 8; it += NT) {
-      const int e = it >> 3, ch = it & 7, ge = e0 + e;
+      const int e = it >> 3, ch = it & 7;
       v4u x = {0, 0, 0, 0};
       if (e < ne) {
-        if (ge < Es) x = *reinterpret_cast<const v4u*>(a.kv_rope + (seq_base + tk[ge]) * kRope + ch * 8);
-        else x = *reinterpret_cast<const v4u*>(a.swa_kv + (swa_base + (ge - Es)) * kKeyDim + kLatent + ch * 8);
+        const int64_t row = s_row[e0 - e_begin + e];
+        const v4u r = row >= 0 ? *reinterpret_cast<const v4u*>(a.kv_rope + row * kRope + ch * 8)
+                               : *reinterpret_cast<const v4u*>(a.swa_kv + (-1 - row) * kKeyDim + kLatent + ch * 8);
+        x = v4u{bf16x2_to_h2(r[0]), bf16x2_to_h2(r[1]), bf16x2_to_h2(r[2]), bf16x2_to_h2(r[3])};
       }
-      *reinterpret_cast<v4u*>(s_k + e * kKLS + kLatent + ch * 8) = x;
+      *reinterpret_cast<v4u*>(s_k + e * kKS + kLatent + ch * 8) = x;
     }
     __syncthreads();
     if (head0 >= H) continue;
@@ -136,10 +150,10 @@ __global__ __launch_bounds__(64 * NW) void k_attend(AttendArgs a) {
     v4f s0 = {0.0f, 0.0f, 0.0f, 0.0f}, s1 = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int ks = 0; ks < kKeyDim / 32; ++ks) {
-      const v8bf k0 = __builtin_bit_cast(v8bf, *reinterpret_cast<const v4u*>(s_k + col * kKLS + ks * 32 + gq * 8));
-      const v8bf k1 = __builtin_bit_cast(v8bf, *reinterpret_cast<const v4u*>(s_k + (16 + col) * kKLS + ks * 32 + gq * 8));
-      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qf[ks], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qf[ks], s1, 0, 0, 0);
+      const v8h k0 = __builtin_bit_cast(v8h, *reinterpret_cast<const v4u*>(s_k + col * kKS + ks * 32 + gq * 8));
+      const v8h k1 = __builtin_bit_cast(v8h, *reinterpret_cast<const v4u*>(s_k + (16 + col) * kKS + ks * 32 + gq * 8));
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(k0, qf[ks], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(k1, qf[ks], s1, 0, 0, 0);
     }
     // lane holds entries 4gq+i (s0) and 16+4gq+i (s1) for head `col`
     float sv[8];
@@ -176,13 +190,15 @@ __global__ __launch_bounds__(64 * NW) void k_attend(AttendArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) o[nt][i] *= ar[i];
     }
-    // ---- O += P . V  (A = P: rows heads, k = entries {4gq..4gq+3, 16+4gq..+3})
+    // ---- O += P . V   (k-slots: entries 4gq..4gq+3, then 16+4gq..16+4gq+3;
+    //      the transpose read hands lane `col` four entries of dim 16nt+col)
+    const int ra = 4 * gq + (col >> 2), cb = 4 * (col & 3);
 #pragma unroll
     for (int nt = 0; nt < kLatent / 16; ++nt) {
-      const _Float16* vr = s_v + (nt * 16 + col) * kVTS;
-      const v2u lo = *reinterpret_cast<const v2u*>(vr + 4 * gq);
-      const v2u hi = *reinterpret_cast<const v2u*>(vr + 16 + 4 * gq);
-      const v8h vb = __builtin_bit_cast(v8h, v4u{lo[0], lo[1], hi[0], hi[1]});
+      const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(s_k + ra * kKS + nt * 16 + cb));
+      const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(s_k + (16 + ra) * kKS + nt * 16 + cb));
+      const v8h vb = __builtin_bit_cast(v8h, (v4u{__builtin_bit_cast(v2u, lo)[0], __builtin_bit_cast(v2u, lo)[1],
+                                                  __builtin_bit_cast(v2u, hi)[0], __builtin_bit_cast(v2u, hi)[1]}));
       o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pf, vb, o[nt], 0, 0, 0);
     }
   }

@@ -76,6 +76,29 @@ __device__ __forceinline__ float e4m3_to_float(uint32_t c) {
   return (c & 0x80) ? -v : v;
 }
 
+// Cross-lane reductions without LDS round trips (gfx950).
+// Sum over the four 16-lane rows of a wave (lanes l, l^16, l^32, l^48): two
+// row swaps.  Every lane ends with the same value, added in the same order.
+__device__ __forceinline__ float sum_rows4(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// Max over each aligned group of 8 lanes: quad_perm [1,0,3,2], [2,3,0,1],
+// then row_half_mirror (lane i <-> 7 - i within each 8).
+__device__ __forceinline__ float max_lanes8(float v) {
+  v = fmaxf(v, dpp_mov<0xB1>(v));
+  v = fmaxf(v, dpp_mov<0x4E>(v));
+  return fmaxf(v, dpp_mov<0x141>(v));
+}
+
 // Block-wide exclusive scan of one uint32 per thread (blockDim.x = NT, a
 // multiple of 64).  `sh` needs NT/64 + 1 words.  Returns the exclusive prefix;
 // *total receives the block sum.  Contains __syncthreads().

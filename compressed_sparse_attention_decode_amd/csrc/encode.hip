@@ -78,11 +78,6 @@ __global__ __launch_bounds__(256) void k_encode(int64_t n, const uint16_t* __res
   }
 }
 
-__global__ void k_fill_u32(uint32_t* p, size_t n, uint32_t v) {
-  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
-    p[i] = v;
-}
-
 }  // namespace
 
 hipError_t launch_encode(int64_t n, const uint16_t* latent, const uint16_t* rope,
@@ -93,14 +88,6 @@ hipError_t launch_encode(int64_t n, const uint16_t* latent, const uint16_t* rope
   const int64_t blocks = (threads + 255) / 256;
   hipLaunchKernelGGL(k_encode, dim3((unsigned)blocks), dim3(256), 0, s, n, latent, rope, dst_row,
                      codes, scales, rope_out);
-  return hipGetLastError();
-}
-
-hipError_t launch_fill_u32(uint32_t* p, size_t n, uint32_t v, hipStream_t s) {
-  if (n == 0) return hipSuccess;
-  size_t blocks = (n + 255) / 256;
-  if (blocks > 4096) blocks = 4096;
-  hipLaunchKernelGGL(k_fill_u32, dim3((unsigned)blocks), dim3(256), 0, s, p, n, v);
   return hipGetLastError();
 }
 

@@ -15,15 +15,15 @@ struct ScanArgs {
   const int32_t* n_visible;  // [n_q]
   int n_q, hi, d, swa, g;    // g: queries per sequence
   int tiles;                 // position tiles per query
+  int tile_pos;              // positions per tile (multiple of 64)
+  int prefetch;              // LDS ring slots per wave (4, 6 or 8)
   float* bscore;             // [n_q, ld]
   int64_t ld;
-  uint32_t* hist;            // [n_q, kHistBins]
 };
 
 struct PoolArgs {
   const float* bscore;
   int64_t ld;
-  const uint32_t* hist;
   const int32_t* n_visible;
   int n_q, swa, pool;
   int32_t* pool_blocks;      // [n_q, pool]
@@ -72,7 +72,6 @@ struct AttendArgs {
 hipError_t launch_encode(int64_t n, const uint16_t* latent, const uint16_t* rope,
                          const int64_t* dst_row, uint8_t* codes, uint8_t* scales,
                          uint16_t* rope_out, hipStream_t s);
-hipError_t launch_fill_u32(uint32_t* p, size_t n, uint32_t v, hipStream_t s);
 hipError_t launch_scan(const ScanArgs& a, hipStream_t s);
 hipError_t launch_pool_select(const PoolArgs& a, hipStream_t s);
 hipError_t launch_reindex(const ReindexArgs& a, hipStream_t s);
@@ -82,7 +81,8 @@ int attend_waves(int heads);   // waves (16 heads each) per attention workgroup
 // Tiling constants the host needs for grids and workspace sizes.
 constexpr int kHistShift = 20;         // coarse histogram: top 12 bits of a key
 constexpr int kHistBins = 1 << (32 - kHistShift);
-constexpr int kScanTile = 2048;        // positions per scan workgroup
+constexpr int kScanTile = 2048;        // default positions per scan workgroup
+constexpr int kScanPrefetch = 6;       // default LDS ring slots per wave
 constexpr int kAttendTile = 32;        // entries per attention tile
 constexpr int kReindexSplit = 16;      // scoring workgroups per query
 constexpr int kMaxVisible = 1 << 21;   // bound of n_visible

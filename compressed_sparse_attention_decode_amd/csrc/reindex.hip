@@ -12,11 +12,14 @@
 //    blocks (16 positions, two contiguous 1 KiB key runs at d = 128) with the
 //    same f16-MFMA contraction as the Full scan and writes fp32 scores;
 //  * k_topk_select: one 1024-thread workgroup per query holds the <= 16,384
-//    order-preserving keys in LDS, finds the K-th largest with a 4-pass radix
-//    select, and compacts in pool order (= ascending positions), admitting
-//    keys equal to the threshold lowest position first.
+//    order-preserving keys in LDS, finds the K-th largest with a radix select
+//    that starts at the highest bit where the smallest and largest key differ
+//    (the common leading bits would pile every key onto one counter), and
+//    compacts in pool order (= ascending positions), admitting keys equal to
+//    the threshold lowest position first.
 #include "common.h"
 #include "internal.h"
+#include "select_common.h"
 
 namespace csa2 {
 namespace {
@@ -40,24 +43,28 @@ __global__ __launch_bounds__(256) void k_reindex_score(ReindexArgs a) {
   v8h qf[HT][KC];
   float wv[HT][4];
   const uint8_t* qp = a.idx_q + (int64_t)q * a.hi * D;
+  // all loads issued back to back from clamped (valid) rows, padded heads
+  // zeroed afterwards: no branch, one wait
+  uint32_t qraw[HT][KC][2];
 #pragma unroll
   for (int t = 0; t < HT; ++t) {
-    const int h = t * 16 + col;
+    const int hc = min(t * 16 + col, a.hi - 1);
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc) {
-      uint32_t w0 = 0, w1 = 0;
-      if (h < a.hi) {
-        const uint32_t* src = reinterpret_cast<const uint32_t*>(qp + (int64_t)h * D + gq * LB + kc * 8);
-        w0 = src[0];
-        w1 = src[1];
-      }
-      qf[t][kc] = fp8x8_to_v8h(w0, w1);
+      const v2u x = *reinterpret_cast<const v2u*>(qp + (int64_t)hc * D + gq * LB + kc * 8);
+      qraw[t][kc][0] = x[0];
+      qraw[t][kc][1] = x[1];
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int hh = t * 16 + gq * 4 + i;
-      wv[t][i] = hh < a.hi ? a.idx_w[(int64_t)q * a.hi + hh] : 0.0f;
-    }
+    for (int i = 0; i < 4; ++i) wv[t][i] = a.idx_w[(int64_t)q * a.hi + min(t * 16 + gq * 4 + i, a.hi - 1)];
+  }
+#pragma unroll
+  for (int t = 0; t < HT; ++t) {
+    const bool live = t * 16 + col < a.hi;
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) qf[t][kc] = fp8x8_to_v8h(live ? qraw[t][kc][0] : 0u, live ? qraw[t][kc][1] : 0u);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) wv[t][i] = t * 16 + gq * 4 + i < a.hi ? wv[t][i] : 0.0f;
   }
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.idx_k + a.seq_base[q] * D, (uint32_t)c * D);
   const int32_t* pool = a.pool_blocks + (int64_t)q * a.pool;
@@ -98,8 +105,7 @@ __global__ __launch_bounds__(256) void k_reindex_score(ReindexArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) sum += wv[t][i] * fmaxf(acc[i], 0.0f);
     }
-    sum += __shfl_xor(sum, 16, 64);
-    sum += __shfl_xor(sum, 32, 64);
+    sum = sum_rows4(sum);
     const int i = i_begin + 2 * s + (col >> 3);
     if (gq == 0 && i < i_end) sc[i * kBlock + (col & 7)] = pos < c ? sum : -__builtin_inff();
     if (more) {
@@ -112,9 +118,14 @@ __global__ __launch_bounds__(256) void k_reindex_score(ReindexArgs a) {
 
 constexpr int kTkThreads = 1024;
 constexpr int kMaxCand = 2048 * kBlock;
+constexpr int kPer = kMaxCand / kTkThreads;        // 16 items per thread
+
+// LDS slot of item i: one pad word per 16 so that a thread's contiguous run
+// and the strided (coalesced) load pattern are both free of bank conflicts.
+__device__ __forceinline__ int kslot(int i) { return i + (i >> 4); }
 
 __global__ __launch_bounds__(kTkThreads) void k_topk_select(ReindexArgs a) {
-  __shared__ uint32_t s_key[kMaxCand];
+  __shared__ uint32_t s_key[kMaxCand + kMaxCand / 16];
   __shared__ uint32_t s_hist[256];
   __shared__ uint32_t s_scan[kTkThreads / 64 + 1];
   __shared__ uint32_t s_misc[4];
@@ -130,55 +141,50 @@ __global__ __launch_bounds__(kTkThreads) void k_topk_select(ReindexArgs a) {
   int32_t* out = a.topk_pos + (int64_t)q * K;
   float* out_s = a.topk_scores ? a.topk_scores + (int64_t)q * K : nullptr;
 
-  // keys in pool order (ascending positions); invalid positions -> key 0
-  constexpr int kPer = kMaxCand / kTkThreads;   // 16 items per thread
-  uint32_t nvalid = 0;
+  // keys in pool order (= ascending positions), coalesced loads; invalid -> 0
+  uint32_t nvalid = 0, lo = 0xFFFFFFFFu, hi = 0;
   for (int k = 0; k < kPer; ++k) {
-    const int i = tid * kPer + k;
+    const int i = k * kTkThreads + tid;
     uint32_t key = 0;
     if (i < N) {
       const int pos = pool[i >> 3] * kBlock + (i & 7);
-      if (pos >= 0 && pos < c) { key = order_key(sc[i]); ++nvalid; }
+      if (pos >= 0 && pos < c) {
+        key = order_key(sc[i]);
+        ++nvalid;
+        lo = min(lo, key);
+        hi = max(hi, key);
+      }
     }
-    s_key[i] = key;
+    s_key[kslot(i)] = key;
   }
   uint32_t total;
   (void)block_exclusive_scan<kTkThreads>(nvalid, s_scan, &total);
   const uint32_t keff = min((uint32_t)K, total);
+  const uint32_t kmin = block_min_u32<kTkThreads>(lo, s_scan);
+  const uint32_t kmax = block_max_u32<kTkThreads>(hi, s_scan);
 
   uint32_t T = 0, need_eq = 0;
   if (keff > 0) {
-    uint32_t prefix = 0, need = keff;
-    for (int ps = 0; ps < 4; ++ps) {
-      const int sh = 24 - 8 * ps;
-      const uint32_t hmask = ps == 0 ? 0u : (~0u << (32 - 8 * ps));
+    const int top = highest_diff_bit(kmin, kmax);
+    uint32_t prefix = (uint32_t)(((uint64_t)kmin >> (top + 1)) << (top + 1));
+    uint32_t need = keff;
+    int fixed_lo = top + 1;            // bits >= fixed_lo are decided
+    while (fixed_lo > 0) {
+      const int sh = max(0, fixed_lo - 8);
+      const uint32_t dmask = (1u << (fixed_lo - sh)) - 1;
       if (tid < 256) s_hist[tid] = 0;
       __syncthreads();
       for (int k = 0; k < kPer; ++k) {
-        const uint32_t key = s_key[tid * kPer + k];
-        if (key != 0 && (key & hmask) == prefix) atomicAdd(&s_hist[(key >> sh) & 255u], 1u);
+        const uint32_t key = s_key[kslot(tid * kPer + k)];
+        if (key != 0 && ((uint64_t)key >> fixed_lo) == ((uint64_t)prefix >> fixed_lo))
+          atomicAdd(&s_hist[(key >> sh) & dmask], 1u);
       }
       __syncthreads();
-      if (tid < 64) {
-        const int lane = tid;
-        uint32_t l4 = 0, cc[4];
-        for (int k = 0; k < 4; ++k) { cc[k] = s_hist[255 - (lane * 4 + k)]; l4 += cc[k]; }
-        uint32_t x = l4;
-        for (int d = 1; d < 64; d <<= 1) {
-          const uint32_t y = __shfl_up(x, d, 64);
-          if (lane >= d) x += y;
-        }
-        uint32_t above = x - l4;
-        if (above < need && need <= x) {
-          for (int k = 0; k < 4; ++k) {
-            if (above + cc[k] >= need) { s_misc[0] = 255 - (lane * 4 + k); s_misc[1] = above; break; }
-            above += cc[k];
-          }
-        }
-      }
+      find_crossing(s_hist, 256, need, s_misc);
       __syncthreads();
       prefix |= s_misc[0] << sh;
       need -= s_misc[1];
+      fixed_lo = sh;
       __syncthreads();
     }
     T = prefix;
@@ -188,14 +194,14 @@ __global__ __launch_bounds__(kTkThreads) void k_topk_select(ReindexArgs a) {
   // ordered compaction: key > T always, key == T lowest positions first
   uint32_t eq = 0;
   if (keff > 0) {
-    for (int k = 0; k < kPer; ++k) eq += s_key[tid * kPer + k] == T;
+    for (int k = 0; k < kPer; ++k) eq += s_key[kslot(tid * kPer + k)] == T;
   }
   uint32_t eq_before = block_exclusive_scan<kTkThreads>(eq, s_scan, &total);
   uint32_t take = 0;
   uint32_t flags = 0;
   if (keff > 0) {
     for (int k = 0; k < kPer; ++k) {
-      const uint32_t key = s_key[tid * kPer + k];
+      const uint32_t key = s_key[kslot(tid * kPer + k)];
       bool sel = key > T;
       if (key == T && eq_before < need_eq) { sel = true; ++eq_before; }
       if (sel) { flags |= 1u << k; ++take; }
@@ -207,7 +213,7 @@ __global__ __launch_bounds__(kTkThreads) void k_topk_select(ReindexArgs a) {
       const int i = tid * kPer + k;
       if (before < (uint32_t)K) {
         out[before] = pool[i >> 3] * kBlock + (i & 7);
-        if (out_s) out_s[before] = key_float(s_key[i]);
+        if (out_s) out_s[before] = key_float(s_key[kslot(i)]);
       }
       ++before;
     }

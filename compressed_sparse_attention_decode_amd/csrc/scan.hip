@@ -1,5 +1,4 @@
-// Full-mode indexer scan: per-position scores, block-of-8 maxima and a
-// coarse histogram of the block scores.
+// Full-mode indexer scan: per-position scores and block-of-8 maxima.
 //
 // Follows "DeepSeek-V4.1-Flash 梗概" §3.2 (hierarchical sparse indexer: the
 // first Full layer scores the whole visible context and pools blocks of 8;
@@ -9,10 +8,12 @@
 // used throughout this library): s_p = sum_h w_h * max(0, q_h . k_p).
 //
 // Layout and mapping (gfx950):
-//  * one workgroup = 4 waves = one query x kScanTile consecutive positions;
-//  * a wave step covers 16 positions: lane l holds key row (l & 15) and the
-//    contiguous byte range [(l >> 4) * d/4, +d/4) of that row, loaded with raw
-//    buffer loads (rows >= c read as zero, so the tail needs no branches);
+//  * one workgroup = 4 waves = one query x tile_pos consecutive positions;
+//  * a wave step covers 16 positions: lane l holds d/4 bytes of key row
+//    (l & 15).  Keys stream with direct-to-LDS raw buffer loads (rows >= c
+//    read as zero, so the tail needs no branches) through a ring of R LDS
+//    slots per wave, R - 1 steps in flight, which costs no VGPRs (the f16
+//    query fragments already hold 64 per lane);
 //  * fp8 keys and queries are converted to f16 in registers (exact) and
 //    contracted with v_mfma_f32_16x16x32_f16: A = 16 query heads, B = 16
 //    positions, K = 32 dims per instruction.  The product and the fp32
@@ -20,8 +21,8 @@
 //    accumulator drops low-order bits), so it is not used;
 //  * the epilogue applies ReLU and the head weights, reduces over the four
 //    lane groups, masks p >= c, takes the max over 8 lanes (one block), and
-//    one lane per block writes the block score and bumps an LDS histogram of
-//    the top 12 key bits, flushed once per workgroup with global atomics.
+//    one lane per block writes the block score to LDS; the tile's scores
+//    leave in one coalesced store (4 bytes per 1 KiB of keys).
 // HBM-bound: 128 bytes of keys per position, 16 KFLOP per position.
 #include "common.h"
 #include "internal.h"
@@ -29,12 +30,37 @@
 namespace csa2 {
 namespace {
 
-template <int D, int HT>
-__global__ __launch_bounds__(256) void k_scan(ScanArgs a) {
-  constexpr int KC = D / 32;            // MFMA k-chunks
-  constexpr int LB = D / 4;             // bytes per lane per position row
-  __shared__ uint32_t s_hist[kHistBins];
+// Byte offset, inside a key row, of the lane's 16-byte chunk `h` (h = 0, 1).
+// For d = 128 chunk 0 covers bytes [16gq, 16gq+16) and chunk 1 bytes
+// [64+16gq, ...): each load instruction reads whole 64-byte halves of 16 rows.
+// The query fragments use the same byte -> k-slot map, so the permutation of
+// the reduction dimension cancels in every dot product.
+template <int D>
+__device__ __forceinline__ int key_chunk(int gq, int h) {
+  return D == 128 ? h * 64 + gq * 16 : gq * 16;
+}
 
+typedef __attribute__((address_space(3))) void lds_void;
+
+// s_waitcnt immediates (gfx9 layout: vmcnt[3:0] and [15:14], expcnt[6:4],
+// lgkmcnt[11:8]); the fields not named are left at "no wait".
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+__device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+constexpr int kMaxTilePos = 4096;
+
+template <int D, int HT, int R>
+__global__ __launch_bounds__(256) void k_scan(ScanArgs a) {
+  constexpr int KC = D / 32;            // MFMA k-chunks of 32 dims
+  constexpr int NH = D / 64;            // 16-byte loads per lane per step
+  __shared__ __attribute__((aligned(16))) uint8_t s_ring[4][R][NH][1024];
+  __shared__ float s_bs[kMaxTilePos / 8];
+  __shared__ __attribute__((aligned(16))) uint8_t s_q[64 * (D + 8)];
+  __shared__ float s_w[64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int gq = lane >> 4, col = lane & 15;
 
@@ -51,115 +77,171 @@ __global__ __launch_bounds__(256) void k_scan(ScanArgs a) {
 
   const int n = a.n_visible[q];
   const int c = max(0, n - a.swa);
-  const int p_begin = tile * kScanTile;
+  const int p_begin = tile * a.tile_pos;
   if (p_begin >= c) return;
-  const int p_end = min(p_begin + kScanTile, c);
+  const int p_end = min(p_begin + a.tile_pos, c);
   const int nsteps = (p_end - p_begin + 15) >> 4;
 
-  for (int i = tid; i < kHistBins; i += 256) s_hist[i] = 0;
-
-  // query fragments (f16) and head weights for this lane
   v8h qf[HT][KC];
   float wv[HT][4];
   const uint8_t* qp = a.idx_q + (int64_t)q * a.hi * D;
+
+  // buffer descriptor over this sequence's candidate keys, built from
+  // wave-uniform scalars (rows >= c read as zero)
+  const uint8_t* kbase = a.idx_k + a.seq_base[q] * D;
+  const uint64_t kaddr = (uint64_t)(uintptr_t)kbase;
+  const v4u rsrc = {(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)kaddr),
+                    (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(kaddr >> 32)) & 0xFFFFu,
+                    (uint32_t)__builtin_amdgcn_readfirstlane(c * D), 0x00020000u};
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+
+  // this wave's steps are s_k = wave + 4k, k < ns, streamed through R LDS
+  // slots with R - 1 steps of direct-to-LDS loads in flight.  The loads are
+  // issued as inline asm so that the compiler neither tracks them (it would
+  // wait for every one of them before each LDS read) nor moves them; the
+  // waits below count them explicitly (vector-memory ops retire in order).
+  const int ns = wave < nsteps ? (nsteps - wave + 3) >> 2 : 0;
+  auto issue = [&](int k) {
+    const uint32_t row = (uint32_t)(p_begin + (wave + 4 * k) * 16 + col) * D;
+    const uint32_t slot = (uint32_t)(uintptr_t)(lds_void*)&s_ring[wave_u][k % R][0][0];
+#pragma unroll
+    for (int h = 0; h < NH; ++h) {
+      const uint32_t m0 = (uint32_t)__builtin_amdgcn_readfirstlane((int)(slot + h * 1024));
+      asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                   :: "s"(m0), "v"(row + key_chunk<D>(gq, h)), "s"(rsrc) : "memory", "m0");
+    }
+  };
+  // fetch: wait until step k has landed (keeping the younger steps in
+  // flight), refill the ring, read the lane's bytes and convert to f16
+  auto fetch = [&](int k, v8h* kf) {
+    if (k + R - 1 < ns) {
+      wait_lgkmcnt0();                 // the slot's previous reads are done
+      issue(k + R - 1);
+      wait_vmcnt<(R - 1) * NH>();      // step k has landed; R - 1 younger in flight
+    } else {
+      wait_vmcnt<0>();
+    }
+    const uint8_t* slot = &s_ring[wave_u][k % R][0][0];
+    uint32_t kb[4 * NH];
+#pragma unroll
+    for (int h = 0; h < NH; ++h) {
+      const v4u x = *reinterpret_cast<const v4u*>(slot + h * 1024 + lane * 16);
+      kb[4 * h + 0] = x[0]; kb[4 * h + 1] = x[1]; kb[4 * h + 2] = x[2]; kb[4 * h + 3] = x[3];
+    }
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) kf[kc] = fp8x8_to_v8h(kb[2 * kc], kb[2 * kc + 1]);
+  };
+  auto contract = [&](const v8h* kf, v4f* acc) {
+#pragma unroll
+    for (int t = 0; t < HT; ++t) acc[t] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) {
+#pragma unroll
+      for (int t = 0; t < HT; ++t) acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qf[t][kc], kf[kc], acc[t], 0, 0, 0);
+    }
+  };
+  auto epilogue = [&](const v4f* acc, int k) {
+    // four independent partial sums (no 16-long dependent chain)
+    float pp[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int t = 0; t < HT; ++t) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pp[i] += wv[t][i] * fmaxf(acc[t][i], 0.0f);
+    }
+    const float part = sum_rows4((pp[0] + pp[1]) + (pp[2] + pp[3]));
+    const int s = wave + 4 * k;
+    const int p0 = p_begin + s * 16;
+    const float v = max_lanes8((p0 + col < c) ? part : -__builtin_inff());
+    if (lane < 16 && (lane & 7) == 0) s_bs[s * 2 + (lane >> 3)] = v;
+  };
+
+  // software pipeline: the MFMAs of step k run while the VALU finishes
+  // step k - 1 (epilogue) and prepares step k + 1 (LDS read, fp8 -> f16),
+  // none of which depends on the MFMAs in flight
+  const int pro = min(R - 1, ns);
+  for (int k = 0; k < pro; ++k) issue(k);
+
+  // query fragments (f16) and head weights for this lane; loaded after the
+  // first key loads are in flight so the two latencies overlap
+  // the workgroup stages the query (H_i x d fp8) and the head weights in LDS
+  // once with 16-byte loads; each wave then reads its fragments from there
+  // (rows padded by 8 bytes so the 16 rows a wave reads hit distinct banks)
+  {
+    const int nvec = a.hi * D / 16;
+    for (int i = tid; i < nvec; i += 256) {
+      const int h = i / (D / 16), o = (i % (D / 16)) * 16;
+      *reinterpret_cast<v4u*>(&s_q[h * (D + 8) + o]) = *reinterpret_cast<const v4u*>(qp + h * D + o);
+    }
+    if (tid < 64) s_w[tid] = tid < a.hi ? a.idx_w[(int64_t)q * a.hi + tid] : 0.0f;
+    __syncthreads();
+  }
 #pragma unroll
   for (int t = 0; t < HT; ++t) {
     const int h = t * 16 + col;
+    const bool live = h < a.hi;
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc) {
-      uint32_t w0 = 0, w1 = 0;
-      if (h < a.hi) {
-        const uint32_t* src = reinterpret_cast<const uint32_t*>(qp + (int64_t)h * D + gq * LB + kc * 8);
-        w0 = src[0];
-        w1 = src[1];
-      }
-      qf[t][kc] = fp8x8_to_v8h(w0, w1);
+      const v2u x = *reinterpret_cast<const v2u*>(&s_q[min(h, a.hi - 1) * (D + 8) + key_chunk<D>(gq, kc >> 1) + (kc & 1) * 8]);
+      qf[t][kc] = fp8x8_to_v8h(live ? x[0] : 0u, live ? x[1] : 0u);
+      // keep the converted fragments resident: without this the compiler
+      // re-converts them inside the loop to save registers
+      asm volatile("" : "+v"(qf[t][kc]));
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int hh = t * 16 + gq * 4 + i;
-      wv[t][i] = hh < a.hi ? a.idx_w[(int64_t)q * a.hi + hh] : 0.0f;
-    }
+    for (int i = 0; i < 4; ++i) wv[t][i] = s_w[t * 16 + gq * 4 + i];
   }
-
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.idx_k + a.seq_base[q] * D, (uint32_t)c * D);
-  float* bs = a.bscore + (int64_t)q * a.ld;
-  __syncthreads();
-
-  auto load = [&](int s, uint32_t* kb) {
-    const uint32_t off = (uint32_t)(p_begin + s * 16 + col) * D + gq * LB;
-    v4u x = buf_load16(rk, off);
-    kb[0] = x[0]; kb[1] = x[1]; kb[2] = x[2]; kb[3] = x[3];
-    if constexpr (LB == 32) {
-      v4u y = buf_load16(rk, off + 16);
-      kb[4] = y[0]; kb[5] = y[1]; kb[6] = y[2]; kb[7] = y[3];
-    }
-  };
-
-  uint32_t kb[LB / 4];
-  if (wave < nsteps) load(wave, kb);
-  for (int s = wave; s < nsteps; s += 4) {
-    uint32_t nx[LB / 4];
-    const bool more = s + 4 < nsteps;
-    if (more) load(s + 4, nx);
-
-    v8h kf[KC];
-#pragma unroll
-    for (int kc = 0; kc < KC; ++kc) kf[kc] = fp8x8_to_v8h(kb[2 * kc], kb[2 * kc + 1]);
-    float part = 0.0f;
-#pragma unroll
-    for (int t = 0; t < HT; ++t) {
-      v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-      for (int kc = 0; kc < KC; ++kc) acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(qf[t][kc], kf[kc], acc, 0, 0, 0);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) part += wv[t][i] * fmaxf(acc[i], 0.0f);
-    }
-    part += __shfl_xor(part, 16, 64);
-    part += __shfl_xor(part, 32, 64);
-    const int p0 = p_begin + s * 16;
-    float v = (p0 + col < c) ? part : -__builtin_inff();
-    v = fmaxf(v, __shfl_xor(v, 1, 64));
-    v = fmaxf(v, __shfl_xor(v, 2, 64));
-    v = fmaxf(v, __shfl_xor(v, 4, 64));
-    if (lane < 16 && (lane & 7) == 0) {
-      const int jb = (p0 + lane) >> 3;
-      if (jb * 8 < c) {
-        bs[jb] = v;
-        atomicAdd(&s_hist[order_key(v) >> kHistShift], 1u);
-      }
-    }
-    if (more) {
-#pragma unroll
-      for (int i = 0; i < LB / 4; ++i) kb[i] = nx[i];
+  if (ns > 0) {
+    // ping-pong between two fragment / accumulator sets (no register copies
+    // of MFMA results, which would stall on the MFMAs in flight)
+    v8h kfa[KC], kfb[KC];
+    v4f acca[HT], accb[HT];
+    fetch(0, kfa);
+    for (int k = 0;; k += 2) {
+      contract(kfa, acca);                       // step k
+      if (k > 0) epilogue(accb, k - 1);
+      if (k + 1 >= ns) { epilogue(acca, k); break; }
+      fetch(k + 1, kfb);
+      contract(kfb, accb);                       // step k + 1
+      epilogue(acca, k);
+      if (k + 2 >= ns) { epilogue(accb, k + 1); break; }
+      fetch(k + 2, kfa);
     }
   }
   __syncthreads();
-  uint32_t* gh = a.hist + (int64_t)q * kHistBins;
-  for (int i = tid; i < kHistBins; i += 256) {
-    const uint32_t v = s_hist[i];
-    if (v) atomicAdd(gh + i, v);
-  }
+  // block scores of the tile, one coalesced store
+  float* bs = a.bscore + (int64_t)q * a.ld + (p_begin >> 3);
+  const int nblk = (p_end - p_begin + 7) >> 3;
+  for (int i = tid; i < nblk; i += 256) bs[i] = s_bs[i];
 }
 
-template <int D>
-hipError_t launch_d(const ScanArgs& a, hipStream_t s) {
+template <int D, int R>
+hipError_t launch_dr(const ScanArgs& a, hipStream_t s) {
   const int ht = (a.hi + 15) / 16;
   const int units = ((a.n_q / a.g) * a.tiles + 7) / 8 * 8;
   const dim3 grid((unsigned)(units * a.g)), block(256);
   switch (ht) {
-    case 1: hipLaunchKernelGGL((k_scan<D, 1>), grid, block, 0, s, a); break;
-    case 2: hipLaunchKernelGGL((k_scan<D, 2>), grid, block, 0, s, a); break;
-    case 3: hipLaunchKernelGGL((k_scan<D, 3>), grid, block, 0, s, a); break;
-    default: hipLaunchKernelGGL((k_scan<D, 4>), grid, block, 0, s, a); break;
+    case 1: hipLaunchKernelGGL((k_scan<D, 1, R>), grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((k_scan<D, 2, R>), grid, block, 0, s, a); break;
+    case 3: hipLaunchKernelGGL((k_scan<D, 3, R>), grid, block, 0, s, a); break;
+    default: hipLaunchKernelGGL((k_scan<D, 4, R>), grid, block, 0, s, a); break;
   }
   return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_d(const ScanArgs& a, hipStream_t s) {
+  switch (a.prefetch) {        // LDS ring slots per wave (steps in flight + 1)
+    case 4: return launch_dr<D, 4>(a, s);
+    case 8: return launch_dr<D, 8>(a, s);
+    default: return launch_dr<D, 6>(a, s);
+  }
 }
 
 }  // namespace
 
 hipError_t launch_scan(const ScanArgs& a, hipStream_t s) {
   if (a.tiles == 0) return hipSuccess;
+  if (a.tile_pos > kMaxTilePos || a.tile_pos % 64) return hipErrorInvalidValue;
   return a.d == 64 ? launch_d<64>(a, s) : launch_d<128>(a, s);
 }
 

@@ -5,19 +5,23 @@
 // (block score descending, block id ascending); the pool is written in
 // ascending block order.
 //
-// One 1024-thread workgroup per query:
-//  1. the scan's coarse histogram (top 12 bits of the order-preserving key)
-//     gives the bin b* holding the P-th best block; blocks in higher bins are
-//     selected outright;
-//  2. one pass over the block scores marks those blocks in an LDS bitmap and
-//     appends the blocks of bin b* to an LDS candidate list (wave ballots);
-//  3. an exact radix select over the low 20 key bits of the candidates finds
-//     the threshold key T and how many blocks equal to T are still needed;
-//     a candidate list that overflows LDS is re-read from global memory;
-//  4. ordered compaction of the bitmap writes ascending block ids, admitting
-//     blocks equal to T in ascending order (ties to the lower id).
+// One 1024-thread workgroup per query, on order-preserving uint32 keys:
+//  1. min/max pass: the bits above the highest bit where min and max differ
+//     are common to every key, so the histograms start below them (keys of
+//     similar scores share their top bits and would otherwise pile onto a few
+//     LDS counters);
+//  2. a 4096-bin LDS histogram of the next 12 bits gives the bin b* holding
+//     the P-th best block;
+//  3. one pass marks blocks in higher bins in an LDS bitmap (wave ballots)
+//     and appends the blocks of bin b* to an LDS candidate list;
+//  4. an exact radix select over the candidates' remaining bits finds the
+//     threshold key T and how many blocks equal to T are still needed (a
+//     candidate list that overflows LDS is re-read from global memory);
+//  5. ordered compaction of the bitmap writes ascending block ids, admitting
+//     blocks equal to T lowest id first.
 #include "common.h"
 #include "internal.h"
+#include "select_common.h"
 
 namespace csa2 {
 namespace {
@@ -30,37 +34,9 @@ __device__ __forceinline__ uint32_t lane_prefix(uint64_t mask) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }
 
-// Wave 0 finds, in a histogram of `nbins` (<= 256) counts, the bin where the
-// count from the top reaches `need`.  Writes {bin, count strictly above} to out.
-__device__ void find_crossing(const uint32_t* hist, int nbins, uint32_t need, uint32_t* out) {
-  const int lane = threadIdx.x & 63;
-  if (threadIdx.x >= 64) return;
-  const int per = (nbins + 63) / 64;
-  // lane handles bins from the top: [nbins - (lane+1)*per, nbins - lane*per)
-  uint32_t local = 0;
-  for (int k = 0; k < per; ++k) {
-    const int b = nbins - 1 - (lane * per + k);
-    if (b >= 0) local += hist[b];
-  }
-  uint32_t x = local;
-  for (int d = 1; d < 64; d <<= 1) {
-    const uint32_t y = __shfl_up(x, d, 64);
-    if (lane >= d) x += y;
-  }
-  uint32_t above = x - local;
-  if (above < need && need <= x) {
-    for (int k = 0; k < per; ++k) {
-      const int b = nbins - 1 - (lane * per + k);
-      if (b < 0) break;
-      const uint32_t cnt = hist[b];
-      if (above + cnt >= need) {
-        out[0] = (uint32_t)b;
-        out[1] = above;
-        break;
-      }
-      above += cnt;
-    }
-  }
+// keys agree on every bit >= lo (lo in [0, 32])
+__device__ __forceinline__ bool same_above(uint32_t a, uint32_t b, int lo) {
+  return ((uint64_t)a >> lo) == ((uint64_t)b >> lo);
 }
 
 __global__ __launch_bounds__(kSelThreads) void k_pool_select(PoolArgs a) {
@@ -86,13 +62,29 @@ __global__ __launch_bounds__(kSelThreads) void k_pool_select(PoolArgs a) {
     return;
   }
   const float* bs = a.bscore + (int64_t)q * a.ld;
-  const uint32_t* gh = a.hist + (int64_t)q * kHistBins;
 
-  // 1. bin b* of the P-th best block (4 bins per thread, from the top)
+  // 1. key range
+  uint32_t lo = 0xFFFFFFFFu, hi = 0;
+  for (int jb = tid; jb < nb; jb += kSelThreads) {
+    const uint32_t k = order_key(bs[jb]);
+    lo = min(lo, k);
+    hi = max(hi, k);
+  }
+  const uint32_t kmin = block_min_u32<kSelThreads>(lo, s_scan);
+  const uint32_t kmax = block_max_u32<kSelThreads>(hi, s_scan);
+  const int top = highest_diff_bit(kmin, kmax);          // -1: all keys equal
+  const int cs = max(0, top - 11);                        // coarse bins: bits [cs, top]
+  const uint32_t cmask = top < 0 ? 0u : (uint32_t)((2ull << (top - cs)) - 1);
+
+  // 2. coarse histogram and the bin b* of the P-th best block
+  for (int i = tid; i < kHistBins; i += kSelThreads) s_hist[i] = 0;
+  __syncthreads();
+  for (int jb = tid; jb < nb; jb += kSelThreads) atomicAdd(&s_hist[(order_key(bs[jb]) >> cs) & cmask], 1u);
+  __syncthreads();
   constexpr int kPer = kHistBins / kSelThreads;
   uint32_t local = 0, cnt[kPer];
   for (int k = 0; k < kPer; ++k) {
-    cnt[k] = gh[kHistBins - 1 - (tid * kPer + k)];
+    cnt[k] = s_hist[kHistBins - 1 - (tid * kPer + k)];
     local += cnt[k];
   }
   uint32_t total;
@@ -114,14 +106,14 @@ __global__ __launch_bounds__(kSelThreads) void k_pool_select(PoolArgs a) {
   const uint32_t bstar = s_misc[0];
   uint32_t need = (uint32_t)P - s_misc[1];
 
-  // 2. mark blocks above b*, collect the blocks of bin b*
+  // 3. mark blocks above b*, collect the blocks of bin b*
   for (int base = 0; base < nb; base += kSelThreads) {
     const int jb = base + tid;
     const uint32_t key = jb < nb ? order_key(bs[jb]) : 0u;
-    const uint32_t bin = key >> kHistShift;
-    const bool hi = jb < nb && bin > bstar;
+    const uint32_t bin = (key >> cs) & cmask;
+    const bool hib = jb < nb && bin > bstar;
     const bool cand = jb < nb && bin == bstar;
-    const uint64_t mhi = __ballot(hi);
+    const uint64_t mhi = __ballot(hib);
     const uint64_t mc = __ballot(cand);
     if (lane == 0) {
       const int w0 = (base + wave * 64) >> 5;
@@ -140,33 +132,31 @@ __global__ __launch_bounds__(kSelThreads) void k_pool_select(PoolArgs a) {
   const uint32_t C = s_ccount;
   const bool in_lds = C <= (uint32_t)kCandCap;
 
-  // 3. radix select of the need-th largest key inside bin b* (bits 19..0)
-  uint32_t prefix = bstar << kHistShift;
-  int fixed = 32 - kHistShift;
-  const int widths[3] = {8, 8, 4};
-  for (int ps = 0; ps < 3; ++ps) {
-    const int wdt = widths[ps];
-    const int sh = 32 - fixed - wdt;
+  // 4. radix select inside bin b* over bits [0, cs)
+  uint32_t prefix = (uint32_t)(((uint64_t)kmin >> (top + 1)) << (top + 1)) | (bstar << cs);
+  int fixed_lo = cs;                    // bits >= fixed_lo are decided
+  while (fixed_lo > 0) {
+    const int sh = max(0, fixed_lo - 8);
+    const uint32_t dmask = (1u << (fixed_lo - sh)) - 1;
     for (int i = tid; i < 256; i += kSelThreads) s_hist[i] = 0;
     __syncthreads();
-    const uint32_t hmask = ~0u << (32 - fixed);
     if (in_lds) {
       for (uint32_t i = tid; i < C; i += kSelThreads) {
         const uint32_t key = s_ckey[i];
-        if ((key & hmask) == prefix) atomicAdd(&s_hist[(key >> sh) & ((1u << wdt) - 1)], 1u);
+        if (same_above(key, prefix, fixed_lo)) atomicAdd(&s_hist[(key >> sh) & dmask], 1u);
       }
     } else {
       for (int jb = tid; jb < nb; jb += kSelThreads) {
         const uint32_t key = order_key(bs[jb]);
-        if ((key & hmask) == prefix) atomicAdd(&s_hist[(key >> sh) & ((1u << wdt) - 1)], 1u);
+        if (same_above(key, prefix, fixed_lo)) atomicAdd(&s_hist[(key >> sh) & dmask], 1u);
       }
     }
     __syncthreads();
-    find_crossing(s_hist, 1 << wdt, need, s_misc + 2);
+    find_crossing(s_hist, 256, need, s_misc + 2);
     __syncthreads();
     prefix |= s_misc[2] << sh;
     need -= s_misc[3];
-    fixed += wdt;
+    fixed_lo = sh;
     __syncthreads();
   }
   const uint32_t T = prefix;
@@ -183,14 +173,14 @@ __global__ __launch_bounds__(kSelThreads) void k_pool_select(PoolArgs a) {
   } else {
     for (int jb = tid; jb < nb; jb += kSelThreads) {
       const uint32_t key = order_key(bs[jb]);
-      if ((key >> kHistShift) != bstar) continue;
+      if (((key >> cs) & cmask) != bstar) continue;
       if (key > T) atomicOr(&s_sel[jb >> 5], 1u << (jb & 31));
       else if (key == T) atomicOr(&s_tie[jb >> 5], 1u << (jb & 31));
     }
   }
   __syncthreads();
 
-  // 4. ordered compaction; ties admitted in ascending block order
+  // 5. ordered compaction; ties admitted in ascending block order
   const int wpt = (nw + kSelThreads - 1) / kSelThreads;
   const int w_lo = min(nw, tid * wpt), w_hi = min(nw, w_lo + wpt);
   uint32_t ties = 0;

@@ -84,7 +84,8 @@ typedef struct csa2_dims {
  *   tokens_per_seq  g in 1..4: queries g*i .. g*i+g-1 belong to one
  *                   sequence (consecutive causal query tokens, e.g. a
  *                   speculative-verify step) and MUST share seq_base; the
- *                   Full scan then reads that sequence's keys once for all g.
+ *                   Full scan runs their workgroups for the same key range on
+ *                   one XCD so the g key streams are served by one L2.
  *                   n_q must be a multiple of g.
  *   max_visible     host-side upper bound of every n_visible[i], at most
  *                   2^21; used only to size launch grids.
@@ -131,25 +132,43 @@ csa2_status csa2_encode_kv(int64_t n, const uint16_t* latent, const uint16_t* ro
                            const int64_t* dst_row, uint8_t* kv_codes, uint8_t* kv_scales,
                            uint16_t* kv_rope, void* stream);
 
-/* Workspace bytes for csa2_index_full (256-byte aligned start required). */
+/* Full-mode indexer, stage 1 of 2: the scan ([atlas] §3.2 hierarchical
+ * sparse indexer and mode table; [newsaint] §3: the Full layer scores every
+ * causally visible position).  For every query:
+ *   s_p = sum_h w_h * max(0, q_h . k_p)  for p in [0, c)   (fp8 inputs, the
+ *         dot products exact, the weighted sum in fp32)
+ *   b_j = max of s_p over p in [8j, min(8j+8, c)),  j < nb = ceil(c / 8)
+ *   idx_q        fp8 [n_q, H_i, d_i]      idx_w  float [n_q, H_i]
+ *   idx_k        fp8 [rows, d_i]  (one key per position, shared by heads)
+ *   block_scores float [n_q, ld_block_scores]: b_j written for j < nb;
+ *                entries at j >= nb are left untouched;
+ *                ld_block_scores >= ceil((max_visible - W) / 8).
+ * One kernel, no workspace.  Queries with n <= W write nothing. */
+csa2_status csa2_index_scan(const csa2_dims* dims, const csa2_queries* q,
+                            const uint8_t* idx_q, const float* idx_w, const uint8_t* idx_k,
+                            float* block_scores, int64_t ld_block_scores, void* stream);
+
+/* Full-mode indexer, stage 2 of 2: the candidate pool ([atlas] §3.2: the
+ * Top-2048 blocks of 8 form the pool).  pool = the min(P, nb) blocks with the
+ * largest b_j, ties to the lower j, written in ascending block order.
+ *   block_scores as written by csa2_index_scan
+ *   pool_blocks  int32 [n_q, P]  ascending block ids, -1 after pool_count
+ *   pool_count   int32 [n_q]     (0 for queries with n <= W)
+ * One kernel, no workspace. */
+csa2_status csa2_index_pool(const csa2_dims* dims, const csa2_queries* q,
+                            const float* block_scores, int64_t ld_block_scores,
+                            int32_t* pool_blocks, int32_t* pool_count, void* stream);
+
+/* Workspace bytes for csa2_index_full (256-byte aligned start required);
+ * used only when block_scores is NULL. */
 csa2_status csa2_index_full_workspace_size(const csa2_dims* dims, const csa2_queries* q,
                                            size_t* bytes);
 
-/* Full-mode hierarchical indexer ([atlas] §3.2 hierarchical sparse indexer
- * and mode table; [newsaint] §3).  For every query:
- *   s_p = sum_h w_h * max(0, q_h . k_p)  for p in [0, c)   (fp8 x fp8, fp32)
- *   b_j = max of s_p over p in [8j, min(8j+8, c)),  j < nb = ceil(c / 8)
- *   pool = the min(P, nb) blocks with the largest b_j, ties to the lower j,
- *          written in ascending block order.
- *   idx_q       fp8 [n_q, H_i, d_i]      idx_w  float [n_q, H_i]
- *   idx_k       fp8 [rows, d_i]  (one key per position, shared by heads)
- *   pool_blocks int32 [n_q, P]  ascending block ids, -1 after pool_count
- *   pool_count  int32 [n_q]
- *   block_scores  optional float [n_q, ld_block_scores] (NULL to skip):
- *               b_j for j < nb; entries at j >= nb are left untouched;
- *               ld_block_scores >= ceil((max_visible - W) / 8).
- *   ws, ws_bytes  workspace of csa2_index_full_workspace_size bytes.
- * Queries with n <= W get pool_count = 0. */
+/* Full-mode indexer: csa2_index_scan followed by csa2_index_pool.
+ *   block_scores  optional float [n_q, ld_block_scores]; NULL keeps the
+ *               block scores in the workspace instead.
+ *   ws, ws_bytes  workspace of csa2_index_full_workspace_size bytes (may be
+ *               NULL / 0 when block_scores is given). */
 csa2_status csa2_index_full(const csa2_dims* dims, const csa2_queries* q,
                             const uint8_t* idx_q, const float* idx_w, const uint8_t* idx_k,
                             int32_t* pool_blocks, int32_t* pool_count,

@@ -48,67 +48,12 @@ def u16(t: torch.Tensor) -> np.ndarray:
     return t.detach().cpu().contiguous().view(torch.int16).numpy().astype(np.uint16)
 
 
-class GpuCase:
-    """Caches, window rows and query batch of a workload on the GPU."""
-
-    def __init__(self, w: wl.Workload, device="cuda", chunk_rows: int = 1 << 18, encode: bool = True):
-        csa2 = lib()
-        self.csa2 = csa2
-        self.w, self.dev = w, device
-        self.lay = lay = wl.layout(w)
-        d = w.dims
-        self.dims = csa2.Dims(n_heads=d.n_heads, idx_heads=d.idx_heads, idx_dim=d.idx_dim,
-                              pool_blocks=d.pool_blocks, topk=d.topk, swa=d.swa)
-        rows = max(lay.rows, 1)
-        self.idx_k = torch.empty(rows, d.idx_dim, dtype=torch.float8_e4m3fn, device=device)
-        self.codes = torch.empty(rows, 256, dtype=torch.uint8, device=device)
-        self.scales = torch.empty(rows, 32, dtype=torch.uint8, device=device)
-        self.kv_rope = torch.empty(rows, 64, dtype=torch.bfloat16, device=device)
-        for r0 in range(0, lay.rows, chunk_rows):
-            n = min(chunk_rows, lay.rows - r0)
-            self.idx_k[r0:r0 + n] = wl.idx_keys(w, r0, n, device)
-            if encode:
-                csa2.encode_kv(wl.latent(w, r0, n, device), wl.rope(w, r0, n, device),
-                               self.codes[r0:r0 + n], self.scales[r0:r0 + n], self.kv_rope[r0:r0 + n])
-        parts = [wl.swa_rows(w, lay, s, device) for s in range(len(lay.ctx))]
-        self.swa_kv = torch.cat(parts) if parts else torch.zeros(1, 576, dtype=torch.bfloat16, device=device)
-        if self.swa_kv.shape[0] == 0:
-            self.swa_kv = torch.zeros(1, 576, dtype=torch.bfloat16, device=device)
-        self.batch = csa2.Batch(
-            seq_base=torch.tensor(lay.q_seq_base, dtype=torch.int64, device=device),
-            n_visible=torch.tensor(lay.q_visible, dtype=torch.int32, device=device),
-            max_visible=max(lay.q_visible) if lay.q_visible else 0,
-            tokens_per_seq=w.tokens_per_seq)
-        self.swa_base = torch.tensor(lay.q_swa_base, dtype=torch.int64, device=device)
-        torch.cuda.synchronize()
-
-    def iq(self, layer: int):
-        n = self.w.n_q
-        return (wl.idx_query(self.w, layer, 0, n, self.dev), wl.idx_weight(self.w, layer, 0, n, self.dev))
-
-    def mq(self, layer: int):
-        n = self.w.n_q
-        return wl.q_latent(self.w, layer, 0, n, self.dev), wl.q_rope(self.w, layer, 0, n, self.dev)
-
-    def full(self, layer=0, block_scores=False):
-        q, w = self.iq(layer)
-        bs = None
-        if block_scores:
-            nb = max(1, -(-(self.batch.max_visible - self.w.dims.swa) // 8))
-            bs = torch.full((self.w.n_q, nb), float("nan"), dtype=torch.float32, device=self.dev)
-        pool, cnt = self.csa2.index_full(self.dims, self.batch, q, w, self.idx_k, block_scores=bs)
-        return pool, cnt, bs
-
-    def reindex(self, layer, pool, cnt, scores=False):
-        q, w = self.iq(layer)
-        ts = torch.empty(self.w.n_q, self.w.dims.topk, dtype=torch.float32, device=self.dev) if scores else None
-        tk, tc = self.csa2.index_reindex(self.dims, self.batch, q, w, self.idx_k, pool, cnt, topk_scores=ts)
-        return tk, tc, ts
-
-    def attend(self, layer, tk, tc):
-        ql, qr = self.mq(layer)
-        return self.csa2.attend(self.dims, self.batch, ql, qr, 1.0, self.codes, self.scales, self.kv_rope,
-                                tk, tc, self.swa_kv, self.swa_base)
+def GpuCase(w: wl.Workload, device="cuda", **kw):
+    """Caches, window rows and query batch of a workload on the GPU (the
+    benchmark's device state)."""
+    lib()
+    from bench import DeviceState
+    return DeviceState(w, device=device, **kw)
 
 
 class OracleQuery:
