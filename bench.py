@@ -99,7 +99,7 @@ class DeviceState:
         q, w = self.iq(layer)
         bs = None
         if block_scores:
-            nb = max(1, self.csa2.n_blocks(self.dims, self.batch))
+            nb = self.csa2.block_scores_ld(self.dims, self.batch)
             bs = torch.full((self.w.n_q, nb), float("nan"), dtype=torch.float32, device=self.dev)
         pool, cnt = self.csa2.index_full(self.dims, self.batch, q, w, self.planes[r][0], block_scores=bs)
         return pool, cnt, bs
@@ -126,7 +126,7 @@ class Step:
         w, csa2, dev = st.w, st.csa2, st.dev
         n_q = w.n_q
         self.layers = list(range(1, w.reindex_layers + 1)) if w.fresh_q_per_layer else [0]
-        self.bs = torch.empty(n_q, max(1, csa2.n_blocks(st.dims, st.batch)), dtype=torch.float32, device=dev)
+        self.bs = torch.empty(n_q, csa2.block_scores_ld(st.dims, st.batch), dtype=torch.float32, device=dev)
         self.pool = torch.empty(n_q, w.dims.pool_blocks, dtype=torch.int32, device=dev)
         self.pcnt = torch.empty(n_q, dtype=torch.int32, device=dev)
         self.tk = torch.empty(len(self.layers), n_q, w.dims.topk, dtype=torch.int32, device=dev)
@@ -377,6 +377,8 @@ def main():
     ap.add_argument("--secondary", default="decode_b1_ctx1m", help="second workload ('' to skip)")
     ap.add_argument("--replicas", type=int, default=0, help="cache replicas (0: enough for >= 1 GB)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle sample budget (0 to skip)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain fp32 copy of MIB MiB four times (calibrates the HBM byte counters)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -388,6 +390,17 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU (the HIP library has no CPU path)", file=sys.stderr)
         sys.exit(2)
+
+    if args.copy_calibration > 0:
+        n = args.copy_calibration << 18
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(4):
+            torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration": {"read_bytes": 4 * n, "write_bytes": 4 * n, "launches": 4}}))
+        return
 
     w = wl.workload(args.workload)
     st, step, res = measure(w, args.steps, args.warmup, args.replicas)

@@ -20,7 +20,7 @@ from typing import Optional, Tuple
 import torch
 
 __all__ = ["Dims", "Batch", "Csa2Error", "lib", "lib_path", "encode_kv", "index_full",
-           "index_scan", "index_pool", "n_blocks",
+           "index_scan", "index_pool", "n_blocks", "block_scores_ld",
            "index_reindex", "attend", "workspace_full", "workspace_reindex",
            "workspace_attend", "abi_version", "Call"]
 
@@ -257,8 +257,13 @@ def index_full(dims: Dims, b: Batch, idx_q: torch.Tensor, idx_w: torch.Tensor, i
 
 
 def n_blocks(dims: Dims, b: Batch) -> int:
-    """Block-score row length needed by index_scan: ceil((max_visible - W) / 8)."""
+    """Most candidate blocks of any query: ceil((max_visible - W) / 8)."""
     return max(0, -(-(b.max_visible - dims.swa) // 8))
+
+
+def block_scores_ld(dims: Dims, b: Batch) -> int:
+    """Row stride of a block-score array: n_blocks rounded up to a multiple of 4 (at least 4)."""
+    return max(4, (n_blocks(dims, b) + 3) // 4 * 4)
 
 
 def _check_idx(dims: Dims, b: Batch, idx_q, idx_w, idx_k):
@@ -278,7 +283,7 @@ def index_scan(dims: Dims, b: Batch, idx_q: torch.Tensor, idx_w: torch.Tensor, i
     _dev(idx_q, idx_w, idx_k, block_scores)
     _check_idx(dims, b, idx_q, idx_w, idx_k)
     if block_scores is None:
-        block_scores = torch.empty(b.n_q, max(1, n_blocks(dims, b)), dtype=torch.float32, device=dev)
+        block_scores = torch.empty(b.n_q, block_scores_ld(dims, b), dtype=torch.float32, device=dev)
     if block_scores.dtype != torch.float32 or block_scores.dim() != 2 or block_scores.shape[0] != b.n_q:
         raise ValueError("block_scores must be float32 [n_q, ld]")
     d, q = dims.c(), b.c()

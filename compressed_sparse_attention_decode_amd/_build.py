@@ -16,6 +16,7 @@ SOURCES = ["api.hip", "encode.hip", "scan.hip", "select.hip", "reindex.hip", "at
 # v_accvgpr_read first) and assume finite scores (non-finite inputs are
 # undefined by the ABI), so max(x, 0) needs no NaN canonicalisation.
 EXTRA = {"scan.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-fno-honor-nans"],
+         "attend.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
          "reindex.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-fno-honor-nans"]}
 
 # No fast-math: the FP4 encoder needs the correctly rounded fp32 division.

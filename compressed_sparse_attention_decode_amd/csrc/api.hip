@@ -99,19 +99,23 @@ size_t reindex_ws(const csa2_dims* d, const csa2_queries* q) {
   return align256((size_t)q->n_q * d->pool_blocks * 8 * 4);
 }
 
-struct AttendPlan { int nw, hg, splits, split_entries; };
+struct AttendPlan { int hg, splits, split_entries; };
 
+// A small batch is spread over more workgroups by splitting each query's
+// entry list (each split costs one fp32 partial output, H x 512, merged by a
+// second kernel); a split keeps at least two tiles so that the gather of one
+// tile overlaps the contraction of the other.
 AttendPlan attend_plan(const csa2_dims* d, const csa2_queries* q) {
   AttendPlan p;
-  p.nw = attend_waves(d->n_heads);
-  p.hg = d->n_heads / (16 * p.nw);
+  p.hg = (d->n_heads + 16 * kAttendWaves - 1) / (16 * kAttendWaves);
   const int emax = d->topk + d->swa;
   const int tiles = (emax + kAttendTile - 1) / kAttendTile;
-  // spread a small batch over more workgroups (splits of the entry list);
-  // each extra split costs one fp32 partial output (H x 512) per query
-  int want = (160 + q->n_q * p.hg - 1) / (q->n_q * p.hg);
-  if (const char* env = getenv("CSA2_ATTEND_SPLITS")) want = atoi(env);
-  int s = want < 1 ? 1 : (want > tiles ? tiles : want);
+  int want = (256 + q->n_q * p.hg - 1) / (q->n_q * p.hg);
+  int cap = tiles / 2;
+  if (const char* env = getenv("CSA2_ATTEND_SPLITS")) { want = atoi(env); cap = tiles; }
+  if (cap > kAttendMaxSplits) cap = kAttendMaxSplits;
+  if (cap < 1) cap = 1;
+  const int s = want < 1 ? 1 : (want > cap ? cap : want);
   const int tps = (tiles + s - 1) / s;
   p.split_entries = tps * kAttendTile;
   p.splits = (emax + p.split_entries - 1) / p.split_entries;
@@ -188,6 +192,8 @@ csa2_status csa2_index_scan(const csa2_dims* d, const csa2_queries* q, const uin
   const int64_t nb = max_blocks(d, q);
   if (ld_block_scores < nb)
     return fail(CSA2_ERR_INVALID_ARG, "ld_block_scores %lld < %lld blocks", (long long)ld_block_scores, (long long)nb);
+  if ((ld_block_scores & 3) || ((uintptr_t)block_scores & 15))
+    return fail(CSA2_ERR_INVALID_ARG, "block_scores must be 16-byte aligned with ld_block_scores a multiple of 4");
   if ((st = check_device())) return st;
   ScanArgs sa;
   sa.idx_q = idx_q; sa.idx_w = idx_w; sa.idx_k = idx_k;
@@ -216,6 +222,8 @@ csa2_status csa2_index_pool(const csa2_dims* d, const csa2_queries* q, const flo
   const int64_t nb = max_blocks(d, q);
   if (ld_block_scores < nb)
     return fail(CSA2_ERR_INVALID_ARG, "ld_block_scores %lld < %lld blocks", (long long)ld_block_scores, (long long)nb);
+  if ((ld_block_scores & 3) || ((uintptr_t)block_scores & 15))
+    return fail(CSA2_ERR_INVALID_ARG, "block_scores must be 16-byte aligned with ld_block_scores a multiple of 4");
   if ((st = check_device())) return st;
   PoolArgs pa;
   pa.bscore = block_scores; pa.ld = ld_block_scores; pa.n_visible = q->n_visible;
@@ -271,10 +279,8 @@ csa2_status csa2_index_reindex(const csa2_dims* d, const csa2_queries* q, const 
   ra.pool_blocks = pool_blocks; ra.pool_count = pool_count;
   ra.n_q = q->n_q; ra.hi = d->idx_heads; ra.d = d->idx_dim; ra.swa = d->swa;
   ra.pool = d->pool_blocks; ra.topk = d->topk;
-  ra.split = kReindexSplit;
-  if (ra.split > (d->pool_blocks + 1) / 2) ra.split = (d->pool_blocks + 1) / 2;
-  if (ra.split < 1) ra.split = 1;
-  ra.scores = (float*)ws;
+  ra.split = (d->pool_blocks + kReindexBlocks - 1) / kReindexBlocks;
+  ra.keys = (uint32_t*)ws;
   ra.topk_pos = topk_pos; ra.topk_count = topk_count; ra.topk_scores = topk_scores;
   hipError_t e = launch_reindex(ra, (hipStream_t)stream);
   return e == hipSuccess ? CSA2_OK : hip_fail(e, "reindex launch");

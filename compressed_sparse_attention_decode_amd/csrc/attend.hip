@@ -8,13 +8,16 @@
 // of a sparse entry is [dequantised latent (512) || bf16 rope (64)] and its
 // value is the dequantised latent; a window row supplies both from bf16.
 //
-// Mapping (gfx950): a workgroup = one query x up to 64 heads (one wave per 16
-// heads) x one split of the entry list.  Entries stream in tiles of 32:
-//  * the split's cache rows are resolved into LDS once; per tile the
-//    workgroup gathers the rows (FP4 codes + E4M3 scales + rope, or window
-//    rows), dequantises on load and stores one row-major f16 image (FP4 x E4M3
-//    values are exact in f16; bf16 window / rope / query values are exact in
-//    f16 inside its normal range, the reason for the |x| < 65504 bound);
+// Mapping (gfx950): a workgroup = 4 waves = one query x up to 64 heads (one
+// wave per 16 heads; waves past the last head only help gather) x one split
+// of the entry list.  Entries stream in tiles of 32:
+//  * the split's cache rows are resolved into LDS once; each tile's raw
+//    bytes (FP4 codes + E4M3 scale, or bf16 window values, and the rope) are
+//    loaded into registers one tile ahead, so the gather of tile t+1 is in
+//    flight while tile t is contracted;
+//  * the raw tile is dequantised into one row-major f16 image in LDS (FP4 x
+//    E4M3 values are exact in f16; bf16 window / rope / query values are exact
+//    in f16 inside its normal range, the reason for the |x| < 65504 bound);
 //  * Q.K^T: v_mfma_f32_16x16x32_f16 with the tile as A (rows = entries) and
 //    the wave's 16 query heads as B (held in registers), giving S^T whose lane
 //    layout is exactly the A layout P.V needs, so P never leaves registers;
@@ -32,6 +35,8 @@ namespace csa2 {
 namespace {
 
 constexpr int kTile = kAttendTile;        // 32 entries
+constexpr int kNW = kAttendWaves;         // waves per workgroup, 16 heads each
+constexpr int kNT = 64 * kNW;
 constexpr int kKS = kKeyDim + 8;          // f16 row stride of the tile image
 constexpr int kMaxSplit = 2048 + 1024;    // entries of one split (topk + swa bounds)
 
@@ -53,11 +58,86 @@ __device__ __forceinline__ uint32_t bf16x2_to_h2(uint32_t w) {
   return pack_h2(__uint_as_float(w << 16), __uint_as_float(w & 0xFFFF0000u));
 }
 
-template <int NW>
-__global__ __launch_bounds__(64 * NW) void k_attend(AttendArgs a) {
-  constexpr int NT = 64 * NW;
+constexpr int kItems = kTile * 32 / kNT;      // (entry, 16-channel group) items per thread
+constexpr int kRopeItems = kTile * 8 / kNT;   // (entry, 8-channel rope chunk) items per thread
+
+// One tile's raw sparse bytes held by a thread, loaded a tile ahead: an item
+// keeps its 8 code bytes in c.xy and its scale byte in c.z.  Window items
+// (at most W rows per query, bf16) are read when the tile is stored.
+struct RawTile {
+  v4u c[kItems];
+  v4u r[kRopeItems];
+};
+
+// rows[e] >= 0: sparse entry at position rows[e] (cache row seq_base + pos);
+// rows[e] < 0: window row swa_base + (-1 - rows[e]).
+__device__ __forceinline__ void load_tile(const AttendArgs& a, const int32_t* rows, int ne, int64_t seq_base,
+                                          int64_t swa_base, int tid, RawTile& t) {
+#pragma unroll
+  for (int k = 0; k < kItems; ++k) {
+    const int it = tid + k * kNT, e = it >> 5, grp = it & 31;
+    t.c[k] = v4u{0u, 0u, 0u, 0u};
+    if (e < ne && rows[e] >= 0) {
+      const int64_t row = seq_base + rows[e];
+      {
+        const v2u cw = *reinterpret_cast<const v2u*>(a.kv_codes + row * kCodeBytes + grp * 8);
+        t.c[k] = v4u{cw[0], cw[1], (uint32_t)a.kv_scales[row * kScaleBytes + grp], 0u};
+      }
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < kRopeItems; ++k) {
+    const int it = tid + k * kNT, e = it >> 3, ch = it & 7;
+    t.r[k] = v4u{0u, 0u, 0u, 0u};
+    if (e < ne) {
+      const int32_t r = rows[e];
+      t.r[k] = r >= 0 ? *reinterpret_cast<const v4u*>(a.kv_rope + (seq_base + r) * kRope + ch * 8)
+                      : *reinterpret_cast<const v4u*>(a.swa_kv + (swa_base + (-1 - r)) * kKeyDim + kLatent + ch * 8);
+    }
+  }
+}
+
+// Dequantise a tile into the f16 image (rows past the tile's end are 0).
+__device__ __forceinline__ void store_tile(const AttendArgs& a, const int32_t* rows, int ne, int64_t swa_base,
+                                           const RawTile& t, int tid, _Float16* s_k) {
+#pragma unroll
+  for (int k = 0; k < kItems; ++k) {
+    const int it = tid + k * kNT, e = it >> 5, grp = it & 31;
+    v4u h0, h1;
+    const int32_t r = e < ne ? rows[e] : 0;
+    if (r < 0) {
+      const v4u* src = reinterpret_cast<const v4u*>(a.swa_kv + (swa_base + (-1 - r)) * kKeyDim + grp * 16);
+      const v4u x0 = src[0], x1 = src[1];
+      h0 = v4u{bf16x2_to_h2(x0[0]), bf16x2_to_h2(x0[1]), bf16x2_to_h2(x0[2]), bf16x2_to_h2(x0[3])};
+      h1 = v4u{bf16x2_to_h2(x1[0]), bf16x2_to_h2(x1[1]), bf16x2_to_h2(x1[2]), bf16x2_to_h2(x1[3])};
+    } else {
+      const float s = e4m3_to_float(t.c[k][2]);
+      uint32_t hv[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const uint32_t byte = (t.c[k][j >> 2] >> (8 * (j & 3))) & 0xFFu;
+        hv[j] = pack_h2(e2m1_value(byte & 15u) * s, e2m1_value(byte >> 4) * s);   // exact
+      }
+      h0 = v4u{hv[0], hv[1], hv[2], hv[3]};
+      h1 = v4u{hv[4], hv[5], hv[6], hv[7]};
+    }
+    v4u* dk = reinterpret_cast<v4u*>(s_k + e * kKS + grp * 16);
+    dk[0] = h0;
+    dk[1] = h1;
+  }
+#pragma unroll
+  for (int k = 0; k < kRopeItems; ++k) {
+    const int it = tid + k * kNT, e = it >> 3, ch = it & 7;
+    const v4u r = t.r[k];
+    *reinterpret_cast<v4u*>(s_k + e * kKS + kLatent + ch * 8) =
+        v4u{bf16x2_to_h2(r[0]), bf16x2_to_h2(r[1]), bf16x2_to_h2(r[2]), bf16x2_to_h2(r[3])};
+  }
+}
+
+__global__ __launch_bounds__(kNT) void k_attend(AttendArgs a) {
   __shared__ __attribute__((aligned(16))) _Float16 s_k[kTile * kKS];
-  __shared__ int64_t s_row[kMaxSplit];     // cache row (>= 0) or -1 - window row
+  __shared__ __attribute__((aligned(16))) _Float16 s_q[kNW * 16 * kKS];   // per wave: 16 heads x 576
+  __shared__ int32_t s_row[kMaxSplit];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int gq = lane >> 4, col = lane & 15;
@@ -66,7 +146,8 @@ __global__ __launch_bounds__(64 * NW) void k_attend(AttendArgs a) {
   const int hg = (blockIdx.x / S) % HG;
   const int sp = blockIdx.x % S;
   const int H = a.heads;
-  const int head0 = (hg * NW + wave) * 16;
+  const int head0 = (hg * kNW + wave) * 16;
+  const bool active = head0 < H;           // wave-uniform
 
   const int n = a.n_visible[q];
   const int c = max(0, n - a.swa);
@@ -78,23 +159,23 @@ __global__ __launch_bounds__(64 * NW) void k_attend(AttendArgs a) {
   const int64_t swa_base = a.swa_base[q];
   const int32_t* tk = a.topk_pos + (int64_t)q * a.topk;
 
-  for (int e = e_begin + tid; e < e_end; e += NT)
-    s_row[e - e_begin] = e < Es ? seq_base + tk[e] : -1 - (swa_base + (e - Es));
-
-  // query fragments (f16): B operand, lane = head (col), k-slots = dims 32ks + 8gq + j
-  v8h qf[kKeyDim / 32];
-  {
-    const int h = head0 + col;
-#pragma unroll
-    for (int ks = 0; ks < kKeyDim / 32; ++ks) {
-      const int d = ks * 32 + gq * 8;
-      const uint16_t* src = d < kLatent ? a.q_lat + ((int64_t)q * H + h) * kLatent + d
-                                        : a.q_rope + ((int64_t)q * H + h) * kRope + (d - kLatent);
-      const v4u raw = *reinterpret_cast<const v4u*>(src);
-      const v4u hv = {bf16x2_to_h2(raw[0]), bf16x2_to_h2(raw[1]), bf16x2_to_h2(raw[2]), bf16x2_to_h2(raw[3])};
-      qf[ks] = __builtin_bit_cast(v8h, hv);
+  for (int e = e_begin + tid; e < e_end; e += kNT) s_row[e - e_begin] = e < Es ? tk[e] : -1 - (e - Es);
+  // the wave's 16 query heads as f16 rows [head][576] (the B operand of Q.K^T)
+  if (active) {
+    _Float16* sq = s_q + wave * 16 * kKS;
+    for (int i = lane; i < 16 * (kKeyDim / 8); i += 64) {
+      const int hh = i / (kKeyDim / 8), d = (i % (kKeyDim / 8)) * 8;
+      const int64_t qh = (int64_t)q * H + head0 + hh;
+      const v4u rq = d < kLatent ? *reinterpret_cast<const v4u*>(a.q_lat + qh * kLatent + d)
+                                 : *reinterpret_cast<const v4u*>(a.q_rope + qh * kRope + (d - kLatent));
+      *reinterpret_cast<v4u*>(sq + hh * kKS + d) =
+          v4u{bf16x2_to_h2(rq[0]), bf16x2_to_h2(rq[1]), bf16x2_to_h2(rq[2]), bf16x2_to_h2(rq[3])};
     }
   }
+  __syncthreads();
+  RawTile raw;
+  if (e_begin < e_end) load_tile(a, s_row, min(kTile, e_end - e_begin), seq_base, swa_base, tid, raw);
+  const _Float16* sqw = s_q + (wave * 16 + col) * kKS + gq * 8;
 
   float m = -__builtin_inff(), l = 0.0f;
   v4f o[kLatent / 16];
@@ -103,48 +184,12 @@ __global__ __launch_bounds__(64 * NW) void k_attend(AttendArgs a) {
 
   for (int e0 = e_begin; e0 < e_end; e0 += kTile) {
     const int ne = min(kTile, e_end - e0);
+    __syncthreads();                         // the previous tile's reads of s_k are done
+    store_tile(a, s_row + (e0 - e_begin), ne, swa_base, raw, tid, s_k);
+    if (e0 + kTile < e_end)
+      load_tile(a, s_row + (e0 + kTile - e_begin), min(kTile, e_end - e0 - kTile), seq_base, swa_base, tid, raw);
     __syncthreads();
-    // ---- gather + dequantise the tile into the f16 image
-    for (int it = tid; it < kTile * 32; it += NT) {
-      const int e = it >> 5, grp = it & 31;
-      v4u w0 = {0, 0, 0, 0}, w1 = {0, 0, 0, 0};
-      if (e < ne) {
-        const int64_t row = s_row[e0 - e_begin + e];
-        if (row >= 0) {
-          const v2u cw = *reinterpret_cast<const v2u*>(a.kv_codes + row * kCodeBytes + grp * 8);
-          const float s = e4m3_to_float(a.kv_scales[row * kScaleBytes + grp]);
-          uint32_t hv[8];
-#pragma unroll
-          for (int k = 0; k < 8; ++k) {
-            const uint32_t byte = (cw[k >> 2] >> (8 * (k & 3))) & 0xFFu;
-            hv[k] = pack_h2(e2m1_value(byte & 15u) * s, e2m1_value(byte >> 4) * s);   // exact
-          }
-          w0 = v4u{hv[0], hv[1], hv[2], hv[3]};
-          w1 = v4u{hv[4], hv[5], hv[6], hv[7]};
-        } else {
-          const v4u* src = reinterpret_cast<const v4u*>(a.swa_kv + (-1 - row) * kKeyDim + grp * 16);
-          const v4u x0 = src[0], x1 = src[1];
-          w0 = v4u{bf16x2_to_h2(x0[0]), bf16x2_to_h2(x0[1]), bf16x2_to_h2(x0[2]), bf16x2_to_h2(x0[3])};
-          w1 = v4u{bf16x2_to_h2(x1[0]), bf16x2_to_h2(x1[1]), bf16x2_to_h2(x1[2]), bf16x2_to_h2(x1[3])};
-        }
-      }
-      v4u* dk = reinterpret_cast<v4u*>(s_k + e * kKS + grp * 16);
-      dk[0] = w0;
-      dk[1] = w1;
-    }
-    for (int it = tid; it < kTile * 8; it += NT) {
-      const int e = it >> 3, ch = it & 7;
-      v4u x = {0, 0, 0, 0};
-      if (e < ne) {
-        const int64_t row = s_row[e0 - e_begin + e];
-        const v4u r = row >= 0 ? *reinterpret_cast<const v4u*>(a.kv_rope + row * kRope + ch * 8)
-                               : *reinterpret_cast<const v4u*>(a.swa_kv + (-1 - row) * kKeyDim + kLatent + ch * 8);
-        x = v4u{bf16x2_to_h2(r[0]), bf16x2_to_h2(r[1]), bf16x2_to_h2(r[2]), bf16x2_to_h2(r[3])};
-      }
-      *reinterpret_cast<v4u*>(s_k + e * kKS + kLatent + ch * 8) = x;
-    }
-    __syncthreads();
-    if (head0 >= H) continue;
+    if (!active) continue;
 
     // ---- S^T = K_tile . Q^T  (rows: entries, cols: heads)
     v4f s0 = {0.0f, 0.0f, 0.0f, 0.0f}, s1 = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -152,8 +197,9 @@ __global__ __launch_bounds__(64 * NW) void k_attend(AttendArgs a) {
     for (int ks = 0; ks < kKeyDim / 32; ++ks) {
       const v8h k0 = __builtin_bit_cast(v8h, *reinterpret_cast<const v4u*>(s_k + col * kKS + ks * 32 + gq * 8));
       const v8h k1 = __builtin_bit_cast(v8h, *reinterpret_cast<const v4u*>(s_k + (16 + col) * kKS + ks * 32 + gq * 8));
-      s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(k0, qf[ks], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(k1, qf[ks], s1, 0, 0, 0);
+      const v8h qb = __builtin_bit_cast(v8h, *reinterpret_cast<const v4u*>(sqw + ks * 32));
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(k0, qb, s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(k1, qb, s1, 0, 0, 0);
     }
     // lane holds entries 4gq+i (s0) and 16+4gq+i (s1) for head `col`
     float sv[8];
@@ -202,7 +248,7 @@ __global__ __launch_bounds__(64 * NW) void k_attend(AttendArgs a) {
       o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pf, vb, o[nt], 0, 0, 0);
     }
   }
-  if (head0 >= H) return;
+  if (!active) return;
 
   // ---- epilogue: lane holds O[head 4gq+i][dim 16nt+col]
   if (S == 1) {
@@ -236,22 +282,38 @@ __global__ __launch_bounds__(64 * NW) void k_attend(AttendArgs a) {
 }
 
 // Merge split partials: out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s.
+// A workgroup per (query, head); every partial load is issued up front.
 __global__ __launch_bounds__(128) void k_attend_combine(AttendArgs a) {
   const int q = blockIdx.x / a.heads, h = blockIdx.x % a.heads;
   const int S = a.splits, H = a.heads;
-  float M = -__builtin_inff();
-  for (int s = 0; s < S; ++s) M = fmaxf(M, a.part_ml[(((int64_t)q * S + s) * H + h) * 2]);
-  float den = 0.0f;
-  float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
   const int d0 = threadIdx.x * 4;
+  float ms[kAttendMaxSplits], ls[kAttendMaxSplits];
+  v4f os[kAttendMaxSplits];
+#pragma unroll
+  for (int s = 0; s < kAttendMaxSplits; ++s) {
+    ms[s] = -__builtin_inff();
+    ls[s] = 0.0f;
+    os[s] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    if (s < S) {
+      const int64_t r = ((int64_t)q * S + s) * H + h;
+      const v2f ml = *reinterpret_cast<const v2f*>(a.part_ml + r * 2);
+      ms[s] = ml[0];
+      ls[s] = ml[1];
+      os[s] = *reinterpret_cast<const v4f*>(a.part_o + r * kLatent + d0);
+    }
+  }
+  float M = ms[0];
+#pragma unroll
+  for (int s = 1; s < kAttendMaxSplits; ++s) M = fmaxf(M, ms[s]);
+  float den = 0.0f;
+  v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
   if (M != -__builtin_inff()) {
-    for (int s = 0; s < S; ++s) {
-      const float* pm = a.part_ml + (((int64_t)q * S + s) * H + h) * 2;
-      if (pm[1] == 0.0f) continue;
-      const float wgt = exp2f(pm[0] - M);
-      den += wgt * pm[1];
-      const v4f ov = *reinterpret_cast<const v4f*>(a.part_o + (((int64_t)q * S + s) * H + h) * kLatent + d0);
-      for (int k = 0; k < 4; ++k) acc[k] += wgt * ov[k];
+#pragma unroll
+    for (int s = 0; s < kAttendMaxSplits; ++s) {
+      const float wgt = ls[s] > 0.0f ? exp2f(ms[s] - M) : 0.0f;
+      den += wgt * ls[s];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) acc[k] += wgt * os[s][k];
     }
   }
   const float inv = den > 0.0f ? 1.0f / den : 0.0f;
@@ -261,29 +323,14 @@ __global__ __launch_bounds__(128) void k_attend_combine(AttendArgs a) {
     a.lse[(int64_t)q * H + h] = den > 0.0f ? (M + log2f(den)) * 0.69314718055994531f : -__builtin_inff();
 }
 
-template <int NW>
-hipError_t launch_nw(const AttendArgs& a, hipStream_t s) {
-  const dim3 grid((unsigned)(a.n_q * a.head_groups * a.splits)), block(64 * NW);
-  hipLaunchKernelGGL((k_attend<NW>), grid, block, 0, s, a);
+}  // namespace
+
+hipError_t launch_attend(const AttendArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(k_attend, dim3((unsigned)(a.n_q * a.head_groups * a.splits)), dim3(kNT), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.splits == 1) return e;
   hipLaunchKernelGGL(k_attend_combine, dim3((unsigned)(a.n_q * a.heads)), dim3(128), 0, s, a);
   return hipGetLastError();
-}
-
-}  // namespace
-
-int attend_waves(int heads) {
-  const int t = heads / 16;
-  return t % 4 == 0 ? 4 : (t % 2 == 0 ? 2 : 1);
-}
-
-hipError_t launch_attend(const AttendArgs& a, hipStream_t s) {
-  switch (a.heads / a.head_groups / 16) {
-    case 4: return launch_nw<4>(a, s);
-    case 2: return launch_nw<2>(a, s);
-    default: return launch_nw<1>(a, s);
-  }
 }
 
 }  // namespace csa2

@@ -39,8 +39,8 @@ struct ReindexArgs {
   const int32_t* pool_blocks;
   const int32_t* pool_count;
   int n_q, hi, d, swa, pool, topk;
-  int split;                 // workgroups per query in the scoring kernel
-  float* scores;             // workspace [n_q, 8 * pool]
+  int split;                 // scoring workgroups per query
+  uint32_t* keys;            // workspace [n_q, 8 * pool]: order keys, 0 = empty
   int32_t* topk_pos;
   int32_t* topk_count;
   float* topk_scores;        // optional
@@ -76,15 +76,16 @@ hipError_t launch_scan(const ScanArgs& a, hipStream_t s);
 hipError_t launch_pool_select(const PoolArgs& a, hipStream_t s);
 hipError_t launch_reindex(const ReindexArgs& a, hipStream_t s);
 hipError_t launch_attend(const AttendArgs& a, hipStream_t s);
-int attend_waves(int heads);   // waves (16 heads each) per attention workgroup
 
 // Tiling constants the host needs for grids and workspace sizes.
 constexpr int kHistShift = 20;         // coarse histogram: top 12 bits of a key
 constexpr int kHistBins = 1 << (32 - kHistShift);
 constexpr int kScanTile = 2048;        // default positions per scan workgroup
-constexpr int kScanPrefetch = 6;       // default LDS ring slots per wave
+constexpr int kScanPrefetch = 4;       // default LDS ring slots per wave
 constexpr int kAttendTile = 32;        // entries per attention tile
-constexpr int kReindexSplit = 16;      // scoring workgroups per query
+constexpr int kAttendWaves = 4;        // waves per attention workgroup (16 heads each)
+constexpr int kAttendMaxSplits = 16;   // entry-list splits per query, at most
+constexpr int kReindexBlocks = 32;     // pool blocks per Reindex scoring workgroup
 constexpr int kMaxVisible = 1 << 21;   // bound of n_visible
 constexpr int kMaxBlocks = kMaxVisible / 8;
 

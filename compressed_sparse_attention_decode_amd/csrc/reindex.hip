@@ -8,15 +8,19 @@
 // gathered).  Ties go to the lower position; output is ascending.
 //
 // Two kernels:
-//  * k_reindex_score: split x n_q workgroups; a wave step scores two pool
-//    blocks (16 positions, two contiguous 1 KiB key runs at d = 128) with the
-//    same f16-MFMA contraction as the Full scan and writes fp32 scores;
-//  * k_topk_select: one 1024-thread workgroup per query holds the <= 16,384
-//    order-preserving keys in LDS, finds the K-th largest with a radix select
-//    that starts at the highest bit where the smallest and largest key differ
-//    (the common leading bits would pile every key onto one counter), and
-//    compacts in pool order (= ascending positions), admitting keys equal to
-//    the threshold lowest position first.
+//  * k_reindex_score: one workgroup per 32 pool blocks of a query; a wave
+//    step scores two pool blocks (16 positions, two contiguous key runs) with
+//    the same f16-MFMA contraction as the Full scan.  Every key load of the
+//    workgroup is issued before the first contraction (the kernel is short
+//    and latency-bound).  Scores are written as order-preserving uint32 keys,
+//    0 marking a slot that holds no candidate position;
+//  * k_topk_select: one 1024-thread workgroup per query keeps its <= 16,384
+//    keys in registers (16 consecutive pool slots per thread), finds the K-th
+//    largest with a radix select of up to 11-bit digits starting at the
+//    highest bit where the smallest and largest key differ (common leading
+//    bits would pile every key onto one counter), and compacts in pool order
+//    (= ascending positions), admitting keys equal to the threshold lowest
+//    position first.
 #include "common.h"
 #include "internal.h"
 #include "select_common.h"
@@ -27,24 +31,46 @@ namespace {
 template <int D, int HT>
 __global__ __launch_bounds__(256) void k_reindex_score(ReindexArgs a) {
   constexpr int KC = D / 32;
-  constexpr int LB = D / 4;
+  constexpr int LB = D / 4;                 // key bytes per lane per position
+  constexpr int SPW = kReindexBlocks / 8;   // wave steps (2 blocks each) per wave
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int gq = lane >> 4, col = lane & 15;
   const int q = blockIdx.x / a.split, part = blockIdx.x % a.split;
   const int cnt = a.pool_count[q];
-  const int per = ((a.pool + a.split - 1) / a.split + 1) & ~1;   // even: 2 blocks per step
-  const int i_begin = part * per;
-  const int i_end = min(cnt, i_begin + per);
+  const int i_begin = part * kReindexBlocks;
+  const int i_end = min(cnt, i_begin + kReindexBlocks);
   if (i_begin >= i_end) return;
-  const int nsteps = (i_end - i_begin + 1) >> 1;
   const int n = a.n_visible[q];
   const int c = max(0, n - a.swa);
+  const int32_t* pool = a.pool_blocks + (int64_t)q * a.pool;
 
+  // pool entries of this wave's steps (step s covers pool slots
+  // i_begin + 2s, +1; lane col>>3 picks the slot, col&7 the position)
+  int pos[SPW];
+#pragma unroll
+  for (int u = 0; u < SPW; ++u) {
+    const int i = i_begin + 2 * (wave + 4 * u) + (col >> 3);
+    pos[u] = i < i_end ? pool[i] * kBlock + (col & 7) : c;
+  }
+  // every key load in flight at once (a position >= c reads zeros)
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.idx_k + a.seq_base[q] * D, (uint32_t)c * D);
+  uint32_t kb[SPW][LB / 4];
+#pragma unroll
+  for (int u = 0; u < SPW; ++u) {
+    if (pos[u] > c || pos[u] < 0) pos[u] = c;
+    const uint32_t off = (uint32_t)pos[u] * D + gq * LB;
+    const v4u x = buf_load16(rk, off);
+    kb[u][0] = x[0]; kb[u][1] = x[1]; kb[u][2] = x[2]; kb[u][3] = x[3];
+    if constexpr (LB == 32) {
+      const v4u y = buf_load16(rk, off + 16);
+      kb[u][4] = y[0]; kb[u][5] = y[1]; kb[u][6] = y[2]; kb[u][7] = y[3];
+    }
+  }
+
+  // query fragments: loads from clamped (valid) rows, padded heads zeroed
   v8h qf[HT][KC];
   float wv[HT][4];
   const uint8_t* qp = a.idx_q + (int64_t)q * a.hi * D;
-  // all loads issued back to back from clamped (valid) rows, padded heads
-  // zeroed afterwards: no branch, one wait
   uint32_t qraw[HT][KC][2];
 #pragma unroll
   for (int t = 0; t < HT; ++t) {
@@ -66,36 +92,15 @@ __global__ __launch_bounds__(256) void k_reindex_score(ReindexArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) wv[t][i] = t * 16 + gq * 4 + i < a.hi ? wv[t][i] : 0.0f;
   }
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.idx_k + a.seq_base[q] * D, (uint32_t)c * D);
-  const int32_t* pool = a.pool_blocks + (int64_t)q * a.pool;
-  float* sc = a.scores + (int64_t)q * a.pool * kBlock;
 
-  auto load = [&](int s, uint32_t* kb, int* pos_out) {
-    const int i = i_begin + 2 * s + (col >> 3);
-    int pos = c;                                   // past the end: reads zero
-    if (i < i_end) pos = pool[i] * kBlock + (col & 7);
-    if (pos > c || pos < 0) pos = c;
-    *pos_out = pos;
-    const uint32_t off = (uint32_t)pos * D + gq * LB;
-    v4u x = buf_load16(rk, off);
-    kb[0] = x[0]; kb[1] = x[1]; kb[2] = x[2]; kb[3] = x[3];
-    if constexpr (LB == 32) {
-      v4u y = buf_load16(rk, off + 16);
-      kb[4] = y[0]; kb[5] = y[1]; kb[6] = y[2]; kb[7] = y[3];
-    }
-  };
-
-  uint32_t kb[LB / 4];
-  int pos = 0;
-  if (wave < nsteps) load(wave, kb, &pos);
-  for (int s = wave; s < nsteps; s += 4) {
-    uint32_t nx[LB / 4];
-    int npos = 0;
-    const bool more = s + 4 < nsteps;
-    if (more) load(s + 4, nx, &npos);
+  uint32_t* ks = a.keys + (int64_t)q * a.pool * kBlock;
+#pragma unroll
+  for (int u = 0; u < SPW; ++u) {
+    const int i = i_begin + 2 * (wave + 4 * u) + (col >> 3);
+    if (i_begin + 2 * (wave + 4 * u) >= i_end) break;              // wave-uniform
     v8h kf[KC];
 #pragma unroll
-    for (int kc = 0; kc < KC; ++kc) kf[kc] = fp8x8_to_v8h(kb[2 * kc], kb[2 * kc + 1]);
+    for (int kc = 0; kc < KC; ++kc) kf[kc] = fp8x8_to_v8h(kb[u][2 * kc], kb[u][2 * kc + 1]);
     float sum = 0.0f;
 #pragma unroll
     for (int t = 0; t < HT; ++t) {
@@ -106,56 +111,46 @@ __global__ __launch_bounds__(256) void k_reindex_score(ReindexArgs a) {
       for (int i = 0; i < 4; ++i) sum += wv[t][i] * fmaxf(acc[i], 0.0f);
     }
     sum = sum_rows4(sum);
-    const int i = i_begin + 2 * s + (col >> 3);
-    if (gq == 0 && i < i_end) sc[i * kBlock + (col & 7)] = pos < c ? sum : -__builtin_inff();
-    if (more) {
-#pragma unroll
-      for (int k = 0; k < LB / 4; ++k) kb[k] = nx[k];
-      pos = npos;
-    }
+    // order-preserving key; 0 marks a slot with no candidate position
+    if (gq == 0 && i < i_end) ks[i * kBlock + (col & 7)] = pos[u] < c ? order_key(sum) : 0u;
   }
 }
 
 constexpr int kTkThreads = 1024;
 constexpr int kMaxCand = 2048 * kBlock;
-constexpr int kPer = kMaxCand / kTkThreads;        // 16 items per thread
-
-// LDS slot of item i: one pad word per 16 so that a thread's contiguous run
-// and the strided (coalesced) load pattern are both free of bank conflicts.
-__device__ __forceinline__ int kslot(int i) { return i + (i >> 4); }
+constexpr int kPer = kMaxCand / kTkThreads;        // 16 keys per thread, in registers
+constexpr int kTkBins = 2048;                      // radix digit: up to 11 bits
 
 __global__ __launch_bounds__(kTkThreads) void k_topk_select(ReindexArgs a) {
-  __shared__ uint32_t s_key[kMaxCand + kMaxCand / 16];
-  __shared__ uint32_t s_hist[256];
+  __shared__ uint32_t s_hist[kTkBins];
   __shared__ uint32_t s_scan[kTkThreads / 64 + 1];
   __shared__ uint32_t s_misc[4];
 
   const int q = blockIdx.x, tid = threadIdx.x;
-  const int cnt = a.pool_count[q];
-  const int N = cnt * kBlock;
-  const int n = a.n_visible[q];
-  const int c = max(0, n - a.swa);
+  const int N = a.pool_count[q] * kBlock;
   const int K = a.topk;
   const int32_t* pool = a.pool_blocks + (int64_t)q * a.pool;
-  const float* sc = a.scores + (int64_t)q * a.pool * kBlock;
+  const uint32_t* ks = a.keys + (int64_t)q * a.pool * kBlock;
   int32_t* out = a.topk_pos + (int64_t)q * K;
   float* out_s = a.topk_scores ? a.topk_scores + (int64_t)q * K : nullptr;
 
-  // keys in pool order (= ascending positions), coalesced loads; invalid -> 0
+  // thread t holds slots [16t, 16t + 16) (pool order = ascending positions);
+  // N is a multiple of 8, so each 4-key vector is wholly valid or not
+  uint32_t key[kPer];
+#pragma unroll
+  for (int v = 0; v < kPer / 4; ++v) {
+    const int i = tid * kPer + v * 4;
+    const v4u x = i < N ? *reinterpret_cast<const v4u*>(ks + i) : v4u{0u, 0u, 0u, 0u};
+    key[4 * v] = x[0]; key[4 * v + 1] = x[1]; key[4 * v + 2] = x[2]; key[4 * v + 3] = x[3];
+  }
   uint32_t nvalid = 0, lo = 0xFFFFFFFFu, hi = 0;
+#pragma unroll
   for (int k = 0; k < kPer; ++k) {
-    const int i = k * kTkThreads + tid;
-    uint32_t key = 0;
-    if (i < N) {
-      const int pos = pool[i >> 3] * kBlock + (i & 7);
-      if (pos >= 0 && pos < c) {
-        key = order_key(sc[i]);
-        ++nvalid;
-        lo = min(lo, key);
-        hi = max(hi, key);
-      }
+    if (key[k] != 0) {
+      ++nvalid;
+      lo = min(lo, key[k]);
+      hi = max(hi, key[k]);
     }
-    s_key[kslot(i)] = key;
   }
   uint32_t total;
   (void)block_exclusive_scan<kTkThreads>(nvalid, s_scan, &total);
@@ -163,57 +158,72 @@ __global__ __launch_bounds__(kTkThreads) void k_topk_select(ReindexArgs a) {
   const uint32_t kmin = block_min_u32<kTkThreads>(lo, s_scan);
   const uint32_t kmax = block_max_u32<kTkThreads>(hi, s_scan);
 
-  uint32_t T = 0, need_eq = 0;
+  // Radix select of the keff-th largest key, from the highest bit where the
+  // smallest and largest keys differ.  Stops early when the crossing digit's
+  // keys are all taken: then every key >= that digit's smallest value is in.
+  int64_t T = 0;              // keys > T are taken ...
+  uint32_t need_eq = 0;       // ... plus need_eq keys == T, lowest slots first
   if (keff > 0) {
     const int top = highest_diff_bit(kmin, kmax);
     uint32_t prefix = (uint32_t)(((uint64_t)kmin >> (top + 1)) << (top + 1));
     uint32_t need = keff;
     int fixed_lo = top + 1;            // bits >= fixed_lo are decided
+    bool whole = false;
     while (fixed_lo > 0) {
-      const int sh = max(0, fixed_lo - 8);
+      const int sh = max(0, fixed_lo - 11);
       const uint32_t dmask = (1u << (fixed_lo - sh)) - 1;
-      if (tid < 256) s_hist[tid] = 0;
+      const int nbins = max(64, (int)dmask + 1);
+      for (int i = tid; i < nbins; i += kTkThreads) s_hist[i] = 0;
       __syncthreads();
+#pragma unroll
       for (int k = 0; k < kPer; ++k) {
-        const uint32_t key = s_key[kslot(tid * kPer + k)];
-        if (key != 0 && ((uint64_t)key >> fixed_lo) == ((uint64_t)prefix >> fixed_lo))
-          atomicAdd(&s_hist[(key >> sh) & dmask], 1u);
+        if (key[k] != 0 && ((uint64_t)key[k] >> fixed_lo) == ((uint64_t)prefix >> fixed_lo))
+          atomicAdd(&s_hist[(key[k] >> sh) & dmask], 1u);
       }
       __syncthreads();
-      find_crossing(s_hist, 256, need, s_misc);
+      find_crossing(s_hist, nbins, need, s_misc);
       __syncthreads();
-      prefix |= s_misc[0] << sh;
-      need -= s_misc[1];
+      const uint32_t bin = s_misc[0], above = s_misc[1];
+      const uint32_t in_bin = s_hist[bin];
+      prefix |= bin << sh;
+      need -= above;
       fixed_lo = sh;
       __syncthreads();
+      if (need == in_bin) { whole = true; break; }
     }
-    T = prefix;
-    need_eq = need;
+    if (whole) {
+      T = (int64_t)prefix - 1;         // prefix: smallest key value of the crossing digit
+      need_eq = 0;
+    } else {
+      T = (int64_t)prefix;
+      need_eq = need;
+    }
   }
 
-  // ordered compaction: key > T always, key == T lowest positions first
+  // ordered compaction
   uint32_t eq = 0;
   if (keff > 0) {
-    for (int k = 0; k < kPer; ++k) eq += s_key[kslot(tid * kPer + k)] == T;
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) eq += key[k] != 0 && (int64_t)key[k] == T;
   }
   uint32_t eq_before = block_exclusive_scan<kTkThreads>(eq, s_scan, &total);
-  uint32_t take = 0;
-  uint32_t flags = 0;
+  uint32_t take = 0, flags = 0;
   if (keff > 0) {
+#pragma unroll
     for (int k = 0; k < kPer; ++k) {
-      const uint32_t key = s_key[kslot(tid * kPer + k)];
-      bool sel = key > T;
-      if (key == T && eq_before < need_eq) { sel = true; ++eq_before; }
+      bool sel = key[k] != 0 && (int64_t)key[k] > T;
+      if (key[k] != 0 && (int64_t)key[k] == T && eq_before < need_eq) { sel = true; ++eq_before; }
       if (sel) { flags |= 1u << k; ++take; }
     }
   }
   uint32_t before = block_exclusive_scan<kTkThreads>(take, s_scan, &total);
+#pragma unroll
   for (int k = 0; k < kPer; ++k) {
     if (flags & (1u << k)) {
       const int i = tid * kPer + k;
       if (before < (uint32_t)K) {
         out[before] = pool[i >> 3] * kBlock + (i & 7);
-        if (out_s) out_s[before] = key_float(s_key[kslot(i)]);
+        if (out_s) out_s[before] = key_float(key[k]);
       }
       ++before;
     }

@@ -39,6 +39,31 @@ __device__ __forceinline__ bool same_above(uint32_t a, uint32_t b, int lo) {
   return ((uint64_t)a >> lo) == ((uint64_t)b >> lo);
 }
 
+// One pass over a query's block scores, 16-byte loads issued kU at a time
+// (kU x 4 blocks per thread in flight).  f(jb0, key[4], valid-mask) sees
+// blocks jb0 .. jb0+3; blocks >= nb are passed with their mask bit clear.
+constexpr int kU = 8;
+template <typename F>
+__device__ __forceinline__ void sweep(const float* bs, int nb, F&& f) {
+  const int tid = threadIdx.x;
+  for (int base = 0; base < nb; base += kSelThreads * 4 * kU) {
+    v4f x[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int jb0 = base + (u * kSelThreads + tid) * 4;
+      x[u] = jb0 < nb ? *reinterpret_cast<const v4f*>(bs + jb0) : v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int jb0 = base + (u * kSelThreads + tid) * 4;
+      const int left = nb - jb0;
+      const uint32_t vm = left >= 4 ? 15u : (left <= 0 ? 0u : (1u << left) - 1u);
+      const uint32_t k[4] = {order_key(x[u][0]), order_key(x[u][1]), order_key(x[u][2]), order_key(x[u][3])};
+      f(jb0, k, vm);
+    }
+  }
+}
+
 __global__ __launch_bounds__(kSelThreads) void k_pool_select(PoolArgs a) {
   __shared__ uint32_t s_hist[kHistBins];
   __shared__ uint32_t s_sel[kMaxWords];
@@ -50,7 +75,7 @@ __global__ __launch_bounds__(kSelThreads) void k_pool_select(PoolArgs a) {
   __shared__ uint32_t s_ccount;
 
   const int q = blockIdx.x;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
   const int n = a.n_visible[q];
   const int c = max(0, n - a.swa);
   const int nb = (c + 7) >> 3;
@@ -65,11 +90,12 @@ __global__ __launch_bounds__(kSelThreads) void k_pool_select(PoolArgs a) {
 
   // 1. key range
   uint32_t lo = 0xFFFFFFFFu, hi = 0;
-  for (int jb = tid; jb < nb; jb += kSelThreads) {
-    const uint32_t k = order_key(bs[jb]);
-    lo = min(lo, k);
-    hi = max(hi, k);
-  }
+  sweep(bs, nb, [&](int, const uint32_t* k, uint32_t vm) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (vm >> e & 1u) { lo = min(lo, k[e]); hi = max(hi, k[e]); }
+    }
+  });
   const uint32_t kmin = block_min_u32<kSelThreads>(lo, s_scan);
   const uint32_t kmax = block_max_u32<kSelThreads>(hi, s_scan);
   const int top = highest_diff_bit(kmin, kmax);          // -1: all keys equal
@@ -79,7 +105,11 @@ __global__ __launch_bounds__(kSelThreads) void k_pool_select(PoolArgs a) {
   // 2. coarse histogram and the bin b* of the P-th best block
   for (int i = tid; i < kHistBins; i += kSelThreads) s_hist[i] = 0;
   __syncthreads();
-  for (int jb = tid; jb < nb; jb += kSelThreads) atomicAdd(&s_hist[(order_key(bs[jb]) >> cs) & cmask], 1u);
+  sweep(bs, nb, [&](int, const uint32_t* k, uint32_t vm) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (vm >> e & 1u) atomicAdd(&s_hist[(k[e] >> cs) & cmask], 1u);
+  });
   __syncthreads();
   constexpr int kPer = kHistBins / kSelThreads;
   uint32_t local = 0, cnt[kPer];
@@ -100,34 +130,48 @@ __global__ __launch_bounds__(kSelThreads) void k_pool_select(PoolArgs a) {
     }
   }
   const int nw = (nb + 31) >> 5;
-  for (int w = tid; w < nw; w += kSelThreads) { s_sel[w] = 0; s_tie[w] = 0; }
+  for (int w = tid; w < nw; w += kSelThreads) s_tie[w] = 0;
   if (tid == 0) s_ccount = 0;
   __syncthreads();
   const uint32_t bstar = s_misc[0];
   uint32_t need = (uint32_t)P - s_misc[1];
 
-  // 3. mark blocks above b*, collect the blocks of bin b*
-  for (int base = 0; base < nb; base += kSelThreads) {
-    const int jb = base + tid;
-    const uint32_t key = jb < nb ? order_key(bs[jb]) : 0u;
-    const uint32_t bin = (key >> cs) & cmask;
-    const bool hib = jb < nb && bin > bstar;
-    const bool cand = jb < nb && bin == bstar;
-    const uint64_t mhi = __ballot(hib);
-    const uint64_t mc = __ballot(cand);
-    if (lane == 0) {
-      const int w0 = (base + wave * 64) >> 5;
-      s_sel[w0] = (uint32_t)mhi;
-      s_sel[w0 + 1] = (uint32_t)(mhi >> 32);
+  // 3. mark blocks above b* (a lane's 4 blocks form one nibble of the
+  //    bitmap; 8 lanes OR their nibbles into a word), collect bin b*
+  sweep(bs, nb, [&](int jb0, const uint32_t* k, uint32_t vm) {
+    uint32_t hib = 0, cand = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t bin = (k[e] >> cs) & cmask;
+      hib |= (uint32_t)((vm >> e & 1u) && bin > bstar) << e;
+      cand |= (uint32_t)((vm >> e & 1u) && bin == bstar) << e;
     }
+    uint32_t word = hib << (4 * (lane & 7));
+    word |= __shfl_xor(word, 1, 64);
+    word |= __shfl_xor(word, 2, 64);
+    word |= __shfl_xor(word, 4, 64);
+    if ((lane & 7) == 0 && jb0 < nb) s_sel[jb0 >> 5] = word;
+    // candidates: slot = wave base + per-element ballot prefixes
+    uint64_t m[4];
+    uint32_t tot = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      m[e] = __ballot(cand >> e & 1u);
+      tot += (uint32_t)__popcll(m[e]);
+    }
+    if (tot == 0) return;
     uint32_t slot0 = 0;
-    if (lane == 0 && mc) slot0 = atomicAdd(&s_ccount, (uint32_t)__popcll(mc));
+    if (lane == 0) slot0 = atomicAdd(&s_ccount, tot);
     slot0 = __shfl(slot0, 0, 64);
-    if (cand) {
-      const uint32_t slot = slot0 + lane_prefix(mc);
-      if (slot < kCandCap) { s_ckey[slot] = key; s_cj[slot] = jb; }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (cand >> e & 1u) {
+        const uint32_t slot = slot0 + lane_prefix(m[e]);
+        if (slot < kCandCap) { s_ckey[slot] = k[e]; s_cj[slot] = jb0 + e; }
+      }
+      slot0 += (uint32_t)__popcll(m[e]);
     }
-  }
+  });
   __syncthreads();
   const uint32_t C = s_ccount;
   const bool in_lds = C <= (uint32_t)kCandCap;

@@ -140,9 +140,10 @@ csa2_status csa2_encode_kv(int64_t n, const uint16_t* latent, const uint16_t* ro
  *   b_j = max of s_p over p in [8j, min(8j+8, c)),  j < nb = ceil(c / 8)
  *   idx_q        fp8 [n_q, H_i, d_i]      idx_w  float [n_q, H_i]
  *   idx_k        fp8 [rows, d_i]  (one key per position, shared by heads)
- *   block_scores float [n_q, ld_block_scores]: b_j written for j < nb;
- *                entries at j >= nb are left untouched;
- *                ld_block_scores >= ceil((max_visible - W) / 8).
+ *   block_scores float [n_q, ld_block_scores], 16-byte aligned: b_j
+ *                written for j < nb; entries at j >= nb are left untouched;
+ *                ld_block_scores >= ceil((max_visible - W) / 8) and a
+ *                multiple of 4.
  * One kernel, no workspace.  Queries with n <= W write nothing. */
 csa2_status csa2_index_scan(const csa2_dims* dims, const csa2_queries* q,
                             const uint8_t* idx_q, const float* idx_w, const uint8_t* idx_k,
@@ -151,7 +152,8 @@ csa2_status csa2_index_scan(const csa2_dims* dims, const csa2_queries* q,
 /* Full-mode indexer, stage 2 of 2: the candidate pool ([atlas] §3.2: the
  * Top-2048 blocks of 8 form the pool).  pool = the min(P, nb) blocks with the
  * largest b_j, ties to the lower j, written in ascending block order.
- *   block_scores as written by csa2_index_scan
+ *   block_scores as written by csa2_index_scan (same alignment and
+ *                ld_block_scores rules)
  *   pool_blocks  int32 [n_q, P]  ascending block ids, -1 after pool_count
  *   pool_count   int32 [n_q]     (0 for queries with n <= W)
  * One kernel, no workspace. */
