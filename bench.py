@@ -133,6 +133,7 @@ class Step:
         self.tc = torch.empty(len(self.layers), n_q, dtype=torch.int32, device=dev)
         self.out = torch.empty(len(self.layers), n_q, w.dims.n_heads, 512, dtype=torch.float32, device=dev)
         self.lse = torch.empty(len(self.layers), n_q, w.dims.n_heads, dtype=torch.float32, device=dev)
+        self.ws_p = torch.empty(csa2.workspace_pool(st.dims, st.batch) + 256, dtype=torch.uint8, device=dev)
         self.ws_r = torch.empty(csa2.workspace_reindex(st.dims, st.batch) + 256, dtype=torch.uint8, device=dev)
         self.ws_a = torch.empty(csa2.workspace_attend(st.dims, st.batch) + 256, dtype=torch.uint8, device=dev)
         for layer in [0] + self.layers:
@@ -155,8 +156,11 @@ class Step:
             if w.fresh_encode:
                 seq.append(("encode", csa2.encode_kv(self.enc_lat, self.enc_rope, *self.enc_planes, prepare=True)))
             q0, w0 = st.iq(0)
-            seq.append(("scan", csa2.index_scan(st.dims, st.batch, q0, w0, idx_k, self.bs, prepare=True)))
-            seq.append(("pool", csa2.index_pool(st.dims, st.batch, self.bs, self.pool, self.pcnt, prepare=True)))
+            # csa2_index_full's two stages, issued separately to time each
+            seq.append(("scan", csa2.index_scan(st.dims, st.batch, q0, w0, idx_k, self.bs, pool_ws=self.ws_p,
+                                                prepare=True)))
+            seq.append(("pool", csa2.index_pool(st.dims, st.batch, self.bs, self.pool, self.pcnt, ws=self.ws_p,
+                                                from_scan=True, prepare=True)))
             for i, layer in enumerate(self.layers):
                 q, wt = st.iq(layer)
                 seq.append(("reindex", csa2.index_reindex(st.dims, st.batch, q, wt, idx_k, self.pool, self.pcnt,
@@ -168,19 +172,10 @@ class Step:
                                                   lse=self.lse[i], ws=self.ws_a, prepare=True)))
             self.calls.append(seq)
 
-    def run(self, r: int, ev=None):
-        """One step on replica r.  `ev` (optional) maps stage -> (start, end)
-        event lists recorded around each stage."""
-        for name, call in self.calls[r]:
-            if ev is not None:
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                e0.record()
-                call()
-                e1.record()
-                ev.setdefault(name, ([], []))[0].append(e0)
-                ev[name][1].append(e1)
-            else:
-                call()
+    def run(self, r: int):
+        """One step on replica r."""
+        for _, call in self.calls[r]:
+            call()
 
 
 # ---------------------------------------------------------------- accounting
@@ -240,6 +235,31 @@ def measured_traffic(workload: str):
 
 
 # ---------------------------------------------------------------- GPU timing
+def _spin_rate() -> float:
+    """Seconds per torch.cuda._sleep cycle."""
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    torch.cuda._sleep(1_000_000)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e-3 / 1_000_000
+
+
+def _timed(launch, n: int, spin_s_per_cycle: float, issue_s: float) -> float:
+    """GPU milliseconds of n back-to-back launch(i) calls.  A bounded spin
+    (at most 2 s) holds the GPU while the host queues every launch, so the
+    events bracket GPU time, not the Python issue rate."""
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    torch.cuda._sleep(int(min(4.0 * issue_s, 2.0) / spin_s_per_cycle))
+    t0.record()
+    for i in range(n):
+        launch(i)
+    t1.record()
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1)
+
+
 def measure(w: wl.Workload, steps: int, warmup: int, replicas: int):
     per_step = scan_bytes(w)
     if replicas <= 0:
@@ -249,35 +269,35 @@ def measure(w: wl.Workload, steps: int, warmup: int, replicas: int):
     for i in range(warmup):
         step.run(i % replicas)
     torch.cuda.synchronize()
-    # calibrate the spin: enough to cover the host's issue time for all steps
+    rate = _spin_rate()
     t0 = time.perf_counter()
     for i in range(min(steps, 10)):
-        step.run(i % replicas, {})
+        step.run(i % replicas)
     issue_s = (time.perf_counter() - t0) / min(steps, 10) * steps
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    torch.cuda._sleep(1_000_000)
-    e1.record()
-    torch.cuda.synchronize()
-    per_cycle_s = e0.elapsed_time(e1) * 1e-3 / 1_000_000
-    sleep_cycles = min(4.0 * issue_s, 2.0) / per_cycle_s    # at most 2 s of spin
-    ev = {}
-    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
+
+    # whole steps: no event inside a step (recording one drains the queue)
     wall0 = time.perf_counter()
-    # hold the GPU briefly (a bounded spin) while the host queues every step,
-    # so the timed region measures GPU time, not the Python issue rate
-    torch.cuda._sleep(int(sleep_cycles))
-    t_start.record()
-    for i in range(steps):
-        step.run(i % replicas, ev)
-    t_end.record()
-    torch.cuda.synchronize()
+    total_ms = _timed(lambda i: step.run(i % replicas), steps, rate, issue_s)
     wall = time.perf_counter() - wall0
-    total_ms = t_start.elapsed_time(t_end)
-    stages = {k: sum(a.elapsed_time(b) for a, b in zip(*v)) / len(v[0]) * 1e3 for k, v in ev.items()}
     ms = total_ms / steps
+
+    # per stage: the stage's launches of `steps` steps back to back (every
+    # stage reads inputs the previous stages left and rewrites the same
+    # outputs, so repeating it is the same work), one event pair per stage
+    stages = {}
+    names = []
+    for name, _ in step.calls[0]:
+        if name not in names:
+            names.append(name)
+    for name in names:
+        per_r = [[c for n, c in step.calls[r] if n == name] for r in range(replicas)]
+        k = len(per_r[0])
+
+        def launch(i, per_r=per_r):
+            for c in per_r[i % replicas]:
+                c()
+        stages[name] = _timed(launch, steps, rate, issue_s) / (steps * k) * 1e3
     scan_us = stages["scan"]
     achieved = per_step / (scan_us * 1e-6) / 1e9
     res = {

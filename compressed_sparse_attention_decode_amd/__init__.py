@@ -20,7 +20,7 @@ from typing import Optional, Tuple
 import torch
 
 __all__ = ["Dims", "Batch", "Csa2Error", "lib", "lib_path", "encode_kv", "index_full",
-           "index_scan", "index_pool", "n_blocks", "block_scores_ld",
+           "index_scan", "index_pool", "n_blocks", "block_scores_ld", "workspace_pool",
            "index_reindex", "attend", "workspace_full", "workspace_reindex",
            "workspace_attend", "abi_version", "Call"]
 
@@ -62,8 +62,9 @@ def lib() -> ctypes.CDLL:
             "csa2_status_string": (ctypes.c_char_p, [I32]),
             "csa2_last_error": (ctypes.c_char_p, []),
             "csa2_encode_kv": (I32, [I64, P, P, P, P, P, P, P]),
-            "csa2_index_scan": (I32, [PD, PQ, P, P, P, P, I64, P]),
-            "csa2_index_pool": (I32, [PD, PQ, P, I64, P, P, P]),
+            "csa2_index_scan": (I32, [PD, PQ, P, P, P, P, I64, P, SZ, P]),
+            "csa2_index_pool_workspace_size": (I32, [PD, PQ, ctypes.POINTER(SZ)]),
+            "csa2_index_pool": (I32, [PD, PQ, P, I64, P, P, P, SZ, I32, P]),
             "csa2_index_full_workspace_size": (I32, [PD, PQ, ctypes.POINTER(SZ)]),
             "csa2_index_full": (I32, [PD, PQ, P, P, P, P, P, P, I64, P, SZ, P]),
             "csa2_index_reindex_workspace_size": (I32, [PD, PQ, ctypes.POINTER(SZ)]),
@@ -175,6 +176,10 @@ def workspace_full(dims: Dims, b: Batch) -> int:
     return _ws_size(lib().csa2_index_full_workspace_size, dims, b)
 
 
+def workspace_pool(dims: Dims, b: Batch) -> int:
+    return _ws_size(lib().csa2_index_pool_workspace_size, dims, b)
+
+
 def workspace_reindex(dims: Dims, b: Batch) -> int:
     return _ws_size(lib().csa2_index_reindex_workspace_size, dims, b)
 
@@ -276,39 +281,52 @@ def _check_idx(dims: Dims, b: Batch, idx_q, idx_w, idx_k):
         raise ValueError("idx_w must be float32 and idx_k [rows, d_i]")
 
 
+POOL_WS_FROM_SCAN = 1
+
+
 def index_scan(dims: Dims, b: Batch, idx_q: torch.Tensor, idx_w: torch.Tensor, idx_k: torch.Tensor,
-               block_scores: Optional[torch.Tensor] = None, prepare: bool = False):
-    """Full-mode scan: block scores float32 [n_q, ld] (b_j for j < nb)."""
+               block_scores: Optional[torch.Tensor] = None, pool_ws: Optional[torch.Tensor] = None,
+               prepare: bool = False):
+    """Full-mode scan: block scores float32 [n_q, ld] (b_j for j < nb).  With
+    `pool_ws` (a pool-select workspace) the scan also prepares it for an
+    index_pool(..., ws=pool_ws, from_scan=True) call on these scores."""
     dev = idx_k.device
-    _dev(idx_q, idx_w, idx_k, block_scores)
+    _dev(idx_q, idx_w, idx_k, block_scores, pool_ws)
     _check_idx(dims, b, idx_q, idx_w, idx_k)
     if block_scores is None:
         block_scores = torch.empty(b.n_q, block_scores_ld(dims, b), dtype=torch.float32, device=dev)
     if block_scores.dtype != torch.float32 or block_scores.dim() != 2 or block_scores.shape[0] != b.n_q:
         raise ValueError("block_scores must be float32 [n_q, ld]")
+    wp, wn = _ws_ptr(pool_ws)
     d, q = dims.c(), b.c()
     args = (ctypes.byref(d), ctypes.byref(q), idx_q.data_ptr(), idx_w.data_ptr(),
-            idx_k.data_ptr(), block_scores.data_ptr(), block_scores.shape[1], _stream(dev))
-    call = _issue(lib().csa2_index_scan, args, (d, q), prepare)
+            idx_k.data_ptr(), block_scores.data_ptr(), block_scores.shape[1], wp, wn, _stream(dev))
+    call = _issue(lib().csa2_index_scan, args, (d, q, pool_ws), prepare)
     return call if prepare else block_scores
 
 
 def index_pool(dims: Dims, b: Batch, block_scores: torch.Tensor,
                pool_blocks: Optional[torch.Tensor] = None, pool_count: Optional[torch.Tensor] = None,
-               prepare: bool = False):
-    """Top-P block pool from index_scan's block scores."""
+               ws: Optional[torch.Tensor] = None, from_scan: bool = False, prepare: bool = False):
+    """Top-P block pool from index_scan's block scores.  `from_scan`: `ws` was
+    passed to the index_scan call that wrote these scores."""
+    if from_scan and ws is None:
+        raise ValueError("from_scan needs the workspace that index_scan prepared")
     dev = block_scores.device
-    _dev(block_scores, pool_blocks, pool_count)
+    _dev(block_scores, pool_blocks, pool_count, ws)
     if block_scores.dtype != torch.float32 or block_scores.dim() != 2 or block_scores.shape[0] != b.n_q:
         raise ValueError("block_scores must be float32 [n_q, ld]")
     if pool_blocks is None:
         pool_blocks = torch.empty(b.n_q, dims.pool_blocks, dtype=torch.int32, device=dev)
     if pool_count is None:
         pool_count = torch.empty(b.n_q, dtype=torch.int32, device=dev)
+    ws = _workspace(workspace_pool(dims, b), dev, ws)
+    wp, wn = _ws_ptr(ws)
     d, q = dims.c(), b.c()
     args = (ctypes.byref(d), ctypes.byref(q), block_scores.data_ptr(), block_scores.shape[1],
-            pool_blocks.data_ptr(), pool_count.data_ptr(), _stream(dev))
-    call = _issue(lib().csa2_index_pool, args, (d, q), prepare)
+            pool_blocks.data_ptr(), pool_count.data_ptr(), wp, wn,
+            POOL_WS_FROM_SCAN if from_scan else 0, _stream(dev))
+    call = _issue(lib().csa2_index_pool, args, (d, q, ws), prepare)
     return call if prepare else (pool_blocks, pool_count)
 
 

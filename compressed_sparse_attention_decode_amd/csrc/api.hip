@@ -91,8 +91,38 @@ int64_t full_ldb(const csa2_dims* d, const csa2_queries* q) {
   return ((nb > 0 ? nb : 1) + 63) / 64 * 64;
 }
 
+int pool_chunks(const csa2_dims* d, const csa2_queries* q) {
+  const int64_t nb = max_blocks(d, q);
+  const int64_t g = (nb + kPoolChunk - 1) / kPoolChunk;
+  return g > 0 ? (int)g : 1;
+}
+
+// Positions per Full-scan workgroup (CSA2_SCAN_TILE overrides for tuning).
+int scan_tile() {
+  int tile = kScanTile;
+  if (const char* env = getenv("CSA2_SCAN_TILE")) tile = atoi(env);
+  if (tile < 64 || tile % 64 || tile > 4096) tile = kScanTile;
+  return tile;
+}
+
+int scan_tiles(const csa2_dims* d, const csa2_queries* q, int tile) {
+  return (int)((max_blocks(d, q) * 8 + tile - 1) / tile);
+}
+
+// (min, max) key pairs per query: one per pool chunk or one per scan tile
+int pool_mm_cap(const csa2_dims* d, const csa2_queries* q) {
+  const int t = scan_tiles(d, q, scan_tile()), g = pool_chunks(d, q);
+  return t > g ? t : g;
+}
+
+size_t pool_ws(const csa2_dims* d, const csa2_queries* q) {
+  return align256((size_t)q->n_q * pool_ws_words(pool_chunks(d, q), pool_mm_cap(d, q)) * 4);
+}
+
+// index_full workspace: the pool workspace, then block scores n_q x ldb f32
+// (used when the caller passes none)
 size_t full_ws(const csa2_dims* d, const csa2_queries* q) {
-  return align256((size_t)q->n_q * full_ldb(d, q) * 4);
+  return pool_ws(d, q) + align256((size_t)q->n_q * full_ldb(d, q) * 4);
 }
 
 size_t reindex_ws(const csa2_dims* d, const csa2_queries* q) {
@@ -182,55 +212,91 @@ csa2_status csa2_index_full_workspace_size(const csa2_dims* d, const csa2_querie
   return CSA2_OK;
 }
 
+csa2_status check_block_scores(const csa2_dims* d, const csa2_queries* q, const float* block_scores,
+                               int64_t ld_block_scores) {
+  const int64_t nb = max_blocks(d, q);
+  if (ld_block_scores < nb)
+    return fail(CSA2_ERR_INVALID_ARG, "ld_block_scores %lld < %lld blocks", (long long)ld_block_scores, (long long)nb);
+  if ((ld_block_scores & 3) || ((uintptr_t)block_scores & 15))
+    return fail(CSA2_ERR_INVALID_ARG, "block_scores must be 16-byte aligned with ld_block_scores a multiple of 4");
+  return CSA2_OK;
+}
+
+// The Full scan; with pool_ws it also leaves the per-tile key ranges and a
+// cleared histogram for the pool select.
+csa2_status run_scan(const csa2_dims* d, const csa2_queries* q, const uint8_t* idx_q, const float* idx_w,
+                     const uint8_t* idx_k, float* block_scores, int64_t ld_block_scores, uint32_t* pool_ws_ptr,
+                     void* stream) {
+  ScanArgs sa;
+  sa.idx_q = idx_q; sa.idx_w = idx_w; sa.idx_k = idx_k;
+  sa.seq_base = q->seq_base; sa.n_visible = q->n_visible;
+  sa.n_q = q->n_q; sa.hi = d->idx_heads; sa.d = d->idx_dim; sa.swa = d->swa; sa.g = q->tokens_per_seq;
+  int pf = kScanPrefetch;
+  if (const char* env = getenv("CSA2_SCAN_PREFETCH")) pf = atoi(env);
+  if (pf != 4 && pf != 6 && pf != 8) pf = kScanPrefetch;
+  sa.tile_pos = scan_tile();
+  sa.prefetch = pf;
+  sa.tiles = scan_tiles(d, q, sa.tile_pos);
+  sa.bscore = block_scores;
+  sa.ld = ld_block_scores;
+  sa.pool_ws = pool_ws_ptr;
+  sa.pool_ws_stride = pool_ws_words(pool_chunks(d, q), pool_mm_cap(d, q));
+  hipError_t e = launch_scan(sa, (hipStream_t)stream);
+  return e == hipSuccess ? CSA2_OK : hip_fail(e, "scan launch");
+}
+
+csa2_status run_pool(const csa2_dims* d, const csa2_queries* q, const float* block_scores, int64_t ld_block_scores,
+                     int32_t* pool_blocks, int32_t* pool_count, void* ws, bool after_scan, void* stream) {
+  PoolArgs pa;
+  pa.bscore = block_scores; pa.ld = ld_block_scores; pa.n_visible = q->n_visible;
+  pa.n_q = q->n_q; pa.swa = d->swa; pa.pool = d->pool_blocks;
+  pa.chunks = pool_chunks(d, q);
+  pa.mm_cap = pool_mm_cap(d, q);
+  pa.ws = (uint32_t*)ws;
+  pa.ws_stride = pool_ws_words(pa.chunks, pa.mm_cap);
+  pa.have_minmax = after_scan;
+  pa.mm_span = after_scan ? scan_tile() / 8 : kPoolChunk;
+  pa.pool_blocks = pool_blocks; pa.pool_count = pool_count;
+  hipError_t e = launch_pool_select(pa, (hipStream_t)stream);
+  return e == hipSuccess ? CSA2_OK : hip_fail(e, "pool select launch");
+}
+
 csa2_status csa2_index_scan(const csa2_dims* d, const csa2_queries* q, const uint8_t* idx_q, const float* idx_w,
-                            const uint8_t* idx_k, float* block_scores, int64_t ld_block_scores, void* stream) {
+                            const uint8_t* idx_k, float* block_scores, int64_t ld_block_scores, void* pool_wsp,
+                            size_t pool_ws_bytes, void* stream) {
   csa2_status st = check_dims(d);
   if (st) return st;
   if ((st = check_queries(q))) return st;
   if (!idx_q || !idx_w || !idx_k || !block_scores) return fail(CSA2_ERR_INVALID_ARG, "required pointer is NULL");
   if (((uintptr_t)idx_q | (uintptr_t)idx_k) & 15) return fail(CSA2_ERR_INVALID_ARG, "idx_q and idx_k must be 16-byte aligned");
-  const int64_t nb = max_blocks(d, q);
-  if (ld_block_scores < nb)
-    return fail(CSA2_ERR_INVALID_ARG, "ld_block_scores %lld < %lld blocks", (long long)ld_block_scores, (long long)nb);
-  if ((ld_block_scores & 3) || ((uintptr_t)block_scores & 15))
-    return fail(CSA2_ERR_INVALID_ARG, "block_scores must be 16-byte aligned with ld_block_scores a multiple of 4");
+  if ((st = check_block_scores(d, q, block_scores, ld_block_scores))) return st;
+  if (pool_wsp && (st = check_ws(pool_wsp, pool_ws_bytes, pool_ws(d, q)))) return st;
   if ((st = check_device())) return st;
-  ScanArgs sa;
-  sa.idx_q = idx_q; sa.idx_w = idx_w; sa.idx_k = idx_k;
-  sa.seq_base = q->seq_base; sa.n_visible = q->n_visible;
-  sa.n_q = q->n_q; sa.hi = d->idx_heads; sa.d = d->idx_dim; sa.swa = d->swa; sa.g = q->tokens_per_seq;
-  int tile = kScanTile, pf = kScanPrefetch;
-  if (const char* env = getenv("CSA2_SCAN_TILE")) tile = atoi(env);
-  if (const char* env = getenv("CSA2_SCAN_PREFETCH")) pf = atoi(env);
-  if (tile < 64 || tile % 64 || tile > 4096) tile = kScanTile;
-  if (pf != 4 && pf != 6 && pf != 8) pf = kScanPrefetch;
-  sa.tile_pos = tile;
-  sa.prefetch = pf;
-  sa.tiles = (int)((nb * 8 + tile - 1) / tile);
-  sa.bscore = block_scores;
-  sa.ld = ld_block_scores;
-  hipError_t e = launch_scan(sa, (hipStream_t)stream);
-  return e == hipSuccess ? CSA2_OK : hip_fail(e, "scan launch");
+  return run_scan(d, q, idx_q, idx_w, idx_k, block_scores, ld_block_scores, (uint32_t*)pool_wsp, stream);
+}
+
+csa2_status csa2_index_pool_workspace_size(const csa2_dims* d, const csa2_queries* q, size_t* bytes) {
+  csa2_status st = check_dims(d);
+  if (st) return st;
+  if ((st = check_queries(q))) return st;
+  if (!bytes) return fail(CSA2_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = pool_ws(d, q);
+  return CSA2_OK;
 }
 
 csa2_status csa2_index_pool(const csa2_dims* d, const csa2_queries* q, const float* block_scores,
-                            int64_t ld_block_scores, int32_t* pool_blocks, int32_t* pool_count, void* stream) {
+                            int64_t ld_block_scores, int32_t* pool_blocks, int32_t* pool_count, void* ws,
+                            size_t ws_bytes, int32_t flags, void* stream) {
   csa2_status st = check_dims(d);
   if (st) return st;
   if ((st = check_queries(q))) return st;
   if (!block_scores || !pool_blocks || !pool_count) return fail(CSA2_ERR_INVALID_ARG, "required pointer is NULL");
-  const int64_t nb = max_blocks(d, q);
-  if (ld_block_scores < nb)
-    return fail(CSA2_ERR_INVALID_ARG, "ld_block_scores %lld < %lld blocks", (long long)ld_block_scores, (long long)nb);
-  if ((ld_block_scores & 3) || ((uintptr_t)block_scores & 15))
-    return fail(CSA2_ERR_INVALID_ARG, "block_scores must be 16-byte aligned with ld_block_scores a multiple of 4");
+  if (flags & ~CSA2_POOL_WS_FROM_SCAN) return fail(CSA2_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
+  if ((st = check_block_scores(d, q, block_scores, ld_block_scores))) return st;
+  if ((st = check_ws(ws, ws_bytes, pool_ws(d, q)))) return st;
   if ((st = check_device())) return st;
-  PoolArgs pa;
-  pa.bscore = block_scores; pa.ld = ld_block_scores; pa.n_visible = q->n_visible;
-  pa.n_q = q->n_q; pa.swa = d->swa; pa.pool = d->pool_blocks;
-  pa.pool_blocks = pool_blocks; pa.pool_count = pool_count;
-  hipError_t e = launch_pool_select(pa, (hipStream_t)stream);
-  return e == hipSuccess ? CSA2_OK : hip_fail(e, "pool select launch");
+  return run_pool(d, q, block_scores, ld_block_scores, pool_blocks, pool_count, ws,
+                  (flags & CSA2_POOL_WS_FROM_SCAN) != 0, stream);
 }
 
 csa2_status csa2_index_full(const csa2_dims* d, const csa2_queries* q, const uint8_t* idx_q, const float* idx_w,
@@ -241,15 +307,19 @@ csa2_status csa2_index_full(const csa2_dims* d, const csa2_queries* q, const uin
   if ((st = check_queries(q))) return st;
   if (!idx_q || !idx_w || !idx_k || !pool_blocks || !pool_count)
     return fail(CSA2_ERR_INVALID_ARG, "required pointer is NULL");
+  if (((uintptr_t)idx_q | (uintptr_t)idx_k) & 15) return fail(CSA2_ERR_INVALID_ARG, "idx_q and idx_k must be 16-byte aligned");
+  const size_t pw = pool_ws(d, q);
+  if ((st = check_ws(ws, ws_bytes, block_scores ? pw : full_ws(d, q)))) return st;
   float* bs = block_scores;
   int64_t ld = ld_block_scores;
   if (!bs) {
-    if ((st = check_ws(ws, ws_bytes, full_ws(d, q)))) return st;
-    bs = (float*)ws;
+    bs = (float*)((char*)ws + pw);
     ld = full_ldb(d, q);
   }
-  if ((st = csa2_index_scan(d, q, idx_q, idx_w, idx_k, bs, ld, stream))) return st;
-  return csa2_index_pool(d, q, bs, ld, pool_blocks, pool_count, stream);
+  if ((st = check_block_scores(d, q, bs, ld))) return st;
+  if ((st = check_device())) return st;
+  if ((st = run_scan(d, q, idx_q, idx_w, idx_k, bs, ld, (uint32_t*)ws, stream))) return st;
+  return run_pool(d, q, bs, ld, pool_blocks, pool_count, ws, true, stream);
 }
 
 csa2_status csa2_index_reindex_workspace_size(const csa2_dims* d, const csa2_queries* q, size_t* bytes) {

@@ -159,22 +159,35 @@ __global__ __launch_bounds__(kNT) void k_attend(AttendArgs a) {
   const int64_t swa_base = a.swa_base[q];
   const int32_t* tk = a.topk_pos + (int64_t)q * a.topk;
 
+  // the wave's 16 query heads as f16 rows [head][576] (the B operand of
+  // Q.K^T): all 18 loads per lane issued before the first use
+  constexpr int kQv = 16 * (kKeyDim / 8) / 64;
+  v4u rq[kQv];
+  if (active) {
+#pragma unroll
+    for (int j = 0; j < kQv; ++j) {
+      const int i = lane + 64 * j, hh = i / (kKeyDim / 8), d = (i % (kKeyDim / 8)) * 8;
+      const int64_t qh = (int64_t)q * H + head0 + hh;
+      rq[j] = d < kLatent ? *reinterpret_cast<const v4u*>(a.q_lat + qh * kLatent + d)
+                          : *reinterpret_cast<const v4u*>(a.q_rope + qh * kRope + (d - kLatent));
+    }
+  }
   for (int e = e_begin + tid; e < e_end; e += kNT) s_row[e - e_begin] = e < Es ? tk[e] : -1 - (e - Es);
-  // the wave's 16 query heads as f16 rows [head][576] (the B operand of Q.K^T)
   if (active) {
     _Float16* sq = s_q + wave * 16 * kKS;
-    for (int i = lane; i < 16 * (kKeyDim / 8); i += 64) {
-      const int hh = i / (kKeyDim / 8), d = (i % (kKeyDim / 8)) * 8;
-      const int64_t qh = (int64_t)q * H + head0 + hh;
-      const v4u rq = d < kLatent ? *reinterpret_cast<const v4u*>(a.q_lat + qh * kLatent + d)
-                                 : *reinterpret_cast<const v4u*>(a.q_rope + qh * kRope + (d - kLatent));
+#pragma unroll
+    for (int j = 0; j < kQv; ++j) {
+      const int i = lane + 64 * j, hh = i / (kKeyDim / 8), d = (i % (kKeyDim / 8)) * 8;
       *reinterpret_cast<v4u*>(sq + hh * kKS + d) =
-          v4u{bf16x2_to_h2(rq[0]), bf16x2_to_h2(rq[1]), bf16x2_to_h2(rq[2]), bf16x2_to_h2(rq[3])};
+          v4u{bf16x2_to_h2(rq[j][0]), bf16x2_to_h2(rq[j][1]), bf16x2_to_h2(rq[j][2]), bf16x2_to_h2(rq[j][3])};
     }
   }
   __syncthreads();
-  RawTile raw;
-  if (e_begin < e_end) load_tile(a, s_row, min(kTile, e_end - e_begin), seq_base, swa_base, tid, raw);
+  // raw tiles two deep: tiles t and t+1 are in flight while t-1 is contracted
+  RawTile ra, rb;
+  if (e_begin < e_end) load_tile(a, s_row, min(kTile, e_end - e_begin), seq_base, swa_base, tid, ra);
+  if (e_begin + kTile < e_end)
+    load_tile(a, s_row + kTile, min(kTile, e_end - e_begin - kTile), seq_base, swa_base, tid, rb);
   const _Float16* sqw = s_q + (wave * 16 + col) * kKS + gq * 8;
 
   float m = -__builtin_inff(), l = 0.0f;
@@ -182,14 +195,14 @@ __global__ __launch_bounds__(kNT) void k_attend(AttendArgs a) {
 #pragma unroll
   for (int nt = 0; nt < kLatent / 16; ++nt) o[nt] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
-  for (int e0 = e_begin; e0 < e_end; e0 += kTile) {
+  auto tile = [&](RawTile& raw, int e0) {
     const int ne = min(kTile, e_end - e0);
     __syncthreads();                         // the previous tile's reads of s_k are done
     store_tile(a, s_row + (e0 - e_begin), ne, swa_base, raw, tid, s_k);
-    if (e0 + kTile < e_end)
-      load_tile(a, s_row + (e0 + kTile - e_begin), min(kTile, e_end - e0 - kTile), seq_base, swa_base, tid, raw);
+    const int e2 = e0 + 2 * kTile;           // this register set's next tile
+    if (e2 < e_end) load_tile(a, s_row + (e2 - e_begin), min(kTile, e_end - e2), seq_base, swa_base, tid, raw);
     __syncthreads();
-    if (!active) continue;
+    if (!active) return;
 
     // ---- S^T = K_tile . Q^T  (rows: entries, cols: heads)
     v4f s0 = {0.0f, 0.0f, 0.0f, 0.0f}, s1 = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -247,7 +260,12 @@ __global__ __launch_bounds__(kNT) void k_attend(AttendArgs a) {
                                                   __builtin_bit_cast(v2u, hi)[0], __builtin_bit_cast(v2u, hi)[1]}));
       o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pf, vb, o[nt], 0, 0, 0);
     }
+  };
+  for (int e0 = e_begin; e0 < e_end; e0 += 2 * kTile) {
+    tile(ra, e0);
+    if (e0 + kTile < e_end) tile(rb, e0 + kTile);
   }
+
   if (!active) return;
 
   // ---- epilogue: lane holds O[head 4gq+i][dim 16nt+col]

@@ -19,6 +19,11 @@ struct ScanArgs {
   int prefetch;              // LDS ring slots per wave (4, 6 or 8)
   float* bscore;             // [n_q, ld]
   int64_t ld;
+  // optional (nullptr: not written): the pool-select workspace, where each
+  // tile stores the (min, max) order keys of its block scores at pair `tile`
+  // and tile 0 clears the query's histogram
+  uint32_t* pool_ws;
+  int64_t pool_ws_stride;
 };
 
 struct PoolArgs {
@@ -26,6 +31,12 @@ struct PoolArgs {
   int64_t ld;
   const int32_t* n_visible;
   int n_q, swa, pool;
+  int chunks;                // kPoolChunk-block chunks per query (grid of K1-K3)
+  uint32_t* ws;              // [n_q, ws_stride] words (histogram, chunk results)
+  int64_t ws_stride;
+  int mm_cap;                // (min, max) key pairs per query in the workspace
+  int mm_span;               // blocks covered by one pair
+  bool have_minmax;          // pairs and a cleared histogram already written (by the scan)
   int32_t* pool_blocks;      // [n_q, pool]
   int32_t* pool_count;
 };
@@ -74,12 +85,14 @@ hipError_t launch_encode(int64_t n, const uint16_t* latent, const uint16_t* rope
                          uint16_t* rope_out, hipStream_t s);
 hipError_t launch_scan(const ScanArgs& a, hipStream_t s);
 hipError_t launch_pool_select(const PoolArgs& a, hipStream_t s);
+int64_t pool_ws_words(int chunks, int mm_cap);   // workspace words per query
 hipError_t launch_reindex(const ReindexArgs& a, hipStream_t s);
 hipError_t launch_attend(const AttendArgs& a, hipStream_t s);
 
 // Tiling constants the host needs for grids and workspace sizes.
-constexpr int kHistShift = 20;         // coarse histogram: top 12 bits of a key
-constexpr int kHistBins = 1 << (32 - kHistShift);
+constexpr int kHistBins = 4096;        // pool histogram bins (12 key bits)
+constexpr int kPoolChunk = 4096;       // blocks per pool-select chunk workgroup
+constexpr int kPoolChunkCand = 1024;   // candidate slots per chunk
 constexpr int kScanTile = 2048;        // default positions per scan workgroup
 constexpr int kScanPrefetch = 4;       // default LDS ring slots per wave
 constexpr int kAttendTile = 32;        // entries per attention tile

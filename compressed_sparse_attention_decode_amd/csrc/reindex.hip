@@ -120,13 +120,47 @@ constexpr int kTkThreads = 1024;
 constexpr int kMaxCand = 2048 * kBlock;
 constexpr int kPer = kMaxCand / kTkThreads;        // 16 keys per thread, in registers
 constexpr int kTkBins = 2048;                      // radix digit: up to 11 bits
+constexpr int kTkWaves = kTkThreads / 64;
+
+// Wave 0 finds, in a kTkBins histogram, the bin where the count from the top
+// first reaches `need`: out[0] = bin, out[1] = keys in higher bins,
+// out[2] = keys in the bin.  Each lane owns 32 bins; both passes over them
+// are branch-free runs of independent LDS reads.
+__device__ __forceinline__ void crossing_2048(const uint32_t* hist, uint32_t need, uint32_t* out) {
+  constexpr int kPB = kTkBins / 64;
+  const int lane = threadIdx.x;
+  const uint32_t* h = hist + kTkBins - kPB * (lane + 1);      // the lane's bins, ascending
+  uint32_t local = 0;
+#pragma unroll
+  for (int k = 0; k < kPB; ++k) local += h[k];
+  uint32_t x = local;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const uint32_t y = __shfl_up(x, d, 64);
+    if (lane >= d) x += y;
+  }
+  if (x - local < need && need <= x) {
+    uint32_t above = x - local;            // keys in bins above the lane's run
+#pragma unroll
+    for (int k = kPB - 1; k >= 0; --k) {   // from the lane's highest bin down
+      const uint32_t c = h[k];
+      if (above < need && need <= above + c) {
+        out[0] = kTkBins - kPB * (lane + 1) + k;
+        out[1] = above;
+        out[2] = c;
+      }
+      above += c;
+    }
+  }
+}
 
 __global__ __launch_bounds__(kTkThreads) void k_topk_select(ReindexArgs a) {
   __shared__ uint32_t s_hist[kTkBins];
-  __shared__ uint32_t s_scan[kTkThreads / 64 + 1];
+  __shared__ uint32_t s_red[3 * kTkWaves];
+  __shared__ uint32_t s_scan[kTkWaves + 1];
   __shared__ uint32_t s_misc[4];
 
-  const int q = blockIdx.x, tid = threadIdx.x;
+  const int q = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int N = a.pool_count[q] * kBlock;
   const int K = a.topk;
   const int32_t* pool = a.pool_blocks + (int64_t)q * a.pool;
@@ -134,15 +168,22 @@ __global__ __launch_bounds__(kTkThreads) void k_topk_select(ReindexArgs a) {
   int32_t* out = a.topk_pos + (int64_t)q * K;
   float* out_s = a.topk_scores ? a.topk_scores + (int64_t)q * K : nullptr;
 
-  // thread t holds slots [16t, 16t + 16) (pool order = ascending positions);
-  // N is a multiple of 8, so each 4-key vector is wholly valid or not
+  // thread t holds slots [16t, 16t + 16) (pool order = ascending positions)
+  // and the two pool blocks they belong to; N is a multiple of 8, so each
+  // 4-key vector and each block is wholly valid or not
   uint32_t key[kPer];
+  int32_t blk[2];
 #pragma unroll
   for (int v = 0; v < kPer / 4; ++v) {
     const int i = tid * kPer + v * 4;
     const v4u x = i < N ? *reinterpret_cast<const v4u*>(ks + i) : v4u{0u, 0u, 0u, 0u};
     key[4 * v] = x[0]; key[4 * v + 1] = x[1]; key[4 * v + 2] = x[2]; key[4 * v + 3] = x[3];
   }
+#pragma unroll
+  for (int j = 0; j < 2; ++j) blk[j] = tid * kPer + 8 * j < N ? pool[tid * 2 + j] : 0;
+  for (int i = tid; i < kTkBins; i += kTkThreads) s_hist[i] = 0;
+
+  // count of valid keys, their min and max: one barrier
   uint32_t nvalid = 0, lo = 0xFFFFFFFFu, hi = 0;
 #pragma unroll
   for (int k = 0; k < kPer; ++k) {
@@ -152,11 +193,26 @@ __global__ __launch_bounds__(kTkThreads) void k_topk_select(ReindexArgs a) {
       hi = max(hi, key[k]);
     }
   }
-  uint32_t total;
-  (void)block_exclusive_scan<kTkThreads>(nvalid, s_scan, &total);
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) {
+    nvalid += __shfl_xor(nvalid, d, 64);
+    lo = min(lo, (uint32_t)__shfl_xor(lo, d, 64));
+    hi = max(hi, (uint32_t)__shfl_xor(hi, d, 64));
+  }
+  if (lane == 0) {
+    s_red[wave] = nvalid;
+    s_red[kTkWaves + wave] = lo;
+    s_red[2 * kTkWaves + wave] = hi;
+  }
+  __syncthreads();
+  uint32_t total = 0, kmin = 0xFFFFFFFFu, kmax = 0;
+#pragma unroll
+  for (int w = 0; w < kTkWaves; ++w) {
+    total += s_red[w];
+    kmin = min(kmin, s_red[kTkWaves + w]);
+    kmax = max(kmax, s_red[2 * kTkWaves + w]);
+  }
   const uint32_t keff = min((uint32_t)K, total);
-  const uint32_t kmin = block_min_u32<kTkThreads>(lo, s_scan);
-  const uint32_t kmax = block_max_u32<kTkThreads>(hi, s_scan);
 
   // Radix select of the keff-th largest key, from the highest bit where the
   // smallest and largest keys differ.  Stops early when the crossing digit's
@@ -172,24 +228,21 @@ __global__ __launch_bounds__(kTkThreads) void k_topk_select(ReindexArgs a) {
     while (fixed_lo > 0) {
       const int sh = max(0, fixed_lo - 11);
       const uint32_t dmask = (1u << (fixed_lo - sh)) - 1;
-      const int nbins = max(64, (int)dmask + 1);
-      for (int i = tid; i < nbins; i += kTkThreads) s_hist[i] = 0;
-      __syncthreads();
 #pragma unroll
       for (int k = 0; k < kPer; ++k) {
         if (key[k] != 0 && ((uint64_t)key[k] >> fixed_lo) == ((uint64_t)prefix >> fixed_lo))
           atomicAdd(&s_hist[(key[k] >> sh) & dmask], 1u);
       }
       __syncthreads();
-      find_crossing(s_hist, nbins, need, s_misc);
+      if (wave == 0) crossing_2048(s_hist, need, s_misc);
       __syncthreads();
-      const uint32_t bin = s_misc[0], above = s_misc[1];
-      const uint32_t in_bin = s_hist[bin];
+      const uint32_t bin = s_misc[0], above = s_misc[1], in_bin = s_misc[2];
       prefix |= bin << sh;
       need -= above;
       fixed_lo = sh;
-      __syncthreads();
+      for (int i = tid; i < kTkBins; i += kTkThreads) s_hist[i] = 0;   // for the next digit
       if (need == in_bin) { whole = true; break; }
+      __syncthreads();                 // the clear is ordered before the next digit's counts
     }
     if (whole) {
       T = (int64_t)prefix - 1;         // prefix: smallest key value of the crossing digit
@@ -200,13 +253,13 @@ __global__ __launch_bounds__(kTkThreads) void k_topk_select(ReindexArgs a) {
     }
   }
 
-  // ordered compaction
+  // ordered compaction: one scan of (ties, then selected) counts
   uint32_t eq = 0;
   if (keff > 0) {
 #pragma unroll
     for (int k = 0; k < kPer; ++k) eq += key[k] != 0 && (int64_t)key[k] == T;
   }
-  uint32_t eq_before = block_exclusive_scan<kTkThreads>(eq, s_scan, &total);
+  uint32_t eq_before = need_eq > 0 ? block_exclusive_scan<kTkThreads>(eq, s_scan, &total) : 0;
   uint32_t take = 0, flags = 0;
   if (keff > 0) {
 #pragma unroll
@@ -220,9 +273,8 @@ __global__ __launch_bounds__(kTkThreads) void k_topk_select(ReindexArgs a) {
 #pragma unroll
   for (int k = 0; k < kPer; ++k) {
     if (flags & (1u << k)) {
-      const int i = tid * kPer + k;
       if (before < (uint32_t)K) {
-        out[before] = pool[i >> 3] * kBlock + (i & 7);
+        out[before] = blk[k >> 3] * kBlock + (k & 7);
         if (out_s) out_s[before] = key_float(key[k]);
       }
       ++before;

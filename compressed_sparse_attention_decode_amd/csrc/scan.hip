@@ -211,7 +211,32 @@ __global__ __launch_bounds__(256) void k_scan(ScanArgs a) {
   // block scores of the tile, one coalesced store
   float* bs = a.bscore + (int64_t)q * a.ld + (p_begin >> 3);
   const int nblk = (p_end - p_begin + 7) >> 3;
-  for (int i = tid; i < nblk; i += 256) bs[i] = s_bs[i];
+  uint32_t lo = 0xFFFFFFFFu, hi = 0;
+  for (int i = tid; i < nblk; i += 256) {
+    const float v = s_bs[i];
+    bs[i] = v;
+    lo = min(lo, order_key(v));
+    hi = max(hi, order_key(v));
+  }
+  if (a.pool_ws) {
+    // the tile's key range for the pool select, and (tile 0) its histogram cleared
+    uint32_t* pw = a.pool_ws + (int64_t)q * a.pool_ws_stride;
+    if (tile == 0) {
+      for (int i = tid * 4; i < kHistBins; i += 256 * 4) *reinterpret_cast<v4u*>(pw + i) = v4u{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) {
+      lo = min(lo, (uint32_t)__shfl_xor(lo, d, 64));
+      hi = max(hi, (uint32_t)__shfl_xor(hi, d, 64));
+    }
+    __shared__ uint32_t s_mm[8];
+    if (lane == 0) { s_mm[wave] = lo; s_mm[4 + wave] = hi; }
+    __syncthreads();
+    if (tid == 0) {
+      *reinterpret_cast<v2u*>(pw + kHistBins + 2 * tile) =
+          v2u{min(min(s_mm[0], s_mm[1]), min(s_mm[2], s_mm[3])), max(max(s_mm[4], s_mm[5]), max(s_mm[6], s_mm[7]))};
+    }
+  }
 }
 
 template <int D, int R>

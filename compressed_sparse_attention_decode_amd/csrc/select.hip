@@ -5,20 +5,28 @@
 // (block score descending, block id ascending); the pool is written in
 // ascending block order.
 //
-// One 1024-thread workgroup per query, on order-preserving uint32 keys:
-//  1. min/max pass: the bits above the highest bit where min and max differ
-//     are common to every key, so the histograms start below them (keys of
-//     similar scores share their top bits and would otherwise pile onto a few
-//     LDS counters);
-//  2. a 4096-bin LDS histogram of the next 12 bits gives the bin b* holding
-//     the P-th best block;
-//  3. one pass marks blocks in higher bins in an LDS bitmap (wave ballots)
-//     and appends the blocks of bin b* to an LDS candidate list;
-//  4. an exact radix select over the candidates' remaining bits finds the
-//     threshold key T and how many blocks equal to T are still needed (a
-//     candidate list that overflows LDS is re-read from global memory);
-//  5. ordered compaction of the bitmap writes ascending block ids, admitting
-//     blocks equal to T lowest id first.
+// Keys are order-preserving uint32 images of the block scores.  One CU streams
+// a few tens of GB/s at most, so a long context (131,056 blocks at 1M) is
+// split into chunks of 4096 blocks, each handled by its own workgroup, and
+// only the final exact step runs one workgroup per query:
+//  K1 k_pool_minmax: per chunk, the smallest and largest key; chunk 0 also
+//     clears the query's global histogram.  (The Full scan can write these
+//     (min, max) pairs per scan tile and clear the histogram itself; then K1
+//     is skipped.)
+//  K2 k_pool_hist: the bits above the highest bit where the query's min and
+//     max keys differ are common to every key, so a 4096-bin histogram of the
+//     next 12 bits spreads the keys (similar scores would otherwise pile onto
+//     a few counters); per chunk in LDS, then added to the query's histogram.
+//  K3 k_pool_mark: every chunk finds the bin b* holding the P-th best block,
+//     writes its blocks of higher bins as a bitmap and lists its blocks of
+//     bin b* as candidates.
+//  K4 k_pool_final: an exact radix select over the candidates' remaining
+//     bits gives the threshold key T and how many blocks equal to T are still
+//     needed; the ordered compaction of the bitmap writes ascending block ids,
+//     admitting blocks equal to T lowest id first; it clears the histogram
+//     again after reading it.  If a chunk listed more
+//     candidates than its slots, this step re-reads the block scores instead
+//     (correct for any input, slow only for near-constant scores).
 #include "common.h"
 #include "internal.h"
 #include "select_common.h"
@@ -26,9 +34,12 @@
 namespace csa2 {
 namespace {
 
-constexpr int kSelThreads = 1024;
-constexpr int kCandCap = 8192;
+constexpr int kCT = 256;                       // chunk workgroup threads
+constexpr int kFT = 1024;                      // final workgroup threads
+constexpr int kCandCap = 8192;                 // candidates the final step holds in LDS
 constexpr int kMaxWords = kMaxBlocks / 32;
+static_assert(kPoolChunk == kCT * 16, "a chunk thread holds 16 blocks");
+static_assert(kHistBins == 4 * kFT, "the final step clears the histogram 4 words per thread");
 
 __device__ __forceinline__ uint32_t lane_prefix(uint64_t mask) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
@@ -39,119 +50,230 @@ __device__ __forceinline__ bool same_above(uint32_t a, uint32_t b, int lo) {
   return ((uint64_t)a >> lo) == ((uint64_t)b >> lo);
 }
 
-// One pass over a query's block scores, 16-byte loads issued kU at a time
-// (kU x 4 blocks per thread in flight).  f(jb0, key[4], valid-mask) sees
-// blocks jb0 .. jb0+3; blocks >= nb are passed with their mask bit clear.
-constexpr int kU = 8;
-template <typename F>
-__device__ __forceinline__ void sweep(const float* bs, int nb, F&& f) {
-  const int tid = threadIdx.x;
-  for (int base = 0; base < nb; base += kSelThreads * 4 * kU) {
-    v4f x[kU];
+struct PoolWs {
+  uint32_t* hist;     // [kHistBins]
+  uint32_t* mm;       // [mm_cap][2] min, max key per span of blocks
+  uint32_t* cnt;      // [G] candidates listed per chunk (may exceed the slots)
+  uint32_t* sel;      // [G * kPoolChunk / 32] bitmap of blocks above bin b*
+  uint32_t* ckey;     // [G][kPoolChunkCand]
+  int32_t* cblk;      // [G][kPoolChunkCand]
+};
+
+__device__ __forceinline__ PoolWs pool_ws(const PoolArgs& a, int q) {
+  PoolWs w;
+  const int G = a.chunks;
+  w.hist = a.ws + (int64_t)q * a.ws_stride;
+  w.mm = w.hist + kHistBins;
+  w.cnt = w.mm + 2 * a.mm_cap;
+  w.sel = w.cnt + G;
+  w.ckey = w.sel + G * (kPoolChunk / 32);
+  w.cblk = reinterpret_cast<int32_t*>(w.ckey + G * kPoolChunkCand);
+  return w;
+}
+
+__device__ __forceinline__ int query_blocks(const PoolArgs& a, int q) {
+  const int c = max(0, a.n_visible[q] - a.swa);
+  return (c + 7) >> 3;
+}
+
+// The thread's 16 keys of a chunk: 4 x 16-byte loads, key e of load u is
+// block jb0(u) + e with jb0(u) = base + (u * kCT + tid) * 4; blocks >= nb are
+// masked out.  Row stride and base are multiples of 4 floats.
+struct ChunkKeys {
+  uint32_t k[4][4];
+  uint32_t vm[4];
+};
+
+__device__ __forceinline__ void load_chunk(const float* bs, int base, int nb, int tid, ChunkKeys& c) {
+  v4f x[4];
 #pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      const int jb0 = base + (u * kSelThreads + tid) * 4;
-      x[u] = jb0 < nb ? *reinterpret_cast<const v4f*>(bs + jb0) : v4f{0.0f, 0.0f, 0.0f, 0.0f};
-    }
+  for (int u = 0; u < 4; ++u) {
+    const int jb0 = base + (u * kCT + tid) * 4;
+    x[u] = jb0 < nb ? *reinterpret_cast<const v4f*>(bs + jb0) : v4f{0.0f, 0.0f, 0.0f, 0.0f};
+  }
 #pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      const int jb0 = base + (u * kSelThreads + tid) * 4;
-      const int left = nb - jb0;
-      const uint32_t vm = left >= 4 ? 15u : (left <= 0 ? 0u : (1u << left) - 1u);
-      const uint32_t k[4] = {order_key(x[u][0]), order_key(x[u][1]), order_key(x[u][2]), order_key(x[u][3])};
-      f(jb0, k, vm);
-    }
+  for (int u = 0; u < 4; ++u) {
+    const int left = nb - (base + (u * kCT + tid) * 4);
+    c.vm[u] = left >= 4 ? 15u : (left <= 0 ? 0u : (1u << left) - 1u);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) c.k[u][e] = order_key(x[u][e]);
   }
 }
 
-__global__ __launch_bounds__(kSelThreads) void k_pool_select(PoolArgs a) {
-  __shared__ uint32_t s_hist[kHistBins];
-  __shared__ uint32_t s_sel[kMaxWords];
-  __shared__ uint32_t s_tie[kMaxWords];
-  __shared__ uint32_t s_ckey[kCandCap];
-  __shared__ int32_t s_cj[kCandCap];
-  __shared__ uint32_t s_scan[kSelThreads / 64 + 1];
-  __shared__ uint32_t s_misc[4];
-  __shared__ uint32_t s_ccount;
-
-  const int q = blockIdx.x;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int n = a.n_visible[q];
-  const int c = max(0, n - a.swa);
-  const int nb = (c + 7) >> 3;
-  const int P = a.pool;
-  int32_t* out = a.pool_blocks + (int64_t)q * P;
-  if (nb <= P) {
-    for (int j = tid; j < P; j += kSelThreads) out[j] = j < nb ? j : -1;
-    if (tid == 0) a.pool_count[q] = nb;
-    return;
-  }
-  const float* bs = a.bscore + (int64_t)q * a.ld;
-
-  // 1. key range
+// The query's key range from the (min, max) pairs of its spans of blocks
+// (chunks of K1, or scan tiles).
+template <int NT>
+__device__ __forceinline__ void key_range(const PoolArgs& a, const PoolWs& w, int nb, uint32_t* s_scan,
+                                          uint32_t* kmin, uint32_t* kmax) {
+  const int n = (nb + a.mm_span - 1) / a.mm_span;
   uint32_t lo = 0xFFFFFFFFu, hi = 0;
-  sweep(bs, nb, [&](int, const uint32_t* k, uint32_t vm) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      if (vm >> e & 1u) { lo = min(lo, k[e]); hi = max(hi, k[e]); }
-    }
-  });
-  const uint32_t kmin = block_min_u32<kSelThreads>(lo, s_scan);
-  const uint32_t kmax = block_max_u32<kSelThreads>(hi, s_scan);
-  const int top = highest_diff_bit(kmin, kmax);          // -1: all keys equal
-  const int cs = max(0, top - 11);                        // coarse bins: bits [cs, top]
-  const uint32_t cmask = top < 0 ? 0u : (uint32_t)((2ull << (top - cs)) - 1);
+  for (int i = threadIdx.x; i < n; i += NT) {
+    const v2u m = *reinterpret_cast<const v2u*>(w.mm + 2 * i);
+    lo = min(lo, m[0]);
+    hi = max(hi, m[1]);
+  }
+  *kmin = block_min_u32<NT>(lo, s_scan);
+  *kmax = block_max_u32<NT>(hi, s_scan);
+}
 
-  // 2. coarse histogram and the bin b* of the P-th best block
-  for (int i = tid; i < kHistBins; i += kSelThreads) s_hist[i] = 0;
+struct Bins {
+  int top, cs;        // histogram over key bits [cs, top]
+  uint32_t cmask;
+};
+
+__device__ __forceinline__ Bins bins_for(uint32_t kmin, uint32_t kmax) {
+  Bins b;
+  b.top = highest_diff_bit(kmin, kmax);     // -1: all keys equal
+  b.cs = max(0, b.top - 11);
+  b.cmask = b.top < 0 ? 0u : (uint32_t)((2ull << (b.top - b.cs)) - 1);
+  return b;
+}
+
+// The thread's histogram bins, counted from the top: bin kHistBins-1-(tid*kPer+k).
+template <int NT>
+struct HistSlice {
+  static constexpr int kPer = kHistBins / NT;
+  uint32_t c[kPer];
+  __device__ __forceinline__ void load(const uint32_t* hist) {
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int k = 0; k < kPer; k += 4) {
+      const v4u x = *reinterpret_cast<const v4u*>(hist + kHistBins - (tid + 1) * kPer + k);
+      c[kPer - 1 - k] = x[0]; c[kPer - 2 - k] = x[1]; c[kPer - 3 - k] = x[2]; c[kPer - 4 - k] = x[3];
+    }
+  }
+};
+
+// Bin b* of the P-th best key and the number of keys in higher bins:
+// s_out[0] = b*, s_out[1] = above.
+template <int NT>
+__device__ __forceinline__ void find_bstar(const HistSlice<NT>& h, uint32_t P, uint32_t* s_scan, uint32_t* s_out) {
+  constexpr int kPer = HistSlice<NT>::kPer;
+  const int tid = threadIdx.x;
+  uint32_t local = 0;
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) local += h.c[k];
+  uint32_t total;
+  uint32_t above = block_exclusive_scan<NT>(local, s_scan, &total);
+  if (above < P && P <= above + local) {
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      if (above < P && P <= above + h.c[k]) {
+        s_out[0] = kHistBins - 1 - (tid * kPer + k);
+        s_out[1] = above;
+      }
+      above += h.c[k];
+    }
+  }
   __syncthreads();
-  sweep(bs, nb, [&](int, const uint32_t* k, uint32_t vm) {
+}
+
+// ---------------------------------------------------------------- K1
+__global__ __launch_bounds__(kCT) void k_pool_minmax(PoolArgs a) {
+  __shared__ uint32_t s_scan[kCT / 64 + 1];
+  const int q = blockIdx.x / a.chunks, g = blockIdx.x % a.chunks, tid = threadIdx.x;
+  const PoolWs w = pool_ws(a, q);
+  if (g == 0) {
+    for (int i = tid * 4; i < kHistBins; i += kCT * 4)
+      *reinterpret_cast<v4u*>(w.hist + i) = v4u{0u, 0u, 0u, 0u};
+  }
+  const int nb = query_blocks(a, q);
+  const int base = g * kPoolChunk;
+  uint32_t lo = 0xFFFFFFFFu, hi = 0;
+  if (nb > a.pool && base < nb) {
+    ChunkKeys c;
+    load_chunk(a.bscore + (int64_t)q * a.ld, base, nb, tid, c);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (c.vm[u] >> e & 1u) {
+          lo = min(lo, c.k[u][e]);
+          hi = max(hi, c.k[u][e]);
+        }
+      }
+    }
+  }
+  lo = block_min_u32<kCT>(lo, s_scan);
+  hi = block_max_u32<kCT>(hi, s_scan);
+  if (tid == 0) {
+    w.mm[2 * g] = lo;
+    w.mm[2 * g + 1] = hi;
+  }
+}
+
+// ---------------------------------------------------------------- K2
+__global__ __launch_bounds__(kCT) void k_pool_hist(PoolArgs a) {
+  __shared__ uint32_t s_hist[kHistBins];
+  __shared__ uint32_t s_scan[kCT / 64 + 1];
+  const int q = blockIdx.x / a.chunks, g = blockIdx.x % a.chunks, tid = threadIdx.x;
+  const int nb = query_blocks(a, q);
+  const int base = g * kPoolChunk;
+  if (nb <= a.pool || base >= nb) return;
+  const PoolWs w = pool_ws(a, q);
+  ChunkKeys c;
+  load_chunk(a.bscore + (int64_t)q * a.ld, base, nb, tid, c);
+  for (int i = tid; i < kHistBins; i += kCT) s_hist[i] = 0;
+  uint32_t kmin, kmax;
+  key_range<kCT>(a, w, nb, s_scan, &kmin, &kmax);     // its barriers order the clear
+  const Bins b = bins_for(kmin, kmax);
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
 #pragma unroll
     for (int e = 0; e < 4; ++e)
-      if (vm >> e & 1u) atomicAdd(&s_hist[(k[e] >> cs) & cmask], 1u);
-  });
-  __syncthreads();
-  constexpr int kPer = kHistBins / kSelThreads;
-  uint32_t local = 0, cnt[kPer];
-  for (int k = 0; k < kPer; ++k) {
-    cnt[k] = s_hist[kHistBins - 1 - (tid * kPer + k)];
-    local += cnt[k];
+      if (c.vm[u] >> e & 1u) atomicAdd(&s_hist[(c.k[u][e] >> b.cs) & b.cmask], 1u);
   }
-  uint32_t total;
-  uint32_t above = block_exclusive_scan<kSelThreads>(local, s_scan, &total);
-  if (above < (uint32_t)P && (uint32_t)P <= above + local) {
-    for (int k = 0; k < kPer; ++k) {
-      if (above + cnt[k] >= (uint32_t)P) {
-        s_misc[0] = kHistBins - 1 - (tid * kPer + k);
-        s_misc[1] = above;
-        break;
-      }
-      above += cnt[k];
-    }
-  }
-  const int nw = (nb + 31) >> 5;
-  for (int w = tid; w < nw; w += kSelThreads) s_tie[w] = 0;
-  if (tid == 0) s_ccount = 0;
   __syncthreads();
-  const uint32_t bstar = s_misc[0];
-  uint32_t need = (uint32_t)P - s_misc[1];
+  for (int i = tid; i < kHistBins; i += kCT) {
+    const uint32_t h = s_hist[i];
+    if (h) atomicAdd(&w.hist[i], h);
+  }
+}
 
-  // 3. mark blocks above b* (a lane's 4 blocks form one nibble of the
-  //    bitmap; 8 lanes OR their nibbles into a word), collect bin b*
-  sweep(bs, nb, [&](int jb0, const uint32_t* k, uint32_t vm) {
+// ---------------------------------------------------------------- K3
+__global__ __launch_bounds__(kCT) void k_pool_mark(PoolArgs a) {
+  __shared__ uint32_t s_scan[kCT / 64 + 1];
+  __shared__ uint32_t s_misc[2];
+  __shared__ uint32_t s_ccount;
+  const int q = blockIdx.x / a.chunks, g = blockIdx.x % a.chunks;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int nb = query_blocks(a, q);
+  const int base = g * kPoolChunk;
+  const PoolWs w = pool_ws(a, q);
+  if (nb <= a.pool || base >= nb) {
+    if (tid == 0) w.cnt[g] = 0;
+    return;
+  }
+  ChunkKeys c;
+  load_chunk(a.bscore + (int64_t)q * a.ld, base, nb, tid, c);
+  HistSlice<kCT> h;
+  h.load(w.hist);
+  if (tid == 0) s_ccount = 0;
+  uint32_t kmin, kmax;
+  key_range<kCT>(a, w, nb, s_scan, &kmin, &kmax);
+  const Bins b = bins_for(kmin, kmax);
+  find_bstar<kCT>(h, (uint32_t)a.pool, s_scan, s_misc);
+  const uint32_t bstar = s_misc[0];
+
+  uint32_t* ck = w.ckey + (int64_t)g * kPoolChunkCand;
+  int32_t* cj = w.cblk + (int64_t)g * kPoolChunkCand;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int jb0 = base + (u * kCT + tid) * 4;
     uint32_t hib = 0, cand = 0;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const uint32_t bin = (k[e] >> cs) & cmask;
-      hib |= (uint32_t)((vm >> e & 1u) && bin > bstar) << e;
-      cand |= (uint32_t)((vm >> e & 1u) && bin == bstar) << e;
+      const bool v = c.vm[u] >> e & 1u;
+      const uint32_t bin = (c.k[u][e] >> b.cs) & b.cmask;
+      hib |= (uint32_t)(v && bin > bstar) << e;
+      cand |= (uint32_t)(v && bin == bstar) << e;
     }
+    // a lane's 4 blocks form one nibble; 8 lanes OR their nibbles into a word
     uint32_t word = hib << (4 * (lane & 7));
     word |= __shfl_xor(word, 1, 64);
     word |= __shfl_xor(word, 2, 64);
     word |= __shfl_xor(word, 4, 64);
-    if ((lane & 7) == 0 && jb0 < nb) s_sel[jb0 >> 5] = word;
-    // candidates: slot = wave base + per-element ballot prefixes
+    if ((lane & 7) == 0 && jb0 < nb) w.sel[jb0 >> 5] = word;
     uint64_t m[4];
     uint32_t tot = 0;
 #pragma unroll
@@ -159,7 +281,7 @@ __global__ __launch_bounds__(kSelThreads) void k_pool_select(PoolArgs a) {
       m[e] = __ballot(cand >> e & 1u);
       tot += (uint32_t)__popcll(m[e]);
     }
-    if (tot == 0) return;
+    if (tot == 0) continue;                       // wave-uniform
     uint32_t slot0 = 0;
     if (lane == 0) slot0 = atomicAdd(&s_ccount, tot);
     slot0 = __shfl(slot0, 0, 64);
@@ -167,99 +289,192 @@ __global__ __launch_bounds__(kSelThreads) void k_pool_select(PoolArgs a) {
     for (int e = 0; e < 4; ++e) {
       if (cand >> e & 1u) {
         const uint32_t slot = slot0 + lane_prefix(m[e]);
-        if (slot < kCandCap) { s_ckey[slot] = k[e]; s_cj[slot] = jb0 + e; }
+        if (slot < (uint32_t)kPoolChunkCand) { ck[slot] = c.k[u][e]; cj[slot] = jb0 + e; }
       }
       slot0 += (uint32_t)__popcll(m[e]);
     }
-  });
+  }
   __syncthreads();
-  const uint32_t C = s_ccount;
-  const bool in_lds = C <= (uint32_t)kCandCap;
+  if (tid == 0) w.cnt[g] = s_ccount;
+}
 
-  // 4. radix select inside bin b* over bits [0, cs)
-  uint32_t prefix = (uint32_t)(((uint64_t)kmin >> (top + 1)) << (top + 1)) | (bstar << cs);
-  int fixed_lo = cs;                    // bits >= fixed_lo are decided
+// ---------------------------------------------------------------- K4
+__global__ __launch_bounds__(kFT) void k_pool_final(PoolArgs a) {
+  __shared__ uint32_t s_hist[256];
+  __shared__ uint32_t s_sel[kMaxWords];
+  __shared__ uint32_t s_tie[kMaxWords];
+  __shared__ uint32_t s_ckey[kCandCap];
+  __shared__ int32_t s_cj[kCandCap];
+  __shared__ uint32_t s_off[kMaxBlocks / kPoolChunk + 1];
+  __shared__ uint32_t s_scan[kFT / 64 + 1];
+  __shared__ uint32_t s_misc[4];
+
+  const int q = blockIdx.x, tid = threadIdx.x;
+  const int nb = query_blocks(a, q);
+  const int P = a.pool, G = a.chunks;
+  int32_t* out = a.pool_blocks + (int64_t)q * P;
+  if (nb <= P) {
+    for (int j = tid; j < P; j += kFT) out[j] = j < nb ? j : -1;
+    if (tid == 0) a.pool_count[q] = nb;
+    return;
+  }
+  const PoolWs w = pool_ws(a, q);
+  const float* bs = a.bscore + (int64_t)q * a.ld;
+  const int nw = (nb + 31) >> 5;
+
+  // every independent read issued before the first wait: the bitmap of
+  // blocks above b*, the histogram, the chunks' candidate counts, the key range
+  constexpr int kSelPer = kMaxWords / kFT;
+  uint32_t selw[kSelPer];
+#pragma unroll
+  for (int k = 0; k < kSelPer; ++k) {
+    const int i = tid + k * kFT;
+    selw[k] = i < nw ? w.sel[i] : 0u;
+  }
+  HistSlice<kFT> h;
+  h.load(w.hist);
+  const uint32_t cnt_v = tid < G ? w.cnt[tid] : 0u;
+  uint32_t kmin, kmax;
+  key_range<kFT>(a, w, nb, s_scan, &kmin, &kmax);
+#pragma unroll
+  for (int k = 0; k < kSelPer; ++k) {
+    const int i = tid + k * kFT;
+    if (i < nw) { s_sel[i] = selw[k]; s_tie[i] = 0; }
+  }
+  const Bins b = bins_for(kmin, kmax);
+  find_bstar<kFT>(h, (uint32_t)P, s_scan, s_misc);
+  const uint32_t bstar = s_misc[0];
+  uint32_t need = (uint32_t)P - s_misc[1];
+
+  // candidate lists of the chunks (offsets by a wave-0 scan over <= 64 chunks)
+  if (tid < 64) {
+    const uint32_t v = cnt_v;
+    const bool over = v > (uint32_t)kPoolChunkCand;
+    uint32_t x = v;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const uint32_t y = __shfl_up(x, d, 64);
+      if (tid >= d) x += y;
+    }
+    if (tid < G) s_off[tid] = x - v;
+    const uint64_t ov = __ballot(over);
+    if (tid == 63) {
+      s_off[G] = x;
+      s_misc[2] = (ov != 0 || x > (uint32_t)kCandCap) ? 1u : 0u;   // fall back to the block scores
+    }
+  }
+  __syncthreads();
+  const uint32_t C = s_off[G];
+  const bool in_lds = s_misc[2] == 0;
+  if (in_lds) {
+    const int wave = tid >> 6, lane = tid & 63;
+    for (int g = wave; g < G; g += kFT / 64) {
+      const uint32_t n = s_off[g + 1] - s_off[g];
+      for (uint32_t i = lane; i < n; i += 64) {
+        s_ckey[s_off[g] + i] = w.ckey[(int64_t)g * kPoolChunkCand + i];
+        s_cj[s_off[g] + i] = w.cblk[(int64_t)g * kPoolChunkCand + i];
+      }
+    }
+  }
+  __syncthreads();
+
+  // radix select inside bin b* over bits [0, cs)
+  uint32_t prefix = (uint32_t)(((uint64_t)kmin >> (b.top + 1)) << (b.top + 1)) | (bstar << b.cs);
+  int fixed_lo = b.cs;                  // bits >= fixed_lo are decided
   while (fixed_lo > 0) {
     const int sh = max(0, fixed_lo - 8);
     const uint32_t dmask = (1u << (fixed_lo - sh)) - 1;
-    for (int i = tid; i < 256; i += kSelThreads) s_hist[i] = 0;
+    if (tid < 256) s_hist[tid] = 0;
     __syncthreads();
     if (in_lds) {
-      for (uint32_t i = tid; i < C; i += kSelThreads) {
+      for (uint32_t i = tid; i < C; i += kFT) {
         const uint32_t key = s_ckey[i];
         if (same_above(key, prefix, fixed_lo)) atomicAdd(&s_hist[(key >> sh) & dmask], 1u);
       }
     } else {
-      for (int jb = tid; jb < nb; jb += kSelThreads) {
+      for (int jb = tid; jb < nb; jb += kFT) {
         const uint32_t key = order_key(bs[jb]);
         if (same_above(key, prefix, fixed_lo)) atomicAdd(&s_hist[(key >> sh) & dmask], 1u);
       }
     }
     __syncthreads();
-    find_crossing(s_hist, 256, need, s_misc + 2);
+    find_crossing(s_hist, 256, need, s_misc);
     __syncthreads();
-    prefix |= s_misc[2] << sh;
-    need -= s_misc[3];
+    prefix |= s_misc[0] << sh;
+    need -= s_misc[1];
     fixed_lo = sh;
     __syncthreads();
   }
   const uint32_t T = prefix;
   const uint32_t need_eq = need;
 
-  // mark candidates above T (selected) and equal to T (tie bits)
+  // candidates above T join the selection; those equal to T are tie bits
   if (in_lds) {
-    for (uint32_t i = tid; i < C; i += kSelThreads) {
+    for (uint32_t i = tid; i < C; i += kFT) {
       const uint32_t key = s_ckey[i];
       const int jb = s_cj[i];
       if (key > T) atomicOr(&s_sel[jb >> 5], 1u << (jb & 31));
       else if (key == T) atomicOr(&s_tie[jb >> 5], 1u << (jb & 31));
     }
   } else {
-    for (int jb = tid; jb < nb; jb += kSelThreads) {
+    for (int jb = tid; jb < nb; jb += kFT) {
       const uint32_t key = order_key(bs[jb]);
-      if (((key >> cs) & cmask) != bstar) continue;
+      if (((key >> b.cs) & b.cmask) != bstar) continue;
       if (key > T) atomicOr(&s_sel[jb >> 5], 1u << (jb & 31));
       else if (key == T) atomicOr(&s_tie[jb >> 5], 1u << (jb & 31));
     }
   }
   __syncthreads();
 
-  // 5. ordered compaction; ties admitted in ascending block order
-  const int wpt = (nw + kSelThreads - 1) / kSelThreads;
+  // ordered compaction; ties admitted in ascending block order
+  const int wpt = (nw + kFT - 1) / kFT;
   const int w_lo = min(nw, tid * wpt), w_hi = min(nw, w_lo + wpt);
-  uint32_t ties = 0;
-  for (int w = w_lo; w < w_hi; ++w) ties += __popc(s_tie[w]);
-  uint32_t tie_before = block_exclusive_scan<kSelThreads>(ties, s_scan, &total);
+  uint32_t ties = 0, total;
+  for (int i = w_lo; i < w_hi; ++i) ties += __popc(s_tie[i]);
+  uint32_t tie_before = block_exclusive_scan<kFT>(ties, s_scan, &total);
   uint32_t sel_local = 0;
-  for (int w = w_lo; w < w_hi; ++w) {
-    uint32_t t = s_tie[w], acc = 0;
+  for (int i = w_lo; i < w_hi; ++i) {
+    uint32_t t = s_tie[i], acc = 0;
     while (t && tie_before < need_eq) {
       const uint32_t bit = t & (0u - t);
       acc |= bit;
       t ^= bit;
       ++tie_before;
     }
-    const uint32_t fin = s_sel[w] | acc;
-    s_sel[w] = fin;
+    const uint32_t fin = s_sel[i] | acc;
+    s_sel[i] = fin;
     sel_local += __popc(fin);
   }
-  uint32_t out_before = block_exclusive_scan<kSelThreads>(sel_local, s_scan, &total);
-  for (int w = w_lo; w < w_hi; ++w) {
-    uint32_t fin = s_sel[w];
+  uint32_t out_before = block_exclusive_scan<kFT>(sel_local, s_scan, &total);
+  for (int i = w_lo; i < w_hi; ++i) {
+    uint32_t fin = s_sel[i];
     while (fin) {
-      const int b = __ffs(fin) - 1;
+      const int bit = __ffs(fin) - 1;
       fin &= fin - 1;
-      if (out_before < (uint32_t)P) out[out_before] = w * 32 + b;
+      if (out_before < (uint32_t)P) out[out_before] = i * 32 + bit;
       ++out_before;
     }
   }
   if (tid == 0) a.pool_count[q] = P;
+  // leave the histogram cleared: a later pool call on the same scan-prepared
+  // workspace (the same block scores) accumulates onto zero again
+  *reinterpret_cast<v4u*>(w.hist + 4 * tid) = v4u{0u, 0u, 0u, 0u};
 }
 
 }  // namespace
 
+int64_t pool_ws_words(int chunks, int mm_cap) {
+  const int64_t words = kHistBins + 2 * (int64_t)mm_cap + chunks + (int64_t)chunks * (kPoolChunk / 32) +
+                        2 * (int64_t)chunks * kPoolChunkCand;
+  return (words + 63) / 64 * 64;
+}
+
 hipError_t launch_pool_select(const PoolArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(k_pool_select, dim3(a.n_q), dim3(kSelThreads), 0, s, a);
+  const dim3 grid((unsigned)(a.n_q * a.chunks));
+  if (!a.have_minmax) hipLaunchKernelGGL(k_pool_minmax, grid, dim3(kCT), 0, s, a);
+  hipLaunchKernelGGL(k_pool_hist, grid, dim3(kCT), 0, s, a);
+  hipLaunchKernelGGL(k_pool_mark, grid, dim3(kCT), 0, s, a);
+  hipLaunchKernelGGL(k_pool_final, dim3((unsigned)a.n_q), dim3(kFT), 0, s, a);
   return hipGetLastError();
 }
 

@@ -144,10 +144,27 @@ csa2_status csa2_encode_kv(int64_t n, const uint16_t* latent, const uint16_t* ro
  *                written for j < nb; entries at j >= nb are left untouched;
  *                ld_block_scores >= ceil((max_visible - W) / 8) and a
  *                multiple of 4.
- * One kernel, no workspace.  Queries with n <= W write nothing. */
+ *   pool_ws      optional (NULL, 0): a workspace of
+ *                csa2_index_pool_workspace_size bytes.  When given, the scan
+ *                also leaves in it what the first pass of csa2_index_pool
+ *                computes (each tile's smallest and largest block score, and
+ *                a cleared histogram), so that the following csa2_index_pool
+ *                call on these block scores, passed the same workspace and
+ *                CSA2_POOL_WS_FROM_SCAN, skips that pass.
+ * One kernel.  Queries with n <= W write no block scores. */
 csa2_status csa2_index_scan(const csa2_dims* dims, const csa2_queries* q,
                             const uint8_t* idx_q, const float* idx_w, const uint8_t* idx_k,
-                            float* block_scores, int64_t ld_block_scores, void* stream);
+                            float* block_scores, int64_t ld_block_scores,
+                            void* pool_ws, size_t pool_ws_bytes, void* stream);
+
+/* csa2_index_pool flag: the workspace was passed to the csa2_index_scan call
+ * that wrote these block scores, and since then it was used only by
+ * csa2_index_pool calls on the same block scores. */
+#define CSA2_POOL_WS_FROM_SCAN 1
+
+/* Workspace bytes for csa2_index_pool (256-byte aligned start required). */
+csa2_status csa2_index_pool_workspace_size(const csa2_dims* dims, const csa2_queries* q,
+                                           size_t* bytes);
 
 /* Full-mode indexer, stage 2 of 2: the candidate pool ([atlas] §3.2: the
  * Top-2048 blocks of 8 form the pool).  pool = the min(P, nb) blocks with the
@@ -156,21 +173,29 @@ csa2_status csa2_index_scan(const csa2_dims* dims, const csa2_queries* q,
  *                ld_block_scores rules)
  *   pool_blocks  int32 [n_q, P]  ascending block ids, -1 after pool_count
  *   pool_count   int32 [n_q]     (0 for queries with n <= W)
- * One kernel, no workspace. */
+ *   ws, ws_bytes workspace of csa2_index_pool_workspace_size bytes; its
+ *                contents need no initialisation unless flags holds
+ *                CSA2_POOL_WS_FROM_SCAN (see csa2_index_scan).
+ *   flags        0 or CSA2_POOL_WS_FROM_SCAN.
+ * Four kernels (per-chunk key range, histogram, marking; one exact final
+ * step per query), three with CSA2_POOL_WS_FROM_SCAN. */
 csa2_status csa2_index_pool(const csa2_dims* dims, const csa2_queries* q,
                             const float* block_scores, int64_t ld_block_scores,
-                            int32_t* pool_blocks, int32_t* pool_count, void* stream);
+                            int32_t* pool_blocks, int32_t* pool_count,
+                            void* ws, size_t ws_bytes, int32_t flags, void* stream);
 
-/* Workspace bytes for csa2_index_full (256-byte aligned start required);
- * used only when block_scores is NULL. */
+/* Workspace bytes for csa2_index_full (256-byte aligned start required):
+ * the pool workspace followed by room for the block scores. */
 csa2_status csa2_index_full_workspace_size(const csa2_dims* dims, const csa2_queries* q,
                                            size_t* bytes);
 
-/* Full-mode indexer: csa2_index_scan followed by csa2_index_pool.
+/* Full-mode indexer: csa2_index_scan followed by csa2_index_pool, the scan
+ * preparing the pool workspace (CSA2_POOL_WS_FROM_SCAN).
  *   block_scores  optional float [n_q, ld_block_scores]; NULL keeps the
  *               block scores in the workspace instead.
- *   ws, ws_bytes  workspace of csa2_index_full_workspace_size bytes (may be
- *               NULL / 0 when block_scores is given). */
+ *   ws, ws_bytes  workspace of csa2_index_full_workspace_size bytes (when
+ *               block_scores is given, csa2_index_pool_workspace_size bytes
+ *               suffice). */
 csa2_status csa2_index_full(const csa2_dims* dims, const csa2_queries* q,
                             const uint8_t* idx_q, const float* idx_w, const uint8_t* idx_k,
                             int32_t* pool_blocks, int32_t* pool_count,

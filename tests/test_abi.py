@@ -1,0 +1,127 @@
+"""Host-side checks of the C ABI (no GPU needed).
+
+The library must load, export every function include/csa2.h declares, and
+reject bad arguments synchronously with the documented status before it
+touches a device.  Workspace-size queries are pure host arithmetic.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import compressed_sparse_attention_decode_amd as csa2
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "csa2.h")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE, HIP = 0, 1, 2, 3, 4
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return re.findall(r"^\s*(?:const\s+)?[A-Za-z_]\w*\s*\*?\s*(csa2_\w+)\s*\(", src, re.M)
+
+
+def test_header_declares_the_entry_points():
+    names = set(declared_functions())
+    for n in ("csa2_encode_kv", "csa2_index_full", "csa2_index_reindex", "csa2_attend",
+              "csa2_index_scan", "csa2_index_pool", "csa2_status_string", "csa2_abi_version"):
+        assert n in names
+
+
+def test_library_exports_every_declared_function():
+    lib = ctypes.CDLL(csa2.lib_path)
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing, f"not exported: {missing}"
+
+
+def test_abi_version_and_status_strings():
+    L = csa2.lib()
+    assert L.csa2_abi_version() == 1
+    for st in (OK, INVALID, UNSUPPORTED, WORKSPACE, HIP):
+        assert L.csa2_status_string(st)
+    assert L.csa2_status_string(99)          # unknown codes still get text
+
+
+def _dims(**kw):
+    d = dict(n_heads=64, idx_heads=64, idx_dim=128, pool_blocks=2048, topk=512, swa=128)
+    d.update(kw)
+    return csa2.Dims(**d)
+
+
+class _HostBatch:
+    """Query batch for host-side calls: non-null placeholder device pointers
+    that the argument checks never dereference."""
+
+    def __init__(self, n_q=8, max_visible=131072, g=1):
+        self.n_q, self.max_visible, self.g = n_q, max_visible, g
+
+    def c(self):
+        return csa2._Queries(self.n_q, self.g, self.max_visible, 0, 0x10000, 0x20000)
+
+
+def _batch(**kw):
+    return _HostBatch(**kw)
+
+
+def _call_ws(fn, dims, batch):
+    n = ctypes.c_size_t(0)
+    d, q = dims.c(), batch.c()
+    st = fn(ctypes.byref(d), ctypes.byref(q), ctypes.byref(n))
+    return st, n.value
+
+
+@pytest.mark.parametrize("bad", [
+    dict(idx_dim=96), dict(n_heads=24), dict(n_heads=0), dict(idx_heads=0), dict(idx_heads=65),
+    dict(pool_blocks=0), dict(pool_blocks=4096), dict(topk=0), dict(topk=8 * 16 + 1, pool_blocks=16),
+    dict(swa=-1), dict(swa=2048),
+])
+def test_bad_dims_rejected(bad):
+    L = csa2.lib()
+    st, _ = _call_ws(L.csa2_attend_workspace_size, _dims(**bad), _batch())
+    assert st == INVALID
+    assert L.csa2_last_error()
+
+
+@pytest.mark.parametrize("kw", [dict(n_q=0), dict(max_visible=(1 << 21) + 1), dict(g=3), dict(g=5),
+                                dict(max_visible=-1)])
+def test_bad_queries_rejected(kw):
+    L = csa2.lib()
+    st, _ = _call_ws(L.csa2_index_full_workspace_size, _dims(), _batch(**kw))
+    assert st == INVALID
+
+
+def test_workspace_sizes_are_consistent():
+    L = csa2.lib()
+    dims = _dims()
+    for n_q, mv in [(1, 4096), (8, 131072), (1, 1048576), (256, 524291)]:
+        b = _batch(n_q=n_q, max_visible=mv, g=4 if n_q == 256 else 1)
+        st, full = _call_ws(L.csa2_index_full_workspace_size, dims, b)
+        assert st == OK
+        st, pool = _call_ws(L.csa2_index_pool_workspace_size, dims, b)
+        assert st == OK
+        nb = -(-(mv - dims.swa) // 8)
+        # full = pool workspace + a block-score array of at least nb floats per query
+        assert full >= pool + n_q * nb * 4
+        assert pool % 256 == 0 and full % 256 == 0
+        st, rx = _call_ws(L.csa2_index_reindex_workspace_size, dims, b)
+        assert st == OK and rx >= n_q * dims.pool_blocks * 8 * 4
+        st, at = _call_ws(L.csa2_attend_workspace_size, dims, b)
+        assert st == OK and at % 256 == 0
+
+
+def test_null_pointers_rejected_before_any_device_work():
+    L = csa2.lib()
+    d, q = _dims().c(), _batch().c()
+    st = L.csa2_index_scan(ctypes.byref(d), ctypes.byref(q), None, None, None, None, 0, None, 0, None)
+    assert st == INVALID
+    assert b"NULL" in L.csa2_last_error()
+    st = L.csa2_encode_kv(-1, None, None, None, None, None, None, None)
+    assert st == INVALID
+    st = L.csa2_index_pool(ctypes.byref(d), ctypes.byref(q), 0x1000, 16384, 0x2000, 0x3000, 0x4000, 1 << 30,
+                           2, None)
+    assert st == INVALID and b"flags" in L.csa2_last_error()
+    st = L.csa2_encode_kv(0, None, None, None, None, None, None, None)
+    assert st in (OK, INVALID)

@@ -247,3 +247,30 @@ def test_ties_lower_position_wins():
     assert np.array_equal(pool.cpu().numpy()[0, :cnt.item()], rpool)
     keep, _, _ = oq.reindex(0, rpool)
     assert np.array_equal(tk.cpu().numpy()[0, :tc.item()], keep)
+
+
+def test_pool_paths_agree(case):
+    """csa2_index_full (scan-prepared pool workspace), csa2_index_scan +
+    csa2_index_pool (the pool's own key-range pass), and repeated pool calls
+    on one scan-prepared workspace give the same pool bit for bit."""
+    name, g, lay = case
+    w = g.w
+    csa2 = g.csa2
+    q, wt = g.iq(0)
+    ref_pool, ref_cnt, _ = g.full(0)
+    bs = csa2.index_scan(g.dims, g.batch, q, wt, g.idx_k)
+    p1, c1 = csa2.index_pool(g.dims, g.batch, bs)
+    ws = torch.empty(csa2.workspace_pool(g.dims, g.batch) + 256, dtype=torch.uint8, device="cuda")
+    bs2 = csa2.index_scan(g.dims, g.batch, q, wt, g.idx_k, pool_ws=ws)
+    outs = [csa2.index_pool(g.dims, g.batch, bs2, ws=ws, from_scan=True) for _ in range(3)]
+    torch.cuda.synchronize()
+    nb = csa2.n_blocks(g.dims, g.batch)
+    for qi in range(w.n_q):     # rows are written up to each query's own block count
+        k = max(0, -(-(lay.q_visible[qi] - w.dims.swa) // 8))
+        assert torch.equal(bs[qi, :k].view(torch.int32), bs2[qi, :k].view(torch.int32))
+    assert nb >= 0
+    for p, c in [(p1, c1)] + outs:
+        assert torch.equal(c, ref_cnt), f"{name}: pool counts differ between paths"
+        for qi in range(w.n_q):
+            k = int(ref_cnt[qi])
+            assert torch.equal(p[qi, :k], ref_pool[qi, :k]), f"{name} q{qi}: pools differ between paths"
