@@ -22,7 +22,8 @@ EXTRA = {"scan.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-fno-honor-nans"],
 # No fast-math: the FP4 encoder needs the correctly rounded fp32 division.
 # Packed fp32 instructions are disabled for every device compile.
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
-         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-Rpass-analysis=kernel-resource-usage"]
 
 
 def hipcc() -> str:
@@ -39,6 +40,20 @@ def _run(cmd):
     return r.returncode, out
 
 
+def _resource_usage(out: str):
+    """(kernel, VGPRs, scratch bytes per lane) from the compiler's
+    kernel-resource-usage remarks."""
+    res, name, vgpr = [], None, None
+    for line in out.splitlines():
+        if "remark: Function Name:" in line:
+            name = line.split("Function Name:")[1].split("[")[0].strip()
+        elif "remark:     VGPRs:" in line:
+            vgpr = int(line.split("VGPRs:")[1].split("[")[0])
+        elif "remark:     ScratchSize [bytes/lane]:" in line and name:
+            res.append((name, vgpr, int(line.split(":")[-1].split("[")[0])))
+    return res
+
+
 def build(verbose: bool = False) -> str:
     cc = hipcc()
     obj_dir = os.path.join(PKG, "_build")
@@ -50,9 +65,21 @@ def build(verbose: bool = False) -> str:
     with cf.ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:
         results = list(ex.map(lambda j: (j[0], *_run(j[1])), jobs))
     failed = [(s, out) for s, rc, out in results if rc != 0]
+    spills = []
     for s, rc, out in results:
-        if verbose and out.strip():
-            print(f"[{s}]\n{out}", file=sys.stderr)
+        usage = _resource_usage(out)
+        spills += [f"{s}: {k} uses {b} B/lane of scratch ({v} VGPRs)" for k, v, b in usage if b > 0]
+        if verbose:
+            for k, v, b in usage:
+                print(f"[{s}] {k}: {v} VGPRs, scratch {b}", file=sys.stderr)
+            rest = "\n".join(l for l in out.splitlines() if "remark" not in l and "kernel-resource-usage" not in l
+                             and not l.strip().startswith(("|", "^")) and l.strip() and not l.strip()[0].isdigit())
+            if rest.strip():
+                print(f"[{s}]\n{rest}", file=sys.stderr)
+    # a register spill to scratch memory costs more than any kernel here can
+    # afford: fail the build rather than ship one
+    if spills:
+        failed.append(("register spills", "\n".join(spills)))
     if failed:
         msg = "\n".join(f"== {s}\n{out}" for s, out in failed)
         raise RuntimeError(f"hipcc failed:\n{msg}")

@@ -43,19 +43,20 @@ constexpr int kMaxSplit = 2048 + 1024;    // entries of one split (topk + swa bo
 typedef short v4s __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4s lds_v4s;
 
-__device__ __forceinline__ float e2m1_value(uint32_t nib) {
-  const uint32_t m = nib & 7u;
-  float v = m < 2 ? 0.5f * (float)m : __uint_as_float((((m >> 1) + 126u) << 23) | ((m & 1u) << 22));
-  return (nib & 8u) ? -v : v;
-}
-
-__device__ __forceinline__ uint32_t pack_h2(float x, float y) {
-  const _Float16 a = (_Float16)x, b = (_Float16)y;
-  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
-}
-
+// bf16 pair -> f16 pair.  Exact for values inside the f16 range (the ABI's
+// |x| < 65504 precondition); round-toward-zero only matters outside it.
 __device__ __forceinline__ uint32_t bf16x2_to_h2(uint32_t w) {
-  return pack_h2(__uint_as_float(w << 16), __uint_as_float(w & 0xFFFF0000u));
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(__uint_as_float(w << 16), __uint_as_float(w & 0xFFFF0000u)));
+}
+
+// Four code bytes (eight E2M1 values, low nibble first) times an E4M3 scale,
+// as four f16 pairs.  The gfx950 conversion at scale 1.0 is exact, and so is
+// the f16 product: E2M1 x E4M3 needs at most 6 significant bits and lies in
+// [2^-13, 2688].
+template <int B>
+__device__ __forceinline__ uint32_t fp4_byte_h2(uint32_t word, v2h s2) {
+  const v2h x = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, B);
+  return __builtin_bit_cast(uint32_t, x * s2);
 }
 
 constexpr int kItems = kTile * 32 / kNT;      // (entry, 16-channel group) items per thread
@@ -111,15 +112,11 @@ __device__ __forceinline__ void store_tile(const AttendArgs& a, const int32_t* r
       h0 = v4u{bf16x2_to_h2(x0[0]), bf16x2_to_h2(x0[1]), bf16x2_to_h2(x0[2]), bf16x2_to_h2(x0[3])};
       h1 = v4u{bf16x2_to_h2(x1[0]), bf16x2_to_h2(x1[1]), bf16x2_to_h2(x1[2]), bf16x2_to_h2(x1[3])};
     } else {
-      const float s = e4m3_to_float(t.c[k][2]);
-      uint32_t hv[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const uint32_t byte = (t.c[k][j >> 2] >> (8 * (j & 3))) & 0xFFu;
-        hv[j] = pack_h2(e2m1_value(byte & 15u) * s, e2m1_value(byte >> 4) * s);   // exact
-      }
-      h0 = v4u{hv[0], hv[1], hv[2], hv[3]};
-      h1 = v4u{hv[4], hv[5], hv[6], hv[7]};
+      const _Float16 sh = (_Float16)e4m3_to_float(t.c[k][2]);     // exact
+      const v2h s2 = {sh, sh};
+      const uint32_t c0 = t.c[k][0], c1 = t.c[k][1];
+      h0 = v4u{fp4_byte_h2<0>(c0, s2), fp4_byte_h2<1>(c0, s2), fp4_byte_h2<2>(c0, s2), fp4_byte_h2<3>(c0, s2)};
+      h1 = v4u{fp4_byte_h2<0>(c1, s2), fp4_byte_h2<1>(c1, s2), fp4_byte_h2<2>(c1, s2), fp4_byte_h2<3>(c1, s2)};
     }
     v4u* dk = reinterpret_cast<v4u*>(s_k + e * kKS + grp * 16);
     dk[0] = h0;

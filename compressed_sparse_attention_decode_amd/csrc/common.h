@@ -100,6 +100,21 @@ __device__ __forceinline__ float max_lanes8(float v) {
   return fmaxf(v, dpp_mov<0x141>(v));
 }
 
+// Reduction over the 64 lanes of a wave without LDS: DPP within each row of
+// 16 (quad_perm [1,0,3,2], [2,3,0,1], row_half_mirror, row_mirror), then the
+// gfx950 row swaps across the four rows.  Every lane ends with the result.
+template <typename Op>
+__device__ __forceinline__ uint32_t wave_reduce_u32(uint32_t v, Op op) {
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false));
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false));
+  auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  v = op(r[0], r[1]);
+  r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return op(r[0], r[1]);
+}
+
 // Block-wide exclusive scan of one uint32 per thread (blockDim.x = NT, a
 // multiple of 64).  `sh` needs NT/64 + 1 words.  Returns the exclusive prefix;
 // *total receives the block sum.  Contains __syncthreads().

@@ -14,8 +14,8 @@
 //    workgroup is issued before the first contraction (the kernel is short
 //    and latency-bound).  Scores are written as order-preserving uint32 keys,
 //    0 marking a slot that holds no candidate position;
-//  * k_topk_select: one 1024-thread workgroup per query keeps its <= 16,384
-//    keys in registers (16 consecutive pool slots per thread), finds the K-th
+//  * k_topk_select: one 512-thread workgroup per query keeps its <= 16,384
+//    keys in registers (32 consecutive pool slots per thread), finds the K-th
 //    largest with a radix select of up to 11-bit digits starting at the
 //    highest bit where the smallest and largest key differ (common leading
 //    bits would pile every key onto one counter), and compacts in pool order
@@ -116,11 +116,13 @@ __global__ __launch_bounds__(256) void k_reindex_score(ReindexArgs a) {
   }
 }
 
-constexpr int kTkThreads = 1024;
+constexpr int kTkThreads = 512;                    // 8 waves: up to 256 VGPRs per thread
 constexpr int kMaxCand = 2048 * kBlock;
-constexpr int kPer = kMaxCand / kTkThreads;        // 16 keys per thread, in registers
+constexpr int kPer = kMaxCand / kTkThreads;        // 32 keys per thread, in registers
+constexpr int kBlkPer = kPer / kBlock;             // pool blocks per thread
 constexpr int kTkBins = 2048;                      // radix digit: up to 11 bits
 constexpr int kTkWaves = kTkThreads / 64;
+constexpr int kRankCap = 128;                     // candidates ranked exactly against each other (quadratic)
 
 // Wave 0 finds, in a kTkBins histogram, the bin where the count from the top
 // first reaches `need`: out[0] = bin, out[1] = keys in higher bins,
@@ -155,50 +157,50 @@ __device__ __forceinline__ void crossing_2048(const uint32_t* hist, uint32_t nee
 }
 
 __global__ __launch_bounds__(kTkThreads) void k_topk_select(ReindexArgs a) {
-  __shared__ uint32_t s_hist[kTkBins];
+  __shared__ uint32_t s_hist[kTkBins + 1];          // + a bin that collects empty slots
+  __shared__ uint64_t s_cand[kRankCap];
   __shared__ uint32_t s_red[3 * kTkWaves];
   __shared__ uint32_t s_scan[kTkWaves + 1];
   __shared__ uint32_t s_misc[4];
 
   const int q = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int N = a.pool_count[q] * kBlock;
   const int K = a.topk;
   const int32_t* pool = a.pool_blocks + (int64_t)q * a.pool;
   const uint32_t* ks = a.keys + (int64_t)q * a.pool * kBlock;
   int32_t* out = a.topk_pos + (int64_t)q * K;
   float* out_s = a.topk_scores ? a.topk_scores + (int64_t)q * K : nullptr;
 
-  // thread t holds slots [16t, 16t + 16) (pool order = ascending positions)
-  // and the two pool blocks they belong to; N is a multiple of 8, so each
-  // 4-key vector and each block is wholly valid or not
+  // thread t holds slots [kPer t, kPer (t + 1)) (pool order = ascending
+  // positions) and the pool blocks they belong to.  The loads do not wait for
+  // the pool count (the rows always hold 8P keys and P blocks): slots past
+  // the count are masked once it arrives.  Empty slots are key 0.
   uint32_t key[kPer];
-  int32_t blk[2];
+  int32_t blk[kBlkPer];
+  const bool mine = tid * kPer < a.pool * kBlock;
 #pragma unroll
   for (int v = 0; v < kPer / 4; ++v) {
     const int i = tid * kPer + v * 4;
-    const v4u x = i < N ? *reinterpret_cast<const v4u*>(ks + i) : v4u{0u, 0u, 0u, 0u};
+    const v4u x = mine ? *reinterpret_cast<const v4u*>(ks + i) : v4u{0u, 0u, 0u, 0u};
     key[4 * v] = x[0]; key[4 * v + 1] = x[1]; key[4 * v + 2] = x[2]; key[4 * v + 3] = x[3];
   }
 #pragma unroll
-  for (int j = 0; j < 2; ++j) blk[j] = tid * kPer + 8 * j < N ? pool[tid * 2 + j] : 0;
-  for (int i = tid; i < kTkBins; i += kTkThreads) s_hist[i] = 0;
+  for (int j = 0; j < kBlkPer; ++j) blk[j] = mine ? pool[tid * kBlkPer + j] : 0;
+  const int N = a.pool_count[q] * kBlock;
+  for (int i = tid; i <= kTkBins; i += kTkThreads) s_hist[i] = 0;
+  if (tid == 0) s_misc[3] = 0;
 
-  // count of valid keys, their min and max: one barrier
+  // count of valid keys, their min and max (branch-free; one barrier)
   uint32_t nvalid = 0, lo = 0xFFFFFFFFu, hi = 0;
 #pragma unroll
   for (int k = 0; k < kPer; ++k) {
-    if (key[k] != 0) {
-      ++nvalid;
-      lo = min(lo, key[k]);
-      hi = max(hi, key[k]);
-    }
+    key[k] = tid * kPer + k < N ? key[k] : 0u;
+    nvalid += key[k] != 0;
+    lo = min(lo, key[k] != 0 ? key[k] : 0xFFFFFFFFu);
+    hi = max(hi, key[k]);
   }
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) {
-    nvalid += __shfl_xor(nvalid, d, 64);
-    lo = min(lo, (uint32_t)__shfl_xor(lo, d, 64));
-    hi = max(hi, (uint32_t)__shfl_xor(hi, d, 64));
-  }
+  nvalid = wave_reduce_u32(nvalid, [](uint32_t x, uint32_t y) { return x + y; });
+  lo = wave_reduce_u32(lo, [](uint32_t x, uint32_t y) { return min(x, y); });
+  hi = wave_reduce_u32(hi, [](uint32_t x, uint32_t y) { return max(x, y); });
   if (lane == 0) {
     s_red[wave] = nvalid;
     s_red[kTkWaves + wave] = lo;
@@ -214,65 +216,141 @@ __global__ __launch_bounds__(kTkThreads) void k_topk_select(ReindexArgs a) {
   }
   const uint32_t keff = min((uint32_t)K, total);
 
-  // Radix select of the keff-th largest key, from the highest bit where the
-  // smallest and largest keys differ.  Stops early when the crossing digit's
-  // keys are all taken: then every key >= that digit's smallest value is in.
-  int64_t T = 0;              // keys > T are taken ...
-  uint32_t need_eq = 0;       // ... plus need_eq keys == T, lowest slots first
+  // Selection.  A histogram over kTkBins linear bins of the score range
+  // [min, max] (monotone in the key, and spread evenly, unlike bit digits of
+  // scores that share an exponent) gives the bin b1 holding the keff-th
+  // largest key.  Its keys are the candidates: up to kRankCap of them are
+  // ranked exactly against each other by (key desc, slot asc), which also
+  // settles ties, and the selected set is {key > T} plus {key == T, slot <=
+  // ST}.  More candidates: radix digits of up to 11 bits over the candidates'
+  // own key range narrow them first; a long run of equal keys falls back to
+  // admitting equal keys lowest slot first with a block scan.
+  int64_t T = 0;
+  int ST = -1;                // with T: keys == T at slots <= ST are taken
+  uint32_t need_eq = 0;       // fallback: need_eq keys == T, lowest slots first
+  bool by_scan = false;
   if (keff > 0) {
-    const int top = highest_diff_bit(kmin, kmax);
-    uint32_t prefix = (uint32_t)(((uint64_t)kmin >> (top + 1)) << (top + 1));
-    uint32_t need = keff;
-    int fixed_lo = top + 1;            // bits >= fixed_lo are decided
-    bool whole = false;
-    while (fixed_lo > 0) {
-      const int sh = max(0, fixed_lo - 11);
-      const uint32_t dmask = (1u << (fixed_lo - sh)) - 1;
+    const float flo = key_float(kmin), fhi = key_float(kmax);
+    float scale = (float)kTkBins / (fhi - flo);
+    if (!(scale > 0.0f && scale < 3.0e38f)) scale = 0.0f;    // all keys equal (or a huge range)
+    auto lbin = [&](uint32_t k) { return min((int)((key_float(k) - flo) * scale), kTkBins - 1); };
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) atomicAdd(&s_hist[key[k] != 0 ? lbin(key[k]) : kTkBins], 1u);
+    __syncthreads();
+    if (wave == 0) crossing_2048(s_hist, keff, s_misc);
+    __syncthreads();
+    const int b1 = (int)s_misc[0];
+    uint32_t need = keff - s_misc[1];
+    uint32_t cand = s_misc[2];
+    uint32_t cm = 0;                 // the thread's keys in bin b1
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) cm |= (uint32_t)(key[k] != 0 && lbin(key[k]) == b1) << k;
+    if (cand > (uint32_t)kRankCap) {
+      // Rare (a large crossing bin, e.g. many equal scores): radix digits
+      // over the candidates' own key range narrow them.  This path re-reads
+      // its keys from memory so that it adds no registers to the common one.
+      auto kget = [&](int k) -> uint32_t {
+        const int slot = tid * kPer + k;
+        return (cm >> k & 1u) ? ks[slot] : 0u;
+      };
+      for (int i = tid; i < kTkBins; i += kTkThreads) s_hist[i] = 0;
+      uint32_t clo = 0xFFFFFFFFu, chi = 0;
+#pragma unroll 1
+      for (int k = 0; k < kPer; ++k) {
+        const uint32_t x = kget(k);
+        clo = min(clo, x != 0 ? x : 0xFFFFFFFFu);
+        chi = max(chi, x);
+      }
+      clo = wave_reduce_u32(clo, [](uint32_t x, uint32_t y) { return min(x, y); });
+      chi = wave_reduce_u32(chi, [](uint32_t x, uint32_t y) { return max(x, y); });
+      if (lane == 0) { s_red[kTkWaves + wave] = clo; s_red[2 * kTkWaves + wave] = chi; }
+      __syncthreads();
+      clo = 0xFFFFFFFFu; chi = 0;
+#pragma unroll 1
+      for (int w = 0; w < kTkWaves; ++w) {
+        clo = min(clo, s_red[kTkWaves + w]);
+        chi = max(chi, s_red[2 * kTkWaves + w]);
+      }
+      int fixed_lo = highest_diff_bit(clo, chi) + 1;   // bits >= fixed_lo are decided
+      uint32_t prefix = (uint32_t)(((uint64_t)clo >> fixed_lo) << fixed_lo);
+      while (cand > (uint32_t)kRankCap && fixed_lo > 0) {
+        const int sh = max(0, fixed_lo - 11);
+        const uint32_t dmask = (1u << (fixed_lo - sh)) - 1;
+#pragma unroll 1
+        for (int k = 0; k < kPer; ++k) {
+          const uint32_t x = kget(k);
+          if (x != 0) atomicAdd(&s_hist[(x >> sh) & dmask], 1u);
+        }
+        __syncthreads();
+        if (wave == 0) crossing_2048(s_hist, need, s_misc);
+        __syncthreads();
+        prefix |= s_misc[0] << sh;
+        need -= s_misc[1];
+        cand = s_misc[2];
+        fixed_lo = sh;
+#pragma unroll 1
+        for (int k = 0; k < kPer; ++k) {
+          const uint32_t x = kget(k);
+          if (x != 0 && ((uint64_t)x >> fixed_lo) != ((uint64_t)prefix >> fixed_lo)) cm &= ~(1u << k);
+        }
+        for (int i = tid; i < kTkBins; i += kTkThreads) s_hist[i] = 0;   // for a next digit
+        __syncthreads();
+      }
+      if (cand > (uint32_t)kRankCap) {
+        T = (int64_t)prefix;           // all bits fixed: a long run of equal keys
+        need_eq = need;
+        by_scan = true;
+      }
+    }
+    if (!by_scan) {
+      // rank the candidates exactly: (key, ~slot) compared as one 64-bit value
 #pragma unroll
       for (int k = 0; k < kPer; ++k) {
-        if (key[k] != 0 && ((uint64_t)key[k] >> fixed_lo) == ((uint64_t)prefix >> fixed_lo))
-          atomicAdd(&s_hist[(key[k] >> sh) & dmask], 1u);
+        if (cm >> k & 1u) {
+          const uint32_t idx = atomicAdd(&s_misc[3], 1u);
+          s_cand[idx] = ((uint64_t)key[k] << 32) | (uint32_t)~(uint32_t)(tid * kPer + k);
+        }
       }
       __syncthreads();
-      if (wave == 0) crossing_2048(s_hist, need, s_misc);
+      for (uint32_t i = tid; i < cand; i += kTkThreads) {
+        const uint64_t ci = s_cand[i];
+        uint32_t r = 0;
+#pragma unroll 8
+        for (uint32_t j = 0; j < cand; ++j) r += s_cand[j] > ci;
+        if (r == need - 1) { s_misc[0] = (uint32_t)(ci >> 32); s_misc[1] = ~(uint32_t)ci; }
+      }
       __syncthreads();
-      const uint32_t bin = s_misc[0], above = s_misc[1], in_bin = s_misc[2];
-      prefix |= bin << sh;
-      need -= above;
-      fixed_lo = sh;
-      for (int i = tid; i < kTkBins; i += kTkThreads) s_hist[i] = 0;   // for the next digit
-      if (need == in_bin) { whole = true; break; }
-      __syncthreads();                 // the clear is ordered before the next digit's counts
-    }
-    if (whole) {
-      T = (int64_t)prefix - 1;         // prefix: smallest key value of the crossing digit
-      need_eq = 0;
-    } else {
-      T = (int64_t)prefix;
-      need_eq = need;
+      T = (int64_t)s_misc[0];
+      ST = (int)s_misc[1];
     }
   }
 
-  // ordered compaction: one scan of (ties, then selected) counts
-  uint32_t eq = 0;
-  if (keff > 0) {
+  // ordered compaction
+  uint32_t eq_before = 0;
+  if (by_scan) {
+    uint32_t eq = 0;
 #pragma unroll
     for (int k = 0; k < kPer; ++k) eq += key[k] != 0 && (int64_t)key[k] == T;
+    eq_before = block_exclusive_scan<kTkThreads>(eq, s_scan, &total);
   }
-  uint32_t eq_before = need_eq > 0 ? block_exclusive_scan<kTkThreads>(eq, s_scan, &total) : 0;
   uint32_t take = 0, flags = 0;
-  if (keff > 0) {
 #pragma unroll
-    for (int k = 0; k < kPer; ++k) {
-      bool sel = key[k] != 0 && (int64_t)key[k] > T;
-      if (key[k] != 0 && (int64_t)key[k] == T && eq_before < need_eq) { sel = true; ++eq_before; }
-      if (sel) { flags |= 1u << k; ++take; }
+  for (int k = 0; k < kPer; ++k) {
+    const int slot = tid * kPer + k;
+    bool sel = key[k] != 0 && ((int64_t)key[k] > T || ((int64_t)key[k] == T && slot <= ST));
+    if (by_scan) {
+      const bool eqk = key[k] != 0 && (int64_t)key[k] == T && eq_before < need_eq;
+      sel = sel || eqk;
+      eq_before += eqk;
     }
+    flags |= (uint32_t)sel << k;
+    take += sel;
   }
+  if (keff == 0) { flags = 0; take = 0; }
   uint32_t before = block_exclusive_scan<kTkThreads>(take, s_scan, &total);
 #pragma unroll
   for (int k = 0; k < kPer; ++k) {
-    if (flags & (1u << k)) {
+    if (flags >> k & 1u) {
       if (before < (uint32_t)K) {
         out[before] = blk[k >> 3] * kBlock + (k & 7);
         if (out_s) out_s[before] = key_float(key[k]);

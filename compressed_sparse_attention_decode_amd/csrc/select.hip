@@ -13,18 +13,19 @@
 //     clears the query's global histogram.  (The Full scan can write these
 //     (min, max) pairs per scan tile and clear the histogram itself; then K1
 //     is skipped.)
-//  K2 k_pool_hist: the bits above the highest bit where the query's min and
-//     max keys differ are common to every key, so a 4096-bin histogram of the
-//     next 12 bits spreads the keys (similar scores would otherwise pile onto
-//     a few counters); per chunk in LDS, then added to the query's histogram.
+//  K2 k_pool_hist: a histogram over 4096 linear bins of the query's score
+//     range [min, max] (monotone in the key, and spread evenly; bit digits of
+//     scores that share an exponent would pile onto a few counters); per
+//     chunk in LDS, then added to the query's histogram.
 //  K3 k_pool_mark: every chunk finds the bin b* holding the P-th best block,
 //     writes its blocks of higher bins as a bitmap and lists its blocks of
 //     bin b* as candidates.
-//  K4 k_pool_final: an exact radix select over the candidates' remaining
-//     bits gives the threshold key T and how many blocks equal to T are still
-//     needed; the ordered compaction of the bitmap writes ascending block ids,
-//     admitting blocks equal to T lowest id first; it clears the histogram
-//     again after reading it.  If a chunk listed more
+//  K4 k_pool_final: the candidates (usually a few dozen) are ranked exactly
+//     against each other by (key desc, block asc) and the best join the
+//     selection (more than 128 candidates: an exact radix select over the bits
+//     below their common prefix gives the threshold key and how many blocks
+//     equal to it are needed, admitted lowest id first); the ordered compaction of the
+//     bitmap writes ascending block ids; the histogram is cleared again.  If a chunk listed more
 //     candidates than its slots, this step re-reads the block scores instead
 //     (correct for any input, slow only for near-constant scores).
 #include "common.h"
@@ -37,6 +38,7 @@ namespace {
 constexpr int kCT = 256;                       // chunk workgroup threads
 constexpr int kFT = 1024;                      // final workgroup threads
 constexpr int kCandCap = 8192;                 // candidates the final step holds in LDS
+constexpr int kRankCap = 128;                 // candidates ranked exactly against each other (quadratic)
 constexpr int kMaxWords = kMaxBlocks / 32;
 static_assert(kPoolChunk == kCT * 16, "a chunk thread holds 16 blocks");
 static_assert(kHistBins == 4 * kFT, "the final step clears the histogram 4 words per thread");
@@ -76,56 +78,72 @@ __device__ __forceinline__ int query_blocks(const PoolArgs& a, int q) {
   return (c + 7) >> 3;
 }
 
-// The thread's 16 keys of a chunk: 4 x 16-byte loads, key e of load u is
-// block jb0(u) + e with jb0(u) = base + (u * kCT + tid) * 4; blocks >= nb are
-// masked out.  Row stride and base are multiples of 4 floats.
+// The thread's 16 blocks of a chunk: 4 x 16-byte loads, block e of load u is
+// jb0(u) + e with jb0(u) = base + (u * kCT + tid) * 4.  The loads are bounded
+// by the row stride only (a multiple of 4 floats), so they need not wait for
+// the query's block count; blocks >= nb are masked afterwards.
 struct ChunkKeys {
+  v4f x[4];
   uint32_t k[4][4];
   uint32_t vm[4];
+  __device__ __forceinline__ void load(const float* bs, int base, int64_t ld, int tid) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int jb0 = base + (u * kCT + tid) * 4;
+      x[u] = jb0 < ld ? *reinterpret_cast<const v4f*>(bs + jb0) : v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+  }
+  __device__ __forceinline__ void finish(int base, int nb, int tid) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int left = nb - (base + (u * kCT + tid) * 4);
+      vm[u] = left >= 4 ? 15u : (left <= 0 ? 0u : (1u << left) - 1u);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) k[u][e] = order_key(x[u][e]);
+    }
+  }
 };
 
-__device__ __forceinline__ void load_chunk(const float* bs, int base, int nb, int tid, ChunkKeys& c) {
-  v4f x[4];
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int jb0 = base + (u * kCT + tid) * 4;
-    x[u] = jb0 < nb ? *reinterpret_cast<const v4f*>(bs + jb0) : v4f{0.0f, 0.0f, 0.0f, 0.0f};
-  }
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int left = nb - (base + (u * kCT + tid) * 4);
-    c.vm[u] = left >= 4 ? 15u : (left <= 0 ? 0u : (1u << left) - 1u);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) c.k[u][e] = order_key(x[u][e]);
-  }
-}
-
 // The query's key range from the (min, max) pairs of its spans of blocks
-// (chunks of K1, or scan tiles).
+// (chunks of K1, or scan tiles).  load() issues the thread's first pair before
+// the block count is known; reduce() masks it and reads any further pairs.
 template <int NT>
-__device__ __forceinline__ void key_range(const PoolArgs& a, const PoolWs& w, int nb, uint32_t* s_scan,
-                                          uint32_t* kmin, uint32_t* kmax) {
-  const int n = (nb + a.mm_span - 1) / a.mm_span;
-  uint32_t lo = 0xFFFFFFFFu, hi = 0;
-  for (int i = threadIdx.x; i < n; i += NT) {
-    const v2u m = *reinterpret_cast<const v2u*>(w.mm + 2 * i);
-    lo = min(lo, m[0]);
-    hi = max(hi, m[1]);
+struct KeyRange {
+  v2u m0;
+  __device__ __forceinline__ void load(const PoolArgs& a, const PoolWs& w) {
+    const int i = threadIdx.x;
+    m0 = i < a.mm_cap ? *reinterpret_cast<const v2u*>(w.mm + 2 * i) : v2u{0xFFFFFFFFu, 0u};
   }
-  *kmin = block_min_u32<NT>(lo, s_scan);
-  *kmax = block_max_u32<NT>(hi, s_scan);
-}
+  __device__ __forceinline__ void reduce(const PoolArgs& a, const PoolWs& w, int nb, uint32_t* s_scan,
+                                         uint32_t* kmin, uint32_t* kmax) {
+    const int n = (nb + a.mm_span - 1) / a.mm_span;
+    uint32_t lo = 0xFFFFFFFFu, hi = 0;
+    if ((int)threadIdx.x < n) { lo = m0[0]; hi = m0[1]; }
+    for (int i = threadIdx.x + NT; i < n; i += NT) {
+      const v2u m = *reinterpret_cast<const v2u*>(w.mm + 2 * i);
+      lo = min(lo, m[0]);
+      hi = max(hi, m[1]);
+    }
+    *kmin = block_min_u32<NT>(lo, s_scan);
+    *kmax = block_max_u32<NT>(hi, s_scan);
+  }
+};
 
+// kHistBins linear bins of the score range [min, max]: monotone in the key
+// (so bins order the keys) and, unlike bit digits of scores that share an
+// exponent, spread evenly.  All keys equal (or a range that overflows): one bin.
 struct Bins {
-  int top, cs;        // histogram over key bits [cs, top]
-  uint32_t cmask;
+  float lo, scale;
+  __device__ __forceinline__ uint32_t bin(uint32_t key) const {
+    return (uint32_t)min((int)((key_float(key) - lo) * scale), kHistBins - 1);
+  }
 };
 
 __device__ __forceinline__ Bins bins_for(uint32_t kmin, uint32_t kmax) {
   Bins b;
-  b.top = highest_diff_bit(kmin, kmax);     // -1: all keys equal
-  b.cs = max(0, b.top - 11);
-  b.cmask = b.top < 0 ? 0u : (uint32_t)((2ull << (b.top - b.cs)) - 1);
+  b.lo = key_float(kmin);
+  b.scale = (float)kHistBins / (key_float(kmax) - b.lo);
+  if (!(b.scale > 0.0f && b.scale < 3.0e38f)) b.scale = 0.0f;
   return b;
 }
 
@@ -177,12 +195,13 @@ __global__ __launch_bounds__(kCT) void k_pool_minmax(PoolArgs a) {
     for (int i = tid * 4; i < kHistBins; i += kCT * 4)
       *reinterpret_cast<v4u*>(w.hist + i) = v4u{0u, 0u, 0u, 0u};
   }
-  const int nb = query_blocks(a, q);
   const int base = g * kPoolChunk;
+  ChunkKeys c;
+  c.load(a.bscore + (int64_t)q * a.ld, base, a.ld, tid);
+  const int nb = query_blocks(a, q);
   uint32_t lo = 0xFFFFFFFFu, hi = 0;
   if (nb > a.pool && base < nb) {
-    ChunkKeys c;
-    load_chunk(a.bscore + (int64_t)q * a.ld, base, nb, tid, c);
+    c.finish(base, nb, tid);
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
 #pragma unroll
@@ -207,21 +226,24 @@ __global__ __launch_bounds__(kCT) void k_pool_hist(PoolArgs a) {
   __shared__ uint32_t s_hist[kHistBins];
   __shared__ uint32_t s_scan[kCT / 64 + 1];
   const int q = blockIdx.x / a.chunks, g = blockIdx.x % a.chunks, tid = threadIdx.x;
-  const int nb = query_blocks(a, q);
   const int base = g * kPoolChunk;
-  if (nb <= a.pool || base >= nb) return;
   const PoolWs w = pool_ws(a, q);
   ChunkKeys c;
-  load_chunk(a.bscore + (int64_t)q * a.ld, base, nb, tid, c);
+  c.load(a.bscore + (int64_t)q * a.ld, base, a.ld, tid);
+  KeyRange<kCT> kr;
+  kr.load(a, w);
+  const int nb = query_blocks(a, q);
+  if (nb <= a.pool || base >= nb) return;
+  c.finish(base, nb, tid);
   for (int i = tid; i < kHistBins; i += kCT) s_hist[i] = 0;
   uint32_t kmin, kmax;
-  key_range<kCT>(a, w, nb, s_scan, &kmin, &kmax);     // its barriers order the clear
+  kr.reduce(a, w, nb, s_scan, &kmin, &kmax);     // its barriers order the clear
   const Bins b = bins_for(kmin, kmax);
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
 #pragma unroll
     for (int e = 0; e < 4; ++e)
-      if (c.vm[u] >> e & 1u) atomicAdd(&s_hist[(c.k[u][e] >> b.cs) & b.cmask], 1u);
+      if (c.vm[u] >> e & 1u) atomicAdd(&s_hist[b.bin(c.k[u][e])], 1u);
   }
   __syncthreads();
   for (int i = tid; i < kHistBins; i += kCT) {
@@ -237,20 +259,23 @@ __global__ __launch_bounds__(kCT) void k_pool_mark(PoolArgs a) {
   __shared__ uint32_t s_ccount;
   const int q = blockIdx.x / a.chunks, g = blockIdx.x % a.chunks;
   const int tid = threadIdx.x, lane = tid & 63;
-  const int nb = query_blocks(a, q);
   const int base = g * kPoolChunk;
   const PoolWs w = pool_ws(a, q);
+  ChunkKeys c;
+  c.load(a.bscore + (int64_t)q * a.ld, base, a.ld, tid);
+  HistSlice<kCT> h;
+  h.load(w.hist);
+  KeyRange<kCT> kr;
+  kr.load(a, w);
+  const int nb = query_blocks(a, q);
   if (nb <= a.pool || base >= nb) {
     if (tid == 0) w.cnt[g] = 0;
     return;
   }
-  ChunkKeys c;
-  load_chunk(a.bscore + (int64_t)q * a.ld, base, nb, tid, c);
-  HistSlice<kCT> h;
-  h.load(w.hist);
+  c.finish(base, nb, tid);
   if (tid == 0) s_ccount = 0;
   uint32_t kmin, kmax;
-  key_range<kCT>(a, w, nb, s_scan, &kmin, &kmax);
+  kr.reduce(a, w, nb, s_scan, &kmin, &kmax);
   const Bins b = bins_for(kmin, kmax);
   find_bstar<kCT>(h, (uint32_t)a.pool, s_scan, s_misc);
   const uint32_t bstar = s_misc[0];
@@ -264,7 +289,7 @@ __global__ __launch_bounds__(kCT) void k_pool_mark(PoolArgs a) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const bool v = c.vm[u] >> e & 1u;
-      const uint32_t bin = (c.k[u][e] >> b.cs) & b.cmask;
+      const uint32_t bin = b.bin(c.k[u][e]);
       hib |= (uint32_t)(v && bin > bstar) << e;
       cand |= (uint32_t)(v && bin == bstar) << e;
     }
@@ -310,32 +335,35 @@ __global__ __launch_bounds__(kFT) void k_pool_final(PoolArgs a) {
   __shared__ uint32_t s_misc[4];
 
   const int q = blockIdx.x, tid = threadIdx.x;
-  const int nb = query_blocks(a, q);
   const int P = a.pool, G = a.chunks;
+  const PoolWs w = pool_ws(a, q);
+  const float* bs = a.bscore + (int64_t)q * a.ld;
+
+  // every independent read issued before the first wait (none waits for the
+  // block count): the bitmap of blocks above b* (the query's whole region),
+  // the histogram, the chunks' candidate counts, the key-range pairs
+  constexpr int kSelPer = kMaxWords / kFT;
+  uint32_t selw[kSelPer];
+#pragma unroll
+  for (int k = 0; k < kSelPer; ++k) {
+    const int i = tid + k * kFT;
+    selw[k] = i < G * (kPoolChunk / 32) ? w.sel[i] : 0u;
+  }
+  HistSlice<kFT> h;
+  h.load(w.hist);
+  const uint32_t cnt_v = tid < G ? w.cnt[tid] : 0u;
+  KeyRange<kFT> kr;
+  kr.load(a, w);
+  const int nb = query_blocks(a, q);
   int32_t* out = a.pool_blocks + (int64_t)q * P;
   if (nb <= P) {
     for (int j = tid; j < P; j += kFT) out[j] = j < nb ? j : -1;
     if (tid == 0) a.pool_count[q] = nb;
     return;
   }
-  const PoolWs w = pool_ws(a, q);
-  const float* bs = a.bscore + (int64_t)q * a.ld;
   const int nw = (nb + 31) >> 5;
-
-  // every independent read issued before the first wait: the bitmap of
-  // blocks above b*, the histogram, the chunks' candidate counts, the key range
-  constexpr int kSelPer = kMaxWords / kFT;
-  uint32_t selw[kSelPer];
-#pragma unroll
-  for (int k = 0; k < kSelPer; ++k) {
-    const int i = tid + k * kFT;
-    selw[k] = i < nw ? w.sel[i] : 0u;
-  }
-  HistSlice<kFT> h;
-  h.load(w.hist);
-  const uint32_t cnt_v = tid < G ? w.cnt[tid] : 0u;
   uint32_t kmin, kmax;
-  key_range<kFT>(a, w, nb, s_scan, &kmin, &kmax);
+  kr.reduce(a, w, nb, s_scan, &kmin, &kmax);
 #pragma unroll
   for (int k = 0; k < kSelPer; ++k) {
     const int i = tid + k * kFT;
@@ -378,73 +406,107 @@ __global__ __launch_bounds__(kFT) void k_pool_final(PoolArgs a) {
   }
   __syncthreads();
 
-  // radix select inside bin b* over bits [0, cs)
-  uint32_t prefix = (uint32_t)(((uint64_t)kmin >> (b.top + 1)) << (b.top + 1)) | (bstar << b.cs);
-  int fixed_lo = b.cs;                  // bits >= fixed_lo are decided
-  while (fixed_lo > 0) {
-    const int sh = max(0, fixed_lo - 8);
-    const uint32_t dmask = (1u << (fixed_lo - sh)) - 1;
-    if (tid < 256) s_hist[tid] = 0;
+  // Up to kRankCap candidates held in LDS are ranked exactly against each
+  // other by (key desc, block asc); the best `need` join the selection.
+  // Otherwise a radix select over bits [0, cs) finds the threshold key T and
+  // how many blocks equal to T are needed, admitted lowest block first.
+  const bool ranked = in_lds && C <= (uint32_t)kRankCap;
+  uint32_t need_eq = 0;
+  if (ranked) {
+    for (uint32_t i = tid; i < C; i += kFT) {
+      const uint32_t ki = s_ckey[i];
+      const int ji = s_cj[i];
+      uint32_t r = 0;
+#pragma unroll 8
+      for (uint32_t j = 0; j < C; ++j) {
+        const uint32_t kj = s_ckey[j];
+        r += kj > ki || (kj == ki && s_cj[j] < ji);
+      }
+      if (r < need) atomicOr(&s_sel[ji >> 5], 1u << (ji & 31));
+    }
     __syncthreads();
+  } else {
+    // the candidates' own key range: its common leading bits are decided
+    uint32_t clo = 0xFFFFFFFFu, chi = 0;
+    if (in_lds) {
+      for (uint32_t i = tid; i < C; i += kFT) { clo = min(clo, s_ckey[i]); chi = max(chi, s_ckey[i]); }
+    } else {
+      for (int jb = tid; jb < nb; jb += kFT) {
+        const uint32_t key = order_key(bs[jb]);
+        if (b.bin(key) == bstar) { clo = min(clo, key); chi = max(chi, key); }
+      }
+    }
+    clo = block_min_u32<kFT>(clo, s_scan);
+    chi = block_max_u32<kFT>(chi, s_scan);
+    int fixed_lo = highest_diff_bit(clo, chi) + 1;     // bits >= fixed_lo are decided
+    uint32_t prefix = (uint32_t)(((uint64_t)clo >> fixed_lo) << fixed_lo);
+    while (fixed_lo > 0) {
+      const int sh = max(0, fixed_lo - 8);
+      const uint32_t dmask = (1u << (fixed_lo - sh)) - 1;
+      if (tid < 256) s_hist[tid] = 0;
+      __syncthreads();
+      if (in_lds) {
+        for (uint32_t i = tid; i < C; i += kFT) {
+          const uint32_t key = s_ckey[i];
+          if (same_above(key, prefix, fixed_lo)) atomicAdd(&s_hist[(key >> sh) & dmask], 1u);
+        }
+      } else {
+        for (int jb = tid; jb < nb; jb += kFT) {
+          const uint32_t key = order_key(bs[jb]);
+          if (b.bin(key) == bstar && same_above(key, prefix, fixed_lo))
+            atomicAdd(&s_hist[(key >> sh) & dmask], 1u);
+        }
+      }
+      __syncthreads();
+      find_crossing(s_hist, 256, need, s_misc);
+      __syncthreads();
+      prefix |= s_misc[0] << sh;
+      need -= s_misc[1];
+      fixed_lo = sh;
+      __syncthreads();
+    }
+    const uint32_t T = prefix;
+    need_eq = need;
+    // candidates above T join the selection; those equal to T are tie bits
     if (in_lds) {
       for (uint32_t i = tid; i < C; i += kFT) {
         const uint32_t key = s_ckey[i];
-        if (same_above(key, prefix, fixed_lo)) atomicAdd(&s_hist[(key >> sh) & dmask], 1u);
+        const int jb = s_cj[i];
+        if (key > T) atomicOr(&s_sel[jb >> 5], 1u << (jb & 31));
+        else if (key == T) atomicOr(&s_tie[jb >> 5], 1u << (jb & 31));
       }
     } else {
       for (int jb = tid; jb < nb; jb += kFT) {
         const uint32_t key = order_key(bs[jb]);
-        if (same_above(key, prefix, fixed_lo)) atomicAdd(&s_hist[(key >> sh) & dmask], 1u);
+        if (b.bin(key) != bstar) continue;
+        if (key > T) atomicOr(&s_sel[jb >> 5], 1u << (jb & 31));
+        else if (key == T) atomicOr(&s_tie[jb >> 5], 1u << (jb & 31));
       }
     }
     __syncthreads();
-    find_crossing(s_hist, 256, need, s_misc);
-    __syncthreads();
-    prefix |= s_misc[0] << sh;
-    need -= s_misc[1];
-    fixed_lo = sh;
-    __syncthreads();
   }
-  const uint32_t T = prefix;
-  const uint32_t need_eq = need;
 
-  // candidates above T join the selection; those equal to T are tie bits
-  if (in_lds) {
-    for (uint32_t i = tid; i < C; i += kFT) {
-      const uint32_t key = s_ckey[i];
-      const int jb = s_cj[i];
-      if (key > T) atomicOr(&s_sel[jb >> 5], 1u << (jb & 31));
-      else if (key == T) atomicOr(&s_tie[jb >> 5], 1u << (jb & 31));
-    }
-  } else {
-    for (int jb = tid; jb < nb; jb += kFT) {
-      const uint32_t key = order_key(bs[jb]);
-      if (((key >> b.cs) & b.cmask) != bstar) continue;
-      if (key > T) atomicOr(&s_sel[jb >> 5], 1u << (jb & 31));
-      else if (key == T) atomicOr(&s_tie[jb >> 5], 1u << (jb & 31));
-    }
-  }
-  __syncthreads();
-
-  // ordered compaction; ties admitted in ascending block order
+  // ordered compaction (ties, in the radix path, admitted in ascending block order)
   const int wpt = (nw + kFT - 1) / kFT;
   const int w_lo = min(nw, tid * wpt), w_hi = min(nw, w_lo + wpt);
-  uint32_t ties = 0, total;
-  for (int i = w_lo; i < w_hi; ++i) ties += __popc(s_tie[i]);
-  uint32_t tie_before = block_exclusive_scan<kFT>(ties, s_scan, &total);
-  uint32_t sel_local = 0;
-  for (int i = w_lo; i < w_hi; ++i) {
-    uint32_t t = s_tie[i], acc = 0;
-    while (t && tie_before < need_eq) {
-      const uint32_t bit = t & (0u - t);
-      acc |= bit;
-      t ^= bit;
-      ++tie_before;
+  uint32_t total;
+  if (!ranked) {
+    uint32_t ties = 0;
+    for (int i = w_lo; i < w_hi; ++i) ties += __popc(s_tie[i]);
+    uint32_t tie_before = block_exclusive_scan<kFT>(ties, s_scan, &total);
+    for (int i = w_lo; i < w_hi; ++i) {
+      uint32_t t = s_tie[i], acc = 0;
+      while (t && tie_before < need_eq) {
+        const uint32_t bit = t & (0u - t);
+        acc |= bit;
+        t ^= bit;
+        ++tie_before;
+      }
+      s_sel[i] |= acc;
     }
-    const uint32_t fin = s_sel[i] | acc;
-    s_sel[i] = fin;
-    sel_local += __popc(fin);
   }
+  uint32_t sel_local = 0;
+  for (int i = w_lo; i < w_hi; ++i) sel_local += __popc(s_sel[i]);
   uint32_t out_before = block_exclusive_scan<kFT>(sel_local, s_scan, &total);
   for (int i = w_lo; i < w_hi; ++i) {
     uint32_t fin = s_sel[i];
