@@ -447,6 +447,10 @@ def main():
                                        "traffic": measured_traffic(w2.name)}}
         print(f"[bench] {w2.name}: {res2['value']:.1f} queries/s, scan {res2['scan']['avg_us']} us = "
               f"{res2['scan']['achieved_gbs']} GB/s", file=sys.stderr, flush=True)
+        if args.cpu_seconds > 0:
+            # parity of the timed step's query against the oracle (one query)
+            _, secondary["parity"] = cpu_baseline(w2, st2, step2, 0.0)
+            print(f"[bench] {w2.name} parity {secondary['parity']}", file=sys.stderr, flush=True)
         del st2, step2
 
     d = w.dims
