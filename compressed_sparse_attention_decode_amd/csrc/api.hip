@@ -231,11 +231,14 @@ csa2_status run_scan(const csa2_dims* d, const csa2_queries* q, const uint8_t* i
   sa.idx_q = idx_q; sa.idx_w = idx_w; sa.idx_k = idx_k;
   sa.seq_base = q->seq_base; sa.n_visible = q->n_visible;
   sa.n_q = q->n_q; sa.hi = d->idx_heads; sa.d = d->idx_dim; sa.swa = d->swa; sa.g = q->tokens_per_seq;
-  int pf = kScanPrefetch;
+  int pf = kScanPrefetch, nw = kScanWaves;
   if (const char* env = getenv("CSA2_SCAN_PREFETCH")) pf = atoi(env);
-  if (pf != 4 && pf != 6 && pf != 8) pf = kScanPrefetch;
+  if (const char* env = getenv("CSA2_SCAN_WAVES")) nw = atoi(env);
+  if (pf != 4 && pf != 6) pf = kScanPrefetch;
+  if (nw != 4 && nw != 8) nw = kScanWaves;
   sa.tile_pos = scan_tile();
   sa.prefetch = pf;
+  sa.waves = nw;
   sa.tiles = scan_tiles(d, q, sa.tile_pos);
   sa.bscore = block_scores;
   sa.ld = ld_block_scores;

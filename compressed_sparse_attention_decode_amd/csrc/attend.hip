@@ -39,6 +39,7 @@ constexpr int kNW = kAttendWaves;         // waves per workgroup, 16 heads each
 constexpr int kNT = 64 * kNW;
 constexpr int kKS = kKeyDim + 8;          // f16 row stride of the tile image
 constexpr int kMaxSplit = 2048 + 1024;    // entries of one split (topk + swa bounds)
+constexpr int kRowPer = (kMaxSplit + kNT - 1) / kNT;   // kept positions per thread
 
 typedef short v4s __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4s lds_v4s;
@@ -146,16 +147,17 @@ __global__ __launch_bounds__(kNT) void k_attend(AttendArgs a) {
   const int head0 = (hg * kNW + wave) * 16;
   const bool active = head0 < H;           // wave-uniform
 
-  const int n = a.n_visible[q];
-  const int c = max(0, n - a.swa);
-  const int Es = min(a.topk_count[q], a.topk);
-  const int E = Es + (n - c);
   const int e_begin = sp * a.split_entries;
-  const int e_end = min(E, e_begin + a.split_entries);
-  const int64_t seq_base = a.seq_base[q];
-  const int64_t swa_base = a.swa_base[q];
   const int32_t* tk = a.topk_pos + (int64_t)q * a.topk;
-
+  int32_t tkv[kRowPer];
+  {
+    const int e_lim = min(a.topk, e_begin + a.split_entries);
+#pragma unroll
+    for (int j = 0; j < kRowPer; ++j) {
+      const int e = e_begin + tid + j * kNT;
+      tkv[j] = e < e_lim ? tk[e] : 0;
+    }
+  }
   // the wave's 16 query heads as f16 rows [head][576] (the B operand of
   // Q.K^T): all 18 loads per lane issued before the first use
   constexpr int kQv = 16 * (kKeyDim / 8) / 64;
@@ -169,7 +171,32 @@ __global__ __launch_bounds__(kNT) void k_attend(AttendArgs a) {
                           : *reinterpret_cast<const v4u*>(a.q_rope + qh * kRope + (d - kLatent));
     }
   }
-  for (int e = e_begin + tid; e < e_end; e += kNT) s_row[e - e_begin] = e < Es ? tk[e] : -1 - (e - Es);
+  const int n = a.n_visible[q];
+  const int c = max(0, n - a.swa);
+  const int Es = min(a.topk_count[q], a.topk);
+  const int E = Es + (n - c);
+  const int e_end = min(E, e_begin + a.split_entries);
+  const int64_t seq_base = a.seq_base[q];
+  const int64_t swa_base = a.swa_base[q];
+
+  {
+    // the split's kept positions: the row always holds `topk` entries, so
+    // these loads were issued before the counts (a.n_visible, a.topk_count)
+    // they are filtered by arrived
+#pragma unroll
+    for (int j = 0; j < kRowPer; ++j) {
+      const int e = e_begin + tid + j * kNT;
+      if (e < e_end) s_row[e - e_begin] = e < Es ? tkv[j] : -1 - (e - Es);
+    }
+  }
+  __syncthreads();
+  // raw tiles two deep: tiles t and t+1 are in flight while t-1 is contracted
+  RawTile ra, rb;
+  if (e_begin < e_end) load_tile(a, s_row, min(kTile, e_end - e_begin), seq_base, swa_base, tid, ra);
+  if (e_begin + kTile < e_end)
+    load_tile(a, s_row + kTile, min(kTile, e_end - e_begin - kTile), seq_base, swa_base, tid, rb);
+  // the query into LDS while the first tiles are in flight (read after the
+  // first tile's barriers)
   if (active) {
     _Float16* sq = s_q + wave * 16 * kKS;
 #pragma unroll
@@ -179,12 +206,6 @@ __global__ __launch_bounds__(kNT) void k_attend(AttendArgs a) {
           v4u{bf16x2_to_h2(rq[j][0]), bf16x2_to_h2(rq[j][1]), bf16x2_to_h2(rq[j][2]), bf16x2_to_h2(rq[j][3])};
     }
   }
-  __syncthreads();
-  // raw tiles two deep: tiles t and t+1 are in flight while t-1 is contracted
-  RawTile ra, rb;
-  if (e_begin < e_end) load_tile(a, s_row, min(kTile, e_end - e_begin), seq_base, swa_base, tid, ra);
-  if (e_begin + kTile < e_end)
-    load_tile(a, s_row + kTile, min(kTile, e_end - e_begin - kTile), seq_base, swa_base, tid, rb);
   const _Float16* sqw = s_q + (wave * 16 + col) * kKS + gq * 8;
 
   float m = -__builtin_inff(), l = 0.0f;
@@ -282,12 +303,13 @@ __global__ __launch_bounds__(kNT) void k_attend(AttendArgs a) {
     if (a.lse && gq == 0)
       a.lse[(int64_t)q * H + head0 + col] = l > 0.0f ? (m + log2f(l)) * 0.69314718055994531f : -__builtin_inff();
   } else {
-    float* po = a.part_o + (((int64_t)q * S + sp) * H + head0) * kLatent;
+    // partial o of the wave's 16 heads in the accumulators' own layout
+    // [nt][lane][4] (one 1 KiB coalesced store per nt); k_attend_combine
+    // reads it back in the same layout
+    float* po = a.part_o + (((int64_t)q * S + sp) * (H / 16) + head0 / 16) * (kLatent * 16);
 #pragma unroll
-    for (int nt = 0; nt < kLatent / 16; ++nt) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) po[(4 * gq + i) * kLatent + nt * 16 + col] = o[nt][i];
-    }
+    for (int nt = 0; nt < kLatent / 16; ++nt)
+      *reinterpret_cast<v4f*>(po + (nt * 64 + lane) * 4) = o[nt];
     if (gq == 0) {
       float* pm = a.part_ml + (((int64_t)q * S + sp) * H + head0 + col) * 2;
       pm[0] = m;
@@ -297,45 +319,51 @@ __global__ __launch_bounds__(kNT) void k_attend(AttendArgs a) {
 }
 
 // Merge split partials: out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s.
-// A workgroup per (query, head); every partial load is issued up front.
-__global__ __launch_bounds__(128) void k_attend_combine(AttendArgs a) {
-  const int q = blockIdx.x / a.heads, h = blockIdx.x % a.heads;
-  const int S = a.splits, H = a.heads;
-  const int d0 = threadIdx.x * 4;
-  float ms[kAttendMaxSplits], ls[kAttendMaxSplits];
+// A workgroup takes one query's 16-head block and 4 of its 32 accumulator
+// tiles; a thread owns one accumulator slot (4 heads x 1 dim) and issues all
+// of its partial loads (every split) before the first use.
+__global__ __launch_bounds__(256) void k_attend_combine(AttendArgs a) {
+  const int S = a.splits, H = a.heads, HB = H / 16;
+  const int q = blockIdx.x / (HB * 8), hb = (blockIdx.x / 8) % HB, ntg = blockIdx.x % 8;
+  const int lane = threadIdx.x & 63, nt = ntg * 4 + (threadIdx.x >> 6);
+  const int gq = lane >> 4, col = lane & 15;
+  const int h0 = hb * 16 + 4 * gq;
   v4f os[kAttendMaxSplits];
+  float ms[kAttendMaxSplits][4], ls[kAttendMaxSplits][4];
 #pragma unroll
   for (int s = 0; s < kAttendMaxSplits; ++s) {
-    ms[s] = -__builtin_inff();
-    ls[s] = 0.0f;
     os[s] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { ms[s][i] = -__builtin_inff(); ls[s][i] = 0.0f; }
     if (s < S) {
-      const int64_t r = ((int64_t)q * S + s) * H + h;
-      const v2f ml = *reinterpret_cast<const v2f*>(a.part_ml + r * 2);
-      ms[s] = ml[0];
-      ls[s] = ml[1];
-      os[s] = *reinterpret_cast<const v4f*>(a.part_o + r * kLatent + d0);
+      os[s] = *reinterpret_cast<const v4f*>(a.part_o + (((int64_t)q * S + s) * HB + hb) * (kLatent * 16) +
+                                            (nt * 64 + lane) * 4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const v2f ml = *reinterpret_cast<const v2f*>(a.part_ml + (((int64_t)q * S + s) * H + h0 + i) * 2);
+        ms[s][i] = ml[0];
+        ls[s][i] = ml[1];
+      }
     }
   }
-  float M = ms[0];
 #pragma unroll
-  for (int s = 1; s < kAttendMaxSplits; ++s) M = fmaxf(M, ms[s]);
-  float den = 0.0f;
-  v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
-  if (M != -__builtin_inff()) {
+  for (int i = 0; i < 4; ++i) {
+    float M = ms[0][i];
 #pragma unroll
-    for (int s = 0; s < kAttendMaxSplits; ++s) {
-      const float wgt = ls[s] > 0.0f ? exp2f(ms[s] - M) : 0.0f;
-      den += wgt * ls[s];
+    for (int s = 1; s < kAttendMaxSplits; ++s) M = fmaxf(M, ms[s][i]);
+    float den = 0.0f, acc = 0.0f;
+    if (M != -__builtin_inff()) {
 #pragma unroll
-      for (int k = 0; k < 4; ++k) acc[k] += wgt * os[s][k];
+      for (int s = 0; s < kAttendMaxSplits; ++s) {
+        const float wgt = ls[s][i] > 0.0f ? exp2f(ms[s][i] - M) : 0.0f;
+        den += wgt * ls[s][i];
+        acc += wgt * os[s][i];
+      }
     }
+    a.out[((int64_t)q * H + h0 + i) * kLatent + nt * 16 + col] = den > 0.0f ? acc / den : 0.0f;
+    if (a.lse && nt == 0 && col == 0)
+      a.lse[(int64_t)q * H + h0 + i] = den > 0.0f ? (M + log2f(den)) * 0.69314718055994531f : -__builtin_inff();
   }
-  const float inv = den > 0.0f ? 1.0f / den : 0.0f;
-  *reinterpret_cast<v4f*>(a.out + ((int64_t)q * H + h) * kLatent + d0) =
-      v4f{acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv};
-  if (a.lse && threadIdx.x == 0)
-    a.lse[(int64_t)q * H + h] = den > 0.0f ? (M + log2f(den)) * 0.69314718055994531f : -__builtin_inff();
 }
 
 }  // namespace
@@ -344,7 +372,7 @@ hipError_t launch_attend(const AttendArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(k_attend, dim3((unsigned)(a.n_q * a.head_groups * a.splits)), dim3(kNT), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.splits == 1) return e;
-  hipLaunchKernelGGL(k_attend_combine, dim3((unsigned)(a.n_q * a.heads)), dim3(128), 0, s, a);
+  hipLaunchKernelGGL(k_attend_combine, dim3((unsigned)(a.n_q * (a.heads / 16) * 8)), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -16,7 +16,8 @@ struct ScanArgs {
   int n_q, hi, d, swa, g;    // g: queries per sequence
   int tiles;                 // position tiles per query
   int tile_pos;              // positions per tile (multiple of 64)
-  int prefetch;              // LDS ring slots per wave (4, 6 or 8)
+  int prefetch;              // LDS ring slots per wave (4 or 6)
+  int waves;                 // waves per workgroup (4 or 8)
   float* bscore;             // [n_q, ld]
   int64_t ld;
   // optional (nullptr: not written): the pool-select workspace, where each
@@ -95,6 +96,7 @@ constexpr int kPoolChunk = 4096;       // blocks per pool-select chunk workgroup
 constexpr int kPoolChunkCand = 1024;   // candidate slots per chunk
 constexpr int kScanTile = 2048;        // default positions per scan workgroup
 constexpr int kScanPrefetch = 4;       // default LDS ring slots per wave
+constexpr int kScanWaves = 4;          // default waves per scan workgroup
 constexpr int kAttendTile = 32;        // entries per attention tile
 constexpr int kAttendWaves = 4;        // waves per attention workgroup (16 heads each)
 constexpr int kAttendMaxSplits = 16;   // entry-list splits per query, at most

@@ -53,14 +53,15 @@ __device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xC
 
 constexpr int kMaxTilePos = 4096;
 
-template <int D, int HT, int R>
-__global__ __launch_bounds__(256) void k_scan(ScanArgs a) {
+template <int D, int HT, int R, int NW>
+__global__ __launch_bounds__(64 * NW) void k_scan(ScanArgs a) {
+  constexpr int NT = 64 * NW;
   constexpr int KC = D / 32;            // MFMA k-chunks of 32 dims
   constexpr int NH = D / 64;            // 16-byte loads per lane per step
-  __shared__ __attribute__((aligned(16))) uint8_t s_ring[4][R][NH][1024];
+  __shared__ __attribute__((aligned(16))) uint8_t s_ring[NW][R][NH][1024];
   __shared__ float s_bs[kMaxTilePos / 8];
-  __shared__ __attribute__((aligned(16))) uint8_t s_q[64 * (D + 8)];
-  __shared__ float s_w[64];
+  __shared__ __attribute__((aligned(16))) uint8_t s_q[64 * D];
+  __shared__ __attribute__((aligned(16))) float s_w[64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int gq = lane >> 4, col = lane & 15;
 
@@ -95,14 +96,14 @@ __global__ __launch_bounds__(256) void k_scan(ScanArgs a) {
                     (uint32_t)__builtin_amdgcn_readfirstlane(c * D), 0x00020000u};
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
 
-  // this wave's steps are s_k = wave + 4k, k < ns, streamed through R LDS
+  // this wave's steps are s_k = wave + NW k, k < ns, streamed through R LDS
   // slots with R - 1 steps of direct-to-LDS loads in flight.  The loads are
   // issued as inline asm so that the compiler neither tracks them (it would
   // wait for every one of them before each LDS read) nor moves them; the
   // waits below count them explicitly (vector-memory ops retire in order).
-  const int ns = wave < nsteps ? (nsteps - wave + 3) >> 2 : 0;
+  const int ns = wave < nsteps ? (nsteps - wave + NW - 1) / NW : 0;
   auto issue = [&](int k) {
-    const uint32_t row = (uint32_t)(p_begin + (wave + 4 * k) * 16 + col) * D;
+    const uint32_t row = (uint32_t)(p_begin + (wave + NW * k) * 16 + col) * D;
     const uint32_t slot = (uint32_t)(uintptr_t)(lds_void*)&s_ring[wave_u][k % R][0][0];
 #pragma unroll
     for (int h = 0; h < NH; ++h) {
@@ -149,7 +150,7 @@ __global__ __launch_bounds__(256) void k_scan(ScanArgs a) {
       for (int i = 0; i < 4; ++i) pp[i] += wv[t][i] * fmaxf(acc[t][i], 0.0f);
     }
     const float part = sum_rows4((pp[0] + pp[1]) + (pp[2] + pp[3]));
-    const int s = wave + 4 * k;
+    const int s = wave + NW * k;
     const int p0 = p_begin + s * 16;
     const float v = max_lanes8((p0 + col < c) ? part : -__builtin_inff());
     if (lane < 16 && (lane & 7) == 0) s_bs[s * 2 + (lane >> 3)] = v;
@@ -158,30 +159,47 @@ __global__ __launch_bounds__(256) void k_scan(ScanArgs a) {
   // software pipeline: the MFMAs of step k run while the VALU finishes
   // step k - 1 (epilogue) and prepares step k + 1 (LDS read, fp8 -> f16),
   // none of which depends on the MFMAs in flight
+  // The query (H_i x d fp8, one contiguous block) and the head weights come
+  // in by direct-to-LDS loads issued before the first key loads, so they land
+  // first: the explicit wait below covers them while the keys stay in flight
+  // (a compiler-tracked vector load here would make the compiler wait for
+  // every load before it, key loads included, and stall the whole stream).
+  {
+    const uint64_t qaddr = (uint64_t)(uintptr_t)qp;
+    const v4u qrsrc = {(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)qaddr),
+                       (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(qaddr >> 32)) & 0xFFFFu,
+                       (uint32_t)__builtin_amdgcn_readfirstlane(a.hi * D), 0x00020000u};
+    const int qvec = (a.hi * D + 1023) >> 10;          // 1 KiB per load instruction
+    for (int v = wave_u; v < qvec; v += NW) {
+      const uint32_t m0 = (uint32_t)__builtin_amdgcn_readfirstlane((int)((uint32_t)(uintptr_t)(lds_void*)s_q + v * 1024));
+      asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                   :: "s"(m0), "v"((uint32_t)(v * 1024 + lane * 16)), "s"(qrsrc) : "memory", "m0");
+    }
+    if (wave_u == 0) {
+      // the head weights, 4 bytes per lane (weights past H_i read as zero)
+      const uint64_t waddr = (uint64_t)(uintptr_t)(a.idx_w + (int64_t)q * a.hi);
+      const v4u wrsrc = {(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)waddr),
+                         (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(waddr >> 32)) & 0xFFFFu,
+                         (uint32_t)__builtin_amdgcn_readfirstlane(a.hi * 4), 0x00020000u};
+      const uint32_t m0 = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(uintptr_t)(lds_void*)s_w);
+      asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+                   :: "s"(m0), "v"((uint32_t)(lane * 4)), "s"(wrsrc) : "memory", "m0");
+    }
+  }
   const int pro = min(R - 1, ns);
   for (int k = 0; k < pro; ++k) issue(k);
+  if (pro == R - 1) wait_vmcnt<(R - 1) * NH>();   // the query loads (older) have landed
+  else wait_vmcnt<0>();
+  __syncthreads();
 
-  // query fragments (f16) and head weights for this lane; loaded after the
-  // first key loads are in flight so the two latencies overlap
-  // the workgroup stages the query (H_i x d fp8) and the head weights in LDS
-  // once with 16-byte loads; each wave then reads its fragments from there
-  // (rows padded by 8 bytes so the 16 rows a wave reads hit distinct banks)
-  {
-    const int nvec = a.hi * D / 16;
-    for (int i = tid; i < nvec; i += 256) {
-      const int h = i / (D / 16), o = (i % (D / 16)) * 16;
-      *reinterpret_cast<v4u*>(&s_q[h * (D + 8) + o]) = *reinterpret_cast<const v4u*>(qp + h * D + o);
-    }
-    if (tid < 64) s_w[tid] = tid < a.hi ? a.idx_w[(int64_t)q * a.hi + tid] : 0.0f;
-    __syncthreads();
-  }
+  // query fragments (f16) and head weights for this lane, from LDS
 #pragma unroll
   for (int t = 0; t < HT; ++t) {
     const int h = t * 16 + col;
     const bool live = h < a.hi;
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc) {
-      const v2u x = *reinterpret_cast<const v2u*>(&s_q[min(h, a.hi - 1) * (D + 8) + key_chunk<D>(gq, kc >> 1) + (kc & 1) * 8]);
+      const v2u x = *reinterpret_cast<const v2u*>(&s_q[min(h, a.hi - 1) * D + key_chunk<D>(gq, kc >> 1) + (kc & 1) * 8]);
       qf[t][kc] = fp8x8_to_v8h(live ? x[0] : 0u, live ? x[1] : 0u);
       // keep the converted fragments resident: without this the compiler
       // re-converts them inside the loop to save registers
@@ -212,7 +230,7 @@ __global__ __launch_bounds__(256) void k_scan(ScanArgs a) {
   float* bs = a.bscore + (int64_t)q * a.ld + (p_begin >> 3);
   const int nblk = (p_end - p_begin + 7) >> 3;
   uint32_t lo = 0xFFFFFFFFu, hi = 0;
-  for (int i = tid; i < nblk; i += 256) {
+  for (int i = tid; i < nblk; i += NT) {
     const float v = s_bs[i];
     bs[i] = v;
     lo = min(lo, order_key(v));
@@ -222,44 +240,44 @@ __global__ __launch_bounds__(256) void k_scan(ScanArgs a) {
     // the tile's key range for the pool select, and (tile 0) its histogram cleared
     uint32_t* pw = a.pool_ws + (int64_t)q * a.pool_ws_stride;
     if (tile == 0) {
-      for (int i = tid * 4; i < kHistBins; i += 256 * 4) *reinterpret_cast<v4u*>(pw + i) = v4u{0u, 0u, 0u, 0u};
+      for (int i = tid * 4; i < kHistBins; i += NT * 4) *reinterpret_cast<v4u*>(pw + i) = v4u{0u, 0u, 0u, 0u};
     }
 #pragma unroll
     for (int d = 32; d >= 1; d >>= 1) {
       lo = min(lo, (uint32_t)__shfl_xor(lo, d, 64));
       hi = max(hi, (uint32_t)__shfl_xor(hi, d, 64));
     }
-    __shared__ uint32_t s_mm[8];
-    if (lane == 0) { s_mm[wave] = lo; s_mm[4 + wave] = hi; }
+    __shared__ uint32_t s_mm[2 * NW];
+    if (lane == 0) { s_mm[wave] = lo; s_mm[NW + wave] = hi; }
     __syncthreads();
     if (tid == 0) {
-      *reinterpret_cast<v2u*>(pw + kHistBins + 2 * tile) =
-          v2u{min(min(s_mm[0], s_mm[1]), min(s_mm[2], s_mm[3])), max(max(s_mm[4], s_mm[5]), max(s_mm[6], s_mm[7]))};
+      uint32_t l2 = s_mm[0], h2 = s_mm[NW];
+#pragma unroll
+      for (int i = 1; i < NW; ++i) { l2 = min(l2, s_mm[i]); h2 = max(h2, s_mm[NW + i]); }
+      *reinterpret_cast<v2u*>(pw + kHistBins + 2 * tile) = v2u{l2, h2};
     }
   }
 }
 
-template <int D, int R>
-hipError_t launch_dr(const ScanArgs& a, hipStream_t s) {
+template <int D, int R, int NW>
+hipError_t launch_drw(const ScanArgs& a, hipStream_t s) {
   const int ht = (a.hi + 15) / 16;
   const int units = ((a.n_q / a.g) * a.tiles + 7) / 8 * 8;
-  const dim3 grid((unsigned)(units * a.g)), block(256);
+  const dim3 grid((unsigned)(units * a.g)), block(64 * NW);
   switch (ht) {
-    case 1: hipLaunchKernelGGL((k_scan<D, 1, R>), grid, block, 0, s, a); break;
-    case 2: hipLaunchKernelGGL((k_scan<D, 2, R>), grid, block, 0, s, a); break;
-    case 3: hipLaunchKernelGGL((k_scan<D, 3, R>), grid, block, 0, s, a); break;
-    default: hipLaunchKernelGGL((k_scan<D, 4, R>), grid, block, 0, s, a); break;
+    case 1: hipLaunchKernelGGL((k_scan<D, 1, R, NW>), grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((k_scan<D, 2, R, NW>), grid, block, 0, s, a); break;
+    case 3: hipLaunchKernelGGL((k_scan<D, 3, R, NW>), grid, block, 0, s, a); break;
+    default: hipLaunchKernelGGL((k_scan<D, 4, R, NW>), grid, block, 0, s, a); break;
   }
   return hipGetLastError();
 }
 
 template <int D>
 hipError_t launch_d(const ScanArgs& a, hipStream_t s) {
-  switch (a.prefetch) {        // LDS ring slots per wave (steps in flight + 1)
-    case 4: return launch_dr<D, 4>(a, s);
-    case 8: return launch_dr<D, 8>(a, s);
-    default: return launch_dr<D, 6>(a, s);
-  }
+  // LDS ring slots per wave (steps in flight + 1) and waves per workgroup
+  if (a.waves == 8) return a.prefetch == 6 ? launch_drw<D, 6, 8>(a, s) : launch_drw<D, 4, 8>(a, s);
+  return a.prefetch == 6 ? launch_drw<D, 6, 4>(a, s) : launch_drw<D, 4, 4>(a, s);
 }
 
 }  // namespace
