@@ -115,30 +115,42 @@ __device__ __forceinline__ uint32_t wave_reduce_u32(uint32_t v, Op op) {
   return op(r[0], r[1]);
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave without LDS: DPP row
+// shifts by 1, 2, 4 and 8 scan each row of 16 (lanes shifted in from outside
+// the row read 0), then row_bcast:15 adds row r's last lane to row r + 1 and
+// row_bcast:31 adds lane 31 to rows 2 and 3.
+__device__ __forceinline__ uint32_t wave_incl_scan_u32(uint32_t x) {
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xF, 0xF, true);
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xF, 0xF, true);
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xF, 0xF, true);
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xF, 0xF, true);
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xA, 0xF, false);
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xC, 0xF, false);
+  return x;
+}
+
 // Block-wide exclusive scan of one uint32 per thread (blockDim.x = NT, a
-// multiple of 64).  `sh` needs NT/64 + 1 words.  Returns the exclusive prefix;
-// *total receives the block sum.  Contains __syncthreads().
+// multiple of 64).  `sh` needs NT/64 words.  Returns the exclusive prefix;
+// *total receives the block sum.  Each wave scans in registers and publishes
+// its sum; every thread then adds the sums of the waves before its own.
+// Contains two __syncthreads() (the second lets `sh` be reused at once).
 template <int NT>
 __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* sh, uint32_t* total) {
+  constexpr int NW = NT / 64;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  uint32_t x = v;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    uint32_t y = __shfl_up(x, d, 64);
-    if (lane >= d) x += y;
-  }
+  const uint32_t x = wave_incl_scan_u32(v);
   if (lane == 63) sh[wave] = x;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    uint32_t acc = 0;
-    for (int w = 0; w < NT / 64; ++w) { uint32_t t = sh[w]; sh[w] = acc; acc += t; }
-    sh[NT / 64] = acc;
+  uint32_t before = 0, sum = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const uint32_t t = sh[w];
+    before += w < wave ? t : 0u;
+    sum += t;
   }
+  *total = sum;
   __syncthreads();
-  uint32_t r = sh[wave] + x - v;
-  *total = sh[NT / 64];
-  __syncthreads();
-  return r;
+  return before + x - v;
 }
 
 }  // namespace csa2

@@ -135,12 +135,7 @@ __device__ __forceinline__ void crossing_2048(const uint32_t* hist, uint32_t nee
   uint32_t local = 0;
 #pragma unroll
   for (int k = 0; k < kPB; ++k) local += h[k];
-  uint32_t x = local;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const uint32_t y = __shfl_up(x, d, 64);
-    if (lane >= d) x += y;
-  }
+  const uint32_t x = wave_incl_scan_u32(local);
   if (x - local < need && need <= x) {
     uint32_t above = x - local;            // keys in bins above the lane's run
 #pragma unroll
@@ -160,7 +155,7 @@ __global__ __launch_bounds__(kTkThreads) void k_topk_select(ReindexArgs a) {
   __shared__ uint32_t s_hist[kTkBins + 1];          // + a bin that collects empty slots
   __shared__ uint64_t s_cand[kRankCap];
   __shared__ uint32_t s_red[3 * kTkWaves];
-  __shared__ uint32_t s_scan[kTkWaves + 1];
+  __shared__ uint32_t s_scan[kTkWaves];
   __shared__ uint32_t s_misc[4];
 
   const int q = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;

@@ -124,8 +124,9 @@ struct KeyRange {
       lo = min(lo, m[0]);
       hi = max(hi, m[1]);
     }
-    *kmin = block_min_u32<NT>(lo, s_scan);
-    *kmax = block_max_u32<NT>(hi, s_scan);
+    block_minmax_u32<NT>(&lo, &hi, s_scan);
+    *kmin = lo;
+    *kmax = hi;
   }
 };
 
@@ -188,7 +189,7 @@ __device__ __forceinline__ void find_bstar(const HistSlice<NT>& h, uint32_t P, u
 
 // ---------------------------------------------------------------- K1
 __global__ __launch_bounds__(kCT) void k_pool_minmax(PoolArgs a) {
-  __shared__ uint32_t s_scan[kCT / 64 + 1];
+  __shared__ uint32_t s_scan[2 * (kCT / 64)];
   const int q = blockIdx.x / a.chunks, g = blockIdx.x % a.chunks, tid = threadIdx.x;
   const PoolWs w = pool_ws(a, q);
   if (g == 0) {
@@ -213,8 +214,7 @@ __global__ __launch_bounds__(kCT) void k_pool_minmax(PoolArgs a) {
       }
     }
   }
-  lo = block_min_u32<kCT>(lo, s_scan);
-  hi = block_max_u32<kCT>(hi, s_scan);
+  block_minmax_u32<kCT>(&lo, &hi, s_scan);
   if (tid == 0) {
     w.mm[2 * g] = lo;
     w.mm[2 * g + 1] = hi;
@@ -224,7 +224,7 @@ __global__ __launch_bounds__(kCT) void k_pool_minmax(PoolArgs a) {
 // ---------------------------------------------------------------- K2
 __global__ __launch_bounds__(kCT) void k_pool_hist(PoolArgs a) {
   __shared__ uint32_t s_hist[kHistBins];
-  __shared__ uint32_t s_scan[kCT / 64 + 1];
+  __shared__ uint32_t s_scan[2 * (kCT / 64)];
   const int q = blockIdx.x / a.chunks, g = blockIdx.x % a.chunks, tid = threadIdx.x;
   const int base = g * kPoolChunk;
   const PoolWs w = pool_ws(a, q);
@@ -254,7 +254,7 @@ __global__ __launch_bounds__(kCT) void k_pool_hist(PoolArgs a) {
 
 // ---------------------------------------------------------------- K3
 __global__ __launch_bounds__(kCT) void k_pool_mark(PoolArgs a) {
-  __shared__ uint32_t s_scan[kCT / 64 + 1];
+  __shared__ uint32_t s_scan[2 * (kCT / 64)];
   __shared__ uint32_t s_misc[2];
   __shared__ uint32_t s_ccount;
   const int q = blockIdx.x / a.chunks, g = blockIdx.x % a.chunks;
@@ -331,7 +331,7 @@ __global__ __launch_bounds__(kFT) void k_pool_final(PoolArgs a) {
   __shared__ uint32_t s_ckey[kCandCap];
   __shared__ int32_t s_cj[kCandCap];
   __shared__ uint32_t s_off[kMaxBlocks / kPoolChunk + 1];
-  __shared__ uint32_t s_scan[kFT / 64 + 1];
+  __shared__ uint32_t s_scan[2 * (kFT / 64)];
   __shared__ uint32_t s_misc[4];
 
   const int q = blockIdx.x, tid = threadIdx.x;
@@ -378,12 +378,7 @@ __global__ __launch_bounds__(kFT) void k_pool_final(PoolArgs a) {
   if (tid < 64) {
     const uint32_t v = cnt_v;
     const bool over = v > (uint32_t)kPoolChunkCand;
-    uint32_t x = v;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const uint32_t y = __shfl_up(x, d, 64);
-      if (tid >= d) x += y;
-    }
+    const uint32_t x = wave_incl_scan_u32(v);
     if (tid < G) s_off[tid] = x - v;
     const uint64_t ov = __ballot(over);
     if (tid == 63) {
@@ -436,8 +431,7 @@ __global__ __launch_bounds__(kFT) void k_pool_final(PoolArgs a) {
         if (b.bin(key) == bstar) { clo = min(clo, key); chi = max(chi, key); }
       }
     }
-    clo = block_min_u32<kFT>(clo, s_scan);
-    chi = block_max_u32<kFT>(chi, s_scan);
+    block_minmax_u32<kFT>(&clo, &chi, s_scan);
     int fixed_lo = highest_diff_bit(clo, chi) + 1;     // bits >= fixed_lo are decided
     uint32_t prefix = (uint32_t)(((uint64_t)clo >> fixed_lo) << fixed_lo);
     while (fixed_lo > 0) {

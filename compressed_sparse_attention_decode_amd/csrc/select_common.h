@@ -5,30 +5,22 @@
 
 namespace csa2 {
 
+// Block-wide min and max of one uint32 per thread in one barrier pair
+// (blockDim.x = NT, a multiple of 64; `sh` needs 2 NT/64 words).
 template <int NT>
-__device__ __forceinline__ uint32_t block_min_u32(uint32_t v, uint32_t* sh) {
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) v = min(v, (uint32_t)__shfl_xor(v, d, 64));
+__device__ __forceinline__ void block_minmax_u32(uint32_t* lo, uint32_t* hi, uint32_t* sh) {
+  constexpr int NW = NT / 64;
+  const uint32_t l = wave_reduce_u32(*lo, [](uint32_t x, uint32_t y) { return min(x, y); });
+  const uint32_t h = wave_reduce_u32(*hi, [](uint32_t x, uint32_t y) { return max(x, y); });
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  if (lane == 0) sh[wave] = v;
+  if (lane == 0) { sh[wave] = l; sh[NW + wave] = h; }
   __syncthreads();
-  uint32_t r = sh[0];
-  for (int w = 1; w < NT / 64; ++w) r = min(r, sh[w]);
-  __syncthreads();
-  return r;
-}
-
-template <int NT>
-__device__ __forceinline__ uint32_t block_max_u32(uint32_t v, uint32_t* sh) {
+  uint32_t rl = 0xFFFFFFFFu, rh = 0;
 #pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) v = max(v, (uint32_t)__shfl_xor(v, d, 64));
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  if (lane == 0) sh[wave] = v;
+  for (int w = 0; w < NW; ++w) { rl = min(rl, sh[w]); rh = max(rh, sh[NW + w]); }
   __syncthreads();
-  uint32_t r = sh[0];
-  for (int w = 1; w < NT / 64; ++w) r = max(r, sh[w]);
-  __syncthreads();
-  return r;
+  *lo = rl;
+  *hi = rh;
 }
 
 // In a histogram of `nbins` (a multiple of 64, <= 4096) counts, wave 0 finds
@@ -40,12 +32,7 @@ __device__ __forceinline__ void find_crossing(const uint32_t* hist, int nbins, u
   const int per = nbins / 64;
   uint32_t local = 0;
   for (int k = 0; k < per; ++k) local += hist[nbins - 1 - (lane * per + k)];
-  uint32_t x = local;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const uint32_t y = __shfl_up(x, d, 64);
-    if (lane >= d) x += y;
-  }
+  const uint32_t x = wave_incl_scan_u32(local);
   uint32_t above = x - local;
   if (above < need && need <= x) {
     for (int k = 0; k < per; ++k) {
@@ -61,13 +48,9 @@ __device__ __forceinline__ void find_crossing(const uint32_t* hist, int nbins, u
   }
 }
 
-// Digit plan for a radix select over keys that all lie in [kmin, kmax]: the
-// bits above the highest bit where kmin and kmax differ are common to every
-// key, so the passes start there (this keeps the first histogram spread out).
-struct DigitPlan {
-  int top;        // highest differing bit, -1 if kmin == kmax
-};
-
+// Radix passes over keys in [kmin, kmax] start below the highest bit where
+// kmin and kmax differ: the bits above it are common to every key, so the
+// first histogram stays spread out.
 __device__ __forceinline__ int highest_diff_bit(uint32_t kmin, uint32_t kmax) {
   const uint32_t d = kmin ^ kmax;
   return d ? 31 - __clz(d) : -1;
