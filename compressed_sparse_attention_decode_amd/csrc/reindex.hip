@@ -121,44 +121,65 @@ constexpr int kMaxCand = 2048 * kBlock;
 constexpr int kPer = kMaxCand / kTkThreads;        // 32 keys per thread, in registers
 constexpr int kBlkPer = kPer / kBlock;             // pool blocks per thread
 constexpr int kTkBins = 2048;                      // radix digit: up to 11 bits
+constexpr int kTkEmpty = 16;                       // bins past kTkBins that count empty slots
 constexpr int kTkWaves = kTkThreads / 64;
-constexpr int kRankCap = 128;                     // candidates ranked exactly against each other (quadratic)
+constexpr int kRankCap = 128;                      // candidates ranked exactly against each other (quadratic)
+static_assert(kTkBins == 4 * kTkThreads, "one 16-byte histogram clear per thread");
 
-// Wave 0 finds, in a kTkBins histogram, the bin where the count from the top
-// first reaches `need`: out[0] = bin, out[1] = keys in higher bins,
-// out[2] = keys in the bin.  Each lane owns 32 bins; both passes over them
-// are branch-free runs of independent LDS reads.
-__device__ __forceinline__ void crossing_2048(const uint32_t* hist, uint32_t need, uint32_t* out) {
+// Wave 0 scans a kTkBins histogram from the top.  total = all counted keys,
+// need = min(want, total).  Writes out[0] = the bin where the count from the
+// top first reaches need, out[1] = keys in higher bins, out[2] = keys in that
+// bin (out[0..2] only if need > 0), out[3] = need, out[4] = total.  Each lane
+// owns 32 consecutive bins, read with 16-byte LDS loads.
+__device__ __forceinline__ void crossing_2048(const uint32_t* hist, uint32_t want, uint32_t* out) {
   constexpr int kPB = kTkBins / 64;
   const int lane = threadIdx.x;
-  const uint32_t* h = hist + kTkBins - kPB * (lane + 1);      // the lane's bins, ascending
+  const int first = kTkBins - kPB * (lane + 1);     // lane 0 holds the highest bins
+  uint32_t c[kPB];
+#pragma unroll
+  for (int v = 0; v < kPB / 4; ++v) {
+    const v4u x = *reinterpret_cast<const v4u*>(hist + first + 4 * v);
+    c[4 * v] = x[0]; c[4 * v + 1] = x[1]; c[4 * v + 2] = x[2]; c[4 * v + 3] = x[3];
+  }
   uint32_t local = 0;
 #pragma unroll
-  for (int k = 0; k < kPB; ++k) local += h[k];
+  for (int k = 0; k < kPB; ++k) local += c[k];
   const uint32_t x = wave_incl_scan_u32(local);
-  if (x - local < need && need <= x) {
-    uint32_t above = x - local;            // keys in bins above the lane's run
+  const uint32_t total = (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
+  const uint32_t need = min(want, total);
+  if (lane == 0) { out[3] = need; out[4] = total; }
+  if (need > 0 && x - local < need && need <= x) {
+    uint32_t above = x - local;              // keys in bins above the lane's run
 #pragma unroll
-    for (int k = kPB - 1; k >= 0; --k) {   // from the lane's highest bin down
-      const uint32_t c = h[k];
-      if (above < need && need <= above + c) {
-        out[0] = kTkBins - kPB * (lane + 1) + k;
+    for (int k = kPB - 1; k >= 0; --k) {     // from the lane's highest bin down
+      if (above < need && need <= above + c[k]) {
+        out[0] = first + k;
         out[1] = above;
-        out[2] = c;
+        out[2] = c[k];
       }
-      above += c;
+      above += c[k];
     }
   }
 }
 
+// One workgroup per query.  The selection is a radix select over the order
+// keys offset by the query's smallest key: the first digit is the (up to) 11
+// bits below the highest bit of (max - min), so its bins are linear in the key
+// and cover the occupied range.  The bin holding the keff-th largest key is
+// narrowed by further digits until it holds at most kRankCap keys, which are
+// then ranked exactly by (key desc, slot asc); a bin that is taken whole ends
+// the search at once, and a run of equal keys that stays above kRankCap is cut
+// at the right slot by a block scan.  The result is a threshold (T, ST): keys
+// above T, and keys equal to T at slots <= ST, are selected.  Every per-key
+// pass is a few branch-free instructions: the workgroup runs on one CU, so
+// its time is VALU issue over the 16,384 keys.
 __global__ __launch_bounds__(kTkThreads) void k_topk_select(ReindexArgs a) {
-  __shared__ uint32_t s_hist[kTkBins + 1];          // + a bin that collects empty slots
+  __shared__ __align__(16) uint32_t s_hist[kTkBins + kTkEmpty];
   __shared__ uint64_t s_cand[kRankCap];
-  __shared__ uint32_t s_red[3 * kTkWaves];
-  __shared__ uint32_t s_scan[kTkWaves];
-  __shared__ uint32_t s_misc[4];
+  __shared__ uint32_t s_red[2 * kTkWaves];
+  __shared__ uint32_t s_misc[8];
 
-  const int q = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int q = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
   const int K = a.topk;
   const int32_t* pool = a.pool_blocks + (int64_t)q * a.pool;
   const uint32_t* ks = a.keys + (int64_t)q * a.pool * kBlock;
@@ -168,184 +189,137 @@ __global__ __launch_bounds__(kTkThreads) void k_topk_select(ReindexArgs a) {
   // thread t holds slots [kPer t, kPer (t + 1)) (pool order = ascending
   // positions) and the pool blocks they belong to.  The loads do not wait for
   // the pool count (the rows always hold 8P keys and P blocks): slots past
-  // the count are masked once it arrives.  Empty slots are key 0.
+  // the count are cleared once it arrives.  Empty slots are key 0.
   uint32_t key[kPer];
   int32_t blk[kBlkPer];
-  const bool mine = tid * kPer < a.pool * kBlock;
+  const int s0 = tid * kPer;
+  const bool mine = s0 < a.pool * kBlock;
 #pragma unroll
   for (int v = 0; v < kPer / 4; ++v) {
-    const int i = tid * kPer + v * 4;
-    const v4u x = mine ? *reinterpret_cast<const v4u*>(ks + i) : v4u{0u, 0u, 0u, 0u};
+    const v4u x = mine ? *reinterpret_cast<const v4u*>(ks + s0 + v * 4) : v4u{0u, 0u, 0u, 0u};
     key[4 * v] = x[0]; key[4 * v + 1] = x[1]; key[4 * v + 2] = x[2]; key[4 * v + 3] = x[3];
   }
 #pragma unroll
   for (int j = 0; j < kBlkPer; ++j) blk[j] = mine ? pool[tid * kBlkPer + j] : 0;
   const int N = a.pool_count[q] * kBlock;
-  for (int i = tid; i <= kTkBins; i += kTkThreads) s_hist[i] = 0;
-  if (tid == 0) s_misc[3] = 0;
+  *reinterpret_cast<v4u*>(s_hist + 4 * tid) = v4u{0u, 0u, 0u, 0u};
+  if (tid < kTkEmpty / 4) *reinterpret_cast<v4u*>(s_hist + kTkBins + 4 * tid) = v4u{0u, 0u, 0u, 0u};
+  if (tid == 0) s_misc[5] = 0;
 
-  // count of valid keys, their min and max (branch-free; one barrier)
-  uint32_t nvalid = 0, lo = 0xFFFFFFFFu, hi = 0;
+  const int nh = N - s0;                     // slots of this thread inside the pool count
+  if (nh < kPer) {
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) key[k] = k < nh ? key[k] : 0u;
+  }
+  // key range: key - 1 sends empty slots to the top for the minimum
+  uint32_t lo = 0xFFFFFFFFu, hi = 0;
 #pragma unroll
   for (int k = 0; k < kPer; ++k) {
-    key[k] = tid * kPer + k < N ? key[k] : 0u;
-    nvalid += key[k] != 0;
-    lo = min(lo, key[k] != 0 ? key[k] : 0xFFFFFFFFu);
+    lo = min(lo, key[k] - 1u);
     hi = max(hi, key[k]);
   }
-  nvalid = wave_reduce_u32(nvalid, [](uint32_t x, uint32_t y) { return x + y; });
-  lo = wave_reduce_u32(lo, [](uint32_t x, uint32_t y) { return min(x, y); });
-  hi = wave_reduce_u32(hi, [](uint32_t x, uint32_t y) { return max(x, y); });
-  if (lane == 0) {
-    s_red[wave] = nvalid;
-    s_red[kTkWaves + wave] = lo;
-    s_red[2 * kTkWaves + wave] = hi;
-  }
-  __syncthreads();
-  uint32_t total = 0, kmin = 0xFFFFFFFFu, kmax = 0;
-#pragma unroll
-  for (int w = 0; w < kTkWaves; ++w) {
-    total += s_red[w];
-    kmin = min(kmin, s_red[kTkWaves + w]);
-    kmax = max(kmax, s_red[2 * kTkWaves + w]);
-  }
-  const uint32_t keff = min((uint32_t)K, total);
+  block_minmax_u32<kTkThreads>(&lo, &hi, s_red);   // its barriers also order the clears
+  const uint32_t kmin = lo + 1u, kmax = hi;
 
-  // Selection.  A histogram over kTkBins linear bins of the score range
-  // [min, max] (monotone in the key, and spread evenly, unlike bit digits of
-  // scores that share an exponent) gives the bin b1 holding the keff-th
-  // largest key.  Its keys are the candidates: up to kRankCap of them are
-  // ranked exactly against each other by (key desc, slot asc), which also
-  // settles ties, and the selected set is {key > T} plus {key == T, slot <=
-  // ST}.  More candidates: radix digits of up to 11 bits over the candidates'
-  // own key range narrow them first; a long run of equal keys falls back to
-  // admitting equal keys lowest slot first with a block scan.
-  int64_t T = 0;
-  int ST = -1;                // with T: keys == T at slots <= ST are taken
-  uint32_t need_eq = 0;       // fallback: need_eq keys == T, lowest slots first
-  bool by_scan = false;
-  if (keff > 0) {
-    const float flo = key_float(kmin), fhi = key_float(kmax);
-    float scale = (float)kTkBins / (fhi - flo);
-    if (!(scale > 0.0f && scale < 3.0e38f)) scale = 0.0f;    // all keys equal (or a huge range)
-    auto lbin = [&](uint32_t k) { return min((int)((key_float(k) - flo) * scale), kTkBins - 1); };
+  uint32_t keff = 0;
+  uint32_t T = 0xFFFFFFFFu;                  // threshold key (no finite score has it)
+  int ST = 0x7FFFFFFF;                       // keys == T at slots <= ST are selected
+  if (kmax != 0) {
+    const uint32_t d = kmax - kmin;
+    int shift = d ? max(0, 21 - (int)__clz(d)) : 0;    // (d >> shift) < 2^11
 #pragma unroll
-    for (int k = 0; k < kPer; ++k) atomicAdd(&s_hist[key[k] != 0 ? lbin(key[k]) : kTkBins], 1u);
-    __syncthreads();
-    if (wave == 0) crossing_2048(s_hist, keff, s_misc);
-    __syncthreads();
-    const int b1 = (int)s_misc[0];
-    uint32_t need = keff - s_misc[1];
-    uint32_t cand = s_misc[2];
-    uint32_t cm = 0;                 // the thread's keys in bin b1
-#pragma unroll
-    for (int k = 0; k < kPer; ++k) cm |= (uint32_t)(key[k] != 0 && lbin(key[k]) == b1) << k;
-    if (cand > (uint32_t)kRankCap) {
-      // Rare (a large crossing bin, e.g. many equal scores): radix digits
-      // over the candidates' own key range narrow them.  This path re-reads
-      // its keys from memory so that it adds no registers to the common one.
-      auto kget = [&](int k) -> uint32_t {
-        const int slot = tid * kPer + k;
-        return (cm >> k & 1u) ? ks[slot] : 0u;
-      };
-      for (int i = tid; i < kTkBins; i += kTkThreads) s_hist[i] = 0;
-      uint32_t clo = 0xFFFFFFFFu, chi = 0;
-#pragma unroll 1
-      for (int k = 0; k < kPer; ++k) {
-        const uint32_t x = kget(k);
-        clo = min(clo, x != 0 ? x : 0xFFFFFFFFu);
-        chi = max(chi, x);
-      }
-      clo = wave_reduce_u32(clo, [](uint32_t x, uint32_t y) { return min(x, y); });
-      chi = wave_reduce_u32(chi, [](uint32_t x, uint32_t y) { return max(x, y); });
-      if (lane == 0) { s_red[kTkWaves + wave] = clo; s_red[2 * kTkWaves + wave] = chi; }
-      __syncthreads();
-      clo = 0xFFFFFFFFu; chi = 0;
-#pragma unroll 1
-      for (int w = 0; w < kTkWaves; ++w) {
-        clo = min(clo, s_red[kTkWaves + w]);
-        chi = max(chi, s_red[2 * kTkWaves + w]);
-      }
-      int fixed_lo = highest_diff_bit(clo, chi) + 1;   // bits >= fixed_lo are decided
-      uint32_t prefix = (uint32_t)(((uint64_t)clo >> fixed_lo) << fixed_lo);
-      while (cand > (uint32_t)kRankCap && fixed_lo > 0) {
-        const int sh = max(0, fixed_lo - 11);
-        const uint32_t dmask = (1u << (fixed_lo - sh)) - 1;
-#pragma unroll 1
-        for (int k = 0; k < kPer; ++k) {
-          const uint32_t x = kget(k);
-          if (x != 0) atomicAdd(&s_hist[(x >> sh) & dmask], 1u);
-        }
-        __syncthreads();
-        if (wave == 0) crossing_2048(s_hist, need, s_misc);
-        __syncthreads();
-        prefix |= s_misc[0] << sh;
-        need -= s_misc[1];
-        cand = s_misc[2];
-        fixed_lo = sh;
-#pragma unroll 1
-        for (int k = 0; k < kPer; ++k) {
-          const uint32_t x = kget(k);
-          if (x != 0 && ((uint64_t)x >> fixed_lo) != ((uint64_t)prefix >> fixed_lo)) cm &= ~(1u << k);
-        }
-        for (int i = tid; i < kTkBins; i += kTkThreads) s_hist[i] = 0;   // for a next digit
-        __syncthreads();
-      }
-      if (cand > (uint32_t)kRankCap) {
-        T = (int64_t)prefix;           // all bits fixed: a long run of equal keys
-        need_eq = need;
-        by_scan = true;
-      }
+    for (int k = 0; k < kPer; ++k) {
+      const uint32_t b = (key[k] - kmin) >> shift;
+      atomicAdd(&s_hist[key[k] != 0 ? b : kTkBins + (lane & (kTkEmpty - 1))], 1u);
     }
-    if (!by_scan) {
-      // rank the candidates exactly: (key, ~slot) compared as one 64-bit value
+    __syncthreads();
+    if (tid < 64) crossing_2048(s_hist, (uint32_t)K, s_misc);
+    __syncthreads();
+    keff = s_misc[3];
+    uint32_t need = keff - s_misc[1];         // keys still to take from the crossing bin
+    uint32_t cand = s_misc[2];
+    uint32_t blo = kmin + (s_misc[0] << shift);    // the crossing bin is [blo, blo + 2^shift)
+
+    // Rare: a crossing bin with more than kRankCap keys (clustered or equal
+    // scores).  Further digits of (key - blo) narrow it.
+    while (cand > (uint32_t)kRankCap && need < cand && shift > 0) {
+      const int sh2 = max(0, shift - 11);
+      __syncthreads();                        // the previous crossing is read
+      *reinterpret_cast<v4u*>(s_hist + 4 * tid) = v4u{0u, 0u, 0u, 0u};
+      __syncthreads();
 #pragma unroll
       for (int k = 0; k < kPer; ++k) {
-        if (cm >> k & 1u) {
-          const uint32_t idx = atomicAdd(&s_misc[3], 1u);
-          s_cand[idx] = ((uint64_t)key[k] << 32) | (uint32_t)~(uint32_t)(tid * kPer + k);
+        const uint32_t r = key[k] - blo;
+        if ((r >> shift) == 0) atomicAdd(&s_hist[r >> sh2], 1u);
+      }
+      __syncthreads();
+      if (tid < 64) crossing_2048(s_hist, need, s_misc);
+      __syncthreads();
+      blo += s_misc[0] << sh2;
+      need -= s_misc[1];
+      cand = s_misc[2];
+      shift = sh2;
+    }
+
+    if (need == cand) {
+      T = blo;                                // the crossing bin is taken whole
+    } else if (cand <= (uint32_t)kRankCap) {
+      // rank the candidates exactly: (key, ~slot) compared as one 64-bit value
+      const uint32_t bw = 1u << shift;
+#pragma unroll
+      for (int k = 0; k < kPer; ++k) {
+        if (key[k] - blo < bw) {
+          const uint32_t idx = atomicAdd(&s_misc[5], 1u);
+          s_cand[idx] = ((uint64_t)key[k] << 32) | (uint32_t)~(uint32_t)(s0 + k);
         }
       }
       __syncthreads();
-      for (uint32_t i = tid; i < cand; i += kTkThreads) {
-        const uint64_t ci = s_cand[i];
+      if (tid < (int)cand) {
+        const uint64_t ci = s_cand[tid];
         uint32_t r = 0;
 #pragma unroll 8
         for (uint32_t j = 0; j < cand; ++j) r += s_cand[j] > ci;
-        if (r == need - 1) { s_misc[0] = (uint32_t)(ci >> 32); s_misc[1] = ~(uint32_t)ci; }
+        if (r == need - 1) { s_misc[6] = (uint32_t)(ci >> 32); s_misc[7] = ~(uint32_t)ci; }
       }
       __syncthreads();
-      T = (int64_t)s_misc[0];
-      ST = (int)s_misc[1];
+      T = s_misc[6];
+      ST = (int)s_misc[7];
+    } else {
+      // all bits fixed: more than kRankCap equal keys, taken lowest slot first
+      T = blo;
+      uint32_t eq = 0;
+#pragma unroll
+      for (int k = 0; k < kPer; ++k) eq += key[k] == T;
+      uint32_t total;
+      uint32_t before = block_exclusive_scan<kTkThreads>(eq, s_red, &total);
+      if (before < need && need <= before + eq) {
+#pragma unroll
+        for (int k = 0; k < kPer; ++k) {
+          before += key[k] == T;
+          if (key[k] == T && before == need) s_misc[7] = (uint32_t)(s0 + k);
+        }
+      }
+      __syncthreads();
+      ST = (int)s_misc[7];
     }
   }
 
-  // ordered compaction
-  uint32_t eq_before = 0;
-  if (by_scan) {
-    uint32_t eq = 0;
+  // Selected: key > T, or key == T at a slot <= ST.  A thread whose slots all
+  // lie past ST compares against T + 1, the others against T; the one thread
+  // that straddles ST first clears its keys equal to T past ST.
+  const uint32_t Tt = s0 > ST ? T + 1u : T;
+  if (s0 <= ST && ST < s0 + kPer - 1) {
 #pragma unroll
-    for (int k = 0; k < kPer; ++k) eq += key[k] != 0 && (int64_t)key[k] == T;
-    eq_before = block_exclusive_scan<kTkThreads>(eq, s_scan, &total);
+    for (int k = 0; k < kPer; ++k) key[k] = (key[k] == T && s0 + k > ST) ? 0u : key[k];
   }
-  uint32_t take = 0, flags = 0;
+  uint32_t take = 0;
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) take += key[k] >= Tt;
+  uint32_t total;
+  uint32_t before = block_exclusive_scan<kTkThreads>(take, s_red, &total);
 #pragma unroll
   for (int k = 0; k < kPer; ++k) {
-    const int slot = tid * kPer + k;
-    bool sel = key[k] != 0 && ((int64_t)key[k] > T || ((int64_t)key[k] == T && slot <= ST));
-    if (by_scan) {
-      const bool eqk = key[k] != 0 && (int64_t)key[k] == T && eq_before < need_eq;
-      sel = sel || eqk;
-      eq_before += eqk;
-    }
-    flags |= (uint32_t)sel << k;
-    take += sel;
-  }
-  if (keff == 0) { flags = 0; take = 0; }
-  uint32_t before = block_exclusive_scan<kTkThreads>(take, s_scan, &total);
-#pragma unroll
-  for (int k = 0; k < kPer; ++k) {
-    if (flags >> k & 1u) {
+    if (key[k] >= Tt) {
       if (before < (uint32_t)K) {
         out[before] = blk[k >> 3] * kBlock + (k & 7);
         if (out_s) out_s[before] = key_float(key[k]);

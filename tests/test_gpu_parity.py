@@ -249,6 +249,62 @@ def test_ties_lower_position_wins():
     assert np.array_equal(tk.cpu().numpy()[0, :tc.item()], keep)
 
 
+def _set_key_rows(oq, g, rows, row):
+    """Overwrite key rows of a one-sequence case in the oracle's and the
+    GPU's copy alike."""
+    oq.keys[rows] = row
+    g.idx_k[rows] = torch.from_numpy(np.ascontiguousarray(row)).view(torch.float8_e4m3fn).cuda()
+
+
+@pytest.mark.parametrize("pool_blocks,ctx", [(256, 20000), (2048, 40000)])
+def test_all_scores_equal(pool_blocks, ctx):
+    """Every position holds the same key, so every score ties: the pool is the
+    lowest blocks and the Top-K the lowest positions.  This drives the equal-
+    run paths of both selections (a pool crossing bin that overflows its
+    chunk candidate slots, and a Top-K run of equal keys longer than the
+    exact-rank cap)."""
+    dims = wl.Dims(n_heads=16, idx_heads=16, idx_dim=128, pool_blocks=pool_blocks, topk=512)
+    w = small(111, dims, [ctx])
+    g = GpuCase(w)
+    oq = OracleQuery(w, wl.layout(w), 0)
+    _set_key_rows(oq, g, slice(None), oq.keys[5].copy())
+    rpool, _, _ = oq.full(0)
+    assert np.array_equal(rpool, np.arange(len(rpool)))
+    pool, cnt, _ = g.full(0)
+    tk, tc, _ = g.reindex(0, pool, cnt)
+    torch.cuda.synchronize()
+    assert np.array_equal(pool.cpu().numpy()[0, :cnt.item()], rpool)
+    keep, _, _ = oq.reindex(0, rpool)
+    assert np.array_equal(tk.cpu().numpy()[0, :tc.item()], keep)
+
+
+def test_outlier_score_narrows_the_range():
+    """One position whose key follows the sign of the weighted query gets a
+    score far above the rest, and its neighbour (an all-zero key) scores 0.
+    The key range then spans both, so the first histogram crowds the
+    ordinary scores into a few bins and the selections must narrow the
+    crossing bin with further digits (on this input: 538 keys in the Top-K
+    crossing bin, against an exact-rank cap of 128)."""
+    dims = wl.Dims(n_heads=16, idx_heads=64, idx_dim=128, pool_blocks=2048, topk=512)
+    w = small(112, dims, [40000])
+    g = GpuCase(w)
+    oq = OracleQuery(w, wl.layout(w), 0)
+    q, wt = oq.iq(0)
+    qs = (wt[:, None] * oracle.e4m3_decode(q)).sum(0)
+    _set_key_rows(oq, g, 777, np.where(qs >= 0, 0x7E, 0xFE).astype(np.uint8))     # +-448
+    _set_key_rows(oq, g, 776, np.zeros(128, np.uint8))
+    rpool, rb, _ = oq.full(0)
+    assert rb[777 // 8] > 100 * np.median(rb)
+    pool, cnt, _ = g.full(0)
+    tk, tc, _ = g.reindex(0, pool, cnt)
+    torch.cuda.synchronize()
+    got_pool = pool.cpu().numpy()[0, :cnt.item()]
+    check_set(got_pool, rpool, lambda j: rb[j], "outlier pool")
+    if np.array_equal(got_pool, rpool):
+        keep, _, _ = oq.reindex(0, rpool)
+        check_set(tk.cpu().numpy()[0, :tc.item()], keep, lambda p: oq.scores_at(0, p), "outlier topk")
+
+
 def test_pool_paths_agree(case):
     """csa2_index_full (scan-prepared pool workspace), csa2_index_scan +
     csa2_index_pool (the pool's own key-range pass), and repeated pool calls
