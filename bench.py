@@ -134,7 +134,7 @@ class Step:
         self.out = torch.empty(len(self.layers), n_q, w.dims.n_heads, 512, dtype=torch.float32, device=dev)
         self.lse = torch.empty(len(self.layers), n_q, w.dims.n_heads, dtype=torch.float32, device=dev)
         self.ws_p = torch.empty(csa2.workspace_pool(st.dims, st.batch) + 256, dtype=torch.uint8, device=dev)
-        self.ws_r = torch.empty(csa2.workspace_reindex(st.dims, st.batch) + 256, dtype=torch.uint8, device=dev)
+        self.ws_r = torch.zeros(csa2.workspace_reindex(st.dims, st.batch) + 256, dtype=torch.uint8, device=dev)
         self.ws_a = torch.empty(csa2.workspace_attend(st.dims, st.batch) + 256, dtype=torch.uint8, device=dev)
         for layer in [0] + self.layers:
             st.iq(layer)

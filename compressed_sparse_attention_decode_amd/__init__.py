@@ -192,7 +192,9 @@ def _workspace(nbytes: int, device, ws: Optional[torch.Tensor]) -> Optional[torc
     if nbytes == 0:
         return ws
     if ws is None or ws.numel() * ws.element_size() < nbytes:
-        ws = torch.empty(nbytes + 256, dtype=torch.uint8, device=device)
+        # zero-filled: the Reindex workspace starts with counters that must
+        # read zero on first use (each call leaves them so)
+        ws = torch.zeros(nbytes + 256, dtype=torch.uint8, device=device)
     return ws
 
 

@@ -125,8 +125,10 @@ size_t full_ws(const csa2_dims* d, const csa2_queries* q) {
   return pool_ws(d, q) + align256((size_t)q->n_q * full_ldb(d, q) * 4);
 }
 
+// Reindex workspace: per-query completion counters (zero between calls),
+// then the order keys n_q x 8P u32
 size_t reindex_ws(const csa2_dims* d, const csa2_queries* q) {
-  return align256((size_t)q->n_q * d->pool_blocks * 8 * 4);
+  return align256((size_t)q->n_q * 4) + align256((size_t)q->n_q * d->pool_blocks * 8 * 4);
 }
 
 struct AttendPlan { int hg, splits, split_entries; };
@@ -353,7 +355,8 @@ csa2_status csa2_index_reindex(const csa2_dims* d, const csa2_queries* q, const 
   ra.n_q = q->n_q; ra.hi = d->idx_heads; ra.d = d->idx_dim; ra.swa = d->swa;
   ra.pool = d->pool_blocks; ra.topk = d->topk;
   ra.split = (d->pool_blocks + kReindexBlocks - 1) / kReindexBlocks;
-  ra.keys = (uint32_t*)ws;
+  ra.done = (uint32_t*)ws;
+  ra.keys = (uint32_t*)((char*)ws + align256((size_t)q->n_q * 4));
   ra.topk_pos = topk_pos; ra.topk_count = topk_count; ra.topk_scores = topk_scores;
   hipError_t e = launch_reindex(ra, (hipStream_t)stream);
   return e == hipSuccess ? CSA2_OK : hip_fail(e, "reindex launch");

@@ -52,6 +52,7 @@ struct ReindexArgs {
   const int32_t* pool_count;
   int n_q, hi, d, swa, pool, topk;
   int split;                 // scoring workgroups per query
+  uint32_t* done;            // workspace [n_q]: scoring workgroups finished (zero between calls)
   uint32_t* keys;            // workspace [n_q, 8 * pool]: order keys, 0 = empty
   int32_t* topk_pos;
   int32_t* topk_count;
@@ -100,7 +101,7 @@ constexpr int kScanWaves = 4;          // default waves per scan workgroup
 constexpr int kAttendTile = 32;        // entries per attention tile
 constexpr int kAttendWaves = 4;        // waves per attention workgroup (16 heads each)
 constexpr int kAttendMaxSplits = 16;   // entry-list splits per query, at most
-constexpr int kReindexBlocks = 32;     // pool blocks per Reindex scoring workgroup
+constexpr int kReindexBlocks = 64;     // pool blocks per Reindex scoring workgroup
 constexpr int kMaxVisible = 1 << 21;   // bound of n_visible
 constexpr int kMaxBlocks = kMaxVisible / 8;
 

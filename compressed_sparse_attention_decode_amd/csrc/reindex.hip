@@ -7,20 +7,19 @@
 // newsaint.id page (constant-size search domain; only the pool's keys are
 // gathered).  Ties go to the lower position; output is ascending.
 //
-// Two kernels:
-//  * k_reindex_score: one workgroup per 32 pool blocks of a query; a wave
-//    step scores two pool blocks (16 positions, two contiguous key runs) with
-//    the same f16-MFMA contraction as the Full scan.  Every key load of the
-//    workgroup is issued before the first contraction (the kernel is short
-//    and latency-bound).  Scores are written as order-preserving uint32 keys,
-//    0 marking a slot that holds no candidate position;
-//  * k_topk_select: one 512-thread workgroup per query keeps its <= 16,384
-//    keys in registers (32 consecutive pool slots per thread), finds the K-th
-//    largest with a radix select of up to 11-bit digits starting at the
-//    highest bit where the smallest and largest key differ (common leading
-//    bits would pile every key onto one counter), and compacts in pool order
-//    (= ascending positions), admitting keys equal to the threshold lowest
-//    position first.
+// One kernel, k_reindex, with 512-thread workgroups:
+//  * scoring: one workgroup per 64 pool blocks of a query; a wave step
+//    scores two pool blocks (16 positions, two contiguous key runs) with the
+//    same f16-MFMA contraction as the Full scan.  Every key load of the
+//    workgroup is issued before the first contraction (the work is short and
+//    latency-bound).  Scores are written as order-preserving uint32 keys, 0
+//    marking a slot that holds no candidate position;
+//  * selection, by the last scoring workgroup of the query to finish: its
+//    <= 16,384 keys sit in registers (32 consecutive pool slots per thread);
+//    a radix select over (key - smallest key), whose first digit is the up
+//    to 11 bits below the highest bit of the key range, finds the K-th
+//    largest; the compaction runs in pool order (= ascending positions),
+//    admitting keys equal to the threshold lowest position first.
 #include "common.h"
 #include "internal.h"
 #include "select_common.h"
@@ -28,18 +27,20 @@
 namespace csa2 {
 namespace {
 
-template <int D, int HT>
-__global__ __launch_bounds__(256) void k_reindex_score(ReindexArgs a) {
+// Scores of pool slots [i_begin, i_begin + kReindexBlocks) of query q (8
+// positions per slot) as order keys.  Slots past the pool count are scored
+// too, from whatever block ids the row holds there (clamped to a zero key
+// row): the selection masks them by the count, so nothing here waits for it.
+template <int D, int HT, int NW>
+__device__ __forceinline__ void score_part(const ReindexArgs& a, int q, int part) {
   constexpr int KC = D / 32;
-  constexpr int LB = D / 4;                 // key bytes per lane per position
-  constexpr int SPW = kReindexBlocks / 8;   // wave steps (2 blocks each) per wave
+  constexpr int LB = D / 4;                        // key bytes per lane per position
+  constexpr int SPW = kReindexBlocks / (2 * NW);   // wave steps (2 blocks each) per wave
+  static_assert(SPW * 2 * NW == kReindexBlocks, "whole wave steps");
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int gq = lane >> 4, col = lane & 15;
-  const int q = blockIdx.x / a.split, part = blockIdx.x % a.split;
-  const int cnt = a.pool_count[q];
   const int i_begin = part * kReindexBlocks;
-  const int i_end = min(cnt, i_begin + kReindexBlocks);
-  if (i_begin >= i_end) return;
+  const int i_end = min(a.pool, i_begin + kReindexBlocks);
   const int n = a.n_visible[q];
   const int c = max(0, n - a.swa);
   const int32_t* pool = a.pool_blocks + (int64_t)q * a.pool;
@@ -49,7 +50,7 @@ __global__ __launch_bounds__(256) void k_reindex_score(ReindexArgs a) {
   int pos[SPW];
 #pragma unroll
   for (int u = 0; u < SPW; ++u) {
-    const int i = i_begin + 2 * (wave + 4 * u) + (col >> 3);
+    const int i = i_begin + 2 * (wave + NW * u) + (col >> 3);
     pos[u] = i < i_end ? pool[i] * kBlock + (col & 7) : c;
   }
   // every key load in flight at once (a position >= c reads zeros)
@@ -96,8 +97,8 @@ __global__ __launch_bounds__(256) void k_reindex_score(ReindexArgs a) {
   uint32_t* ks = a.keys + (int64_t)q * a.pool * kBlock;
 #pragma unroll
   for (int u = 0; u < SPW; ++u) {
-    const int i = i_begin + 2 * (wave + 4 * u) + (col >> 3);
-    if (i_begin + 2 * (wave + 4 * u) >= i_end) break;              // wave-uniform
+    const int i = i_begin + 2 * (wave + NW * u) + (col >> 3);
+    if (i_begin + 2 * (wave + NW * u) >= i_end) break;             // wave-uniform
     v8h kf[KC];
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc) kf[kc] = fp8x8_to_v8h(kb[u][2 * kc], kb[u][2 * kc + 1]);
@@ -130,7 +131,7 @@ static_assert(kTkBins == 4 * kTkThreads, "one 16-byte histogram clear per thread
 // need = min(want, total).  Writes out[0] = the bin where the count from the
 // top first reaches need, out[1] = keys in higher bins, out[2] = keys in that
 // bin (out[0..2] only if need > 0), out[3] = need, out[4] = total.  Each lane
-// owns 32 consecutive bins, read with 16-byte LDS loads.
+// owns 32 consecutive bins, read with 16-byte LDS loads.  Called by wave 0.
 __device__ __forceinline__ void crossing_2048(const uint32_t* hist, uint32_t want, uint32_t* out) {
   constexpr int kPB = kTkBins / 64;
   const int lane = threadIdx.x;
@@ -148,17 +149,19 @@ __device__ __forceinline__ void crossing_2048(const uint32_t* hist, uint32_t wan
   const uint32_t total = (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
   const uint32_t need = min(want, total);
   if (lane == 0) { out[3] = need; out[4] = total; }
-  if (need > 0 && x - local < need && need <= x) {
-    uint32_t above = x - local;              // keys in bins above the lane's run
-#pragma unroll
-    for (int k = kPB - 1; k >= 0; --k) {     // from the lane's highest bin down
-      if (above < need && need <= above + c[k]) {
-        out[0] = first + k;
-        out[1] = above;
-        out[2] = c[k];
-      }
-      above += c[k];
-    }
+  // the lane whose run holds the crossing; its bins go one per lane (highest
+  // first) through a second wave scan
+  const uint64_t hit = __ballot(need > 0 && x - local < need && need <= x);
+  if (hit == 0) return;
+  const int L = __builtin_ctzll(hit);
+  const uint32_t above_l = (uint32_t)__builtin_amdgcn_readlane((int)(x - local), L);
+  const int top = kTkBins - 1 - kPB * L;           // the run's highest bin
+  const uint32_t v = lane < kPB ? hist[top - lane] : 0u;
+  const uint32_t above = above_l + wave_incl_scan_u32(v) - v;
+  if (lane < kPB && above < need && need <= above + v) {
+    out[0] = top - lane;
+    out[1] = above;
+    out[2] = v;
   }
 }
 
@@ -173,13 +176,13 @@ __device__ __forceinline__ void crossing_2048(const uint32_t* hist, uint32_t wan
 // above T, and keys equal to T at slots <= ST, are selected.  Every per-key
 // pass is a few branch-free instructions: the workgroup runs on one CU, so
 // its time is VALU issue over the 16,384 keys.
-__global__ __launch_bounds__(kTkThreads) void k_topk_select(ReindexArgs a) {
+__device__ __forceinline__ void topk_select(const ReindexArgs& a, int q) {
   __shared__ __align__(16) uint32_t s_hist[kTkBins + kTkEmpty];
   __shared__ uint64_t s_cand[kRankCap];
   __shared__ uint32_t s_red[2 * kTkWaves];
   __shared__ uint32_t s_misc[8];
 
-  const int q = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
   const int K = a.topk;
   const int32_t* pool = a.pool_blocks + (int64_t)q * a.pool;
   const uint32_t* ks = a.keys + (int64_t)q * a.pool * kBlock;
@@ -312,19 +315,32 @@ __global__ __launch_bounds__(kTkThreads) void k_topk_select(ReindexArgs a) {
 #pragma unroll
     for (int k = 0; k < kPer; ++k) key[k] = (key[k] == T && s0 + k > ST) ? 0u : key[k];
   }
-  uint32_t take = 0;
+  uint32_t flags = 0;
 #pragma unroll
-  for (int k = 0; k < kPer; ++k) take += key[k] >= Tt;
+  for (int k = 0; k < kPer; ++k) flags |= (uint32_t)(key[k] >= Tt) << k;
   uint32_t total;
-  uint32_t before = block_exclusive_scan<kTkThreads>(take, s_red, &total);
+  uint32_t before = block_exclusive_scan<kTkThreads>(__builtin_popcount(flags), s_red, &total);
+  if (!out_s) {
+    // a thread holds about one selected key: visit only the set bits
+    while (flags) {
+      const int k = __builtin_ctz(flags);
+      flags &= flags - 1;
+      int32_t b = blk[0];
 #pragma unroll
-  for (int k = 0; k < kPer; ++k) {
-    if (key[k] >= Tt) {
-      if (before < (uint32_t)K) {
-        out[before] = blk[k >> 3] * kBlock + (k & 7);
-        if (out_s) out_s[before] = key_float(key[k]);
-      }
+      for (int j = 1; j < kBlkPer; ++j) b = (k >> 3) == j ? blk[j] : b;
+      if (before < (uint32_t)K) out[before] = b * kBlock + (k & 7);
       ++before;
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      if (flags >> k & 1u) {
+        if (before < (uint32_t)K) {
+          out[before] = blk[k >> 3] * kBlock + (k & 7);
+          out_s[before] = key_float(key[k]);
+        }
+        ++before;
+      }
     }
   }
   for (int t = (int)keff + tid; t < K; t += kTkThreads) {
@@ -334,15 +350,46 @@ __global__ __launch_bounds__(kTkThreads) void k_topk_select(ReindexArgs a) {
   if (tid == 0) a.topk_count[q] = (int32_t)keff;
 }
 
+// One kernel per Reindex call.  Every workgroup scores its kReindexBlocks
+// pool slots; the last workgroup of a query to finish (a per-query counter in
+// the workspace, left at zero for the next call) selects that query's Top-K
+// from all of its keys.  The keys cross workgroups through memory: after a
+// barrier, each workgroup's release fence publishes its stores before it
+// counts itself in, and the last one's acquire fence makes the others'
+// visible before it reads them.
+template <int D, int HT>
+__global__ __launch_bounds__(kTkThreads) void k_reindex(ReindexArgs a) {
+  __shared__ uint32_t s_last;
+  const int q = blockIdx.x / a.split, part = blockIdx.x % a.split;
+  score_part<D, HT, kTkWaves>(a, q, part);
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's key stores have reached L2
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    // one release per workgroup (an L2 write-back), one acquire (an
+    // invalidate) only in the last: per-wave fences would flush and drop the
+    // L2 that the other workgroups are reading
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    const uint32_t prev = __hip_atomic_fetch_add(a.done + q, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = prev == (uint32_t)(a.split - 1);
+    if (s_last) {
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      a.done[q] = 0;
+    }
+  }
+  __syncthreads();
+  if (!s_last) return;
+  topk_select(a, q);
+}
+
 template <int D>
-hipError_t launch_score(const ReindexArgs& a, hipStream_t s) {
+hipError_t launch_d(const ReindexArgs& a, hipStream_t s) {
   const int ht = (a.hi + 15) / 16;
-  const dim3 grid((unsigned)(a.n_q * a.split)), block(256);
+  const dim3 grid((unsigned)(a.n_q * a.split)), block(kTkThreads);
   switch (ht) {
-    case 1: hipLaunchKernelGGL((k_reindex_score<D, 1>), grid, block, 0, s, a); break;
-    case 2: hipLaunchKernelGGL((k_reindex_score<D, 2>), grid, block, 0, s, a); break;
-    case 3: hipLaunchKernelGGL((k_reindex_score<D, 3>), grid, block, 0, s, a); break;
-    default: hipLaunchKernelGGL((k_reindex_score<D, 4>), grid, block, 0, s, a); break;
+    case 1: hipLaunchKernelGGL((k_reindex<D, 1>), grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((k_reindex<D, 2>), grid, block, 0, s, a); break;
+    case 3: hipLaunchKernelGGL((k_reindex<D, 3>), grid, block, 0, s, a); break;
+    default: hipLaunchKernelGGL((k_reindex<D, 4>), grid, block, 0, s, a); break;
   }
   return hipGetLastError();
 }
@@ -350,10 +397,7 @@ hipError_t launch_score(const ReindexArgs& a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_reindex(const ReindexArgs& a, hipStream_t s) {
-  hipError_t e = a.d == 64 ? launch_score<64>(a, s) : launch_score<128>(a, s);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_topk_select, dim3(a.n_q), dim3(kTkThreads), 0, s, a);
-  return hipGetLastError();
+  return a.d == 64 ? launch_d<64>(a, s) : launch_d<128>(a, s);
 }
 
 }  // namespace csa2

@@ -216,7 +216,14 @@ csa2_status csa2_index_reindex_workspace_size(const csa2_dims* dims, const csa2_
  *   topk_pos    int32 [n_q, K]  ascending positions, -1 after topk_count
  *   topk_count  int32 [n_q]
  *   topk_scores optional float [n_q, K] (NULL to skip): the score of each
- *               kept position, same order as topk_pos. */
+ *               kept position, same order as topk_pos.
+ *   ws, ws_bytes  workspace of csa2_index_reindex_workspace_size bytes.  Its
+ *               first bytes are per-query completion counters of the
+ *               scoring workgroups: they must be zero before the first call
+ *               on a workspace (allocate it zero-filled), and every call
+ *               leaves them zero.  Calls sharing a workspace must be ordered
+ *               on one stream.
+ * One kernel: the last scoring workgroup of each query selects its Top-K. */
 csa2_status csa2_index_reindex(const csa2_dims* dims, const csa2_queries* q,
                                const uint8_t* idx_q, const float* idx_w, const uint8_t* idx_k,
                                const int32_t* pool_blocks, const int32_t* pool_count,

@@ -330,3 +330,24 @@ def test_pool_paths_agree(case):
         for qi in range(w.n_q):
             k = int(ref_cnt[qi])
             assert torch.equal(p[qi, :k], ref_pool[qi, :k]), f"{name} q{qi}: pools differ between paths"
+
+
+def test_reindex_workspace_reuse(case):
+    """Repeated Reindex calls on one workspace agree bit for bit (with and
+    without the score output), and leave its per-query completion counters
+    at zero, as the next call needs."""
+    name, g, lay = case
+    csa2 = g.csa2
+    pool, cnt, _ = g.full(0)
+    q, wt = g.iq(0)
+    idx_k = g.planes[0][0]
+    ws = torch.zeros(csa2.workspace_reindex(g.dims, g.batch) + 256, dtype=torch.uint8, device="cuda")
+    ts = torch.empty(g.w.n_q, g.w.dims.topk, dtype=torch.float32, device="cuda")
+    outs = [csa2.index_reindex(g.dims, g.batch, q, wt, idx_k, pool, cnt, ws=ws,
+                               topk_scores=ts if i == 1 else None) for i in range(3)]
+    torch.cuda.synchronize()
+    for tk, tc in outs[1:]:
+        assert torch.equal(tc, outs[0][1]), f"{name}: topk counts differ between calls"
+        assert torch.equal(tk, outs[0][0]), f"{name}: topk differs between calls"
+    off = (-ws.data_ptr()) % 256
+    assert int(ws[off:off + 4 * g.w.n_q].count_nonzero()) == 0, f"{name}: counters not left at zero"
