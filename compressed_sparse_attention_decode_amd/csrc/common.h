@@ -38,6 +38,16 @@ __device__ __forceinline__ float key_float(uint32_t k) {
   return __uint_as_float(u);
 }
 
+// A wave-uniform read of memory that no kernel writes while it runs, through
+// the scalar cache: the constant address space lets the compiler use a scalar
+// load where it cannot prove on its own that nothing in the kernel clobbers
+// the location (a vector load there makes every address built from the value
+// divergent, and buffer loads over it waterfall loops).
+template <typename T>
+__device__ __forceinline__ T load_uniform(const T* p) {
+  return *(const __attribute__((address_space(4))) T*)p;
+}
+
 // Raw buffer resource over [base, base + bytes): loads past the end return 0.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);

@@ -37,11 +37,12 @@ __device__ __forceinline__ void score_part(const ReindexArgs& a, int q, int part
   constexpr int LB = D / 4;                        // key bytes per lane per position
   constexpr int SPW = kReindexBlocks / (2 * NW);   // wave steps (2 blocks each) per wave
   static_assert(SPW * 2 * NW == kReindexBlocks, "whole wave steps");
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // known wave-uniform: no waterfall loops
   const int gq = lane >> 4, col = lane & 15;
   const int i_begin = part * kReindexBlocks;
   const int i_end = min(a.pool, i_begin + kReindexBlocks);
-  const int n = a.n_visible[q];
+  const int n = load_uniform(a.n_visible + q);
   const int c = max(0, n - a.swa);
   const int32_t* pool = a.pool_blocks + (int64_t)q * a.pool;
 
@@ -49,12 +50,19 @@ __device__ __forceinline__ void score_part(const ReindexArgs& a, int q, int part
   // i_begin + 2s, +1; lane col>>3 picks the slot, col&7 the position)
   int pos[SPW];
 #pragma unroll
+  for (int u = 0; u < SPW; ++u) pos[u] = pool[min(i_begin + 2 * (wave + NW * u) + (col >> 3), a.pool - 1)];
+  // the empty asm uses every loaded id, so the loads stay unconditional and
+  // all in flight together (a load the compiler sinks into the masked
+  // branch below waits on its own)
+#pragma unroll
+  for (int u = 0; u < SPW; ++u) asm volatile("" : "+v"(pos[u]));
+#pragma unroll
   for (int u = 0; u < SPW; ++u) {
     const int i = i_begin + 2 * (wave + NW * u) + (col >> 3);
-    pos[u] = i < i_end ? pool[i] * kBlock + (col & 7) : c;
+    pos[u] = i < i_end ? pos[u] * kBlock + (col & 7) : c;
   }
   // every key load in flight at once (a position >= c reads zeros)
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.idx_k + a.seq_base[q] * D, (uint32_t)c * D);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.idx_k + load_uniform(a.seq_base + q) * D, (uint32_t)c * D);
   uint32_t kb[SPW][LB / 4];
 #pragma unroll
   for (int u = 0; u < SPW; ++u) {
@@ -85,6 +93,9 @@ __device__ __forceinline__ void score_part(const ReindexArgs& a, int q, int part
 #pragma unroll
     for (int i = 0; i < 4; ++i) wv[t][i] = a.idx_w[(int64_t)q * a.hi + min(t * 16 + gq * 4 + i, a.hi - 1)];
   }
+  // every load above is issued before the first wait (the scheduler would
+  // otherwise place later steps' key loads after the query conversion)
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int t = 0; t < HT; ++t) {
     const bool live = t * 16 + col < a.hi;
@@ -98,7 +109,6 @@ __device__ __forceinline__ void score_part(const ReindexArgs& a, int q, int part
 #pragma unroll
   for (int u = 0; u < SPW; ++u) {
     const int i = i_begin + 2 * (wave + NW * u) + (col >> 3);
-    if (i_begin + 2 * (wave + NW * u) >= i_end) break;             // wave-uniform
     v8h kf[KC];
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc) kf[kc] = fp8x8_to_v8h(kb[u][2 * kc], kb[u][2 * kc + 1]);
@@ -176,7 +186,10 @@ __device__ __forceinline__ void crossing_2048(const uint32_t* hist, uint32_t wan
 // above T, and keys equal to T at slots <= ST, are selected.  Every per-key
 // pass is a few branch-free instructions: the workgroup runs on one CU, so
 // its time is VALU issue over the 16,384 keys.
-__device__ __forceinline__ void topk_select(const ReindexArgs& a, int q) {
+__device__ __forceinline__ void topk_select(const ReindexArgs& a, int q, int32_t b0, int32_t b1, int32_t b2,
+                                            int32_t b3, int pcnt) {
+  static_assert(kBlkPer == 4, "four pool blocks per thread");
+  const int32_t blk[kBlkPer] = {b0, b1, b2, b3};
   __shared__ __align__(16) uint32_t s_hist[kTkBins + kTkEmpty];
   __shared__ uint64_t s_cand[kRankCap];
   __shared__ uint32_t s_red[2 * kTkWaves];
@@ -184,17 +197,14 @@ __device__ __forceinline__ void topk_select(const ReindexArgs& a, int q) {
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int K = a.topk;
-  const int32_t* pool = a.pool_blocks + (int64_t)q * a.pool;
   const uint32_t* ks = a.keys + (int64_t)q * a.pool * kBlock;
   int32_t* out = a.topk_pos + (int64_t)q * K;
   float* out_s = a.topk_scores ? a.topk_scores + (int64_t)q * K : nullptr;
 
   // thread t holds slots [kPer t, kPer (t + 1)) (pool order = ascending
-  // positions) and the pool blocks they belong to.  The loads do not wait for
-  // the pool count (the rows always hold 8P keys and P blocks): slots past
-  // the count are cleared once it arrives.  Empty slots are key 0.
+  // positions); blk holds the pool blocks they belong to.  The rows always
+  // hold 8P keys: slots past the pool count are cleared.  Empty slots are key 0.
   uint32_t key[kPer];
-  int32_t blk[kBlkPer];
   const int s0 = tid * kPer;
   const bool mine = s0 < a.pool * kBlock;
 #pragma unroll
@@ -202,9 +212,7 @@ __device__ __forceinline__ void topk_select(const ReindexArgs& a, int q) {
     const v4u x = mine ? *reinterpret_cast<const v4u*>(ks + s0 + v * 4) : v4u{0u, 0u, 0u, 0u};
     key[4 * v] = x[0]; key[4 * v + 1] = x[1]; key[4 * v + 2] = x[2]; key[4 * v + 3] = x[3];
   }
-#pragma unroll
-  for (int j = 0; j < kBlkPer; ++j) blk[j] = mine ? pool[tid * kBlkPer + j] : 0;
-  const int N = a.pool_count[q] * kBlock;
+  const int N = pcnt * kBlock;
   *reinterpret_cast<v4u*>(s_hist + 4 * tid) = v4u{0u, 0u, 0u, 0u};
   if (tid < kTkEmpty / 4) *reinterpret_cast<v4u*>(s_hist + kTkBins + 4 * tid) = v4u{0u, 0u, 0u, 0u};
   if (tid == 0) s_misc[5] = 0;
@@ -277,12 +285,16 @@ __device__ __forceinline__ void topk_select(const ReindexArgs& a, int q) {
         }
       }
       __syncthreads();
-      if (tid < (int)cand) {
-        const uint64_t ci = s_cand[tid];
+      // four threads per candidate, each comparing a quarter of the others
+      const int ci_idx = tid >> 2, part = tid & 3;
+      if (ci_idx < (int)cand) {
+        const uint64_t ci = s_cand[ci_idx];
         uint32_t r = 0;
-#pragma unroll 8
-        for (uint32_t j = 0; j < cand; ++j) r += s_cand[j] > ci;
-        if (r == need - 1) { s_misc[6] = (uint32_t)(ci >> 32); s_misc[7] = ~(uint32_t)ci; }
+#pragma unroll 4
+        for (uint32_t j = part; j < cand; j += 4) r += s_cand[j] > ci;
+        r += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)r, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
+        r += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)r, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]
+        if (part == 0 && r == need - 1) { s_misc[6] = (uint32_t)(ci >> 32); s_misc[7] = ~(uint32_t)ci; }
       }
       __syncthreads();
       T = s_misc[6];
@@ -361,6 +373,13 @@ template <int D, int HT>
 __global__ __launch_bounds__(kTkThreads) void k_reindex(ReindexArgs a) {
   __shared__ uint32_t s_last;
   const int q = blockIdx.x / a.split, part = blockIdx.x % a.split;
+  // the selection's pool blocks and count (inputs of this call) are loaded by
+  // every workgroup before its scoring, so the last one has them at hand
+  const int32_t* pool = a.pool_blocks + (int64_t)q * a.pool;
+  const int j0 = (int)threadIdx.x * kBlkPer;
+  const int32_t b0 = pool[min(j0, a.pool - 1)], b1 = pool[min(j0 + 1, a.pool - 1)];
+  const int32_t b2 = pool[min(j0 + 2, a.pool - 1)], b3 = pool[min(j0 + 3, a.pool - 1)];
+  const int pcnt = load_uniform(a.pool_count + q);
   score_part<D, HT, kTkWaves>(a, q, part);
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's key stores have reached L2
   __syncthreads();
@@ -378,7 +397,7 @@ __global__ __launch_bounds__(kTkThreads) void k_reindex(ReindexArgs a) {
   }
   __syncthreads();
   if (!s_last) return;
-  topk_select(a, q);
+  topk_select(a, q, b0, b1, b2, b3, pcnt);
 }
 
 template <int D>
