@@ -63,57 +63,116 @@ __device__ __forceinline__ uint32_t fp4_byte_h2(uint32_t word, v2h s2) {
 constexpr int kItems = kTile * 32 / kNT;      // (entry, 16-channel group) items per thread
 constexpr int kRopeItems = kTile * 8 / kNT;   // (entry, 8-channel rope chunk) items per thread
 
-// One tile's raw sparse bytes held by a thread, loaded a tile ahead: an item
-// keeps its 8 code bytes in c.xy and its scale byte in c.z.  Window items
-// (at most W rows per query, bf16) are read when the tile is stored.
+// One tile's raw bytes held by a thread, loaded a tile ahead: an item keeps
+// its 8 code bytes in c.xy and the aligned word holding its scale byte in
+// c.z; a rope chunk comes from the cache (r) or a window row (rw), the other
+// reading zeros.  Window items' latent values (at most W rows per query,
+// bf16) are read when the tile is stored.
 struct RawTile {
   v4u c[kItems];
   v4u r[kRopeItems];
+  v4u rw[kRopeItems];
 };
 
-// rows[e] >= 0: sparse entry at position rows[e] (cache row seq_base + pos);
-// rows[e] < 0: window row swa_base + (-1 - rows[e]).
-__device__ __forceinline__ void load_tile(const AttendArgs& a, const int32_t* rows, int ne, int64_t seq_base,
-                                          int64_t swa_base, int tid, RawTile& t) {
+// The query's sources as buffer resources over exactly its rows, so that a
+// load at offset kOob returns zeros: every load below is issued for every
+// item, masked by its offset instead of a branch (a load inside a divergent
+// branch waits for itself, and for everything issued before it), and no
+// loaded value is touched before the tile is stored.
+constexpr uint32_t kOob = 0xFFFFFF00u;
+struct TileSrc {
+  __amdgpu_buffer_rsrc_t codes, scales, rope, win;
+};
+
+__device__ __forceinline__ TileSrc tile_src(const AttendArgs& a, int64_t seq_base, int64_t swa_base, int n, int w) {
+  TileSrc s;
+  s.codes = make_rsrc(a.kv_codes + seq_base * kCodeBytes, (uint32_t)n * kCodeBytes);
+  s.scales = make_rsrc(a.kv_scales + seq_base * kScaleBytes, (uint32_t)n * kScaleBytes);
+  s.rope = make_rsrc(a.kv_rope + seq_base * kRope, (uint32_t)n * kRope * 2);
+  s.win = make_rsrc(a.swa_kv + swa_base * kKeyDim, (uint32_t)w * kKeyDim * 2);
+  return s;
+}
+
+// The row ids of a thread's items in a tile of ne entries: rows[e] >= 0
+// is a sparse entry at position rows[e] (cache row seq_base + pos), rows[e]
+// < 0 the window row swa_base + (-1 - rows[e]); entries e >= ne read as
+// kNoRow.  All LDS reads first, then the selects.
+constexpr int32_t kNoRow = 0x7FFFFFFF;
+struct TileRows {
+  int32_t it[kItems];
+  int32_t rp[kRopeItems];
+};
+
+__device__ __forceinline__ TileRows tile_rows(const int32_t* rows, int ne, int tid) {
+  TileRows t;
+#pragma unroll
+  for (int k = 0; k < kItems; ++k) t.it[k] = rows[max(0, min((tid + k * kNT) >> 5, ne - 1))];
+#pragma unroll
+  for (int k = 0; k < kRopeItems; ++k) t.rp[k] = rows[max(0, min((tid + k * kNT) >> 3, ne - 1))];
+#pragma unroll
+  for (int k = 0; k < kItems; ++k) asm volatile("" : "+v"(t.it[k]));
+#pragma unroll
+  for (int k = 0; k < kRopeItems; ++k) asm volatile("" : "+v"(t.rp[k]));
+#pragma unroll
+  for (int k = 0; k < kItems; ++k) t.it[k] = ((tid + k * kNT) >> 5) < ne ? t.it[k] : kNoRow;
+#pragma unroll
+  for (int k = 0; k < kRopeItems; ++k) t.rp[k] = ((tid + k * kNT) >> 3) < ne ? t.rp[k] : kNoRow;
+  return t;
+}
+
+__device__ __forceinline__ void load_tile(const TileSrc& src, const int32_t* rows, int ne, int tid, RawTile& t) {
+  const TileRows tr = tile_rows(rows, ne, tid);
 #pragma unroll
   for (int k = 0; k < kItems; ++k) {
-    const int it = tid + k * kNT, e = it >> 5, grp = it & 31;
-    t.c[k] = v4u{0u, 0u, 0u, 0u};
-    if (e < ne && rows[e] >= 0) {
-      const int64_t row = seq_base + rows[e];
-      {
-        const v2u cw = *reinterpret_cast<const v2u*>(a.kv_codes + row * kCodeBytes + grp * 8);
-        t.c[k] = v4u{cw[0], cw[1], (uint32_t)a.kv_scales[row * kScaleBytes + grp], 0u};
-      }
-    }
+    const int grp = (tid + k * kNT) & 31;
+    const int32_t r = tr.it[k];
+    const bool sp = r >= 0 && r != kNoRow;
+    const v2u cw = __builtin_amdgcn_raw_buffer_load_b64(src.codes, sp ? (uint32_t)r * kCodeBytes + grp * 8 : kOob, 0, 0);
+    const uint32_t sw = __builtin_amdgcn_raw_buffer_load_b32(src.scales, sp ? ((uint32_t)r * kScaleBytes + grp) & ~3u : kOob, 0, 0);
+    t.c[k] = v4u{cw[0], cw[1], sw, 0u};
   }
 #pragma unroll
   for (int k = 0; k < kRopeItems; ++k) {
-    const int it = tid + k * kNT, e = it >> 3, ch = it & 7;
-    t.r[k] = v4u{0u, 0u, 0u, 0u};
-    if (e < ne) {
-      const int32_t r = rows[e];
-      t.r[k] = r >= 0 ? *reinterpret_cast<const v4u*>(a.kv_rope + (seq_base + r) * kRope + ch * 8)
-                      : *reinterpret_cast<const v4u*>(a.swa_kv + (swa_base + (-1 - r)) * kKeyDim + kLatent + ch * 8);
-    }
+    const int ch = (tid + k * kNT) & 7;
+    const int32_t r = tr.rp[k];
+    const uint32_t osp = r >= 0 && r != kNoRow ? (uint32_t)r * (kRope * 2) + ch * 16 : kOob;
+    const uint32_t ow = r < 0 ? (uint32_t)(-1 - r) * (kKeyDim * 2) + kLatent * 2 + ch * 16 : kOob;
+    t.r[k] = buf_load16(src.rope, osp);
+    t.rw[k] = buf_load16(src.win, ow);
   }
 }
 
-// Dequantise a tile into the f16 image (rows past the tile's end are 0).
-__device__ __forceinline__ void store_tile(const AttendArgs& a, const int32_t* rows, int ne, int64_t swa_base,
+// Dequantise a tile into the f16 image (rows past the tile's end are 0).  The
+// window rows' bf16 values are loaded here, all items at once.
+__device__ __forceinline__ void store_tile(const TileSrc& src, const int32_t* rows, int ne, bool has_win,
                                            const RawTile& t, int tid, _Float16* s_k) {
+  const TileRows tr = tile_rows(rows, ne, tid);
+  v4u w0[kItems], w1[kItems];
+  if (has_win) {
+    // a tile that reaches into the window (uniform): every item's window
+    // load is issued before the first is used
+#pragma unroll
+    for (int k = 0; k < kItems; ++k) {
+      const int grp = (tid + k * kNT) & 31;
+      const uint32_t ow = tr.it[k] < 0 ? (uint32_t)(-1 - tr.it[k]) * (kKeyDim * 2) + grp * 32 : kOob;
+      w0[k] = buf_load16(src.win, ow);
+      w1[k] = buf_load16(src.win, ow + 16);
+    }
+#pragma unroll
+    for (int k = 0; k < kItems; ++k) asm volatile("" : "+v"(w0[k]), "+v"(w1[k]));
+  } else {
+#pragma unroll
+    for (int k = 0; k < kItems; ++k) { w0[k] = v4u{0u, 0u, 0u, 0u}; w1[k] = w0[k]; }
+  }
 #pragma unroll
   for (int k = 0; k < kItems; ++k) {
     const int it = tid + k * kNT, e = it >> 5, grp = it & 31;
     v4u h0, h1;
-    const int32_t r = e < ne ? rows[e] : 0;
-    if (r < 0) {
-      const v4u* src = reinterpret_cast<const v4u*>(a.swa_kv + (swa_base + (-1 - r)) * kKeyDim + grp * 16);
-      const v4u x0 = src[0], x1 = src[1];
-      h0 = v4u{bf16x2_to_h2(x0[0]), bf16x2_to_h2(x0[1]), bf16x2_to_h2(x0[2]), bf16x2_to_h2(x0[3])};
-      h1 = v4u{bf16x2_to_h2(x1[0]), bf16x2_to_h2(x1[1]), bf16x2_to_h2(x1[2]), bf16x2_to_h2(x1[3])};
+    if (tr.it[k] < 0) {
+      h0 = v4u{bf16x2_to_h2(w0[k][0]), bf16x2_to_h2(w0[k][1]), bf16x2_to_h2(w0[k][2]), bf16x2_to_h2(w0[k][3])};
+      h1 = v4u{bf16x2_to_h2(w1[k][0]), bf16x2_to_h2(w1[k][1]), bf16x2_to_h2(w1[k][2]), bf16x2_to_h2(w1[k][3])};
     } else {
-      const _Float16 sh = (_Float16)e4m3_to_float(t.c[k][2]);     // exact
+      const _Float16 sh = (_Float16)e4m3_to_float((t.c[k][2] >> (8 * (grp & 3))) & 0xFFu);     // exact
       const v2h s2 = {sh, sh};
       const uint32_t c0 = t.c[k][0], c1 = t.c[k][1];
       h0 = v4u{fp4_byte_h2<0>(c0, s2), fp4_byte_h2<1>(c0, s2), fp4_byte_h2<2>(c0, s2), fp4_byte_h2<3>(c0, s2)};
@@ -126,7 +185,7 @@ __device__ __forceinline__ void store_tile(const AttendArgs& a, const int32_t* r
 #pragma unroll
   for (int k = 0; k < kRopeItems; ++k) {
     const int it = tid + k * kNT, e = it >> 3, ch = it & 7;
-    const v4u r = t.r[k];
+    const v4u r = t.r[k] | t.rw[k];
     *reinterpret_cast<v4u*>(s_k + e * kKS + kLatent + ch * 8) =
         v4u{bf16x2_to_h2(r[0]), bf16x2_to_h2(r[1]), bf16x2_to_h2(r[2]), bf16x2_to_h2(r[3])};
   }
@@ -137,7 +196,8 @@ __global__ __launch_bounds__(kNT) void k_attend(AttendArgs a) {
   __shared__ __attribute__((aligned(16))) _Float16 s_q[kNW * 16 * kKS];   // per wave: 16 heads x 576
   __shared__ int32_t s_row[kMaxSplit];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int gq = lane >> 4, col = lane & 15;
   const int S = a.splits, HG = a.head_groups;
   const int q = blockIdx.x / (HG * S);
@@ -155,7 +215,8 @@ __global__ __launch_bounds__(kNT) void k_attend(AttendArgs a) {
 #pragma unroll
     for (int j = 0; j < kRowPer; ++j) {
       const int e = e_begin + tid + j * kNT;
-      tkv[j] = e < e_lim ? tk[e] : 0;
+      const int32_t v = tk[min(e, a.topk - 1)];      // the row always holds topk entries
+      tkv[j] = e < e_lim ? v : 0;
     }
   }
   // the wave's 16 query heads as f16 rows [head][576] (the B operand of
@@ -167,17 +228,16 @@ __global__ __launch_bounds__(kNT) void k_attend(AttendArgs a) {
     for (int j = 0; j < kQv; ++j) {
       const int i = lane + 64 * j, hh = i / (kKeyDim / 8), d = (i % (kKeyDim / 8)) * 8;
       const int64_t qh = (int64_t)q * H + head0 + hh;
-      rq[j] = d < kLatent ? *reinterpret_cast<const v4u*>(a.q_lat + qh * kLatent + d)
-                          : *reinterpret_cast<const v4u*>(a.q_rope + qh * kRope + (d - kLatent));
+      const uint16_t* src = d < kLatent ? a.q_lat + qh * kLatent + d : a.q_rope + qh * kRope + (d - kLatent);
+      rq[j] = *reinterpret_cast<const v4u*>(src);
     }
   }
-  const int n = a.n_visible[q];
+  const int n = load_uniform(a.n_visible + q);
   const int c = max(0, n - a.swa);
-  const int Es = min(a.topk_count[q], a.topk);
+  const int Es = min(load_uniform(a.topk_count + q), a.topk);
   const int E = Es + (n - c);
   const int e_end = min(E, e_begin + a.split_entries);
-  const int64_t seq_base = a.seq_base[q];
-  const int64_t swa_base = a.swa_base[q];
+  const TileSrc src = tile_src(a, load_uniform(a.seq_base + q), load_uniform(a.swa_base + q), n, n - c);
 
   {
     // the split's kept positions: the row always holds `topk` entries, so
@@ -192,9 +252,9 @@ __global__ __launch_bounds__(kNT) void k_attend(AttendArgs a) {
   __syncthreads();
   // raw tiles two deep: tiles t and t+1 are in flight while t-1 is contracted
   RawTile ra, rb;
-  if (e_begin < e_end) load_tile(a, s_row, min(kTile, e_end - e_begin), seq_base, swa_base, tid, ra);
-  if (e_begin + kTile < e_end)
-    load_tile(a, s_row + kTile, min(kTile, e_end - e_begin - kTile), seq_base, swa_base, tid, rb);
+  // (unconditional: a tile past the split's end loads zeros)
+  load_tile(src, s_row, min(kTile, e_end - e_begin), tid, ra);
+  load_tile(src, s_row + kTile, min(kTile, e_end - e_begin - kTile), tid, rb);
   // the query into LDS while the first tiles are in flight (read after the
   // first tile's barriers)
   if (active) {
@@ -216,9 +276,9 @@ __global__ __launch_bounds__(kNT) void k_attend(AttendArgs a) {
   auto tile = [&](RawTile& raw, int e0) {
     const int ne = min(kTile, e_end - e0);
     __syncthreads();                         // the previous tile's reads of s_k are done
-    store_tile(a, s_row + (e0 - e_begin), ne, swa_base, raw, tid, s_k);
+    store_tile(src, s_row + (e0 - e_begin), ne, e0 + ne > Es, raw, tid, s_k);
     const int e2 = e0 + 2 * kTile;           // this register set's next tile
-    if (e2 < e_end) load_tile(a, s_row + (e2 - e_begin), min(kTile, e_end - e2), seq_base, swa_base, tid, raw);
+    if (e2 < e_end) load_tile(src, s_row + (e2 - e_begin), min(kTile, e_end - e2), tid, raw);
     __syncthreads();
     if (!active) return;
 
