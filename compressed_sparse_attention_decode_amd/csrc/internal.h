@@ -38,6 +38,7 @@ struct PoolArgs {
   int mm_cap;                // (min, max) key pairs per query in the workspace
   int mm_span;               // blocks covered by one pair
   bool have_minmax;          // pairs and a cleared histogram already written (by the scan)
+  int nw_cap;                // bitmap words of the longest query's blocks (final step LDS)
   int32_t* pool_blocks;      // [n_q, pool]
   int32_t* pool_count;
 };

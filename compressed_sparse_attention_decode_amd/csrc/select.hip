@@ -7,8 +7,7 @@
 //
 // Keys are order-preserving uint32 images of the block scores.  One CU streams
 // a few tens of GB/s at most, so a long context (131,056 blocks at 1M) is
-// split into chunks of 4096 blocks, each handled by its own workgroup, and
-// only the final exact step runs one workgroup per query:
+// split into chunks of 4096 blocks, each handled by its own workgroup:
 //  K1 k_pool_minmax: per chunk, the smallest and largest key; chunk 0 also
 //     clears the query's global histogram.  (The Full scan can write these
 //     (min, max) pairs per scan tile and clear the histogram itself; then K1
@@ -19,15 +18,16 @@
 //     chunk in LDS, then added to the query's histogram.
 //  K3 k_pool_mark: every chunk finds the bin b* holding the P-th best block,
 //     writes its blocks of higher bins as a bitmap and lists its blocks of
-//     bin b* as candidates.
-//  K4 k_pool_final: the candidates (usually a few dozen) are ranked exactly
-//     against each other by (key desc, block asc) and the best join the
-//     selection (more than 128 candidates: an exact radix select over the bits
-//     below their common prefix gives the threshold key and how many blocks
-//     equal to it are needed, admitted lowest id first); the ordered compaction of the
-//     bitmap writes ascending block ids; the histogram is cleared again.  If a chunk listed more
-//     candidates than its slots, this step re-reads the block scores instead
-//     (correct for any input, slow only for near-constant scores).
+//     bin b* as candidates.  The last chunk workgroup of the query to finish
+//     then runs the final step: the candidates (usually a few dozen) are
+//     ranked exactly against each other by (key desc, block asc) and the
+//     best join the selection (more than 128 candidates: an exact radix
+//     select over the bits below their common prefix gives the threshold key
+//     and how many blocks equal to it are needed, admitted lowest id first);
+//     the ordered compaction of the bitmap writes ascending block ids; the
+//     histogram is cleared again.  If a chunk listed more candidates than
+//     its slots, this step re-reads the block scores instead (correct for
+//     any input, slow only for near-constant scores).
 #include "common.h"
 #include "internal.h"
 #include "select_common.h"
@@ -35,13 +35,11 @@
 namespace csa2 {
 namespace {
 
-constexpr int kCT = 256;                       // chunk workgroup threads
-constexpr int kFT = 1024;                      // final workgroup threads
-constexpr int kCandCap = 8192;                 // candidates the final step holds in LDS
+constexpr int kCT = 1024;                      // chunk workgroup threads
+constexpr int kCU = kPoolChunk / (kCT * 4);    // 16-byte block-score loads per chunk thread
+constexpr int kCandCap = 2048;                 // candidates the final step holds in LDS
 constexpr int kRankCap = 128;                 // candidates ranked exactly against each other (quadratic)
-constexpr int kMaxWords = kMaxBlocks / 32;
-static_assert(kPoolChunk == kCT * 16, "a chunk thread holds 16 blocks");
-static_assert(kHistBins == 4 * kFT, "the final step clears the histogram 4 words per thread");
+static_assert(kPoolChunk == kCT * 4 * kCU, "a chunk thread holds 4 kCU blocks");
 
 __device__ __forceinline__ uint32_t lane_prefix(uint64_t mask) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
@@ -56,6 +54,7 @@ struct PoolWs {
   uint32_t* hist;     // [kHistBins]
   uint32_t* mm;       // [mm_cap][2] min, max key per span of blocks
   uint32_t* cnt;      // [G] candidates listed per chunk (may exceed the slots)
+  uint32_t* done;     // [1] chunk workgroups of K3 finished (K2 clears it)
   uint32_t* sel;      // [G * kPoolChunk / 32] bitmap of blocks above bin b*
   uint32_t* ckey;     // [G][kPoolChunkCand]
   int32_t* cblk;      // [G][kPoolChunkCand]
@@ -67,7 +66,8 @@ __device__ __forceinline__ PoolWs pool_ws(const PoolArgs& a, int q) {
   w.hist = a.ws + (int64_t)q * a.ws_stride;
   w.mm = w.hist + kHistBins;
   w.cnt = w.mm + 2 * a.mm_cap;
-  w.sel = w.cnt + G;
+  w.done = w.cnt + G;
+  w.sel = w.done + 1;
   w.ckey = w.sel + G * (kPoolChunk / 32);
   w.cblk = reinterpret_cast<int32_t*>(w.ckey + G * kPoolChunkCand);
   return w;
@@ -78,24 +78,24 @@ __device__ __forceinline__ int query_blocks(const PoolArgs& a, int q) {
   return (c + 7) >> 3;
 }
 
-// The thread's 16 blocks of a chunk: 4 x 16-byte loads, block e of load u is
-// jb0(u) + e with jb0(u) = base + (u * kCT + tid) * 4.  The loads are bounded
+// The thread's 4 kCU blocks of a chunk: kCU 16-byte loads, block e of load u
+// is jb0(u) + e with jb0(u) = base + (u * kCT + tid) * 4.  The loads are bounded
 // by the row stride only (a multiple of 4 floats), so they need not wait for
 // the query's block count; blocks >= nb are masked afterwards.
 struct ChunkKeys {
-  v4f x[4];
-  uint32_t k[4][4];
-  uint32_t vm[4];
+  v4f x[kCU];
+  uint32_t k[kCU][4];
+  uint32_t vm[kCU];
   __device__ __forceinline__ void load(const float* bs, int base, int64_t ld, int tid) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < kCU; ++u) {
       const int jb0 = base + (u * kCT + tid) * 4;
       x[u] = jb0 < ld ? *reinterpret_cast<const v4f*>(bs + jb0) : v4f{0.0f, 0.0f, 0.0f, 0.0f};
     }
   }
   __device__ __forceinline__ void finish(int base, int nb, int tid) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < kCU; ++u) {
       const int left = nb - (base + (u * kCT + tid) * 4);
       vm[u] = left >= 4 ? 15u : (left <= 0 ? 0u : (1u << left) - 1u);
 #pragma unroll
@@ -105,24 +105,32 @@ struct ChunkKeys {
 };
 
 // The query's key range from the (min, max) pairs of its spans of blocks
-// (chunks of K1, or scan tiles).  load() issues the thread's first pair before
-// the block count is known; reduce() masks it and reads any further pairs.
+// (chunks of K1, or scan tiles).  load() issues the thread's first kKrPer
+// pairs (clamped to the workspace, so before the block count is known);
+// reduce() masks them by the count and reads any further pairs.
+constexpr int kKrPer = 4;
 template <int NT>
 struct KeyRange {
-  v2u m0;
+  v2u m[kKrPer];
   __device__ __forceinline__ void load(const PoolArgs& a, const PoolWs& w) {
-    const int i = threadIdx.x;
-    m0 = i < a.mm_cap ? *reinterpret_cast<const v2u*>(w.mm + 2 * i) : v2u{0xFFFFFFFFu, 0u};
+#pragma unroll
+    for (int r = 0; r < kKrPer; ++r)
+      m[r] = *reinterpret_cast<const v2u*>(w.mm + 2 * min((int)threadIdx.x + r * NT, a.mm_cap - 1));
   }
   __device__ __forceinline__ void reduce(const PoolArgs& a, const PoolWs& w, int nb, uint32_t* s_scan,
                                          uint32_t* kmin, uint32_t* kmax) {
-    const int n = (nb + a.mm_span - 1) / a.mm_span;
+    const int n = min(a.mm_cap, (nb + a.mm_span - 1) / a.mm_span);
     uint32_t lo = 0xFFFFFFFFu, hi = 0;
-    if ((int)threadIdx.x < n) { lo = m0[0]; hi = m0[1]; }
-    for (int i = threadIdx.x + NT; i < n; i += NT) {
-      const v2u m = *reinterpret_cast<const v2u*>(w.mm + 2 * i);
-      lo = min(lo, m[0]);
-      hi = max(hi, m[1]);
+#pragma unroll
+    for (int r = 0; r < kKrPer; ++r) {
+      const bool v = (int)threadIdx.x + r * NT < n;
+      lo = min(lo, v ? m[r][0] : 0xFFFFFFFFu);
+      hi = max(hi, v ? m[r][1] : 0u);
+    }
+    for (int i = threadIdx.x + kKrPer * NT; i < n; i += NT) {
+      const v2u x = *reinterpret_cast<const v2u*>(w.mm + 2 * i);
+      lo = min(lo, x[0]);
+      hi = max(hi, x[1]);
     }
     block_minmax_u32<NT>(&lo, &hi, s_scan);
     *kmin = lo;
@@ -204,7 +212,7 @@ __global__ __launch_bounds__(kCT) void k_pool_minmax(PoolArgs a) {
   if (nb > a.pool && base < nb) {
     c.finish(base, nb, tid);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < kCU; ++u) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         if (c.vm[u] >> e & 1u) {
@@ -232,6 +240,7 @@ __global__ __launch_bounds__(kCT) void k_pool_hist(PoolArgs a) {
   c.load(a.bscore + (int64_t)q * a.ld, base, a.ld, tid);
   KeyRange<kCT> kr;
   kr.load(a, w);
+  if (g == 0 && tid == 0) *w.done = 0;
   const int nb = query_blocks(a, q);
   if (nb <= a.pool || base >= nb) return;
   c.finish(base, nb, tid);
@@ -240,7 +249,7 @@ __global__ __launch_bounds__(kCT) void k_pool_hist(PoolArgs a) {
   kr.reduce(a, w, nb, s_scan, &kmin, &kmax);     // its barriers order the clear
   const Bins b = bins_for(kmin, kmax);
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
+  for (int u = 0; u < kCU; ++u) {
 #pragma unroll
     for (int e = 0; e < 4; ++e)
       if (c.vm[u] >> e & 1u) atomicAdd(&s_hist[b.bin(c.k[u][e])], 1u);
@@ -252,131 +261,61 @@ __global__ __launch_bounds__(kCT) void k_pool_hist(PoolArgs a) {
   }
 }
 
-// ---------------------------------------------------------------- K3
-__global__ __launch_bounds__(kCT) void k_pool_mark(PoolArgs a) {
-  __shared__ uint32_t s_scan[2 * (kCT / 64)];
-  __shared__ uint32_t s_misc[2];
-  __shared__ uint32_t s_ccount;
-  const int q = blockIdx.x / a.chunks, g = blockIdx.x % a.chunks;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int base = g * kPoolChunk;
-  const PoolWs w = pool_ws(a, q);
-  ChunkKeys c;
-  c.load(a.bscore + (int64_t)q * a.ld, base, a.ld, tid);
-  HistSlice<kCT> h;
-  h.load(w.hist);
-  KeyRange<kCT> kr;
-  kr.load(a, w);
-  const int nb = query_blocks(a, q);
-  if (nb <= a.pool || base >= nb) {
-    if (tid == 0) w.cnt[g] = 0;
-    return;
-  }
-  c.finish(base, nb, tid);
-  if (tid == 0) s_ccount = 0;
-  uint32_t kmin, kmax;
-  kr.reduce(a, w, nb, s_scan, &kmin, &kmax);
-  const Bins b = bins_for(kmin, kmax);
-  find_bstar<kCT>(h, (uint32_t)a.pool, s_scan, s_misc);
-  const uint32_t bstar = s_misc[0];
-
-  uint32_t* ck = w.ckey + (int64_t)g * kPoolChunkCand;
-  int32_t* cj = w.cblk + (int64_t)g * kPoolChunkCand;
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int jb0 = base + (u * kCT + tid) * 4;
-    uint32_t hib = 0, cand = 0;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const bool v = c.vm[u] >> e & 1u;
-      const uint32_t bin = b.bin(c.k[u][e]);
-      hib |= (uint32_t)(v && bin > bstar) << e;
-      cand |= (uint32_t)(v && bin == bstar) << e;
-    }
-    // a lane's 4 blocks form one nibble; 8 lanes OR their nibbles into a word
-    uint32_t word = hib << (4 * (lane & 7));
-    word |= __shfl_xor(word, 1, 64);
-    word |= __shfl_xor(word, 2, 64);
-    word |= __shfl_xor(word, 4, 64);
-    if ((lane & 7) == 0 && jb0 < nb) w.sel[jb0 >> 5] = word;
-    uint64_t m[4];
-    uint32_t tot = 0;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      m[e] = __ballot(cand >> e & 1u);
-      tot += (uint32_t)__popcll(m[e]);
-    }
-    if (tot == 0) continue;                       // wave-uniform
-    uint32_t slot0 = 0;
-    if (lane == 0) slot0 = atomicAdd(&s_ccount, tot);
-    slot0 = __shfl(slot0, 0, 64);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      if (cand >> e & 1u) {
-        const uint32_t slot = slot0 + lane_prefix(m[e]);
-        if (slot < (uint32_t)kPoolChunkCand) { ck[slot] = c.k[u][e]; cj[slot] = jb0 + e; }
-      }
-      slot0 += (uint32_t)__popcll(m[e]);
-    }
-  }
-  __syncthreads();
-  if (tid == 0) w.cnt[g] = s_ccount;
-}
-
-// ---------------------------------------------------------------- K4
-__global__ __launch_bounds__(kFT) void k_pool_final(PoolArgs a) {
+// ---------------------------------------------------------------- K3 + K4
+// The final step of one query, run by the last of its chunk workgroups
+// (NT threads).  dyn: LDS of 2 * nw_cap + 2 * kCandCap words (the selection
+// and tie bitmaps, the gathered candidates).
+template <int NT>
+__device__ __forceinline__ void pool_final(const PoolArgs& a, int q, const PoolWs& w, uint32_t* dyn) {
   __shared__ uint32_t s_hist[256];
-  __shared__ uint32_t s_sel[kMaxWords];
-  __shared__ uint32_t s_tie[kMaxWords];
-  __shared__ uint32_t s_ckey[kCandCap];
-  __shared__ int32_t s_cj[kCandCap];
   __shared__ uint32_t s_off[kMaxBlocks / kPoolChunk + 1];
-  __shared__ uint32_t s_scan[2 * (kFT / 64)];
+  __shared__ uint32_t s_scan[2 * (NT / 64)];
   __shared__ uint32_t s_misc[4];
+  uint32_t* s_sel = dyn;
+  uint32_t* s_tie = dyn + a.nw_cap;
+  uint32_t* s_ckey = dyn + 2 * a.nw_cap;
+  int32_t* s_cj = reinterpret_cast<int32_t*>(s_ckey + kCandCap);
 
-  const int q = blockIdx.x, tid = threadIdx.x;
+  const int tid = threadIdx.x;
   const int P = a.pool, G = a.chunks;
-  const PoolWs w = pool_ws(a, q);
   const float* bs = a.bscore + (int64_t)q * a.ld;
-
-  // every independent read issued before the first wait (none waits for the
-  // block count): the bitmap of blocks above b* (the query's whole region),
-  // the histogram, the chunks' candidate counts, the key-range pairs
-  constexpr int kSelPer = kMaxWords / kFT;
-  uint32_t selw[kSelPer];
-#pragma unroll
-  for (int k = 0; k < kSelPer; ++k) {
-    const int i = tid + k * kFT;
-    selw[k] = i < G * (kPoolChunk / 32) ? w.sel[i] : 0u;
-  }
-  HistSlice<kFT> h;
-  h.load(w.hist);
-  const uint32_t cnt_v = tid < G ? w.cnt[tid] : 0u;
-  KeyRange<kFT> kr;
-  kr.load(a, w);
   const int nb = query_blocks(a, q);
   int32_t* out = a.pool_blocks + (int64_t)q * P;
   if (nb <= P) {
-    for (int j = tid; j < P; j += kFT) out[j] = j < nb ? j : -1;
+    for (int j = tid; j < P; j += NT) out[j] = j < nb ? j : -1;
     if (tid == 0) a.pool_count[q] = nb;
+    for (int i = tid * 4; i < kHistBins; i += NT * 4) *reinterpret_cast<v4u*>(w.hist + i) = v4u{0u, 0u, 0u, 0u};
     return;
   }
   const int nw = (nb + 31) >> 5;
+
+  // every independent read issued before the first wait: the bitmap of
+  // blocks above b*, the histogram, the chunks' candidate counts, the
+  // key-range pairs
+  constexpr int kSelPer = (kMaxBlocks / 32 + NT - 1) / NT;
+  uint32_t selw[kSelPer];
+#pragma unroll
+  for (int k = 0; k < kSelPer; ++k) selw[k] = w.sel[min(tid + k * NT, nw - 1)];
+  HistSlice<NT> h;
+  h.load(w.hist);
+  const uint32_t cnt_v = w.cnt[min(tid, G - 1)];
+  KeyRange<NT> kr;
+  kr.load(a, w);
   uint32_t kmin, kmax;
   kr.reduce(a, w, nb, s_scan, &kmin, &kmax);
 #pragma unroll
   for (int k = 0; k < kSelPer; ++k) {
-    const int i = tid + k * kFT;
+    const int i = tid + k * NT;
     if (i < nw) { s_sel[i] = selw[k]; s_tie[i] = 0; }
   }
   const Bins b = bins_for(kmin, kmax);
-  find_bstar<kFT>(h, (uint32_t)P, s_scan, s_misc);
+  find_bstar<NT>(h, (uint32_t)P, s_scan, s_misc);
   const uint32_t bstar = s_misc[0];
   uint32_t need = (uint32_t)P - s_misc[1];
 
   // candidate lists of the chunks (offsets by a wave-0 scan over <= 64 chunks)
   if (tid < 64) {
-    const uint32_t v = cnt_v;
+    const uint32_t v = tid < G ? cnt_v : 0u;
     const bool over = v > (uint32_t)kPoolChunkCand;
     const uint32_t x = wave_incl_scan_u32(v);
     if (tid < G) s_off[tid] = x - v;
@@ -391,7 +330,7 @@ __global__ __launch_bounds__(kFT) void k_pool_final(PoolArgs a) {
   const bool in_lds = s_misc[2] == 0;
   if (in_lds) {
     const int wave = tid >> 6, lane = tid & 63;
-    for (int g = wave; g < G; g += kFT / 64) {
+    for (int g = wave; g < G; g += NT / 64) {
       const uint32_t n = s_off[g + 1] - s_off[g];
       for (uint32_t i = lane; i < n; i += 64) {
         s_ckey[s_off[g] + i] = w.ckey[(int64_t)g * kPoolChunkCand + i];
@@ -403,12 +342,13 @@ __global__ __launch_bounds__(kFT) void k_pool_final(PoolArgs a) {
 
   // Up to kRankCap candidates held in LDS are ranked exactly against each
   // other by (key desc, block asc); the best `need` join the selection.
-  // Otherwise a radix select over bits [0, cs) finds the threshold key T and
-  // how many blocks equal to T are needed, admitted lowest block first.
+  // Otherwise a radix select over the candidates' own key range finds the
+  // threshold key T and how many blocks equal to T are needed, admitted
+  // lowest block first.
   const bool ranked = in_lds && C <= (uint32_t)kRankCap;
   uint32_t need_eq = 0;
   if (ranked) {
-    for (uint32_t i = tid; i < C; i += kFT) {
+    for (uint32_t i = tid; i < C; i += NT) {
       const uint32_t ki = s_ckey[i];
       const int ji = s_cj[i];
       uint32_t r = 0;
@@ -424,28 +364,28 @@ __global__ __launch_bounds__(kFT) void k_pool_final(PoolArgs a) {
     // the candidates' own key range: its common leading bits are decided
     uint32_t clo = 0xFFFFFFFFu, chi = 0;
     if (in_lds) {
-      for (uint32_t i = tid; i < C; i += kFT) { clo = min(clo, s_ckey[i]); chi = max(chi, s_ckey[i]); }
+      for (uint32_t i = tid; i < C; i += NT) { clo = min(clo, s_ckey[i]); chi = max(chi, s_ckey[i]); }
     } else {
-      for (int jb = tid; jb < nb; jb += kFT) {
+      for (int jb = tid; jb < nb; jb += NT) {
         const uint32_t key = order_key(bs[jb]);
         if (b.bin(key) == bstar) { clo = min(clo, key); chi = max(chi, key); }
       }
     }
-    block_minmax_u32<kFT>(&clo, &chi, s_scan);
+    block_minmax_u32<NT>(&clo, &chi, s_scan);
     int fixed_lo = highest_diff_bit(clo, chi) + 1;     // bits >= fixed_lo are decided
     uint32_t prefix = (uint32_t)(((uint64_t)clo >> fixed_lo) << fixed_lo);
     while (fixed_lo > 0) {
       const int sh = max(0, fixed_lo - 8);
       const uint32_t dmask = (1u << (fixed_lo - sh)) - 1;
-      if (tid < 256) s_hist[tid] = 0;
+      for (int i = tid; i < 256; i += NT) s_hist[i] = 0;
       __syncthreads();
       if (in_lds) {
-        for (uint32_t i = tid; i < C; i += kFT) {
+        for (uint32_t i = tid; i < C; i += NT) {
           const uint32_t key = s_ckey[i];
           if (same_above(key, prefix, fixed_lo)) atomicAdd(&s_hist[(key >> sh) & dmask], 1u);
         }
       } else {
-        for (int jb = tid; jb < nb; jb += kFT) {
+        for (int jb = tid; jb < nb; jb += NT) {
           const uint32_t key = order_key(bs[jb]);
           if (b.bin(key) == bstar && same_above(key, prefix, fixed_lo))
             atomicAdd(&s_hist[(key >> sh) & dmask], 1u);
@@ -463,14 +403,14 @@ __global__ __launch_bounds__(kFT) void k_pool_final(PoolArgs a) {
     need_eq = need;
     // candidates above T join the selection; those equal to T are tie bits
     if (in_lds) {
-      for (uint32_t i = tid; i < C; i += kFT) {
+      for (uint32_t i = tid; i < C; i += NT) {
         const uint32_t key = s_ckey[i];
         const int jb = s_cj[i];
         if (key > T) atomicOr(&s_sel[jb >> 5], 1u << (jb & 31));
         else if (key == T) atomicOr(&s_tie[jb >> 5], 1u << (jb & 31));
       }
     } else {
-      for (int jb = tid; jb < nb; jb += kFT) {
+      for (int jb = tid; jb < nb; jb += NT) {
         const uint32_t key = order_key(bs[jb]);
         if (b.bin(key) != bstar) continue;
         if (key > T) atomicOr(&s_sel[jb >> 5], 1u << (jb & 31));
@@ -481,13 +421,13 @@ __global__ __launch_bounds__(kFT) void k_pool_final(PoolArgs a) {
   }
 
   // ordered compaction (ties, in the radix path, admitted in ascending block order)
-  const int wpt = (nw + kFT - 1) / kFT;
+  const int wpt = (nw + NT - 1) / NT;
   const int w_lo = min(nw, tid * wpt), w_hi = min(nw, w_lo + wpt);
   uint32_t total;
   if (!ranked) {
     uint32_t ties = 0;
     for (int i = w_lo; i < w_hi; ++i) ties += __popc(s_tie[i]);
-    uint32_t tie_before = block_exclusive_scan<kFT>(ties, s_scan, &total);
+    uint32_t tie_before = block_exclusive_scan<NT>(ties, s_scan, &total);
     for (int i = w_lo; i < w_hi; ++i) {
       uint32_t t = s_tie[i], acc = 0;
       while (t && tie_before < need_eq) {
@@ -501,7 +441,7 @@ __global__ __launch_bounds__(kFT) void k_pool_final(PoolArgs a) {
   }
   uint32_t sel_local = 0;
   for (int i = w_lo; i < w_hi; ++i) sel_local += __popc(s_sel[i]);
-  uint32_t out_before = block_exclusive_scan<kFT>(sel_local, s_scan, &total);
+  uint32_t out_before = block_exclusive_scan<NT>(sel_local, s_scan, &total);
   for (int i = w_lo; i < w_hi; ++i) {
     uint32_t fin = s_sel[i];
     while (fin) {
@@ -514,23 +454,124 @@ __global__ __launch_bounds__(kFT) void k_pool_final(PoolArgs a) {
   if (tid == 0) a.pool_count[q] = P;
   // leave the histogram cleared: a later pool call on the same scan-prepared
   // workspace (the same block scores) accumulates onto zero again
-  *reinterpret_cast<v4u*>(w.hist + 4 * tid) = v4u{0u, 0u, 0u, 0u};
+  for (int i = tid * 4; i < kHistBins; i += NT * 4) *reinterpret_cast<v4u*>(w.hist + i) = v4u{0u, 0u, 0u, 0u};
+}
+
+// Marking per chunk; the last chunk workgroup of a query to finish (counted
+// in the workspace's done word, which K2 clears) runs the final step.  The
+// marks cross workgroups through memory: after a store drain and a barrier,
+// one release fence per workgroup publishes them before it counts itself
+// in, and the last one's acquire fence makes the others' visible.
+__global__ __launch_bounds__(kCT) void k_pool_mark(PoolArgs a) {
+  extern __shared__ uint32_t s_dyn[];
+  __shared__ uint32_t s_scan[2 * (kCT / 64)];
+  __shared__ uint32_t s_misc[2];
+  __shared__ uint32_t s_ccount;
+  __shared__ uint32_t s_last;
+  const int q = blockIdx.x / a.chunks, g = blockIdx.x % a.chunks;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int base = g * kPoolChunk;
+  const PoolWs w = pool_ws(a, q);
+  ChunkKeys c;
+  c.load(a.bscore + (int64_t)q * a.ld, base, a.ld, tid);
+  HistSlice<kCT> h;
+  h.load(w.hist);
+  KeyRange<kCT> kr;
+  kr.load(a, w);
+  const int nb = query_blocks(a, q);
+  if (nb > a.pool && base < nb) {
+    c.finish(base, nb, tid);
+    if (tid == 0) s_ccount = 0;
+    uint32_t kmin, kmax;
+    kr.reduce(a, w, nb, s_scan, &kmin, &kmax);
+    const Bins b = bins_for(kmin, kmax);
+    find_bstar<kCT>(h, (uint32_t)a.pool, s_scan, s_misc);
+    const uint32_t bstar = s_misc[0];
+
+    uint32_t* ck = w.ckey + (int64_t)g * kPoolChunkCand;
+    int32_t* cj = w.cblk + (int64_t)g * kPoolChunkCand;
+#pragma unroll
+    for (int u = 0; u < kCU; ++u) {
+      const int jb0 = base + (u * kCT + tid) * 4;
+      uint32_t hib = 0, cand = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bool v = c.vm[u] >> e & 1u;
+        const uint32_t bin = b.bin(c.k[u][e]);
+        hib |= (uint32_t)(v && bin > bstar) << e;
+        cand |= (uint32_t)(v && bin == bstar) << e;
+      }
+      // a lane's 4 blocks form one nibble; 8 lanes OR their nibbles into a word
+      uint32_t word = hib << (4 * (lane & 7));
+      word |= __shfl_xor(word, 1, 64);
+      word |= __shfl_xor(word, 2, 64);
+      word |= __shfl_xor(word, 4, 64);
+      if ((lane & 7) == 0 && jb0 < nb) w.sel[jb0 >> 5] = word;
+      uint64_t m[4];
+      uint32_t tot = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        m[e] = __ballot(cand >> e & 1u);
+        tot += (uint32_t)__popcll(m[e]);
+      }
+      if (tot == 0) continue;                       // wave-uniform
+      uint32_t slot0 = 0;
+      if (lane == 0) slot0 = atomicAdd(&s_ccount, tot);
+      slot0 = __shfl(slot0, 0, 64);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (cand >> e & 1u) {
+          const uint32_t slot = slot0 + lane_prefix(m[e]);
+          if (slot < (uint32_t)kPoolChunkCand) { ck[slot] = c.k[u][e]; cj[slot] = jb0 + e; }
+        }
+        slot0 += (uint32_t)__popcll(m[e]);
+      }
+    }
+    __syncthreads();
+    if (tid == 0) w.cnt[g] = s_ccount;
+  } else if (tid == 0) {
+    w.cnt[g] = 0;
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's stores have reached L2
+  __syncthreads();
+  if (tid == 0) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    const uint32_t prev = __hip_atomic_fetch_add(w.done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = prev == (uint32_t)(a.chunks - 1);
+    if (s_last) {
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      *w.done = 0;
+    }
+  }
+  __syncthreads();
+  if (!s_last) return;
+  pool_final<kCT>(a, q, w, s_dyn);
 }
 
 }  // namespace
 
 int64_t pool_ws_words(int chunks, int mm_cap) {
-  const int64_t words = kHistBins + 2 * (int64_t)mm_cap + chunks + (int64_t)chunks * (kPoolChunk / 32) +
+  const int64_t words = kHistBins + 2 * (int64_t)mm_cap + chunks + 1 + (int64_t)chunks * (kPoolChunk / 32) +
                         2 * (int64_t)chunks * kPoolChunkCand;
   return (words + 63) / 64 * 64;
 }
 
+size_t pool_final_lds(int nw_cap) { return ((size_t)2 * nw_cap + 2 * kCandCap) * 4; }
+
 hipError_t launch_pool_select(const PoolArgs& a, hipStream_t s) {
   const dim3 grid((unsigned)(a.n_q * a.chunks));
+  const size_t lds = pool_final_lds(a.nw_cap);
+  // dynamic LDS above the default limit must be allowed once per size
+  static size_t lds_allowed = 0;
+  if (lds > 48 * 1024 && lds > lds_allowed) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_pool_mark),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    lds_allowed = lds;
+  }
   if (!a.have_minmax) hipLaunchKernelGGL(k_pool_minmax, grid, dim3(kCT), 0, s, a);
   hipLaunchKernelGGL(k_pool_hist, grid, dim3(kCT), 0, s, a);
-  hipLaunchKernelGGL(k_pool_mark, grid, dim3(kCT), 0, s, a);
-  hipLaunchKernelGGL(k_pool_final, dim3((unsigned)a.n_q), dim3(kFT), 0, s, a);
+  hipLaunchKernelGGL(k_pool_mark, grid, dim3(kCT), lds, s, a);
   return hipGetLastError();
 }
 
