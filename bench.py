@@ -36,7 +36,7 @@ import workloads as wl  # noqa: E402
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 SCAN_SOURCES = ["compressed_sparse_attention_decode_amd/csrc/scan.hip",
                 "compressed_sparse_attention_decode_amd/csrc/common.h",
-                "compressed_sparse_attention_decode_amd/csrc/internal.h"]
+                "compressed_sparse_attention_decode_amd/csrc/scan_args.h"]
 
 
 # ---------------------------------------------------------------- device state

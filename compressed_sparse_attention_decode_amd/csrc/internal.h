@@ -5,27 +5,9 @@
 #include <stddef.h>
 #include <stdint.h>
 
-namespace csa2 {
+#include "scan_args.h"
 
-struct ScanArgs {
-  const uint8_t* idx_q;      // [n_q, Hi, d]
-  const float* idx_w;        // [n_q, Hi]
-  const uint8_t* idx_k;      // [rows, d]
-  const int64_t* seq_base;   // [n_q]
-  const int32_t* n_visible;  // [n_q]
-  int n_q, hi, d, swa, g;    // g: queries per sequence
-  int tiles;                 // position tiles per query
-  int tile_pos;              // positions per tile (multiple of 64)
-  int prefetch;              // LDS ring slots per wave (4 or 6)
-  int waves;                 // waves per workgroup (4 or 8)
-  float* bscore;             // [n_q, ld]
-  int64_t ld;
-  // optional (nullptr: not written): the pool-select workspace, where each
-  // tile stores the (min, max) order keys of its block scores at pair `tile`
-  // and tile 0 clears the query's histogram
-  uint32_t* pool_ws;
-  int64_t pool_ws_stride;
-};
+namespace csa2 {
 
 struct PoolArgs {
   const float* bscore;
@@ -86,19 +68,14 @@ struct AttendArgs {
 hipError_t launch_encode(int64_t n, const uint16_t* latent, const uint16_t* rope,
                          const int64_t* dst_row, uint8_t* codes, uint8_t* scales,
                          uint16_t* rope_out, hipStream_t s);
-hipError_t launch_scan(const ScanArgs& a, hipStream_t s);
 hipError_t launch_pool_select(const PoolArgs& a, hipStream_t s);
 int64_t pool_ws_words(int chunks, int mm_cap);   // workspace words per query
 hipError_t launch_reindex(const ReindexArgs& a, hipStream_t s);
 hipError_t launch_attend(const AttendArgs& a, hipStream_t s);
 
 // Tiling constants the host needs for grids and workspace sizes.
-constexpr int kHistBins = 4096;        // pool histogram bins (12 key bits)
 constexpr int kPoolChunk = 4096;       // blocks per pool-select chunk workgroup
 constexpr int kPoolChunkCand = 1024;   // candidate slots per chunk
-constexpr int kScanTile = 2048;        // default positions per scan workgroup
-constexpr int kScanPrefetch = 4;       // default LDS ring slots per wave
-constexpr int kScanWaves = 4;          // default waves per scan workgroup
 constexpr int kAttendTile = 32;        // entries per attention tile
 constexpr int kAttendWaves = 4;        // waves per attention workgroup (16 heads each)
 constexpr int kAttendMaxSplits = 16;   // entry-list splits per query, at most

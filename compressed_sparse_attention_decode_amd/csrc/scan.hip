@@ -25,7 +25,7 @@
 //    leave in one coalesced store (4 bytes per 1 KiB of keys).
 // HBM-bound: 128 bytes of keys per position, 16 KFLOP per position.
 #include "common.h"
-#include "internal.h"
+#include "scan_args.h"
 
 namespace csa2 {
 namespace {

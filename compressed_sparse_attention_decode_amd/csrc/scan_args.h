@@ -1,0 +1,38 @@
+// The Full scan's launch arguments and constants (kept apart from the other
+// stages' so that a change elsewhere leaves the scan's sources untouched).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace csa2 {
+
+struct ScanArgs {
+  const uint8_t* idx_q;      // [n_q, Hi, d]
+  const float* idx_w;        // [n_q, Hi]
+  const uint8_t* idx_k;      // [rows, d]
+  const int64_t* seq_base;   // [n_q]
+  const int32_t* n_visible;  // [n_q]
+  int n_q, hi, d, swa, g;    // g: queries per sequence
+  int tiles;                 // position tiles per query
+  int tile_pos;              // positions per tile (multiple of 64)
+  int prefetch;              // LDS ring slots per wave (4 or 6)
+  int waves;                 // waves per workgroup (4 or 8)
+  float* bscore;             // [n_q, ld]
+  int64_t ld;
+  // optional (nullptr: not written): the pool-select workspace, where each
+  // tile stores the (min, max) order keys of its block scores at pair `tile`
+  // and tile 0 clears the query's histogram
+  uint32_t* pool_ws;
+  int64_t pool_ws_stride;
+};
+
+hipError_t launch_scan(const ScanArgs& a, hipStream_t s);
+
+constexpr int kHistBins = 4096;        // pool histogram bins, cleared by the scan's tile 0
+constexpr int kScanTile = 2048;        // default positions per scan workgroup
+constexpr int kScanPrefetch = 4;       // default LDS ring slots per wave
+constexpr int kScanWaves = 4;          // default waves per scan workgroup
+
+}  // namespace csa2
