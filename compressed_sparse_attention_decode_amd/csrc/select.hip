@@ -262,11 +262,20 @@ __global__ __launch_bounds__(kCT) void k_pool_hist(PoolArgs a) {
 }
 
 // ---------------------------------------------------------------- K3 + K4
+// What a marking workgroup already knows of its query (the same for every
+// chunk): the key range, the bin b* and the count of blocks above it.
+struct MarkState {
+  bool valid;
+  uint32_t kmin, kmax, bstar, above;
+};
+
 // The final step of one query, run by the last of its chunk workgroups
 // (NT threads).  dyn: LDS of 2 * nw_cap + 2 * kCandCap words (the selection
-// and tie bitmaps, the gathered candidates).
+// and tie bitmaps, the gathered candidates).  With a valid MarkState the
+// histogram and the key-range pairs are not read again.
 template <int NT>
-__device__ __forceinline__ void pool_final(const PoolArgs& a, int q, const PoolWs& w, uint32_t* dyn) {
+__device__ __forceinline__ void pool_final(const PoolArgs& a, int q, const PoolWs& w, uint32_t* dyn,
+                                           const MarkState& ms) {
   __shared__ uint32_t s_hist[256];
   __shared__ uint32_t s_off[kMaxBlocks / kPoolChunk + 1];
   __shared__ uint32_t s_scan[2 * (NT / 64)];
@@ -296,22 +305,25 @@ __device__ __forceinline__ void pool_final(const PoolArgs& a, int q, const PoolW
   uint32_t selw[kSelPer];
 #pragma unroll
   for (int k = 0; k < kSelPer; ++k) selw[k] = w.sel[min(tid + k * NT, nw - 1)];
-  HistSlice<NT> h;
-  h.load(w.hist);
   const uint32_t cnt_v = w.cnt[min(tid, G - 1)];
-  KeyRange<NT> kr;
-  kr.load(a, w);
-  uint32_t kmin, kmax;
-  kr.reduce(a, w, nb, s_scan, &kmin, &kmax);
+  uint32_t kmin = ms.kmin, kmax = ms.kmax, bstar = ms.bstar, above = ms.above;
+  if (!ms.valid) {                       // uniform: the workgroup marked no chunk
+    HistSlice<NT> h;
+    h.load(w.hist);
+    KeyRange<NT> kr;
+    kr.load(a, w);
+    kr.reduce(a, w, nb, s_scan, &kmin, &kmax);
+    find_bstar<NT>(h, (uint32_t)P, s_scan, s_misc);
+    bstar = s_misc[0];
+    above = s_misc[1];
+  }
 #pragma unroll
   for (int k = 0; k < kSelPer; ++k) {
     const int i = tid + k * NT;
     if (i < nw) { s_sel[i] = selw[k]; s_tie[i] = 0; }
   }
   const Bins b = bins_for(kmin, kmax);
-  find_bstar<NT>(h, (uint32_t)P, s_scan, s_misc);
-  const uint32_t bstar = s_misc[0];
-  uint32_t need = (uint32_t)P - s_misc[1];
+  uint32_t need = (uint32_t)P - above;
 
   // candidate lists of the chunks (offsets by a wave-0 scan over <= 64 chunks)
   if (tid < 64) {
@@ -479,6 +491,7 @@ __global__ __launch_bounds__(kCT) void k_pool_mark(PoolArgs a) {
   KeyRange<kCT> kr;
   kr.load(a, w);
   const int nb = query_blocks(a, q);
+  MarkState ms = {false, 0u, 0u, 0u, 0u};
   if (nb > a.pool && base < nb) {
     c.finish(base, nb, tid);
     if (tid == 0) s_ccount = 0;
@@ -487,6 +500,7 @@ __global__ __launch_bounds__(kCT) void k_pool_mark(PoolArgs a) {
     const Bins b = bins_for(kmin, kmax);
     find_bstar<kCT>(h, (uint32_t)a.pool, s_scan, s_misc);
     const uint32_t bstar = s_misc[0];
+    ms = {true, kmin, kmax, bstar, s_misc[1]};
 
     uint32_t* ck = w.ckey + (int64_t)g * kPoolChunkCand;
     int32_t* cj = w.cblk + (int64_t)g * kPoolChunkCand;
@@ -545,7 +559,7 @@ __global__ __launch_bounds__(kCT) void k_pool_mark(PoolArgs a) {
   }
   __syncthreads();
   if (!s_last) return;
-  pool_final<kCT>(a, q, w, s_dyn);
+  pool_final<kCT>(a, q, w, s_dyn, ms);
 }
 
 }  // namespace
