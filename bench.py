@@ -465,7 +465,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8 keys / fp4 KV; f16+bf16 MFMA, fp32 accumulate",
+        "dtype": "f16",
+        "dtype_detail": "e4m3 indexer keys and E2M1/E4M3 KV, converted exactly to f16 for the MFMAs; fp32 accumulate",
         "data": "synthetic (seeded N(0,1) fp8 keys and queries, bf16 latents FP4-encoded, U(0,1) weights)",
         "config": {"workload": w.name, "batch": w.n_seq, "tokens_per_seq": w.tokens_per_seq,
                    "ctx": list(w.ctx), "heads": d.n_heads, "idx_heads": d.idx_heads, "idx_dim": d.idx_dim,
