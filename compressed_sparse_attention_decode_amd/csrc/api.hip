@@ -258,6 +258,8 @@ csa2_status run_pool(const csa2_dims* d, const csa2_queries* q, const float* blo
   pa.chunks = pool_chunks(d, q);
   pa.mm_cap = pool_mm_cap(d, q);
   pa.nw_cap = (int)((max_blocks(d, q) + 31) / 32);
+  pa.small = max_blocks(d, q) <= kPoolSmallBlocks;
+  if (const char* env = getenv("CSA2_POOL_SMALL")) pa.small = pa.small && atoi(env) != 0;
   pa.ws = (uint32_t*)ws;
   pa.ws_stride = pool_ws_words(pa.chunks, pa.mm_cap);
   pa.have_minmax = after_scan;

@@ -21,6 +21,7 @@ struct PoolArgs {
   int mm_span;               // blocks covered by one pair
   bool have_minmax;          // pairs and a cleared histogram already written (by the scan)
   int nw_cap;                // bitmap words of the longest query's blocks (final step LDS)
+  bool small;                // every query has <= kPoolSmallBlocks blocks: one-workgroup selection
   int32_t* pool_blocks;      // [n_q, pool]
   int32_t* pool_count;
 };
@@ -76,6 +77,7 @@ hipError_t launch_attend(const AttendArgs& a, hipStream_t s);
 // Tiling constants the host needs for grids and workspace sizes.
 constexpr int kPoolChunk = 4096;       // blocks per pool-select chunk workgroup
 constexpr int kPoolChunkCand = 1024;   // candidate slots per chunk
+constexpr int kPoolSmallBlocks = 16384;   // blocks a one-workgroup pool selection holds
 constexpr int kAttendTile = 32;        // entries per attention tile
 constexpr int kAttendWaves = 4;        // waves per attention workgroup (16 heads each)
 constexpr int kAttendMaxSplits = 16;   // entry-list splits per query, at most

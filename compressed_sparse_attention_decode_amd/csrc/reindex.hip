@@ -22,6 +22,7 @@
 //    admitting keys equal to the threshold lowest position first.
 #include "common.h"
 #include "internal.h"
+#include "radix_topk.h"
 #include "select_common.h"
 
 namespace csa2 {
@@ -127,75 +128,16 @@ __device__ __forceinline__ void score_part(const ReindexArgs& a, int q, int part
   }
 }
 
-constexpr int kTkThreads = 512;                    // 8 waves: up to 256 VGPRs per thread
-constexpr int kMaxCand = 2048 * kBlock;
-constexpr int kPer = kMaxCand / kTkThreads;        // 32 keys per thread, in registers
-constexpr int kBlkPer = kPer / kBlock;             // pool blocks per thread
-constexpr int kTkBins = 2048;                      // radix digit: up to 11 bits
-constexpr int kTkEmpty = 16;                       // bins past kTkBins that count empty slots
-constexpr int kTkWaves = kTkThreads / 64;
-constexpr int kRankCap = 128;                      // candidates ranked exactly against each other (quadratic)
-static_assert(kTkBins == 4 * kTkThreads, "one 16-byte histogram clear per thread");
+constexpr int kBlkPer = kPer / kBlock;             // pool blocks per selecting thread
+static_assert(kMaxCand == 2048 * kBlock, "the largest pool's positions");
 
-// Wave 0 scans a kTkBins histogram from the top.  total = all counted keys,
-// need = min(want, total).  Writes out[0] = the bin where the count from the
-// top first reaches need, out[1] = keys in higher bins, out[2] = keys in that
-// bin (out[0..2] only if need > 0), out[3] = need, out[4] = total.  Each lane
-// owns 32 consecutive bins, read with 16-byte LDS loads.  Called by wave 0.
-__device__ __forceinline__ void crossing_2048(const uint32_t* hist, uint32_t want, uint32_t* out) {
-  constexpr int kPB = kTkBins / 64;
-  const int lane = threadIdx.x;
-  const int first = kTkBins - kPB * (lane + 1);     // lane 0 holds the highest bins
-  uint32_t c[kPB];
-#pragma unroll
-  for (int v = 0; v < kPB / 4; ++v) {
-    const v4u x = *reinterpret_cast<const v4u*>(hist + first + 4 * v);
-    c[4 * v] = x[0]; c[4 * v + 1] = x[1]; c[4 * v + 2] = x[2]; c[4 * v + 3] = x[3];
-  }
-  uint32_t local = 0;
-#pragma unroll
-  for (int k = 0; k < kPB; ++k) local += c[k];
-  const uint32_t x = wave_incl_scan_u32(local);
-  const uint32_t total = (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
-  const uint32_t need = min(want, total);
-  if (lane == 0) { out[3] = need; out[4] = total; }
-  // the lane whose run holds the crossing; its bins go one per lane (highest
-  // first) through a second wave scan
-  const uint64_t hit = __ballot(need > 0 && x - local < need && need <= x);
-  if (hit == 0) return;
-  const int L = __builtin_ctzll(hit);
-  const uint32_t above_l = (uint32_t)__builtin_amdgcn_readlane((int)(x - local), L);
-  const int top = kTkBins - 1 - kPB * L;           // the run's highest bin
-  const uint32_t v = lane < kPB ? hist[top - lane] : 0u;
-  const uint32_t above = above_l + wave_incl_scan_u32(v) - v;
-  if (lane < kPB && above < need && need <= above + v) {
-    out[0] = top - lane;
-    out[1] = above;
-    out[2] = v;
-  }
-}
-
-// One workgroup per query.  The selection is a radix select over the order
-// keys offset by the query's smallest key: the first digit is the (up to) 11
-// bits below the highest bit of (max - min), so its bins are linear in the key
-// and cover the occupied range.  The bin holding the keff-th largest key is
-// narrowed by further digits until it holds at most kRankCap keys, which are
-// then ranked exactly by (key desc, slot asc); a bin that is taken whole ends
-// the search at once, and a run of equal keys that stays above kRankCap is cut
-// at the right slot by a block scan.  The result is a threshold (T, ST): keys
-// above T, and keys equal to T at slots <= ST, are selected.  Every per-key
-// pass is a few branch-free instructions: the workgroup runs on one CU, so
-// its time is VALU issue over the 16,384 keys.
+// The Top-K of the query's pool positions from the scoring workgroups' keys.
 __device__ __forceinline__ void topk_select(const ReindexArgs& a, int q, int32_t b0, int32_t b1, int32_t b2,
                                             int32_t b3, int pcnt) {
   static_assert(kBlkPer == 4, "four pool blocks per thread");
   const int32_t blk[kBlkPer] = {b0, b1, b2, b3};
-  __shared__ __align__(16) uint32_t s_hist[kTkBins + kTkEmpty];
-  __shared__ uint64_t s_cand[kRankCap];
-  __shared__ uint32_t s_red[2 * kTkWaves];
-  __shared__ uint32_t s_misc[8];
-
-  const int tid = threadIdx.x, lane = tid & 63;
+  __shared__ uint32_t s_scan[kTkWaves];
+  const int tid = threadIdx.x;
   const int K = a.topk;
   const uint32_t* ks = a.keys + (int64_t)q * a.pool * kBlock;
   int32_t* out = a.topk_pos + (int64_t)q * K;
@@ -203,7 +145,7 @@ __device__ __forceinline__ void topk_select(const ReindexArgs& a, int q, int32_t
 
   // thread t holds slots [kPer t, kPer (t + 1)) (pool order = ascending
   // positions); blk holds the pool blocks they belong to.  The rows always
-  // hold 8P keys: slots past the pool count are cleared.  Empty slots are key 0.
+  // hold 8P keys: slots past the pool count are cleared.
   uint32_t key[kPer];
   const int s0 = tid * kPer;
   const bool mine = s0 < a.pool * kBlock;
@@ -212,126 +154,18 @@ __device__ __forceinline__ void topk_select(const ReindexArgs& a, int q, int32_t
     const v4u x = mine ? *reinterpret_cast<const v4u*>(ks + s0 + v * 4) : v4u{0u, 0u, 0u, 0u};
     key[4 * v] = x[0]; key[4 * v + 1] = x[1]; key[4 * v + 2] = x[2]; key[4 * v + 3] = x[3];
   }
-  const int N = pcnt * kBlock;
-  *reinterpret_cast<v4u*>(s_hist + 4 * tid) = v4u{0u, 0u, 0u, 0u};
-  if (tid < kTkEmpty / 4) *reinterpret_cast<v4u*>(s_hist + kTkBins + 4 * tid) = v4u{0u, 0u, 0u, 0u};
-  if (tid == 0) s_misc[5] = 0;
-
-  const int nh = N - s0;                     // slots of this thread inside the pool count
+  const int nh = pcnt * kBlock - s0;         // slots of this thread inside the pool count
   if (nh < kPer) {
 #pragma unroll
     for (int k = 0; k < kPer; ++k) key[k] = k < nh ? key[k] : 0u;
   }
-  // key range: key - 1 sends empty slots to the top for the minimum
-  uint32_t lo = 0xFFFFFFFFu, hi = 0;
-#pragma unroll
-  for (int k = 0; k < kPer; ++k) {
-    lo = min(lo, key[k] - 1u);
-    hi = max(hi, key[k]);
-  }
-  block_minmax_u32<kTkThreads>(&lo, &hi, s_red);   // its barriers also order the clears
-  const uint32_t kmin = lo + 1u, kmax = hi;
+  const TopkCut cut = radix_topk(key, K);
 
-  uint32_t keff = 0;
-  uint32_t T = 0xFFFFFFFFu;                  // threshold key (no finite score has it)
-  int ST = 0x7FFFFFFF;                       // keys == T at slots <= ST are selected
-  if (kmax != 0) {
-    const uint32_t d = kmax - kmin;
-    int shift = d ? max(0, 21 - (int)__clz(d)) : 0;    // (d >> shift) < 2^11
-#pragma unroll
-    for (int k = 0; k < kPer; ++k) {
-      const uint32_t b = (key[k] - kmin) >> shift;
-      atomicAdd(&s_hist[key[k] != 0 ? b : kTkBins + (lane & (kTkEmpty - 1))], 1u);
-    }
-    __syncthreads();
-    if (tid < 64) crossing_2048(s_hist, (uint32_t)K, s_misc);
-    __syncthreads();
-    keff = s_misc[3];
-    uint32_t need = keff - s_misc[1];         // keys still to take from the crossing bin
-    uint32_t cand = s_misc[2];
-    uint32_t blo = kmin + (s_misc[0] << shift);    // the crossing bin is [blo, blo + 2^shift)
-
-    // Rare: a crossing bin with more than kRankCap keys (clustered or equal
-    // scores).  Further digits of (key - blo) narrow it.
-    while (cand > (uint32_t)kRankCap && need < cand && shift > 0) {
-      const int sh2 = max(0, shift - 11);
-      __syncthreads();                        // the previous crossing is read
-      *reinterpret_cast<v4u*>(s_hist + 4 * tid) = v4u{0u, 0u, 0u, 0u};
-      __syncthreads();
-#pragma unroll
-      for (int k = 0; k < kPer; ++k) {
-        const uint32_t r = key[k] - blo;
-        if ((r >> shift) == 0) atomicAdd(&s_hist[r >> sh2], 1u);
-      }
-      __syncthreads();
-      if (tid < 64) crossing_2048(s_hist, need, s_misc);
-      __syncthreads();
-      blo += s_misc[0] << sh2;
-      need -= s_misc[1];
-      cand = s_misc[2];
-      shift = sh2;
-    }
-
-    if (need == cand) {
-      T = blo;                                // the crossing bin is taken whole
-    } else if (cand <= (uint32_t)kRankCap) {
-      // rank the candidates exactly: (key, ~slot) compared as one 64-bit value
-      const uint32_t bw = 1u << shift;
-#pragma unroll
-      for (int k = 0; k < kPer; ++k) {
-        if (key[k] - blo < bw) {
-          const uint32_t idx = atomicAdd(&s_misc[5], 1u);
-          s_cand[idx] = ((uint64_t)key[k] << 32) | (uint32_t)~(uint32_t)(s0 + k);
-        }
-      }
-      __syncthreads();
-      // four threads per candidate, each comparing a quarter of the others
-      const int ci_idx = tid >> 2, part = tid & 3;
-      if (ci_idx < (int)cand) {
-        const uint64_t ci = s_cand[ci_idx];
-        uint32_t r = 0;
-#pragma unroll 4
-        for (uint32_t j = part; j < cand; j += 4) r += s_cand[j] > ci;
-        r += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)r, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
-        r += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)r, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]
-        if (part == 0 && r == need - 1) { s_misc[6] = (uint32_t)(ci >> 32); s_misc[7] = ~(uint32_t)ci; }
-      }
-      __syncthreads();
-      T = s_misc[6];
-      ST = (int)s_misc[7];
-    } else {
-      // all bits fixed: more than kRankCap equal keys, taken lowest slot first
-      T = blo;
-      uint32_t eq = 0;
-#pragma unroll
-      for (int k = 0; k < kPer; ++k) eq += key[k] == T;
-      uint32_t total;
-      uint32_t before = block_exclusive_scan<kTkThreads>(eq, s_red, &total);
-      if (before < need && need <= before + eq) {
-#pragma unroll
-        for (int k = 0; k < kPer; ++k) {
-          before += key[k] == T;
-          if (key[k] == T && before == need) s_misc[7] = (uint32_t)(s0 + k);
-        }
-      }
-      __syncthreads();
-      ST = (int)s_misc[7];
-    }
-  }
-
-  // Selected: key > T, or key == T at a slot <= ST.  A thread whose slots all
-  // lie past ST compares against T + 1, the others against T; the one thread
-  // that straddles ST first clears its keys equal to T past ST.
-  const uint32_t Tt = s0 > ST ? T + 1u : T;
-  if (s0 <= ST && ST < s0 + kPer - 1) {
-#pragma unroll
-    for (int k = 0; k < kPer; ++k) key[k] = (key[k] == T && s0 + k > ST) ? 0u : key[k];
-  }
   uint32_t flags = 0;
 #pragma unroll
-  for (int k = 0; k < kPer; ++k) flags |= (uint32_t)(key[k] >= Tt) << k;
+  for (int k = 0; k < kPer; ++k) flags |= (uint32_t)(key[k] >= cut.tt) << k;
   uint32_t total;
-  uint32_t before = block_exclusive_scan<kTkThreads>(__builtin_popcount(flags), s_red, &total);
+  uint32_t before = block_exclusive_scan<kTkThreads>(__builtin_popcount(flags), s_scan, &total);
   if (!out_s) {
     // a thread holds about one selected key: visit only the set bits
     while (flags) {
@@ -355,11 +189,11 @@ __device__ __forceinline__ void topk_select(const ReindexArgs& a, int q, int32_t
       }
     }
   }
-  for (int t = (int)keff + tid; t < K; t += kTkThreads) {
+  for (int t = (int)cut.keff + tid; t < K; t += kTkThreads) {
     out[t] = -1;
     if (out_s) out_s[t] = 0.0f;
   }
-  if (tid == 0) a.topk_count[q] = (int32_t)keff;
+  if (tid == 0) a.topk_count[q] = (int32_t)cut.keff;
 }
 
 // One kernel per Reindex call.  Every workgroup scores its kReindexBlocks

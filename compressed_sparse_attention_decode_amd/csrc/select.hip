@@ -5,9 +5,12 @@
 // (block score descending, block id ascending); the pool is written in
 // ascending block order.
 //
-// Keys are order-preserving uint32 images of the block scores.  One CU streams
-// a few tens of GB/s at most, so a long context (131,056 blocks at 1M) is
-// split into chunks of 4096 blocks, each handled by its own workgroup:
+// Keys are order-preserving uint32 images of the block scores.  A batch
+// whose queries all have at most kPoolSmallBlocks (16,384) blocks is selected
+// by k_pool_small, one workgroup per query (see the end of this file).
+// Otherwise, since one CU streams a few tens of GB/s at most, a long context
+// (131,056 blocks at 1M) is split into chunks of 4096 blocks, each handled by
+// its own workgroup:
 //  K1 k_pool_minmax: per chunk, the smallest and largest key; chunk 0 also
 //     clears the query's global histogram.  (The Full scan can write these
 //     (min, max) pairs per scan tile and clear the histogram itself; then K1
@@ -30,6 +33,7 @@
 //     any input, slow only for near-constant scores).
 #include "common.h"
 #include "internal.h"
+#include "radix_topk.h"
 #include "select_common.h"
 
 namespace csa2 {
@@ -562,6 +566,54 @@ __global__ __launch_bounds__(kCT) void k_pool_mark(PoolArgs a) {
   pool_final<kCT>(a, q, w, s_dyn, ms);
 }
 
+// ---------------------------------------------------------------- small pools
+// A query with at most kPoolSmallBlocks blocks (contexts up to 131,200
+// positions) is selected by one 512-thread workgroup that holds all of its
+// block keys in registers and runs the radix Top-K of radix_topk.h: one
+// launch instead of the histogram and marking kernels.  Same result: the
+// min(P, nb) largest blocks, ties to the lower id, written in ascending order.
+static_assert(kPoolSmallBlocks == kMaxCand, "one key per register slot");
+
+__global__ __launch_bounds__(kTkThreads) void k_pool_small(PoolArgs a) {
+  __shared__ uint32_t s_scan[kTkWaves];
+  const int q = blockIdx.x, tid = threadIdx.x;
+  const int P = a.pool;
+  const float* bs = a.bscore + (int64_t)q * a.ld;
+  int32_t* out = a.pool_blocks + (int64_t)q * P;
+  // thread t holds blocks [kPer t, kPer (t + 1)); the loads are bounded by
+  // the row stride (a multiple of 4 floats) only, so they need not wait for
+  // the block count, which masks them afterwards
+  const int s0 = tid * kPer;
+  v4f x[kPer / 4];
+#pragma unroll
+  for (int v = 0; v < kPer / 4; ++v) {
+    const int j = s0 + 4 * v;
+    x[v] = j < a.ld ? *reinterpret_cast<const v4f*>(bs + j) : v4f{0.0f, 0.0f, 0.0f, 0.0f};
+  }
+  const int nb = query_blocks(a, q);
+  uint32_t key[kPer];
+#pragma unroll
+  for (int v = 0; v < kPer / 4; ++v) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) key[4 * v + e] = s0 + 4 * v + e < nb ? order_key(x[v][e]) : 0u;
+  }
+  const TopkCut cut = radix_topk(key, P);
+
+  uint32_t flags = 0;
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) flags |= (uint32_t)(key[k] >= cut.tt) << k;
+  uint32_t total;
+  uint32_t before = block_exclusive_scan<kTkThreads>(__builtin_popcount(flags), s_scan, &total);
+  while (flags) {
+    const int k = __builtin_ctz(flags);
+    flags &= flags - 1;
+    if (before < (uint32_t)P) out[before] = s0 + k;
+    ++before;
+  }
+  for (int t = (int)cut.keff + tid; t < P; t += kTkThreads) out[t] = -1;
+  if (tid == 0) a.pool_count[q] = (int32_t)cut.keff;
+}
+
 }  // namespace
 
 int64_t pool_ws_words(int chunks, int mm_cap) {
@@ -573,6 +625,10 @@ int64_t pool_ws_words(int chunks, int mm_cap) {
 size_t pool_final_lds(int nw_cap) { return ((size_t)2 * nw_cap + 2 * kCandCap) * 4; }
 
 hipError_t launch_pool_select(const PoolArgs& a, hipStream_t s) {
+  if (a.small) {
+    hipLaunchKernelGGL(k_pool_small, dim3((unsigned)a.n_q), dim3(kTkThreads), 0, s, a);
+    return hipGetLastError();
+  }
   const dim3 grid((unsigned)(a.n_q * a.chunks));
   const size_t lds = pool_final_lds(a.nw_cap);
   // dynamic LDS above the default limit must be allowed once per size

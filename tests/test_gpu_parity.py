@@ -4,6 +4,8 @@ Bars: FP4 bytes bit-exact; index sets equal except within a 1e-5 relative
 score band around the k-th score (ties to the lower index); indexer scores
 within 1e-3 relative; attention within 2e-3 of max|ref| per (query, head).
 """
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -256,8 +258,18 @@ def _set_key_rows(oq, g, rows, row):
     g.idx_k[rows] = torch.from_numpy(np.ascontiguousarray(row)).view(torch.float8_e4m3fn).cuda()
 
 
+@pytest.fixture(params=["default", "chunked"])
+def pool_path(request):
+    """The pool selection as chosen (one workgroup per query for these
+    sizes), or the chunked kernels forced."""
+    if request.param == "chunked":
+        os.environ["CSA2_POOL_SMALL"] = "0"
+    yield request.param
+    os.environ.pop("CSA2_POOL_SMALL", None)
+
+
 @pytest.mark.parametrize("pool_blocks,ctx", [(256, 20000), (2048, 40000)])
-def test_all_scores_equal(pool_blocks, ctx):
+def test_all_scores_equal(pool_blocks, ctx, pool_path):
     """Every position holds the same key, so every score ties: the pool is the
     lowest blocks and the Top-K the lowest positions.  This drives the equal-
     run paths of both selections (a pool crossing bin that overflows its
@@ -278,7 +290,7 @@ def test_all_scores_equal(pool_blocks, ctx):
     assert np.array_equal(tk.cpu().numpy()[0, :tc.item()], keep)
 
 
-def test_outlier_score_narrows_the_range():
+def test_outlier_score_narrows_the_range(pool_path):
     """One position whose key follows the sign of the weighted query gets a
     score far above the rest, and its neighbour (an all-zero key) scores 0.
     The key range then spans both, so the first histogram crowds the
@@ -307,8 +319,9 @@ def test_outlier_score_narrows_the_range():
 
 def test_pool_paths_agree(case):
     """csa2_index_full (scan-prepared pool workspace), csa2_index_scan +
-    csa2_index_pool (the pool's own key-range pass), and repeated pool calls
-    on one scan-prepared workspace give the same pool bit for bit."""
+    csa2_index_pool (the pool's own key-range pass), repeated pool calls on
+    one scan-prepared workspace, and the chunked pool kernels forced where
+    the one-workgroup selection would run give the same pool bit for bit."""
     name, g, lay = case
     w = g.w
     csa2 = g.csa2
@@ -319,6 +332,13 @@ def test_pool_paths_agree(case):
     ws = torch.empty(csa2.workspace_pool(g.dims, g.batch) + 256, dtype=torch.uint8, device="cuda")
     bs2 = csa2.index_scan(g.dims, g.batch, q, wt, g.idx_k, pool_ws=ws)
     outs = [csa2.index_pool(g.dims, g.batch, bs2, ws=ws, from_scan=True) for _ in range(3)]
+    # the chunked kernels also where the one-workgroup selection would run
+    os.environ["CSA2_POOL_SMALL"] = "0"
+    try:
+        outs.append(csa2.index_pool(g.dims, g.batch, bs2, ws=ws, from_scan=True))
+        outs.append(csa2.index_pool(g.dims, g.batch, bs))
+    finally:
+        del os.environ["CSA2_POOL_SMALL"]
     torch.cuda.synchronize()
     nb = csa2.n_blocks(g.dims, g.batch)
     for qi in range(w.n_q):     # rows are written up to each query's own block count
