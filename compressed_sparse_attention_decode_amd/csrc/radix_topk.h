@@ -156,14 +156,27 @@ __device__ __forceinline__ TopkCut radix_topk(uint32_t (&key)[kPer], int K) {
     if (need == cand) {
       T = blo;                                // the crossing bin is taken whole
     } else if (cand <= (uint32_t)kRankCap) {
-      // rank the candidates exactly: (key, ~slot) compared as one 64-bit value
+      // rank the candidates exactly: (key, ~slot) compared as one 64-bit value.
+      // Gather: each thread marks its candidates, a wave scan and one LDS
+      // atomic per wave give the offsets, then plain stores (no per-key
+      // atomic round trip).
       const uint32_t bw = 1u << shift;
+      uint32_t cm = 0;
 #pragma unroll
-      for (int k = 0; k < kPer; ++k) {
-        if (key[k] - blo < bw) {
-          const uint32_t idx = atomicAdd(&s_misc[5], 1u);
-          s_cand[idx] = ((uint64_t)key[k] << 32) | (uint32_t)~(uint32_t)(s0 + k);
-        }
+      for (int k = 0; k < kPer; ++k) cm |= (uint32_t)(key[k] - blo < bw) << k;
+      const uint32_t nc = __builtin_popcount(cm);
+      const uint32_t incl = wave_incl_scan_u32(nc);
+      uint32_t wbase = 0;
+      if (lane == 63 && incl) wbase = atomicAdd(&s_misc[5], incl);
+      uint32_t idx = (uint32_t)__builtin_amdgcn_readlane((int)wbase, 63) + incl - nc;
+      // only the slots where some lane of the wave has a candidate (a
+      // wave-uniform index, so key[k] is a uniform-indexed register read)
+      uint32_t any = wave_reduce_u32(cm, [](uint32_t x, uint32_t y) { return x | y; });
+      any = (uint32_t)__builtin_amdgcn_readfirstlane((int)any);
+      while (any) {
+        const int k = __builtin_ctz(any);
+        any &= any - 1;
+        if (cm >> k & 1u) s_cand[idx++] = ((uint64_t)key[k] << 32) | (uint32_t)~(uint32_t)(s0 + k);
       }
       __syncthreads();
       // four threads per candidate, each comparing a quarter of the others
