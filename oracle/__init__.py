@@ -1,7 +1,8 @@
 """CPU oracle for the CSA2 decode path (test infrastructure only).
 
 A plain, slow, float64 NumPy statement of what the decode path computes:
-FP4 main-KV encode/decode, the Full-mode indexer (scores, block-of-8 maxima,
+FP4 main-KV encode/decode (and the same codec at other widths for the FP4
+indexer variant), the Full-mode indexer (scores, block-of-8 maxima,
 the Top-P block pool), Reindex inside the pool, and the joint sparse + window
 attention with one softmax.  Each function cites the page passage it follows.
 
@@ -25,15 +26,18 @@ format constants (E2M1 levels, the E4M3 maximum, group and block sizes).
 """
 from .formats import (E2M1_LEVELS, bf16_to_f64, e4m3_decode, e4m3_encode_rne,
                       e2m1_encode_rne)
-from .codec import encode_kv, decode_kv, BYTES_CODES, BYTES_SCALES, GROUP
+from .codec import encode_kv, decode_kv, encode_fp4, decode_fp4, BYTES_CODES, BYTES_SCALES, GROUP
 from .indexer import (candidates, index_scores, block_scores, select_pool,
-                      pool_positions, reindex, index_full, rank_order)
+                      pool_positions, reindex, index_full, rank_order, decode_rows,
+                      take_rows, n_rows)
 from .attention import attend, gather_entries
 
 __all__ = [
     "E2M1_LEVELS", "bf16_to_f64", "e4m3_decode", "e4m3_encode_rne",
-    "e2m1_encode_rne", "encode_kv", "decode_kv", "BYTES_CODES", "BYTES_SCALES",
+    "e2m1_encode_rne", "encode_kv", "decode_kv", "encode_fp4", "decode_fp4",
+    "BYTES_CODES", "BYTES_SCALES",
     "GROUP", "candidates", "index_scores", "block_scores", "select_pool",
-    "pool_positions", "reindex", "index_full", "rank_order", "attend",
+    "pool_positions", "reindex", "index_full", "rank_order", "decode_rows",
+    "take_rows", "n_rows", "attend",
     "gather_entries",
 ]

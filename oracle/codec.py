@@ -18,6 +18,13 @@ notes):
   a group whose scale rounds to 0 stores all codes 0x0;
 * two codes per byte, the even channel in the low nibble; the 32 scale bytes
   are stored apart from the 256 code bytes.
+
+The same row codec at other widths (any multiple of 16 channels) encodes the
+indexer's keys and queries in the FP4 indexer variant: [newsaint] section 4
+states that DeepSeek-V4 already trained the indexer's query and key with FP4
+QAT, before V4.1 extended FP4 to the main KV.  Reading: those rows use this
+same E2M1 + one-E4M3-scale-per-16 format (the pages give no other FP4 layout
+for them).
 """
 from __future__ import annotations
 
@@ -31,38 +38,58 @@ BYTES_CODES = D_LATENT // 2        # 256 code bytes per entry
 BYTES_SCALES = D_LATENT // GROUP   # 32 scale bytes per entry
 
 
-def encode_kv(latent_bits: np.ndarray):
-    """Encode bf16 latent rows [n, 512] (uint16 bit patterns) to
-    (codes uint8 [n, 256], scales uint8 [n, 32])."""
-    lb = np.asarray(latent_bits).astype(np.uint16)
-    n = lb.shape[0]
-    if lb.shape != (n, D_LATENT):
-        raise ValueError("latent must be [n, 512]")
-    x = bf16_to_f64(lb).reshape(n, BYTES_SCALES, GROUP)
-    neg = ((lb >> 15) & 1).astype(np.uint8).reshape(n, BYTES_SCALES, GROUP)
-    amax = np.abs(x).max(axis=-1)                              # [n, 32]
+def encode_fp4(bits: np.ndarray):
+    """Encode bf16 rows [n, width] (uint16 bit patterns, width a multiple of
+    16) to (codes uint8 [n, width / 2], scales uint8 [n, width / 16])."""
+    lb = np.asarray(bits).astype(np.uint16)
+    if lb.ndim != 2 or lb.shape[1] % GROUP:
+        raise ValueError("rows must be [n, width], width a multiple of 16")
+    n, width = lb.shape
+    ng = width // GROUP
+    x = bf16_to_f64(lb).reshape(n, ng, GROUP)
+    neg = ((lb >> 15) & 1).astype(np.uint8).reshape(n, ng, GROUP)
+    amax = np.abs(x).max(axis=-1)                              # [n, groups]
     t = np.minimum(amax / 6.0, 448.0)
-    scale_code = e4m3_encode_rne(t)                            # [n, 32]
+    scale_code = e4m3_encode_rne(t)                            # [n, groups]
     s = e4m3_decode(scale_code)
     zero = s == 0.0
     ratio = np.abs(x) / np.where(zero, 1.0, s)[..., None]
-    mag = e2m1_encode_rne(ratio)                               # [n, 32, 16]
+    mag = e2m1_encode_rne(ratio)                               # [n, groups, 16]
     code = (neg << 3) | mag
     code = np.where(zero[..., None], 0, code).astype(np.uint8)
-    code = code.reshape(n, D_LATENT)
+    code = code.reshape(n, width)
     packed = (code[:, 0::2] | (code[:, 1::2] << 4)).astype(np.uint8)
-    return packed, scale_code
+    return packed, scale_code.astype(np.uint8)
 
 
-def decode_kv(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
-    """(codes [n, 256], scales [n, 32]) -> float64 latent [n, 512]:
+def decode_fp4(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """(codes [n, width / 2], scales [n, width / 16]) -> float64 [n, width]:
     value = (-1)^sign * E2M1 level * E4M3 scale (exact in float64)."""
     c = np.asarray(codes).astype(np.uint8)
-    n = c.shape[0]
-    nib = np.empty((n, D_LATENT), dtype=np.uint8)
+    n, half = c.shape
+    sc = np.asarray(scales)
+    if sc.shape != (n, 2 * half // GROUP):
+        raise ValueError("scales must be [n, width / 16]")
+    nib = np.empty((n, 2 * half), dtype=np.uint8)
     nib[:, 0::2] = c & 0xF
     nib[:, 1::2] = c >> 4
     sgn = np.where(nib >> 3, -1.0, 1.0)
     lev = E2M1_LEVELS[nib & 7]
-    s = np.repeat(e4m3_decode(np.asarray(scales)), GROUP, axis=1)
+    s = np.repeat(e4m3_decode(sc), GROUP, axis=1)
     return sgn * lev * s
+
+
+def encode_kv(latent_bits: np.ndarray):
+    """Encode bf16 latent rows [n, 512] (uint16 bit patterns) to
+    (codes uint8 [n, 256], scales uint8 [n, 32])."""
+    lb = np.asarray(latent_bits).astype(np.uint16)
+    if lb.ndim != 2 or lb.shape[1] != D_LATENT:
+        raise ValueError("latent must be [n, 512]")
+    return encode_fp4(lb)
+
+
+def decode_kv(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """(codes [n, 256], scales [n, 32]) -> float64 latent [n, 512]."""
+    if np.asarray(codes).shape[1:] != (BYTES_CODES,):
+        raise ValueError("codes must be [n, 256]")
+    return decode_fp4(codes, scales)

@@ -19,11 +19,17 @@ Readings where the pages are silent (also listed in the design notes):
   positions; the partial block at c takes its max over p < c only;
 * order is (score descending, position or block ascending): ties go to the
   lower index; outputs are ascending; fewer candidates than capacity -> all.
+
+FP4 indexer variant ([newsaint] section 4: DeepSeek-V4 trained the indexer's
+query and key with FP4 QAT): every function below also takes its queries and
+keys as FP4 pairs (codes [.., d / 2], scales [.., d / 16]) in the row codec of
+`codec.encode_fp4`; the scores are the same formula over the decoded values.
 """
 from __future__ import annotations
 
 import numpy as np
 
+from .codec import decode_fp4
 from .formats import e4m3_decode
 
 BLOCK = 8
@@ -34,15 +40,40 @@ def candidates(n: int, W: int) -> int:
     return max(0, int(n) - int(W))
 
 
-def index_scores(q_codes: np.ndarray, w: np.ndarray, k_codes: np.ndarray) -> np.ndarray:
+def decode_rows(x) -> np.ndarray:
+    """Indexer rows as float64: fp8 E4M3FN bytes [.., d], or an FP4 pair
+    (codes [.., d / 2], scales [.., d / 16]) decoded by the FP4 codec."""
+    if isinstance(x, tuple):
+        codes, scales = (np.asarray(v) for v in x)
+        lead = codes.shape[:-1]
+        v = decode_fp4(codes.reshape(-1, codes.shape[-1]), scales.reshape(-1, scales.shape[-1]))
+        return v.reshape(*lead, v.shape[-1])
+    return e4m3_decode(x)
+
+
+def take_rows(x, idx):
+    """Rows `idx` of an fp8 row array or of both planes of an FP4 pair."""
+    if isinstance(x, tuple):
+        return tuple(np.asarray(v)[idx] for v in x)
+    return np.asarray(x)[idx]
+
+
+def n_rows(x) -> int:
+    return len(x[0]) if isinstance(x, tuple) else len(x)
+
+
+def index_scores(q_codes, w: np.ndarray, k_codes) -> np.ndarray:
     """s_p = sum_h w_h * max(0, sum_i q[h,i] k[p,i]) in float64.
 
-    q_codes uint8 [H_i, d], w float32 [H_i], k_codes uint8 [c, d] (e4m3fn).
-    The inner sums are exact in float64: fp8 products carry at most 8
-    significant bits within [2^-18, 2^18], and d <= 128 of them fit 53 bits.
+    q_codes [H_i, d], w float32 [H_i], k_codes [c, d]: fp8 e4m3fn bytes, or
+    FP4 pairs (see `decode_rows`).  The inner sums are exact in float64.
+    fp8: products carry at most 8 significant bits and are multiples of
+    2^-18 below 2^18, so d <= 128 of them span under 53 bits.  FP4: a value
+    (E2M1 level x E4M3 scale) is a multiple of 2^-10 below 2688, so products
+    are multiples of 2^-20 below 2^23, and 128 of them span under 51 bits.
     """
-    q = e4m3_decode(q_codes)                        # [H_i, d]
-    k = e4m3_decode(k_codes)                        # [c, d]
+    q = decode_rows(q_codes)                        # [H_i, d]
+    k = decode_rows(k_codes)                        # [c, d]
     dots = k @ q.T                                   # [c, H_i]
     return np.maximum(dots, 0.0) @ np.asarray(w, dtype=np.float64)
 
@@ -79,10 +110,10 @@ def reindex(q_codes, w, k_codes_all, pool, c: int, K: int):
 
     k_codes_all: the query's key rows indexed by position (at least c rows).
     Returns (ascending positions int64, scores of all pool positions, R)."""
-    if len(k_codes_all) < c:
+    if n_rows(k_codes_all) < c:
         raise ValueError("key rows must cover every candidate position")
     R = pool_positions(pool, c)
-    s = index_scores(q_codes, w, np.asarray(k_codes_all)[R]) if len(R) else np.zeros(0)
+    s = index_scores(q_codes, w, take_rows(k_codes_all, R)) if len(R) else np.zeros(0)
     keep = np.sort(R[rank_order(s)[: min(K, len(R))]])
     return keep, s, R
 
@@ -91,8 +122,8 @@ def index_full(q_codes, w, k_codes_all, n: int, W: int, P: int):
     """Full mode: scores over every candidate, block maxima, Top-P blocks.
     Returns (pool ascending int64, block scores float64, position scores)."""
     c = candidates(n, W)
-    if len(k_codes_all) < c:
+    if n_rows(k_codes_all) < c:
         raise ValueError("key rows must cover every candidate position")
-    s = index_scores(q_codes, w, np.asarray(k_codes_all)[:c]) if c else np.zeros(0)
+    s = index_scores(q_codes, w, take_rows(k_codes_all, slice(0, c))) if c else np.zeros(0)
     b = block_scores(s)
     return select_pool(b, P), b, s
