@@ -54,13 +54,21 @@ class DeviceState:
         self.dims = csa2.Dims(n_heads=d.n_heads, idx_heads=d.idx_heads, idx_dim=d.idx_dim,
                               pool_blocks=d.pool_blocks, topk=d.topk, swa=d.swa)
         rows = max(lay.rows, 1)
-        idx_k = torch.empty(rows, d.idx_dim, dtype=torch.float8_e4m3fn, device=device)
+        if w.idx_fp4:
+            # FP4 indexer rows: (codes, scales) planes encoded on the device
+            idx_k = (torch.empty(rows, d.idx_dim // 2, dtype=torch.uint8, device=device),
+                     torch.empty(rows, d.idx_dim // 16, dtype=torch.uint8, device=device))
+        else:
+            idx_k = torch.empty(rows, d.idx_dim, dtype=torch.float8_e4m3fn, device=device)
         codes = torch.empty(rows, 256, dtype=torch.uint8, device=device)
         scales = torch.empty(rows, 32, dtype=torch.uint8, device=device)
         kv_rope = torch.empty(rows, 64, dtype=torch.bfloat16, device=device)
         for r0 in range(0, lay.rows, chunk_rows):
             n = min(chunk_rows, lay.rows - r0)
-            idx_k[r0:r0 + n] = wl.idx_keys(w, r0, n, device)
+            if w.idx_fp4:
+                csa2.encode_fp4(wl.idx_keys_bf16(w, r0, n, device), idx_k[0][r0:r0 + n], idx_k[1][r0:r0 + n])
+            else:
+                idx_k[r0:r0 + n] = wl.idx_keys(w, r0, n, device)
             if encode:
                 csa2.encode_kv(wl.latent(w, r0, n, device), wl.rope(w, r0, n, device),
                                codes[r0:r0 + n], scales[r0:r0 + n], kv_rope[r0:r0 + n])
@@ -69,7 +77,8 @@ class DeviceState:
         swa_kv = torch.cat(parts) if parts else torch.zeros(1, 576, dtype=torch.bfloat16, device=device)
         self.planes = [(idx_k, codes, scales, kv_rope, swa_kv)]
         for _ in range(replicas - 1):
-            self.planes.append(tuple(t.clone() for t in self.planes[0]))
+            self.planes.append(tuple(tuple(x.clone() for x in t) if isinstance(t, tuple) else t.clone()
+                                     for t in self.planes[0]))
         self.idx_k, self.codes, self.scales, self.kv_rope, self.swa_kv = self.planes[0]
         self.batch = csa2.Batch(
             seq_base=torch.tensor(lay.q_seq_base, dtype=torch.int64, device=device),
@@ -84,8 +93,16 @@ class DeviceState:
     def iq(self, layer: int):
         k = ("i", layer)
         if k not in self._q:
-            n = self.w.n_q
-            self._q[k] = (wl.idx_query(self.w, layer, 0, n, self.dev), wl.idx_weight(self.w, layer, 0, n, self.dev))
+            n, d = self.w.n_q, self.w.dims
+            if self.w.idx_fp4:
+                qb = wl.idx_query_bf16(self.w, layer, 0, n, self.dev)
+                qc = torch.empty(n, d.idx_heads, d.idx_dim // 2, dtype=torch.uint8, device=self.dev)
+                qs = torch.empty(n, d.idx_heads, d.idx_dim // 16, dtype=torch.uint8, device=self.dev)
+                self.csa2.encode_fp4(qb.view(-1, d.idx_dim), qc.view(-1, d.idx_dim // 2), qs.view(-1, d.idx_dim // 16))
+                q = (qc, qs)
+            else:
+                q = wl.idx_query(self.w, layer, 0, n, self.dev)
+            self._q[k] = (q, wl.idx_weight(self.w, layer, 0, n, self.dev))
         return self._q[k]
 
     def mq(self, layer: int):
@@ -179,16 +196,23 @@ class Step:
 
 
 # ---------------------------------------------------------------- accounting
+def key_bytes(w: wl.Workload) -> int:
+    """Bytes of one indexer key: d_i fp8 bytes, or d_i / 2 FP4 code bytes
+    plus d_i / 16 scale bytes."""
+    d = w.dims.idx_dim
+    return d // 2 + d // 16 if w.idx_fp4 else d
+
+
 def scan_bytes(w: wl.Workload) -> int:
-    """Algorithmic bytes of one scan launch: d_i bytes per candidate position
-    (the key), summed over the batch's sequences (tokens of one sequence share
-    one key stream)."""
+    """Algorithmic bytes of one scan launch: one key per candidate position,
+    summed over the batch's sequences (tokens of one sequence share one key
+    stream)."""
     lay = wl.layout(w)
     g = w.tokens_per_seq
     tot = 0
     for s in range(len(lay.ctx)):
         n_max = lay.q_visible[s * g + g - 1]
-        tot += max(0, n_max - w.dims.swa) * w.dims.idx_dim
+        tot += max(0, n_max - w.dims.swa) * key_bytes(w)
     return tot
 
 
@@ -205,7 +229,7 @@ def step_bytes(w: wl.Workload) -> int:
         pool = min(d.pool_blocks, nb)
         kk = min(d.topk, 8 * pool)
         win = n - c
-        reidx = 8 * pool * d.idx_dim
+        reidx = 8 * pool * key_bytes(w)
         att = kk * 416 + win * 1152 + d.n_heads * (1152 + 2048)
         b += n_layers * (reidx + att)
     b += w.fresh_encode * 1576

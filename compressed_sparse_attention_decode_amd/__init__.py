@@ -6,9 +6,14 @@ and the current HIP stream.  There is no CPU fallback: if the library is not
 built, or the device is not gfx950, every call raises.
 
     encode_kv      FP4 main-KV encode (E2M1 + one E4M3 scale per 16 channels)
+    encode_fp4     the same codec for rows of any width (FP4 indexer rows)
     index_full     Full-mode indexer: scores, block-of-8 maxima, Top-P pool
     index_reindex  Reindex inside the pool: Top-K positions
     attend         sparse FP4 + sliding-window attention, one softmax
+
+The indexer calls take their query and key rows either as float8_e4m3fn
+tensors or, for the FP4 indexer variant, as (codes, scales) uint8 pairs
+written by encode_fp4 at width d_i.
 """
 from __future__ import annotations
 
@@ -19,7 +24,7 @@ from typing import Optional, Tuple
 
 import torch
 
-__all__ = ["Dims", "Batch", "Csa2Error", "lib", "lib_path", "encode_kv", "index_full",
+__all__ = ["Dims", "Batch", "Csa2Error", "lib", "lib_path", "encode_kv", "encode_fp4", "index_full",
            "index_scan", "index_pool", "n_blocks", "block_scores_ld", "workspace_pool",
            "index_reindex", "attend", "workspace_full", "workspace_reindex",
            "workspace_attend", "abi_version", "Call"]
@@ -62,13 +67,17 @@ def lib() -> ctypes.CDLL:
             "csa2_status_string": (ctypes.c_char_p, [I32]),
             "csa2_last_error": (ctypes.c_char_p, []),
             "csa2_encode_kv": (I32, [I64, P, P, P, P, P, P, P]),
+            "csa2_encode_fp4": (I32, [I64, I32, P, P, P, P, P]),
             "csa2_index_scan": (I32, [PD, PQ, P, P, P, P, I64, P, SZ, P]),
+            "csa2_index_scan_fp4": (I32, [PD, PQ, P, P, P, P, P, P, I64, P, SZ, P]),
             "csa2_index_pool_workspace_size": (I32, [PD, PQ, ctypes.POINTER(SZ)]),
             "csa2_index_pool": (I32, [PD, PQ, P, I64, P, P, P, SZ, I32, P]),
             "csa2_index_full_workspace_size": (I32, [PD, PQ, ctypes.POINTER(SZ)]),
             "csa2_index_full": (I32, [PD, PQ, P, P, P, P, P, P, I64, P, SZ, P]),
+            "csa2_index_full_fp4": (I32, [PD, PQ, P, P, P, P, P, P, P, P, I64, P, SZ, P]),
             "csa2_index_reindex_workspace_size": (I32, [PD, PQ, ctypes.POINTER(SZ)]),
             "csa2_index_reindex": (I32, [PD, PQ, P, P, P, P, P, P, P, P, P, SZ, P]),
+            "csa2_index_reindex_fp4": (I32, [PD, PQ, P, P, P, P, P, P, P, P, P, P, P, SZ, P]),
             "csa2_attend_workspace_size": (I32, [PD, PQ, ctypes.POINTER(SZ)]),
             "csa2_attend": (I32, [PD, PQ, P, P, ctypes.c_float, P, P, P, P, P, P, P, P, P, P, SZ, P]),
         }
@@ -230,21 +239,70 @@ def encode_kv(latent: torch.Tensor, rope: torch.Tensor, kv_codes: torch.Tensor,
     return _issue(lib().csa2_encode_kv, args, (), prepare)
 
 
-def index_full(dims: Dims, b: Batch, idx_q: torch.Tensor, idx_w: torch.Tensor, idx_k: torch.Tensor,
+def encode_fp4(src: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor,
+               dst_row: Optional[torch.Tensor] = None, prepare: bool = False):
+    """Encode bf16 rows [n, width] into FP4 planes codes uint8 [rows, width/2]
+    and scales uint8 [rows, width/16] at rows dst_row (int64 [n]) or 0..n-1."""
+    _dev(src, codes, scales, dst_row)
+    if src.dtype != torch.bfloat16 or src.dim() != 2:
+        raise TypeError("src must be bfloat16 [n, width]")
+    n, width = src.shape
+    rows = codes.shape[0]
+    if codes.dtype != torch.uint8 or scales.dtype != torch.uint8 or codes.shape != (rows, width // 2) \
+            or scales.shape != (rows, width // 16):
+        raise ValueError("codes / scales must be uint8 [rows, width/2] / [rows, width/16]")
+    if dst_row is None and n > rows:
+        raise ValueError("more rows than the planes hold")
+    if dst_row is not None and (dst_row.dtype != torch.int64 or dst_row.shape != (n,)):
+        raise ValueError("dst_row must be int64 [n]")
+    args = (n, width, src.data_ptr(), _ptr(dst_row), codes.data_ptr(), scales.data_ptr(), _stream(src.device))
+    return _issue(lib().csa2_encode_fp4, args, (), prepare)
+
+
+def _rows_dev(x) -> torch.device:
+    return x[0].device if isinstance(x, tuple) else x.device
+
+
+def _check_idx(dims: Dims, b: Batch, idx_q, idx_w, idx_k):
+    """Validates the indexer rows; returns (fp4, [q ptr(s)], [k ptr(s)]).
+    fp8: float8_e4m3fn tensors; FP4: (codes, scales) uint8 pairs."""
+    n_q, hi, d = b.n_q, dims.idx_heads, dims.idx_dim
+    if idx_w.dtype != torch.float32 or idx_w.shape != (n_q, hi):
+        raise ValueError("idx_w must be float32 [n_q, H_i]")
+    _dev(idx_w)
+    if isinstance(idx_q, tuple) != isinstance(idx_k, tuple):
+        raise TypeError("idx_q and idx_k must both be fp8 tensors or both FP4 (codes, scales) pairs")
+    if isinstance(idx_q, tuple):
+        (qc, qs), (kc, ks) = idx_q, idx_k
+        _dev(qc, qs, kc, ks)
+        if any(t.dtype != torch.uint8 for t in (qc, qs, kc, ks)):
+            raise TypeError("FP4 codes and scales must be uint8")
+        if qc.shape != (n_q, hi, d // 2) or qs.shape != (n_q, hi, d // 16):
+            raise ValueError("FP4 query must be [n_q, H_i, d_i/2] codes and [n_q, H_i, d_i/16] scales")
+        if kc.dim() != 2 or kc.shape[1] != d // 2 or ks.shape != (kc.shape[0], d // 16):
+            raise ValueError("FP4 keys must be [rows, d_i/2] codes and [rows, d_i/16] scales")
+        return True, [qc.data_ptr(), qs.data_ptr()], [kc.data_ptr(), ks.data_ptr()]
+    _dev(idx_q, idx_k)
+    if idx_q.dtype != torch.float8_e4m3fn or idx_k.dtype != torch.float8_e4m3fn:
+        raise TypeError("idx_q and idx_k must be float8_e4m3fn")
+    if idx_q.shape != (n_q, hi, d):
+        raise ValueError("idx_q / idx_w shape mismatch")
+    if idx_k.dim() != 2 or idx_k.shape[1] != d:
+        raise ValueError("idx_k must be [rows, d_i]")
+    return False, [idx_q.data_ptr()], [idx_k.data_ptr()]
+
+
+def index_full(dims: Dims, b: Batch, idx_q, idx_w: torch.Tensor, idx_k,
                pool_blocks: Optional[torch.Tensor] = None, pool_count: Optional[torch.Tensor] = None,
                block_scores: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None
                ) -> Tuple[torch.Tensor, torch.Tensor]:
-    """Full-mode indexer. idx_q fp8 [n_q, H_i, d_i], idx_w f32 [n_q, H_i],
-    idx_k fp8 [rows, d_i].  Returns (pool_blocks int32 [n_q, P], pool_count)."""
-    dev = idx_k.device
-    _dev(idx_q, idx_w, idx_k, pool_blocks, pool_count, block_scores)
+    """Full-mode indexer. idx_q fp8 [n_q, H_i, d_i] (or an FP4 pair),
+    idx_w f32 [n_q, H_i], idx_k fp8 [rows, d_i] (or an FP4 pair).  Returns
+    (pool_blocks int32 [n_q, P], pool_count)."""
+    dev = _rows_dev(idx_k)
+    _dev(pool_blocks, pool_count, block_scores)
     n_q = b.n_q
-    if idx_q.dtype != torch.float8_e4m3fn or idx_k.dtype != torch.float8_e4m3fn:
-        raise TypeError("idx_q and idx_k must be float8_e4m3fn")
-    if idx_q.shape != (n_q, dims.idx_heads, dims.idx_dim) or idx_w.shape != (n_q, dims.idx_heads):
-        raise ValueError("idx_q / idx_w shape mismatch")
-    if idx_w.dtype != torch.float32 or idx_k.shape[1] != dims.idx_dim:
-        raise ValueError("idx_w must be float32 and idx_k [rows, d_i]")
+    fp4, qp, kp = _check_idx(dims, b, idx_q, idx_w, idx_k)
     if pool_blocks is None:
         pool_blocks = torch.empty(n_q, dims.pool_blocks, dtype=torch.int32, device=dev)
     if pool_count is None:
@@ -257,9 +315,9 @@ def index_full(dims: Dims, b: Batch, idx_q: torch.Tensor, idx_w: torch.Tensor, i
     ws = _workspace(workspace_full(dims, b), dev, ws)
     wp, wn = _ws_ptr(ws)
     d, q = dims.c(), b.c()
-    _check(lib().csa2_index_full(ctypes.byref(d), ctypes.byref(q), idx_q.data_ptr(), idx_w.data_ptr(),
-                                 idx_k.data_ptr(), pool_blocks.data_ptr(), pool_count.data_ptr(),
-                                 _ptr(block_scores), ld, wp, wn, _stream(dev)))
+    fn = lib().csa2_index_full_fp4 if fp4 else lib().csa2_index_full
+    _check(fn(ctypes.byref(d), ctypes.byref(q), *qp, idx_w.data_ptr(), *kp, pool_blocks.data_ptr(),
+              pool_count.data_ptr(), _ptr(block_scores), ld, wp, wn, _stream(dev)))
     return pool_blocks, pool_count
 
 
@@ -273,37 +331,28 @@ def block_scores_ld(dims: Dims, b: Batch) -> int:
     return max(4, (n_blocks(dims, b) + 3) // 4 * 4)
 
 
-def _check_idx(dims: Dims, b: Batch, idx_q, idx_w, idx_k):
-    n_q = b.n_q
-    if idx_q.dtype != torch.float8_e4m3fn or idx_k.dtype != torch.float8_e4m3fn:
-        raise TypeError("idx_q and idx_k must be float8_e4m3fn")
-    if idx_q.shape != (n_q, dims.idx_heads, dims.idx_dim) or idx_w.shape != (n_q, dims.idx_heads):
-        raise ValueError("idx_q / idx_w shape mismatch")
-    if idx_w.dtype != torch.float32 or idx_k.dim() != 2 or idx_k.shape[1] != dims.idx_dim:
-        raise ValueError("idx_w must be float32 and idx_k [rows, d_i]")
-
-
 POOL_WS_FROM_SCAN = 1
 
 
-def index_scan(dims: Dims, b: Batch, idx_q: torch.Tensor, idx_w: torch.Tensor, idx_k: torch.Tensor,
+def index_scan(dims: Dims, b: Batch, idx_q, idx_w: torch.Tensor, idx_k,
                block_scores: Optional[torch.Tensor] = None, pool_ws: Optional[torch.Tensor] = None,
                prepare: bool = False):
     """Full-mode scan: block scores float32 [n_q, ld] (b_j for j < nb).  With
     `pool_ws` (a pool-select workspace) the scan also prepares it for an
     index_pool(..., ws=pool_ws, from_scan=True) call on these scores."""
-    dev = idx_k.device
-    _dev(idx_q, idx_w, idx_k, block_scores, pool_ws)
-    _check_idx(dims, b, idx_q, idx_w, idx_k)
+    dev = _rows_dev(idx_k)
+    _dev(block_scores, pool_ws)
+    fp4, qp, kp = _check_idx(dims, b, idx_q, idx_w, idx_k)
     if block_scores is None:
         block_scores = torch.empty(b.n_q, block_scores_ld(dims, b), dtype=torch.float32, device=dev)
     if block_scores.dtype != torch.float32 or block_scores.dim() != 2 or block_scores.shape[0] != b.n_q:
         raise ValueError("block_scores must be float32 [n_q, ld]")
     wp, wn = _ws_ptr(pool_ws)
     d, q = dims.c(), b.c()
-    args = (ctypes.byref(d), ctypes.byref(q), idx_q.data_ptr(), idx_w.data_ptr(),
-            idx_k.data_ptr(), block_scores.data_ptr(), block_scores.shape[1], wp, wn, _stream(dev))
-    call = _issue(lib().csa2_index_scan, args, (d, q, pool_ws), prepare)
+    args = (ctypes.byref(d), ctypes.byref(q), *qp, idx_w.data_ptr(), *kp, block_scores.data_ptr(),
+            block_scores.shape[1], wp, wn, _stream(dev))
+    fn = lib().csa2_index_scan_fp4 if fp4 else lib().csa2_index_scan
+    call = _issue(fn, args, (d, q, pool_ws), prepare)
     return call if prepare else block_scores
 
 
@@ -332,19 +381,16 @@ def index_pool(dims: Dims, b: Batch, block_scores: torch.Tensor,
     return call if prepare else (pool_blocks, pool_count)
 
 
-def index_reindex(dims: Dims, b: Batch, idx_q: torch.Tensor, idx_w: torch.Tensor, idx_k: torch.Tensor,
+def index_reindex(dims: Dims, b: Batch, idx_q, idx_w: torch.Tensor, idx_k,
                   pool_blocks: torch.Tensor, pool_count: torch.Tensor,
                   topk_pos: Optional[torch.Tensor] = None, topk_count: Optional[torch.Tensor] = None,
                   topk_scores: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None,
                   prepare: bool = False):
     """Reindex inside the pool. Returns (topk_pos int32 [n_q, K], topk_count)."""
-    dev = idx_k.device
-    _dev(idx_q, idx_w, idx_k, pool_blocks, pool_count, topk_pos, topk_count, topk_scores)
+    dev = _rows_dev(idx_k)
+    _dev(pool_blocks, pool_count, topk_pos, topk_count, topk_scores)
     n_q = b.n_q
-    if idx_q.dtype != torch.float8_e4m3fn or idx_k.dtype != torch.float8_e4m3fn:
-        raise TypeError("idx_q and idx_k must be float8_e4m3fn")
-    if idx_q.shape != (n_q, dims.idx_heads, dims.idx_dim) or idx_w.shape != (n_q, dims.idx_heads):
-        raise ValueError("idx_q / idx_w shape mismatch")
+    fp4, qp, kp = _check_idx(dims, b, idx_q, idx_w, idx_k)
     if pool_blocks.shape != (n_q, dims.pool_blocks) or pool_count.shape != (n_q,):
         raise ValueError("pool shape mismatch")
     if topk_pos is None:
@@ -356,10 +402,11 @@ def index_reindex(dims: Dims, b: Batch, idx_q: torch.Tensor, idx_w: torch.Tensor
     ws = _workspace(workspace_reindex(dims, b), dev, ws)
     wp, wn = _ws_ptr(ws)
     d, q = dims.c(), b.c()
-    args = (ctypes.byref(d), ctypes.byref(q), idx_q.data_ptr(), idx_w.data_ptr(),
-            idx_k.data_ptr(), pool_blocks.data_ptr(), pool_count.data_ptr(),
-            topk_pos.data_ptr(), topk_count.data_ptr(), _ptr(topk_scores), wp, wn, _stream(dev))
-    call = _issue(lib().csa2_index_reindex, args, (d, q, ws), prepare)
+    args = (ctypes.byref(d), ctypes.byref(q), *qp, idx_w.data_ptr(), *kp, pool_blocks.data_ptr(),
+            pool_count.data_ptr(), topk_pos.data_ptr(), topk_count.data_ptr(), _ptr(topk_scores), wp, wn,
+            _stream(dev))
+    fn = lib().csa2_index_reindex_fp4 if fp4 else lib().csa2_index_reindex
+    call = _issue(fn, args, (d, q, ws), prepare)
     return call if prepare else (topk_pos, topk_count)
 
 

@@ -205,6 +205,22 @@ csa2_status csa2_encode_kv(int64_t n, const uint16_t* latent, const uint16_t* ro
   return e == hipSuccess ? CSA2_OK : hip_fail(e, "encode launch");
 }
 
+csa2_status csa2_encode_fp4(int64_t n, int32_t width, const uint16_t* src, const int64_t* dst_row,
+                            uint8_t* codes, uint8_t* scales, void* stream) {
+  if (n < 0) return fail(CSA2_ERR_INVALID_ARG, "n must be >= 0 (got %lld)", (long long)n);
+  if (n > ((int64_t)1 << 36)) return fail(CSA2_ERR_INVALID_ARG, "n too large");
+  if (width != 16 && width != 32 && width != 64 && width != 128 && width != 256 && width != 512 && width != 1024)
+    return fail(CSA2_ERR_INVALID_ARG, "width must be 16 times a power of two, at most 1024 (got %d)", width);
+  if (n == 0) return CSA2_OK;
+  if (!src || !codes || !scales) return fail(CSA2_ERR_INVALID_ARG, "required pointer is NULL");
+  if ((uintptr_t)src & 15) return fail(CSA2_ERR_INVALID_ARG, "src must be 16-byte aligned");
+  if ((uintptr_t)codes & 7) return fail(CSA2_ERR_INVALID_ARG, "codes must be 8-byte aligned");
+  csa2_status st = check_device();
+  if (st) return st;
+  hipError_t e = launch_encode_rows(n, width, src, dst_row, codes, scales, (hipStream_t)stream);
+  return e == hipSuccess ? CSA2_OK : hip_fail(e, "encode launch");
+}
+
 csa2_status csa2_index_full_workspace_size(const csa2_dims* d, const csa2_queries* q, size_t* bytes) {
   csa2_status st = check_dims(d);
   if (st) return st;
@@ -214,8 +230,8 @@ csa2_status csa2_index_full_workspace_size(const csa2_dims* d, const csa2_querie
   return CSA2_OK;
 }
 
-csa2_status check_block_scores(const csa2_dims* d, const csa2_queries* q, const float* block_scores,
-                               int64_t ld_block_scores) {
+static csa2_status check_block_scores(const csa2_dims* d, const csa2_queries* q, const float* block_scores,
+                                      int64_t ld_block_scores) {
   const int64_t nb = max_blocks(d, q);
   if (ld_block_scores < nb)
     return fail(CSA2_ERR_INVALID_ARG, "ld_block_scores %lld < %lld blocks", (long long)ld_block_scores, (long long)nb);
@@ -226,11 +242,12 @@ csa2_status check_block_scores(const csa2_dims* d, const csa2_queries* q, const 
 
 // The Full scan; with pool_ws it also leaves the per-tile key ranges and a
 // cleared histogram for the pool select.
-csa2_status run_scan(const csa2_dims* d, const csa2_queries* q, const uint8_t* idx_q, const float* idx_w,
-                     const uint8_t* idx_k, float* block_scores, int64_t ld_block_scores, uint32_t* pool_ws_ptr,
-                     void* stream) {
+static csa2_status run_scan(const csa2_dims* d, const csa2_queries* q, const uint8_t* idx_q, const uint8_t* q_scales,
+                            const float* idx_w, const uint8_t* idx_k, const uint8_t* k_scales, float* block_scores,
+                            int64_t ld_block_scores, uint32_t* pool_ws_ptr, void* stream) {
   ScanArgs sa;
   sa.idx_q = idx_q; sa.idx_w = idx_w; sa.idx_k = idx_k;
+  sa.idx_q_scales = q_scales; sa.idx_k_scales = k_scales;
   sa.seq_base = q->seq_base; sa.n_visible = q->n_visible;
   sa.n_q = q->n_q; sa.hi = d->idx_heads; sa.d = d->idx_dim; sa.swa = d->swa; sa.g = q->tokens_per_seq;
   int pf = kScanPrefetch, nw = kScanWaves;
@@ -250,8 +267,8 @@ csa2_status run_scan(const csa2_dims* d, const csa2_queries* q, const uint8_t* i
   return e == hipSuccess ? CSA2_OK : hip_fail(e, "scan launch");
 }
 
-csa2_status run_pool(const csa2_dims* d, const csa2_queries* q, const float* block_scores, int64_t ld_block_scores,
-                     int32_t* pool_blocks, int32_t* pool_count, void* ws, bool after_scan, void* stream) {
+static csa2_status run_pool(const csa2_dims* d, const csa2_queries* q, const float* block_scores, int64_t ld_block_scores,
+                            int32_t* pool_blocks, int32_t* pool_count, void* ws, bool after_scan, void* stream) {
   PoolArgs pa;
   pa.bscore = block_scores; pa.ld = ld_block_scores; pa.n_visible = q->n_visible;
   pa.n_q = q->n_q; pa.swa = d->swa; pa.pool = d->pool_blocks;
@@ -269,18 +286,50 @@ csa2_status run_pool(const csa2_dims* d, const csa2_queries* q, const float* blo
   return e == hipSuccess ? CSA2_OK : hip_fail(e, "pool select launch");
 }
 
-csa2_status csa2_index_scan(const csa2_dims* d, const csa2_queries* q, const uint8_t* idx_q, const float* idx_w,
-                            const uint8_t* idx_k, float* block_scores, int64_t ld_block_scores, void* pool_wsp,
-                            size_t pool_ws_bytes, void* stream) {
+// The indexer rows of a call: fp8 (no scale planes) or FP4 (both planes).
+static csa2_status check_index_rows(const csa2_dims* d, const uint8_t* idx_q, const uint8_t* q_scales, const float* idx_w,
+                                    const uint8_t* idx_k, const uint8_t* k_scales, bool fp4) {
+  if (!idx_q || !idx_w || !idx_k) return fail(CSA2_ERR_INVALID_ARG, "required pointer is NULL");
+  if (((uintptr_t)idx_q | (uintptr_t)idx_k) & 15)
+    return fail(CSA2_ERR_INVALID_ARG, "query and key rows must be 16-byte aligned");
+  if (fp4) {
+    if (!q_scales || !k_scales) return fail(CSA2_ERR_INVALID_ARG, "FP4 scale pointer is NULL");
+    if (((uintptr_t)q_scales | (uintptr_t)k_scales) & 7)
+      return fail(CSA2_ERR_INVALID_ARG, "FP4 scale planes must be 8-byte aligned");
+    if (d->idx_dim != 128) return fail(CSA2_ERR_INVALID_ARG, "FP4 indexer rows need idx_dim 128 (got %d)", d->idx_dim);
+  }
+  return CSA2_OK;
+}
+
+static csa2_status index_scan(const csa2_dims* d, const csa2_queries* q, const uint8_t* idx_q, const uint8_t* q_scales,
+                              const float* idx_w, const uint8_t* idx_k, const uint8_t* k_scales, bool fp4,
+                              float* block_scores, int64_t ld_block_scores, void* pool_wsp, size_t pool_ws_bytes,
+                              void* stream) {
   csa2_status st = check_dims(d);
   if (st) return st;
   if ((st = check_queries(q))) return st;
-  if (!idx_q || !idx_w || !idx_k || !block_scores) return fail(CSA2_ERR_INVALID_ARG, "required pointer is NULL");
-  if (((uintptr_t)idx_q | (uintptr_t)idx_k) & 15) return fail(CSA2_ERR_INVALID_ARG, "idx_q and idx_k must be 16-byte aligned");
+  if ((st = check_index_rows(d, idx_q, q_scales, idx_w, idx_k, k_scales, fp4))) return st;
+  if (!block_scores) return fail(CSA2_ERR_INVALID_ARG, "block_scores is NULL");
   if ((st = check_block_scores(d, q, block_scores, ld_block_scores))) return st;
   if (pool_wsp && (st = check_ws(pool_wsp, pool_ws_bytes, pool_ws(d, q)))) return st;
   if ((st = check_device())) return st;
-  return run_scan(d, q, idx_q, idx_w, idx_k, block_scores, ld_block_scores, (uint32_t*)pool_wsp, stream);
+  return run_scan(d, q, idx_q, fp4 ? q_scales : nullptr, idx_w, idx_k, fp4 ? k_scales : nullptr, block_scores,
+                  ld_block_scores, (uint32_t*)pool_wsp, stream);
+}
+
+csa2_status csa2_index_scan(const csa2_dims* d, const csa2_queries* q, const uint8_t* idx_q, const float* idx_w,
+                            const uint8_t* idx_k, float* block_scores, int64_t ld_block_scores, void* pool_wsp,
+                            size_t pool_ws_bytes, void* stream) {
+  return index_scan(d, q, idx_q, nullptr, idx_w, idx_k, nullptr, false, block_scores, ld_block_scores, pool_wsp,
+                    pool_ws_bytes, stream);
+}
+
+csa2_status csa2_index_scan_fp4(const csa2_dims* d, const csa2_queries* q, const uint8_t* q_codes,
+                                const uint8_t* q_scales, const float* idx_w, const uint8_t* k_codes,
+                                const uint8_t* k_scales, float* block_scores, int64_t ld_block_scores,
+                                void* pool_wsp, size_t pool_ws_bytes, void* stream) {
+  return index_scan(d, q, q_codes, q_scales, idx_w, k_codes, k_scales, true, block_scores, ld_block_scores,
+                    pool_wsp, pool_ws_bytes, stream);
 }
 
 csa2_status csa2_index_pool_workspace_size(const csa2_dims* d, const csa2_queries* q, size_t* bytes) {
@@ -307,15 +356,15 @@ csa2_status csa2_index_pool(const csa2_dims* d, const csa2_queries* q, const flo
                   (flags & CSA2_POOL_WS_FROM_SCAN) != 0, stream);
 }
 
-csa2_status csa2_index_full(const csa2_dims* d, const csa2_queries* q, const uint8_t* idx_q, const float* idx_w,
-                            const uint8_t* idx_k, int32_t* pool_blocks, int32_t* pool_count, float* block_scores,
-                            int64_t ld_block_scores, void* ws, size_t ws_bytes, void* stream) {
+static csa2_status index_full(const csa2_dims* d, const csa2_queries* q, const uint8_t* idx_q, const uint8_t* q_scales,
+                              const float* idx_w, const uint8_t* idx_k, const uint8_t* k_scales, bool fp4,
+                              int32_t* pool_blocks, int32_t* pool_count, float* block_scores, int64_t ld_block_scores,
+                              void* ws, size_t ws_bytes, void* stream) {
   csa2_status st = check_dims(d);
   if (st) return st;
   if ((st = check_queries(q))) return st;
-  if (!idx_q || !idx_w || !idx_k || !pool_blocks || !pool_count)
-    return fail(CSA2_ERR_INVALID_ARG, "required pointer is NULL");
-  if (((uintptr_t)idx_q | (uintptr_t)idx_k) & 15) return fail(CSA2_ERR_INVALID_ARG, "idx_q and idx_k must be 16-byte aligned");
+  if ((st = check_index_rows(d, idx_q, q_scales, idx_w, idx_k, k_scales, fp4))) return st;
+  if (!pool_blocks || !pool_count) return fail(CSA2_ERR_INVALID_ARG, "required pointer is NULL");
   const size_t pw = pool_ws(d, q);
   if ((st = check_ws(ws, ws_bytes, block_scores ? pw : full_ws(d, q)))) return st;
   float* bs = block_scores;
@@ -326,8 +375,26 @@ csa2_status csa2_index_full(const csa2_dims* d, const csa2_queries* q, const uin
   }
   if ((st = check_block_scores(d, q, bs, ld))) return st;
   if ((st = check_device())) return st;
-  if ((st = run_scan(d, q, idx_q, idx_w, idx_k, bs, ld, (uint32_t*)ws, stream))) return st;
+  if ((st = run_scan(d, q, idx_q, fp4 ? q_scales : nullptr, idx_w, idx_k, fp4 ? k_scales : nullptr, bs, ld,
+                     (uint32_t*)ws, stream)))
+    return st;
   return run_pool(d, q, bs, ld, pool_blocks, pool_count, ws, true, stream);
+}
+
+csa2_status csa2_index_full(const csa2_dims* d, const csa2_queries* q, const uint8_t* idx_q, const float* idx_w,
+                            const uint8_t* idx_k, int32_t* pool_blocks, int32_t* pool_count, float* block_scores,
+                            int64_t ld_block_scores, void* ws, size_t ws_bytes, void* stream) {
+  return index_full(d, q, idx_q, nullptr, idx_w, idx_k, nullptr, false, pool_blocks, pool_count, block_scores,
+                    ld_block_scores, ws, ws_bytes, stream);
+}
+
+csa2_status csa2_index_full_fp4(const csa2_dims* d, const csa2_queries* q, const uint8_t* q_codes,
+                                const uint8_t* q_scales, const float* idx_w, const uint8_t* k_codes,
+                                const uint8_t* k_scales, int32_t* pool_blocks, int32_t* pool_count,
+                                float* block_scores, int64_t ld_block_scores, void* ws, size_t ws_bytes,
+                                void* stream) {
+  return index_full(d, q, q_codes, q_scales, idx_w, k_codes, k_scales, true, pool_blocks, pool_count, block_scores,
+                    ld_block_scores, ws, ws_bytes, stream);
 }
 
 csa2_status csa2_index_reindex_workspace_size(const csa2_dims* d, const csa2_queries* q, size_t* bytes) {
@@ -339,20 +406,22 @@ csa2_status csa2_index_reindex_workspace_size(const csa2_dims* d, const csa2_que
   return CSA2_OK;
 }
 
-csa2_status csa2_index_reindex(const csa2_dims* d, const csa2_queries* q, const uint8_t* idx_q, const float* idx_w,
-                               const uint8_t* idx_k, const int32_t* pool_blocks, const int32_t* pool_count,
-                               int32_t* topk_pos, int32_t* topk_count, float* topk_scores, void* ws,
-                               size_t ws_bytes, void* stream) {
+static csa2_status index_reindex(const csa2_dims* d, const csa2_queries* q, const uint8_t* idx_q, const uint8_t* q_scales,
+                                 const float* idx_w, const uint8_t* idx_k, const uint8_t* k_scales, bool fp4,
+                                 const int32_t* pool_blocks, const int32_t* pool_count, int32_t* topk_pos,
+                                 int32_t* topk_count, float* topk_scores, void* ws, size_t ws_bytes, void* stream) {
   csa2_status st = check_dims(d);
   if (st) return st;
   if ((st = check_queries(q))) return st;
-  if (!idx_q || !idx_w || !idx_k || !pool_blocks || !pool_count || !topk_pos || !topk_count)
+  if ((st = check_index_rows(d, idx_q, q_scales, idx_w, idx_k, k_scales, fp4))) return st;
+  if (!pool_blocks || !pool_count || !topk_pos || !topk_count)
     return fail(CSA2_ERR_INVALID_ARG, "required pointer is NULL");
-  if (((uintptr_t)idx_q | (uintptr_t)idx_k) & 15) return fail(CSA2_ERR_INVALID_ARG, "idx_q and idx_k must be 16-byte aligned");
   if ((st = check_ws(ws, ws_bytes, reindex_ws(d, q)))) return st;
   if ((st = check_device())) return st;
   ReindexArgs ra;
   ra.idx_q = idx_q; ra.idx_w = idx_w; ra.idx_k = idx_k;
+  ra.idx_q_scales = fp4 ? q_scales : nullptr;
+  ra.idx_k_scales = fp4 ? k_scales : nullptr;
   ra.seq_base = q->seq_base; ra.n_visible = q->n_visible;
   ra.pool_blocks = pool_blocks; ra.pool_count = pool_count;
   ra.n_q = q->n_q; ra.hi = d->idx_heads; ra.d = d->idx_dim; ra.swa = d->swa;
@@ -363,6 +432,23 @@ csa2_status csa2_index_reindex(const csa2_dims* d, const csa2_queries* q, const 
   ra.topk_pos = topk_pos; ra.topk_count = topk_count; ra.topk_scores = topk_scores;
   hipError_t e = launch_reindex(ra, (hipStream_t)stream);
   return e == hipSuccess ? CSA2_OK : hip_fail(e, "reindex launch");
+}
+
+csa2_status csa2_index_reindex(const csa2_dims* d, const csa2_queries* q, const uint8_t* idx_q, const float* idx_w,
+                               const uint8_t* idx_k, const int32_t* pool_blocks, const int32_t* pool_count,
+                               int32_t* topk_pos, int32_t* topk_count, float* topk_scores, void* ws,
+                               size_t ws_bytes, void* stream) {
+  return index_reindex(d, q, idx_q, nullptr, idx_w, idx_k, nullptr, false, pool_blocks, pool_count, topk_pos,
+                       topk_count, topk_scores, ws, ws_bytes, stream);
+}
+
+csa2_status csa2_index_reindex_fp4(const csa2_dims* d, const csa2_queries* q, const uint8_t* q_codes,
+                                   const uint8_t* q_scales, const float* idx_w, const uint8_t* k_codes,
+                                   const uint8_t* k_scales, const int32_t* pool_blocks, const int32_t* pool_count,
+                                   int32_t* topk_pos, int32_t* topk_count, float* topk_scores, void* ws,
+                                   size_t ws_bytes, void* stream) {
+  return index_reindex(d, q, q_codes, q_scales, idx_w, k_codes, k_scales, true, pool_blocks, pool_count, topk_pos,
+                       topk_count, topk_scores, ws, ws_bytes, stream);
 }
 
 csa2_status csa2_attend_workspace_size(const csa2_dims* d, const csa2_queries* q, size_t* bytes) {

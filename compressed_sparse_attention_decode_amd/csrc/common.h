@@ -76,6 +76,29 @@ __device__ __forceinline__ v8h fp8x8_to_v8h(uint32_t a, uint32_t b) {
   return r;
 }
 
+// Eight E2M1 codes (one dword, low nibble = lower channel) times their
+// group's E4M3 scale, given as f16 in both halves of s2: one v8h MFMA
+// operand.  Exact: the gfx950 conversion at scale 1.0 gives the E2M1 level,
+// and level x scale needs at most 6 significant bits within [2^-10, 2688].
+__device__ __forceinline__ v8h fp4x8_to_v8h(uint32_t w, v2h s2) {
+  const v2h p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * s2;
+  const v2h p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * s2;
+  const v2h p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * s2;
+  const v2h p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * s2;
+  v8h r;
+  r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
+  r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
+  return r;
+}
+
+// The two E4M3 scale bytes of a lane's 32 FP4 channels (groups 2*gq and
+// 2*gq + 1 of a 128-wide row, whose 8 scale bytes sit in two dwords): `sw`
+// is the dword holding them, `hi` selects its upper half.  Returns the two
+// scales as f16 (exact).
+__device__ __forceinline__ v2h fp4_pair_scales(uint32_t sw, bool hi) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi ? sw >> 16 : sw, 1.0f, false);
+}
+
 __device__ __forceinline__ float bf16_to_float(uint16_t b) {
   return __uint_as_float((uint32_t)b << 16);
 }

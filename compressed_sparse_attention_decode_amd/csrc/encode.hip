@@ -10,6 +10,11 @@
 // scale byte out.  A 256-thread block covers 8 entries; the bf16 reads and the
 // code writes are contiguous across the block.  HBM-bound (1,576 bytes moved
 // per entry, about 4 ALU ops per byte).
+//
+// k_encode_rows applies the same per-group codec to rows of any power-of-two
+// multiple of 16 channels with no RoPE part: the FP4 indexer rows (§4 of the
+// newsaint.id page: DeepSeek-V4 trained the indexer's query and key with FP4
+// QAT) are 128-channel rows of this format.
 #include "common.h"
 #include "internal.h"
 
@@ -26,19 +31,11 @@ __device__ __forceinline__ uint32_t e4m3_rne(float t) {
   return (u >> 20) - (120u << 3);
 }
 
-__global__ __launch_bounds__(256) void k_encode(int64_t n, const uint16_t* __restrict__ latent,
-                                                const uint16_t* __restrict__ rope,
-                                                const int64_t* __restrict__ dst_row,
-                                                uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
-                                                uint16_t* __restrict__ rope_out) {
-  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t e = gid >> 5;
-  const int g = (int)(gid & 31);
-  if (e >= n) return;
-  const int64_t row = dst_row ? dst_row[e] : e;
-
-  const v4u* src = reinterpret_cast<const v4u*>(latent + e * kLatent + g * kGroup);
-  v4u a = src[0], b = src[1];
+// One 16-channel group (32 bytes of bf16 at `src`): its 8 code bytes in
+// (lo, hi) and its scale byte as the return value.
+__device__ __forceinline__ uint32_t encode_group(const uint16_t* src, uint32_t& lo, uint32_t& hi) {
+  const v4u* s16 = reinterpret_cast<const v4u*>(src);
+  v4u a = s16[0], b = s16[1];
   uint32_t w[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 
   // group maximum of |x| on the bit patterns (finite bf16 magnitudes order as integers)
@@ -52,7 +49,8 @@ __global__ __launch_bounds__(256) void k_encode(int64_t n, const uint16_t* __res
   const uint32_t S = e4m3_rne(t);
   const float s = e4m3_to_float(S);
 
-  uint32_t lo = 0, hi = 0;
+  lo = 0;
+  hi = 0;
   if (s != 0.0f) {
     const float t025 = 0.25f * s, t075 = 0.75f * s, t125 = 1.25f * s, t175 = 1.75f * s;
     const float t250 = 2.5f * s, t350 = 3.5f * s, t500 = 5.0f * s;
@@ -69,6 +67,21 @@ __global__ __launch_bounds__(256) void k_encode(int64_t n, const uint16_t* __res
       else hi |= code << (4 * (i - 8));
     }
   }
+  return S;
+}
+
+__global__ __launch_bounds__(256) void k_encode(int64_t n, const uint16_t* __restrict__ latent,
+                                                const uint16_t* __restrict__ rope,
+                                                const int64_t* __restrict__ dst_row,
+                                                uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
+                                                uint16_t* __restrict__ rope_out) {
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t e = gid >> 5;
+  const int g = (int)(gid & 31);
+  if (e >= n) return;
+  const int64_t row = dst_row ? dst_row[e] : e;
+  uint32_t lo, hi;
+  const uint32_t S = encode_group(latent + e * kLatent + g * kGroup, lo, hi);
   v2u packed = {lo, hi};
   *reinterpret_cast<v2u*>(codes + row * kCodeBytes + g * 8) = packed;
   scales[row * kScaleBytes + g] = (uint8_t)S;
@@ -78,7 +91,34 @@ __global__ __launch_bounds__(256) void k_encode(int64_t n, const uint16_t* __res
   }
 }
 
+// Rows of 16 << lg channels: one thread per group, 1 << lg groups per row.
+__global__ __launch_bounds__(256) void k_encode_rows(int64_t n, int lg, const uint16_t* __restrict__ src,
+                                                     const int64_t* __restrict__ dst_row,
+                                                     uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t e = gid >> lg;
+  const int g = (int)(gid & ((1 << lg) - 1));
+  if (e >= n) return;
+  const int64_t row = dst_row ? dst_row[e] : e;
+  const int64_t groups = (int64_t)1 << lg;
+  uint32_t lo, hi;
+  const uint32_t S = encode_group(src + (e * groups + g) * kGroup, lo, hi);
+  *reinterpret_cast<v2u*>(codes + (row * groups + g) * 8) = v2u{lo, hi};
+  scales[row * groups + g] = (uint8_t)S;
+}
+
 }  // namespace
+
+hipError_t launch_encode_rows(int64_t n, int width, const uint16_t* src, const int64_t* dst_row,
+                              uint8_t* codes, uint8_t* scales, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  int lg = 0;
+  while ((kGroup << lg) < width) ++lg;
+  if ((kGroup << lg) != width) return hipErrorInvalidValue;
+  const int64_t blocks = ((n << lg) + 255) / 256;
+  hipLaunchKernelGGL(k_encode_rows, dim3((unsigned)blocks), dim3(256), 0, s, n, lg, src, dst_row, codes, scales);
+  return hipGetLastError();
+}
 
 hipError_t launch_encode(int64_t n, const uint16_t* latent, const uint16_t* rope,
                          const int64_t* dst_row, uint8_t* codes, uint8_t* scales,

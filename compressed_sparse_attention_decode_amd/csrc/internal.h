@@ -27,9 +27,11 @@ struct PoolArgs {
 };
 
 struct ReindexArgs {
-  const uint8_t* idx_q;
+  const uint8_t* idx_q;      // fp8 [n_q, Hi, d], or FP4 codes [n_q, Hi, d / 2]
   const float* idx_w;
-  const uint8_t* idx_k;
+  const uint8_t* idx_k;      // fp8 [rows, d], or FP4 codes [rows, d / 2]
+  const uint8_t* idx_q_scales;   // FP4 rows (nullptr: fp8): [n_q, Hi, d / 16]
+  const uint8_t* idx_k_scales;   // [rows, d / 16]
   const int64_t* seq_base;
   const int32_t* n_visible;
   const int32_t* pool_blocks;
@@ -69,6 +71,8 @@ struct AttendArgs {
 hipError_t launch_encode(int64_t n, const uint16_t* latent, const uint16_t* rope,
                          const int64_t* dst_row, uint8_t* codes, uint8_t* scales,
                          uint16_t* rope_out, hipStream_t s);
+hipError_t launch_encode_rows(int64_t n, int width, const uint16_t* src, const int64_t* dst_row,
+                              uint8_t* codes, uint8_t* scales, hipStream_t s);
 hipError_t launch_pool_select(const PoolArgs& a, hipStream_t s);
 int64_t pool_ws_words(int chunks, int mm_cap);   // workspace words per query
 hipError_t launch_reindex(const ReindexArgs& a, hipStream_t s);

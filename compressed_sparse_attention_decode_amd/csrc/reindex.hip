@@ -20,6 +20,10 @@
 //    to 11 bits below the highest bit of the key range, finds the K-th
 //    largest; the compaction runs in pool order (= ascending positions),
 //    admitting keys equal to the threshold lowest position first.
+//
+// FP4 indexer rows (d = 128): a lane's 32 channels of a key are one 16-byte
+// load of E2M1 codes and one dword holding its two E4M3 group scales; the
+// query likewise.  Codes times scale are exact in f16.
 #include "common.h"
 #include "internal.h"
 #include "radix_topk.h"
@@ -32,10 +36,13 @@ namespace {
 // positions per slot) as order keys.  Slots past the pool count are scored
 // too, from whatever block ids the row holds there (clamped to a zero key
 // row): the selection masks them by the count, so nothing here waits for it.
-template <int D, int HT, int NW>
+template <int D, int HT, int NW, bool F4>
 __device__ __forceinline__ void score_part(const ReindexArgs& a, int q, int part) {
+  static_assert(!F4 || D == 128, "FP4 rows are 128 channels wide");
   constexpr int KC = D / 32;
-  constexpr int LB = D / 4;                        // key bytes per lane per position
+  constexpr int LB = F4 ? 16 : D / 4;              // key code bytes per lane per position
+  constexpr int RB = F4 ? D / 2 : D;               // key code bytes per position
+  constexpr int SB = D / 16;                       // FP4 scale bytes per position
   constexpr int SPW = kReindexBlocks / (2 * NW);   // wave steps (2 blocks each) per wave
   static_assert(SPW * 2 * NW == kReindexBlocks, "whole wave steps");
   const int tid = threadIdx.x, lane = tid & 63;
@@ -63,15 +70,20 @@ __device__ __forceinline__ void score_part(const ReindexArgs& a, int q, int part
     pos[u] = i < i_end ? pos[u] * kBlock + (col & 7) : c;
   }
   // every key load in flight at once (a position >= c reads zeros)
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.idx_k + load_uniform(a.seq_base + q) * D, (uint32_t)c * D);
+  const int64_t sbase = load_uniform(a.seq_base + q);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.idx_k + sbase * RB, (uint32_t)c * RB);
+  const __amdgpu_buffer_rsrc_t rks = make_rsrc(F4 ? a.idx_k_scales + sbase * SB : a.idx_k, (uint32_t)c * SB);
   uint32_t kb[SPW][LB / 4];
+  uint32_t ksw[SPW];                               // FP4: the dword holding the lane's two scales
 #pragma unroll
   for (int u = 0; u < SPW; ++u) {
     if (pos[u] > c || pos[u] < 0) pos[u] = c;
-    const uint32_t off = (uint32_t)pos[u] * D + gq * LB;
+    const uint32_t off = (uint32_t)pos[u] * RB + gq * LB;
     const v4u x = buf_load16(rk, off);
     kb[u][0] = x[0]; kb[u][1] = x[1]; kb[u][2] = x[2]; kb[u][3] = x[3];
-    if constexpr (LB == 32) {
+    if constexpr (F4) {
+      ksw[u] = __builtin_amdgcn_raw_buffer_load_b32(rks, (uint32_t)pos[u] * SB + (gq >> 1) * 4, 0, 0);
+    } else if constexpr (LB == 32) {
       const v4u y = buf_load16(rk, off + 16);
       kb[u][4] = y[0]; kb[u][5] = y[1]; kb[u][6] = y[2]; kb[u][7] = y[3];
     }
@@ -80,16 +92,24 @@ __device__ __forceinline__ void score_part(const ReindexArgs& a, int q, int part
   // query fragments: loads from clamped (valid) rows, padded heads zeroed
   v8h qf[HT][KC];
   float wv[HT][4];
-  const uint8_t* qp = a.idx_q + (int64_t)q * a.hi * D;
+  const uint8_t* qp = a.idx_q + (int64_t)q * a.hi * RB;
   uint32_t qraw[HT][KC][2];
+  uint32_t qsw[HT];
 #pragma unroll
   for (int t = 0; t < HT; ++t) {
     const int hc = min(t * 16 + col, a.hi - 1);
+    if constexpr (F4) {
+      const v4u x = *reinterpret_cast<const v4u*>(qp + (int64_t)hc * RB + gq * 16);
 #pragma unroll
-    for (int kc = 0; kc < KC; ++kc) {
-      const v2u x = *reinterpret_cast<const v2u*>(qp + (int64_t)hc * D + gq * LB + kc * 8);
-      qraw[t][kc][0] = x[0];
-      qraw[t][kc][1] = x[1];
+      for (int kc = 0; kc < KC; ++kc) qraw[t][kc][0] = x[kc];
+      qsw[t] = *reinterpret_cast<const uint32_t*>(a.idx_q_scales + ((int64_t)q * a.hi + hc) * SB + (gq >> 1) * 4);
+    } else {
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) {
+        const v2u x = *reinterpret_cast<const v2u*>(qp + (int64_t)hc * D + gq * LB + kc * 8);
+        qraw[t][kc][0] = x[0];
+        qraw[t][kc][1] = x[1];
+      }
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) wv[t][i] = a.idx_w[(int64_t)q * a.hi + min(t * 16 + gq * 4 + i, a.hi - 1)];
@@ -100,8 +120,17 @@ __device__ __forceinline__ void score_part(const ReindexArgs& a, int q, int part
 #pragma unroll
   for (int t = 0; t < HT; ++t) {
     const bool live = t * 16 + col < a.hi;
+    if constexpr (F4) {
+      const v2h sc = fp4_pair_scales(qsw[t], gq & 1);
 #pragma unroll
-    for (int kc = 0; kc < KC; ++kc) qf[t][kc] = fp8x8_to_v8h(live ? qraw[t][kc][0] : 0u, live ? qraw[t][kc][1] : 0u);
+      for (int kc = 0; kc < KC; ++kc) {
+        const _Float16 s = kc < 2 ? sc[0] : sc[1];
+        qf[t][kc] = fp4x8_to_v8h(live ? qraw[t][kc][0] : 0u, v2h{s, s});
+      }
+    } else {
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) qf[t][kc] = fp8x8_to_v8h(live ? qraw[t][kc][0] : 0u, live ? qraw[t][kc][1] : 0u);
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) wv[t][i] = t * 16 + gq * 4 + i < a.hi ? wv[t][i] : 0.0f;
   }
@@ -111,8 +140,15 @@ __device__ __forceinline__ void score_part(const ReindexArgs& a, int q, int part
   for (int u = 0; u < SPW; ++u) {
     const int i = i_begin + 2 * (wave + NW * u) + (col >> 3);
     v8h kf[KC];
+    if constexpr (F4) {
+      const v2h sc = fp4_pair_scales(ksw[u], gq & 1);
+      const v2h s0 = {sc[0], sc[0]}, s1 = {sc[1], sc[1]};
 #pragma unroll
-    for (int kc = 0; kc < KC; ++kc) kf[kc] = fp8x8_to_v8h(kb[u][2 * kc], kb[u][2 * kc + 1]);
+      for (int kc = 0; kc < KC; ++kc) kf[kc] = fp4x8_to_v8h(kb[u][kc], kc < 2 ? s0 : s1);
+    } else {
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) kf[kc] = fp8x8_to_v8h(kb[u][2 * kc], kb[u][2 * kc + 1]);
+    }
     float sum = 0.0f;
 #pragma unroll
     for (int t = 0; t < HT; ++t) {
@@ -203,7 +239,7 @@ __device__ __forceinline__ void topk_select(const ReindexArgs& a, int q, int32_t
 // barrier, each workgroup's release fence publishes its stores before it
 // counts itself in, and the last one's acquire fence makes the others'
 // visible before it reads them.
-template <int D, int HT>
+template <int D, int HT, bool F4>
 __global__ __launch_bounds__(kTkThreads) void k_reindex(ReindexArgs a) {
   __shared__ uint32_t s_last;
   const int q = blockIdx.x / a.split, part = blockIdx.x % a.split;
@@ -214,7 +250,7 @@ __global__ __launch_bounds__(kTkThreads) void k_reindex(ReindexArgs a) {
   const int32_t b0 = pool[min(j0, a.pool - 1)], b1 = pool[min(j0 + 1, a.pool - 1)];
   const int32_t b2 = pool[min(j0 + 2, a.pool - 1)], b3 = pool[min(j0 + 3, a.pool - 1)];
   const int pcnt = load_uniform(a.pool_count + q);
-  score_part<D, HT, kTkWaves>(a, q, part);
+  score_part<D, HT, kTkWaves, F4>(a, q, part);
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's key stores have reached L2
   __syncthreads();
   if (threadIdx.x == 0) {
@@ -234,15 +270,15 @@ __global__ __launch_bounds__(kTkThreads) void k_reindex(ReindexArgs a) {
   topk_select(a, q, b0, b1, b2, b3, pcnt);
 }
 
-template <int D>
+template <int D, bool F4>
 hipError_t launch_d(const ReindexArgs& a, hipStream_t s) {
   const int ht = (a.hi + 15) / 16;
   const dim3 grid((unsigned)(a.n_q * a.split)), block(kTkThreads);
   switch (ht) {
-    case 1: hipLaunchKernelGGL((k_reindex<D, 1>), grid, block, 0, s, a); break;
-    case 2: hipLaunchKernelGGL((k_reindex<D, 2>), grid, block, 0, s, a); break;
-    case 3: hipLaunchKernelGGL((k_reindex<D, 3>), grid, block, 0, s, a); break;
-    default: hipLaunchKernelGGL((k_reindex<D, 4>), grid, block, 0, s, a); break;
+    case 1: hipLaunchKernelGGL((k_reindex<D, 1, F4>), grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((k_reindex<D, 2, F4>), grid, block, 0, s, a); break;
+    case 3: hipLaunchKernelGGL((k_reindex<D, 3, F4>), grid, block, 0, s, a); break;
+    default: hipLaunchKernelGGL((k_reindex<D, 4, F4>), grid, block, 0, s, a); break;
   }
   return hipGetLastError();
 }
@@ -250,7 +286,11 @@ hipError_t launch_d(const ReindexArgs& a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_reindex(const ReindexArgs& a, hipStream_t s) {
-  return a.d == 64 ? launch_d<64>(a, s) : launch_d<128>(a, s);
+  if (a.idx_k_scales) {
+    if (a.d != 128 || !a.idx_q_scales) return hipErrorInvalidValue;
+    return launch_d<128, true>(a, s);
+  }
+  return a.d == 64 ? launch_d<64, false>(a, s) : launch_d<128, false>(a, s);
 }
 
 }  // namespace csa2

@@ -24,6 +24,14 @@
 //    one lane per block writes the block score to LDS; the tile's scores
 //    leave in one coalesced store (4 bytes per 1 KiB of keys).
 // HBM-bound: 128 bytes of keys per position, 16 KFLOP per position.
+//
+// FP4 indexer rows (§4 of the newsaint.id page: DeepSeek-V4 trained the
+// indexer's query and key with FP4 QAT), d = 128 only: a key is 64 bytes of
+// E2M1 codes plus 8 E4M3 scale bytes (one per 16 channels), the query the
+// same per head.  A wave step then moves 1 KiB of codes (lane l: row l & 15,
+// channels 32 (l >> 4) .. +32) and the step's 128 scale bytes into the ring;
+// codes times scale are exact in f16 and feed the same MFMAs.  72 bytes per
+// position.
 #include "common.h"
 #include "scan_args.h"
 
@@ -53,12 +61,19 @@ __device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xC
 
 constexpr int kMaxTilePos = 4096;
 
-template <int D, int HT, int R, int NW>
+constexpr uint32_t kOob = 0xFFFFFF00u;   // a buffer offset past any row: reads zero
+
+template <int D, int HT, int R, int NW, bool F4>
 __global__ __launch_bounds__(64 * NW) void k_scan(ScanArgs a) {
+  static_assert(!F4 || D == 128, "FP4 rows are 128 channels wide");
   constexpr int NT = 64 * NW;
   constexpr int KC = D / 32;            // MFMA k-chunks of 32 dims
-  constexpr int NH = D / 64;            // 16-byte loads per lane per step
-  __shared__ __attribute__((aligned(16))) uint8_t s_ring[NW][R][NH][1024];
+  constexpr int NH = F4 ? 1 : D / 64;   // 16-byte key loads per lane per step
+  constexpr int LPS = F4 ? 2 : NH;      // load instructions per lane per step (FP4: + scales)
+  constexpr int RB = F4 ? D / 2 : D;    // key code bytes per position
+  constexpr int SB = D / 16;            // FP4 scale bytes per position
+  constexpr int SLOT = F4 ? 1024 + 256 : NH * 1024;   // LDS bytes per ring slot
+  __shared__ __attribute__((aligned(16))) uint8_t s_ring[NW][R][SLOT];
   __shared__ float s_bs[kMaxTilePos / 8];
   __shared__ __attribute__((aligned(16))) uint8_t s_q[64 * D];
   __shared__ __attribute__((aligned(16))) float s_w[64];
@@ -85,15 +100,22 @@ __global__ __launch_bounds__(64 * NW) void k_scan(ScanArgs a) {
 
   v8h qf[HT][KC];
   float wv[HT][4];
-  const uint8_t* qp = a.idx_q + (int64_t)q * a.hi * D;
+  const uint8_t* qp = a.idx_q + (int64_t)q * a.hi * RB;
 
   // buffer descriptor over this sequence's candidate keys, built from
   // wave-uniform scalars (rows >= c read as zero)
-  const uint8_t* kbase = a.idx_k + a.seq_base[q] * D;
-  const uint64_t kaddr = (uint64_t)(uintptr_t)kbase;
+  const int64_t sbase = a.seq_base[q];
+  const uint64_t kaddr = (uint64_t)(uintptr_t)(a.idx_k + sbase * RB);
   const v4u rsrc = {(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)kaddr),
                     (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(kaddr >> 32)) & 0xFFFFu,
-                    (uint32_t)__builtin_amdgcn_readfirstlane(c * D), 0x00020000u};
+                    (uint32_t)__builtin_amdgcn_readfirstlane(c * RB), 0x00020000u};
+  v4u srsrc = rsrc;                     // FP4: the candidates' scale rows
+  if constexpr (F4) {
+    const uint64_t saddr = (uint64_t)(uintptr_t)(a.idx_k_scales + sbase * SB);
+    srsrc = v4u{(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)saddr),
+                (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(saddr >> 32)) & 0xFFFFu,
+                (uint32_t)__builtin_amdgcn_readfirstlane(c * SB), 0x00020000u};
+  }
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
 
   // this wave's steps are s_k = wave + NW k, k < ns, streamed through R LDS
@@ -103,13 +125,25 @@ __global__ __launch_bounds__(64 * NW) void k_scan(ScanArgs a) {
   // waits below count them explicitly (vector-memory ops retire in order).
   const int ns = wave < nsteps ? (nsteps - wave + NW - 1) / NW : 0;
   auto issue = [&](int k) {
-    const uint32_t row = (uint32_t)(p_begin + (wave + NW * k) * 16 + col) * D;
-    const uint32_t slot = (uint32_t)(uintptr_t)(lds_void*)&s_ring[wave_u][k % R][0][0];
-#pragma unroll
-    for (int h = 0; h < NH; ++h) {
-      const uint32_t m0 = (uint32_t)__builtin_amdgcn_readfirstlane((int)(slot + h * 1024));
+    const int row0 = p_begin + (wave + NW * k) * 16;
+    const uint32_t row = (uint32_t)(row0 + col) * RB;
+    const uint32_t slot = (uint32_t)(uintptr_t)(lds_void*)&s_ring[wave_u][k % R][0];
+    if constexpr (F4) {
+      const uint32_t m0 = (uint32_t)__builtin_amdgcn_readfirstlane((int)slot);
       asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-                   :: "s"(m0), "v"(row + key_chunk<D>(gq, h)), "s"(rsrc) : "memory", "m0");
+                   :: "s"(m0), "v"(row + gq * 16), "s"(rsrc) : "memory", "m0");
+      // the step's 16 x 8 scale bytes: dword `lane` of them for lanes < 32
+      const uint32_t m1 = (uint32_t)__builtin_amdgcn_readfirstlane((int)(slot + 1024));
+      const uint32_t so = lane < 32 ? (uint32_t)row0 * SB + lane * 4 : kOob;
+      asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+                   :: "s"(m1), "v"(so), "s"(srsrc) : "memory", "m0");
+    } else {
+#pragma unroll
+      for (int h = 0; h < NH; ++h) {
+        const uint32_t m0 = (uint32_t)__builtin_amdgcn_readfirstlane((int)(slot + h * 1024));
+        asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                     :: "s"(m0), "v"(row + key_chunk<D>(gq, h)), "s"(rsrc) : "memory", "m0");
+      }
     }
   };
   // fetch: wait until step k has landed (keeping the younger steps in
@@ -118,19 +152,32 @@ __global__ __launch_bounds__(64 * NW) void k_scan(ScanArgs a) {
     if (k + R - 1 < ns) {
       wait_lgkmcnt0();                 // the slot's previous reads are done
       issue(k + R - 1);
-      wait_vmcnt<(R - 1) * NH>();      // step k has landed; R - 1 younger in flight
+      wait_vmcnt<(R - 1) * LPS>();     // step k has landed; R - 1 younger in flight
     } else {
       wait_vmcnt<0>();
     }
-    const uint8_t* slot = &s_ring[wave_u][k % R][0][0];
-    uint32_t kb[4 * NH];
+    const uint8_t* slot = &s_ring[wave_u][k % R][0];
+    if constexpr (F4) {
+      // the lane's 32 channels: four code dwords (8 channels each) and the
+      // scales of its two 16-channel groups (row col, scale bytes 2gq, 2gq + 1)
+      const v4u x = *reinterpret_cast<const v4u*>(slot + lane * 16);
+      const uint32_t sw = *reinterpret_cast<const uint32_t*>(slot + 1024 + (col * 2 + (gq >> 1)) * 4);
+      const v2h sc = fp4_pair_scales(sw, gq & 1);
+      const v2h s0 = {sc[0], sc[0]}, s1 = {sc[1], sc[1]};
+      kf[0] = fp4x8_to_v8h(x[0], s0);
+      kf[1] = fp4x8_to_v8h(x[1], s0);
+      kf[2] = fp4x8_to_v8h(x[2], s1);
+      kf[3] = fp4x8_to_v8h(x[3], s1);
+    } else {
+      uint32_t kb[4 * NH];
 #pragma unroll
-    for (int h = 0; h < NH; ++h) {
-      const v4u x = *reinterpret_cast<const v4u*>(slot + h * 1024 + lane * 16);
-      kb[4 * h + 0] = x[0]; kb[4 * h + 1] = x[1]; kb[4 * h + 2] = x[2]; kb[4 * h + 3] = x[3];
+      for (int h = 0; h < NH; ++h) {
+        const v4u x = *reinterpret_cast<const v4u*>(slot + h * 1024 + lane * 16);
+        kb[4 * h + 0] = x[0]; kb[4 * h + 1] = x[1]; kb[4 * h + 2] = x[2]; kb[4 * h + 3] = x[3];
+      }
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) kf[kc] = fp8x8_to_v8h(kb[2 * kc], kb[2 * kc + 1]);
     }
-#pragma unroll
-    for (int kc = 0; kc < KC; ++kc) kf[kc] = fp8x8_to_v8h(kb[2 * kc], kb[2 * kc + 1]);
   };
   auto contract = [&](const v8h* kf, v4f* acc) {
 #pragma unroll
@@ -168,12 +215,26 @@ __global__ __launch_bounds__(64 * NW) void k_scan(ScanArgs a) {
     const uint64_t qaddr = (uint64_t)(uintptr_t)qp;
     const v4u qrsrc = {(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)qaddr),
                        (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(qaddr >> 32)) & 0xFFFFu,
-                       (uint32_t)__builtin_amdgcn_readfirstlane(a.hi * D), 0x00020000u};
-    const int qvec = (a.hi * D + 1023) >> 10;          // 1 KiB per load instruction
+                       (uint32_t)__builtin_amdgcn_readfirstlane(a.hi * RB), 0x00020000u};
+    const int qvec = (a.hi * RB + 1023) >> 10;         // 1 KiB per load instruction
     for (int v = wave_u; v < qvec; v += NW) {
       const uint32_t m0 = (uint32_t)__builtin_amdgcn_readfirstlane((int)((uint32_t)(uintptr_t)(lds_void*)s_q + v * 1024));
       asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                    :: "s"(m0), "v"((uint32_t)(v * 1024 + lane * 16)), "s"(qrsrc) : "memory", "m0");
+    }
+    if constexpr (F4) {
+      // the query's scale rows (H_i x 8 bytes) after its codes, 256 bytes per load
+      const uint64_t saddr = (uint64_t)(uintptr_t)(a.idx_q_scales + (int64_t)q * a.hi * SB);
+      const v4u qsrsrc = {(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)saddr),
+                          (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(saddr >> 32)) & 0xFFFFu,
+                          (uint32_t)__builtin_amdgcn_readfirstlane(a.hi * SB), 0x00020000u};
+      const int svec = (a.hi * SB + 255) >> 8;
+      for (int v = wave_u; v < svec; v += NW) {
+        const uint32_t m0 = (uint32_t)__builtin_amdgcn_readfirstlane(
+            (int)((uint32_t)(uintptr_t)(lds_void*)s_q + 64 * RB + v * 256));
+        asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+                     :: "s"(m0), "v"((uint32_t)(v * 256 + lane * 4)), "s"(qsrsrc) : "memory", "m0");
+      }
     }
     if (wave_u == 0) {
       // the head weights, 4 bytes per lane (weights past H_i read as zero)
@@ -188,7 +249,7 @@ __global__ __launch_bounds__(64 * NW) void k_scan(ScanArgs a) {
   }
   const int pro = min(R - 1, ns);
   for (int k = 0; k < pro; ++k) issue(k);
-  if (pro == R - 1) wait_vmcnt<(R - 1) * NH>();   // the query loads (older) have landed
+  if (pro == R - 1) wait_vmcnt<(R - 1) * LPS>();   // the query loads (older) have landed
   else wait_vmcnt<0>();
   __syncthreads();
 
@@ -197,10 +258,23 @@ __global__ __launch_bounds__(64 * NW) void k_scan(ScanArgs a) {
   for (int t = 0; t < HT; ++t) {
     const int h = t * 16 + col;
     const bool live = h < a.hi;
+    v4u qx = {0u, 0u, 0u, 0u};
+    v2h qsc = {(_Float16)0.0f, (_Float16)0.0f};
+    if constexpr (F4) {
+      // head h's channels 32gq .. +32 (the keys' k-slot map) and their scales
+      const int hc = min(h, a.hi - 1);
+      qx = *reinterpret_cast<const v4u*>(&s_q[hc * RB + gq * 16]);
+      qsc = fp4_pair_scales(*reinterpret_cast<const uint32_t*>(&s_q[64 * RB + hc * SB + (gq >> 1) * 4]), gq & 1);
+    }
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc) {
-      const v2u x = *reinterpret_cast<const v2u*>(&s_q[min(h, a.hi - 1) * D + key_chunk<D>(gq, kc >> 1) + (kc & 1) * 8]);
-      qf[t][kc] = fp8x8_to_v8h(live ? x[0] : 0u, live ? x[1] : 0u);
+      if constexpr (F4) {
+        const _Float16 s = kc < 2 ? qsc[0] : qsc[1];
+        qf[t][kc] = fp4x8_to_v8h(live ? qx[kc] : 0u, v2h{s, s});
+      } else {
+        const v2u x = *reinterpret_cast<const v2u*>(&s_q[min(h, a.hi - 1) * D + key_chunk<D>(gq, kc >> 1) + (kc & 1) * 8]);
+        qf[t][kc] = fp8x8_to_v8h(live ? x[0] : 0u, live ? x[1] : 0u);
+      }
       // keep the converted fragments resident: without this the compiler
       // re-converts them inside the loop to save registers
       asm volatile("" : "+v"(qf[t][kc]));
@@ -259,25 +333,25 @@ __global__ __launch_bounds__(64 * NW) void k_scan(ScanArgs a) {
   }
 }
 
-template <int D, int R, int NW>
+template <int D, int R, int NW, bool F4>
 hipError_t launch_drw(const ScanArgs& a, hipStream_t s) {
   const int ht = (a.hi + 15) / 16;
   const int units = ((a.n_q / a.g) * a.tiles + 7) / 8 * 8;
   const dim3 grid((unsigned)(units * a.g)), block(64 * NW);
   switch (ht) {
-    case 1: hipLaunchKernelGGL((k_scan<D, 1, R, NW>), grid, block, 0, s, a); break;
-    case 2: hipLaunchKernelGGL((k_scan<D, 2, R, NW>), grid, block, 0, s, a); break;
-    case 3: hipLaunchKernelGGL((k_scan<D, 3, R, NW>), grid, block, 0, s, a); break;
-    default: hipLaunchKernelGGL((k_scan<D, 4, R, NW>), grid, block, 0, s, a); break;
+    case 1: hipLaunchKernelGGL((k_scan<D, 1, R, NW, F4>), grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((k_scan<D, 2, R, NW, F4>), grid, block, 0, s, a); break;
+    case 3: hipLaunchKernelGGL((k_scan<D, 3, R, NW, F4>), grid, block, 0, s, a); break;
+    default: hipLaunchKernelGGL((k_scan<D, 4, R, NW, F4>), grid, block, 0, s, a); break;
   }
   return hipGetLastError();
 }
 
-template <int D>
+template <int D, bool F4>
 hipError_t launch_d(const ScanArgs& a, hipStream_t s) {
   // LDS ring slots per wave (steps in flight + 1) and waves per workgroup
-  if (a.waves == 8) return a.prefetch == 6 ? launch_drw<D, 6, 8>(a, s) : launch_drw<D, 4, 8>(a, s);
-  return a.prefetch == 6 ? launch_drw<D, 6, 4>(a, s) : launch_drw<D, 4, 4>(a, s);
+  if (a.waves == 8) return a.prefetch == 6 ? launch_drw<D, 6, 8, F4>(a, s) : launch_drw<D, 4, 8, F4>(a, s);
+  return a.prefetch == 6 ? launch_drw<D, 6, 4, F4>(a, s) : launch_drw<D, 4, 4, F4>(a, s);
 }
 
 }  // namespace
@@ -285,7 +359,11 @@ hipError_t launch_d(const ScanArgs& a, hipStream_t s) {
 hipError_t launch_scan(const ScanArgs& a, hipStream_t s) {
   if (a.tiles == 0) return hipSuccess;
   if (a.tile_pos > kMaxTilePos || a.tile_pos % 64) return hipErrorInvalidValue;
-  return a.d == 64 ? launch_d<64>(a, s) : launch_d<128>(a, s);
+  if (a.idx_k_scales) {
+    if (a.d != 128 || !a.idx_q_scales) return hipErrorInvalidValue;
+    return launch_d<128, true>(a, s);
+  }
+  return a.d == 64 ? launch_d<64, false>(a, s) : launch_d<128, false>(a, s);
 }
 
 }  // namespace csa2

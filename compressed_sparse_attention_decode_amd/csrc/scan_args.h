@@ -9,9 +9,12 @@
 namespace csa2 {
 
 struct ScanArgs {
-  const uint8_t* idx_q;      // [n_q, Hi, d]
+  const uint8_t* idx_q;      // [n_q, Hi, d] fp8, or FP4 codes [n_q, Hi, d / 2]
   const float* idx_w;        // [n_q, Hi]
-  const uint8_t* idx_k;      // [rows, d]
+  const uint8_t* idx_k;      // [rows, d] fp8, or FP4 codes [rows, d / 2]
+  // FP4 indexer rows (nullptr: fp8 rows): one E4M3 scale per 16 channels
+  const uint8_t* idx_q_scales;   // [n_q, Hi, d / 16]
+  const uint8_t* idx_k_scales;   // [rows, d / 16]
   const int64_t* seq_base;   // [n_q]
   const int32_t* n_visible;  // [n_q]
   int n_q, hi, d, swa, g;    // g: queries per sequence

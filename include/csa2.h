@@ -28,6 +28,10 @@
  *     query reads must exist in the caller's buffers.
  *   - bf16 arrays are passed as uint16_t bit patterns; fp8 arrays as uint8_t
  *     OCP E4M3FN bytes (maximum 448, the MI355X FP8 format).
+ *   - FP4 rows (main KV, and the indexer rows of the *_fp4 calls) are two
+ *     planes: codes, two E2M1 values per byte (the even channel in the low
+ *     nibble, sign in bit 3 of each nibble), and scales, one E4M3FN byte per
+ *     16 channels; value = E2M1 level x scale.
  *   - Non-finite inputs give undefined (but memory-safe) results.
  *   - Calls on different streams may run concurrently if their workspaces
  *     and outputs do not overlap.  The library keeps no mutable state except
@@ -132,6 +136,20 @@ csa2_status csa2_encode_kv(int64_t n, const uint16_t* latent, const uint16_t* ro
                            const int64_t* dst_row, uint8_t* kv_codes, uint8_t* kv_scales,
                            uint16_t* kv_rope, void* stream);
 
+/* FP4 row encode at any width: the per-group codec of csa2_encode_kv applied
+ * to rows of `width` channels, without a RoPE part.  It writes the indexer
+ * rows of the FP4 indexer calls below ([newsaint] §4: DeepSeek-V4 trained
+ * the indexer's query and key with FP4 QAT).
+ *   width    16, 32, 64, 128, 256, 512 or 1024
+ *   src      bf16 [n, width], 16-byte aligned
+ *   dst_row  int64 [n] destination rows, or NULL for rows 0..n-1
+ *   codes    uint8 [rows, width / 2], 8-byte aligned
+ *   scales   uint8 [rows, width / 16]
+ * n == 0 is a no-op.  Errors: CSA2_ERR_INVALID_ARG for n < 0, another width,
+ * a null pointer (dst_row excepted) or a misaligned array. */
+csa2_status csa2_encode_fp4(int64_t n, int32_t width, const uint16_t* src, const int64_t* dst_row,
+                            uint8_t* codes, uint8_t* scales, void* stream);
+
 /* Full-mode indexer, stage 1 of 2: the scan ([atlas] §3.2 hierarchical
  * sparse indexer and mode table; [newsaint] §3: the Full layer scores every
  * causally visible position).  For every query:
@@ -156,6 +174,21 @@ csa2_status csa2_index_scan(const csa2_dims* dims, const csa2_queries* q,
                             const uint8_t* idx_q, const float* idx_w, const uint8_t* idx_k,
                             float* block_scores, int64_t ld_block_scores,
                             void* pool_ws, size_t pool_ws_bytes, void* stream);
+
+/* FP4 indexer variant of csa2_index_scan ([newsaint] §4: DeepSeek-V4 trained
+ * the indexer's query and key with FP4 QAT).  Same scores and outputs, with
+ * the query and key rows in the FP4 format (see the conventions above;
+ * csa2_encode_fp4 at width d_i writes them), 72 bytes per key instead of 128:
+ *   q_codes  uint8 [n_q, H_i, d_i / 2]   q_scales uint8 [n_q, H_i, d_i / 16]
+ *   k_codes  uint8 [rows, d_i / 2]       k_scales uint8 [rows, d_i / 16]
+ * Code planes 16-byte aligned, scale planes 8-byte aligned; d_i must be 128
+ * (CSA2_ERR_INVALID_ARG otherwise).  The products are exact and the sums
+ * fp32, as for fp8 rows. */
+csa2_status csa2_index_scan_fp4(const csa2_dims* dims, const csa2_queries* q,
+                                const uint8_t* q_codes, const uint8_t* q_scales, const float* idx_w,
+                                const uint8_t* k_codes, const uint8_t* k_scales,
+                                float* block_scores, int64_t ld_block_scores,
+                                void* pool_ws, size_t pool_ws_bytes, void* stream);
 
 /* csa2_index_pool flag: the workspace was passed to the csa2_index_scan call
  * that wrote these block scores, and since then it was used only by
@@ -202,6 +235,15 @@ csa2_status csa2_index_full(const csa2_dims* dims, const csa2_queries* q,
                             float* block_scores, int64_t ld_block_scores,
                             void* ws, size_t ws_bytes, void* stream);
 
+/* csa2_index_full with FP4 indexer rows (as csa2_index_scan_fp4); the same
+ * workspace size. */
+csa2_status csa2_index_full_fp4(const csa2_dims* dims, const csa2_queries* q,
+                                const uint8_t* q_codes, const uint8_t* q_scales, const float* idx_w,
+                                const uint8_t* k_codes, const uint8_t* k_scales,
+                                int32_t* pool_blocks, int32_t* pool_count,
+                                float* block_scores, int64_t ld_block_scores,
+                                void* ws, size_t ws_bytes, void* stream);
+
 /* Workspace bytes for csa2_index_reindex. */
 csa2_status csa2_index_reindex_workspace_size(const csa2_dims* dims, const csa2_queries* q,
                                               size_t* bytes);
@@ -229,6 +271,15 @@ csa2_status csa2_index_reindex(const csa2_dims* dims, const csa2_queries* q,
                                const int32_t* pool_blocks, const int32_t* pool_count,
                                int32_t* topk_pos, int32_t* topk_count, float* topk_scores,
                                void* ws, size_t ws_bytes, void* stream);
+
+/* csa2_index_reindex with FP4 indexer rows (as csa2_index_scan_fp4); the
+ * same workspace size and contract. */
+csa2_status csa2_index_reindex_fp4(const csa2_dims* dims, const csa2_queries* q,
+                                   const uint8_t* q_codes, const uint8_t* q_scales, const float* idx_w,
+                                   const uint8_t* k_codes, const uint8_t* k_scales,
+                                   const int32_t* pool_blocks, const int32_t* pool_count,
+                                   int32_t* topk_pos, int32_t* topk_count, float* topk_scores,
+                                   void* ws, size_t ws_bytes, void* stream);
 
 /* Workspace bytes for csa2_attend. */
 csa2_status csa2_attend_workspace_size(const csa2_dims* dims, const csa2_queries* q,

@@ -68,13 +68,19 @@ class OracleQuery:
         self.c = oracle.candidates(self.n, d.swa)
         seq = qi // w.tokens_per_seq
         if keys is None:
-            keys = u8(wl.idx_keys(w, self.base, max(lay.seq_rows[seq], 1)))
-        assert len(keys) >= self.c
+            rows = max(lay.seq_rows[seq], 1)
+            if w.idx_fp4:
+                keys = oracle.encode_fp4(u16(wl.idx_keys_bf16(w, self.base, rows)))
+            else:
+                keys = u8(wl.idx_keys(w, self.base, rows))
+        assert oracle.n_rows(keys) >= self.c
         self.keys = keys
 
     def iq(self, layer):
-        return (u8(wl.idx_query(self.w, layer, self.qi, 1)[0]),
-                wl.idx_weight(self.w, layer, self.qi, 1)[0].numpy())
+        wt = wl.idx_weight(self.w, layer, self.qi, 1)[0].numpy()
+        if self.w.idx_fp4:
+            return oracle.encode_fp4(u16(wl.idx_query_bf16(self.w, layer, self.qi, 1)[0])), wt
+        return u8(wl.idx_query(self.w, layer, self.qi, 1)[0]), wt
 
     def full(self, layer=0):
         q, wt = self.iq(layer)
@@ -87,7 +93,7 @@ class OracleQuery:
     def scores_at(self, layer, pos):
         q, wt = self.iq(layer)
         pos = np.asarray(pos, dtype=np.int64)
-        return oracle.index_scores(q, wt, self.keys[pos]) if len(pos) else np.zeros(0)
+        return oracle.index_scores(q, wt, oracle.take_rows(self.keys, pos)) if len(pos) else np.zeros(0)
 
     def attention(self, layer, keep, scale=1.0):
         w = self.w

@@ -5,6 +5,7 @@ reject bad arguments synchronously with the documented status before it
 touches a device.  Workspace-size queries are pure host arithmetic.
 """
 import ctypes
+import dataclasses
 import os
 import re
 
@@ -27,7 +28,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = set(declared_functions())
     for n in ("csa2_encode_kv", "csa2_index_full", "csa2_index_reindex", "csa2_attend",
-              "csa2_index_scan", "csa2_index_pool", "csa2_status_string", "csa2_abi_version"):
+              "csa2_index_scan", "csa2_index_pool", "csa2_status_string", "csa2_abi_version",
+              "csa2_encode_fp4", "csa2_index_scan_fp4", "csa2_index_full_fp4", "csa2_index_reindex_fp4"):
         assert n in names
 
 
@@ -125,3 +127,26 @@ def test_null_pointers_rejected_before_any_device_work():
     assert st == INVALID and b"flags" in L.csa2_last_error()
     st = L.csa2_encode_kv(0, None, None, None, None, None, None, None)
     assert st in (OK, INVALID)
+
+
+def test_fp4_indexer_calls_rejected_before_any_device_work():
+    L = csa2.lib()
+    q = _batch().c()
+    # FP4 indexer rows need d_i = 128 and both scale planes
+    d64 = dataclasses.replace(_dims(), idx_dim=64).c()
+    st = L.csa2_index_full_fp4(ctypes.byref(d64), ctypes.byref(q), 0x1000, 0x2000, 0x3000, 0x4000, 0x5000,
+                               0x6000, 0x7000, None, 0, 0x8000, 1 << 30, None)
+    assert st == INVALID and b"idx_dim 128" in L.csa2_last_error()
+    d = _dims().c()
+    st = L.csa2_index_reindex_fp4(ctypes.byref(d), ctypes.byref(q), 0x1000, None, 0x3000, 0x4000, 0x5000,
+                                  0x6000, 0x7000, 0x8000, 0x9000, None, 0xA000, 1 << 30, None)
+    assert st == INVALID and b"scale" in L.csa2_last_error()
+    st = L.csa2_index_scan_fp4(ctypes.byref(d), ctypes.byref(q), 0x1000, 0x2004, 0x3000, 0x4000, 0x5000,
+                               0x6000, 1 << 20, None, 0, None)
+    assert st == INVALID and b"8-byte" in L.csa2_last_error()
+    # encode: widths are 16 times a power of two up to 1024
+    for width in (0, 48, 2048):
+        assert L.csa2_encode_fp4(4, width, 0x1000, None, 0x2000, 0x3000, None) == INVALID
+    assert L.csa2_encode_fp4(-1, 128, None, None, None, None, None) == INVALID
+    assert L.csa2_encode_fp4(4, 128, None, None, 0x2000, 0x3000, None) == INVALID
+    assert L.csa2_encode_fp4(0, 128, None, None, None, None, None) in (OK, INVALID)

@@ -31,6 +31,8 @@ SAMPLES = {
     "decode_b1_ctx1m": [0],
     "cluster_b32_ctx32k-256k_full1_reindex5": [0, 19, 31],
     "specverify_b64x4_ctx16k-512k_encode64k": [0, 1, 2, 3, 254],
+    "decode_b8_ctx128k_fp4idx": [0, 7],
+    "decode_b1_ctx1m_fp4idx": [0],
 }
 
 

@@ -20,9 +20,10 @@ pytestmark = pytest.mark.gpu
 BIG = wl.Dims(n_heads=64, idx_heads=64, idx_dim=128, pool_blocks=256, topk=512)
 
 
-def small(idx, dims, ctx_list, g=1, name="small"):
+def small(idx, dims, ctx_list, g=1, name="small", fp4=False):
     ns = len(ctx_list)
-    return wl.Workload(idx, name, dims, n_seq=ns, ctx=(0, 0), tokens_per_seq=g, ctx_list=tuple(ctx_list))
+    return wl.Workload(idx, name, dims, n_seq=ns, ctx=(0, 0), tokens_per_seq=g, ctx_list=tuple(ctx_list),
+                       idx_fp4=fp4)
 
 
 # several scan tiles (2048 positions) with ragged tails, several queries
@@ -37,6 +38,15 @@ CASES = {
     "w0_h128": small(106, wl.Dims(n_heads=128, idx_heads=1, idx_dim=128, pool_blocks=32, topk=64, swa=0), [3000]),
     "max_pk": small(107, wl.Dims(n_heads=64, idx_heads=64, idx_dim=128, pool_blocks=2048, topk=2048, swa=1024),
                     [40000, 17000]),
+    # FP4 indexer rows (codes + one E4M3 scale per 16 channels, d_i = 128)
+    "fp4_ragged_b3": small(121, BIG, [20005, 9003, 4099], fp4=True),
+    "fp4_ragged_g4": small(122, BIG, [6001, 12345], g=4, fp4=True),
+    "fp4_h_odd": small(123, wl.Dims(n_heads=32, idx_heads=40, idx_dim=128, pool_blocks=100, topk=300, swa=64),
+                       [5000, 2001], fp4=True),
+    "fp4_edge_short": small(124, wl.Dims(n_heads=16, idx_heads=16, idx_dim=128, pool_blocks=4, topk=16),
+                            [0, 1, 100, 128, 129, 136, 137, 160], fp4=True),
+    "fp4_w0_h1": small(125, wl.Dims(n_heads=16, idx_heads=1, idx_dim=128, pool_blocks=32, topk=64, swa=0),
+                       [3000], fp4=True),
 }
 
 
@@ -123,6 +133,42 @@ def test_encode_exhaustive_scales_and_values():
     assert np.array_equal(u8(scales), rs)
     bad = np.argwhere(u8(codes) != rc)
     assert len(bad) == 0, f"{len(bad)} code bytes differ, first rows {bad[:5]}"
+
+
+@pytest.mark.parametrize("width,n", [(128, 4096 + 37), (16, 1000), (512, 777), (1024, 300)])
+def test_encode_fp4_rows_bit_exact(width, n):
+    """csa2_encode_fp4 against the oracle's row codec, scattered rows."""
+    csa2 = lib()
+    w = wl.workload(6)
+    src = wl.idx_keys_bf16(w, 0, n * width // 128 + 1, "cuda").view(-1)[:n * width].view(n, width).contiguous()
+    rows = 2 * n
+    perm = torch.randperm(rows, generator=torch.Generator().manual_seed(width))[:n].to("cuda")
+    codes = torch.zeros(rows, width // 2, dtype=torch.uint8, device="cuda")
+    scales = torch.zeros(rows, width // 16, dtype=torch.uint8, device="cuda")
+    csa2.encode_fp4(src, codes, scales, dst_row=perm)
+    torch.cuda.synchronize()
+    rc, rs = oracle.encode_fp4(u16(src))
+    p = perm.cpu().numpy()
+    assert np.array_equal(u8(codes)[p], rc)
+    assert np.array_equal(u8(scales)[p], rs)
+    untouched = np.setdiff1d(np.arange(rows), p)
+    assert not u8(codes)[untouched].any() and not u8(scales)[untouched].any()
+
+
+def test_encode_fp4_exhaustive_groups_width_128():
+    """Every (E4M3 scale, bf16 value) group of the main-KV exhaustive test,
+    as 128-wide rows."""
+    csa2 = lib()
+    rows = _exhaustive_groups().reshape(-1, 128)
+    n = rows.shape[0]
+    rc, rs = oracle.encode_fp4(rows)
+    t = torch.from_numpy(rows.astype(np.int16)).view(torch.bfloat16).to("cuda")
+    codes = torch.empty(n, 64, dtype=torch.uint8, device="cuda")
+    scales = torch.empty(n, 8, dtype=torch.uint8, device="cuda")
+    csa2.encode_fp4(t, codes, scales)
+    torch.cuda.synchronize()
+    assert np.array_equal(u8(scales), rs)
+    assert np.array_equal(u8(codes), rc)
 
 
 def test_full_index(case):

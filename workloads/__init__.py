@@ -36,7 +36,7 @@ __all__ = [
     "Dims", "Workload", "WORKLOADS", "workload", "Layout", "layout",
     "idx_keys", "latent", "rope", "idx_query", "idx_weight", "q_latent",
     "q_rope", "fresh_latent", "fresh_rope", "swa_rows", "mix64_reference",
-    "latent_at", "rope_at",
+    "latent_at", "rope_at", "idx_keys_bf16", "idx_query_bf16",
 ]
 
 _MASK64 = (1 << 64) - 1
@@ -152,6 +152,7 @@ class Workload:
     fresh_q_per_layer: bool = False  # True: every Reindex layer draws new Q
     fresh_encode: int = 0         # entries encoded by each step
     ctx_list: Optional[Tuple[int, ...]] = None   # explicit contexts (tests)
+    idx_fp4: bool = False         # indexer rows in FP4 (from idx_keys_bf16 / idx_query_bf16)
 
     @property
     def key(self) -> int:
@@ -174,6 +175,9 @@ WORKLOADS: List[Workload] = [
              ctx=(32768, 262144), reindex_layers=5, fresh_q_per_layer=True),
     Workload(4, "specverify_b64x4_ctx16k-512k_encode64k", _BIG, n_seq=64,
              ctx=(16384, 524288), tokens_per_seq=4, fresh_encode=65536),
+    # the FP4 indexer variant of the two decode workloads
+    Workload(5, "decode_b8_ctx128k_fp4idx", _BIG, n_seq=8, ctx=(131072, 131072), idx_fp4=True),
+    Workload(6, "decode_b1_ctx1m_fp4idx", _BIG, n_seq=1, ctx=(1048576, 1048576), idx_fp4=True),
 ]
 
 
@@ -246,6 +250,22 @@ def idx_keys(w: Workload, row0: int, nrows: int, device="cpu") -> torch.Tensor:
     d = w.dims.idx_dim
     s = _stream_seed(w.key, "idx_k")
     return _normal("e4m3", s, row0 * d, nrows * d, device).view(nrows, d)
+
+
+def idx_keys_bf16(w: Workload, row0: int, nrows: int, device="cpu") -> torch.Tensor:
+    """Indexer keys before FP4 encoding (FP4 indexer variant), bf16
+    [nrows, d_i], N(0,1)."""
+    d = w.dims.idx_dim
+    s = _stream_seed(w.key, "idx_k_bf16")
+    return _normal("bf16", s, row0 * d, nrows * d, device).view(nrows, d)
+
+
+def idx_query_bf16(w: Workload, layer: int, q0: int, nq: int, device="cpu") -> torch.Tensor:
+    """Indexer query before FP4 encoding (FP4 indexer variant), bf16
+    [nq, H_i, d_i], N(0,1)."""
+    hi, d = w.dims.idx_heads, w.dims.idx_dim
+    s = _stream_seed(w.key, f"idx_q_bf16/{layer}")
+    return _normal("bf16", s, q0 * hi * d, nq * hi * d, device).view(nq, hi, d)
 
 
 def latent(w: Workload, row0: int, nrows: int, device="cpu") -> torch.Tensor:
