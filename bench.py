@@ -52,7 +52,7 @@ class DeviceState:
         self.lay = lay = wl.layout(w)
         d = w.dims
         self.dims = csa2.Dims(n_heads=d.n_heads, idx_heads=d.idx_heads, idx_dim=d.idx_dim,
-                              pool_blocks=d.pool_blocks, topk=d.topk, swa=d.swa)
+                              pool_blocks=d.pool_blocks, topk=d.topk, swa=d.swa, kv_group=d.kv_group)
         rows = max(lay.rows, 1)
         if w.idx_fp4:
             # FP4 indexer rows: (codes, scales) planes encoded on the device
@@ -61,7 +61,7 @@ class DeviceState:
         else:
             idx_k = torch.empty(rows, d.idx_dim, dtype=torch.float8_e4m3fn, device=device)
         codes = torch.empty(rows, 256, dtype=torch.uint8, device=device)
-        scales = torch.empty(rows, 32, dtype=torch.uint8, device=device)
+        scales = torch.empty(rows, 512 // d.kv_group, dtype=torch.uint8, device=device)
         kv_rope = torch.empty(rows, 64, dtype=torch.bfloat16, device=device)
         for r0 in range(0, lay.rows, chunk_rows):
             n = min(chunk_rows, lay.rows - r0)
@@ -71,7 +71,7 @@ class DeviceState:
                 idx_k[r0:r0 + n] = wl.idx_keys(w, r0, n, device)
             if encode:
                 csa2.encode_kv(wl.latent(w, r0, n, device), wl.rope(w, r0, n, device),
-                               codes[r0:r0 + n], scales[r0:r0 + n], kv_rope[r0:r0 + n])
+                               codes[r0:r0 + n], scales[r0:r0 + n], kv_rope[r0:r0 + n], group=d.kv_group)
         parts = [wl.swa_rows(w, lay, s, device) for s in range(len(lay.ctx))]
         parts = [p for p in parts if p.shape[0]]
         swa_kv = torch.cat(parts) if parts else torch.zeros(1, 576, dtype=torch.bfloat16, device=device)
@@ -161,7 +161,7 @@ class Step:
             self.enc_lat = wl.fresh_latent(w, 0, 0, n, dev)
             self.enc_rope = wl.fresh_rope(w, 0, 0, n, dev)
             self.enc_planes = (torch.empty(n, 256, dtype=torch.uint8, device=dev),
-                               torch.empty(n, 32, dtype=torch.uint8, device=dev),
+                               torch.empty(n, 512 // w.dims.kv_group, dtype=torch.uint8, device=dev),
                                torch.empty(n, 64, dtype=torch.bfloat16, device=dev))
         torch.cuda.synchronize()
 
@@ -171,7 +171,8 @@ class Step:
             idx_k, codes, scales, kv_rope, swa_kv = st.planes[r]
             seq = []
             if w.fresh_encode:
-                seq.append(("encode", csa2.encode_kv(self.enc_lat, self.enc_rope, *self.enc_planes, prepare=True)))
+                seq.append(("encode", csa2.encode_kv(self.enc_lat, self.enc_rope, *self.enc_planes, prepare=True,
+                                                     group=w.dims.kv_group)))
             q0, w0 = st.iq(0)
             # csa2_index_full's two stages, issued separately to time each
             seq.append(("scan", csa2.index_scan(st.dims, st.batch, q0, w0, idx_k, self.bs, pool_ws=self.ws_p,
@@ -230,9 +231,10 @@ def step_bytes(w: wl.Workload) -> int:
         kk = min(d.topk, 8 * pool)
         win = n - c
         reidx = 8 * pool * key_bytes(w)
-        att = kk * 416 + win * 1152 + d.n_heads * (1152 + 2048)
+        entry = 256 + 512 // d.kv_group + 128            # FP4 codes + scales + bf16 rope
+        att = kk * entry + win * 1152 + d.n_heads * (1152 + 2048)
         b += n_layers * (reidx + att)
-    b += w.fresh_encode * 1576
+    b += w.fresh_encode * (1152 + 256 + 512 // d.kv_group + 128)
     return b
 
 
@@ -419,6 +421,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode_b8_ctx128k")
     ap.add_argument("--secondary", default="decode_b1_ctx1m", help="second workload ('' to skip)")
+    ap.add_argument("--variants", default="decode_b8_ctx128k_fp4idx,decode_b1_ctx1m_fp4idx,decode_b8_ctx128k_kvg32",
+                    help="comma-separated further workloads reported under 'variants' ('' to skip)")
     ap.add_argument("--replicas", type=int, default=0, help="cache replicas (0: enough for >= 1 GB)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle sample budget (0 to skip)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -457,25 +461,38 @@ def main():
               file=sys.stderr, flush=True)
     del st, step
     torch.cuda.empty_cache()
-    secondary = None
-    if args.secondary:
-        w2 = wl.workload(args.secondary)
+    def other(name):
+        w2 = wl.workload(name)
         st2, step2, res2 = measure(w2, args.steps, args.warmup, args.replicas)
-        secondary = {"workload": w2.name, "metric": "decode queries/s", "value": round(res2["value"], 2),
-                     "unit": "queries/s", "ms_per_step": round(res2["ms_per_step"], 5),
-                     "stages_us": res2["stages_us"], "replicas": res2["replicas"],
-                     "scan_roofline": {"bound": "hbm", "achieved": res2["scan"]["achieved_gbs"],
-                                       "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": res2["scan"]["frac"],
-                                       "bytes_per_launch": res2["scan"]["bytes_per_launch"],
-                                       "avg_us": res2["scan"]["avg_us"],
-                                       "traffic": measured_traffic(w2.name)}}
+        rec = {"workload": w2.name, "metric": "decode queries/s", "value": round(res2["value"], 2),
+               "unit": "queries/s", "ms_per_step": round(res2["ms_per_step"], 5),
+               "indexer_rows": "fp4 (E2M1 + E4M3 per 16)" if w2.idx_fp4 else "fp8 e4m3",
+               "kv_scale_group": w2.dims.kv_group,
+               "stages_us": res2["stages_us"], "replicas": res2["replicas"],
+               "scan_roofline": {"bound": "hbm", "achieved": res2["scan"]["achieved_gbs"],
+                                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": res2["scan"]["frac"],
+                                 "bytes_per_launch": res2["scan"]["bytes_per_launch"],
+                                 "avg_us": res2["scan"]["avg_us"],
+                                 "traffic": measured_traffic(w2.name)}}
         print(f"[bench] {w2.name}: {res2['value']:.1f} queries/s, scan {res2['scan']['avg_us']} us = "
               f"{res2['scan']['achieved_gbs']} GB/s", file=sys.stderr, flush=True)
+        return w2, st2, step2, rec
+
+    secondary = None
+    if args.secondary:
+        w2, st2, step2, secondary = other(args.secondary)
         if args.cpu_seconds > 0:
             # parity of the timed step's query against the oracle (one query)
             _, secondary["parity"] = cpu_baseline(w2, st2, step2, 0.0)
             print(f"[bench] {w2.name} parity {secondary['parity']}", file=sys.stderr, flush=True)
         del st2, step2
+        torch.cuda.empty_cache()
+    variants = []
+    for name in [v for v in args.variants.split(",") if v]:
+        _, st3, step3, rec = other(name)
+        variants.append(rec)
+        del st3, step3
+        torch.cuda.empty_cache()
 
     d = w.dims
     line = {
@@ -506,6 +523,7 @@ def main():
         "cpu_baseline": cpu,
         "parity": parity,
         "secondary": secondary,
+        "variants": variants,
     }
     print(json.dumps(line), flush=True)
 

@@ -40,7 +40,7 @@ class Csa2Error(RuntimeError):
 class _Dims(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
                 ("n_heads", "d_latent", "d_rope", "idx_heads", "idx_dim", "block",
-                 "pool_blocks", "topk", "swa")]
+                 "pool_blocks", "topk", "swa", "kv_group")]
 
 
 class _Queries(ctypes.Structure):
@@ -67,6 +67,7 @@ def lib() -> ctypes.CDLL:
             "csa2_status_string": (ctypes.c_char_p, [I32]),
             "csa2_last_error": (ctypes.c_char_p, []),
             "csa2_encode_kv": (I32, [I64, P, P, P, P, P, P, P]),
+            "csa2_encode_kv_grouped": (I32, [I64, I32, P, P, P, P, P, P, P]),
             "csa2_encode_fp4": (I32, [I64, I32, P, P, P, P, P]),
             "csa2_index_scan": (I32, [PD, PQ, P, P, P, P, I64, P, SZ, P]),
             "csa2_index_scan_fp4": (I32, [PD, PQ, P, P, P, P, P, P, I64, P, SZ, P]),
@@ -130,10 +131,11 @@ class Dims:
     d_latent: int = 512
     d_rope: int = 64
     block: int = 8
+    kv_group: int = 16        # channels per main-KV FP4 scale (16, or 32 for the group-32 codec)
 
     def c(self) -> _Dims:
         return _Dims(self.n_heads, self.d_latent, self.d_rope, self.idx_heads, self.idx_dim,
-                     self.block, self.pool_blocks, self.topk, self.swa)
+                     self.block, self.pool_blocks, self.topk, self.swa, self.kv_group)
 
 
 @dataclasses.dataclass
@@ -217,10 +219,10 @@ def _ws_ptr(ws: Optional[torch.Tensor]):
 
 def encode_kv(latent: torch.Tensor, rope: torch.Tensor, kv_codes: torch.Tensor,
               kv_scales: torch.Tensor, kv_rope: torch.Tensor,
-              dst_row: Optional[torch.Tensor] = None, prepare: bool = False):
+              dst_row: Optional[torch.Tensor] = None, prepare: bool = False, group: int = 16):
     """Encode bf16 latent [n, 512] (+ rope [n, 64]) into the FP4 cache planes
-    kv_codes uint8 [rows, 256], kv_scales uint8 [rows, 32], kv_rope bf16
-    [rows, 64] at rows dst_row (int64 [n]) or 0..n-1."""
+    kv_codes uint8 [rows, 256], kv_scales uint8 [rows, 512/group], kv_rope
+    bf16 [rows, 64] at rows dst_row (int64 [n]) or 0..n-1."""
     _dev(latent, rope, kv_codes, kv_scales, kv_rope, dst_row)
     if latent.dtype != torch.bfloat16 or rope.dtype != torch.bfloat16 or kv_rope.dtype != torch.bfloat16:
         raise TypeError("latent, rope and kv_rope must be bfloat16")
@@ -228,15 +230,17 @@ def encode_kv(latent: torch.Tensor, rope: torch.Tensor, kv_codes: torch.Tensor,
     if latent.shape != (n, 512) or rope.shape != (n, 64):
         raise ValueError("latent must be [n, 512] and rope [n, 64]")
     rows = kv_codes.shape[0]
-    if kv_codes.shape != (rows, 256) or kv_scales.shape != (rows, 32) or kv_rope.shape != (rows, 64):
-        raise ValueError("cache planes must be [rows, 256] / [rows, 32] / [rows, 64]")
+    if group not in (16, 32):
+        raise ValueError("group must be 16 or 32")
+    if kv_codes.shape != (rows, 256) or kv_scales.shape != (rows, 512 // group) or kv_rope.shape != (rows, 64):
+        raise ValueError("cache planes must be [rows, 256] / [rows, 512/group] / [rows, 64]")
     if dst_row is None and n > rows:
         raise ValueError("more entries than cache rows")
     if dst_row is not None and (dst_row.dtype != torch.int64 or dst_row.shape != (n,)):
         raise ValueError("dst_row must be int64 [n]")
-    args = (n, latent.data_ptr(), rope.data_ptr(), _ptr(dst_row), kv_codes.data_ptr(),
+    args = (n, group, latent.data_ptr(), rope.data_ptr(), _ptr(dst_row), kv_codes.data_ptr(),
             kv_scales.data_ptr(), kv_rope.data_ptr(), _stream(latent.device))
-    return _issue(lib().csa2_encode_kv, args, (), prepare)
+    return _issue(lib().csa2_encode_kv_grouped, args, (), prepare)
 
 
 def encode_fp4(src: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor,

@@ -62,6 +62,8 @@ csa2_status check_dims(const csa2_dims* d) {
   if (d->topk < 1 || d->topk > 2048 || d->topk > 8 * d->pool_blocks)
     return fail(CSA2_ERR_INVALID_ARG, "topk must be in [1, min(2048, 8*pool_blocks)] (got %d)", d->topk);
   if (d->swa < 0 || d->swa > 1024) return fail(CSA2_ERR_INVALID_ARG, "swa must be in [0, 1024] (got %d)", d->swa);
+  if (d->kv_group != 0 && d->kv_group != 16 && d->kv_group != 32)
+    return fail(CSA2_ERR_INVALID_ARG, "kv_group must be 0, 16 or 32 (got %d)", d->kv_group);
   return CSA2_OK;
 }
 
@@ -191,6 +193,13 @@ const char* csa2_last_error(void) { return g_err; }
 
 csa2_status csa2_encode_kv(int64_t n, const uint16_t* latent, const uint16_t* rope, const int64_t* dst_row,
                            uint8_t* kv_codes, uint8_t* kv_scales, uint16_t* kv_rope, void* stream) {
+  return csa2_encode_kv_grouped(n, 16, latent, rope, dst_row, kv_codes, kv_scales, kv_rope, stream);
+}
+
+csa2_status csa2_encode_kv_grouped(int64_t n, int32_t group, const uint16_t* latent, const uint16_t* rope,
+                                   const int64_t* dst_row, uint8_t* kv_codes, uint8_t* kv_scales,
+                                   uint16_t* kv_rope, void* stream) {
+  if (group != 16 && group != 32) return fail(CSA2_ERR_INVALID_ARG, "group must be 16 or 32 (got %d)", group);
   if (n < 0) return fail(CSA2_ERR_INVALID_ARG, "n must be >= 0 (got %lld)", (long long)n);
   if (n > ((int64_t)1 << 36)) return fail(CSA2_ERR_INVALID_ARG, "n too large");
   if (n == 0) return CSA2_OK;
@@ -201,7 +210,8 @@ csa2_status csa2_encode_kv(int64_t n, const uint16_t* latent, const uint16_t* ro
   if ((uintptr_t)kv_codes & 7) return fail(CSA2_ERR_INVALID_ARG, "kv_codes must be 8-byte aligned");
   csa2_status st = check_device();
   if (st) return st;
-  hipError_t e = launch_encode(n, latent, rope, dst_row, kv_codes, kv_scales, kv_rope, (hipStream_t)stream);
+  if (group == 32 && ((uintptr_t)kv_codes & 15)) return fail(CSA2_ERR_INVALID_ARG, "kv_codes must be 16-byte aligned");
+  hipError_t e = launch_encode(n, group, latent, rope, dst_row, kv_codes, kv_scales, kv_rope, (hipStream_t)stream);
   return e == hipSuccess ? CSA2_OK : hip_fail(e, "encode launch");
 }
 
@@ -253,7 +263,7 @@ static csa2_status run_scan(const csa2_dims* d, const csa2_queries* q, const uin
   int pf = kScanPrefetch, nw = kScanWaves;
   if (const char* env = getenv("CSA2_SCAN_PREFETCH")) pf = atoi(env);
   if (const char* env = getenv("CSA2_SCAN_WAVES")) nw = atoi(env);
-  if (pf != 4 && pf != 6) pf = kScanPrefetch;
+  if (pf != 4 && pf != 6 && pf != 8) pf = kScanPrefetch;
   if (nw != 4 && nw != 8) nw = kScanWaves;
   sa.tile_pos = scan_tile();
   sa.prefetch = pf;
@@ -482,6 +492,7 @@ csa2_status csa2_attend(const csa2_dims* d, const csa2_queries* q, const uint16_
   AttendArgs aa;
   aa.q_lat = q_lat; aa.q_rope = q_rope; aa.scale_log2 = softmax_scale * 1.4426950408889634f;
   aa.kv_codes = kv_codes; aa.kv_scales = kv_scales; aa.kv_rope = kv_rope;
+  aa.kv_gshift = d->kv_group == 32 ? 1 : 0;
   aa.topk_pos = topk_pos; aa.topk_count = topk_count; aa.swa_kv = swa_kv; aa.swa_base = swa_base;
   aa.seq_base = q->seq_base; aa.n_visible = q->n_visible;
   aa.n_q = q->n_q; aa.heads = d->n_heads; aa.topk = d->topk; aa.swa = d->swa;

@@ -7,6 +7,9 @@
 // newsaint.id page (FP4 main KV dequantised just before attention).  The key
 // of a sparse entry is [dequantised latent (512) || bf16 rope (64)] and its
 // value is the dequantised latent; a window row supplies both from bf16.
+// The FP4 scales cover 16 channels, or 32 in the group-32 codec variant (the
+// akhunji.com page, "Microscopic FP4 (E2M1) Cache Compression"): a gathered
+// 16-channel item then reads the scale byte of its 32-channel group.
 //
 // Mapping (gfx950): a workgroup = 4 waves = one query x up to 64 heads (one
 // wave per 16 heads; waves past the last head only help gather) x one split
@@ -82,12 +85,16 @@ struct RawTile {
 constexpr uint32_t kOob = 0xFFFFFF00u;
 struct TileSrc {
   __amdgpu_buffer_rsrc_t codes, scales, rope, win;
+  uint32_t sbytes;           // scale bytes per entry (32, or 16 with 32-channel groups)
+  int gshift;                // 16-channel item -> its scale byte: item >> gshift
 };
 
 __device__ __forceinline__ TileSrc tile_src(const AttendArgs& a, int64_t seq_base, int64_t swa_base, int n, int w) {
   TileSrc s;
   s.codes = make_rsrc(a.kv_codes + seq_base * kCodeBytes, (uint32_t)n * kCodeBytes);
-  s.scales = make_rsrc(a.kv_scales + seq_base * kScaleBytes, (uint32_t)n * kScaleBytes);
+  s.gshift = a.kv_gshift;
+  s.sbytes = (uint32_t)kScaleBytes >> a.kv_gshift;
+  s.scales = make_rsrc(a.kv_scales + seq_base * s.sbytes, (uint32_t)n * s.sbytes);
   s.rope = make_rsrc(a.kv_rope + seq_base * kRope, (uint32_t)n * kRope * 2);
   s.win = make_rsrc(a.swa_kv + swa_base * kKeyDim, (uint32_t)w * kKeyDim * 2);
   return s;
@@ -128,7 +135,8 @@ __device__ __forceinline__ void load_tile(const TileSrc& src, const int32_t* row
     const int32_t r = tr.it[k];
     const bool sp = r >= 0 && r != kNoRow;
     const v2u cw = __builtin_amdgcn_raw_buffer_load_b64(src.codes, sp ? (uint32_t)r * kCodeBytes + grp * 8 : kOob, 0, 0);
-    const uint32_t sw = __builtin_amdgcn_raw_buffer_load_b32(src.scales, sp ? ((uint32_t)r * kScaleBytes + grp) & ~3u : kOob, 0, 0);
+    const uint32_t sw = __builtin_amdgcn_raw_buffer_load_b32(
+        src.scales, sp ? ((uint32_t)r * src.sbytes + (grp >> src.gshift)) & ~3u : kOob, 0, 0);
     t.c[k] = v4u{cw[0], cw[1], sw, 0u};
   }
 #pragma unroll
@@ -172,7 +180,7 @@ __device__ __forceinline__ void store_tile(const TileSrc& src, const int32_t* ro
       h0 = v4u{bf16x2_to_h2(w0[k][0]), bf16x2_to_h2(w0[k][1]), bf16x2_to_h2(w0[k][2]), bf16x2_to_h2(w0[k][3])};
       h1 = v4u{bf16x2_to_h2(w1[k][0]), bf16x2_to_h2(w1[k][1]), bf16x2_to_h2(w1[k][2]), bf16x2_to_h2(w1[k][3])};
     } else {
-      const _Float16 sh = (_Float16)e4m3_to_float((t.c[k][2] >> (8 * (grp & 3))) & 0xFFu);     // exact
+      const _Float16 sh = (_Float16)e4m3_to_float((t.c[k][2] >> (8 * ((grp >> src.gshift) & 3))) & 0xFFu);  // exact
       const v2h s2 = {sh, sh};
       const uint32_t c0 = t.c[k][0], c1 = t.c[k][1];
       h0 = v4u{fp4_byte_h2<0>(c0, s2), fp4_byte_h2<1>(c0, s2), fp4_byte_h2<2>(c0, s2), fp4_byte_h2<3>(c0, s2)};

@@ -50,7 +50,8 @@ struct AttendArgs {
   const uint16_t* q_rope;    // [n_q, H, 64]
   float scale_log2;          // softmax_scale * log2(e)
   const uint8_t* kv_codes;
-  const uint8_t* kv_scales;
+  const uint8_t* kv_scales;  // [rows, 512 >> (4 + kv_gshift)]
+  int kv_gshift;             // FP4 scale group: 16 << kv_gshift channels (0 or 1)
   const uint16_t* kv_rope;
   const int32_t* topk_pos;
   const int32_t* topk_count;
@@ -68,7 +69,7 @@ struct AttendArgs {
   float* part_ml;            // [n_q, splits, H, 2]
 };
 
-hipError_t launch_encode(int64_t n, const uint16_t* latent, const uint16_t* rope,
+hipError_t launch_encode(int64_t n, int group, const uint16_t* latent, const uint16_t* rope,
                          const int64_t* dst_row, uint8_t* codes, uint8_t* scales,
                          uint16_t* rope_out, hipStream_t s);
 hipError_t launch_encode_rows(int64_t n, int width, const uint16_t* src, const int64_t* dst_row,

@@ -350,7 +350,11 @@ hipError_t launch_drw(const ScanArgs& a, hipStream_t s) {
 template <int D, bool F4>
 hipError_t launch_d(const ScanArgs& a, hipStream_t s) {
   // LDS ring slots per wave (steps in flight + 1) and waves per workgroup
-  if (a.waves == 8) return a.prefetch == 6 ? launch_drw<D, 6, 8, F4>(a, s) : launch_drw<D, 4, 8, F4>(a, s);
+  if (a.waves == 8) {
+    if (a.prefetch == 8) return launch_drw<D, 8, 8, F4>(a, s);
+    return a.prefetch == 6 ? launch_drw<D, 6, 8, F4>(a, s) : launch_drw<D, 4, 8, F4>(a, s);
+  }
+  if (a.prefetch == 8) return launch_drw<D, 8, 4, F4>(a, s);
   return a.prefetch == 6 ? launch_drw<D, 6, 4, F4>(a, s) : launch_drw<D, 4, 4, F4>(a, s);
 }
 

@@ -20,7 +20,7 @@ struct ScanArgs {
   int n_q, hi, d, swa, g;    // g: queries per sequence
   int tiles;                 // position tiles per query
   int tile_pos;              // positions per tile (multiple of 64)
-  int prefetch;              // LDS ring slots per wave (4 or 6)
+  int prefetch;              // LDS ring slots per wave (4, 6 or 8)
   int waves;                 // waves per workgroup (4 or 8)
   float* bscore;             // [n_q, ld]
   int64_t ld;

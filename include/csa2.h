@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define CSA2_ABI_VERSION 1
+#define CSA2_ABI_VERSION 2
 
 typedef enum csa2_status {
   CSA2_OK = 0,
@@ -70,7 +70,10 @@ typedef enum csa2_status {
  *                     ([atlas] §3.2: Top-2048 blocks, about 16,384 positions)
  *   topk         K    positions kept by Reindex, 1..min(8*P, 2048)
  *                     ([atlas] §3.2: Top-512 inside the pool)
- *   swa          W    sliding-window rows, 0..1024 */
+ *   swa          W    sliding-window rows, 0..1024
+ *   kv_group          channels per main-KV FP4 scale: 16 ([atlas] §3.2), or
+ *                     32 for the group-32 codec variant ([akhunji],
+ *                     "Microscopic FP4 (E2M1) Cache Compression"); 0 means 16 */
 typedef struct csa2_dims {
   int32_t n_heads;
   int32_t d_latent;
@@ -81,6 +84,7 @@ typedef struct csa2_dims {
   int32_t pool_blocks;
   int32_t topk;
   int32_t swa;
+  int32_t kv_group;
 } csa2_dims;
 
 /* A batch of decode queries.
@@ -135,6 +139,15 @@ const char* csa2_last_error(void);
 csa2_status csa2_encode_kv(int64_t n, const uint16_t* latent, const uint16_t* rope,
                            const int64_t* dst_row, uint8_t* kv_codes, uint8_t* kv_scales,
                            uint16_t* kv_rope, void* stream);
+
+/* csa2_encode_kv with `group` (16 or 32) channels per E4M3 scale: the same
+ * rule over each group ([akhunji], "Microscopic FP4 (E2M1) Cache
+ * Compression", for 32).  kv_scales is uint8 [rows, 512 / group]; codes and
+ * rope as in csa2_encode_kv.  Errors: as csa2_encode_kv, and
+ * CSA2_ERR_INVALID_ARG for another group. */
+csa2_status csa2_encode_kv_grouped(int64_t n, int32_t group, const uint16_t* latent, const uint16_t* rope,
+                                   const int64_t* dst_row, uint8_t* kv_codes, uint8_t* kv_scales,
+                                   uint16_t* kv_rope, void* stream);
 
 /* FP4 row encode at any width: the per-group codec of csa2_encode_kv applied
  * to rows of `width` channels, without a RoPE part.  It writes the indexer
@@ -299,7 +312,8 @@ csa2_status csa2_attend_workspace_size(const csa2_dims* dims, const csa2_queries
  *   lse_h = log sum_j exp(l_j).  A query with no entries gets out = 0 and
  *   lse = -inf.
  *   q_lat  bf16 [n_q, H, 512]     q_rope bf16 [n_q, H, 64]
- *   kv_codes, kv_scales, kv_rope  as written by csa2_encode_kv
+ *   kv_codes, kv_scales, kv_rope  as written by csa2_encode_kv (kv_scales
+ *          [rows, 512 / kv_group]; csa2_encode_kv_grouped for kv_group 32)
  *   topk_pos, topk_count          as produced by csa2_index_reindex
  *   swa_kv bf16 [swa_rows, 576]   swa_base int64 [n_q] (device)
  *   out    float [n_q, H, 512]    lse float [n_q, H] or NULL

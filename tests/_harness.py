@@ -100,7 +100,9 @@ class OracleQuery:
         rows = self.base + np.asarray(keep, dtype=np.int64)
         lat = u16(wl.latent_at(w, rows)) if len(rows) else np.zeros((0, 512), np.uint16)
         rp = u16(wl.rope_at(w, rows)) if len(rows) else np.zeros((0, 64), np.uint16)
-        codes, scales = oracle.encode_kv(lat) if len(rows) else (np.zeros((0, 256), np.uint8), np.zeros((0, 32), np.uint8))
+        grp = w.dims.kv_group
+        codes, scales = oracle.encode_kv(lat, grp) if len(rows) else (np.zeros((0, 256), np.uint8),
+                                                                      np.zeros((0, 512 // grp), np.uint8))
         win = self.base + np.arange(self.c, self.n, dtype=np.int64)
         swa = np.concatenate([u16(wl.latent_at(w, win)), u16(wl.rope_at(w, win))], axis=1) \
             if len(win) else np.zeros((0, 576), np.uint16)

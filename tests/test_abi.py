@@ -27,7 +27,7 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = set(declared_functions())
-    for n in ("csa2_encode_kv", "csa2_index_full", "csa2_index_reindex", "csa2_attend",
+    for n in ("csa2_encode_kv", "csa2_encode_kv_grouped", "csa2_index_full", "csa2_index_reindex", "csa2_attend",
               "csa2_index_scan", "csa2_index_pool", "csa2_status_string", "csa2_abi_version",
               "csa2_encode_fp4", "csa2_index_scan_fp4", "csa2_index_full_fp4", "csa2_index_reindex_fp4"):
         assert n in names
@@ -41,7 +41,9 @@ def test_library_exports_every_declared_function():
 
 def test_abi_version_and_status_strings():
     L = csa2.lib()
-    assert L.csa2_abi_version() == 1
+    # the header's version, which the library was built from
+    want = int(re.search(r"#define CSA2_ABI_VERSION (\d+)", open(HEADER).read()).group(1))
+    assert L.csa2_abi_version() == want == 2
     for st in (OK, INVALID, UNSUPPORTED, WORKSPACE, HIP):
         assert L.csa2_status_string(st)
     assert L.csa2_status_string(99)          # unknown codes still get text
@@ -78,7 +80,7 @@ def _call_ws(fn, dims, batch):
 @pytest.mark.parametrize("bad", [
     dict(idx_dim=96), dict(n_heads=24), dict(n_heads=0), dict(idx_heads=0), dict(idx_heads=65),
     dict(pool_blocks=0), dict(pool_blocks=4096), dict(topk=0), dict(topk=8 * 16 + 1, pool_blocks=16),
-    dict(swa=-1), dict(swa=2048),
+    dict(swa=-1), dict(swa=2048), dict(kv_group=8), dict(kv_group=64),
 ])
 def test_bad_dims_rejected(bad):
     L = csa2.lib()
@@ -150,3 +152,18 @@ def test_fp4_indexer_calls_rejected_before_any_device_work():
     assert L.csa2_encode_fp4(-1, 128, None, None, None, None, None) == INVALID
     assert L.csa2_encode_fp4(4, 128, None, None, 0x2000, 0x3000, None) == INVALID
     assert L.csa2_encode_fp4(0, 128, None, None, None, None, None) in (OK, INVALID)
+
+
+def test_dims_struct_matches_header():
+    # the binding's struct carries every csa2_dims field, in order
+    src = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    body = re.search(r"typedef struct csa2_dims \{(.*?)\} csa2_dims;", src, re.S).group(1)
+    fields = re.findall(r"int32_t\s+(\w+);", body)
+    assert fields == [f for f, _ in csa2._Dims._fields_]
+
+
+def test_grouped_encode_rejects_other_groups():
+    L = csa2.lib()
+    for g in (0, 8, 64):
+        assert L.csa2_encode_kv_grouped(4, g, 0x1000, 0x2000, None, 0x3000, 0x4000, 0x5000, None) == INVALID
+        assert b"group" in L.csa2_last_error()

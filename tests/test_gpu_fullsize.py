@@ -33,6 +33,7 @@ SAMPLES = {
     "specverify_b64x4_ctx16k-512k_encode64k": [0, 1, 2, 3, 254],
     "decode_b8_ctx128k_fp4idx": [0, 7],
     "decode_b1_ctx1m_fp4idx": [0],
+    "decode_b8_ctx128k_kvg32": [0, 7],
 }
 
 
@@ -79,7 +80,7 @@ def test_full_size_step(name):
         n = w.fresh_encode
         for e0 in (0, n // 2 - 128, n - 256):
             rows = slice(e0, e0 + 256)
-            ref_c, ref_s = oracle.encode_kv(u16(wl.fresh_latent(w, 0, e0, 256)))
+            ref_c, ref_s = oracle.encode_kv(u16(wl.fresh_latent(w, 0, e0, 256)), w.dims.kv_group)
             assert np.array_equal(u8(codes[rows]), ref_c), f"{name}: encoded codes differ at rows {e0}+"
             assert np.array_equal(u8(scales[rows]), ref_s), f"{name}: encoded scales differ at rows {e0}+"
             assert np.array_equal(u16(rope[rows]), u16(wl.fresh_rope(w, 0, e0, 256))), f"{name}: rope copy"

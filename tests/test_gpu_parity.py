@@ -4,6 +4,7 @@ Bars: FP4 bytes bit-exact; index sets equal except within a 1e-5 relative
 score band around the k-th score (ties to the lower index); indexer scores
 within 1e-3 relative; attention within 2e-3 of max|ref| per (query, head).
 """
+import dataclasses
 import os
 
 import numpy as np
@@ -47,6 +48,10 @@ CASES = {
                             [0, 1, 100, 128, 129, 136, 137, 160], fp4=True),
     "fp4_w0_h1": small(125, wl.Dims(n_heads=16, idx_heads=1, idx_dim=128, pool_blocks=32, topk=64, swa=0),
                        [3000], fp4=True),
+    # the group-32 main-KV codec (one E4M3 scale per 32 latent channels)
+    "kvg32_ragged_b3": small(131, dataclasses.replace(BIG, kv_group=32), [20005, 9003, 4099]),
+    "kvg32_edge_short": small(132, wl.Dims(n_heads=16, idx_heads=16, idx_dim=128, pool_blocks=4, topk=16,
+                                           kv_group=32), [0, 1, 100, 128, 129, 136, 137, 160]),
 }
 
 
@@ -63,7 +68,8 @@ def _oq(w, lay, keys_cache, qi):
     return oq
 
 
-def test_encode_bit_exact_generated():
+@pytest.mark.parametrize("group", [16, 32])
+def test_encode_bit_exact_generated(group):
     csa2 = lib()
     w = wl.workload(4)
     n = 4096 + 37
@@ -71,11 +77,11 @@ def test_encode_bit_exact_generated():
     rows = 3 * n
     perm = torch.randperm(rows, generator=torch.Generator().manual_seed(5))[:n].to("cuda")
     codes = torch.zeros(rows, 256, dtype=torch.uint8, device="cuda")
-    scales = torch.zeros(rows, 32, dtype=torch.uint8, device="cuda")
+    scales = torch.zeros(rows, 512 // group, dtype=torch.uint8, device="cuda")
     kr = torch.zeros(rows, 64, dtype=torch.bfloat16, device="cuda")
-    csa2.encode_kv(lat, rp, codes, scales, kr, dst_row=perm)
+    csa2.encode_kv(lat, rp, codes, scales, kr, dst_row=perm, group=group)
     torch.cuda.synchronize()
-    rc, rs = oracle.encode_kv(u16(wl.fresh_latent(w, 0, 0, n)))
+    rc, rs = oracle.encode_kv(u16(wl.fresh_latent(w, 0, 0, n)), group)
     p = perm.cpu().numpy()
     assert np.array_equal(u8(codes)[p], rc)
     assert np.array_equal(u8(scales)[p], rs)
@@ -118,17 +124,18 @@ def _exhaustive_groups():
     return out.reshape(rows, 512)
 
 
-def test_encode_exhaustive_scales_and_values():
+@pytest.mark.parametrize("group", [16, 32])
+def test_encode_exhaustive_scales_and_values(group):
     csa2 = lib()
     lat = _exhaustive_groups()
     n = lat.shape[0]
-    rc, rs = oracle.encode_kv(lat)
+    rc, rs = oracle.encode_kv(lat, group)
     t = torch.from_numpy(lat.astype(np.int16)).view(torch.bfloat16).to("cuda")
     rp = torch.zeros(n, 64, dtype=torch.bfloat16, device="cuda")
     codes = torch.empty(n, 256, dtype=torch.uint8, device="cuda")
-    scales = torch.empty(n, 32, dtype=torch.uint8, device="cuda")
+    scales = torch.empty(n, 512 // group, dtype=torch.uint8, device="cuda")
     kr = torch.empty(n, 64, dtype=torch.bfloat16, device="cuda")
-    csa2.encode_kv(t, rp, codes, scales, kr)
+    csa2.encode_kv(t, rp, codes, scales, kr, group=group)
     torch.cuda.synchronize()
     assert np.array_equal(u8(scales), rs)
     bad = np.argwhere(u8(codes) != rc)

@@ -138,6 +138,7 @@ class Dims:
     d_latent: int = 512
     d_rope: int = 64
     block: int = 8
+    kv_group: int = 16    # channels per main-KV FP4 scale (32: the group-32 codec variant)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -178,6 +179,9 @@ WORKLOADS: List[Workload] = [
     # the FP4 indexer variant of the two decode workloads
     Workload(5, "decode_b8_ctx128k_fp4idx", _BIG, n_seq=8, ctx=(131072, 131072), idx_fp4=True),
     Workload(6, "decode_b1_ctx1m_fp4idx", _BIG, n_seq=1, ctx=(1048576, 1048576), idx_fp4=True),
+    # the group-32 main-KV codec variant of the batch-8 decode workload
+    Workload(7, "decode_b8_ctx128k_kvg32", dataclasses.replace(_BIG, kv_group=32), n_seq=8,
+             ctx=(131072, 131072)),
 ]
 
 
