@@ -27,6 +27,8 @@ csa2_status hip_fail(hipError_t e, const char* what) {
   return fail(CSA2_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+int g_cus[64] = {0};                 // compute units per checked device
+
 // gfx950 check, once per device.
 csa2_status check_device() {
   static std::mutex mu;
@@ -41,6 +43,7 @@ csa2_status check_device() {
     e = hipGetDeviceProperties(&p, dev);
     if (e != hipSuccess) return hip_fail(e, "hipGetDeviceProperties");
     known[dev] = strncmp(p.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    g_cus[dev] = p.multiProcessorCount;
   }
   if (known[dev] != 1) return fail(CSA2_ERR_UNSUPPORTED, "device %d is not gfx950", dev);
   return CSA2_OK;
@@ -109,6 +112,22 @@ int scan_tile() {
 
 int scan_tiles(const csa2_dims* d, const csa2_queries* q, int tile) {
   return (int)((max_blocks(d, q) * 8 + tile - 1) / tile);
+}
+
+// Uneven scan tiles: when the whole grid is one round of at most two
+// workgroups per CU, the first-dispatched workgroup on a CU streams faster
+// than the second, so the first half of the tiles take kScanTileExtra more
+// positions and the second half as many fewer (measured: 0.4 us at 8 x 128K,
+// 1 us at 1M).  CSA2_SCAN_SPLIT overrides the shift (0 disables it).  Called
+// after check_device; the scan and the pool that reads its key ranges agree.
+int scan_tile_extra(const csa2_dims* d, const csa2_queries* q, int tile, int tiles) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  const int64_t units = ((int64_t)(q->n_q / q->tokens_per_seq) * tiles + 7) / 8 * 8;
+  int extra = units * q->tokens_per_seq <= 2 * (int64_t)g_cus[dev] ? kScanTileExtra : 0;
+  if (const char* env = getenv("CSA2_SCAN_SPLIT")) extra = atoi(env);
+  if (extra < 0 || extra % 8 || extra >= tile || tile + extra > 4096 || (tiles & 1)) extra = 0;
+  return extra;
 }
 
 // (min, max) key pairs per query: one per pool chunk or one per scan tile
@@ -269,6 +288,7 @@ static csa2_status run_scan(const csa2_dims* d, const csa2_queries* q, const uin
   sa.prefetch = pf;
   sa.waves = nw;
   sa.tiles = scan_tiles(d, q, sa.tile_pos);
+  sa.tile_extra = scan_tile_extra(d, q, sa.tile_pos, sa.tiles);
   sa.bscore = block_scores;
   sa.ld = ld_block_scores;
   sa.pool_ws = pool_ws_ptr;
@@ -290,7 +310,20 @@ static csa2_status run_pool(const csa2_dims* d, const csa2_queries* q, const flo
   pa.ws = (uint32_t*)ws;
   pa.ws_stride = pool_ws_words(pa.chunks, pa.mm_cap);
   pa.have_minmax = after_scan;
+  pa.mm_half = 0;
   pa.mm_span = after_scan ? scan_tile() / 8 : kPoolChunk;
+  if (after_scan) {
+    // the scan's tiles: the first half longer when it split them unevenly
+    const int tile = scan_tile(), tiles = scan_tiles(d, q, tile);
+    const int extra = scan_tile_extra(d, q, tile, tiles);
+    if (extra) {
+      pa.mm_half = tiles / 2;
+      pa.mm_span = (tile - extra) / 8;
+    }
+    pa.mm_span1 = (tile + extra) / 8;
+  } else {
+    pa.mm_span1 = pa.mm_span;
+  }
   pa.pool_blocks = pool_blocks; pa.pool_count = pool_count;
   hipError_t e = launch_pool_select(pa, (hipStream_t)stream);
   return e == hipSuccess ? CSA2_OK : hip_fail(e, "pool select launch");

@@ -18,7 +18,9 @@ struct PoolArgs {
   uint32_t* ws;              // [n_q, ws_stride] words (histogram, chunk results)
   int64_t ws_stride;
   int mm_cap;                // (min, max) key pairs per query in the workspace
-  int mm_span;               // blocks covered by one pair
+  int mm_half;               // pairs [0, mm_half) cover mm_span1 blocks each, later pairs mm_span
+  int mm_span1;
+  int mm_span;               // blocks covered by one pair (after the first mm_half)
   bool have_minmax;          // pairs and a cleared histogram already written (by the scan)
   int nw_cap;                // bitmap words of the longest query's blocks (final step LDS)
   bool small;                // every query has <= kPoolSmallBlocks blocks: one-workgroup selection

@@ -93,9 +93,13 @@ __global__ __launch_bounds__(64 * NW) void k_scan(ScanArgs a) {
 
   const int n = a.n_visible[q];
   const int c = max(0, n - a.swa);
-  const int p_begin = tile * a.tile_pos;
+  // with two workgroups per CU, the one dispatched first (the first half of
+  // the tile indices) streams faster, so it gets the longer tile
+  const int half_t = a.tiles >> 1;
+  const int t_long = a.tile_pos + a.tile_extra, t_short = a.tile_pos - a.tile_extra;
+  const int p_begin = tile < half_t ? tile * t_long : half_t * t_long + (tile - half_t) * t_short;
   if (p_begin >= c) return;
-  const int p_end = min(p_begin + a.tile_pos, c);
+  const int p_end = min(p_begin + (tile < half_t ? t_long : t_short), c);
   const int nsteps = (p_end - p_begin + 15) >> 4;
 
   v8h qf[HT][KC];
@@ -363,6 +367,9 @@ hipError_t launch_d(const ScanArgs& a, hipStream_t s) {
 hipError_t launch_scan(const ScanArgs& a, hipStream_t s) {
   if (a.tiles == 0) return hipSuccess;
   if (a.tile_pos > kMaxTilePos || a.tile_pos % 64) return hipErrorInvalidValue;
+  if (a.tile_extra < 0 || a.tile_extra % 8 || a.tile_extra >= a.tile_pos ||
+      a.tile_pos + a.tile_extra > kMaxTilePos || (a.tile_extra && (a.tiles & 1)))
+    return hipErrorInvalidValue;
   if (a.idx_k_scales) {
     if (a.d != 128 || !a.idx_q_scales) return hipErrorInvalidValue;
     return launch_d<128, true>(a, s);

@@ -20,6 +20,8 @@ struct ScanArgs {
   int n_q, hi, d, swa, g;    // g: queries per sequence
   int tiles;                 // position tiles per query
   int tile_pos;              // positions per tile (multiple of 64)
+  int tile_extra;            // tiles [0, tiles / 2) take tile_pos + tile_extra positions, the
+                             // rest tile_pos - tile_extra (a multiple of 8; 0: equal tiles)
   int prefetch;              // LDS ring slots per wave (4, 6 or 8)
   int waves;                 // waves per workgroup (4 or 8)
   float* bscore;             // [n_q, ld]
@@ -37,5 +39,6 @@ constexpr int kHistBins = 4096;        // pool histogram bins, cleared by the sc
 constexpr int kScanTile = 2048;        // default positions per scan workgroup
 constexpr int kScanPrefetch = 4;       // default LDS ring slots per wave
 constexpr int kScanWaves = 4;          // default waves per scan workgroup
+constexpr int kScanTileExtra = 512;    // uneven-tile shift when the grid is one round of two per CU
 
 }  // namespace csa2

@@ -123,7 +123,9 @@ struct KeyRange {
   }
   __device__ __forceinline__ void reduce(const PoolArgs& a, const PoolWs& w, int nb, uint32_t* s_scan,
                                          uint32_t* kmin, uint32_t* kmax) {
-    const int n = min(a.mm_cap, (nb + a.mm_span - 1) / a.mm_span);
+    const int nb1 = a.mm_half * a.mm_span1;
+    const int n = min(a.mm_cap, nb <= nb1 ? (nb + a.mm_span1 - 1) / a.mm_span1
+                                          : a.mm_half + (nb - nb1 + a.mm_span - 1) / a.mm_span);
     uint32_t lo = 0xFFFFFFFFu, hi = 0;
 #pragma unroll
     for (int r = 0; r < kKrPer; ++r) {
