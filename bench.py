@@ -337,6 +337,42 @@ def measure(w: wl.Workload, steps: int, warmup: int, replicas: int):
         "step_bytes": step_bytes(w),
     }
     res["step_gbs"] = round(res["step_bytes"] / (ms * 1e-3) / 1e9, 1)
+    # the same step as one csa2_decode_step call (Full layer), and that call
+    # captured into one HIP graph per replica and replayed
+    if w.reindex_layers == 1 and not w.fresh_encode:
+        csa2 = st.csa2
+        ws_g = torch.zeros(csa2.workspace_step(st.dims, st.batch) + 256, dtype=torch.uint8, device=st.dev)
+        q0, w0 = st.iq(0)
+        ql, qr = st.mq(0)
+
+        def layer(r):
+            idx_k, codes, scales, kv_rope, swa_kv = st.planes[r]
+            csa2.decode_step(st.dims, st.batch, csa2.LAYER_FULL, q0, w0, idx_k, step.pool, step.pcnt, step.tk[0],
+                             step.tc[0], ql, qr, 1.0, codes, scales, kv_rope, swa_kv, st.swa_base, step.out[0],
+                             step.lse[0], ws=ws_g)
+        for i in range(warmup):
+            layer(i % replicas)
+        torch.cuda.synchronize()
+        call_ms = _timed(lambda i: layer(i % replicas), steps, rate, issue_s)
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            layer(0)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graphs = []
+        for r in range(replicas):
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gr):
+                layer(r)
+            graphs.append(gr)
+        for i in range(warmup):
+            graphs[i % replicas].replay()
+        torch.cuda.synchronize()
+        graph_ms = _timed(lambda i: graphs[i % replicas].replay(), steps, rate, issue_s)
+        res["layer_step_us"] = {"stage_calls": round(ms * 1e3, 2), "decode_step": round(call_ms / steps * 1e3, 2),
+                                "graph_replay": round(graph_ms / steps * 1e3, 2)}
+        del graphs
     # spread of the step time: 20 short blocks of 5 steps, one event pair each
     import numpy as np
     blocks = []
@@ -528,6 +564,7 @@ def main():
                "indexer_rows": "fp4 (E2M1 + E4M3 per 16)" if w2.idx_fp4 else "fp8 e4m3",
                "kv_scale_group": w2.dims.kv_group,
                "stages_us": res2["stages_us"], "step_us_spread": res2["step_us_spread"],
+               "layer_step_us": res2.get("layer_step_us"),
                "replicas": res2["replicas"],
                "scan_roofline": {"bound": "hbm", "achieved": res2["scan"]["achieved_gbs"],
                                  "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": res2["scan"]["frac"],
@@ -579,6 +616,7 @@ def main():
                      "bytes_per_launch": res["scan"]["bytes_per_launch"], "avg_us": res["scan"]["avg_us"]},
         "stages_us": res["stages_us"],
         "step_us_spread": res["step_us_spread"],
+        "layer_step_us": res.get("layer_step_us"),
         "step_bytes": res["step_bytes"],
         "step_gbs": res["step_gbs"],
         "cpu_baseline": cpu,

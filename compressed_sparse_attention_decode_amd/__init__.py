@@ -27,7 +27,8 @@ import torch
 __all__ = ["Dims", "Batch", "Csa2Error", "lib", "lib_path", "encode_kv", "encode_fp4", "index_full",
            "index_scan", "index_pool", "n_blocks", "block_scores_ld", "workspace_pool",
            "index_reindex", "attend", "workspace_full", "workspace_reindex",
-           "workspace_attend", "abi_version", "Call"]
+           "workspace_attend", "abi_version", "Call", "decode_step", "workspace_step",
+           "LAYER_FULL", "LAYER_REINDEX", "LAYER_REUSE"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 lib_path = os.path.join(_PKG, "libcsa2.so")
@@ -81,6 +82,9 @@ def lib() -> ctypes.CDLL:
             "csa2_index_reindex_fp4": (I32, [PD, PQ, P, P, P, P, P, P, P, P, P, P, P, SZ, P]),
             "csa2_attend_workspace_size": (I32, [PD, PQ, ctypes.POINTER(SZ)]),
             "csa2_attend": (I32, [PD, PQ, P, P, ctypes.c_float, P, P, P, P, P, P, P, P, P, P, SZ, P]),
+            "csa2_decode_step_workspace_size": (I32, [PD, PQ, ctypes.POINTER(SZ)]),
+            "csa2_decode_step": (I32, [PD, PQ, I32, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_float,
+                                       P, P, P, P, P, P, P, P, SZ, P]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -197,6 +201,10 @@ def workspace_reindex(dims: Dims, b: Batch) -> int:
 
 def workspace_attend(dims: Dims, b: Batch) -> int:
     return _ws_size(lib().csa2_attend_workspace_size, dims, b)
+
+
+def workspace_step(dims: Dims, b: Batch) -> int:
+    return _ws_size(lib().csa2_decode_step_workspace_size, dims, b)
 
 
 def _workspace(nbytes: int, device, ws: Optional[torch.Tensor]) -> Optional[torch.Tensor]:
@@ -444,3 +452,50 @@ def attend(dims: Dims, b: Batch, q_lat: torch.Tensor, q_rope: torch.Tensor, soft
             out.data_ptr(), _ptr(lse), wp, wn, _stream(dev))
     call = _issue(lib().csa2_attend, args, (d, q, ws), prepare)
     return call if prepare else (out, lse)
+
+
+LAYER_FULL, LAYER_REINDEX, LAYER_REUSE = 0, 1, 2
+
+
+def decode_step(dims: Dims, b: Batch, mode: int, idx_q, idx_w, idx_k,
+                pool_blocks: torch.Tensor, pool_count: torch.Tensor,
+                topk_pos: torch.Tensor, topk_count: torch.Tensor,
+                q_lat: torch.Tensor, q_rope: torch.Tensor, softmax_scale: float,
+                kv_codes: torch.Tensor, kv_scales: torch.Tensor, kv_rope: torch.Tensor,
+                swa_kv: torch.Tensor, swa_base: torch.Tensor, out: torch.Tensor,
+                lse: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None, prepare: bool = False):
+    """One decode layer (csa2_decode_step): LAYER_FULL writes the pool and the
+    Top-K and attends; LAYER_REINDEX reads the pool, writes the Top-K and
+    attends; LAYER_REUSE attends over the given Top-K.  Indexer rows as for
+    index_full (None allowed for LAYER_REUSE).  `ws` must come from a
+    zero-filled allocation of at least workspace_step bytes (+256 for
+    alignment); it is allocated zero-filled when None."""
+    if mode not in (LAYER_FULL, LAYER_REINDEX, LAYER_REUSE):
+        raise ValueError("mode must be LAYER_FULL, LAYER_REINDEX or LAYER_REUSE")
+    dev = q_lat.device
+    n_q, H = b.n_q, dims.n_heads
+    _dev(pool_blocks, pool_count, topk_pos, topk_count, q_lat, q_rope, kv_codes, kv_scales, kv_rope, swa_kv,
+         swa_base, out, lse)
+    if pool_blocks.shape != (n_q, dims.pool_blocks) or pool_count.shape != (n_q,):
+        raise ValueError("pool shape mismatch")
+    if topk_pos.shape != (n_q, dims.topk) or topk_count.shape != (n_q,):
+        raise ValueError("topk shape mismatch")
+    if q_lat.shape != (n_q, H, 512) or q_rope.shape != (n_q, H, 64) or out.shape != (n_q, H, 512):
+        raise ValueError("q_lat / q_rope / out shape mismatch")
+    if swa_kv.dim() != 2 or swa_kv.shape[1] != 576 or swa_base.shape != (n_q,):
+        raise ValueError("swa_kv must be [rows, 576] and swa_base [n_q]")
+    if mode == LAYER_REUSE and idx_q is None:
+        qp, kp, wp_ = [None, None], [None, None], None
+    else:
+        fp4, qp, kp = _check_idx(dims, b, idx_q, idx_w, idx_k)
+        if not fp4:
+            qp, kp = [qp[0], None], [kp[0], None]
+        wp_ = idx_w.data_ptr()
+    ws = _workspace(workspace_step(dims, b), dev, ws)
+    wsp, wn = _ws_ptr(ws)
+    d, q = dims.c(), b.c()
+    args = (ctypes.byref(d), ctypes.byref(q), mode, qp[0], qp[1], wp_, kp[0], kp[1], pool_blocks.data_ptr(),
+            pool_count.data_ptr(), topk_pos.data_ptr(), topk_count.data_ptr(), q_lat.data_ptr(), q_rope.data_ptr(),
+            float(softmax_scale), kv_codes.data_ptr(), kv_scales.data_ptr(), kv_rope.data_ptr(), swa_kv.data_ptr(),
+            swa_base.data_ptr(), out.data_ptr(), _ptr(lse), wsp, wn, _stream(dev))
+    return _issue(lib().csa2_decode_step, args, (d, q, ws), prepare)

@@ -402,7 +402,7 @@ csa2_status csa2_index_pool(const csa2_dims* d, const csa2_queries* q, const flo
 static csa2_status index_full(const csa2_dims* d, const csa2_queries* q, const uint8_t* idx_q, const uint8_t* q_scales,
                               const float* idx_w, const uint8_t* idx_k, const uint8_t* k_scales, bool fp4,
                               int32_t* pool_blocks, int32_t* pool_count, float* block_scores, int64_t ld_block_scores,
-                              void* ws, size_t ws_bytes, void* stream) {
+                              void* ws, size_t ws_bytes, void* stream, bool dry = false) {
   csa2_status st = check_dims(d);
   if (st) return st;
   if ((st = check_queries(q))) return st;
@@ -418,6 +418,7 @@ static csa2_status index_full(const csa2_dims* d, const csa2_queries* q, const u
   }
   if ((st = check_block_scores(d, q, bs, ld))) return st;
   if ((st = check_device())) return st;
+  if (dry) return CSA2_OK;
   if ((st = run_scan(d, q, idx_q, fp4 ? q_scales : nullptr, idx_w, idx_k, fp4 ? k_scales : nullptr, bs, ld,
                      (uint32_t*)ws, stream)))
     return st;
@@ -452,7 +453,8 @@ csa2_status csa2_index_reindex_workspace_size(const csa2_dims* d, const csa2_que
 static csa2_status index_reindex(const csa2_dims* d, const csa2_queries* q, const uint8_t* idx_q, const uint8_t* q_scales,
                                  const float* idx_w, const uint8_t* idx_k, const uint8_t* k_scales, bool fp4,
                                  const int32_t* pool_blocks, const int32_t* pool_count, int32_t* topk_pos,
-                                 int32_t* topk_count, float* topk_scores, void* ws, size_t ws_bytes, void* stream) {
+                                 int32_t* topk_count, float* topk_scores, void* ws, size_t ws_bytes, void* stream,
+                                 bool dry = false) {
   csa2_status st = check_dims(d);
   if (st) return st;
   if ((st = check_queries(q))) return st;
@@ -461,6 +463,7 @@ static csa2_status index_reindex(const csa2_dims* d, const csa2_queries* q, cons
     return fail(CSA2_ERR_INVALID_ARG, "required pointer is NULL");
   if ((st = check_ws(ws, ws_bytes, reindex_ws(d, q)))) return st;
   if ((st = check_device())) return st;
+  if (dry) return CSA2_OK;
   ReindexArgs ra;
   ra.idx_q = idx_q; ra.idx_w = idx_w; ra.idx_k = idx_k;
   ra.idx_q_scales = fp4 ? q_scales : nullptr;
@@ -503,11 +506,11 @@ csa2_status csa2_attend_workspace_size(const csa2_dims* d, const csa2_queries* q
   return CSA2_OK;
 }
 
-csa2_status csa2_attend(const csa2_dims* d, const csa2_queries* q, const uint16_t* q_lat, const uint16_t* q_rope,
-                        float softmax_scale, const uint8_t* kv_codes, const uint8_t* kv_scales,
-                        const uint16_t* kv_rope, const int32_t* topk_pos, const int32_t* topk_count,
-                        const uint16_t* swa_kv, const int64_t* swa_base, float* out, float* lse, void* ws,
-                        size_t ws_bytes, void* stream) {
+static csa2_status attend(const csa2_dims* d, const csa2_queries* q, const uint16_t* q_lat, const uint16_t* q_rope,
+                          float softmax_scale, const uint8_t* kv_codes, const uint8_t* kv_scales,
+                          const uint16_t* kv_rope, const int32_t* topk_pos, const int32_t* topk_count,
+                          const uint16_t* swa_kv, const int64_t* swa_base, float* out, float* lse, void* ws,
+                          size_t ws_bytes, void* stream, bool dry = false) {
   csa2_status st = check_dims(d);
   if (st) return st;
   if ((st = check_queries(q))) return st;
@@ -521,6 +524,7 @@ csa2_status csa2_attend(const csa2_dims* d, const csa2_queries* q, const uint16_
   if ((uintptr_t)kv_codes & 7) return fail(CSA2_ERR_INVALID_ARG, "kv_codes must be 8-byte aligned");
   if ((st = check_ws(ws, ws_bytes, attend_ws(d, q)))) return st;
   if ((st = check_device())) return st;
+  if (dry) return CSA2_OK;
   const AttendPlan p = attend_plan(d, q);
   AttendArgs aa;
   aa.q_lat = q_lat; aa.q_rope = q_rope; aa.scale_log2 = softmax_scale * 1.4426950408889634f;
@@ -541,6 +545,69 @@ csa2_status csa2_attend(const csa2_dims* d, const csa2_queries* q, const uint16_
   }
   hipError_t e = launch_attend(aa, (hipStream_t)stream);
   return e == hipSuccess ? CSA2_OK : hip_fail(e, "attend launch");
+}
+
+csa2_status csa2_attend(const csa2_dims* d, const csa2_queries* q, const uint16_t* q_lat, const uint16_t* q_rope,
+                        float softmax_scale, const uint8_t* kv_codes, const uint8_t* kv_scales,
+                        const uint16_t* kv_rope, const int32_t* topk_pos, const int32_t* topk_count,
+                        const uint16_t* swa_kv, const int64_t* swa_base, float* out, float* lse, void* ws,
+                        size_t ws_bytes, void* stream) {
+  return attend(d, q, q_lat, q_rope, softmax_scale, kv_codes, kv_scales, kv_rope, topk_pos, topk_count, swa_kv,
+                swa_base, out, lse, ws, ws_bytes, stream);
+}
+
+// The layer step's workspace: the Full index's (pool + block scores), then
+// the Reindex one (its counters first), then the attention partials.
+static size_t step_ws_full(const csa2_dims* d, const csa2_queries* q) { return full_ws(d, q); }
+static size_t step_ws_reindex(const csa2_dims* d, const csa2_queries* q) { return align256(reindex_ws(d, q)); }
+
+csa2_status csa2_decode_step_workspace_size(const csa2_dims* d, const csa2_queries* q, size_t* bytes) {
+  csa2_status st = check_dims(d);
+  if (st) return st;
+  if ((st = check_queries(q))) return st;
+  if (!bytes) return fail(CSA2_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = step_ws_full(d, q) + step_ws_reindex(d, q) + attend_ws(d, q);
+  return CSA2_OK;
+}
+
+csa2_status csa2_decode_step(const csa2_dims* d, const csa2_queries* q, int32_t mode, const uint8_t* idx_q,
+                             const uint8_t* idx_q_scales, const float* idx_w, const uint8_t* idx_k,
+                             const uint8_t* idx_k_scales, int32_t* pool_blocks, int32_t* pool_count,
+                             int32_t* topk_pos, int32_t* topk_count, const uint16_t* q_lat, const uint16_t* q_rope,
+                             float softmax_scale, const uint8_t* kv_codes, const uint8_t* kv_scales,
+                             const uint16_t* kv_rope, const uint16_t* swa_kv, const int64_t* swa_base, float* out,
+                             float* lse, void* ws, size_t ws_bytes, void* stream) {
+  csa2_status st = check_dims(d);
+  if (st) return st;
+  if ((st = check_queries(q))) return st;
+  if (mode != CSA2_LAYER_FULL && mode != CSA2_LAYER_REINDEX && mode != CSA2_LAYER_REUSE)
+    return fail(CSA2_ERR_INVALID_ARG, "mode must be CSA2_LAYER_FULL, _REINDEX or _REUSE (got %d)", mode);
+  if ((idx_q_scales == nullptr) != (idx_k_scales == nullptr))
+    return fail(CSA2_ERR_INVALID_ARG, "idx_q_scales and idx_k_scales must both be given (FP4 rows) or both NULL");
+  const bool fp4 = idx_q_scales != nullptr;
+  size_t need = 0;
+  if ((st = csa2_decode_step_workspace_size(d, q, &need))) return st;
+  if ((st = check_ws(ws, ws_bytes, need))) return st;
+  char* w_full = (char*)ws;
+  char* w_re = w_full + step_ws_full(d, q);
+  char* w_att = w_re + step_ws_reindex(d, q);
+  const size_t n_full = step_ws_full(d, q), n_re = step_ws_reindex(d, q), n_att = ws_bytes - n_full - n_re;
+  // every stage's arguments are checked before the first launch
+  for (int pass = 0; pass < 2; ++pass) {
+    const bool dry = pass == 0;
+    if (mode == CSA2_LAYER_FULL &&
+        (st = index_full(d, q, idx_q, idx_q_scales, idx_w, idx_k, idx_k_scales, fp4, pool_blocks, pool_count,
+                         nullptr, 0, w_full, n_full, stream, dry)))
+      return st;
+    if (mode != CSA2_LAYER_REUSE &&
+        (st = index_reindex(d, q, idx_q, idx_q_scales, idx_w, idx_k, idx_k_scales, fp4, pool_blocks, pool_count,
+                            topk_pos, topk_count, nullptr, w_re, n_re, stream, dry)))
+      return st;
+    if ((st = attend(d, q, q_lat, q_rope, softmax_scale, kv_codes, kv_scales, kv_rope, topk_pos, topk_count, swa_kv,
+                     swa_base, out, lse, attend_ws(d, q) ? w_att : nullptr, n_att, stream, dry)))
+      return st;
+  }
+  return CSA2_OK;
 }
 
 }  // extern "C"

@@ -326,6 +326,41 @@ csa2_status csa2_attend(const csa2_dims* dims, const csa2_queries* q,
                         const uint16_t* swa_kv, const int64_t* swa_base,
                         float* out, float* lse, void* ws, size_t ws_bytes, void* stream);
 
+/* One decode layer in one call ([atlas] §3.2 mode table: a Full layer
+ * scores the whole context and takes a new index set, a Reindex layer
+ * re-scores the inherited pool with its own indexer query, a Reuse layer
+ * only attends over the inherited index set with its own main Q).  The call
+ * checks every stage's arguments, then enqueues, on `stream`:
+ *   CSA2_LAYER_FULL     csa2_index_full (pool_blocks, pool_count written),
+ *                       csa2_index_reindex with the same indexer query
+ *                       (topk_pos, topk_count written), csa2_attend;
+ *   CSA2_LAYER_REINDEX  csa2_index_reindex on the given pool, csa2_attend;
+ *   CSA2_LAYER_REUSE    csa2_attend on the given topk_pos / topk_count
+ *                       (the idx_* arguments may be NULL).
+ * The indexer rows are fp8 when idx_q_scales and idx_k_scales are NULL and
+ * FP4 (as the *_fp4 calls) when both are given.  Every other argument is as
+ * in the stage calls.  No kernel is fused: the chain is the stages' own
+ * launches (5 kernels for a Full layer at batch 8), which a caller can also
+ * capture into a HIP graph (no memset or allocation is enqueued).
+ *   ws, ws_bytes  csa2_decode_step_workspace_size bytes, 256-byte aligned,
+ *               zero-filled before its first use (it holds the Reindex
+ *               completion counters, which every call leaves at zero);
+ *               calls sharing it must be ordered on one stream. */
+#define CSA2_LAYER_FULL 0
+#define CSA2_LAYER_REINDEX 1
+#define CSA2_LAYER_REUSE 2
+
+csa2_status csa2_decode_step_workspace_size(const csa2_dims* dims, const csa2_queries* q, size_t* bytes);
+
+csa2_status csa2_decode_step(const csa2_dims* dims, const csa2_queries* q, int32_t mode,
+                             const uint8_t* idx_q, const uint8_t* idx_q_scales, const float* idx_w,
+                             const uint8_t* idx_k, const uint8_t* idx_k_scales,
+                             int32_t* pool_blocks, int32_t* pool_count, int32_t* topk_pos, int32_t* topk_count,
+                             const uint16_t* q_lat, const uint16_t* q_rope, float softmax_scale,
+                             const uint8_t* kv_codes, const uint8_t* kv_scales, const uint16_t* kv_rope,
+                             const uint16_t* swa_kv, const int64_t* swa_base, float* out, float* lse,
+                             void* ws, size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -29,7 +29,8 @@ def test_header_declares_the_entry_points():
     names = set(declared_functions())
     for n in ("csa2_encode_kv", "csa2_encode_kv_grouped", "csa2_index_full", "csa2_index_reindex", "csa2_attend",
               "csa2_index_scan", "csa2_index_pool", "csa2_status_string", "csa2_abi_version",
-              "csa2_encode_fp4", "csa2_index_scan_fp4", "csa2_index_full_fp4", "csa2_index_reindex_fp4"):
+              "csa2_encode_fp4", "csa2_index_scan_fp4", "csa2_index_full_fp4", "csa2_index_reindex_fp4",
+              "csa2_decode_step", "csa2_decode_step_workspace_size"):
         assert n in names
 
 
@@ -167,3 +168,31 @@ def test_grouped_encode_rejects_other_groups():
     for g in (0, 8, 64):
         assert L.csa2_encode_kv_grouped(4, g, 0x1000, 0x2000, None, 0x3000, 0x4000, 0x5000, None) == INVALID
         assert b"group" in L.csa2_last_error()
+
+
+def test_decode_step_rejected_before_any_device_work():
+    L = csa2.lib()
+    d, q = _dims().c(), _batch().c()
+    args = [0x1000] * 17 + [None, 0x2000, 1 << 30, None]
+    # bad mode
+    st = L.csa2_decode_step(ctypes.byref(d), ctypes.byref(q), 7, 0x1000, None, 0x1000, 0x1000, None,
+                            0x1000, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000, 1.0, 0x1000, 0x1000, 0x1000,
+                            0x1000, 0x1000, 0x1000, None, 0x2000, 1 << 30, None)
+    assert st == INVALID and b"mode" in L.csa2_last_error()
+    # one FP4 scale plane without the other
+    st = L.csa2_decode_step(ctypes.byref(d), ctypes.byref(q), 0, 0x1000, 0x1100, 0x1000, 0x1000, None,
+                            0x1000, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000, 1.0, 0x1000, 0x1000, 0x1000,
+                            0x1000, 0x1000, 0x1000, None, 0x2000, 1 << 30, None)
+    assert st == INVALID and b"scales" in L.csa2_last_error()
+    # workspace too small
+    st = L.csa2_decode_step(ctypes.byref(d), ctypes.byref(q), 2, None, None, None, None, None,
+                            0x1000, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000, 1.0, 0x1000, 0x1000, 0x1000,
+                            0x1000, 0x1000, 0x1000, None, 0x2000, 16, None)
+    assert st == WORKSPACE
+    del args
+    n = ctypes.c_size_t(0)
+    assert L.csa2_decode_step_workspace_size(ctypes.byref(d), ctypes.byref(q), ctypes.byref(n)) == OK
+    parts = [_call_ws(f, _dims(), _batch())[1] for f in (L.csa2_index_full_workspace_size,
+                                                         L.csa2_index_reindex_workspace_size,
+                                                         L.csa2_attend_workspace_size)]
+    assert n.value >= sum(parts)
