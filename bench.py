@@ -34,6 +34,7 @@ import torch  # noqa: E402
 import workloads as wl  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+F16_PEAK_TFLOPS = 2500.0       # MI355X dense fp16 / bf16 matrix, published
 SCAN_SOURCES = ["compressed_sparse_attention_decode_amd/csrc/scan.hip",
                 "compressed_sparse_attention_decode_amd/csrc/common.h",
                 "compressed_sparse_attention_decode_amd/csrc/scan_args.h"]
@@ -217,6 +218,15 @@ def scan_bytes(w: wl.Workload) -> int:
     return tot
 
 
+def scan_flops(w: wl.Workload) -> int:
+    """Algorithmic flops of one scan launch: 2 * H_i * d_i per candidate
+    position of every query (tokens of one sequence share the keys, not the
+    dot products)."""
+    lay = wl.layout(w)
+    d = w.dims
+    return sum(2 * d.idx_heads * d.idx_dim * max(0, n - d.swa) for n in lay.q_visible)
+
+
 def step_bytes(w: wl.Workload) -> int:
     """Algorithmic HBM bytes of one step (scan + Reindex + attention + encode)."""
     d = w.dims
@@ -333,7 +343,9 @@ def measure(w: wl.Workload, steps: int, warmup: int, replicas: int):
         "stages_us": {k: round(v, 2) for k, v in stages.items()},
         "replicas": replicas,
         "scan": {"bytes_per_launch": per_step, "avg_us": round(scan_us, 3),
-                 "achieved_gbs": round(achieved, 1), "frac": round(achieved / HBM_PEAK_GBS, 4)},
+                 "achieved_gbs": round(achieved, 1), "frac": round(achieved / HBM_PEAK_GBS, 4),
+                 "mfma_tflops": round(scan_flops(w) / (scan_us * 1e-6) / 1e12, 1),
+                 "mfma_frac": round(scan_flops(w) / (scan_us * 1e-6) / 1e12 / F16_PEAK_TFLOPS, 4)},
         "step_bytes": step_bytes(w),
     }
     res["step_gbs"] = round(res["step_bytes"] / (ms * 1e-3) / 1e9, 1)
@@ -516,7 +528,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode_b8_ctx128k")
     ap.add_argument("--secondary", default="decode_b1_ctx1m", help="second workload ('' to skip)")
-    ap.add_argument("--variants", default="decode_b8_ctx128k_fp4idx,decode_b1_ctx1m_fp4idx,decode_b8_ctx128k_kvg32",
+    ap.add_argument("--variants", default="decode_b8_ctx128k_fp4idx,decode_b1_ctx1m_fp4idx,decode_b8_ctx128k_kvg32,"
+                                          "chunk_b1x64_ctx128k",
                     help="comma-separated further workloads reported under 'variants' ('' to skip)")
     ap.add_argument("--replicas", type=int, default=0, help="cache replicas (0: enough for >= 1 GB)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle sample budget (0 to skip)")
@@ -570,7 +583,9 @@ def main():
                                  "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": res2["scan"]["frac"],
                                  "bytes_per_launch": res2["scan"]["bytes_per_launch"],
                                  "avg_us": res2["scan"]["avg_us"],
-                                 "traffic": measured_traffic(w2.name)}}
+                                 "traffic": measured_traffic(w2.name)},
+               "scan_mfma": {"achieved_tflops": res2["scan"]["mfma_tflops"], "peak_tflops": F16_PEAK_TFLOPS,
+                             "frac": res2["scan"]["mfma_frac"], "dtype": "f16 (exact fp8 / FP4 conversions)"}}
         print(f"[bench] {w2.name}: {res2['value']:.1f} queries/s, scan {res2['scan']['avg_us']} us = "
               f"{res2['scan']['achieved_gbs']} GB/s", file=sys.stderr, flush=True)
         return w2, st2, step2, rec

@@ -74,8 +74,9 @@ csa2_status check_queries(const csa2_queries* q) {
   if (!q) return fail(CSA2_ERR_INVALID_ARG, "queries is NULL");
   if (q->n_q < 1) return fail(CSA2_ERR_INVALID_ARG, "n_q must be >= 1 (got %d)", q->n_q);
   if (q->n_q > (1 << 20)) return fail(CSA2_ERR_INVALID_ARG, "n_q must be <= 2^20 (got %d)", q->n_q);
-  if (q->tokens_per_seq < 1 || q->tokens_per_seq > 4 || q->n_q % q->tokens_per_seq)
-    return fail(CSA2_ERR_INVALID_ARG, "tokens_per_seq must be 1..4 and divide n_q (got %d)", q->tokens_per_seq);
+  if (q->tokens_per_seq < 1 || q->tokens_per_seq > kMaxTokensPerSeq || q->n_q % q->tokens_per_seq)
+    return fail(CSA2_ERR_INVALID_ARG, "tokens_per_seq must be 1..%d and divide n_q (got %d)", kMaxTokensPerSeq,
+                q->tokens_per_seq);
   if (q->max_visible < 0 || q->max_visible > kMaxVisible)
     return fail(CSA2_ERR_INVALID_ARG, "max_visible must be in [0, 2^21] (got %d)", q->max_visible);
   if (q->reserved != 0) return fail(CSA2_ERR_INVALID_ARG, "reserved must be 0");

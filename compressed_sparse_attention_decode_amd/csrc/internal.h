@@ -90,6 +90,7 @@ constexpr int kAttendWaves = 4;        // waves per attention workgroup (16 head
 constexpr int kAttendMaxSplits = 16;   // entry-list splits per query, at most
 constexpr int kReindexBlocks = 64;     // pool blocks per Reindex scoring workgroup
 constexpr int kMaxVisible = 1 << 21;   // bound of n_visible
+constexpr int kMaxTokensPerSeq = 64;   // query tokens of one sequence sharing its key stream
 constexpr int kMaxBlocks = kMaxVisible / 8;
 
 }  // namespace csa2

@@ -89,9 +89,10 @@ typedef struct csa2_dims {
 
 /* A batch of decode queries.
  *   n_q             number of queries (>= 1).
- *   tokens_per_seq  g in 1..4: queries g*i .. g*i+g-1 belong to one
- *                   sequence (consecutive causal query tokens, e.g. a
- *                   speculative-verify step) and MUST share seq_base; the
+ *   tokens_per_seq  g in 1..64: queries g*i .. g*i+g-1 belong to one
+ *                   sequence (consecutive causal query tokens: a
+ *                   speculative-verify step, or a prefill chunk scored by
+ *                   the indexer against the cache) and MUST share seq_base; the
  *                   Full scan runs their workgroups for the same key range on
  *                   one XCD so the g key streams are served by one L2.
  *                   n_q must be a multiple of g.

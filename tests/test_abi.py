@@ -90,12 +90,18 @@ def test_bad_dims_rejected(bad):
     assert L.csa2_last_error()
 
 
-@pytest.mark.parametrize("kw", [dict(n_q=0), dict(max_visible=(1 << 21) + 1), dict(g=3), dict(g=5),
+@pytest.mark.parametrize("kw", [dict(n_q=0), dict(max_visible=(1 << 21) + 1), dict(g=3), dict(n_q=130, g=65),
                                 dict(max_visible=-1)])
 def test_bad_queries_rejected(kw):
     L = csa2.lib()
     st, _ = _call_ws(L.csa2_index_full_workspace_size, _dims(), _batch(**kw))
     assert st == INVALID
+
+
+def test_tokens_per_seq_up_to_64():
+    L = csa2.lib()
+    st, n = _call_ws(L.csa2_index_full_workspace_size, _dims(), _batch(n_q=128, g=64))
+    assert st == OK and n > 0
 
 
 def test_workspace_sizes_are_consistent():

@@ -34,6 +34,7 @@ SAMPLES = {
     "decode_b8_ctx128k_fp4idx": [0, 7],
     "decode_b1_ctx1m_fp4idx": [0],
     "decode_b8_ctx128k_kvg32": [0, 7],
+    "chunk_b1x64_ctx128k": [0, 31, 63],
 }
 
 

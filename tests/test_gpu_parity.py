@@ -48,6 +48,8 @@ CASES = {
                             [0, 1, 100, 128, 129, 136, 137, 160], fp4=True),
     "fp4_w0_h1": small(125, wl.Dims(n_heads=16, idx_heads=1, idx_dim=128, pool_blocks=32, topk=64, swa=0),
                        [3000], fp4=True),
+    # 16 query tokens of one sequence (a chunk scored against one key stream)
+    "chunk_g16": small(141, BIG, [9000], g=16),
     # the group-32 main-KV codec (one E4M3 scale per 32 latent channels)
     "kvg32_ragged_b3": small(131, dataclasses.replace(BIG, kv_group=32), [20005, 9003, 4099]),
     "kvg32_edge_short": small(132, wl.Dims(n_heads=16, idx_heads=16, idx_dim=128, pool_blocks=4, topk=16,

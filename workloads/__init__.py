@@ -182,6 +182,8 @@ WORKLOADS: List[Workload] = [
     # the group-32 main-KV codec variant of the batch-8 decode workload
     Workload(7, "decode_b8_ctx128k_kvg32", dataclasses.replace(_BIG, kv_group=32), n_seq=8,
              ctx=(131072, 131072)),
+    # many query tokens against one cache (a 64-token chunk at 128K context)
+    Workload(8, "chunk_b1x64_ctx128k", _BIG, n_seq=1, ctx=(131072, 131072), tokens_per_seq=64),
 ]
 
 
