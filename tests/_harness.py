@@ -32,7 +32,7 @@ def have_gpu() -> bool:
 
 
 def lib():
-    """The HIP binding; on a GPU machine a missing library is an error, not a skip."""
+    """The HIP binding; with a GPU present, a missing library is an error, not a skip."""
     if not have_gpu():
         pytest.skip("no GPU")
     import compressed_sparse_attention_decode_amd as csa2
