@@ -584,13 +584,16 @@ __global__ __launch_bounds__(kTkThreads) void k_pool_small(PoolArgs a) {
   int32_t* out = a.pool_blocks + (int64_t)q * P;
   // thread t holds blocks [kPer t, kPer (t + 1)); the loads are bounded by
   // the row stride (a multiple of 4 floats) only, so they need not wait for
-  // the block count, which masks them afterwards
+  // the block count, which masks them afterwards.  Every load is issued,
+  // clamped into the row, and masked after it: a load under a condition
+  // would be waited for at once, which made four round trips of the eight.
   const int s0 = tid * kPer;
   v4f x[kPer / 4];
 #pragma unroll
+  for (int v = 0; v < kPer / 4; ++v) x[v] = *reinterpret_cast<const v4f*>(bs + min(s0 + 4 * v, (int)a.ld - 4));
+#pragma unroll
   for (int v = 0; v < kPer / 4; ++v) {
-    const int j = s0 + 4 * v;
-    x[v] = j < a.ld ? *reinterpret_cast<const v4f*>(bs + j) : v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    if (s0 + 4 * v >= a.ld) x[v] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
   }
   const int nb = query_blocks(a, q);
   uint32_t key[kPer];
