@@ -27,7 +27,7 @@ import torch
 __all__ = ["Dims", "Batch", "Csa2Error", "lib", "lib_path", "encode_kv", "encode_fp4", "index_full",
            "index_scan", "index_pool", "n_blocks", "block_scores_ld", "workspace_pool",
            "index_reindex", "attend", "workspace_full", "workspace_reindex",
-           "workspace_attend", "abi_version", "Call", "decode_step", "workspace_step",
+           "workspace_attend", "abi_version", "Call", "decode_step", "workspace_step", "Pages", "page_rows",
            "LAYER_FULL", "LAYER_REINDEX", "LAYER_REUSE"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -53,6 +53,11 @@ class _Queries(ctypes.Structure):
 _lib = None
 
 
+class _Pages(ctypes.Structure):
+    _fields_ = [("table", ctypes.c_void_p), ("page_size", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("rows", ctypes.c_int64)]
+
+
 def lib() -> ctypes.CDLL:
     """Load libcsa2.so from the package directory (raises if it is missing)."""
     global _lib
@@ -62,7 +67,7 @@ def lib() -> ctypes.CDLL:
                             "or python -m compressed_sparse_attention_decode_amd._build")
         L = ctypes.CDLL(lib_path)
         P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
-        PD, PQ = ctypes.POINTER(_Dims), ctypes.POINTER(_Queries)
+        PD, PQ, PP = ctypes.POINTER(_Dims), ctypes.POINTER(_Queries), ctypes.POINTER(_Pages)
         sig = {
             "csa2_abi_version": (I32, []),
             "csa2_status_string": (ctypes.c_char_p, [I32]),
@@ -82,6 +87,9 @@ def lib() -> ctypes.CDLL:
             "csa2_index_reindex_fp4": (I32, [PD, PQ, P, P, P, P, P, P, P, P, P, P, P, SZ, P]),
             "csa2_attend_workspace_size": (I32, [PD, PQ, ctypes.POINTER(SZ)]),
             "csa2_attend": (I32, [PD, PQ, P, P, ctypes.c_float, P, P, P, P, P, P, P, P, P, P, SZ, P]),
+            "csa2_index_reindex_paged": (I32, [PD, PQ, PP, P, P, P, P, P, P, P, P, P, P, P, SZ, P]),
+            "csa2_attend_paged": (I32, [PD, PQ, PP, P, P, ctypes.c_float, P, P, P, P, P, P, P, P, P, P, SZ, P]),
+            "csa2_page_rows": (I32, [PP, I64, P, P, P, P]),
             "csa2_decode_step_workspace_size": (I32, [PD, PQ, ctypes.POINTER(SZ)]),
             "csa2_decode_step": (I32, [PD, PQ, I32, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_float,
                                        P, P, P, P, P, P, P, P, SZ, P]),
@@ -160,6 +168,40 @@ class Batch:
         _dev(self.seq_base, self.n_visible)
         return _Queries(self.n_q, self.tokens_per_seq, self.max_visible, 0,
                         self.seq_base.data_ptr(), self.n_visible.data_ptr())
+
+
+@dataclasses.dataclass
+class Pages:
+    """Paged per-position planes (csa2_pages): device int32 `table` of
+    physical page ids; position p of a query's sequence is row
+    table[seq_base + p // page_size] * page_size + p % page_size, where the
+    Batch's seq_base then holds each query's offset in `table`.  `rows` is
+    the row count of every plane the call reads."""
+    table: torch.Tensor
+    page_size: int
+    rows: int
+
+    def c(self) -> _Pages:
+        if self.table.dtype != torch.int32 or not self.table.is_contiguous():
+            raise TypeError("the page table must be contiguous int32")
+        _dev(self.table)
+        return _Pages(self.table.data_ptr(), self.page_size, 0, self.rows)
+
+
+def page_rows(pages: Pages, table_off: torch.Tensor, pos: torch.Tensor,
+              dst_row: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Rows of (table offset, position) pairs in paged planes
+    (csa2_page_rows), e.g. as encode_kv's dst_row to append into pages."""
+    _dev(table_off, pos, dst_row)
+    if table_off.dtype != torch.int64 or pos.dtype != torch.int32 or table_off.shape != pos.shape:
+        raise TypeError("table_off must be int64 and pos int32, of one shape")
+    n = pos.numel()
+    if dst_row is None:
+        dst_row = torch.empty(n, dtype=torch.int64, device=pos.device)
+    pg = pages.c()
+    _check(lib().csa2_page_rows(ctypes.byref(pg), n, table_off.data_ptr(), pos.data_ptr(), dst_row.data_ptr(),
+                                _stream(pos.device)))
+    return dst_row
 
 
 def _dev(*ts):
@@ -397,8 +439,9 @@ def index_reindex(dims: Dims, b: Batch, idx_q, idx_w: torch.Tensor, idx_k,
                   pool_blocks: torch.Tensor, pool_count: torch.Tensor,
                   topk_pos: Optional[torch.Tensor] = None, topk_count: Optional[torch.Tensor] = None,
                   topk_scores: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None,
-                  prepare: bool = False):
-    """Reindex inside the pool. Returns (topk_pos int32 [n_q, K], topk_count)."""
+                  prepare: bool = False, pages: Optional[Pages] = None):
+    """Reindex inside the pool. Returns (topk_pos int32 [n_q, K], topk_count).
+    With `pages` the keys are paged (csa2_index_reindex_paged)."""
     dev = _rows_dev(idx_k)
     _dev(pool_blocks, pool_count, topk_pos, topk_count, topk_scores)
     n_q = b.n_q
@@ -417,6 +460,17 @@ def index_reindex(dims: Dims, b: Batch, idx_q, idx_w: torch.Tensor, idx_k,
     args = (ctypes.byref(d), ctypes.byref(q), *qp, idx_w.data_ptr(), *kp, pool_blocks.data_ptr(),
             pool_count.data_ptr(), topk_pos.data_ptr(), topk_count.data_ptr(), _ptr(topk_scores), wp, wn,
             _stream(dev))
+    if pages is not None:
+        krows = idx_k[0].shape[0] if fp4 else idx_k.shape[0]
+        if pages.rows > krows:
+            raise ValueError(f"pages.rows ({pages.rows}) exceeds the key planes' {krows} rows")
+        pg = pages.c()
+        qs, ks = (qp[1], kp[1]) if fp4 else (None, None)
+        args = (ctypes.byref(d), ctypes.byref(q), ctypes.byref(pg), qp[0], qs, idx_w.data_ptr(), kp[0], ks,
+                pool_blocks.data_ptr(), pool_count.data_ptr(), topk_pos.data_ptr(), topk_count.data_ptr(),
+                _ptr(topk_scores), wp, wn, _stream(dev))
+        call = _issue(lib().csa2_index_reindex_paged, args, (d, q, pg, ws, pages.table), prepare)
+        return call if prepare else (topk_pos, topk_count)
     fn = lib().csa2_index_reindex_fp4 if fp4 else lib().csa2_index_reindex
     call = _issue(fn, args, (d, q, ws), prepare)
     return call if prepare else (topk_pos, topk_count)
@@ -426,8 +480,10 @@ def attend(dims: Dims, b: Batch, q_lat: torch.Tensor, q_rope: torch.Tensor, soft
            kv_codes: torch.Tensor, kv_scales: torch.Tensor, kv_rope: torch.Tensor,
            topk_pos: torch.Tensor, topk_count: torch.Tensor, swa_kv: torch.Tensor, swa_base: torch.Tensor,
            out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-           ws: Optional[torch.Tensor] = None, want_lse: bool = True, prepare: bool = False):
-    """Sparse FP4 + window attention. Returns (out f32 [n_q, H, 512], lse)."""
+           ws: Optional[torch.Tensor] = None, want_lse: bool = True, prepare: bool = False,
+           pages: Optional[Pages] = None):
+    """Sparse FP4 + window attention. Returns (out f32 [n_q, H, 512], lse).
+    With `pages` the main-KV planes are paged (csa2_attend_paged)."""
     dev = q_lat.device
     _dev(q_lat, q_rope, kv_codes, kv_scales, kv_rope, topk_pos, topk_count, swa_kv, swa_base, out, lse)
     n_q, H = b.n_q, dims.n_heads
@@ -450,6 +506,13 @@ def attend(dims: Dims, b: Batch, q_lat: torch.Tensor, q_rope: torch.Tensor, soft
             float(softmax_scale), kv_codes.data_ptr(), kv_scales.data_ptr(), kv_rope.data_ptr(),
             topk_pos.data_ptr(), topk_count.data_ptr(), swa_kv.data_ptr(), swa_base.data_ptr(),
             out.data_ptr(), _ptr(lse), wp, wn, _stream(dev))
+    if pages is not None:
+        if pages.rows > min(kv_codes.shape[0], kv_scales.shape[0], kv_rope.shape[0]):
+            raise ValueError(f"pages.rows ({pages.rows}) exceeds the main-KV planes' rows")
+        pg = pages.c()
+        call = _issue(lib().csa2_attend_paged, args[:2] + (ctypes.byref(pg),) + args[2:], (d, q, pg, ws, pages.table),
+                      prepare)
+        return call if prepare else (out, lse)
     call = _issue(lib().csa2_attend, args, (d, q, ws), prepare)
     return call if prepare else (out, lse)
 

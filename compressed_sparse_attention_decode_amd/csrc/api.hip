@@ -84,6 +84,25 @@ csa2_status check_queries(const csa2_queries* q) {
   return CSA2_OK;
 }
 
+// Paged planes: the page table, a power-of-two page, and planes whose byte
+// offsets (rows x the widest plane's row bytes) stay inside one 32-bit
+// buffer range, as the gathers address them.
+csa2_status check_pages(const csa2_pages* p, int64_t row_bytes) {
+  if (!p || !p->table) return fail(CSA2_ERR_INVALID_ARG, "pages / pages->table is NULL");
+  if (p->reserved != 0) return fail(CSA2_ERR_INVALID_ARG, "pages->reserved must be 0");
+  if (p->page_size < 16 || p->page_size > 65536 || (p->page_size & (p->page_size - 1)))
+    return fail(CSA2_ERR_INVALID_ARG, "page_size must be a power of two in [16, 65536] (got %d)", p->page_size);
+  if (p->rows < 1 || p->rows % p->page_size)
+    return fail(CSA2_ERR_INVALID_ARG, "pages->rows must be a positive multiple of page_size (got %lld)",
+                (long long)p->rows);
+  if (p->rows > (int64_t)0xFFFFFF00 / row_bytes)
+    return fail(CSA2_ERR_INVALID_ARG, "paged planes of %lld rows x %lld bytes exceed the 4 GiB gather range",
+                (long long)p->rows, (long long)row_bytes);
+  return CSA2_OK;
+}
+
+int page_shift(const csa2_pages* p) { return __builtin_ctz((unsigned)p->page_size); }
+
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 int64_t max_blocks(const csa2_dims* d, const csa2_queries* q) {
@@ -455,11 +474,12 @@ static csa2_status index_reindex(const csa2_dims* d, const csa2_queries* q, cons
                                  const float* idx_w, const uint8_t* idx_k, const uint8_t* k_scales, bool fp4,
                                  const int32_t* pool_blocks, const int32_t* pool_count, int32_t* topk_pos,
                                  int32_t* topk_count, float* topk_scores, void* ws, size_t ws_bytes, void* stream,
-                                 bool dry = false) {
+                                 bool dry = false, const csa2_pages* pages = nullptr) {
   csa2_status st = check_dims(d);
   if (st) return st;
   if ((st = check_queries(q))) return st;
   if ((st = check_index_rows(d, idx_q, q_scales, idx_w, idx_k, k_scales, fp4))) return st;
+  if (pages && (st = check_pages(pages, fp4 ? d->idx_dim / 2 : d->idx_dim))) return st;
   if (!pool_blocks || !pool_count || !topk_pos || !topk_count)
     return fail(CSA2_ERR_INVALID_ARG, "required pointer is NULL");
   if ((st = check_ws(ws, ws_bytes, reindex_ws(d, q)))) return st;
@@ -477,6 +497,9 @@ static csa2_status index_reindex(const csa2_dims* d, const csa2_queries* q, cons
   ra.done = (uint32_t*)ws;
   ra.keys = (uint32_t*)((char*)ws + align256((size_t)q->n_q * 4));
   ra.topk_pos = topk_pos; ra.topk_count = topk_count; ra.topk_scores = topk_scores;
+  ra.pages = pages ? pages->table : nullptr;
+  ra.page_shift = pages ? page_shift(pages) : 0;
+  ra.rows = pages ? pages->rows : 0;
   hipError_t e = launch_reindex(ra, (hipStream_t)stream);
   return e == hipSuccess ? CSA2_OK : hip_fail(e, "reindex launch");
 }
@@ -498,6 +521,18 @@ csa2_status csa2_index_reindex_fp4(const csa2_dims* d, const csa2_queries* q, co
                        topk_count, topk_scores, ws, ws_bytes, stream);
 }
 
+csa2_status csa2_index_reindex_paged(const csa2_dims* d, const csa2_queries* q, const csa2_pages* pages,
+                                     const uint8_t* idx_q, const uint8_t* idx_q_scales, const float* idx_w,
+                                     const uint8_t* idx_k, const uint8_t* idx_k_scales, const int32_t* pool_blocks,
+                                     const int32_t* pool_count, int32_t* topk_pos, int32_t* topk_count,
+                                     float* topk_scores, void* ws, size_t ws_bytes, void* stream) {
+  if ((idx_q_scales == nullptr) != (idx_k_scales == nullptr))
+    return fail(CSA2_ERR_INVALID_ARG, "idx_q_scales and idx_k_scales must both be given (FP4 rows) or both NULL");
+  if (!pages) return fail(CSA2_ERR_INVALID_ARG, "pages is NULL");
+  return index_reindex(d, q, idx_q, idx_q_scales, idx_w, idx_k, idx_k_scales, idx_q_scales != nullptr, pool_blocks,
+                       pool_count, topk_pos, topk_count, topk_scores, ws, ws_bytes, stream, false, pages);
+}
+
 csa2_status csa2_attend_workspace_size(const csa2_dims* d, const csa2_queries* q, size_t* bytes) {
   csa2_status st = check_dims(d);
   if (st) return st;
@@ -511,10 +546,11 @@ static csa2_status attend(const csa2_dims* d, const csa2_queries* q, const uint1
                           float softmax_scale, const uint8_t* kv_codes, const uint8_t* kv_scales,
                           const uint16_t* kv_rope, const int32_t* topk_pos, const int32_t* topk_count,
                           const uint16_t* swa_kv, const int64_t* swa_base, float* out, float* lse, void* ws,
-                          size_t ws_bytes, void* stream, bool dry = false) {
+                          size_t ws_bytes, void* stream, bool dry = false, const csa2_pages* pages = nullptr) {
   csa2_status st = check_dims(d);
   if (st) return st;
   if ((st = check_queries(q))) return st;
+  if (pages && (st = check_pages(pages, 256))) return st;   // kv_codes: the widest plane
   if (!q_lat || !q_rope || !kv_codes || !kv_scales || !kv_rope || !topk_pos || !topk_count || !swa_base || !out)
     return fail(CSA2_ERR_INVALID_ARG, "required pointer is NULL");
   if (!swa_kv && d->swa > 0) return fail(CSA2_ERR_INVALID_ARG, "swa_kv is NULL");
@@ -536,6 +572,9 @@ static csa2_status attend(const csa2_dims* d, const csa2_queries* q, const uint1
   aa.n_q = q->n_q; aa.heads = d->n_heads; aa.topk = d->topk; aa.swa = d->swa;
   aa.head_groups = p.hg; aa.splits = p.splits; aa.split_entries = p.split_entries;
   aa.out = out; aa.lse = lse;
+  aa.pages = pages ? pages->table : nullptr;
+  aa.page_shift = pages ? page_shift(pages) : 0;
+  aa.rows = pages ? pages->rows : 0;
   if (p.splits > 1) {
     const size_t rows = (size_t)q->n_q * p.splits * d->n_heads;
     aa.part_o = (float*)ws;
@@ -555,6 +594,28 @@ csa2_status csa2_attend(const csa2_dims* d, const csa2_queries* q, const uint16_
                         size_t ws_bytes, void* stream) {
   return attend(d, q, q_lat, q_rope, softmax_scale, kv_codes, kv_scales, kv_rope, topk_pos, topk_count, swa_kv,
                 swa_base, out, lse, ws, ws_bytes, stream);
+}
+
+csa2_status csa2_attend_paged(const csa2_dims* d, const csa2_queries* q, const csa2_pages* pages,
+                              const uint16_t* q_lat, const uint16_t* q_rope, float softmax_scale,
+                              const uint8_t* kv_codes, const uint8_t* kv_scales, const uint16_t* kv_rope,
+                              const int32_t* topk_pos, const int32_t* topk_count, const uint16_t* swa_kv,
+                              const int64_t* swa_base, float* out, float* lse, void* ws, size_t ws_bytes,
+                              void* stream) {
+  if (!pages) return fail(CSA2_ERR_INVALID_ARG, "pages is NULL");
+  return attend(d, q, q_lat, q_rope, softmax_scale, kv_codes, kv_scales, kv_rope, topk_pos, topk_count, swa_kv,
+                swa_base, out, lse, ws, ws_bytes, stream, false, pages);
+}
+
+csa2_status csa2_page_rows(const csa2_pages* pages, int64_t n, const int64_t* table_off, const int32_t* pos,
+                           int64_t* dst_row, void* stream) {
+  csa2_status st = check_pages(pages, 1);
+  if (st) return st;
+  if (n < 0) return fail(CSA2_ERR_INVALID_ARG, "n must be >= 0");
+  if (n > 0 && (!table_off || !pos || !dst_row)) return fail(CSA2_ERR_INVALID_ARG, "required pointer is NULL");
+  if ((st = check_device())) return st;
+  hipError_t e = launch_page_rows(n, pages->table, page_shift(pages), table_off, pos, dst_row, (hipStream_t)stream);
+  return e == hipSuccess ? CSA2_OK : hip_fail(e, "page rows launch");
 }
 
 // The layer step's workspace: the Full index's (pool + block scores), then

@@ -245,7 +245,21 @@ __global__ __launch_bounds__(kNT) void k_attend(AttendArgs a) {
   const int Es = min(load_uniform(a.topk_count + q), a.topk);
   const int E = Es + (n - c);
   const int e_end = min(E, e_begin + a.split_entries);
-  const TileSrc src = tile_src(a, load_uniform(a.seq_base + q), load_uniform(a.swa_base + q), n, n - c);
+  const int64_t sbase = load_uniform(a.seq_base + q);
+  // paged main KV: the kept positions become rows of the whole planes (one
+  // page id per position, loaded unconditionally from a clamped slot)
+  const bool paged = a.pages != nullptr;
+  if (paged && c > 0) {
+    int32_t pg[kRowPer];
+#pragma unroll
+    for (int j = 0; j < kRowPer; ++j) pg[j] = a.pages[sbase + (min(max(tkv[j], 0), c - 1) >> a.page_shift)];
+#pragma unroll
+    for (int j = 0; j < kRowPer; ++j) asm volatile("" : "+v"(pg[j]));
+#pragma unroll
+    for (int j = 0; j < kRowPer; ++j)
+      tkv[j] = (int32_t)(((uint32_t)pg[j] << a.page_shift) | ((uint32_t)tkv[j] & ((1u << a.page_shift) - 1u)));
+  }
+  const TileSrc src = tile_src(a, paged ? 0 : sbase, load_uniform(a.swa_base + q), paged ? (int)a.rows : n, n - c);
 
   {
     // the split's kept positions: the row always holds `topk` entries, so

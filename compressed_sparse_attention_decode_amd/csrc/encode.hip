@@ -123,7 +123,26 @@ __global__ __launch_bounds__(256) void k_encode_rows(int64_t n, int lg, const ui
   scales[row * groups + g] = (uint8_t)S;
 }
 
+// Rows of (sequence, position) pairs in paged planes: entry i is position
+// pos[i] of the sequence whose page-table row starts at table_off[i].
+__global__ __launch_bounds__(256) void k_page_rows(int64_t n, const int32_t* pages, int shift,
+                                                   const int64_t* table_off, const int32_t* pos, int64_t* dst_row) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  const int32_t p = pos[i];
+  const int64_t page = pages[table_off[i] + (p >> shift)];
+  dst_row[i] = (page << shift) | (p & ((1 << shift) - 1));
+}
+
 }  // namespace
+
+hipError_t launch_page_rows(int64_t n, const int32_t* pages, int page_shift, const int64_t* table_off,
+                            const int32_t* pos, int64_t* dst_row, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_page_rows, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, n, pages, page_shift,
+                     table_off, pos, dst_row);
+  return hipGetLastError();
+}
 
 hipError_t launch_encode_rows(int64_t n, int width, const uint16_t* src, const int64_t* dst_row,
                               uint8_t* codes, uint8_t* scales, hipStream_t s) {

@@ -45,6 +45,12 @@ struct ReindexArgs {
   int32_t* topk_pos;
   int32_t* topk_count;
   float* topk_scores;        // optional
+  // paged caches (nullptr: position p of query q's sequence is row
+  // seq_base[q] + p): it is row (pages[seq_base[q] + (p >> page_shift)] <<
+  // page_shift) + (p mod 2^page_shift) of planes of `rows` rows
+  const int32_t* pages;
+  int page_shift;
+  int64_t rows;
 };
 
 struct AttendArgs {
@@ -69,6 +75,9 @@ struct AttendArgs {
   float* lse;                // optional [n_q, H]
   float* part_o;             // [n_q, splits, H, 512] when splits > 1
   float* part_ml;            // [n_q, splits, H, 2]
+  const int32_t* pages;      // paged main-KV planes (as ReindexArgs; the window stays apart)
+  int page_shift;
+  int64_t rows;
 };
 
 hipError_t launch_encode(int64_t n, int group, const uint16_t* latent, const uint16_t* rope,
@@ -76,6 +85,8 @@ hipError_t launch_encode(int64_t n, int group, const uint16_t* latent, const uin
                          uint16_t* rope_out, hipStream_t s);
 hipError_t launch_encode_rows(int64_t n, int width, const uint16_t* src, const int64_t* dst_row,
                               uint8_t* codes, uint8_t* scales, hipStream_t s);
+hipError_t launch_page_rows(int64_t n, const int32_t* pages, int page_shift, const int64_t* table_off,
+                            const int32_t* pos, int64_t* dst_row, hipStream_t s);
 hipError_t launch_pool_select(const PoolArgs& a, hipStream_t s);
 int64_t pool_ws_words(int chunks, int mm_cap);   // workspace words per query
 hipError_t launch_reindex(const ReindexArgs& a, hipStream_t s);

@@ -32,6 +32,9 @@
 namespace csa2 {
 namespace {
 
+constexpr uint32_t kNoKeyRow = 0xFFFFFFFFu;   // a lane with no candidate position (paged rows)
+constexpr uint32_t kNoKeyOff = 0xFFFFFF00u;   // a buffer offset past any plane: reads zero
+
 // Scores of pool slots [i_begin, i_begin + kReindexBlocks) of query q (8
 // positions per slot) as order keys.  Slots past the pool count are scored
 // too, from whatever block ids the row holds there (clamped to a zero key
@@ -71,18 +74,43 @@ __device__ __forceinline__ void score_part(const ReindexArgs& a, int q, int part
   }
   // every key load in flight at once (a position >= c reads zeros)
   const int64_t sbase = load_uniform(a.seq_base + q);
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.idx_k + sbase * RB, (uint32_t)c * RB);
-  const __amdgpu_buffer_rsrc_t rks = make_rsrc(F4 ? a.idx_k_scales + sbase * SB : a.idx_k, (uint32_t)c * SB);
+#pragma unroll
+  for (int u = 0; u < SPW; ++u) {
+    if (pos[u] > c || pos[u] < 0) pos[u] = c;
+  }
+  // the lane's key row: seq_base + p, or through the page table (one page id
+  // per position, all loaded unconditionally from clamped slots before the
+  // first use; a position with no candidate reads past the plane, zeros)
+  uint32_t row[SPW];
+  const bool paged = a.pages != nullptr;
+  if (paged && c > 0) {
+    int32_t pg[SPW];
+    const uint32_t pmask = (1u << a.page_shift) - 1u;
+#pragma unroll
+    for (int u = 0; u < SPW; ++u) pg[u] = a.pages[sbase + (min(pos[u], c - 1) >> a.page_shift)];
+#pragma unroll
+    for (int u = 0; u < SPW; ++u) asm volatile("" : "+v"(pg[u]));
+#pragma unroll
+    for (int u = 0; u < SPW; ++u)
+      row[u] = pos[u] < c ? ((uint32_t)pg[u] << a.page_shift) | ((uint32_t)pos[u] & pmask) : kNoKeyRow;
+  } else {
+#pragma unroll
+    for (int u = 0; u < SPW; ++u) row[u] = paged ? kNoKeyRow : (uint32_t)pos[u];
+  }
+  const int64_t kbase = paged ? 0 : sbase;
+  const uint32_t krows = paged ? (uint32_t)a.rows : (uint32_t)c;
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.idx_k + kbase * RB, krows * RB);
+  const __amdgpu_buffer_rsrc_t rks = make_rsrc(F4 ? a.idx_k_scales + kbase * SB : a.idx_k, krows * SB);
   uint32_t kb[SPW][LB / 4];
   uint32_t ksw[SPW];                               // FP4: the dword holding the lane's two scales
 #pragma unroll
   for (int u = 0; u < SPW; ++u) {
-    if (pos[u] > c || pos[u] < 0) pos[u] = c;
-    const uint32_t off = (uint32_t)pos[u] * RB + gq * LB;
+    const uint32_t off = row[u] == kNoKeyRow ? kNoKeyOff : row[u] * RB + gq * LB;
     const v4u x = buf_load16(rk, off);
     kb[u][0] = x[0]; kb[u][1] = x[1]; kb[u][2] = x[2]; kb[u][3] = x[3];
     if constexpr (F4) {
-      ksw[u] = __builtin_amdgcn_raw_buffer_load_b32(rks, (uint32_t)pos[u] * SB + (gq >> 1) * 4, 0, 0);
+      ksw[u] = __builtin_amdgcn_raw_buffer_load_b32(
+          rks, row[u] == kNoKeyRow ? kNoKeyOff : row[u] * SB + (gq >> 1) * 4, 0, 0);
     } else if constexpr (LB == 32) {
       const v4u y = buf_load16(rk, off + 16);
       kb[u][4] = y[0]; kb[u][5] = y[1]; kb[u][6] = y[2]; kb[u][7] = y[3];

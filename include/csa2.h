@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define CSA2_ABI_VERSION 2
+#define CSA2_ABI_VERSION 3
 
 typedef enum csa2_status {
   CSA2_OK = 0,
@@ -113,6 +113,32 @@ typedef struct csa2_queries {
   const int64_t* seq_base;
   const int32_t* n_visible;
 } csa2_queries;
+
+/* Paged caches (serving integration: the pages' stack appends each new
+ * token's main KV as a Full layer runs — [atlas] §3.2 mode table, "Full
+ * writes main KV" — and a serving cache grows page by page).  In a call that
+ * takes a csa2_pages, position p of query q's sequence lives at row
+ *   table[seq_base[q] + p / page_size] * page_size + p % page_size
+ * of every per-position plane the call reads (indexer keys and their scales;
+ * kv_codes, kv_scales, kv_rope); seq_base[q] is then the offset in `table`
+ * of the sequence's first page, not a row.  The window rows (swa_kv,
+ * swa_base) are unchanged.
+ *   table      device int32: physical page ids; entries for the pages that
+ *              hold positions [0, n) of each query must be valid (< rows /
+ *              page_size).  Caller-owned, read only.
+ *   page_size  positions per page: a power of two in [16, 65536].
+ *   reserved   must be 0.
+ *   rows       rows of each plane the call reads (a multiple of page_size).
+ *              The gathers address a plane with 32-bit byte offsets, so rows x
+ *              the widest plane's row bytes (256 for kv_codes, d_i for fp8
+ *              keys, d_i / 2 for FP4 key codes) must stay below 2^32 - 256:
+ *              CSA2_ERR_INVALID_ARG otherwise. */
+typedef struct csa2_pages {
+  const int32_t* table;
+  int32_t page_size;
+  int32_t reserved;
+  int64_t rows;
+} csa2_pages;
 
 /* ABI version of the loaded library (CSA2_ABI_VERSION). */
 int32_t csa2_abi_version(void);
@@ -326,6 +352,39 @@ csa2_status csa2_attend(const csa2_dims* dims, const csa2_queries* q,
                         const int32_t* topk_pos, const int32_t* topk_count,
                         const uint16_t* swa_kv, const int64_t* swa_base,
                         float* out, float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/* csa2_index_reindex over paged indexer keys (see csa2_pages): the same
+ * selection from the same scores.  FP4 indexer rows when idx_q_scales and
+ * idx_k_scales are both given (as csa2_index_reindex_fp4), fp8 when both are
+ * NULL.  Same workspace as csa2_index_reindex.  One extra dependent load per
+ * pool position (its page id) before the key gather. */
+csa2_status csa2_index_reindex_paged(const csa2_dims* dims, const csa2_queries* q, const csa2_pages* pages,
+                                     const uint8_t* idx_q, const uint8_t* idx_q_scales, const float* idx_w,
+                                     const uint8_t* idx_k, const uint8_t* idx_k_scales,
+                                     const int32_t* pool_blocks, const int32_t* pool_count,
+                                     int32_t* topk_pos, int32_t* topk_count, float* topk_scores,
+                                     void* ws, size_t ws_bytes, void* stream);
+
+/* csa2_attend over paged main-KV planes (see csa2_pages): the same outputs
+ * from the same entries; the kept positions are turned into rows (one page
+ * id load each) before the FP4 gather.  The window rows come from swa_kv at
+ * swa_base as in csa2_attend.  Same workspace as csa2_attend. */
+csa2_status csa2_attend_paged(const csa2_dims* dims, const csa2_queries* q, const csa2_pages* pages,
+                              const uint16_t* q_lat, const uint16_t* q_rope, float softmax_scale,
+                              const uint8_t* kv_codes, const uint8_t* kv_scales, const uint16_t* kv_rope,
+                              const int32_t* topk_pos, const int32_t* topk_count,
+                              const uint16_t* swa_kv, const int64_t* swa_base,
+                              float* out, float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/* Rows of paged positions, so that csa2_encode_kv (through dst_row) appends
+ * new entries into their pages:
+ *   dst_row[i] = table[table_off[i] + pos[i] / page_size] * page_size
+ *                + pos[i] % page_size
+ *   table_off  device int64 [n]   pos  device int32 [n] (>= 0)
+ *   dst_row    device int64 [n]   (output)
+ * One kernel. */
+csa2_status csa2_page_rows(const csa2_pages* pages, int64_t n, const int64_t* table_off, const int32_t* pos,
+                           int64_t* dst_row, void* stream);
 
 /* One decode layer in one call ([atlas] §3.2 mode table: a Full layer
  * scores the whole context and takes a new index set, a Reindex layer

@@ -30,7 +30,8 @@ def test_header_declares_the_entry_points():
     for n in ("csa2_encode_kv", "csa2_encode_kv_grouped", "csa2_index_full", "csa2_index_reindex", "csa2_attend",
               "csa2_index_scan", "csa2_index_pool", "csa2_status_string", "csa2_abi_version",
               "csa2_encode_fp4", "csa2_index_scan_fp4", "csa2_index_full_fp4", "csa2_index_reindex_fp4",
-              "csa2_decode_step", "csa2_decode_step_workspace_size"):
+              "csa2_decode_step", "csa2_decode_step_workspace_size", "csa2_index_reindex_paged",
+              "csa2_attend_paged", "csa2_page_rows"):
         assert n in names
 
 
@@ -44,7 +45,7 @@ def test_abi_version_and_status_strings():
     L = csa2.lib()
     # the header's version, which the library was built from
     want = int(re.search(r"#define CSA2_ABI_VERSION (\d+)", open(HEADER).read()).group(1))
-    assert L.csa2_abi_version() == want == 2
+    assert L.csa2_abi_version() == want == 3
     for st in (OK, INVALID, UNSUPPORTED, WORKSPACE, HIP):
         assert L.csa2_status_string(st)
     assert L.csa2_status_string(99)          # unknown codes still get text
@@ -159,6 +160,45 @@ def test_fp4_indexer_calls_rejected_before_any_device_work():
     assert L.csa2_encode_fp4(-1, 128, None, None, None, None, None) == INVALID
     assert L.csa2_encode_fp4(4, 128, None, None, 0x2000, 0x3000, None) == INVALID
     assert L.csa2_encode_fp4(0, 128, None, None, None, None, None) in (OK, INVALID)
+
+
+def test_paged_calls_rejected_before_any_device_work():
+    """Page descriptors are checked on the host: a power-of-two page of 16 to
+    65536 positions, rows a multiple of it, and planes inside the gathers'
+    32-bit byte range (256 B per row for the main-KV codes, d_i for fp8 keys)."""
+    L = csa2.lib()
+    d, q = _dims().c(), _batch().c()
+
+    def attend(pg):
+        return L.csa2_attend_paged(ctypes.byref(d), ctypes.byref(q), pg, 0x1000, 0x2000, 1.0, 0x3000, 0x4000,
+                                   0x5000, 0x6000, 0x7000, 0x8000, 0x9000, 0xA000, None, 0xB000, 1 << 30, None)
+
+    def reindex(pg):
+        return L.csa2_index_reindex_paged(ctypes.byref(d), ctypes.byref(q), pg, 0x1000, None, 0x2000, 0x3000, None,
+                                          0x4000, 0x5000, 0x6000, 0x7000, None, 0x8000, 1 << 30, None)
+
+    assert attend(None) == INVALID and b"pages" in L.csa2_last_error()
+    bad = [csa2._Pages(None, 64, 0, 1 << 10),          # no table
+           csa2._Pages(0x1000, 48, 0, 1 << 10),        # not a power of two
+           csa2._Pages(0x1000, 8, 0, 1 << 10),         # below 16
+           csa2._Pages(0x1000, 1 << 17, 0, 1 << 17),   # above 65536
+           csa2._Pages(0x1000, 64, 1, 1 << 10),        # reserved
+           csa2._Pages(0x1000, 64, 0, 1000),           # rows not a multiple of the page
+           csa2._Pages(0x1000, 64, 0, 0)]              # no rows
+    for pg in bad:
+        assert attend(ctypes.byref(pg)) == INVALID
+        assert reindex(ctypes.byref(pg)) == INVALID
+        assert L.csa2_page_rows(ctypes.byref(pg), 4, 0x1000, 0x2000, 0x3000, None) == INVALID
+    # 2^24 rows: 4 GiB of 256-byte main-KV code rows is past the range, while
+    # 128-byte fp8 key rows still fit
+    big = csa2._Pages(0x1000, 64, 0, 1 << 24)
+    assert attend(ctypes.byref(big)) == INVALID and b"4 GiB" in L.csa2_last_error()
+    # (a NULL pool stops this call after the page check, before any launch)
+    st = L.csa2_index_reindex_paged(ctypes.byref(d), ctypes.byref(q), ctypes.byref(big), 0x1000, None, 0x2000,
+                                    0x3000, None, None, 0x5000, 0x6000, 0x7000, None, 0x8000, 1 << 30, None)
+    assert st == INVALID and b"NULL" in L.csa2_last_error()
+    ok = csa2._Pages(0x1000, 64, 0, 1 << 10)
+    assert L.csa2_page_rows(ctypes.byref(ok), -1, None, None, None, None) == INVALID
 
 
 def test_dims_struct_matches_header():

@@ -1,0 +1,156 @@
+"""GPU parity of the paged caches (csa2_pages): the same rows scattered into
+pages in a shuffled physical order give the contiguous path's outputs bit
+for bit (Reindex Top-K sets and scores, attention outputs and LSE), the
+contiguous path being the one checked against the oracle elsewhere; one
+query per case is also checked against the oracle directly.
+csa2_page_rows + csa2_encode_kv append fresh entries into their pages
+with the contiguous encoder's bytes."""
+import numpy as np
+import pytest
+import torch
+
+import workloads as wl
+from tests._harness import GpuCase, OracleQuery, check_attention, check_set
+from tests.test_gpu_parity import BIG, small
+
+pytestmark = pytest.mark.gpu
+
+CASES = {
+    "ragged_b3_p64": (small(201, BIG, [20005, 9003, 4099]), 64),
+    "fp4_ragged_b3_p256": (small(202, BIG, [20005, 9003, 4099], fp4=True), 256),
+    "edge_short_p16": (small(203, wl.Dims(n_heads=16, idx_heads=16, idx_dim=128, pool_blocks=4, topk=16),
+                             [0, 1, 100, 128, 129, 136, 137, 160]), 16),
+    "g4_p128": (small(204, BIG, [6001, 12345], g=4), 128),
+    "kvg32_p32": (small(205, wl.Dims(n_heads=32, idx_heads=8, idx_dim=64, pool_blocks=64, topk=128, kv_group=32),
+                        [7777, 3000]), 32),
+}
+
+
+class Paged:
+    """Every per-position plane of a case with each sequence's rows in pages
+    of `ps` positions at shuffled physical pages (with unused pages between
+    them), the page table, and a batch whose seq_base holds table offsets."""
+
+    def __init__(self, g, ps: int, seed: int):
+        csa2, lay, w = g.csa2, g.lay, g.w
+        rng = np.random.default_rng(seed)
+        npg = [-(-r // ps) for r in lay.seq_rows]
+        total = sum(npg) + 7                      # a few pages no sequence uses
+        perm = rng.permutation(total).astype(np.int32)
+        table, off, k = [], [], 0
+        for n in npg:
+            off.append(len(table))
+            table.extend(perm[k:k + n])
+            k += n
+        table.append(0)                           # a table of at least one entry
+        self.ps, self.rows = ps, total * ps
+        self.table = torch.tensor(np.asarray(table, np.int32), device=g.dev)
+        # physical row of every logical row of the flat layout
+        src, dst = [], []
+        for s, r in enumerate(lay.seq_rows):
+            p = np.arange(r, dtype=np.int64)
+            phys = np.asarray(table, np.int64)[off[s] + p // ps] * ps + p % ps
+            src.append(lay.seq_base[s] + p)
+            dst.append(phys)
+        src = torch.tensor(np.concatenate(src), device=g.dev)
+        dst = torch.tensor(np.concatenate(dst), device=g.dev)
+
+        def scatter(t):
+            out = torch.zeros((self.rows,) + tuple(t.shape[1:]), dtype=t.dtype, device=g.dev)
+            if len(src):
+                out.view(torch.uint8).view(self.rows, -1)[dst] = t.view(torch.uint8).view(t.shape[0], -1)[src]
+            return out
+
+        idx_k, codes, scales, kv_rope, _ = g.planes[0]
+        self.idx_k = tuple(scatter(x) for x in idx_k) if isinstance(idx_k, tuple) else scatter(idx_k)
+        self.codes, self.scales, self.kv_rope = scatter(codes), scatter(scales), scatter(kv_rope)
+        q_off = [off[qi // w.tokens_per_seq] for qi in range(w.n_q)]
+        self.batch = csa2.Batch(torch.tensor(q_off, dtype=torch.int64, device=g.dev), g.batch.n_visible,
+                                g.batch.max_visible, g.batch.tokens_per_seq)
+        self.pages = csa2.Pages(self.table, ps, self.rows)
+        self.seq_off = off
+
+
+@pytest.fixture(scope="module", params=list(CASES))
+def case(request):
+    w, ps = CASES[request.param]
+    g = GpuCase(w)
+    return request.param, g, Paged(g, ps, seed=ps + len(request.param))
+
+
+def test_paged_reindex_and_attention_match_contiguous(case):
+    name, g, pg = case
+    csa2, w = g.csa2, g.w
+    pool, cnt, _ = g.full(0)
+    q, wt = g.iq(0)
+    ts = torch.empty(w.n_q, w.dims.topk, dtype=torch.float32, device="cuda")
+    tk, tc = csa2.index_reindex(g.dims, g.batch, q, wt, g.planes[0][0], pool, cnt, topk_scores=ts)
+    ts2 = torch.empty_like(ts)
+    tk2, tc2 = csa2.index_reindex(g.dims, pg.batch, q, wt, pg.idx_k, pool, cnt, topk_scores=ts2, pages=pg.pages)
+    ql, qr = g.mq(0)
+    _, codes, scales, kv_rope, swa_kv = g.planes[0]
+    out, lse = csa2.attend(g.dims, g.batch, ql, qr, 1.0, codes, scales, kv_rope, tk, tc, swa_kv, g.swa_base)
+    out2, lse2 = csa2.attend(g.dims, pg.batch, ql, qr, 1.0, pg.codes, pg.scales, pg.kv_rope, tk, tc, swa_kv,
+                             g.swa_base, pages=pg.pages)
+    torch.cuda.synchronize()
+    assert torch.equal(tc2, tc), f"{name}: paged Top-K counts differ"
+    for qi in range(w.n_q):
+        k = int(tc[qi])
+        assert torch.equal(tk2[qi, :k], tk[qi, :k]), f"{name} q{qi}: paged Top-K differs"
+        assert torch.equal(ts2[qi, :k].view(torch.int32), ts[qi, :k].view(torch.int32)), \
+            f"{name} q{qi}: paged Top-K scores differ"
+    assert torch.equal(out2.view(torch.int32), out.view(torch.int32)), f"{name}: paged attention output differs"
+    assert torch.equal(lse2.view(torch.int32), lse.view(torch.int32)), f"{name}: paged LSE differs"
+
+    # the oracle, on the query with the longest context
+    qi = int(np.argmax(g.lay.q_visible))
+    oq = OracleQuery(w, g.lay, qi)
+    rpool, rb, _ = oq.full(0)
+    if np.array_equal(pool.cpu().numpy()[qi, :int(cnt[qi])], rpool):
+        keep, _, _ = oq.reindex(0, rpool)
+        got = tk2.cpu().numpy()[qi, :int(tc2[qi])]
+        check_set(got, keep, lambda x: oq.scores_at(0, x), f"{name} paged topk")
+        ref_o, ref_l = oq.attention(0, got)
+        check_attention(out2.cpu().numpy()[qi], lse2.cpu().numpy()[qi], ref_o, ref_l, f"{name} paged attention")
+
+
+def test_page_rows_append_into_pages(case):
+    """Fresh entries encoded at the rows csa2_page_rows gives land in their
+    pages byte for byte as the contiguous encoder writes them."""
+    name, g, pg = case
+    csa2, lay = g.csa2, g.lay
+    rng = np.random.default_rng(7)
+    seqs = [s for s, r in enumerate(lay.seq_rows) if r > 0]
+    if not seqs:
+        pytest.skip("no rows")
+    n = 300
+    s_of = rng.choice(seqs, n)
+    pos = np.array([rng.integers(0, lay.seq_rows[s]) for s in s_of], np.int32)
+    # one entry per (sequence, position): the writes must not overlap
+    _, keep = np.unique(s_of.astype(np.int64) * (1 << 32) + pos, return_index=True)
+    s_of, pos = s_of[keep], pos[keep]
+    table_off = torch.tensor([pg.seq_off[s] for s in s_of], dtype=torch.int64, device="cuda")
+    pos_t = torch.tensor(pos, device="cuda")
+    rows = csa2.page_rows(pg.pages, table_off, pos_t)
+    table = pg.table.cpu().numpy().astype(np.int64)
+    want = table[np.array([pg.seq_off[s] for s in s_of]) + pos // pg.ps] * pg.ps + pos % pg.ps
+    assert np.array_equal(rows.cpu().numpy(), want), f"{name}: page rows differ"
+    m = len(pos)
+    lat = wl.fresh_latent(g.w, 0, 0, m, "cuda")
+    rope = wl.fresh_rope(g.w, 0, 0, m, "cuda")
+    grp = g.w.dims.kv_group
+    codes = pg.codes.clone()
+    scales = pg.scales.clone()
+    kv_rope = pg.kv_rope.clone()
+    csa2.encode_kv(lat, rope, codes, scales, kv_rope, dst_row=rows, group=grp)
+    ref = (torch.zeros(m, 256, dtype=torch.uint8, device="cuda"),
+           torch.zeros(m, 512 // grp, dtype=torch.uint8, device="cuda"),
+           torch.zeros(m, 64, dtype=torch.bfloat16, device="cuda"))
+    csa2.encode_kv(lat, rope, *ref, group=grp)
+    torch.cuda.synchronize()
+    assert torch.equal(codes[rows], ref[0]), f"{name}: appended codes differ"
+    assert torch.equal(scales[rows], ref[1]), f"{name}: appended scales differ"
+    assert torch.equal(kv_rope[rows].view(torch.int16), ref[2].view(torch.int16)), f"{name}: appended rope differs"
+    untouched = torch.ones(pg.rows, dtype=torch.bool, device="cuda")
+    untouched[rows] = False
+    assert torch.equal(codes[untouched], pg.codes[untouched]), f"{name}: rows outside the appended ones changed"
