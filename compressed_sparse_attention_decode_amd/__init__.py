@@ -90,6 +90,9 @@ def lib() -> ctypes.CDLL:
             "csa2_index_reindex_paged": (I32, [PD, PQ, PP, P, P, P, P, P, P, P, P, P, P, P, SZ, P]),
             "csa2_attend_paged": (I32, [PD, PQ, PP, P, P, ctypes.c_float, P, P, P, P, P, P, P, P, P, P, SZ, P]),
             "csa2_page_rows": (I32, [PP, I64, P, P, P, P]),
+            "csa2_index_full_paged": (I32, [PD, PQ, PP, P, P, P, P, P, P, P, P, I64, P, SZ, P]),
+            "csa2_decode_step_paged": (I32, [PD, PQ, PP, I32, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_float,
+                                             P, P, P, P, P, P, P, P, SZ, P]),
             "csa2_decode_step_workspace_size": (I32, [PD, PQ, ctypes.POINTER(SZ)]),
             "csa2_decode_step": (I32, [PD, PQ, I32, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_float,
                                        P, P, P, P, P, P, P, P, SZ, P]),
@@ -186,6 +189,12 @@ class Pages:
             raise TypeError("the page table must be contiguous int32")
         _dev(self.table)
         return _Pages(self.table.data_ptr(), self.page_size, 0, self.rows)
+
+
+def _check_page_rows(pages: Pages, *planes: torch.Tensor):
+    rows = min(t.shape[0] for t in planes)
+    if pages.rows > rows:
+        raise ValueError(f"pages.rows ({pages.rows}) exceeds the planes' {rows} rows")
 
 
 def page_rows(pages: Pages, table_off: torch.Tensor, pos: torch.Tensor,
@@ -348,11 +357,12 @@ def _check_idx(dims: Dims, b: Batch, idx_q, idx_w, idx_k):
 
 def index_full(dims: Dims, b: Batch, idx_q, idx_w: torch.Tensor, idx_k,
                pool_blocks: Optional[torch.Tensor] = None, pool_count: Optional[torch.Tensor] = None,
-               block_scores: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None
-               ) -> Tuple[torch.Tensor, torch.Tensor]:
+               block_scores: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None,
+               pages: Optional[Pages] = None) -> Tuple[torch.Tensor, torch.Tensor]:
     """Full-mode indexer. idx_q fp8 [n_q, H_i, d_i] (or an FP4 pair),
     idx_w f32 [n_q, H_i], idx_k fp8 [rows, d_i] (or an FP4 pair).  Returns
-    (pool_blocks int32 [n_q, P], pool_count)."""
+    (pool_blocks int32 [n_q, P], pool_count).  With `pages` the keys are
+    paged (csa2_index_full_paged)."""
     dev = _rows_dev(idx_k)
     _dev(pool_blocks, pool_count, block_scores)
     n_q = b.n_q
@@ -369,6 +379,14 @@ def index_full(dims: Dims, b: Batch, idx_q, idx_w: torch.Tensor, idx_k,
     ws = _workspace(workspace_full(dims, b), dev, ws)
     wp, wn = _ws_ptr(ws)
     d, q = dims.c(), b.c()
+    if pages is not None:
+        _check_page_rows(pages, idx_k[0] if fp4 else idx_k)
+        pg = pages.c()
+        qs, ks = (qp[1], kp[1]) if fp4 else (None, None)
+        _check(lib().csa2_index_full_paged(ctypes.byref(d), ctypes.byref(q), ctypes.byref(pg), qp[0], qs,
+                                           idx_w.data_ptr(), kp[0], ks, pool_blocks.data_ptr(),
+                                           pool_count.data_ptr(), _ptr(block_scores), ld, wp, wn, _stream(dev)))
+        return pool_blocks, pool_count
     fn = lib().csa2_index_full_fp4 if fp4 else lib().csa2_index_full
     _check(fn(ctypes.byref(d), ctypes.byref(q), *qp, idx_w.data_ptr(), *kp, pool_blocks.data_ptr(),
               pool_count.data_ptr(), _ptr(block_scores), ld, wp, wn, _stream(dev)))
@@ -526,8 +544,9 @@ def decode_step(dims: Dims, b: Batch, mode: int, idx_q, idx_w, idx_k,
                 q_lat: torch.Tensor, q_rope: torch.Tensor, softmax_scale: float,
                 kv_codes: torch.Tensor, kv_scales: torch.Tensor, kv_rope: torch.Tensor,
                 swa_kv: torch.Tensor, swa_base: torch.Tensor, out: torch.Tensor,
-                lse: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None, prepare: bool = False):
-    """One decode layer (csa2_decode_step): LAYER_FULL writes the pool and the
+                lse: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None, prepare: bool = False,
+                pages: Optional[Pages] = None):
+    """One decode layer (csa2_decode_step; csa2_decode_step_paged with `pages`): LAYER_FULL writes the pool and the
     Top-K and attends; LAYER_REINDEX reads the pool, writes the Top-K and
     attends; LAYER_REUSE attends over the given Top-K.  Indexer rows as for
     index_full (None allowed for LAYER_REUSE).  `ws` must come from a
@@ -561,4 +580,12 @@ def decode_step(dims: Dims, b: Batch, mode: int, idx_q, idx_w, idx_k,
             pool_count.data_ptr(), topk_pos.data_ptr(), topk_count.data_ptr(), q_lat.data_ptr(), q_rope.data_ptr(),
             float(softmax_scale), kv_codes.data_ptr(), kv_scales.data_ptr(), kv_rope.data_ptr(), swa_kv.data_ptr(),
             swa_base.data_ptr(), out.data_ptr(), _ptr(lse), wsp, wn, _stream(dev))
+    if pages is not None:
+        planes = [kv_codes, kv_scales, kv_rope]
+        if idx_k is not None:
+            planes += list(idx_k) if isinstance(idx_k, tuple) else [idx_k]
+        _check_page_rows(pages, *planes)
+        pg = pages.c()
+        return _issue(lib().csa2_decode_step_paged, args[:2] + (ctypes.byref(pg),) + args[2:],
+                      (d, q, pg, ws, pages.table), prepare)
     return _issue(lib().csa2_decode_step, args, (d, q, ws), prepare)

@@ -146,7 +146,7 @@ int scan_tile_extra(const csa2_dims* d, const csa2_queries* q, int tile, int til
   const int64_t units = ((int64_t)(q->n_q / q->tokens_per_seq) * tiles + 7) / 8 * 8;
   int extra = units * q->tokens_per_seq <= 2 * (int64_t)g_cus[dev] ? kScanTileExtra : 0;
   if (const char* env = getenv("CSA2_SCAN_SPLIT")) extra = atoi(env);
-  if (extra < 0 || extra % 8 || extra >= tile || tile + extra > 4096 || (tiles & 1)) extra = 0;
+  if (extra < 0 || extra % 16 || extra >= tile || tile + extra > 4096 || (tiles & 1)) extra = 0;
   return extra;
 }
 
@@ -293,7 +293,8 @@ static csa2_status check_block_scores(const csa2_dims* d, const csa2_queries* q,
 // cleared histogram for the pool select.
 static csa2_status run_scan(const csa2_dims* d, const csa2_queries* q, const uint8_t* idx_q, const uint8_t* q_scales,
                             const float* idx_w, const uint8_t* idx_k, const uint8_t* k_scales, float* block_scores,
-                            int64_t ld_block_scores, uint32_t* pool_ws_ptr, void* stream) {
+                            int64_t ld_block_scores, uint32_t* pool_ws_ptr, void* stream,
+                            const csa2_pages* pages = nullptr) {
   ScanArgs sa;
   sa.idx_q = idx_q; sa.idx_w = idx_w; sa.idx_k = idx_k;
   sa.idx_q_scales = q_scales; sa.idx_k_scales = k_scales;
@@ -313,6 +314,9 @@ static csa2_status run_scan(const csa2_dims* d, const csa2_queries* q, const uin
   sa.ld = ld_block_scores;
   sa.pool_ws = pool_ws_ptr;
   sa.pool_ws_stride = pool_ws_words(pool_chunks(d, q), pool_mm_cap(d, q));
+  sa.pages = pages ? pages->table : nullptr;
+  sa.page_shift = pages ? page_shift(pages) : 0;
+  sa.rows = pages ? pages->rows : 0;
   hipError_t e = launch_scan(sa, (hipStream_t)stream);
   return e == hipSuccess ? CSA2_OK : hip_fail(e, "scan launch");
 }
@@ -422,11 +426,13 @@ csa2_status csa2_index_pool(const csa2_dims* d, const csa2_queries* q, const flo
 static csa2_status index_full(const csa2_dims* d, const csa2_queries* q, const uint8_t* idx_q, const uint8_t* q_scales,
                               const float* idx_w, const uint8_t* idx_k, const uint8_t* k_scales, bool fp4,
                               int32_t* pool_blocks, int32_t* pool_count, float* block_scores, int64_t ld_block_scores,
-                              void* ws, size_t ws_bytes, void* stream, bool dry = false) {
+                              void* ws, size_t ws_bytes, void* stream, bool dry = false,
+                              const csa2_pages* pages = nullptr) {
   csa2_status st = check_dims(d);
   if (st) return st;
   if ((st = check_queries(q))) return st;
   if ((st = check_index_rows(d, idx_q, q_scales, idx_w, idx_k, k_scales, fp4))) return st;
+  if (pages && (st = check_pages(pages, fp4 ? d->idx_dim / 2 : d->idx_dim))) return st;
   if (!pool_blocks || !pool_count) return fail(CSA2_ERR_INVALID_ARG, "required pointer is NULL");
   const size_t pw = pool_ws(d, q);
   if ((st = check_ws(ws, ws_bytes, block_scores ? pw : full_ws(d, q)))) return st;
@@ -440,7 +446,7 @@ static csa2_status index_full(const csa2_dims* d, const csa2_queries* q, const u
   if ((st = check_device())) return st;
   if (dry) return CSA2_OK;
   if ((st = run_scan(d, q, idx_q, fp4 ? q_scales : nullptr, idx_w, idx_k, fp4 ? k_scales : nullptr, bs, ld,
-                     (uint32_t*)ws, stream)))
+                     (uint32_t*)ws, stream, pages)))
     return st;
   return run_pool(d, q, bs, ld, pool_blocks, pool_count, ws, true, stream);
 }
@@ -459,6 +465,18 @@ csa2_status csa2_index_full_fp4(const csa2_dims* d, const csa2_queries* q, const
                                 void* stream) {
   return index_full(d, q, q_codes, q_scales, idx_w, k_codes, k_scales, true, pool_blocks, pool_count, block_scores,
                     ld_block_scores, ws, ws_bytes, stream);
+}
+
+csa2_status csa2_index_full_paged(const csa2_dims* d, const csa2_queries* q, const csa2_pages* pages,
+                                  const uint8_t* idx_q, const uint8_t* idx_q_scales, const float* idx_w,
+                                  const uint8_t* idx_k, const uint8_t* idx_k_scales, int32_t* pool_blocks,
+                                  int32_t* pool_count, float* block_scores, int64_t ld_block_scores, void* ws,
+                                  size_t ws_bytes, void* stream) {
+  if ((idx_q_scales == nullptr) != (idx_k_scales == nullptr))
+    return fail(CSA2_ERR_INVALID_ARG, "idx_q_scales and idx_k_scales must both be given (FP4 rows) or both NULL");
+  if (!pages) return fail(CSA2_ERR_INVALID_ARG, "pages is NULL");
+  return index_full(d, q, idx_q, idx_q_scales, idx_w, idx_k, idx_k_scales, idx_q_scales != nullptr, pool_blocks,
+                    pool_count, block_scores, ld_block_scores, ws, ws_bytes, stream, false, pages);
 }
 
 csa2_status csa2_index_reindex_workspace_size(const csa2_dims* d, const csa2_queries* q, size_t* bytes) {
@@ -632,13 +650,13 @@ csa2_status csa2_decode_step_workspace_size(const csa2_dims* d, const csa2_queri
   return CSA2_OK;
 }
 
-csa2_status csa2_decode_step(const csa2_dims* d, const csa2_queries* q, int32_t mode, const uint8_t* idx_q,
-                             const uint8_t* idx_q_scales, const float* idx_w, const uint8_t* idx_k,
-                             const uint8_t* idx_k_scales, int32_t* pool_blocks, int32_t* pool_count,
-                             int32_t* topk_pos, int32_t* topk_count, const uint16_t* q_lat, const uint16_t* q_rope,
-                             float softmax_scale, const uint8_t* kv_codes, const uint8_t* kv_scales,
-                             const uint16_t* kv_rope, const uint16_t* swa_kv, const int64_t* swa_base, float* out,
-                             float* lse, void* ws, size_t ws_bytes, void* stream) {
+static csa2_status decode_step(const csa2_dims* d, const csa2_queries* q, int32_t mode, const uint8_t* idx_q,
+                               const uint8_t* idx_q_scales, const float* idx_w, const uint8_t* idx_k,
+                               const uint8_t* idx_k_scales, int32_t* pool_blocks, int32_t* pool_count,
+                               int32_t* topk_pos, int32_t* topk_count, const uint16_t* q_lat, const uint16_t* q_rope,
+                               float softmax_scale, const uint8_t* kv_codes, const uint8_t* kv_scales,
+                               const uint16_t* kv_rope, const uint16_t* swa_kv, const int64_t* swa_base, float* out,
+                               float* lse, void* ws, size_t ws_bytes, void* stream, const csa2_pages* pages) {
   csa2_status st = check_dims(d);
   if (st) return st;
   if ((st = check_queries(q))) return st;
@@ -659,17 +677,43 @@ csa2_status csa2_decode_step(const csa2_dims* d, const csa2_queries* q, int32_t 
     const bool dry = pass == 0;
     if (mode == CSA2_LAYER_FULL &&
         (st = index_full(d, q, idx_q, idx_q_scales, idx_w, idx_k, idx_k_scales, fp4, pool_blocks, pool_count,
-                         nullptr, 0, w_full, n_full, stream, dry)))
+                         nullptr, 0, w_full, n_full, stream, dry, pages)))
       return st;
     if (mode != CSA2_LAYER_REUSE &&
         (st = index_reindex(d, q, idx_q, idx_q_scales, idx_w, idx_k, idx_k_scales, fp4, pool_blocks, pool_count,
-                            topk_pos, topk_count, nullptr, w_re, n_re, stream, dry)))
+                            topk_pos, topk_count, nullptr, w_re, n_re, stream, dry, pages)))
       return st;
     if ((st = attend(d, q, q_lat, q_rope, softmax_scale, kv_codes, kv_scales, kv_rope, topk_pos, topk_count, swa_kv,
-                     swa_base, out, lse, attend_ws(d, q) ? w_att : nullptr, n_att, stream, dry)))
+                     swa_base, out, lse, attend_ws(d, q) ? w_att : nullptr, n_att, stream, dry, pages)))
       return st;
   }
   return CSA2_OK;
+}
+
+csa2_status csa2_decode_step(const csa2_dims* d, const csa2_queries* q, int32_t mode, const uint8_t* idx_q,
+                             const uint8_t* idx_q_scales, const float* idx_w, const uint8_t* idx_k,
+                             const uint8_t* idx_k_scales, int32_t* pool_blocks, int32_t* pool_count,
+                             int32_t* topk_pos, int32_t* topk_count, const uint16_t* q_lat, const uint16_t* q_rope,
+                             float softmax_scale, const uint8_t* kv_codes, const uint8_t* kv_scales,
+                             const uint16_t* kv_rope, const uint16_t* swa_kv, const int64_t* swa_base, float* out,
+                             float* lse, void* ws, size_t ws_bytes, void* stream) {
+  return decode_step(d, q, mode, idx_q, idx_q_scales, idx_w, idx_k, idx_k_scales, pool_blocks, pool_count, topk_pos,
+                     topk_count, q_lat, q_rope, softmax_scale, kv_codes, kv_scales, kv_rope, swa_kv, swa_base, out,
+                     lse, ws, ws_bytes, stream, nullptr);
+}
+
+csa2_status csa2_decode_step_paged(const csa2_dims* d, const csa2_queries* q, const csa2_pages* pages,
+                                   int32_t mode, const uint8_t* idx_q, const uint8_t* idx_q_scales,
+                                   const float* idx_w, const uint8_t* idx_k, const uint8_t* idx_k_scales,
+                                   int32_t* pool_blocks, int32_t* pool_count, int32_t* topk_pos,
+                                   int32_t* topk_count, const uint16_t* q_lat, const uint16_t* q_rope,
+                                   float softmax_scale, const uint8_t* kv_codes, const uint8_t* kv_scales,
+                                   const uint16_t* kv_rope, const uint16_t* swa_kv, const int64_t* swa_base,
+                                   float* out, float* lse, void* ws, size_t ws_bytes, void* stream) {
+  if (!pages) return fail(CSA2_ERR_INVALID_ARG, "pages is NULL");
+  return decode_step(d, q, mode, idx_q, idx_q_scales, idx_w, idx_k, idx_k_scales, pool_blocks, pool_count, topk_pos,
+                     topk_count, q_lat, q_rope, softmax_scale, kv_codes, kv_scales, kv_rope, swa_kv, swa_base, out,
+                     lse, ws, ws_bytes, stream, pages);
 }
 
 }  // extern "C"

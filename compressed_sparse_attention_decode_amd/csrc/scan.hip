@@ -63,7 +63,7 @@ constexpr int kMaxTilePos = 4096;
 
 constexpr uint32_t kOob = 0xFFFFFF00u;   // a buffer offset past any row: reads zero
 
-template <int D, int HT, int R, int NW, bool F4>
+template <int D, int HT, int R, int NW, bool F4, bool PG>
 __global__ __launch_bounds__(64 * NW) void k_scan(ScanArgs a) {
   static_assert(!F4 || D == 128, "FP4 rows are 128 channels wide");
   constexpr int NT = 64 * NW;
@@ -77,6 +77,7 @@ __global__ __launch_bounds__(64 * NW) void k_scan(ScanArgs a) {
   __shared__ float s_bs[kMaxTilePos / 8];
   __shared__ __attribute__((aligned(16))) uint8_t s_q[64 * D];
   __shared__ __attribute__((aligned(16))) float s_w[64];
+  __shared__ int32_t s_pg[PG ? kMaxTilePos / 16 + 1 : 1];   // paged: the tile's page ids
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int gq = lane >> 4, col = lane & 15;
 
@@ -108,18 +109,22 @@ __global__ __launch_bounds__(64 * NW) void k_scan(ScanArgs a) {
 
   // buffer descriptor over this sequence's candidate keys, built from
   // wave-uniform scalars (rows >= c read as zero)
+  // (paged: over the whole plane; rows >= c are then masked per lane)
   const int64_t sbase = a.seq_base[q];
-  const uint64_t kaddr = (uint64_t)(uintptr_t)(a.idx_k + sbase * RB);
+  const int64_t kbase = PG ? 0 : sbase;
+  const uint32_t krows = PG ? (uint32_t)a.rows : (uint32_t)c;
+  const uint64_t kaddr = (uint64_t)(uintptr_t)(a.idx_k + kbase * RB);
   const v4u rsrc = {(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)kaddr),
                     (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(kaddr >> 32)) & 0xFFFFu,
-                    (uint32_t)__builtin_amdgcn_readfirstlane(c * RB), 0x00020000u};
+                    (uint32_t)__builtin_amdgcn_readfirstlane((int)(krows * RB)), 0x00020000u};
   v4u srsrc = rsrc;                     // FP4: the candidates' scale rows
   if constexpr (F4) {
-    const uint64_t saddr = (uint64_t)(uintptr_t)(a.idx_k_scales + sbase * SB);
+    const uint64_t saddr = (uint64_t)(uintptr_t)(a.idx_k_scales + kbase * SB);
     srsrc = v4u{(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)saddr),
                 (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(saddr >> 32)) & 0xFFFFu,
-                (uint32_t)__builtin_amdgcn_readfirstlane(c * SB), 0x00020000u};
+                (uint32_t)__builtin_amdgcn_readfirstlane((int)(krows * SB)), 0x00020000u};
   }
+  const int pg0 = PG ? p_begin >> a.page_shift : 0;   // the tile's first page
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
 
   // this wave's steps are s_k = wave + NW k, k < ns, streamed through R LDS
@@ -130,7 +135,12 @@ __global__ __launch_bounds__(64 * NW) void k_scan(ScanArgs a) {
   const int ns = wave < nsteps ? (nsteps - wave + NW - 1) / NW : 0;
   auto issue = [&](int k) {
     const int row0 = p_begin + (wave + NW * k) * 16;
-    const uint32_t row = (uint32_t)(row0 + col) * RB;
+    // the step's 16 rows are 16-aligned, so they share one page
+    uint32_t prow0 = (uint32_t)row0;
+    if constexpr (PG)
+      prow0 = ((uint32_t)s_pg[(row0 >> a.page_shift) - pg0] << a.page_shift) |
+              ((uint32_t)row0 & ((1u << a.page_shift) - 1u));
+    const uint32_t row = !PG || row0 + col < c ? (prow0 + col) * RB : kOob;
     const uint32_t slot = (uint32_t)(uintptr_t)(lds_void*)&s_ring[wave_u][k % R][0];
     if constexpr (F4) {
       const uint32_t m0 = (uint32_t)__builtin_amdgcn_readfirstlane((int)slot);
@@ -138,7 +148,7 @@ __global__ __launch_bounds__(64 * NW) void k_scan(ScanArgs a) {
                    :: "s"(m0), "v"(row + gq * 16), "s"(rsrc) : "memory", "m0");
       // the step's 16 x 8 scale bytes: dword `lane` of them for lanes < 32
       const uint32_t m1 = (uint32_t)__builtin_amdgcn_readfirstlane((int)(slot + 1024));
-      const uint32_t so = lane < 32 ? (uint32_t)row0 * SB + lane * 4 : kOob;
+      const uint32_t so = lane < 32 && (!PG || row0 + (lane >> 1) < c) ? prow0 * SB + lane * 4 : kOob;
       asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
                    :: "s"(m1), "v"(so), "s"(srsrc) : "memory", "m0");
     } else {
@@ -251,6 +261,12 @@ __global__ __launch_bounds__(64 * NW) void k_scan(ScanArgs a) {
                    :: "s"(m0), "v"((uint32_t)(lane * 4)), "s"(wrsrc) : "memory", "m0");
     }
   }
+  if constexpr (PG) {
+    // the tile's page ids into LDS before the first key load
+    const int npg = ((p_end - 1) >> a.page_shift) - pg0 + 1;
+    for (int t = tid; t < npg; t += NT) s_pg[t] = a.pages[sbase + pg0 + t];
+    __syncthreads();
+  }
   const int pro = min(R - 1, ns);
   for (int k = 0; k < pro; ++k) issue(k);
   if (pro == R - 1) wait_vmcnt<(R - 1) * LPS>();   // the query loads (older) have landed
@@ -337,22 +353,24 @@ __global__ __launch_bounds__(64 * NW) void k_scan(ScanArgs a) {
   }
 }
 
-template <int D, int R, int NW, bool F4>
+template <int D, int R, int NW, bool F4, bool PG = false>
 hipError_t launch_drw(const ScanArgs& a, hipStream_t s) {
   const int ht = (a.hi + 15) / 16;
   const int units = ((a.n_q / a.g) * a.tiles + 7) / 8 * 8;
   const dim3 grid((unsigned)(units * a.g)), block(64 * NW);
   switch (ht) {
-    case 1: hipLaunchKernelGGL((k_scan<D, 1, R, NW, F4>), grid, block, 0, s, a); break;
-    case 2: hipLaunchKernelGGL((k_scan<D, 2, R, NW, F4>), grid, block, 0, s, a); break;
-    case 3: hipLaunchKernelGGL((k_scan<D, 3, R, NW, F4>), grid, block, 0, s, a); break;
-    default: hipLaunchKernelGGL((k_scan<D, 4, R, NW, F4>), grid, block, 0, s, a); break;
+    case 1: hipLaunchKernelGGL((k_scan<D, 1, R, NW, F4, PG>), grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((k_scan<D, 2, R, NW, F4, PG>), grid, block, 0, s, a); break;
+    case 3: hipLaunchKernelGGL((k_scan<D, 3, R, NW, F4, PG>), grid, block, 0, s, a); break;
+    default: hipLaunchKernelGGL((k_scan<D, 4, R, NW, F4, PG>), grid, block, 0, s, a); break;
   }
   return hipGetLastError();
 }
 
 template <int D, bool F4>
 hipError_t launch_d(const ScanArgs& a, hipStream_t s) {
+  // paged keys: the default ring and wave count only
+  if (a.pages) return launch_drw<D, kScanPrefetch, kScanWaves, F4, true>(a, s);
   // LDS ring slots per wave (steps in flight + 1) and waves per workgroup
   if (a.waves == 8) {
     if (a.prefetch == 8) return launch_drw<D, 8, 8, F4>(a, s);
@@ -367,6 +385,8 @@ hipError_t launch_d(const ScanArgs& a, hipStream_t s) {
 hipError_t launch_scan(const ScanArgs& a, hipStream_t s) {
   if (a.tiles == 0) return hipSuccess;
   if (a.tile_pos > kMaxTilePos || a.tile_pos % 64) return hipErrorInvalidValue;
+  if (a.pages && (a.tile_extra % 16 || a.page_shift < 4 || a.page_shift > 16 || a.rows * (a.d / (a.idx_k_scales ? 2 : 1)) > 0xFFFFFF00LL))
+    return hipErrorInvalidValue;
   if (a.tile_extra < 0 || a.tile_extra % 8 || a.tile_extra >= a.tile_pos ||
       a.tile_pos + a.tile_extra > kMaxTilePos || (a.tile_extra && (a.tiles & 1)))
     return hipErrorInvalidValue;

@@ -31,6 +31,12 @@ struct ScanArgs {
   // and tile 0 clears the query's histogram
   uint32_t* pool_ws;
   int64_t pool_ws_stride;
+  // paged keys (nullptr: position p of query q's sequence is row
+  // seq_base[q] + p): row (pages[seq_base[q] + (p >> page_shift)] <<
+  // page_shift) + (p mod 2^page_shift) of planes of `rows` rows
+  const int32_t* pages;
+  int page_shift;
+  int64_t rows;
 };
 
 hipError_t launch_scan(const ScanArgs& a, hipStream_t s);

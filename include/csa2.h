@@ -365,6 +365,19 @@ csa2_status csa2_index_reindex_paged(const csa2_dims* dims, const csa2_queries* 
                                      int32_t* topk_pos, int32_t* topk_count, float* topk_scores,
                                      void* ws, size_t ws_bytes, void* stream);
 
+/* csa2_index_full over paged indexer keys (see csa2_pages): the same block
+ * scores and pool.  Each scan workgroup first loads its tile's page ids (one
+ * extra round trip before its key stream starts); every 16-position step of
+ * the stream then reads 16 rows of one page.  FP4 rows when idx_q_scales and
+ * idx_k_scales are both given, fp8 when both are NULL.  Same workspace as
+ * csa2_index_full. */
+csa2_status csa2_index_full_paged(const csa2_dims* dims, const csa2_queries* q, const csa2_pages* pages,
+                                  const uint8_t* idx_q, const uint8_t* idx_q_scales, const float* idx_w,
+                                  const uint8_t* idx_k, const uint8_t* idx_k_scales,
+                                  int32_t* pool_blocks, int32_t* pool_count,
+                                  float* block_scores, int64_t ld_block_scores,
+                                  void* ws, size_t ws_bytes, void* stream);
+
 /* csa2_attend over paged main-KV planes (see csa2_pages): the same outputs
  * from the same entries; the kept positions are turned into rows (one page
  * id load each) before the FP4 gather.  The window rows come from swa_kv at
@@ -411,6 +424,18 @@ csa2_status csa2_page_rows(const csa2_pages* pages, int64_t n, const int64_t* ta
 #define CSA2_LAYER_REUSE 2
 
 csa2_status csa2_decode_step_workspace_size(const csa2_dims* dims, const csa2_queries* q, size_t* bytes);
+
+/* csa2_decode_step with every per-position plane paged (see csa2_pages):
+ * the stages' paged calls (csa2_index_full_paged, csa2_index_reindex_paged,
+ * csa2_attend_paged) in the same order and with the same workspace. */
+csa2_status csa2_decode_step_paged(const csa2_dims* dims, const csa2_queries* q, const csa2_pages* pages,
+                                   int32_t mode, const uint8_t* idx_q, const uint8_t* idx_q_scales,
+                                   const float* idx_w, const uint8_t* idx_k, const uint8_t* idx_k_scales,
+                                   int32_t* pool_blocks, int32_t* pool_count, int32_t* topk_pos,
+                                   int32_t* topk_count, const uint16_t* q_lat, const uint16_t* q_rope,
+                                   float softmax_scale, const uint8_t* kv_codes, const uint8_t* kv_scales,
+                                   const uint16_t* kv_rope, const uint16_t* swa_kv, const int64_t* swa_base,
+                                   float* out, float* lse, void* ws, size_t ws_bytes, void* stream);
 
 csa2_status csa2_decode_step(const csa2_dims* dims, const csa2_queries* q, int32_t mode,
                              const uint8_t* idx_q, const uint8_t* idx_q_scales, const float* idx_w,

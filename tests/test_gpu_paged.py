@@ -154,3 +154,65 @@ def test_page_rows_append_into_pages(case):
     untouched = torch.ones(pg.rows, dtype=torch.bool, device="cuda")
     untouched[rows] = False
     assert torch.equal(codes[untouched], pg.codes[untouched]), f"{name}: rows outside the appended ones changed"
+
+
+def test_paged_full_index_matches_contiguous(case):
+    """csa2_index_full_paged: the scan reads each tile's keys through the
+    page table; block scores and pool equal the contiguous call's bit for
+    bit (twice in a row on one workspace)."""
+    name, g, pg = case
+    csa2, w = g.csa2, g.w
+    q, wt = g.iq(0)
+    ld = csa2.block_scores_ld(g.dims, g.batch)
+    bs = torch.full((w.n_q, ld), float("nan"), dtype=torch.float32, device="cuda")
+    bs2 = torch.full_like(bs, float("nan"))
+    pool, cnt = csa2.index_full(g.dims, g.batch, q, wt, g.planes[0][0], block_scores=bs)
+    ws = torch.zeros(csa2.workspace_full(g.dims, pg.batch) + 256, dtype=torch.uint8, device="cuda")
+    outs = [csa2.index_full(g.dims, pg.batch, q, wt, pg.idx_k, block_scores=bs2, ws=ws, pages=pg.pages)
+            for _ in range(2)]
+    torch.cuda.synchronize()
+    for qi in range(w.n_q):
+        k = max(0, -(-(g.lay.q_visible[qi] - w.dims.swa) // 8))
+        assert torch.equal(bs2[qi, :k].view(torch.int32), bs[qi, :k].view(torch.int32)), \
+            f"{name} q{qi}: paged block scores differ"
+    for p2, c2 in outs:
+        assert torch.equal(c2, cnt), f"{name}: paged pool counts differ"
+        for qi in range(w.n_q):
+            k = int(cnt[qi])
+            assert torch.equal(p2[qi, :k], pool[qi, :k]), f"{name} q{qi}: paged pool differs"
+
+
+def test_paged_decode_step_matches_contiguous(case):
+    """csa2_decode_step_paged (Full layer: paged scan, Reindex and attention)
+    writes the contiguous step's pool, Top-K, outputs and LSE bit for bit."""
+    name, g, pg = case
+    csa2, w, d = g.csa2, g.w, g.w.dims
+    n_q = w.n_q
+    q, wt = g.iq(0)
+    ql, qr = g.mq(0)
+    _, codes, scales, kv_rope, swa_kv = g.planes[0]
+
+    def bufs():
+        return dict(pool_blocks=torch.empty(n_q, d.pool_blocks, dtype=torch.int32, device="cuda"),
+                    pool_count=torch.empty(n_q, dtype=torch.int32, device="cuda"),
+                    topk_pos=torch.empty(n_q, d.topk, dtype=torch.int32, device="cuda"),
+                    topk_count=torch.empty(n_q, dtype=torch.int32, device="cuda"),
+                    out=torch.empty(n_q, d.n_heads, 512, dtype=torch.float32, device="cuda"),
+                    lse=torch.empty(n_q, d.n_heads, dtype=torch.float32, device="cuda"))
+
+    a, b = bufs(), bufs()
+    csa2.decode_step(g.dims, g.batch, csa2.LAYER_FULL, q, wt, g.planes[0][0], a["pool_blocks"], a["pool_count"],
+                     a["topk_pos"], a["topk_count"], ql, qr, 1.0, codes, scales, kv_rope, swa_kv, g.swa_base,
+                     a["out"], a["lse"])
+    csa2.decode_step(g.dims, pg.batch, csa2.LAYER_FULL, q, wt, pg.idx_k, b["pool_blocks"], b["pool_count"],
+                     b["topk_pos"], b["topk_count"], ql, qr, 1.0, pg.codes, pg.scales, pg.kv_rope, swa_kv,
+                     g.swa_base, b["out"], b["lse"], pages=pg.pages)
+    torch.cuda.synchronize()
+    assert torch.equal(b["pool_count"], a["pool_count"]) and torch.equal(b["topk_count"], a["topk_count"])
+    for qi in range(n_q):
+        k = int(a["pool_count"][qi])
+        assert torch.equal(b["pool_blocks"][qi, :k], a["pool_blocks"][qi, :k]), f"{name} q{qi}: step pool differs"
+        k = int(a["topk_count"][qi])
+        assert torch.equal(b["topk_pos"][qi, :k], a["topk_pos"][qi, :k]), f"{name} q{qi}: step Top-K differs"
+    assert torch.equal(b["out"].view(torch.int32), a["out"].view(torch.int32)), f"{name}: step output differs"
+    assert torch.equal(b["lse"].view(torch.int32), a["lse"].view(torch.int32)), f"{name}: step LSE differs"
