@@ -29,6 +29,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
+import numpy as np  # noqa: E402
 import torch  # noqa: E402
 
 import workloads as wl  # noqa: E402
@@ -88,7 +89,48 @@ class DeviceState:
             tokens_per_seq=w.tokens_per_seq)
         self.swa_base = torch.tensor(lay.q_swa_base, dtype=torch.int64, device=device)
         self._q = {}
+        self.pages = None
+        if w.page_size:
+            self._page(w.page_size)
         torch.cuda.synchronize()
+
+    def _page(self, ps: int):
+        """Moves every per-position plane into pages of `ps` positions at a
+        seeded shuffled physical order (with a few unused pages), and points
+        the batch's seq_base at each sequence's page-table row."""
+        csa2, lay, w, dev = self.csa2, self.lay, self.w, self.dev
+        rng = np.random.default_rng(w.key)
+        npg = [-(-r // ps) for r in lay.seq_rows]
+        total = sum(npg) + 7
+        perm = rng.permutation(total).astype(np.int64)
+        off, k, table = [], 0, []
+        for n in npg:
+            off.append(k)                    # the sequence's first entry in the table
+            table.append(perm[k:k + n])
+            k += n
+        table = np.concatenate(table + [np.zeros(1, np.int64)])
+        rows = total * ps
+        src = np.concatenate([lay.seq_base[s] + np.arange(r, dtype=np.int64) for s, r in enumerate(lay.seq_rows)])
+        dst = np.concatenate([table[off[s] + np.arange(r) // ps] * ps + np.arange(r) % ps
+                              for s, r in enumerate(lay.seq_rows)])
+        src_t, dst_t = torch.from_numpy(src).to(dev), torch.from_numpy(dst).to(dev)
+
+        def scatter(t):
+            out = torch.zeros((rows,) + tuple(t.shape[1:]), dtype=t.dtype, device=dev)
+            out.view(torch.uint8).view(rows, -1)[dst_t] = t.view(torch.uint8).view(t.shape[0], -1)[src_t]
+            return out
+
+        paged = []
+        for idx_k, codes, scales, kv_rope, swa_kv in self.planes:
+            pk = tuple(scatter(x) for x in idx_k) if isinstance(idx_k, tuple) else scatter(idx_k)
+            paged.append((pk, scatter(codes), scatter(scales), scatter(kv_rope), swa_kv))
+        self.planes = paged
+        self.idx_k, self.codes, self.scales, self.kv_rope, self.swa_kv = self.planes[0]
+        self.table = torch.from_numpy(table.astype(np.int32)).to(dev)
+        self.pages = csa2.Pages(self.table, ps, rows)
+        q_off = [off[qi // w.tokens_per_seq] for qi in range(w.n_q)]
+        self.batch = csa2.Batch(torch.tensor(q_off, dtype=torch.int64, device=dev), self.batch.n_visible,
+                                self.batch.max_visible, self.batch.tokens_per_seq)
 
     # queries are generated once per layer and kept resident
     def iq(self, layer: int):
@@ -119,20 +161,22 @@ class DeviceState:
         if block_scores:
             nb = self.csa2.block_scores_ld(self.dims, self.batch)
             bs = torch.full((self.w.n_q, nb), float("nan"), dtype=torch.float32, device=self.dev)
-        pool, cnt = self.csa2.index_full(self.dims, self.batch, q, w, self.planes[r][0], block_scores=bs)
+        pool, cnt = self.csa2.index_full(self.dims, self.batch, q, w, self.planes[r][0], block_scores=bs,
+                                          pages=self.pages)
         return pool, cnt, bs
 
     def reindex(self, layer, pool, cnt, scores=False, r=0):
         q, w = self.iq(layer)
         ts = torch.empty(self.w.n_q, self.w.dims.topk, dtype=torch.float32, device=self.dev) if scores else None
-        tk, tc = self.csa2.index_reindex(self.dims, self.batch, q, w, self.planes[r][0], pool, cnt, topk_scores=ts)
+        tk, tc = self.csa2.index_reindex(self.dims, self.batch, q, w, self.planes[r][0], pool, cnt, topk_scores=ts,
+                                         pages=self.pages)
         return tk, tc, ts
 
     def attend(self, layer, tk, tc, r=0):
         ql, qr = self.mq(layer)
         _, codes, scales, kv_rope, swa_kv = self.planes[r]
         return self.csa2.attend(self.dims, self.batch, ql, qr, 1.0, codes, scales, kv_rope,
-                                tk, tc, swa_kv, self.swa_base)
+                                tk, tc, swa_kv, self.swa_base, pages=self.pages)
 
 
 # ---------------------------------------------------------------- one step
@@ -177,18 +221,18 @@ class Step:
             q0, w0 = st.iq(0)
             # csa2_index_full's two stages, issued separately to time each
             seq.append(("scan", csa2.index_scan(st.dims, st.batch, q0, w0, idx_k, self.bs, pool_ws=self.ws_p,
-                                                prepare=True)))
+                                                prepare=True, pages=st.pages)))
             seq.append(("pool", csa2.index_pool(st.dims, st.batch, self.bs, self.pool, self.pcnt, ws=self.ws_p,
                                                 from_scan=True, prepare=True)))
             for i, layer in enumerate(self.layers):
                 q, wt = st.iq(layer)
                 seq.append(("reindex", csa2.index_reindex(st.dims, st.batch, q, wt, idx_k, self.pool, self.pcnt,
                                                           topk_pos=self.tk[i], topk_count=self.tc[i],
-                                                          ws=self.ws_r, prepare=True)))
+                                                          ws=self.ws_r, prepare=True, pages=st.pages)))
                 ql, qr = st.mq(layer)
                 seq.append(("attend", csa2.attend(st.dims, st.batch, ql, qr, 1.0, codes, scales, kv_rope,
                                                   self.tk[i], self.tc[i], swa_kv, st.swa_base, out=self.out[i],
-                                                  lse=self.lse[i], ws=self.ws_a, prepare=True)))
+                                                  lse=self.lse[i], ws=self.ws_a, prepare=True, pages=st.pages)))
             self.calls.append(seq)
 
     def run(self, r: int):
@@ -361,7 +405,7 @@ def measure(w: wl.Workload, steps: int, warmup: int, replicas: int):
             idx_k, codes, scales, kv_rope, swa_kv = st.planes[r]
             csa2.decode_step(st.dims, st.batch, csa2.LAYER_FULL, q0, w0, idx_k, step.pool, step.pcnt, step.tk[0],
                              step.tc[0], ql, qr, 1.0, codes, scales, kv_rope, swa_kv, st.swa_base, step.out[0],
-                             step.lse[0], ws=ws_g)
+                             step.lse[0], ws=ws_g, pages=st.pages)
         for i in range(warmup):
             layer(i % replicas)
         torch.cuda.synchronize()
@@ -529,7 +573,7 @@ def main():
     ap.add_argument("--workload", default="decode_b8_ctx128k")
     ap.add_argument("--secondary", default="decode_b1_ctx1m", help="second workload ('' to skip)")
     ap.add_argument("--variants", default="decode_b8_ctx128k_fp4idx,decode_b1_ctx1m_fp4idx,decode_b8_ctx128k_kvg32,"
-                                          "chunk_b1x64_ctx128k",
+                                          "chunk_b1x64_ctx128k,decode_b8_ctx128k_paged64,decode_b1_ctx1m_paged64",
                     help="comma-separated further workloads reported under 'variants' ('' to skip)")
     ap.add_argument("--replicas", type=int, default=0, help="cache replicas (0: enough for >= 1 GB)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle sample budget (0 to skip)")
@@ -576,6 +620,7 @@ def main():
                "unit": "queries/s", "ms_per_step": round(res2["ms_per_step"], 5),
                "indexer_rows": "fp4 (E2M1 + E4M3 per 16)" if w2.idx_fp4 else "fp8 e4m3",
                "kv_scale_group": w2.dims.kv_group,
+               "page_size": w2.page_size or None,
                "stages_us": res2["stages_us"], "step_us_spread": res2["step_us_spread"],
                "layer_step_us": res2.get("layer_step_us"),
                "replicas": res2["replicas"],
@@ -588,6 +633,10 @@ def main():
                              "frac": res2["scan"]["mfma_frac"], "dtype": "f16 (exact fp8 / FP4 conversions)"}}
         print(f"[bench] {w2.name}: {res2['value']:.1f} queries/s, scan {res2['scan']['avg_us']} us = "
               f"{res2['scan']['achieved_gbs']} GB/s", file=sys.stderr, flush=True)
+        if w2.page_size and args.cpu_seconds > 0 and name != args.secondary:
+            # the paged step's sampled query against the oracle
+            _, rec["parity"] = cpu_baseline(w2, st2, step2, 0.0)
+            print(f"[bench] {w2.name} parity {rec['parity']}", file=sys.stderr, flush=True)
         return w2, st2, step2, rec
 
     secondary = None

@@ -91,6 +91,7 @@ def lib() -> ctypes.CDLL:
             "csa2_attend_paged": (I32, [PD, PQ, PP, P, P, ctypes.c_float, P, P, P, P, P, P, P, P, P, P, SZ, P]),
             "csa2_page_rows": (I32, [PP, I64, P, P, P, P]),
             "csa2_index_full_paged": (I32, [PD, PQ, PP, P, P, P, P, P, P, P, P, I64, P, SZ, P]),
+            "csa2_index_scan_paged": (I32, [PD, PQ, PP, P, P, P, P, P, P, I64, P, SZ, P]),
             "csa2_decode_step_paged": (I32, [PD, PQ, PP, I32, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_float,
                                              P, P, P, P, P, P, P, P, SZ, P]),
             "csa2_decode_step_workspace_size": (I32, [PD, PQ, ctypes.POINTER(SZ)]),
@@ -408,10 +409,11 @@ POOL_WS_FROM_SCAN = 1
 
 def index_scan(dims: Dims, b: Batch, idx_q, idx_w: torch.Tensor, idx_k,
                block_scores: Optional[torch.Tensor] = None, pool_ws: Optional[torch.Tensor] = None,
-               prepare: bool = False):
+               prepare: bool = False, pages: Optional[Pages] = None):
     """Full-mode scan: block scores float32 [n_q, ld] (b_j for j < nb).  With
     `pool_ws` (a pool-select workspace) the scan also prepares it for an
-    index_pool(..., ws=pool_ws, from_scan=True) call on these scores."""
+    index_pool(..., ws=pool_ws, from_scan=True) call on these scores.  With
+    `pages` the keys are paged (csa2_index_scan_paged)."""
     dev = _rows_dev(idx_k)
     _dev(block_scores, pool_ws)
     fp4, qp, kp = _check_idx(dims, b, idx_q, idx_w, idx_k)
@@ -423,6 +425,14 @@ def index_scan(dims: Dims, b: Batch, idx_q, idx_w: torch.Tensor, idx_k,
     d, q = dims.c(), b.c()
     args = (ctypes.byref(d), ctypes.byref(q), *qp, idx_w.data_ptr(), *kp, block_scores.data_ptr(),
             block_scores.shape[1], wp, wn, _stream(dev))
+    if pages is not None:
+        _check_page_rows(pages, *(idx_k if fp4 else (idx_k,)))
+        pg = pages.c()
+        qs, ks = (qp[1], kp[1]) if fp4 else (None, None)
+        args = (ctypes.byref(d), ctypes.byref(q), ctypes.byref(pg), qp[0], qs, idx_w.data_ptr(), kp[0], ks,
+                block_scores.data_ptr(), block_scores.shape[1], wp, wn, _stream(dev))
+        call = _issue(lib().csa2_index_scan_paged, args, (d, q, pg, pool_ws, pages.table), prepare)
+        return call if prepare else block_scores
     fn = lib().csa2_index_scan_fp4 if fp4 else lib().csa2_index_scan
     call = _issue(fn, args, (d, q, pool_ws), prepare)
     return call if prepare else block_scores

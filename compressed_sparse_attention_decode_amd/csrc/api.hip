@@ -371,17 +371,29 @@ static csa2_status check_index_rows(const csa2_dims* d, const uint8_t* idx_q, co
 static csa2_status index_scan(const csa2_dims* d, const csa2_queries* q, const uint8_t* idx_q, const uint8_t* q_scales,
                               const float* idx_w, const uint8_t* idx_k, const uint8_t* k_scales, bool fp4,
                               float* block_scores, int64_t ld_block_scores, void* pool_wsp, size_t pool_ws_bytes,
-                              void* stream) {
+                              void* stream, const csa2_pages* pages = nullptr) {
   csa2_status st = check_dims(d);
   if (st) return st;
   if ((st = check_queries(q))) return st;
   if ((st = check_index_rows(d, idx_q, q_scales, idx_w, idx_k, k_scales, fp4))) return st;
+  if (pages && (st = check_pages(pages, fp4 ? d->idx_dim / 2 : d->idx_dim))) return st;
   if (!block_scores) return fail(CSA2_ERR_INVALID_ARG, "block_scores is NULL");
   if ((st = check_block_scores(d, q, block_scores, ld_block_scores))) return st;
   if (pool_wsp && (st = check_ws(pool_wsp, pool_ws_bytes, pool_ws(d, q)))) return st;
   if ((st = check_device())) return st;
   return run_scan(d, q, idx_q, fp4 ? q_scales : nullptr, idx_w, idx_k, fp4 ? k_scales : nullptr, block_scores,
-                  ld_block_scores, (uint32_t*)pool_wsp, stream);
+                  ld_block_scores, (uint32_t*)pool_wsp, stream, pages);
+}
+
+csa2_status csa2_index_scan_paged(const csa2_dims* d, const csa2_queries* q, const csa2_pages* pages,
+                                  const uint8_t* idx_q, const uint8_t* idx_q_scales, const float* idx_w,
+                                  const uint8_t* idx_k, const uint8_t* idx_k_scales, float* block_scores,
+                                  int64_t ld_block_scores, void* pool_wsp, size_t pool_ws_bytes, void* stream) {
+  if ((idx_q_scales == nullptr) != (idx_k_scales == nullptr))
+    return fail(CSA2_ERR_INVALID_ARG, "idx_q_scales and idx_k_scales must both be given (FP4 rows) or both NULL");
+  if (!pages) return fail(CSA2_ERR_INVALID_ARG, "pages is NULL");
+  return index_scan(d, q, idx_q, idx_q_scales, idx_w, idx_k, idx_k_scales, idx_q_scales != nullptr, block_scores,
+                    ld_block_scores, pool_wsp, pool_ws_bytes, stream, pages);
 }
 
 csa2_status csa2_index_scan(const csa2_dims* d, const csa2_queries* q, const uint8_t* idx_q, const float* idx_w,

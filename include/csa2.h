@@ -365,6 +365,16 @@ csa2_status csa2_index_reindex_paged(const csa2_dims* dims, const csa2_queries* 
                                      int32_t* topk_pos, int32_t* topk_count, float* topk_scores,
                                      void* ws, size_t ws_bytes, void* stream);
 
+/* csa2_index_scan over paged indexer keys (see csa2_pages): the same block
+ * scores, and the same pool-workspace preparation when pool_ws is given.
+ * FP4 rows when idx_q_scales and idx_k_scales are both given, fp8 when both
+ * are NULL. */
+csa2_status csa2_index_scan_paged(const csa2_dims* dims, const csa2_queries* q, const csa2_pages* pages,
+                                  const uint8_t* idx_q, const uint8_t* idx_q_scales, const float* idx_w,
+                                  const uint8_t* idx_k, const uint8_t* idx_k_scales,
+                                  float* block_scores, int64_t ld_block_scores,
+                                  void* pool_ws, size_t pool_ws_bytes, void* stream);
+
 /* csa2_index_full over paged indexer keys (see csa2_pages): the same block
  * scores and pool.  Each scan workgroup first loads its tile's page ids (one
  * extra round trip before its key stream starts); every 16-position step of

@@ -31,7 +31,8 @@ def test_header_declares_the_entry_points():
               "csa2_index_scan", "csa2_index_pool", "csa2_status_string", "csa2_abi_version",
               "csa2_encode_fp4", "csa2_index_scan_fp4", "csa2_index_full_fp4", "csa2_index_reindex_fp4",
               "csa2_decode_step", "csa2_decode_step_workspace_size", "csa2_index_reindex_paged",
-              "csa2_attend_paged", "csa2_page_rows", "csa2_index_full_paged", "csa2_decode_step_paged"):
+              "csa2_attend_paged", "csa2_page_rows", "csa2_index_full_paged", "csa2_decode_step_paged",
+              "csa2_index_scan_paged"):
         assert n in names
 
 

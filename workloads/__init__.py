@@ -154,6 +154,7 @@ class Workload:
     fresh_encode: int = 0         # entries encoded by each step
     ctx_list: Optional[Tuple[int, ...]] = None   # explicit contexts (tests)
     idx_fp4: bool = False         # indexer rows in FP4 (from idx_keys_bf16 / idx_query_bf16)
+    page_size: int = 0            # > 0: per-position planes in pages of this many positions, shuffled
 
     @property
     def key(self) -> int:
@@ -184,6 +185,11 @@ WORKLOADS: List[Workload] = [
              ctx=(131072, 131072)),
     # many query tokens against one cache (a 64-token chunk at 128K context)
     Workload(8, "chunk_b1x64_ctx128k", _BIG, n_seq=1, ctx=(131072, 131072), tokens_per_seq=64),
+    # the decode workloads over paged caches (pages of 64 positions in a shuffled physical order)
+    Workload(9, "decode_b8_ctx128k_paged64", _BIG, n_seq=8, ctx=(131072, 131072), page_size=64),
+    Workload(10, "decode_b1_ctx1m_paged64", _BIG, n_seq=1, ctx=(1048576, 1048576), page_size=64),
+    Workload(11, "decode_b8_ctx128k_paged256", _BIG, n_seq=8, ctx=(131072, 131072), page_size=256),
+    Workload(12, "decode_b1_ctx1m_paged256", _BIG, n_seq=1, ctx=(1048576, 1048576), page_size=256),
 ]
 
 
