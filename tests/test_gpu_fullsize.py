@@ -35,6 +35,9 @@ SAMPLES = {
     "decode_b1_ctx1m_fp4idx": [0],
     "decode_b8_ctx128k_kvg32": [0, 7],
     "chunk_b1x64_ctx128k": [0, 31, 63],
+    # every per-position plane in shuffled pages of 64 positions (paged calls)
+    "decode_b8_ctx128k_paged64": [0, 7],
+    "decode_b1_ctx1m_paged64": [0],
 }
 
 

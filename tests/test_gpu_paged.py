@@ -216,3 +216,62 @@ def test_paged_decode_step_matches_contiguous(case):
         assert torch.equal(b["topk_pos"][qi, :k], a["topk_pos"][qi, :k]), f"{name} q{qi}: step Top-K differs"
     assert torch.equal(b["out"].view(torch.int32), a["out"].view(torch.int32)), f"{name}: step output differs"
     assert torch.equal(b["lse"].view(torch.int32), a["lse"].view(torch.int32)), f"{name}: step LSE differs"
+
+
+def test_paged_step_graph_replays(case):
+    """csa2_decode_step_paged (Full layer) captured into a HIP graph: every
+    replay, with eager work and a synchronisation between replays and the
+    outputs overwritten before each, reproduces the eager outputs bit for
+    bit (the paged calls enqueue no memset and allocate nothing)."""
+    name, g, pg = case
+    csa2, w, d = g.csa2, g.w, g.w.dims
+    n_q = w.n_q
+    q, wt = g.iq(0)
+    ql, qr = g.mq(0)
+    swa_kv = g.planes[0][4]
+    ws = torch.zeros(csa2.workspace_step(g.dims, pg.batch) + 256, dtype=torch.uint8, device="cuda")
+
+    def bufs():
+        return dict(pool_blocks=torch.full((n_q, d.pool_blocks), 7, dtype=torch.int32, device="cuda"),
+                    pool_count=torch.full((n_q,), 7, dtype=torch.int32, device="cuda"),
+                    topk_pos=torch.full((n_q, d.topk), 7, dtype=torch.int32, device="cuda"),
+                    topk_count=torch.full((n_q,), 7, dtype=torch.int32, device="cuda"),
+                    out=torch.full((n_q, d.n_heads, 512), 7.0, dtype=torch.float32, device="cuda"),
+                    lse=torch.full((n_q, d.n_heads), 7.0, dtype=torch.float32, device="cuda"))
+
+    def step(b):
+        csa2.decode_step(g.dims, pg.batch, csa2.LAYER_FULL, q, wt, pg.idx_k, b["pool_blocks"], b["pool_count"],
+                         b["topk_pos"], b["topk_count"], ql, qr, 1.0, pg.codes, pg.scales, pg.kv_rope, swa_kv,
+                         g.swa_base, b["out"], b["lse"], ws=ws, pages=pg.pages)
+
+    eager = bufs()
+    step(eager)
+    torch.cuda.synchronize()
+    b = bufs()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):          # warm the binding's host path on the capture stream
+        step(b)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step(b)
+    for rep in range(4):
+        for t in b.values():
+            t.fill_(5)                      # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for key in eager:
+            if key in ("pool_blocks", "topk_pos"):
+                cnt = eager["pool_count" if key == "pool_blocks" else "topk_count"]
+                for qi in range(n_q):
+                    k = int(cnt[qi])
+                    assert torch.equal(b[key][qi, :k], eager[key][qi, :k]), f"{name} replay {rep} {key} q{qi}"
+            else:
+                x, y = b[key], eager[key]
+                if x.dtype == torch.float32:
+                    x, y = x.view(torch.int32), y.view(torch.int32)
+                assert torch.equal(x, y), f"{name} replay {rep} {key}"
+    del graph
