@@ -100,7 +100,9 @@ typedef struct csa2_dims {
  *                   2^21; used only to size launch grids.
  *   seq_base        device int64 [n_q]: cache row of position 0 of the
  *                   query's sequence.  Position p lives at row seq_base + p
- *                   in idx_k, kv_codes, kv_scales and kv_rope.
+ *                   in idx_k, kv_codes, kv_scales and kv_rope.  In the
+ *                   paged calls (csa2_pages) it is instead the offset of the
+ *                   sequence's first page in the page table.
  *   n_visible       device int32 [n_q]: the query sees positions [0, n).
  * A query's sparse candidates are positions [0, c), c = max(0, n - W); the
  * window is [c, n) ([atlas] §3.2 heterogeneous KV: the indexer and Top-K
