@@ -91,5 +91,30 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+def build_host_asan() -> str:
+    """libcsa2 with AddressSanitizer on its host code only (argument checks,
+    workspace sizing, launch planning), for the host-side tests.  The device
+    code is compiled as usual (it never runs there).  Written to
+    _build/asan/libcsa2_asan.so."""
+    cc = hipcc()
+    out_dir = os.path.join(PKG, "_build", "asan")
+    os.makedirs(out_dir, exist_ok=True)
+    host = ["--offload-arch=gfx950", "-O1", "-g", "-std=c++17", "-fPIC",
+            "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer"]
+    jobs = [(s, [cc, *host, "-c", os.path.join(CSRC, s), "-o", os.path.join(out_dir, s.replace(".hip", ".o"))])
+            for s in SOURCES]
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:
+        results = list(ex.map(lambda j: (j[0], *_run(j[1])), jobs))
+    failed = [(s, out) for s, rc, out in results if rc != 0]
+    if failed:
+        raise RuntimeError("hipcc (host ASan) failed:\n" + "\n".join(f"== {s}\n{out}" for s, out in failed))
+    lib = os.path.join(out_dir, "libcsa2_asan.so")
+    rc, out = _run([cc, "--offload-arch=gfx950", "-shared", "-fPIC", "-Xarch_host", "-fsanitize=address", "-o", lib,
+                    *[os.path.join(out_dir, s.replace(".hip", ".o")) for s in SOURCES]])
+    if rc != 0:
+        raise RuntimeError(f"link (host ASan) failed:\n{out}")
+    return lib
+
+
 if __name__ == "__main__":
     print(build(verbose=True))
