@@ -172,6 +172,25 @@ size_t reindex_ws(const csa2_dims* d, const csa2_queries* q) {
   return align256((size_t)q->n_q * 4) + align256((size_t)q->n_q * d->pool_blocks * 8 * 4);
 }
 
+// Pool blocks per Reindex scoring workgroup: 64, or 128 when 64-block
+// workgroups would exceed two per CU (the grid then takes several rounds,
+// and fewer, longer workgroups measured faster: 42.5 against 56.9 us per
+// layer for 32 queries; at 1 and 8 queries 64 is faster).
+// CSA2_REINDEX_BLOCKS (64 or 128) overrides.  Called after check_device.
+int reindex_blocks_per_wg(const csa2_dims* d, const csa2_queries* q) {
+  int dev = 0;
+  int bpw = kReindexBlocks;
+  if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < 64 && g_cus[dev] > 0) {
+    const int64_t wgs = (int64_t)q->n_q * ((d->pool_blocks + kReindexBlocks - 1) / kReindexBlocks);
+    if (wgs > 2 * (int64_t)g_cus[dev]) bpw = kReindexBlocksWide;
+  }
+  if (const char* env = getenv("CSA2_REINDEX_BLOCKS")) {
+    const int v = atoi(env);
+    if (v == kReindexBlocks || v == kReindexBlocksWide) bpw = v;
+  }
+  return bpw;
+}
+
 struct AttendPlan { int hg, splits, split_entries; };
 
 // A small batch is spread over more workgroups by splitting each query's
@@ -523,7 +542,8 @@ static csa2_status index_reindex(const csa2_dims* d, const csa2_queries* q, cons
   ra.pool_blocks = pool_blocks; ra.pool_count = pool_count;
   ra.n_q = q->n_q; ra.hi = d->idx_heads; ra.d = d->idx_dim; ra.swa = d->swa;
   ra.pool = d->pool_blocks; ra.topk = d->topk;
-  ra.split = (d->pool_blocks + kReindexBlocks - 1) / kReindexBlocks;
+  ra.blocks_per_wg = reindex_blocks_per_wg(d, q);
+  ra.split = (d->pool_blocks + ra.blocks_per_wg - 1) / ra.blocks_per_wg;
   ra.done = (uint32_t*)ws;
   ra.keys = (uint32_t*)((char*)ws + align256((size_t)q->n_q * 4));
   ra.topk_pos = topk_pos; ra.topk_count = topk_count; ra.topk_scores = topk_scores;

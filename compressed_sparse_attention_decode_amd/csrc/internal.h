@@ -40,6 +40,7 @@ struct ReindexArgs {
   const int32_t* pool_count;
   int n_q, hi, d, swa, pool, topk;
   int split;                 // scoring workgroups per query
+  int blocks_per_wg;         // pool blocks per scoring workgroup (kReindexBlocks or kReindexBlocksWide)
   uint32_t* done;            // workspace [n_q]: scoring workgroups finished (zero between calls)
   uint32_t* keys;            // workspace [n_q, 8 * pool]: order keys, 0 = empty
   int32_t* topk_pos;
@@ -99,7 +100,8 @@ constexpr int kPoolSmallBlocks = 16384;   // blocks a one-workgroup pool selecti
 constexpr int kAttendTile = 32;        // entries per attention tile
 constexpr int kAttendWaves = 4;        // waves per attention workgroup (16 heads each)
 constexpr int kAttendMaxSplits = 16;   // entry-list splits per query, at most
-constexpr int kReindexBlocks = 64;     // pool blocks per Reindex scoring workgroup
+constexpr int kReindexBlocks = 64;     // pool blocks per Reindex scoring workgroup (one-round grids)
+constexpr int kReindexBlocksWide = 128;   // ... when 64-block workgroups would exceed two per CU
 constexpr int kMaxVisible = 1 << 21;   // bound of n_visible
 constexpr int kMaxTokensPerSeq = 64;   // query tokens of one sequence sharing its key stream
 constexpr int kMaxBlocks = kMaxVisible / 8;

@@ -35,24 +35,24 @@ namespace {
 constexpr uint32_t kNoKeyRow = 0xFFFFFFFFu;   // a lane with no candidate position (paged rows)
 constexpr uint32_t kNoKeyOff = 0xFFFFFF00u;   // a buffer offset past any plane: reads zero
 
-// Scores of pool slots [i_begin, i_begin + kReindexBlocks) of query q (8
+// Scores of pool slots [i_begin, i_begin + BPW) of query q (8
 // positions per slot) as order keys.  Slots past the pool count are scored
 // too, from whatever block ids the row holds there (clamped to a zero key
 // row): the selection masks them by the count, so nothing here waits for it.
-template <int D, int HT, int NW, bool F4>
+template <int D, int HT, int NW, bool F4, int BPW>
 __device__ __forceinline__ void score_part(const ReindexArgs& a, int q, int part) {
   static_assert(!F4 || D == 128, "FP4 rows are 128 channels wide");
   constexpr int KC = D / 32;
   constexpr int LB = F4 ? 16 : D / 4;              // key code bytes per lane per position
   constexpr int RB = F4 ? D / 2 : D;               // key code bytes per position
   constexpr int SB = D / 16;                       // FP4 scale bytes per position
-  constexpr int SPW = kReindexBlocks / (2 * NW);   // wave steps (2 blocks each) per wave
-  static_assert(SPW * 2 * NW == kReindexBlocks, "whole wave steps");
+  constexpr int SPW = BPW / (2 * NW);              // wave steps (2 blocks each) per wave
+  static_assert(SPW * 2 * NW == BPW, "whole wave steps");
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // known wave-uniform: no waterfall loops
   const int gq = lane >> 4, col = lane & 15;
-  const int i_begin = part * kReindexBlocks;
-  const int i_end = min(a.pool, i_begin + kReindexBlocks);
+  const int i_begin = part * BPW;
+  const int i_end = min(a.pool, i_begin + BPW);
   const int n = load_uniform(a.n_visible + q);
   const int c = max(0, n - a.swa);
   const int32_t* pool = a.pool_blocks + (int64_t)q * a.pool;
@@ -260,14 +260,14 @@ __device__ __forceinline__ void topk_select(const ReindexArgs& a, int q, int32_t
   if (tid == 0) a.topk_count[q] = (int32_t)cut.keff;
 }
 
-// One kernel per Reindex call.  Every workgroup scores its kReindexBlocks
-// pool slots; the last workgroup of a query to finish (a per-query counter in
+// One kernel per Reindex call.  Every workgroup scores its BPW pool slots
+// (64, or 128 when the grid would otherwise take several rounds); the last workgroup of a query to finish (a per-query counter in
 // the workspace, left at zero for the next call) selects that query's Top-K
 // from all of its keys.  The keys cross workgroups through memory: after a
 // barrier, each workgroup's release fence publishes its stores before it
 // counts itself in, and the last one's acquire fence makes the others'
 // visible before it reads them.
-template <int D, int HT, bool F4>
+template <int D, int HT, bool F4, int BPW>
 __global__ __launch_bounds__(kTkThreads) void k_reindex(ReindexArgs a) {
   __shared__ uint32_t s_last;
   const int q = blockIdx.x / a.split, part = blockIdx.x % a.split;
@@ -278,7 +278,7 @@ __global__ __launch_bounds__(kTkThreads) void k_reindex(ReindexArgs a) {
   const int32_t b0 = pool[min(j0, a.pool - 1)], b1 = pool[min(j0 + 1, a.pool - 1)];
   const int32_t b2 = pool[min(j0 + 2, a.pool - 1)], b3 = pool[min(j0 + 3, a.pool - 1)];
   const int pcnt = load_uniform(a.pool_count + q);
-  score_part<D, HT, kTkWaves, F4>(a, q, part);
+  score_part<D, HT, kTkWaves, F4, BPW>(a, q, part);
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's key stores have reached L2
   __syncthreads();
   if (threadIdx.x == 0) {
@@ -298,17 +298,23 @@ __global__ __launch_bounds__(kTkThreads) void k_reindex(ReindexArgs a) {
   topk_select(a, q, b0, b1, b2, b3, pcnt);
 }
 
-template <int D, bool F4>
-hipError_t launch_d(const ReindexArgs& a, hipStream_t s) {
+template <int D, bool F4, int BPW>
+hipError_t launch_db(const ReindexArgs& a, hipStream_t s) {
   const int ht = (a.hi + 15) / 16;
   const dim3 grid((unsigned)(a.n_q * a.split)), block(kTkThreads);
   switch (ht) {
-    case 1: hipLaunchKernelGGL((k_reindex<D, 1, F4>), grid, block, 0, s, a); break;
-    case 2: hipLaunchKernelGGL((k_reindex<D, 2, F4>), grid, block, 0, s, a); break;
-    case 3: hipLaunchKernelGGL((k_reindex<D, 3, F4>), grid, block, 0, s, a); break;
-    default: hipLaunchKernelGGL((k_reindex<D, 4, F4>), grid, block, 0, s, a); break;
+    case 1: hipLaunchKernelGGL((k_reindex<D, 1, F4, BPW>), grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((k_reindex<D, 2, F4, BPW>), grid, block, 0, s, a); break;
+    case 3: hipLaunchKernelGGL((k_reindex<D, 3, F4, BPW>), grid, block, 0, s, a); break;
+    default: hipLaunchKernelGGL((k_reindex<D, 4, F4, BPW>), grid, block, 0, s, a); break;
   }
   return hipGetLastError();
+}
+
+template <int D, bool F4>
+hipError_t launch_d(const ReindexArgs& a, hipStream_t s) {
+  if (a.blocks_per_wg == kReindexBlocksWide) return launch_db<D, F4, kReindexBlocksWide>(a, s);
+  return launch_db<D, F4, kReindexBlocks>(a, s);
 }
 
 }  // namespace
