@@ -172,21 +172,25 @@ size_t reindex_ws(const csa2_dims* d, const csa2_queries* q) {
   return align256((size_t)q->n_q * 4) + align256((size_t)q->n_q * d->pool_blocks * 8 * 4);
 }
 
-// Pool blocks per Reindex scoring workgroup: 64, or 128 when 64-block
-// workgroups would exceed two per CU (the grid then takes several rounds,
-// and fewer, longer workgroups measured faster: 42.5 against 56.9 us per
-// layer for 32 queries; at 1 and 8 queries 64 is faster).
-// CSA2_REINDEX_BLOCKS (64 or 128) overrides.  Called after check_device.
+// Pool blocks per Reindex scoring workgroup: 32 when 32-block workgroups
+// fit in one per CU (a batch of a few queries: more of them share the
+// scoring), 64 when 64-block workgroups fit in two per CU, else 128 (the
+// grid takes several rounds, and fewer, longer workgroups are faster).
+// Measured per Reindex call: 1 query 14.4 / 15.4 us (32 / 64), 8 queries
+// 19.2 / 25.8 us (64 / 32), 32 queries 42.5 / 56.9 us (128 / 64).
+// CSA2_REINDEX_BLOCKS (32, 64 or 128) overrides.  Called after check_device.
 int reindex_blocks_per_wg(const csa2_dims* d, const csa2_queries* q) {
   int dev = 0;
   int bpw = kReindexBlocks;
   if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < 64 && g_cus[dev] > 0) {
-    const int64_t wgs = (int64_t)q->n_q * ((d->pool_blocks + kReindexBlocks - 1) / kReindexBlocks);
-    if (wgs > 2 * (int64_t)g_cus[dev]) bpw = kReindexBlocksWide;
+    const int64_t cus = g_cus[dev];
+    const int64_t wgs32 = (int64_t)q->n_q * ((d->pool_blocks + kReindexBlocksNarrow - 1) / kReindexBlocksNarrow);
+    const int64_t wgs64 = (int64_t)q->n_q * ((d->pool_blocks + kReindexBlocks - 1) / kReindexBlocks);
+    bpw = wgs32 <= cus ? kReindexBlocksNarrow : wgs64 <= 2 * cus ? kReindexBlocks : kReindexBlocksWide;
   }
   if (const char* env = getenv("CSA2_REINDEX_BLOCKS")) {
     const int v = atoi(env);
-    if (v == kReindexBlocks || v == kReindexBlocksWide) bpw = v;
+    if (v == kReindexBlocks || v == kReindexBlocksWide || v == kReindexBlocksNarrow) bpw = v;
   }
   return bpw;
 }

@@ -408,17 +408,16 @@ def test_pool_paths_agree(case):
 
 
 def test_reindex_workgroup_sizes_agree(case):
-    """Reindex scored by 64-block and by 128-block workgroups (the size the
-    library picks for batches whose grid would take several rounds) selects
-    the same Top-K with bit-identical scores: the per-position arithmetic
-    does not depend on how the pool is split."""
+    """Reindex scored by 32-, 64- and 128-block workgroups (the library picks
+    by batch size) selects the same Top-K with bit-identical scores: the
+    per-position arithmetic does not depend on how the pool is split."""
     name, g, lay = case
     csa2 = g.csa2
     pool, cnt, _ = g.full(0)
     q, wt = g.iq(0)
     idx_k = g.planes[0][0]
     outs = []
-    for bpw in ("64", "128"):
+    for bpw in ("64", "128", "32"):
         os.environ["CSA2_REINDEX_BLOCKS"] = bpw
         try:
             ts = torch.empty(g.w.n_q, g.w.dims.topk, dtype=torch.float32, device="cuda")
@@ -427,13 +426,14 @@ def test_reindex_workgroup_sizes_agree(case):
         finally:
             del os.environ["CSA2_REINDEX_BLOCKS"]
     torch.cuda.synchronize()
-    (tk0, tc0, ts0), (tk1, tc1, ts1) = outs
-    assert torch.equal(tc0, tc1), f"{name}: Top-K counts differ between workgroup sizes"
-    for qi in range(g.w.n_q):
-        k = int(tc0[qi])
-        assert torch.equal(tk0[qi, :k], tk1[qi, :k]), f"{name} q{qi}: Top-K differs between workgroup sizes"
-        assert torch.equal(ts0[qi, :k].view(torch.int32), ts1[qi, :k].view(torch.int32)), \
-            f"{name} q{qi}: Top-K scores differ between workgroup sizes"
+    tk0, tc0, ts0 = outs[0]
+    for tk1, tc1, ts1 in outs[1:]:
+        assert torch.equal(tc0, tc1), f"{name}: Top-K counts differ between workgroup sizes"
+        for qi in range(g.w.n_q):
+            k = int(tc0[qi])
+            assert torch.equal(tk0[qi, :k], tk1[qi, :k]), f"{name} q{qi}: Top-K differs between workgroup sizes"
+            assert torch.equal(ts0[qi, :k].view(torch.int32), ts1[qi, :k].view(torch.int32)), \
+                f"{name} q{qi}: Top-K scores differ between workgroup sizes"
 
 
 def test_reindex_workspace_reuse(case):
