@@ -195,6 +195,28 @@ int reindex_blocks_per_wg(const csa2_dims* d, const csa2_queries* q) {
   return bpw;
 }
 
+// Marking workgroups per query: one per chunk, unless that grid would exceed
+// two workgroups per CU; then as many as keep it to two per CU, each taking
+// a run of chunks (256 queries with 16 chunks each: 198 us of marking with a
+// workgroup per chunk, 16 rounds).  CSA2_POOL_MARK_WGS overrides (1..chunks).
+// Called after check_device.
+int pool_mark_wgs(const csa2_queries* q, int chunks) {
+  int dev = 0;
+  int wpq = chunks;
+  if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < 64 && g_cus[dev] > 0) {
+    const int64_t cap = 2 * (int64_t)g_cus[dev];
+    if ((int64_t)q->n_q * chunks > cap) {
+      const int64_t w = cap / q->n_q;
+      wpq = (int)(w < 1 ? 1 : w);
+    }
+  }
+  if (const char* env = getenv("CSA2_POOL_MARK_WGS")) {
+    const int v = atoi(env);
+    if (v >= 1) wpq = v;
+  }
+  return wpq < chunks ? wpq : chunks;
+}
+
 struct AttendPlan { int hg, splits, split_entries; };
 
 // A small batch is spread over more workgroups by splitting each query's
@@ -350,6 +372,7 @@ static csa2_status run_pool(const csa2_dims* d, const csa2_queries* q, const flo
   pa.bscore = block_scores; pa.ld = ld_block_scores; pa.n_visible = q->n_visible;
   pa.n_q = q->n_q; pa.swa = d->swa; pa.pool = d->pool_blocks;
   pa.chunks = pool_chunks(d, q);
+  pa.mark_wgs = pool_mark_wgs(q, pa.chunks);
   pa.mm_cap = pool_mm_cap(d, q);
   pa.nw_cap = (int)((max_blocks(d, q) + 31) / 32);
   pa.small = max_blocks(d, q) <= kPoolSmallBlocks;

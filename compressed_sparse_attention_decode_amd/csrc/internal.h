@@ -14,7 +14,8 @@ struct PoolArgs {
   int64_t ld;
   const int32_t* n_visible;
   int n_q, swa, pool;
-  int chunks;                // kPoolChunk-block chunks per query (grid of K1-K3)
+  int chunks;                // kPoolChunk-block chunks per query (grid of K1, K2)
+  int mark_wgs;              // marking workgroups per query (1..chunks; each takes a run of chunks)
   uint32_t* ws;              // [n_q, ws_stride] words (histogram, chunk results)
   int64_t ws_stride;
   int mm_cap;                // (min, max) key pairs per query in the workspace

@@ -475,38 +475,57 @@ __device__ __forceinline__ void pool_final(const PoolArgs& a, int q, const PoolW
   for (int i = tid * 4; i < kHistBins; i += NT * 4) *reinterpret_cast<v4u*>(w.hist + i) = v4u{0u, 0u, 0u, 0u};
 }
 
-// Marking per chunk; the last chunk workgroup of a query to finish (counted
-// in the workspace's done word, which K2 clears) runs the final step.  The
-// marks cross workgroups through memory: after a store drain and a barrier,
-// one release fence per workgroup publishes them before it counts itself
-// in, and the last one's acquire fence makes the others' visible.
+// Marking per chunk; the last marking workgroup of a query to finish
+// (counted in the workspace's done word, which K2 clears) runs the final
+// step.  A workgroup marks a run of its query's chunks (one chunk, unless the
+// grid would exceed two workgroups per CU: then fewer workgroups take several
+// chunks each, and the key range and the bin b* are found once per
+// workgroup).  The marks cross workgroups through memory: after a store
+// drain and a barrier, one release fence per workgroup publishes them before
+// it counts itself in, and the last one's acquire fence makes the others'
+// visible.
 __global__ __launch_bounds__(kCT) void k_pool_mark(PoolArgs a) {
   extern __shared__ uint32_t s_dyn[];
   __shared__ uint32_t s_scan[2 * (kCT / 64)];
   __shared__ uint32_t s_misc[2];
   __shared__ uint32_t s_ccount;
   __shared__ uint32_t s_last;
-  const int q = blockIdx.x / a.chunks, g = blockIdx.x % a.chunks;
+  const int WPQ = a.mark_wgs;
+  const int q = blockIdx.x / WPQ, wq = blockIdx.x % WPQ;
+  const int cpw = (a.chunks + WPQ - 1) / WPQ;
+  const int g0 = wq * cpw, g1 = min(a.chunks, g0 + cpw);
   const int tid = threadIdx.x, lane = tid & 63;
-  const int base = g * kPoolChunk;
   const PoolWs w = pool_ws(a, q);
+  const float* bsq = a.bscore + (int64_t)q * a.ld;
   ChunkKeys c;
-  c.load(a.bscore + (int64_t)q * a.ld, base, a.ld, tid);
+  c.load(bsq, g0 * kPoolChunk, a.ld, tid);     // the first chunk's scores, before the rest
   HistSlice<kCT> h;
   h.load(w.hist);
   KeyRange<kCT> kr;
   kr.load(a, w);
   const int nb = query_blocks(a, q);
   MarkState ms = {false, 0u, 0u, 0u, 0u};
-  if (nb > a.pool && base < nb) {
-    c.finish(base, nb, tid);
-    if (tid == 0) s_ccount = 0;
+  const bool marks = nb > a.pool && g0 < g1 && g0 * kPoolChunk < nb;   // uniform
+  Bins b{};
+  uint32_t bstar = 0;
+  if (marks) {
     uint32_t kmin, kmax;
     kr.reduce(a, w, nb, s_scan, &kmin, &kmax);
-    const Bins b = bins_for(kmin, kmax);
+    b = bins_for(kmin, kmax);
     find_bstar<kCT>(h, (uint32_t)a.pool, s_scan, s_misc);
-    const uint32_t bstar = s_misc[0];
+    bstar = s_misc[0];
     ms = {true, kmin, kmax, bstar, s_misc[1]};
+  }
+  for (int g = g0; g < g1; ++g) {
+    const int base = g * kPoolChunk;
+    if (!(marks && base < nb)) {
+      if (tid == 0) w.cnt[g] = 0;
+      continue;
+    }
+    if (g != g0) c.load(bsq, base, a.ld, tid);
+    c.finish(base, nb, tid);
+    if (tid == 0) s_ccount = 0;
+    __syncthreads();                        // the count is cleared (and the last chunk's read)
 
     uint32_t* ck = w.ckey + (int64_t)g * kPoolChunkCand;
     int32_t* cj = w.cblk + (int64_t)g * kPoolChunkCand;
@@ -549,15 +568,13 @@ __global__ __launch_bounds__(kCT) void k_pool_mark(PoolArgs a) {
     }
     __syncthreads();
     if (tid == 0) w.cnt[g] = s_ccount;
-  } else if (tid == 0) {
-    w.cnt[g] = 0;
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's stores have reached L2
   __syncthreads();
   if (tid == 0) {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
     const uint32_t prev = __hip_atomic_fetch_add(w.done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    s_last = prev == (uint32_t)(a.chunks - 1);
+    s_last = prev == (uint32_t)(WPQ - 1);
     if (s_last) {
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
       *w.done = 0;
@@ -635,6 +652,7 @@ hipError_t launch_pool_select(const PoolArgs& a, hipStream_t s) {
     return hipGetLastError();
   }
   const dim3 grid((unsigned)(a.n_q * a.chunks));
+  const dim3 mgrid((unsigned)(a.n_q * a.mark_wgs));
   const size_t lds = pool_final_lds(a.nw_cap);
   // dynamic LDS above the default limit must be allowed once per size
   static size_t lds_allowed = 0;
@@ -646,7 +664,7 @@ hipError_t launch_pool_select(const PoolArgs& a, hipStream_t s) {
   }
   if (!a.have_minmax) hipLaunchKernelGGL(k_pool_minmax, grid, dim3(kCT), 0, s, a);
   hipLaunchKernelGGL(k_pool_hist, grid, dim3(kCT), 0, s, a);
-  hipLaunchKernelGGL(k_pool_mark, grid, dim3(kCT), lds, s, a);
+  hipLaunchKernelGGL(k_pool_mark, mgrid, dim3(kCT), lds, s, a);
   return hipGetLastError();
 }
 

@@ -376,7 +376,8 @@ def test_pool_paths_agree(case):
     """csa2_index_full (scan-prepared pool workspace), csa2_index_scan +
     csa2_index_pool (the pool's own key-range pass), repeated pool calls on
     one scan-prepared workspace, and the chunked pool kernels forced where
-    the one-workgroup selection would run give the same pool bit for bit."""
+    the one-workgroup selection would run (with a marking workgroup per
+    chunk, and with one per query) give the same pool bit for bit."""
     name, g, lay = case
     w = g.w
     csa2 = g.csa2
@@ -387,13 +388,19 @@ def test_pool_paths_agree(case):
     ws = torch.empty(csa2.workspace_pool(g.dims, g.batch) + 256, dtype=torch.uint8, device="cuda")
     bs2 = csa2.index_scan(g.dims, g.batch, q, wt, g.idx_k, pool_ws=ws)
     outs = [csa2.index_pool(g.dims, g.batch, bs2, ws=ws, from_scan=True) for _ in range(3)]
-    # the chunked kernels also where the one-workgroup selection would run
+    # the chunked kernels also where the one-workgroup selection would run,
+    # and with one marking workgroup per query taking all of its chunks (the
+    # layout large batches use)
     os.environ["CSA2_POOL_SMALL"] = "0"
     try:
         outs.append(csa2.index_pool(g.dims, g.batch, bs2, ws=ws, from_scan=True))
         outs.append(csa2.index_pool(g.dims, g.batch, bs))
+        os.environ["CSA2_POOL_MARK_WGS"] = "1"
+        outs.append(csa2.index_pool(g.dims, g.batch, bs2, ws=ws, from_scan=True))
+        outs.append(csa2.index_pool(g.dims, g.batch, bs))
     finally:
         del os.environ["CSA2_POOL_SMALL"]
+        os.environ.pop("CSA2_POOL_MARK_WGS", None)
     torch.cuda.synchronize()
     nb = csa2.n_blocks(g.dims, g.batch)
     for qi in range(w.n_q):     # rows are written up to each query's own block count
