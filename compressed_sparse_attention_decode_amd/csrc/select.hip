@@ -236,29 +236,39 @@ __global__ __launch_bounds__(kCT) void k_pool_minmax(PoolArgs a) {
 }
 
 // ---------------------------------------------------------------- K2
+// A workgroup histograms a run of its query's chunks (one chunk, unless
+// that grid would exceed two workgroups per CU; the runs are the marking
+// kernel's) into LDS, then adds the nonzero bins to the query's histogram.
 __global__ __launch_bounds__(kCT) void k_pool_hist(PoolArgs a) {
   __shared__ uint32_t s_hist[kHistBins];
   __shared__ uint32_t s_scan[2 * (kCT / 64)];
-  const int q = blockIdx.x / a.chunks, g = blockIdx.x % a.chunks, tid = threadIdx.x;
-  const int base = g * kPoolChunk;
+  const int WPQ = a.mark_wgs;
+  const int q = blockIdx.x / WPQ, wq = blockIdx.x % WPQ, tid = threadIdx.x;
+  const int cpw = (a.chunks + WPQ - 1) / WPQ;
+  const int g0 = wq * cpw, g1 = min(a.chunks, g0 + cpw);
   const PoolWs w = pool_ws(a, q);
+  const float* bsq = a.bscore + (int64_t)q * a.ld;
   ChunkKeys c;
-  c.load(a.bscore + (int64_t)q * a.ld, base, a.ld, tid);
+  c.load(bsq, g0 * kPoolChunk, a.ld, tid);
   KeyRange<kCT> kr;
   kr.load(a, w);
-  if (g == 0 && tid == 0) *w.done = 0;
+  if (wq == 0 && tid == 0) *w.done = 0;
   const int nb = query_blocks(a, q);
-  if (nb <= a.pool || base >= nb) return;
-  c.finish(base, nb, tid);
+  if (nb <= a.pool || g0 >= g1 || g0 * kPoolChunk >= nb) return;
   for (int i = tid; i < kHistBins; i += kCT) s_hist[i] = 0;
   uint32_t kmin, kmax;
   kr.reduce(a, w, nb, s_scan, &kmin, &kmax);     // its barriers order the clear
   const Bins b = bins_for(kmin, kmax);
+  for (int g = g0; g < g1 && g * kPoolChunk < nb; ++g) {
+    const int base = g * kPoolChunk;
+    if (g != g0) c.load(bsq, base, a.ld, tid);
+    c.finish(base, nb, tid);
 #pragma unroll
-  for (int u = 0; u < kCU; ++u) {
+    for (int u = 0; u < kCU; ++u) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      if (c.vm[u] >> e & 1u) atomicAdd(&s_hist[b.bin(c.k[u][e])], 1u);
+      for (int e = 0; e < 4; ++e)
+        if (c.vm[u] >> e & 1u) atomicAdd(&s_hist[b.bin(c.k[u][e])], 1u);
+    }
   }
   __syncthreads();
   for (int i = tid; i < kHistBins; i += kCT) {
@@ -663,7 +673,7 @@ hipError_t launch_pool_select(const PoolArgs& a, hipStream_t s) {
     lds_allowed = lds;
   }
   if (!a.have_minmax) hipLaunchKernelGGL(k_pool_minmax, grid, dim3(kCT), 0, s, a);
-  hipLaunchKernelGGL(k_pool_hist, grid, dim3(kCT), 0, s, a);
+  hipLaunchKernelGGL(k_pool_hist, mgrid, dim3(kCT), 0, s, a);
   hipLaunchKernelGGL(k_pool_mark, mgrid, dim3(kCT), lds, s, a);
   return hipGetLastError();
 }
