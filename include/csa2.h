@@ -116,9 +116,9 @@ typedef struct csa2_queries {
   const int32_t* n_visible;
 } csa2_queries;
 
-/* Paged caches (serving integration: the pages' stack appends each new
- * token's main KV as a Full layer runs — [atlas] §3.2 mode table, "Full
- * writes main KV" — and a serving cache grows page by page).  In a call that
+/* Paged caches (serving integration: in [atlas] §3.2's mode figure a Full
+ * layer writes each new token's main KV as decoding runs, and a serving cache
+ * grows page by page; [akhunji], serving highlights).  In a call that
  * takes a csa2_pages, position p of query q's sequence lives at row
  *   table[seq_base[q] + p / page_size] * page_size + p % page_size
  * of every per-position plane the call reads (indexer keys and their scales;
