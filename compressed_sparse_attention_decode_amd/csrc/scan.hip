@@ -13,7 +13,9 @@
 //    (l & 15).  Keys stream with direct-to-LDS raw buffer loads (rows >= c
 //    read as zero, so the tail needs no branches) through a ring of R LDS
 //    slots per wave, R - 1 steps in flight, which costs no VGPRs (the f16
-//    query fragments already hold 64 per lane);
+//    query fragments already hold 64 per lane).  Each load instruction covers
+//    whole 128-byte lines with the nontemporal hint: the keys are read once,
+//    and a line split over two instructions would be fetched twice;
 //  * fp8 keys and queries are converted to f16 in registers (exact) and
 //    contracted with v_mfma_f32_16x16x32_f16: A = 16 query heads, B = 16
 //    positions, K = 32 dims per instruction.  The product and the fp32
@@ -38,11 +40,10 @@
 namespace csa2 {
 namespace {
 
-// Byte offset, inside a key row, of the lane's 16-byte chunk `h` (h = 0, 1).
-// For d = 128 chunk 0 covers bytes [16gq, 16gq+16) and chunk 1 bytes
-// [64+16gq, ...): each load instruction reads whole 64-byte halves of 16 rows.
-// The query fragments use the same byte -> k-slot map, so the permutation of
-// the reduction dimension cancels in every dot product.
+// Byte offset, inside a key row, of the MFMA lane's 16-byte chunk `h` (h = 0,
+// 1).  For d = 128 chunk 0 covers bytes [16gq, 16gq+16) and chunk 1 bytes
+// [64+16gq, ...).  The query fragments use the same byte -> k-slot map, so the
+// permutation of the reduction dimension cancels in every dot product.
 template <int D>
 __device__ __forceinline__ int key_chunk(int gq, int h) {
   return D == 128 ? h * 64 + gq * 16 : gq * 16;
@@ -126,51 +127,79 @@ __global__ __launch_bounds__(64 * NW) void k_scan(ScanArgs a) {
   }
   const int pg0 = PG ? p_begin >> a.page_shift : 0;   // the tile's first page
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  // Whole-line key loads.  The reduction dimension is split into 16-byte
+  // chunks: MFMA lane (col, gq) needs chunk gq (and, for d = 128, chunk 4 + gq)
+  // of row col.  A load instruction instead gives lane l one chunk of a row so
+  // that it covers whole 128-byte lines, and the chunk index is rotated by the
+  // row so that the MFMA-side LDS reads of 8 consecutive lanes (8 rows, one
+  // chunk) fall on 8 different 16-byte bank groups.
+  //   d = 128: instruction h holds rows 8h .. 8h+7; lane l = 8a + j holds row
+  //            8h + a, chunk (j - a) mod 8.
+  //   d = 64:  one instruction holds the 16 rows; lane l = 4r + j holds row r,
+  //            chunk (j - (r >> 1)) mod 4.
+  const int ld_row = D == 128 ? lane >> 3 : lane >> 2;
+  const int ld_chunk = D == 128 ? ((lane & 7) - (lane >> 3)) & 7 : ((lane & 3) - ((lane >> 3) & 3)) & 3;
+  int rd_pos[NH];
+#pragma unroll
+  for (int h = 0; h < NH; ++h) {
+    const int ch = gq + 4 * h;               // the chunk this lane's MFMA operand needs
+    rd_pos[h] = D == 128 ? (col >> 3) * 64 + (col & 7) * 8 + ((ch + (col & 7)) & 7)
+                         : col * 4 + ((ch + ((col >> 1) & 3)) & 3);
+  }
 
   // this wave's steps are s_k = wave + NW k, k < ns, streamed through R LDS
   // slots with R - 1 steps of direct-to-LDS loads in flight.  The loads are
   // issued as inline asm so that the compiler neither tracks them (it would
   // wait for every one of them before each LDS read) nor moves them; the
   // waits below count them explicitly (vector-memory ops retire in order).
-  const int ns = wave < nsteps ? (nsteps - wave + NW - 1) / NW : 0;
-  auto issue = [&](int k) {
+  // (wave-uniform: the loop below branches on scalars, with no exec masking)
+  const int ns = __builtin_amdgcn_readfirstlane(wave_u < nsteps ? (nsteps - wave_u + NW - 1) / NW : 0);
+  // step k goes to ring slot sl = k mod R; every call site passes sl as a
+  // constant (the loop is unrolled by R), so slot addresses are immediates
+  auto issue = [&](int k, int sl) {
     const int row0 = p_begin + (wave + NW * k) * 16;
     // the step's 16 rows are 16-aligned, so they share one page
     uint32_t prow0 = (uint32_t)row0;
     if constexpr (PG)
       prow0 = ((uint32_t)s_pg[(row0 >> a.page_shift) - pg0] << a.page_shift) |
               ((uint32_t)row0 & ((1u << a.page_shift) - 1u));
-    const uint32_t row = !PG || row0 + col < c ? (prow0 + col) * RB : kOob;
-    const uint32_t slot = (uint32_t)(uintptr_t)(lds_void*)&s_ring[wave_u][k % R][0];
+    const uint32_t slot = (uint32_t)(uintptr_t)(lds_void*)&s_ring[wave_u][sl][0];
     if constexpr (F4) {
+      // 16 rows of 64 code bytes: one whole KiB (lane l: row l & 15, bytes 16 (l >> 4) .. +16)
+      const uint32_t row = !PG || row0 + col < c ? (prow0 + col) * RB : kOob;
       const uint32_t m0 = (uint32_t)__builtin_amdgcn_readfirstlane((int)slot);
-      asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+      asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen nt lds"
                    :: "s"(m0), "v"(row + gq * 16), "s"(rsrc) : "memory", "m0");
       // the step's 16 x 8 scale bytes: dword `lane` of them for lanes < 32
       const uint32_t m1 = (uint32_t)__builtin_amdgcn_readfirstlane((int)(slot + 1024));
       const uint32_t so = lane < 32 && (!PG || row0 + (lane >> 1) < c) ? prow0 * SB + lane * 4 : kOob;
-      asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+      asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen nt lds"
                    :: "s"(m1), "v"(so), "s"(srsrc) : "memory", "m0");
     } else {
+      // each load instruction reads whole 128-byte lines (1 KiB contiguous):
+      // lane l -> (row ld_row + 8h or 16 rows of 64 B, chunk ld_chunk), stored
+      // at LDS position l of the instruction's KiB
 #pragma unroll
       for (int h = 0; h < NH; ++h) {
+        const int r = ld_row + 8 * h;
+        const uint32_t row = !PG || row0 + r < c ? (prow0 + r) * RB + ld_chunk * 16 : kOob;
         const uint32_t m0 = (uint32_t)__builtin_amdgcn_readfirstlane((int)(slot + h * 1024));
-        asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-                     :: "s"(m0), "v"(row + key_chunk<D>(gq, h)), "s"(rsrc) : "memory", "m0");
+        asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen nt lds"
+                     :: "s"(m0), "v"(row), "s"(rsrc) : "memory", "m0");
       }
     }
   };
   // fetch: wait until step k has landed (keeping the younger steps in
   // flight), refill the ring, read the lane's bytes and convert to f16
-  auto fetch = [&](int k, v8h* kf) {
+  auto fetch = [&](int k, int sl, v8h* kf) {
     if (k + R - 1 < ns) {
       wait_lgkmcnt0();                 // the slot's previous reads are done
-      issue(k + R - 1);
+      issue(k + R - 1, (sl + R - 1) % R);
       wait_vmcnt<(R - 1) * LPS>();     // step k has landed; R - 1 younger in flight
     } else {
       wait_vmcnt<0>();
     }
-    const uint8_t* slot = &s_ring[wave_u][k % R][0];
+    const uint8_t* slot = &s_ring[wave_u][sl][0];
     if constexpr (F4) {
       // the lane's 32 channels: four code dwords (8 channels each) and the
       // scales of its two 16-channel groups (row col, scale bytes 2gq, 2gq + 1)
@@ -186,7 +215,7 @@ __global__ __launch_bounds__(64 * NW) void k_scan(ScanArgs a) {
       uint32_t kb[4 * NH];
 #pragma unroll
       for (int h = 0; h < NH; ++h) {
-        const v4u x = *reinterpret_cast<const v4u*>(slot + h * 1024 + lane * 16);
+        const v4u x = *reinterpret_cast<const v4u*>(slot + rd_pos[h] * 16);
         kb[4 * h + 0] = x[0]; kb[4 * h + 1] = x[1]; kb[4 * h + 2] = x[2]; kb[4 * h + 3] = x[3];
       }
 #pragma unroll
@@ -202,7 +231,9 @@ __global__ __launch_bounds__(64 * NW) void k_scan(ScanArgs a) {
       for (int t = 0; t < HT; ++t) acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qf[t][kc], kf[kc], acc[t], 0, 0, 0);
     }
   };
-  auto epilogue = [&](const v4f* acc, int k) {
+  // last: the wave's final step, the only one that can reach past c (the
+  // tile's last step is the last step of the wave that has it)
+  auto epilogue = [&](const v4f* acc, int k, bool last) {
     // four independent partial sums (no 16-long dependent chain)
     float pp[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
@@ -213,7 +244,10 @@ __global__ __launch_bounds__(64 * NW) void k_scan(ScanArgs a) {
     const float part = sum_rows4((pp[0] + pp[1]) + (pp[2] + pp[3]));
     const int s = wave + NW * k;
     const int p0 = p_begin + s * 16;
-    const float v = max_lanes8((p0 + col < c) ? part : -__builtin_inff());
+    // positions >= c (only in a wave's last step) score -inf
+    float v = part;
+    if (last) v = p0 + col < c ? part : -__builtin_inff();
+    v = max_lanes8(v);
     if (lane < 16 && (lane & 7) == 0) s_bs[s * 2 + (lane >> 3)] = v;
   };
 
@@ -268,7 +302,9 @@ __global__ __launch_bounds__(64 * NW) void k_scan(ScanArgs a) {
     __syncthreads();
   }
   const int pro = min(R - 1, ns);
-  for (int k = 0; k < pro; ++k) issue(k);
+#pragma unroll
+  for (int k = 0; k < R - 1; ++k)
+    if (k < pro) issue(k, k);
   if (pro == R - 1) wait_vmcnt<(R - 1) * LPS>();   // the query loads (older) have landed
   else wait_vmcnt<0>();
   __syncthreads();
@@ -307,17 +343,22 @@ __global__ __launch_bounds__(64 * NW) void k_scan(ScanArgs a) {
     // of MFMA results, which would stall on the MFMAs in flight)
     v8h kfa[KC], kfb[KC];
     v4f acca[HT], accb[HT];
-    fetch(0, kfa);
-    for (int k = 0;; k += 2) {
-      contract(kfa, acca);                       // step k
-      if (k > 0) epilogue(accb, k - 1);
-      if (k + 1 >= ns) { epilogue(acca, k); break; }
-      fetch(k + 1, kfb);
-      contract(kfb, accb);                       // step k + 1
-      epilogue(acca, k);
-      if (k + 2 >= ns) { epilogue(accb, k + 1); break; }
-      fetch(k + 2, kfa);
+    fetch(0, 0, kfa);
+    for (int k0 = 0;; k0 += R) {
+#pragma unroll
+      for (int u = 0; u < R; u += 2) {
+        const int k = k0 + u;                    // step k uses slot u, step k + 1 slot u + 1
+        contract(kfa, acca);                     // step k
+        if (k > 0) epilogue(accb, k - 1, false);
+        if (k + 1 >= ns) { epilogue(acca, k, true); goto stream_done; }
+        fetch(k + 1, u + 1, kfb);
+        contract(kfb, accb);                     // step k + 1
+        epilogue(acca, k, false);
+        if (k + 2 >= ns) { epilogue(accb, k + 1, true); goto stream_done; }
+        fetch(k + 2, (u + 2) % R, kfa);
+      }
     }
+  stream_done:;
   }
   __syncthreads();
   // block scores of the tile, one coalesced store
