@@ -441,25 +441,93 @@ def measure(w: wl.Workload, steps: int, warmup: int, replicas: int):
 
 
 # ---------------------------------------------------------------- CPU oracle
-def cpu_baseline(w: wl.Workload, st: DeviceState, step: Step, seconds: float):
-    """The oracle on this host's cores over sampled queries of the same step;
-    also checks those queries' GPU results (last timed step) against it."""
+def _oracle_query(w, oq, layers, keys, qi, gpu=None):
+    """The oracle's calls for one query of a step (Full scan + pool, then
+    Reindex + attention per layer, and its share of the step's fresh-entry
+    encode).  Returns (timed seconds, parity record updates).  Inputs the
+    GPU side also holds resident (keys, queries, encoded cache rows, window
+    rows) are prepared untimed.  With `gpu` (pool, count, topk, topk count,
+    out, lse as numpy arrays, and a callable running the GPU attention of a
+    layer on given Top-K rows) the query's GPU results are checked against
+    the oracle's: pool and Top-K within the selection band, attention on the
+    GPU's own set when it is the oracle's, else the GPU attention recomputed
+    on the oracle's set."""
+    import numpy as np
+    import oracle
+    from tests._harness import check_attention, check_set, u16
+    timed = 0.0
+    par = {"pool_exact": 0, "topk_exact": 0, "attention_checked": 0, "attention_on_oracle_set": 0, "max_attn_rel": 0.0}
+    qs = {layer: oq.iq(layer) for layer in [0] + list(layers)}
+    t0 = time.perf_counter()
+    rpool, rb, _ = oracle.index_full(qs[0][0], qs[0][1], keys, oq.n, w.dims.swa, w.dims.pool_blocks)
+    timed += time.perf_counter() - t0
+    if gpu is not None:
+        pool, pcnt = gpu["pool"], gpu["pcnt"]
+        check_set(pool[qi, :pcnt[qi]], rpool, lambda j: rb[j], f"q{qi} pool")
+        par["pool_exact"] += int(np.array_equal(pool[qi, :pcnt[qi]], rpool))
+    for i, layer in enumerate(layers):
+        t0 = time.perf_counter()
+        keep, _, _ = oracle.reindex(qs[layer][0], qs[layer][1], keys, rpool, oq.c, w.dims.topk)
+        timed += time.perf_counter() - t0
+        rows = oq.base + keep
+        lat = np.asarray(wl.latent_at(w, rows).view(torch.int16).numpy(), dtype=np.uint16)
+        rp = np.asarray(wl.rope_at(w, rows).view(torch.int16).numpy(), dtype=np.uint16)
+        codes, scales = oracle.encode_kv(lat, w.dims.kv_group)      # the cache is encoded ahead of time
+        win = oq.base + np.arange(oq.c, oq.n)
+        swa = np.concatenate([wl.latent_at(w, win).view(torch.int16).numpy(),
+                              wl.rope_at(w, win).view(torch.int16).numpy()], axis=1).astype(np.uint16)
+        ql = u16(wl.q_latent(w, layer, qi, 1)[0])
+        qr = u16(wl.q_rope(w, layer, qi, 1)[0])
+        t0 = time.perf_counter()
+        ro, rl = oracle.attend(ql, qr, 1.0, oracle.gather_entries(codes, scales, rp, swa))
+        timed += time.perf_counter() - t0
+        if gpu is not None:
+            got = gpu["tk"][i, qi, :gpu["tc"][i, qi]]
+            check_set(got, keep, lambda p: oq.scores_at(layer, p), f"q{qi} layer {layer} topk")
+            if np.array_equal(got, keep):
+                par["topk_exact"] += 1
+                o, l = gpu["out"][i, qi], gpu["lse"][i, qi]
+            else:
+                o, l = gpu["attend_on"](i, layer, qi, keep)
+                par["attention_on_oracle_set"] += 1
+            e = check_attention(o, l, ro, rl, f"q{qi} layer {layer} attention")
+            par["attention_checked"] += 1
+            par["max_attn_rel"] = max(par["max_attn_rel"], e)
+    if w.fresh_encode:
+        # this query's share of the step's fresh-entry encode
+        share = max(1, w.fresh_encode // w.n_q)
+        e0 = (qi * share) % max(1, w.fresh_encode - share + 1)
+        lat = np.asarray(wl.fresh_latent(w, 0, e0, share).view(torch.int16).numpy(), dtype=np.uint16)
+        t0 = time.perf_counter()
+        oracle.encode_kv(lat, w.dims.kv_group)
+        timed += time.perf_counter() - t0
+    return timed, par
+
+
+def cpu_baseline(w: wl.Workload, st: DeviceState, step: Step, seconds: float, one_thread: bool = False):
+    """The oracle on this host's cores over queries of the same step, cycling
+    over them until `seconds` of oracle time (at least one query); the first
+    pass also checks those queries' GPU results (last timed step) against it.
+    Returns (cpu_baseline record, parity record)."""
     import numpy as np
     from threadpoolctl import threadpool_info, threadpool_limits
-    from tests._harness import OracleQuery, check_attention, check_set
-    import oracle
+    from tests._harness import OracleQuery, with_oracle_rows
 
     cores = len(os.sched_getaffinity(0))
     lay = st.lay
-    pool = step.pool.cpu().numpy()
-    pcnt = step.pcnt.cpu().numpy()
-    tk = step.tk.cpu().numpy()
-    tc = step.tc.cpu().numpy()
-    out = step.out.cpu().numpy()
-    lse = step.lse.cpu().numpy()
-    timed = 0.0
-    done = 0
-    parity = {"queries": 0, "pool_exact": 0, "topk_exact": 0, "attention_checked": 0, "max_attn_rel": 0.0}
+    gpu = {"pool": step.pool.cpu().numpy(), "pcnt": step.pcnt.cpu().numpy(), "tk": step.tk.cpu().numpy(),
+           "tc": step.tc.cpu().numpy(), "out": step.out.cpu().numpy(), "lse": step.lse.cpu().numpy()}
+
+    def attend_on(i, layer, qi, keep):
+        tk2, tc2 = with_oracle_rows(step.tk[i], step.tc[i], {qi: keep})
+        o, l = st.attend(layer, tk2, tc2)
+        torch.cuda.synchronize()
+        return o[qi].cpu().numpy(), l[qi].cpu().numpy()
+    gpu["attend_on"] = attend_on
+
+    timed, done, checked = 0.0, 0, 0
+    parity = {"queries": 0, "pool_exact": 0, "topk_exact": 0, "attention_checked": 0, "attention_on_oracle_set": 0,
+              "max_attn_rel": 0.0}
     order = list(range(w.n_q))
     first_pass = True           # later passes over the same queries only add timing
     with threadpool_limits(limits=cores):
@@ -467,85 +535,34 @@ def cpu_baseline(w: wl.Workload, st: DeviceState, step: Step, seconds: float):
         keys_cache = {}
         while timed < seconds or done == 0:
             if not order:
-                if seconds <= 0:
-                    break
                 order, first_pass = list(range(w.n_q)), False
             qi = order.pop(0)
             seq = qi // w.tokens_per_seq
             oq = OracleQuery(w, lay, qi, keys_cache.get(seq))
-            keys_cache[seq] = oq.keys
-            # untimed: the query's inputs (already resident on the GPU side)
-            qs = {layer: oq.iq(layer) for layer in [0] + step.layers}
-            t0 = time.perf_counter()
-            rpool, rb, _ = oracle.index_full(qs[0][0], qs[0][1], oq.keys, oq.n, w.dims.swa, w.dims.pool_blocks)
-            timed += time.perf_counter() - t0
+            keys_cache = {seq: oq.keys}
+            t, par = _oracle_query(w, oq, step.layers, oq.keys, qi, gpu if first_pass else None)
+            timed += t
+            done += 1
             if first_pass:
                 parity["queries"] += 1
-                check_set(pool[qi, :pcnt[qi]], rpool, lambda j: rb[j], f"q{qi} pool")
-                parity["pool_exact"] += int(np.array_equal(pool[qi, :pcnt[qi]], rpool))
-            for i, layer in enumerate(step.layers):
-                t0 = time.perf_counter()
-                keep, _, _ = oracle.reindex(qs[layer][0], qs[layer][1], oq.keys, rpool, oq.c, w.dims.topk)
-                timed += time.perf_counter() - t0
-                got = tk[i, qi, :tc[i, qi]]
-                if first_pass and np.array_equal(pool[qi, :pcnt[qi]], rpool):
-                    check_set(got, keep, lambda p: oq.scores_at(layer, p), f"q{qi} topk")
-                    parity["topk_exact"] += int(np.array_equal(got, keep))
-                # attention inputs: FP4 rows of the kept positions (the cache is
-                # encoded ahead of time on both sides), timed from decode on
-                rows = oq.base + keep
-                lat = np.asarray(wl.latent_at(w, rows).view(torch.int16).numpy(), dtype=np.uint16)
-                rp = np.asarray(wl.rope_at(w, rows).view(torch.int16).numpy(), dtype=np.uint16)
-                codes, scales = oracle.encode_kv(lat)
-                win = oq.base + np.arange(oq.c, oq.n)
-                swa = np.concatenate([wl.latent_at(w, win).view(torch.int16).numpy(),
-                                      wl.rope_at(w, win).view(torch.int16).numpy()], axis=1).astype(np.uint16)
-                from tests._harness import u16
-                ql = u16(wl.q_latent(w, layer, qi, 1)[0])
-                qr = u16(wl.q_rope(w, layer, qi, 1)[0])
-                t0 = time.perf_counter()
-                keys = oracle.gather_entries(codes, scales, rp, swa)
-                ro, rl = oracle.attend(ql, qr, 1.0, keys)
-                timed += time.perf_counter() - t0
-                if first_pass and np.array_equal(got, keep):
-                    e = check_attention(out[i, qi], lse[i, qi], ro, rl, f"q{qi} attention")
-                    parity["attention_checked"] += 1
-                    parity["max_attn_rel"] = max(parity["max_attn_rel"], e)
-            done += 1
+                for k in ("pool_exact", "topk_exact", "attention_checked", "attention_on_oracle_set"):
+                    parity[k] += par[k]
+                parity["max_attn_rel"] = max(parity["max_attn_rel"], par["max_attn_rel"])
     parity["max_attn_rel"] = float(f"{parity['max_attn_rel']:.3e}")
-    res = {"value": done / timed, "unit": "queries/s", "cores": int(threads), "kind": "oracle",
+    unit = "query-tokens/s" if w.tokens_per_seq > 1 else "queries/s"
+    res = {"value": done / timed, "unit": unit, "cores": int(threads), "kind": "oracle",
            "sample": f"{done} query passes over the {w.n_q} queries of one {w.name} step (Full scan + "
-                     f"pool, {len(step.layers)} Reindex + attention each), float64 NumPy, "
-                     f"{cores} host cores available", "seconds": round(timed, 2),
+                     f"pool, {len(step.layers)} Reindex + attention each"
+                     + (", its share of the fresh-entry encode" if w.fresh_encode else "")
+                     + f"), float64 NumPy, {cores} host cores available", "seconds": round(timed, 2),
            "host": _host_info(threads)}
-    if seconds > 0:
-        # the same oracle calls for query 0 on one thread (inputs prepared untimed)
+    if one_thread:
+        # the same oracle calls for query 0 on one thread
         with threadpool_limits(limits=1):
-            from tests._harness import u16
             oq = OracleQuery(w, lay, 0, keys_cache.get(0))
-            qs = {layer: oq.iq(layer) for layer in [0] + step.layers}
-            t1 = 0.0
-            t0 = time.perf_counter()
-            rpool, _, _ = oracle.index_full(qs[0][0], qs[0][1], oq.keys, oq.n, w.dims.swa, w.dims.pool_blocks)
-            t1 += time.perf_counter() - t0
-            for layer in step.layers:
-                t0 = time.perf_counter()
-                keep, _, _ = oracle.reindex(qs[layer][0], qs[layer][1], oq.keys, rpool, oq.c, w.dims.topk)
-                t1 += time.perf_counter() - t0
-                rows = oq.base + keep
-                lat = np.asarray(wl.latent_at(w, rows).view(torch.int16).numpy(), dtype=np.uint16)
-                rp = np.asarray(wl.rope_at(w, rows).view(torch.int16).numpy(), dtype=np.uint16)
-                codes, scales = oracle.encode_kv(lat)
-                win = oq.base + np.arange(oq.c, oq.n)
-                swa = np.concatenate([wl.latent_at(w, win).view(torch.int16).numpy(),
-                                      wl.rope_at(w, win).view(torch.int16).numpy()], axis=1).astype(np.uint16)
-                ql = u16(wl.q_latent(w, layer, 0, 1)[0])
-                qr = u16(wl.q_rope(w, layer, 0, 1)[0])
-                t0 = time.perf_counter()
-                oracle.attend(ql, qr, 1.0, oracle.gather_entries(codes, scales, rp, swa))
-                t1 += time.perf_counter() - t0
-            res["one_thread"] = {"value": 1.0 / t1, "unit": "queries/s",
-                                 "sample": "query 0, the same timed oracle calls, 1 BLAS thread"}
+            t1, _ = _oracle_query(w, oq, step.layers, oq.keys, 0)
+        res["one_thread"] = {"value": 1.0 / t1, "unit": unit,
+                             "sample": "query 0, the same timed oracle calls, 1 BLAS thread"}
     return res, parity
 
 
@@ -564,7 +581,79 @@ def _host_info(threads: int) -> dict:
             "affinity_cores": len(os.sched_getaffinity(0)), "blas_threads": int(threads)}
 
 
+# ---------------------------------------------------------------- read ceiling
+def read_ceiling(steps: int) -> dict:
+    """This GPU's plain streaming-read rate (csa2_stream_read: nontemporal
+    16-byte loads into registers, one contiguous chunk per workgroup), at the
+    1M-context scan's size over 8 rotating buffers (so the 256 MB Infinity
+    Cache cannot serve repeats) and over one 1 GiB buffer."""
+    import compressed_sparse_attention_decode_amd as csa2
+    rate = _spin_rate()
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    res = {"kernel": "k_stream_read (csa2_stream_read)"}
+    small = scan_bytes(wl.workload("decode_b1_ctx1m"))
+    for label, nbytes, nbuf in (("scan_size", small, 8), ("1GiB", 1 << 30, 1)):
+        bufs = [torch.ones(nbytes // 4, dtype=torch.int32, device="cuda") for _ in range(nbuf)]
+        calls = [csa2.stream_read(b, sink, prepare=True) for b in bufs]
+        for c in calls:
+            c()
+        n = max(steps, 16)
+        ms = _timed(lambda k: calls[k % nbuf](), n, rate, 1e-3) / n
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        res[label] = {"bytes": nbytes, "avg_us": round(ms * 1e3, 3), "achieved_gbs": round(gbs, 1),
+                      "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4)}
+        del bufs, calls
+    torch.cuda.empty_cache()
+    return res
+
+
+# ---------------------------------------------------------------- records
+def _is_mfma_bound(w: wl.Workload) -> bool:
+    """Tokens of one sequence share each key: the scan does g * 2 H_i d_i
+    flops per key of key_bytes bytes, bound by the f16 matrix cores once that
+    exceeds their ridge, 2.5 PFLOP/s / 8 TB/s = 312.5 flops per byte (one
+    token at d_i = 128: 128)."""
+    per_byte = w.tokens_per_seq * 2 * w.dims.idx_heads * w.dims.idx_dim / key_bytes(w)
+    return per_byte > F16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+
+
+def record(w: wl.Workload, res: dict) -> dict:
+    """One workload's figures: throughput, stage times, the step's roofline
+    (algorithmic bytes of the whole step over its time) and the scan's
+    (HBM-bound, or bound by the f16 matrix cores where tokens share keys)."""
+    unit = "query-tokens/s" if w.tokens_per_seq > 1 else "queries/s"
+    sc = res["scan"]
+    if _is_mfma_bound(w):
+        scan_rl = {"bound": "mfma", "achieved": sc["mfma_tflops"], "peak": F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                   "frac": sc["mfma_frac"], "dtype": "f16 (exact fp8 / FP4 conversions)",
+                   "flops_per_launch": scan_flops(w), "avg_us": sc["avg_us"],
+                   "hbm_gbs": sc["achieved_gbs"], "hbm_frac": sc["frac"]}
+    else:
+        scan_rl = {"bound": "hbm", "achieved": sc["achieved_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                   "frac": sc["frac"], "bytes_per_launch": sc["bytes_per_launch"], "avg_us": sc["avg_us"],
+                   "traffic": measured_traffic(w.name)}
+    step_gbs = res["step_bytes"] / (res["ms_per_step"] * 1e-3) / 1e9
+    ceiling = w.n_q / (res["step_bytes"] / (HBM_PEAK_GBS * 1e9))
+    return {"workload": w.name, "metric": "decode " + unit, "value": round(res["value"], 2), "unit": unit,
+            "ms_per_step": round(res["ms_per_step"], 5),
+            "indexer_rows": "fp4 (E2M1 + E4M3 per 16)" if w.idx_fp4 else "fp8 e4m3",
+            "kv_scale_group": w.dims.kv_group, "page_size": w.page_size or None,
+            "batch": w.n_seq, "tokens_per_seq": w.tokens_per_seq, "ctx": list(w.ctx_list or w.ctx),
+            "reindex_layers": w.reindex_layers, "fresh_encode": w.fresh_encode,
+            "stages_us": res["stages_us"], "step_us_spread": res["step_us_spread"],
+            "layer_step_us": res.get("layer_step_us"), "replicas": res["replicas"],
+            "step_roofline": {"bound": "hbm", "achieved": round(step_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                              "frac": round(step_gbs / HBM_PEAK_GBS, 4), "step_bytes": res["step_bytes"],
+                              "ceiling_value": round(ceiling, 1)},
+            "scan_roofline": scan_rl}
+
+
 # ---------------------------------------------------------------- main
+CONFIGS = "decode_b1_ctx4k_small,cluster_b32_ctx32k-256k_full1_reindex5,specverify_b64x4_ctx16k-512k_encode64k"
+VARIANTS = ("decode_b8_ctx128k_fp4idx,decode_b1_ctx1m_fp4idx,decode_b8_ctx128k_kvg32,chunk_b1x64_ctx128k,"
+            "decode_b8_ctx128k_paged64,decode_b1_ctx1m_paged64")
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -572,11 +661,15 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode_b8_ctx128k")
     ap.add_argument("--secondary", default="decode_b1_ctx1m", help="second workload ('' to skip)")
-    ap.add_argument("--variants", default="decode_b8_ctx128k_fp4idx,decode_b1_ctx1m_fp4idx,decode_b8_ctx128k_kvg32,"
-                                          "chunk_b1x64_ctx128k,decode_b8_ctx128k_paged64,decode_b1_ctx1m_paged64",
+    ap.add_argument("--configs", default=CONFIGS, help="the other configurations, each with its oracle figure and "
+                                                       "parity ('' to skip)")
+    ap.add_argument("--variants", default=VARIANTS,
                     help="comma-separated further workloads reported under 'variants' ('' to skip)")
     ap.add_argument("--replicas", type=int, default=0, help="cache replicas (0: enough for >= 1 GB)")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle sample budget (0 to skip)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle sample budget of the headline "
+                                                                    "workload (0 skips every oracle leg)")
+    ap.add_argument("--config-cpu-seconds", type=float, default=4.0,
+                    help="oracle sample budget of the secondary workload and of each configuration")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain fp32 copy of MIB MiB four times (calibrates the HBM byte counters)")
     args = ap.parse_args()
@@ -602,58 +695,33 @@ def main():
         print(json.dumps({"copy_calibration": {"read_bytes": 4 * n, "write_bytes": 4 * n, "launches": 4}}))
         return
 
-    w = wl.workload(args.workload)
-    st, step, res = measure(w, args.steps, args.warmup, args.replicas)
-    print(f"[bench] {w.name}: {res['value']:.1f} queries/s, {res['ms_per_step'] * 1e3:.1f} us/step, "
-          f"scan {res['scan']['avg_us']} us = {res['scan']['achieved_gbs']} GB/s", file=sys.stderr, flush=True)
-    cpu, parity = None, None
-    if args.cpu_seconds > 0:
-        cpu, parity = cpu_baseline(w, st, step, args.cpu_seconds)
-        print(f"[bench] oracle: {cpu['value']:.3f} queries/s on {cpu['cores']} threads; parity {parity}",
-              file=sys.stderr, flush=True)
-    del st, step
-    torch.cuda.empty_cache()
-    def other(name):
+    ceiling = read_ceiling(args.steps)
+    print(f"[bench] streaming read: {ceiling['scan_size']['avg_us']} us per {ceiling['scan_size']['bytes']} B "
+          f"({ceiling['scan_size']['frac_of_peak']} of 8 TB/s), 1 GiB at {ceiling['1GiB']['frac_of_peak']}",
+          file=sys.stderr, flush=True)
+
+    def run(name, cpu_s, one_thread=False, parity_only=False):
         w2 = wl.workload(name)
         st2, step2, res2 = measure(w2, args.steps, args.warmup, args.replicas)
-        rec = {"workload": w2.name, "metric": "decode queries/s", "value": round(res2["value"], 2),
-               "unit": "queries/s", "ms_per_step": round(res2["ms_per_step"], 5),
-               "indexer_rows": "fp4 (E2M1 + E4M3 per 16)" if w2.idx_fp4 else "fp8 e4m3",
-               "kv_scale_group": w2.dims.kv_group,
-               "page_size": w2.page_size or None,
-               "stages_us": res2["stages_us"], "step_us_spread": res2["step_us_spread"],
-               "layer_step_us": res2.get("layer_step_us"),
-               "replicas": res2["replicas"],
-               "scan_roofline": {"bound": "hbm", "achieved": res2["scan"]["achieved_gbs"],
-                                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": res2["scan"]["frac"],
-                                 "bytes_per_launch": res2["scan"]["bytes_per_launch"],
-                                 "avg_us": res2["scan"]["avg_us"],
-                                 "traffic": measured_traffic(w2.name)},
-               "scan_mfma": {"achieved_tflops": res2["scan"]["mfma_tflops"], "peak_tflops": F16_PEAK_TFLOPS,
-                             "frac": res2["scan"]["mfma_frac"], "dtype": "f16 (exact fp8 / FP4 conversions)"}}
-        print(f"[bench] {w2.name}: {res2['value']:.1f} queries/s, scan {res2['scan']['avg_us']} us = "
-              f"{res2['scan']['achieved_gbs']} GB/s", file=sys.stderr, flush=True)
-        if w2.page_size and args.cpu_seconds > 0 and name != args.secondary:
-            # the paged step's sampled query against the oracle
-            _, rec["parity"] = cpu_baseline(w2, st2, step2, 0.0)
-            print(f"[bench] {w2.name} parity {rec['parity']}", file=sys.stderr, flush=True)
-        return w2, st2, step2, rec
-
-    secondary = None
-    if args.secondary:
-        w2, st2, step2, secondary = other(args.secondary)
+        rec = record(w2, res2)
+        print(f"[bench] {w2.name}: {res2['value']:.1f} {rec['unit']}, {res2['ms_per_step'] * 1e3:.1f} us/step, "
+              f"scan {res2['scan']['avg_us']} us = {res2['scan']['achieved_gbs']} GB/s", file=sys.stderr, flush=True)
         if args.cpu_seconds > 0:
-            # parity of the timed step's query against the oracle (one query)
-            _, secondary["parity"] = cpu_baseline(w2, st2, step2, 0.0)
-            print(f"[bench] {w2.name} parity {secondary['parity']}", file=sys.stderr, flush=True)
+            cpu, rec["parity"] = cpu_baseline(w2, st2, step2, 0.0 if parity_only else cpu_s, one_thread)
+            if not parity_only:
+                rec["cpu_baseline"] = cpu
+                print(f"[bench] {w2.name} oracle: {cpu['value']:.3f} {cpu['unit']} on {cpu['cores']} threads",
+                      file=sys.stderr, flush=True)
+            print(f"[bench] {w2.name} parity {rec['parity']}", file=sys.stderr, flush=True)
         del st2, step2
         torch.cuda.empty_cache()
-    variants = []
-    for name in [v for v in args.variants.split(",") if v]:
-        _, st3, step3, rec = other(name)
-        variants.append(rec)
-        del st3, step3
-        torch.cuda.empty_cache()
+        return w2, res2, rec
+
+    w, res, prim = run(args.workload, args.cpu_seconds, one_thread=True)
+    secondary = run(args.secondary, args.config_cpu_seconds)[2] if args.secondary else None
+    configs = [run(n, args.config_cpu_seconds, one_thread=(n == "decode_b1_ctx4k_small"))[2]
+               for n in args.configs.split(",") if n]
+    variants = [run(n, 0.0, parity_only=True)[2] for n in args.variants.split(",") if n]
 
     d = w.dims
     line = {
@@ -677,17 +745,25 @@ def main():
         "roofline": {"bound": "hbm", "achieved": res["scan"]["achieved_gbs"], "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": res["scan"]["frac"], "traffic": measured_traffic(w.name),
                      "kernel": "k_scan (Full-mode indexer scan)",
-                     "bytes_per_launch": res["scan"]["bytes_per_launch"], "avg_us": res["scan"]["avg_us"]},
+                     "bytes_per_launch": res["scan"]["bytes_per_launch"], "avg_us": res["scan"]["avg_us"],
+                     "frac_of_read_ceiling": round(res["scan"]["achieved_gbs"] /
+                                                   ceiling["scan_size"]["achieved_gbs"], 4)},
+        "read_ceiling": ceiling,
         "stages_us": res["stages_us"],
         "step_us_spread": res["step_us_spread"],
         "layer_step_us": res.get("layer_step_us"),
         "step_bytes": res["step_bytes"],
         "step_gbs": res["step_gbs"],
-        "cpu_baseline": cpu,
-        "parity": parity,
+        "step_roofline": prim["step_roofline"],
+        "cpu_baseline": prim.get("cpu_baseline"),
+        "parity": prim.get("parity"),
         "secondary": secondary,
+        "configs": configs,
         "variants": variants,
     }
+    if secondary is not None:
+        secondary["scan_roofline"]["frac_of_read_ceiling"] = round(
+            secondary["scan_roofline"]["achieved"] / ceiling["scan_size"]["achieved_gbs"], 4)
     print(json.dumps(line), flush=True)
 
 

@@ -28,7 +28,7 @@ __all__ = ["Dims", "Batch", "Csa2Error", "lib", "lib_path", "encode_kv", "encode
            "index_scan", "index_pool", "n_blocks", "block_scores_ld", "workspace_pool",
            "index_reindex", "attend", "workspace_full", "workspace_reindex",
            "workspace_attend", "abi_version", "Call", "decode_step", "workspace_step", "Pages", "page_rows",
-           "LAYER_FULL", "LAYER_REINDEX", "LAYER_REUSE"]
+           "LAYER_FULL", "LAYER_REINDEX", "LAYER_REUSE", "stream_read"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 lib_path = os.path.join(_PKG, "libcsa2.so")
@@ -97,6 +97,7 @@ def lib() -> ctypes.CDLL:
             "csa2_decode_step_workspace_size": (I32, [PD, PQ, ctypes.POINTER(SZ)]),
             "csa2_decode_step": (I32, [PD, PQ, I32, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_float,
                                        P, P, P, P, P, P, P, P, SZ, P]),
+            "csa2_stream_read": (I32, [P, I64, P, P]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -599,3 +600,13 @@ def decode_step(dims: Dims, b: Batch, mode: int, idx_q, idx_w, idx_k,
         return _issue(lib().csa2_decode_step_paged, args[:2] + (ctypes.byref(pg),) + args[2:],
                       (d, q, pg, ws, pages.table), prepare)
     return _issue(lib().csa2_decode_step, args, (d, q, ws), prepare)
+
+
+def stream_read(buf: torch.Tensor, sink: torch.Tensor, prepare: bool = False):
+    """One nontemporal read of every byte of `buf` (csa2_stream_read): the
+    streaming-read reference the Full scan's bandwidth is compared with.
+    `sink` is an int32 device tensor of at least one element."""
+    _dev(buf, sink)
+    nbytes = buf.numel() * buf.element_size()
+    args = (buf.data_ptr(), nbytes - nbytes % 16, sink.data_ptr(), _stream(buf.device))
+    return _issue(lib().csa2_stream_read, args, (), prepare)

@@ -10,7 +10,7 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libcsa2.so")
-SOURCES = ["api.hip", "encode.hip", "scan.hip", "select.hip", "reindex.hip", "attend.hip"]
+SOURCES = ["api.hip", "encode.hip", "scan.hip", "select.hip", "reindex.hip", "attend.hip", "calib.hip"]
 # The indexer contractions keep their MFMA accumulators in VGPRs (the epilogue
 # reads every result with VALU ops; AGPR results would each need a
 # v_accvgpr_read first) and assume finite scores (non-finite inputs are

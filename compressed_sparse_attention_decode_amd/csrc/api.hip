@@ -27,6 +27,8 @@ csa2_status hip_fail(hipError_t e, const char* what) {
   return fail(CSA2_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+// Per-device properties, filled once under check_device's lock (before the
+// device is marked known) and read only after a successful check_device.
 int g_cus[64] = {0};                 // compute units per checked device
 
 // gfx950 check, once per device.
@@ -54,8 +56,8 @@ csa2_status check_dims(const csa2_dims* d) {
   if (d->d_latent != 512) return fail(CSA2_ERR_INVALID_ARG, "d_latent must be 512 (got %d)", d->d_latent);
   if (d->d_rope != 64) return fail(CSA2_ERR_INVALID_ARG, "d_rope must be 64 (got %d)", d->d_rope);
   if (d->block != 8) return fail(CSA2_ERR_INVALID_ARG, "block must be 8 (got %d)", d->block);
-  if (d->n_heads < 16 || d->n_heads > 128 || d->n_heads % 16)
-    return fail(CSA2_ERR_INVALID_ARG, "n_heads must be a multiple of 16 in [16, 128] (got %d)", d->n_heads);
+  if (d->n_heads < 8 || d->n_heads > 128 || d->n_heads % 8)
+    return fail(CSA2_ERR_INVALID_ARG, "n_heads must be a multiple of 8 in [8, 128] (got %d)", d->n_heads);
   if (d->idx_heads < 1 || d->idx_heads > 64)
     return fail(CSA2_ERR_INVALID_ARG, "idx_heads must be in [1, 64] (got %d)", d->idx_heads);
   if (d->idx_dim != 64 && d->idx_dim != 128)
@@ -244,7 +246,7 @@ AttendPlan attend_plan(const csa2_dims* d, const csa2_queries* q) {
 size_t attend_ws(const csa2_dims* d, const csa2_queries* q) {
   const AttendPlan p = attend_plan(d, q);
   if (p.splits == 1) return 0;
-  const size_t rows = (size_t)q->n_q * p.splits * d->n_heads;
+  const size_t rows = (size_t)q->n_q * p.splits * ((d->n_heads + 15) / 16 * 16);   // heads padded to 16
   return align256(rows * 512 * 4) + align256(rows * 2 * 4);
 }
 
@@ -326,9 +328,12 @@ csa2_status csa2_index_full_workspace_size(const csa2_dims* d, const csa2_querie
 
 static csa2_status check_block_scores(const csa2_dims* d, const csa2_queries* q, const float* block_scores,
                                       int64_t ld_block_scores) {
+  // at least 4 even with no blocks: the pool select's clamped 16-byte loads
+  // read inside [0, ld) of every row
   const int64_t nb = max_blocks(d, q);
-  if (ld_block_scores < nb)
-    return fail(CSA2_ERR_INVALID_ARG, "ld_block_scores %lld < %lld blocks", (long long)ld_block_scores, (long long)nb);
+  if (ld_block_scores < nb || ld_block_scores < 4)
+    return fail(CSA2_ERR_INVALID_ARG, "ld_block_scores %lld < max(4, %lld blocks)", (long long)ld_block_scores,
+                (long long)nb);
   if ((ld_block_scores & 3) || ((uintptr_t)block_scores & 15))
     return fail(CSA2_ERR_INVALID_ARG, "block_scores must be 16-byte aligned with ld_block_scores a multiple of 4");
   return CSA2_OK;
@@ -653,7 +658,7 @@ static csa2_status attend(const csa2_dims* d, const csa2_queries* q, const uint1
   aa.page_shift = pages ? page_shift(pages) : 0;
   aa.rows = pages ? pages->rows : 0;
   if (p.splits > 1) {
-    const size_t rows = (size_t)q->n_q * p.splits * d->n_heads;
+    const size_t rows = (size_t)q->n_q * p.splits * ((d->n_heads + 15) / 16 * 16);
     aa.part_o = (float*)ws;
     aa.part_ml = (float*)((char*)ws + align256(rows * 512 * 4));
   } else {
@@ -773,6 +778,19 @@ csa2_status csa2_decode_step_paged(const csa2_dims* d, const csa2_queries* q, co
   return decode_step(d, q, mode, idx_q, idx_q_scales, idx_w, idx_k, idx_k_scales, pool_blocks, pool_count, topk_pos,
                      topk_count, q_lat, q_rope, softmax_scale, kv_codes, kv_scales, kv_rope, swa_kv, swa_base, out,
                      lse, ws, ws_bytes, stream, pages);
+}
+
+csa2_status csa2_stream_read(const void* buf, int64_t bytes, uint32_t* sink, void* stream) {
+  if (bytes < 0 || (bytes & 15)) return fail(CSA2_ERR_INVALID_ARG, "bytes must be a non-negative multiple of 16");
+  if (bytes > 0 && (!buf || !sink)) return fail(CSA2_ERR_INVALID_ARG, "required pointer is NULL");
+  if (((uintptr_t)buf & 15) || ((uintptr_t)sink & 3)) return fail(CSA2_ERR_INVALID_ARG, "misaligned buffer");
+  csa2_status st = check_device();
+  if (st) return st;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  e = launch_stream_read(buf, bytes, sink, g_cus[dev], (hipStream_t)stream);
+  return e == hipSuccess ? CSA2_OK : hip_fail(e, "stream read launch");
 }
 
 }  // extern "C"

@@ -235,9 +235,11 @@ __global__ __launch_bounds__(kNT) void k_attend(AttendArgs a) {
 #pragma unroll
     for (int j = 0; j < kQv; ++j) {
       const int i = lane + 64 * j, hh = i / (kKeyDim / 8), d = (i % (kKeyDim / 8)) * 8;
-      const int64_t qh = (int64_t)q * H + head0 + hh;
+      // heads past H (H a multiple of 8, not 16) read as zero rows
+      const int64_t qh = (int64_t)q * H + min(head0 + hh, H - 1);
       const uint16_t* src = d < kLatent ? a.q_lat + qh * kLatent + d : a.q_rope + qh * kRope + (d - kLatent);
       rq[j] = *reinterpret_cast<const v4u*>(src);
+      if (head0 + hh >= H) rq[j] = v4u{0u, 0u, 0u, 0u};
     }
   }
   const int n = load_uniform(a.n_visible + q);
@@ -380,20 +382,23 @@ __global__ __launch_bounds__(kNT) void k_attend(AttendArgs a) {
     for (int nt = 0; nt < kLatent / 16; ++nt) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        a.out[((int64_t)q * H + head0 + 4 * gq + i) * kLatent + nt * 16 + col] = o[nt][i] * inv[i];
+        if (head0 + 4 * gq + i < H)
+          a.out[((int64_t)q * H + head0 + 4 * gq + i) * kLatent + nt * 16 + col] = o[nt][i] * inv[i];
     }
-    if (a.lse && gq == 0)
+    if (a.lse && gq == 0 && head0 + col < H)
       a.lse[(int64_t)q * H + head0 + col] = l > 0.0f ? (m + log2f(l)) * 0.69314718055994531f : -__builtin_inff();
   } else {
     // partial o of the wave's 16 heads in the accumulators' own layout
     // [nt][lane][4] (one 1 KiB coalesced store per nt); k_attend_combine
     // reads it back in the same layout
-    float* po = a.part_o + (((int64_t)q * S + sp) * (H / 16) + head0 / 16) * (kLatent * 16);
+    // (partials cover the heads padded to a multiple of 16)
+    const int HB = (H + 15) / 16;
+    float* po = a.part_o + (((int64_t)q * S + sp) * HB + head0 / 16) * (kLatent * 16);
 #pragma unroll
     for (int nt = 0; nt < kLatent / 16; ++nt)
       *reinterpret_cast<v4f*>(po + (nt * 64 + lane) * 4) = o[nt];
     if (gq == 0) {
-      float* pm = a.part_ml + (((int64_t)q * S + sp) * H + head0 + col) * 2;
+      float* pm = a.part_ml + (((int64_t)q * S + sp) * (HB * 16) + head0 + col) * 2;
       pm[0] = m;
       pm[1] = l;
     }
@@ -405,7 +410,7 @@ __global__ __launch_bounds__(kNT) void k_attend(AttendArgs a) {
 // tiles; a thread owns one accumulator slot (4 heads x 1 dim) and issues all
 // of its partial loads (every split) before the first use.
 __global__ __launch_bounds__(256) void k_attend_combine(AttendArgs a) {
-  const int S = a.splits, H = a.heads, HB = H / 16;
+  const int S = a.splits, H = a.heads, HB = (H + 15) / 16;
   const int q = blockIdx.x / (HB * 8), hb = (blockIdx.x / 8) % HB, ntg = blockIdx.x % 8;
   const int lane = threadIdx.x & 63, nt = ntg * 4 + (threadIdx.x >> 6);
   const int gq = lane >> 4, col = lane & 15;
@@ -422,7 +427,7 @@ __global__ __launch_bounds__(256) void k_attend_combine(AttendArgs a) {
                                             (nt * 64 + lane) * 4);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const v2f ml = *reinterpret_cast<const v2f*>(a.part_ml + (((int64_t)q * S + s) * H + h0 + i) * 2);
+        const v2f ml = *reinterpret_cast<const v2f*>(a.part_ml + (((int64_t)q * S + s) * (HB * 16) + h0 + i) * 2);
         ms[s][i] = ml[0];
         ls[s][i] = ml[1];
       }
@@ -442,6 +447,7 @@ __global__ __launch_bounds__(256) void k_attend_combine(AttendArgs a) {
         acc += wgt * os[s][i];
       }
     }
+    if (h0 + i >= H) continue;               // padding heads (H a multiple of 8)
     a.out[((int64_t)q * H + h0 + i) * kLatent + nt * 16 + col] = den > 0.0f ? acc / den : 0.0f;
     if (a.lse && nt == 0 && col == 0)
       a.lse[(int64_t)q * H + h0 + i] = den > 0.0f ? (M + log2f(den)) * 0.69314718055994531f : -__builtin_inff();
@@ -454,7 +460,7 @@ hipError_t launch_attend(const AttendArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(k_attend, dim3((unsigned)(a.n_q * a.head_groups * a.splits)), dim3(kNT), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.splits == 1) return e;
-  hipLaunchKernelGGL(k_attend_combine, dim3((unsigned)(a.n_q * (a.heads / 16) * 8)), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(k_attend_combine, dim3((unsigned)(a.n_q * ((a.heads + 15) / 16) * 8)), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

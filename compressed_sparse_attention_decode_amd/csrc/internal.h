@@ -93,6 +93,7 @@ hipError_t launch_pool_select(const PoolArgs& a, hipStream_t s);
 int64_t pool_ws_words(int chunks, int mm_cap);   // workspace words per query
 hipError_t launch_reindex(const ReindexArgs& a, hipStream_t s);
 hipError_t launch_attend(const AttendArgs& a, hipStream_t s);
+hipError_t launch_stream_read(const void* buf, int64_t bytes, uint32_t* sink, int cus, hipStream_t s);
 
 // Tiling constants the host needs for grids and workspace sizes.
 constexpr int kPoolChunk = 4096;       // blocks per pool-select chunk workgroup

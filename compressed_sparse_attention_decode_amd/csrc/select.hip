@@ -31,6 +31,8 @@
 //     histogram is cleared again.  If a chunk listed more candidates than
 //     its slots, this step re-reads the block scores instead (correct for
 //     any input, slow only for near-constant scores).
+#include <mutex>
+
 #include "common.h"
 #include "internal.h"
 #include "radix_topk.h"
@@ -664,13 +666,23 @@ hipError_t launch_pool_select(const PoolArgs& a, hipStream_t s) {
   const dim3 grid((unsigned)(a.n_q * a.chunks));
   const dim3 mgrid((unsigned)(a.n_q * a.mark_wgs));
   const size_t lds = pool_final_lds(a.nw_cap);
-  // dynamic LDS above the default limit must be allowed once per size
-  static size_t lds_allowed = 0;
-  if (lds > 48 * 1024 && lds > lds_allowed) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_pool_mark),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  // dynamic LDS above the default limit must be allowed, once per device for
+  // the largest size asked so far (the record is per device and locked, so
+  // calls on several threads and devices agree)
+  if (lds > 48 * 1024) {
+    static std::mutex mu;
+    static size_t lds_allowed[64] = {0};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
-    lds_allowed = lds;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lk(mu);
+    if (lds > lds_allowed[dev]) {
+      e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_pool_mark),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      if (e != hipSuccess) return e;
+      lds_allowed[dev] = lds;
+    }
   }
   if (!a.have_minmax) hipLaunchKernelGGL(k_pool_minmax, grid, dim3(kCT), 0, s, a);
   hipLaunchKernelGGL(k_pool_hist, mgrid, dim3(kCT), 0, s, a);

@@ -34,8 +34,10 @@
  *     16 channels; value = E2M1 level x scale.
  *   - Non-finite inputs give undefined (but memory-safe) results.
  *   - Calls on different streams may run concurrently if their workspaces
- *     and outputs do not overlap.  The library keeps no mutable state except
- *     a per-device architecture check done once.
+ *     and outputs do not overlap.  The library's only mutable host state is
+ *     per device and set once under a lock: the architecture check with the
+ *     CU count it reads, and the largest dynamic-LDS size allowed for the
+ *     pool kernel.
  *   - On error the call enqueues nothing and returns a status;
  *     csa2_last_error() gives a message for the calling thread.
  */
@@ -60,10 +62,12 @@ typedef enum csa2_status {
 } csa2_status;
 
 /* Problem dimensions.  Supported values:
- *   n_heads      H    main attention heads, a multiple of 16, 16..128
+ *   n_heads      H    main attention heads, a multiple of 8, 8..128
  *   d_latent          512 (the latent shared across heads; [stamatios])
  *   d_rope            64  (the bf16 RoPE key part)
- *   idx_heads    H_i  indexer heads, 1..64
+ *   idx_heads    H_i  indexer heads, 1..64 (the scan keeps the query of all
+ *                     heads resident in registers as f16 MFMA operands: 64
+ *                     VGPRs per lane at 64 heads x 128 dims)
  *   idx_dim      d_i  indexer key / query width, 64 or 128
  *   block             8   (indexer block size; [atlas] §3.2)
  *   pool_blocks  P    blocks kept by the Full indexer, 1..2048
@@ -195,15 +199,15 @@ csa2_status csa2_encode_fp4(int64_t n, int32_t width, const uint16_t* src, const
 /* Full-mode indexer, stage 1 of 2: the scan ([atlas] §3.2 hierarchical
  * sparse indexer and mode table; [newsaint] §3: the Full layer scores every
  * causally visible position).  For every query:
- *   s_p = sum_h w_h * max(0, q_h . k_p)  for p in [0, c)   (fp8 inputs, the
- *         dot products exact, the weighted sum in fp32)
+ *   s_p = sum_h w_h * max(0, q_h . k_p)  for p in [0, c)   (fp8 inputs: the
+ *         products exact, the dot products and the weighted sum in fp32)
  *   b_j = max of s_p over p in [8j, min(8j+8, c)),  j < nb = ceil(c / 8)
  *   idx_q        fp8 [n_q, H_i, d_i]      idx_w  float [n_q, H_i]
  *   idx_k        fp8 [rows, d_i]  (one key per position, shared by heads)
  *   block_scores float [n_q, ld_block_scores], 16-byte aligned: b_j
  *                written for j < nb; entries at j >= nb are left untouched;
- *                ld_block_scores >= ceil((max_visible - W) / 8) and a
- *                multiple of 4.
+ *                ld_block_scores >= max(4, ceil((max_visible - W) / 8)) and
+ *                a multiple of 4.
  *   pool_ws      optional (NULL, 0): a workspace of
  *                csa2_index_pool_workspace_size bytes.  When given, the scan
  *                also leaves in it what the first pass of csa2_index_pool
@@ -252,8 +256,10 @@ csa2_status csa2_index_pool_workspace_size(const csa2_dims* dims, const csa2_que
  *                contents need no initialisation unless flags holds
  *                CSA2_POOL_WS_FROM_SCAN (see csa2_index_scan).
  *   flags        0 or CSA2_POOL_WS_FROM_SCAN.
- * Four kernels (per-chunk key range, histogram, marking; one exact final
- * step per query), three with CSA2_POOL_WS_FROM_SCAN. */
+ * When no query has more than 16,384 blocks: one kernel (one workgroup per
+ * query selects from all of its block scores).  Otherwise: a per-chunk key
+ * range (skipped with CSA2_POOL_WS_FROM_SCAN), a histogram, and a marking
+ * kernel whose last workgroup per query runs the exact final step. */
 csa2_status csa2_index_pool(const csa2_dims* dims, const csa2_queries* q,
                             const float* block_scores, int64_t ld_block_scores,
                             int32_t* pool_blocks, int32_t* pool_count,
@@ -457,6 +463,17 @@ csa2_status csa2_decode_step(const csa2_dims* dims, const csa2_queries* q, int32
                              const uint8_t* kv_codes, const uint8_t* kv_scales, const uint16_t* kv_rope,
                              const uint16_t* swa_kv, const int64_t* swa_base, float* out, float* lse,
                              void* ws, size_t ws_bytes, void* stream);
+
+/* Measurement helper, not a step of the method: reads `bytes` bytes of
+ * device memory at `buf` once (16-byte nontemporal loads into registers, two
+ * workgroups per CU, each over one contiguous chunk) and writes nothing,
+ * except that `sink` (a device word) may receive a value in a case that
+ * does not arise for any data.  Timing it gives the streaming-read rate of
+ * this GPU's HBM that the Full scan's bandwidth is compared with.
+ *   buf    16-byte aligned; bytes a multiple of 16 (0 is a no-op)
+ *   sink   4-byte aligned device word
+ * Errors: CSA2_ERR_INVALID_ARG for a bad size, NULL or misaligned pointer. */
+csa2_status csa2_stream_read(const void* buf, int64_t bytes, uint32_t* sink, void* stream);
 
 #ifdef __cplusplus
 }

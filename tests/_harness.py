@@ -146,3 +146,18 @@ def check_attention(out, lse, ref_out, ref_lse, label=""):
         assert np.array_equal(np.isfinite(lse), fin), f"{label}: lse finiteness differs"
         assert np.allclose(lse[fin], ref_lse[fin], rtol=1e-4, atol=1e-4), f"{label}: lse mismatch"
     return float(rel.max()) if rel.size else 0.0
+
+
+def with_oracle_rows(tk: torch.Tensor, tc: torch.Tensor, rows: dict):
+    """Copies of the library's topk_pos / topk_count inputs in which the
+    queries in `rows` (query -> oracle Top-K, ascending) carry the oracle's
+    own kept positions, so that the library's attention can be compared with
+    the oracle's on the same set (oracle outputs feed the library, never the
+    other way round)."""
+    tk2, tc2 = tk.clone(), tc.clone()
+    for qi, keep in rows.items():
+        tk2[qi].fill_(-1)
+        if len(keep):
+            tk2[qi, :len(keep)] = torch.as_tensor(np.asarray(keep, dtype=np.int32), device=tk.device)
+        tc2[qi] = len(keep)
+    return tk2, tc2

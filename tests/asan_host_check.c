@@ -68,7 +68,7 @@ int main(void) {
 
   /* bad dimensions */
   q.n_q = 8; q.tokens_per_seq = 1; q.max_visible = 131072;
-  const csa2_dims bad[] = {dims(24, 64, 128, 2048, 512, 128, 16), dims(16, 0, 128, 2048, 512, 128, 16),
+  const csa2_dims bad[] = {dims(20, 64, 128, 2048, 512, 128, 16), dims(16, 0, 128, 2048, 512, 128, 16),
                            dims(16, 65, 128, 2048, 512, 128, 16), dims(16, 64, 96, 2048, 512, 128, 16),
                            dims(16, 64, 128, 0, 512, 128, 16), dims(16, 64, 128, 4096, 512, 128, 16),
                            dims(16, 64, 128, 8, 65, 128, 16), dims(16, 64, 128, 2048, 512, 2048, 16),

@@ -81,7 +81,8 @@ def _call_ws(fn, dims, batch):
 
 
 @pytest.mark.parametrize("bad", [
-    dict(idx_dim=96), dict(n_heads=24), dict(n_heads=0), dict(idx_heads=0), dict(idx_heads=65),
+    dict(idx_dim=96), dict(n_heads=20), dict(n_heads=0), dict(n_heads=136), dict(n_heads=4),
+    dict(idx_heads=0), dict(idx_heads=65),
     dict(pool_blocks=0), dict(pool_blocks=4096), dict(topk=0), dict(topk=8 * 16 + 1, pool_blocks=16),
     dict(swa=-1), dict(swa=2048), dict(kv_group=8), dict(kv_group=64),
 ])
@@ -90,6 +91,42 @@ def test_bad_dims_rejected(bad):
     st, _ = _call_ws(L.csa2_attend_workspace_size, _dims(**bad), _batch())
     assert st == INVALID
     assert L.csa2_last_error()
+
+
+@pytest.mark.parametrize("good", [dict(n_heads=8), dict(n_heads=24), dict(n_heads=120), dict(n_heads=128),
+                                  dict(idx_heads=1), dict(idx_heads=40), dict(idx_heads=64), dict(idx_dim=64),
+                                  dict(pool_blocks=1, topk=8), dict(topk=2048), dict(swa=0), dict(swa=1024),
+                                  dict(kv_group=32)])
+def test_documented_dims_accepted(good):
+    """The ranges include/csa2.h documents: H a multiple of 8 up to 128,
+    H_i 1..64, d_i 64 or 128, P 1..2048, K 1..min(8P, 2048), W 0..1024."""
+    L = csa2.lib()
+    for fn in (L.csa2_attend_workspace_size, L.csa2_index_full_workspace_size,
+               L.csa2_index_reindex_workspace_size, L.csa2_decode_step_workspace_size):
+        st, n = _call_ws(fn, _dims(**good), _batch())
+        assert st == OK, L.csa2_last_error()
+
+
+def test_attention_workspace_pads_heads_to_16():
+    """Attention partials are laid out in 16-head blocks: 24 heads take as
+    much workspace as 32."""
+    L = csa2.lib()
+    st, w24 = _call_ws(L.csa2_attend_workspace_size, _dims(n_heads=24), _batch(n_q=1))
+    assert st == OK
+    st, w32 = _call_ws(L.csa2_attend_workspace_size, _dims(n_heads=32), _batch(n_q=1))
+    assert st == OK and w24 == w32 > 0
+
+
+def test_block_score_stride_at_least_four():
+    """ld_block_scores must be >= 4 even when no query has candidates (the
+    pool select reads 16-byte groups inside each row)."""
+    L = csa2.lib()
+    d = _dims().c()
+    q = _batch(n_q=1, max_visible=100).c()          # n <= W: no blocks
+    st = L.csa2_index_pool(ctypes.byref(d), ctypes.byref(q), 0x1000, 0, 0x2000, 0x3000, 0x4000, 1 << 30, 0, None)
+    assert st == INVALID and b"ld_block_scores" in L.csa2_last_error()
+    st = L.csa2_index_scan(ctypes.byref(d), ctypes.byref(q), 0x1000, 0x2000, 0x3000, 0x4000, 0, None, 0, None)
+    assert st == INVALID and b"ld_block_scores" in L.csa2_last_error()
 
 
 @pytest.mark.parametrize("kw", [dict(n_q=0), dict(max_visible=(1 << 21) + 1), dict(g=3), dict(n_q=130, g=65),

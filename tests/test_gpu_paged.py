@@ -10,7 +10,7 @@ import pytest
 import torch
 
 import workloads as wl
-from tests._harness import GpuCase, OracleQuery, check_attention, check_set
+from tests._harness import GpuCase, OracleQuery, check_attention, check_set, with_oracle_rows
 from tests.test_gpu_parity import BIG, small
 
 pytestmark = pytest.mark.gpu
@@ -106,12 +106,18 @@ def test_paged_reindex_and_attention_match_contiguous(case):
     qi = int(np.argmax(g.lay.q_visible))
     oq = OracleQuery(w, g.lay, qi)
     rpool, rb, _ = oq.full(0)
-    if np.array_equal(pool.cpu().numpy()[qi, :int(cnt[qi])], rpool):
-        keep, _, _ = oq.reindex(0, rpool)
-        got = tk2.cpu().numpy()[qi, :int(tc2[qi])]
-        check_set(got, keep, lambda x: oq.scores_at(0, x), f"{name} paged topk")
-        ref_o, ref_l = oq.attention(0, got)
-        check_attention(out2.cpu().numpy()[qi], lse2.cpu().numpy()[qi], ref_o, ref_l, f"{name} paged attention")
+    check_set(pool.cpu().numpy()[qi, :int(cnt[qi])], rpool, lambda j: rb[j], f"{name} pool")
+    keep, _, _ = oq.reindex(0, rpool)
+    got = tk2.cpu().numpy()[qi, :int(tc2[qi])]
+    check_set(got, keep, lambda x: oq.scores_at(0, x), f"{name} paged topk")
+    ref_o, ref_l = oq.attention(0, keep)
+    if not np.array_equal(got, keep):
+        # the paged attention on the oracle's own Top-K
+        tk3, tc3 = with_oracle_rows(tk2, tc2, {qi: keep})
+        out2, lse2 = csa2.attend(g.dims, pg.batch, ql, qr, 1.0, pg.codes, pg.scales, pg.kv_rope, tk3, tc3, swa_kv,
+                                 g.swa_base, pages=pg.pages)
+        torch.cuda.synchronize()
+    check_attention(out2.cpu().numpy()[qi], lse2.cpu().numpy()[qi], ref_o, ref_l, f"{name} paged attention")
 
 
 def test_page_rows_append_into_pages(case):

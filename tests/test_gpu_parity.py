@@ -14,7 +14,7 @@ import torch
 import oracle
 import workloads as wl
 from tests._harness import (GpuCase, OracleQuery, check_attention, check_set, lib, u8, u16,
-                            SCORE_TOL)
+                            SCORE_TOL, with_oracle_rows)
 
 pytestmark = pytest.mark.gpu
 
@@ -37,6 +37,10 @@ CASES = {
     "edge_short": small(105, wl.Dims(n_heads=16, idx_heads=16, idx_dim=128, pool_blocks=4, topk=16),
                         [0, 1, 100, 128, 129, 136, 137, 160]),
     "w0_h128": small(106, wl.Dims(n_heads=128, idx_heads=1, idx_dim=128, pool_blocks=32, topk=64, swa=0), [3000]),
+    # head counts that are multiples of 8 but not of 16 (padded head blocks)
+    "h24_ragged": small(108, wl.Dims(n_heads=24, idx_heads=64, idx_dim=128, pool_blocks=200, topk=400),
+                        [12000, 5003]),
+    "h8_d64": small(109, wl.Dims(n_heads=8, idx_heads=8, idx_dim=64, pool_blocks=16, topk=64), [700, 129, 2050]),
     "max_pk": small(107, wl.Dims(n_heads=64, idx_heads=64, idx_dim=128, pool_blocks=2048, topk=2048, swa=1024),
                     [40000, 17000]),
     # FP4 indexer rows (codes + one E4M3 scale per 16 channels, d_i = 128)
@@ -267,19 +271,28 @@ def test_pipeline_end_to_end_and_deterministic(case):
     for a, b in zip(*runs):
         assert torch.equal(a.view(torch.uint8) if a.dtype == torch.float32 else a,
                            b.view(torch.uint8) if b.dtype == torch.float32 else b), f"{name}: run-to-run difference"
+    tk_t, tc_t = runs[0][2].cuda(), runs[0][3].cuda()
     pool, cnt, tk, tc, out, lse = [t.numpy() for t in runs[0]]
     kc = {}
+    other = {}
     for qi in range(w.n_q):
         oq = _oq(w, lay, kc, qi)
         rpool, rb, _ = oq.full(0)
         check_set(pool[qi, :cnt[qi]], rpool, lambda j: rb[j], f"{name} q{qi} pool")
-        if not np.array_equal(pool[qi, :cnt[qi]], rpool):
-            continue
         keep, _, _ = oq.reindex(layer, rpool)
         check_set(tk[qi, :tc[qi]], keep, lambda p: oq.scores_at(layer, p), f"{name} q{qi} topk")
+        ro, rl = oq.attention(layer, keep)
         if np.array_equal(tk[qi, :tc[qi]], keep):
-            ro, rl = oq.attention(layer, keep)
             check_attention(out[qi], lse[qi], ro, rl, f"{name} q{qi}")
+        else:
+            other[qi] = (keep, ro, rl)
+    if other:
+        # attention on the oracle's own Top-K where the sets differ in the band
+        tk2, tc2 = with_oracle_rows(tk_t, tc_t, {qi: v[0] for qi, v in other.items()})
+        o2, l2 = g.attend(layer, tk2, tc2)
+        torch.cuda.synchronize()
+        for qi, (_, ro, rl) in other.items():
+            check_attention(o2[qi].cpu().numpy(), l2[qi].cpu().numpy(), ro, rl, f"{name} q{qi} oracle-set")
 
 
 def test_ties_lower_position_wins():

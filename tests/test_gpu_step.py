@@ -4,13 +4,14 @@ bit for bit), and the same call captured into a HIP graph and replayed.
 
 The stage calls themselves are checked against the oracle in
 test_gpu_parity.py; here the step's outputs are also checked against the
-oracle for the Full layer of one query per case."""
+oracle: every query's Full layer, and a Reuse layer (a fresh main query over
+the oracle's own Top-K of the Reindex layer)."""
 import numpy as np
 import pytest
 import torch
 
 import workloads as wl
-from tests._harness import GpuCase, OracleQuery, check_attention, check_set, lib
+from tests._harness import GpuCase, OracleQuery, check_attention, check_set, lib, with_oracle_rows
 from tests.test_gpu_parity import CASES
 
 pytestmark = pytest.mark.gpu
@@ -69,17 +70,31 @@ def test_step_modes_match_stage_calls(name):
     _same(bufs["topk_count"], tc, f"{name} topk count")
     _same(bufs["out"], out, f"{name} out")
     _same(bufs["lse"], lse, f"{name} lse")
-    # the Full layer of query 0 against the oracle
-    oq = OracleQuery(w, wl.layout(w), 0)
-    rpool, rb, _ = oq.full(0)
-    check_set(bufs["pool_blocks"][0, :int(cnt[0])].cpu().numpy(), rpool, lambda j: rb[j], f"{name} step pool")
-    if np.array_equal(bufs["pool_blocks"][0, :int(cnt[0])].cpu().numpy(), rpool):
+    # every query's Full layer against the oracle: pool and Top-K within the
+    # selection band; attention on the step's own output when the Top-K is
+    # the oracle's, else the same attention call on the oracle's set
+    lay = wl.layout(w)
+    oqs, rpools, keep1, other = {}, {}, {}, {}
+    for qi in range(n_q):
+        oq = oqs[qi] = OracleQuery(w, lay, qi)
+        rpool, rb, _ = oq.full(0)
+        rpools[qi] = rpool
+        check_set(bufs["pool_blocks"][qi, :int(cnt[qi])].cpu().numpy(), rpool, lambda j: rb[j], f"{name} q{qi} step pool")
         keep, _, _ = oq.reindex(0, rpool)
-        got = bufs["topk_pos"][0, :int(tc[0])].cpu().numpy()
-        check_set(got, keep, lambda p: oq.scores_at(0, p), f"{name} step topk")
+        got = bufs["topk_pos"][qi, :int(tc[qi])].cpu().numpy()
+        check_set(got, keep, lambda p, oq=oq: oq.scores_at(0, p), f"{name} q{qi} step topk")
+        ro, rl = oq.attention(0, keep)
         if np.array_equal(got, keep):
-            ro, rl = oq.attention(0, keep)
-            check_attention(bufs["out"][0].cpu().numpy(), bufs["lse"][0].cpu().numpy(), ro, rl, f"{name} step")
+            check_attention(bufs["out"][qi].cpu().numpy(), bufs["lse"][qi].cpu().numpy(), ro, rl, f"{name} q{qi} step")
+        else:
+            other[qi] = (keep, ro, rl)
+        keep1[qi] = oq.reindex(1, rpool)[0]
+    if other:
+        tk2, tc2 = with_oracle_rows(tk, tc, {qi: v[0] for qi, v in other.items()})
+        out_o, lse_o = g.attend(0, tk2, tc2)
+        torch.cuda.synchronize()
+        for qi, (_, ro, rl) in other.items():
+            check_attention(out_o[qi].cpu().numpy(), lse_o[qi].cpu().numpy(), ro, rl, f"{name} q{qi} oracle-set")
     # Reindex layer (fresh indexer and main queries) on the Full layer's pool
     _step(g, csa2.LAYER_REINDEX, 1, bufs, ws)
     tk1, tc1, _ = g.reindex(1, pool, cnt)
@@ -99,6 +114,17 @@ def test_step_modes_match_stage_calls(name):
     torch.cuda.synchronize()
     _same(bufs["out"], out2, f"{name} reuse out")
     _same(bufs["lse"], lse2, f"{name} reuse lse")
+    # a Reuse layer against the oracle: a fresh main query (layer 2) over an
+    # inherited Top-K, here the oracle's Top-K of the Reindex layer (layer 1)
+    tk_o, tc_o = with_oracle_rows(tk1, tc1, keep1)
+    bufs["out"].fill_(3.0)
+    csa2.decode_step(g.dims, g.batch, csa2.LAYER_REUSE, None, None, None, bufs["pool_blocks"], bufs["pool_count"],
+                     tk_o, tc_o, ql, qr, 1.0, codes, scales, kv_rope, swa_kv, g.swa_base, bufs["out"], bufs["lse"],
+                     ws=ws)
+    torch.cuda.synchronize()
+    for qi in range(n_q):
+        ro, rl = oqs[qi].attention(2, keep1[qi])
+        check_attention(bufs["out"][qi].cpu().numpy(), bufs["lse"][qi].cpu().numpy(), ro, rl, f"{name} q{qi} reuse")
     # the step leaves the Reindex counters (after the Full index's part of
     # the workspace) at zero for the next call
     off = (-ws.data_ptr()) % 256 + csa2.workspace_full(g.dims, g.batch)
