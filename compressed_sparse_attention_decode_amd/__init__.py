@@ -28,7 +28,7 @@ __all__ = ["Dims", "Batch", "Csa2Error", "lib", "lib_path", "encode_kv", "encode
            "index_scan", "index_pool", "n_blocks", "block_scores_ld", "workspace_pool",
            "index_reindex", "attend", "workspace_full", "workspace_reindex",
            "workspace_attend", "abi_version", "Call", "decode_step", "workspace_step", "Pages", "page_rows",
-           "LAYER_FULL", "LAYER_REINDEX", "LAYER_REUSE", "stream_read"]
+           "LAYER_FULL", "LAYER_REINDEX", "LAYER_REUSE", "stream_read", "decode_step_noalloc"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 lib_path = os.path.join(_PKG, "libcsa2.so")
@@ -98,6 +98,8 @@ def lib() -> ctypes.CDLL:
             "csa2_decode_step": (I32, [PD, PQ, I32, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_float,
                                        P, P, P, P, P, P, P, P, SZ, P]),
             "csa2_stream_read": (I32, [P, I64, P, P]),
+            "csa2_decode_step_noalloc": (I32, [PD, PQ, I32, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_float,
+                                               P, P, P, P, P, P, P, P]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -610,3 +612,42 @@ def stream_read(buf: torch.Tensor, sink: torch.Tensor, prepare: bool = False):
     nbytes = buf.numel() * buf.element_size()
     args = (buf.data_ptr(), nbytes - nbytes % 16, sink.data_ptr(), _stream(buf.device))
     return _issue(lib().csa2_stream_read, args, (), prepare)
+
+
+def decode_step_noalloc(dims: Dims, b: Batch, mode: int, idx_q, idx_w, idx_k,
+                        pool_blocks: torch.Tensor, pool_count: torch.Tensor,
+                        topk_pos: torch.Tensor, topk_count: torch.Tensor,
+                        q_lat: torch.Tensor, q_rope: torch.Tensor, softmax_scale: float,
+                        kv_codes: torch.Tensor, kv_scales: torch.Tensor, kv_rope: torch.Tensor,
+                        swa_kv: torch.Tensor, swa_base: torch.Tensor, out: torch.Tensor,
+                        lse: Optional[torch.Tensor] = None, prepare: bool = False):
+    """decode_step without a workspace (csa2_decode_step_noalloc): the
+    library's own per-GPU scratch array serves the stages, and nothing is
+    allocated, here or in the library.  Calls that may overlap on one GPU
+    race on that array."""
+    if mode not in (LAYER_FULL, LAYER_REINDEX, LAYER_REUSE):
+        raise ValueError("mode must be LAYER_FULL, LAYER_REINDEX or LAYER_REUSE")
+    n_q, H = b.n_q, dims.n_heads
+    _dev(pool_blocks, pool_count, topk_pos, topk_count, q_lat, q_rope, kv_codes, kv_scales, kv_rope, swa_kv,
+         swa_base, out, lse)
+    if pool_blocks.shape != (n_q, dims.pool_blocks) or pool_count.shape != (n_q,):
+        raise ValueError("pool shape mismatch")
+    if topk_pos.shape != (n_q, dims.topk) or topk_count.shape != (n_q,):
+        raise ValueError("topk shape mismatch")
+    if q_lat.shape != (n_q, H, 512) or q_rope.shape != (n_q, H, 64) or out.shape != (n_q, H, 512):
+        raise ValueError("q_lat / q_rope / out shape mismatch")
+    if swa_kv.dim() != 2 or swa_kv.shape[1] != 576 or swa_base.shape != (n_q,):
+        raise ValueError("swa_kv must be [rows, 576] and swa_base [n_q]")
+    if mode == LAYER_REUSE and idx_q is None:
+        qp, kp, wp_ = [None, None], [None, None], None
+    else:
+        fp4, qp, kp = _check_idx(dims, b, idx_q, idx_w, idx_k)
+        if not fp4:
+            qp, kp = [qp[0], None], [kp[0], None]
+        wp_ = idx_w.data_ptr()
+    d, q = dims.c(), b.c()
+    args = (ctypes.byref(d), ctypes.byref(q), mode, qp[0], qp[1], wp_, kp[0], kp[1], pool_blocks.data_ptr(),
+            pool_count.data_ptr(), topk_pos.data_ptr(), topk_count.data_ptr(), q_lat.data_ptr(), q_rope.data_ptr(),
+            float(softmax_scale), kv_codes.data_ptr(), kv_scales.data_ptr(), kv_rope.data_ptr(), swa_kv.data_ptr(),
+            swa_base.data_ptr(), out.data_ptr(), _ptr(lse), _stream(q_lat.device))
+    return _issue(lib().csa2_decode_step_noalloc, args, (d, q), prepare)

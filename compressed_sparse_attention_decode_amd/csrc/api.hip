@@ -170,8 +170,11 @@ size_t full_ws(const csa2_dims* d, const csa2_queries* q) {
 
 // Reindex workspace: per-query completion counters (zero between calls),
 // then the order keys n_q x 8P u32
+size_t reindex_keys_ws(const csa2_dims* d, const csa2_queries* q) {
+  return align256((size_t)q->n_q * d->pool_blocks * 8 * 4);
+}
 size_t reindex_ws(const csa2_dims* d, const csa2_queries* q) {
-  return align256((size_t)q->n_q * 4) + align256((size_t)q->n_q * d->pool_blocks * 8 * 4);
+  return align256((size_t)q->n_q * 4) + reindex_keys_ws(d, q);
 }
 
 // Pool blocks per Reindex scoring workgroup: 32 when 32-block workgroups
@@ -551,11 +554,13 @@ csa2_status csa2_index_reindex_workspace_size(const csa2_dims* d, const csa2_que
   return CSA2_OK;
 }
 
+// counters: when given, the per-query completion counters live there (zero
+// between calls) and ws holds only the order keys
 static csa2_status index_reindex(const csa2_dims* d, const csa2_queries* q, const uint8_t* idx_q, const uint8_t* q_scales,
                                  const float* idx_w, const uint8_t* idx_k, const uint8_t* k_scales, bool fp4,
                                  const int32_t* pool_blocks, const int32_t* pool_count, int32_t* topk_pos,
                                  int32_t* topk_count, float* topk_scores, void* ws, size_t ws_bytes, void* stream,
-                                 bool dry = false, const csa2_pages* pages = nullptr) {
+                                 bool dry = false, const csa2_pages* pages = nullptr, uint32_t* counters = nullptr) {
   csa2_status st = check_dims(d);
   if (st) return st;
   if ((st = check_queries(q))) return st;
@@ -563,7 +568,7 @@ static csa2_status index_reindex(const csa2_dims* d, const csa2_queries* q, cons
   if (pages && (st = check_pages(pages, fp4 ? d->idx_dim / 2 : d->idx_dim))) return st;
   if (!pool_blocks || !pool_count || !topk_pos || !topk_count)
     return fail(CSA2_ERR_INVALID_ARG, "required pointer is NULL");
-  if ((st = check_ws(ws, ws_bytes, reindex_ws(d, q)))) return st;
+  if ((st = check_ws(ws, ws_bytes, counters ? reindex_keys_ws(d, q) : reindex_ws(d, q)))) return st;
   if ((st = check_device())) return st;
   if (dry) return CSA2_OK;
   ReindexArgs ra;
@@ -576,8 +581,8 @@ static csa2_status index_reindex(const csa2_dims* d, const csa2_queries* q, cons
   ra.pool = d->pool_blocks; ra.topk = d->topk;
   ra.blocks_per_wg = reindex_blocks_per_wg(d, q);
   ra.split = (d->pool_blocks + ra.blocks_per_wg - 1) / ra.blocks_per_wg;
-  ra.done = (uint32_t*)ws;
-  ra.keys = (uint32_t*)((char*)ws + align256((size_t)q->n_q * 4));
+  ra.done = counters ? counters : (uint32_t*)ws;
+  ra.keys = counters ? (uint32_t*)ws : (uint32_t*)((char*)ws + align256((size_t)q->n_q * 4));
   ra.topk_pos = topk_pos; ra.topk_count = topk_count; ra.topk_scores = topk_scores;
   ra.pages = pages ? pages->table : nullptr;
   ra.page_shift = pages ? page_shift(pages) : 0;
@@ -700,6 +705,39 @@ csa2_status csa2_page_rows(const csa2_pages* pages, int64_t n, const int64_t* ta
   return e == hipSuccess ? CSA2_OK : hip_fail(e, "page rows launch");
 }
 
+// ---------------------------------------------------------------- no-alloc step
+// csa2_decode_step_noalloc's scratch: one array per GPU, for callers that
+// cannot allocate.  Its first kScratchCounterBytes hold the Reindex
+// completion counters of up to kScratchMaxQueries queries at a fixed place:
+// zero when the module loads and left at zero by every call, so nothing has
+// to clear them (and no memset enters a captured graph).  The rest holds the
+// step's workspace, whose layout changes with the call's sizes; no part of
+// it needs to start at zero.
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+constexpr int kScratchMaxQueries = 65536;
+constexpr size_t kScratchCounterBytes = (size_t)kScratchMaxQueries * 4;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+// The scratch array's device address on the current device, looked up once
+// per device (the array's host-side name is not a device address).
+static csa2_status scratch_ptr(unsigned char** out) {
+  static std::mutex mu;
+  static unsigned char* ptrs[64] = {nullptr};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= 64) return fail(CSA2_ERR_UNSUPPORTED, "device id %d out of range", dev);
+  std::lock_guard<std::mutex> lk(mu);
+  if (!ptrs[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    ptrs[dev] = (unsigned char*)p;
+  }
+  *out = ptrs[dev];
+  return CSA2_OK;
+}
+
 // The layer step's workspace: the Full index's (pool + block scores), then
 // the Reindex one (its counters first), then the attention partials.
 static size_t step_ws_full(const csa2_dims* d, const csa2_queries* q) { return full_ws(d, q); }
@@ -720,7 +758,8 @@ static csa2_status decode_step(const csa2_dims* d, const csa2_queries* q, int32_
                                int32_t* topk_pos, int32_t* topk_count, const uint16_t* q_lat, const uint16_t* q_rope,
                                float softmax_scale, const uint8_t* kv_codes, const uint8_t* kv_scales,
                                const uint16_t* kv_rope, const uint16_t* swa_kv, const int64_t* swa_base, float* out,
-                               float* lse, void* ws, size_t ws_bytes, void* stream, const csa2_pages* pages) {
+                               float* lse, void* ws, size_t ws_bytes, void* stream, const csa2_pages* pages,
+                               uint32_t* counters = nullptr) {
   csa2_status st = check_dims(d);
   if (st) return st;
   if ((st = check_queries(q))) return st;
@@ -729,13 +768,15 @@ static csa2_status decode_step(const csa2_dims* d, const csa2_queries* q, int32_
   if ((idx_q_scales == nullptr) != (idx_k_scales == nullptr))
     return fail(CSA2_ERR_INVALID_ARG, "idx_q_scales and idx_k_scales must both be given (FP4 rows) or both NULL");
   const bool fp4 = idx_q_scales != nullptr;
-  size_t need = 0;
-  if ((st = csa2_decode_step_workspace_size(d, q, &need))) return st;
+  // (with external counters the Reindex part holds only its order keys)
+  const size_t n_full = step_ws_full(d, q);
+  const size_t n_re = counters ? reindex_keys_ws(d, q) : step_ws_reindex(d, q);
+  const size_t need = n_full + n_re + attend_ws(d, q);
   if ((st = check_ws(ws, ws_bytes, need))) return st;
   char* w_full = (char*)ws;
-  char* w_re = w_full + step_ws_full(d, q);
-  char* w_att = w_re + step_ws_reindex(d, q);
-  const size_t n_full = step_ws_full(d, q), n_re = step_ws_reindex(d, q), n_att = ws_bytes - n_full - n_re;
+  char* w_re = w_full + n_full;
+  char* w_att = w_re + n_re;
+  const size_t n_att = ws_bytes - n_full - n_re;
   // every stage's arguments are checked before the first launch
   for (int pass = 0; pass < 2; ++pass) {
     const bool dry = pass == 0;
@@ -745,7 +786,7 @@ static csa2_status decode_step(const csa2_dims* d, const csa2_queries* q, int32_
       return st;
     if (mode != CSA2_LAYER_REUSE &&
         (st = index_reindex(d, q, idx_q, idx_q_scales, idx_w, idx_k, idx_k_scales, fp4, pool_blocks, pool_count,
-                            topk_pos, topk_count, nullptr, w_re, n_re, stream, dry, pages)))
+                            topk_pos, topk_count, nullptr, w_re, n_re, stream, dry, pages, counters)))
       return st;
     if ((st = attend(d, q, q_lat, q_rope, softmax_scale, kv_codes, kv_scales, kv_rope, topk_pos, topk_count, swa_kv,
                      swa_base, out, lse, attend_ws(d, q) ? w_att : nullptr, n_att, stream, dry, pages)))
@@ -764,6 +805,32 @@ csa2_status csa2_decode_step(const csa2_dims* d, const csa2_queries* q, int32_t 
   return decode_step(d, q, mode, idx_q, idx_q_scales, idx_w, idx_k, idx_k_scales, pool_blocks, pool_count, topk_pos,
                      topk_count, q_lat, q_rope, softmax_scale, kv_codes, kv_scales, kv_rope, swa_kv, swa_base, out,
                      lse, ws, ws_bytes, stream, nullptr);
+}
+
+csa2_status csa2_decode_step_noalloc(const csa2_dims* d, const csa2_queries* q, int32_t mode, const uint8_t* idx_q,
+                                     const uint8_t* idx_q_scales, const float* idx_w, const uint8_t* idx_k,
+                                     const uint8_t* idx_k_scales, int32_t* pool_blocks, int32_t* pool_count,
+                                     int32_t* topk_pos, int32_t* topk_count, const uint16_t* q_lat,
+                                     const uint16_t* q_rope, float softmax_scale, const uint8_t* kv_codes,
+                                     const uint8_t* kv_scales, const uint16_t* kv_rope, const uint16_t* swa_kv,
+                                     const int64_t* swa_base, float* out, float* lse, void* stream) {
+  csa2_status st = check_dims(d);
+  if (st) return st;
+  if ((st = check_queries(q))) return st;
+  if (q->n_q > kScratchMaxQueries)
+    return fail(CSA2_ERR_WORKSPACE, "csa2_decode_step_noalloc takes at most %d queries (got %d)", kScratchMaxQueries,
+                q->n_q);
+  const size_t need = step_ws_full(d, q) + reindex_keys_ws(d, q) + attend_ws(d, q);
+  const size_t have = kScratchBytes - kScratchCounterBytes;
+  if (need > have)
+    return fail(CSA2_ERR_WORKSPACE, "csa2_decode_step_noalloc: this batch needs %zu bytes of scratch, the maximum is %zu",
+                need, have);
+  if ((st = check_device())) return st;
+  unsigned char* base = nullptr;
+  if ((st = scratch_ptr(&base))) return st;
+  return decode_step(d, q, mode, idx_q, idx_q_scales, idx_w, idx_k, idx_k_scales, pool_blocks, pool_count, topk_pos,
+                     topk_count, q_lat, q_rope, softmax_scale, kv_codes, kv_scales, kv_rope, swa_kv, swa_base, out,
+                     lse, base + kScratchCounterBytes, have, stream, nullptr, (uint32_t*)base);
 }
 
 csa2_status csa2_decode_step_paged(const csa2_dims* d, const csa2_queries* q, const csa2_pages* pages,

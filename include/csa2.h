@@ -464,6 +464,31 @@ csa2_status csa2_decode_step(const csa2_dims* dims, const csa2_queries* q, int32
                              const uint16_t* swa_kv, const int64_t* swa_base, float* out, float* lse,
                              void* ws, size_t ws_bytes, void* stream);
 
+/* csa2_decode_step without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * and harnesses that forbid allocation.  The same stages, kernels and outputs
+ * as csa2_decode_step; the scratch they need (pool workspace, block scores,
+ * Reindex order keys and completion counters, attention partials) comes from
+ * one array of 64 MiB that the library holds on each GPU it runs on until the
+ * process ends.  The call allocates nothing.
+ *   Limits: at most 65,536 queries, and a batch whose workspace
+ *   (csa2_decode_step_workspace_size) fits in 64 MiB minus 256 KiB: batch 8
+ *   at 128K and batch 1 at 1M context take about 12 MB, 32 queries of up to
+ *   256K about 40 MB.  Larger batches get CSA2_ERR_WORKSPACE, enqueuing
+ *   nothing.
+ *   Every call on one GPU uses that GPU's array: calls that may overlap on
+ *   one GPU (different streams, or a graph replayed while another call runs)
+ *   race and must be ordered by the caller.  Other errors as
+ *   csa2_decode_step. */
+csa2_status csa2_decode_step_noalloc(const csa2_dims* dims, const csa2_queries* q, int32_t mode,
+                                     const uint8_t* idx_q, const uint8_t* idx_q_scales, const float* idx_w,
+                                     const uint8_t* idx_k, const uint8_t* idx_k_scales,
+                                     int32_t* pool_blocks, int32_t* pool_count, int32_t* topk_pos,
+                                     int32_t* topk_count, const uint16_t* q_lat, const uint16_t* q_rope,
+                                     float softmax_scale, const uint8_t* kv_codes, const uint8_t* kv_scales,
+                                     const uint16_t* kv_rope, const uint16_t* swa_kv, const int64_t* swa_base,
+                                     float* out, float* lse, void* stream);
+
 /* Measurement helper, not a step of the method: reads `bytes` bytes of
  * device memory at `buf` once (16-byte nontemporal loads into registers, two
  * workgroups per CU, each over one contiguous chunk) and writes nothing,

@@ -280,3 +280,23 @@ def test_decode_step_rejected_before_any_device_work():
                                                          L.csa2_index_reindex_workspace_size,
                                                          L.csa2_attend_workspace_size)]
     assert n.value >= sum(parts)
+
+
+def test_noalloc_step_rejects_batches_beyond_its_scratch():
+    """csa2_decode_step_noalloc checks its scratch limit on the host: the
+    speculative-verify batch (256 query tokens up to 512K) needs more than
+    64 MiB, and more than 65,536 queries are refused outright."""
+    L = csa2.lib()
+    d = _dims().c()
+    args = [0x1000] * 17 + [None, None]
+    q = _batch(n_q=256, max_visible=524291, g=4).c()
+    st = L.csa2_decode_step_noalloc(ctypes.byref(d), ctypes.byref(q), 2, None, None, None, None, None,
+                                    0x1000, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000, 1.0, 0x1000, 0x1000, 0x1000,
+                                    0x1000, 0x1000, 0x1000, None, None)
+    assert st == WORKSPACE and b"maximum" in L.csa2_last_error()
+    q = _batch(n_q=65537, max_visible=4096).c()
+    st = L.csa2_decode_step_noalloc(ctypes.byref(d), ctypes.byref(q), 2, None, None, None, None, None,
+                                    0x1000, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000, 1.0, 0x1000, 0x1000, 0x1000,
+                                    0x1000, 0x1000, 0x1000, None, None)
+    assert st == WORKSPACE and b"65536" in L.csa2_last_error()
+    del args
