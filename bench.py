@@ -198,6 +198,11 @@ class Step:
         self.ws_p = torch.empty(csa2.workspace_pool(st.dims, st.batch) + 256, dtype=torch.uint8, device=dev)
         self.ws_r = torch.zeros(csa2.workspace_reindex(st.dims, st.batch) + 256, dtype=torch.uint8, device=dev)
         self.ws_a = torch.empty(csa2.workspace_attend(st.dims, st.batch) + 256, dtype=torch.uint8, device=dev)
+        # a Full layer's Top-K comes from the scan's own scores (same query):
+        # the scan keeps every position's score as an order key
+        self.full_topk = not w.fresh_q_per_layer
+        self.pk = torch.empty(n_q, csa2.pos_keys_ld(st.dims, st.batch), dtype=torch.int32, device=dev) \
+            if self.full_topk else None
         for layer in [0] + self.layers:
             st.iq(layer)
             st.mq(layer)
@@ -219,12 +224,20 @@ class Step:
                 seq.append(("encode", csa2.encode_kv(self.enc_lat, self.enc_rope, *self.enc_planes, prepare=True,
                                                      group=w.dims.kv_group)))
             q0, w0 = st.iq(0)
-            # csa2_index_full's two stages, issued separately to time each
+            # the stages of a Full layer (csa2_decode_step's chain), issued
+            # separately to time each
             seq.append(("scan", csa2.index_scan(st.dims, st.batch, q0, w0, idx_k, self.bs, pool_ws=self.ws_p,
-                                                prepare=True, pages=st.pages)))
+                                                prepare=True, pages=st.pages, pos_keys=self.pk)))
             seq.append(("pool", csa2.index_pool(st.dims, st.batch, self.bs, self.pool, self.pcnt, ws=self.ws_p,
                                                 from_scan=True, prepare=True)))
-            for i, layer in enumerate(self.layers):
+            if self.full_topk:
+                seq.append(("topk", csa2.index_topk_keys(st.dims, st.batch, self.pool, self.pcnt, self.bs, self.pk,
+                                                         topk_pos=self.tk[0], topk_count=self.tc[0], prepare=True)))
+                ql, qr = st.mq(0)
+                seq.append(("attend", csa2.attend(st.dims, st.batch, ql, qr, 1.0, codes, scales, kv_rope,
+                                                  self.tk[0], self.tc[0], swa_kv, st.swa_base, out=self.out[0],
+                                                  lse=self.lse[0], ws=self.ws_a, prepare=True, pages=st.pages)))
+            for i, layer in enumerate(self.layers if not self.full_topk else []):
                 q, wt = st.iq(layer)
                 seq.append(("reindex", csa2.index_reindex(st.dims, st.batch, q, wt, idx_k, self.pool, self.pcnt,
                                                           topk_pos=self.tk[i], topk_count=self.tc[i],

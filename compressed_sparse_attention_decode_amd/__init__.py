@@ -28,7 +28,7 @@ __all__ = ["Dims", "Batch", "Csa2Error", "lib", "lib_path", "encode_kv", "encode
            "index_scan", "index_pool", "n_blocks", "block_scores_ld", "workspace_pool",
            "index_reindex", "attend", "workspace_full", "workspace_reindex",
            "workspace_attend", "abi_version", "Call", "decode_step", "workspace_step", "Pages", "page_rows",
-           "LAYER_FULL", "LAYER_REINDEX", "LAYER_REUSE", "stream_read", "decode_step_noalloc"]
+           "LAYER_FULL", "LAYER_REINDEX", "LAYER_REUSE", "stream_read", "decode_step_noalloc", "index_topk_keys", "pos_keys_ld"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 lib_path = os.path.join(_PKG, "libcsa2.so")
@@ -98,6 +98,8 @@ def lib() -> ctypes.CDLL:
             "csa2_decode_step": (I32, [PD, PQ, I32, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_float,
                                        P, P, P, P, P, P, P, P, SZ, P]),
             "csa2_stream_read": (I32, [P, I64, P, P]),
+            "csa2_index_scan_keys": (I32, [PD, PQ, PP, P, P, P, P, P, P, I64, P, I64, P, SZ, P]),
+            "csa2_index_topk_keys": (I32, [PD, PQ, P, P, P, I64, P, I64, P, P, P, P]),
             "csa2_decode_step_noalloc": (I32, [PD, PQ, I32, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_float,
                                                P, P, P, P, P, P, P, P]),
         }
@@ -410,15 +412,22 @@ def block_scores_ld(dims: Dims, b: Batch) -> int:
 POOL_WS_FROM_SCAN = 1
 
 
+def pos_keys_ld(dims: Dims, b: Batch) -> int:
+    """Row stride of a position-key array: 8 n_blocks rounded up to 32 (at least 32)."""
+    return max(32, (8 * n_blocks(dims, b) + 31) // 32 * 32)
+
+
 def index_scan(dims: Dims, b: Batch, idx_q, idx_w: torch.Tensor, idx_k,
                block_scores: Optional[torch.Tensor] = None, pool_ws: Optional[torch.Tensor] = None,
-               prepare: bool = False, pages: Optional[Pages] = None):
+               prepare: bool = False, pages: Optional[Pages] = None, pos_keys: Optional[torch.Tensor] = None):
     """Full-mode scan: block scores float32 [n_q, ld] (b_j for j < nb).  With
     `pool_ws` (a pool-select workspace) the scan also prepares it for an
     index_pool(..., ws=pool_ws, from_scan=True) call on these scores.  With
-    `pages` the keys are paged (csa2_index_scan_paged)."""
+    `pages` the keys are paged (csa2_index_scan_paged).  With `pos_keys`
+    (int32 [n_q, ld], ld from pos_keys_ld) it also keeps every candidate
+    position's score as an order key (csa2_index_scan_keys)."""
     dev = _rows_dev(idx_k)
-    _dev(block_scores, pool_ws)
+    _dev(block_scores, pool_ws, pos_keys)
     fp4, qp, kp = _check_idx(dims, b, idx_q, idx_w, idx_k)
     if block_scores is None:
         block_scores = torch.empty(b.n_q, block_scores_ld(dims, b), dtype=torch.float32, device=dev)
@@ -426,6 +435,19 @@ def index_scan(dims: Dims, b: Batch, idx_q, idx_w: torch.Tensor, idx_k,
         raise ValueError("block_scores must be float32 [n_q, ld]")
     wp, wn = _ws_ptr(pool_ws)
     d, q = dims.c(), b.c()
+    if pos_keys is not None:
+        if pos_keys.dtype != torch.int32 or pos_keys.dim() != 2 or pos_keys.shape[0] != b.n_q:
+            raise ValueError("pos_keys must be int32 [n_q, ld]")
+        pg = pages.c() if pages is not None else None
+        if pages is not None:
+            _check_page_rows(pages, *(idx_k if fp4 else (idx_k,)))
+        qs, ks = (qp[1], kp[1]) if fp4 else (None, None)
+        args = (ctypes.byref(d), ctypes.byref(q), ctypes.byref(pg) if pg is not None else None, qp[0], qs,
+                idx_w.data_ptr(), kp[0], ks, block_scores.data_ptr(), block_scores.shape[1], pos_keys.data_ptr(),
+                pos_keys.shape[1], wp, wn, _stream(dev))
+        keep = (d, q, pg, pool_ws) + ((pages.table,) if pages is not None else ())
+        call = _issue(lib().csa2_index_scan_keys, args, keep, prepare)
+        return call if prepare else block_scores
     args = (ctypes.byref(d), ctypes.byref(q), *qp, idx_w.data_ptr(), *kp, block_scores.data_ptr(),
             block_scores.shape[1], wp, wn, _stream(dev))
     if pages is not None:
@@ -651,3 +673,29 @@ def decode_step_noalloc(dims: Dims, b: Batch, mode: int, idx_q, idx_w, idx_k,
             float(softmax_scale), kv_codes.data_ptr(), kv_scales.data_ptr(), kv_rope.data_ptr(), swa_kv.data_ptr(),
             swa_base.data_ptr(), out.data_ptr(), _ptr(lse), _stream(q_lat.device))
     return _issue(lib().csa2_decode_step_noalloc, args, (d, q), prepare)
+
+
+def index_topk_keys(dims: Dims, b: Batch, pool_blocks: torch.Tensor, pool_count: torch.Tensor,
+                    block_scores: torch.Tensor, pos_keys: torch.Tensor,
+                    topk_pos: Optional[torch.Tensor] = None, topk_count: Optional[torch.Tensor] = None,
+                    topk_scores: Optional[torch.Tensor] = None, prepare: bool = False):
+    """A Full layer's Top-K from index_scan(..., pos_keys=...)'s scores
+    (csa2_index_topk_keys): the same set as index_reindex with the scan's
+    query.  Returns (topk_pos int32 [n_q, K], topk_count)."""
+    dev = pool_blocks.device
+    _dev(pool_blocks, pool_count, block_scores, pos_keys, topk_pos, topk_count, topk_scores)
+    n_q = b.n_q
+    if pool_blocks.shape != (n_q, dims.pool_blocks) or pool_count.shape != (n_q,):
+        raise ValueError("pool shape mismatch")
+    if topk_pos is None:
+        topk_pos = torch.empty(n_q, dims.topk, dtype=torch.int32, device=dev)
+    if topk_count is None:
+        topk_count = torch.empty(n_q, dtype=torch.int32, device=dev)
+    if topk_scores is not None and topk_scores.shape != (n_q, dims.topk):
+        raise ValueError("topk_scores must be float32 [n_q, K]")
+    d, q = dims.c(), b.c()
+    args = (ctypes.byref(d), ctypes.byref(q), pool_blocks.data_ptr(), pool_count.data_ptr(), block_scores.data_ptr(),
+            block_scores.shape[1], pos_keys.data_ptr(), pos_keys.shape[1], topk_pos.data_ptr(),
+            topk_count.data_ptr(), _ptr(topk_scores), _stream(dev))
+    call = _issue(lib().csa2_index_topk_keys, args, (d, q), prepare)
+    return call if prepare else (topk_pos, topk_count)

@@ -168,6 +168,13 @@ size_t full_ws(const csa2_dims* d, const csa2_queries* q) {
   return pool_ws(d, q) + align256((size_t)q->n_q * full_ldb(d, q) * 4);
 }
 
+// A Full layer's position keys (decode step): n_q x (8 x the block-score
+// stride) order keys, one per candidate position
+int64_t full_ldpk(const csa2_dims* d, const csa2_queries* q) { return full_ldb(d, q) * 8; }
+size_t pkey_ws(const csa2_dims* d, const csa2_queries* q) {
+  return align256((size_t)q->n_q * full_ldpk(d, q) * 4);
+}
+
 // Reindex workspace: per-query completion counters (zero between calls),
 // then the order keys n_q x 8P u32
 size_t reindex_keys_ws(const csa2_dims* d, const csa2_queries* q) {
@@ -342,12 +349,22 @@ static csa2_status check_block_scores(const csa2_dims* d, const csa2_queries* q,
   return CSA2_OK;
 }
 
+// Position keys: a multiple of 32 per row, covering every candidate position
+// rounded up to 32 (the scan writes whole 16-position steps), 16-byte aligned.
+static csa2_status check_pos_keys(const csa2_dims* d, const csa2_queries* q, const uint32_t* pkey, int64_t ld) {
+  const int64_t need = (max_blocks(d, q) * 8 + 31) / 32 * 32;
+  if (ld < need || ld % 32 || ((uintptr_t)pkey & 15))
+    return fail(CSA2_ERR_INVALID_ARG, "pos_keys: ld_pos_keys %lld must be a multiple of 32 >= %lld, 16-byte aligned",
+                (long long)ld, (long long)need);
+  return CSA2_OK;
+}
+
 // The Full scan; with pool_ws it also leaves the per-tile key ranges and a
 // cleared histogram for the pool select.
 static csa2_status run_scan(const csa2_dims* d, const csa2_queries* q, const uint8_t* idx_q, const uint8_t* q_scales,
                             const float* idx_w, const uint8_t* idx_k, const uint8_t* k_scales, float* block_scores,
                             int64_t ld_block_scores, uint32_t* pool_ws_ptr, void* stream,
-                            const csa2_pages* pages = nullptr) {
+                            const csa2_pages* pages = nullptr, uint32_t* pkey = nullptr, int64_t ld_pkey = 0) {
   ScanArgs sa;
   sa.idx_q = idx_q; sa.idx_w = idx_w; sa.idx_k = idx_k;
   sa.idx_q_scales = q_scales; sa.idx_k_scales = k_scales;
@@ -370,6 +387,8 @@ static csa2_status run_scan(const csa2_dims* d, const csa2_queries* q, const uin
   sa.pages = pages ? pages->table : nullptr;
   sa.page_shift = pages ? page_shift(pages) : 0;
   sa.rows = pages ? pages->rows : 0;
+  sa.pkey = pkey;
+  sa.ld_pkey = ld_pkey;
   hipError_t e = launch_scan(sa, (hipStream_t)stream);
   return e == hipSuccess ? CSA2_OK : hip_fail(e, "scan launch");
 }
@@ -425,7 +444,8 @@ static csa2_status check_index_rows(const csa2_dims* d, const uint8_t* idx_q, co
 static csa2_status index_scan(const csa2_dims* d, const csa2_queries* q, const uint8_t* idx_q, const uint8_t* q_scales,
                               const float* idx_w, const uint8_t* idx_k, const uint8_t* k_scales, bool fp4,
                               float* block_scores, int64_t ld_block_scores, void* pool_wsp, size_t pool_ws_bytes,
-                              void* stream, const csa2_pages* pages = nullptr) {
+                              void* stream, const csa2_pages* pages = nullptr, uint32_t* pkey = nullptr,
+                              int64_t ld_pkey = 0) {
   csa2_status st = check_dims(d);
   if (st) return st;
   if ((st = check_queries(q))) return st;
@@ -434,9 +454,44 @@ static csa2_status index_scan(const csa2_dims* d, const csa2_queries* q, const u
   if (!block_scores) return fail(CSA2_ERR_INVALID_ARG, "block_scores is NULL");
   if ((st = check_block_scores(d, q, block_scores, ld_block_scores))) return st;
   if (pool_wsp && (st = check_ws(pool_wsp, pool_ws_bytes, pool_ws(d, q)))) return st;
+  if (pkey && (st = check_pos_keys(d, q, pkey, ld_pkey))) return st;
   if ((st = check_device())) return st;
   return run_scan(d, q, idx_q, fp4 ? q_scales : nullptr, idx_w, idx_k, fp4 ? k_scales : nullptr, block_scores,
-                  ld_block_scores, (uint32_t*)pool_wsp, stream, pages);
+                  ld_block_scores, (uint32_t*)pool_wsp, stream, pages, pkey, ld_pkey);
+}
+
+csa2_status csa2_index_scan_keys(const csa2_dims* d, const csa2_queries* q, const csa2_pages* pages,
+                                 const uint8_t* idx_q, const uint8_t* idx_q_scales, const float* idx_w,
+                                 const uint8_t* idx_k, const uint8_t* idx_k_scales, float* block_scores,
+                                 int64_t ld_block_scores, uint32_t* pos_keys, int64_t ld_pos_keys, void* pool_wsp,
+                                 size_t pool_ws_bytes, void* stream) {
+  if ((idx_q_scales == nullptr) != (idx_k_scales == nullptr))
+    return fail(CSA2_ERR_INVALID_ARG, "idx_q_scales and idx_k_scales must both be given (FP4 rows) or both NULL");
+  if (!pos_keys) return fail(CSA2_ERR_INVALID_ARG, "pos_keys is NULL");
+  return index_scan(d, q, idx_q, idx_q_scales, idx_w, idx_k, idx_k_scales, idx_q_scales != nullptr, block_scores,
+                    ld_block_scores, pool_wsp, pool_ws_bytes, stream, pages, pos_keys, ld_pos_keys);
+}
+
+csa2_status csa2_index_topk_keys(const csa2_dims* d, const csa2_queries* q, const int32_t* pool_blocks,
+                                 const int32_t* pool_count, const float* block_scores, int64_t ld_block_scores,
+                                 const uint32_t* pos_keys, int64_t ld_pos_keys, int32_t* topk_pos,
+                                 int32_t* topk_count, float* topk_scores, void* stream) {
+  csa2_status st = check_dims(d);
+  if (st) return st;
+  if ((st = check_queries(q))) return st;
+  if (!pool_blocks || !pool_count || !block_scores || !pos_keys || !topk_pos || !topk_count)
+    return fail(CSA2_ERR_INVALID_ARG, "required pointer is NULL");
+  if ((st = check_block_scores(d, q, block_scores, ld_block_scores))) return st;
+  if ((st = check_pos_keys(d, q, pos_keys, ld_pos_keys))) return st;
+  if ((st = check_device())) return st;
+  TopkKeysArgs ta;
+  ta.pool_blocks = pool_blocks; ta.pool_count = pool_count;
+  ta.bscore = block_scores; ta.ld = ld_block_scores;
+  ta.pkey = pos_keys; ta.ld_pkey = ld_pos_keys;
+  ta.n_q = q->n_q; ta.pool = d->pool_blocks; ta.topk = d->topk;
+  ta.topk_pos = topk_pos; ta.topk_count = topk_count; ta.topk_scores = topk_scores;
+  hipError_t e = launch_topk_keys(ta, (hipStream_t)stream);
+  return e == hipSuccess ? CSA2_OK : hip_fail(e, "top-k launch");
 }
 
 csa2_status csa2_index_scan_paged(const csa2_dims* d, const csa2_queries* q, const csa2_pages* pages,
@@ -493,7 +548,7 @@ static csa2_status index_full(const csa2_dims* d, const csa2_queries* q, const u
                               const float* idx_w, const uint8_t* idx_k, const uint8_t* k_scales, bool fp4,
                               int32_t* pool_blocks, int32_t* pool_count, float* block_scores, int64_t ld_block_scores,
                               void* ws, size_t ws_bytes, void* stream, bool dry = false,
-                              const csa2_pages* pages = nullptr) {
+                              const csa2_pages* pages = nullptr, uint32_t* pkey = nullptr) {
   csa2_status st = check_dims(d);
   if (st) return st;
   if ((st = check_queries(q))) return st;
@@ -512,7 +567,7 @@ static csa2_status index_full(const csa2_dims* d, const csa2_queries* q, const u
   if ((st = check_device())) return st;
   if (dry) return CSA2_OK;
   if ((st = run_scan(d, q, idx_q, fp4 ? q_scales : nullptr, idx_w, idx_k, fp4 ? k_scales : nullptr, bs, ld,
-                     (uint32_t*)ws, stream, pages)))
+                     (uint32_t*)ws, stream, pages, pkey, pkey ? full_ldpk(d, q) : 0)))
     return st;
   return run_pool(d, q, bs, ld, pool_blocks, pool_count, ws, true, stream);
 }
@@ -740,7 +795,7 @@ static csa2_status scratch_ptr(unsigned char** out) {
 
 // The layer step's workspace: the Full index's (pool + block scores), then
 // the Reindex one (its counters first), then the attention partials.
-static size_t step_ws_full(const csa2_dims* d, const csa2_queries* q) { return full_ws(d, q); }
+static size_t step_ws_full(const csa2_dims* d, const csa2_queries* q) { return full_ws(d, q) + pkey_ws(d, q); }
 static size_t step_ws_reindex(const csa2_dims* d, const csa2_queries* q) { return align256(reindex_ws(d, q)); }
 
 csa2_status csa2_decode_step_workspace_size(const csa2_dims* d, const csa2_queries* q, size_t* bytes) {
@@ -780,11 +835,27 @@ static csa2_status decode_step(const csa2_dims* d, const csa2_queries* q, int32_
   // every stage's arguments are checked before the first launch
   for (int pass = 0; pass < 2; ++pass) {
     const bool dry = pass == 0;
-    if (mode == CSA2_LAYER_FULL &&
-        (st = index_full(d, q, idx_q, idx_q_scales, idx_w, idx_k, idx_k_scales, fp4, pool_blocks, pool_count,
-                         nullptr, 0, w_full, n_full, stream, dry, pages)))
-      return st;
-    if (mode != CSA2_LAYER_REUSE &&
+    if (mode == CSA2_LAYER_FULL) {
+      // the scan also keeps every position's score; the Top-K then comes
+      // from those scores (the layer's own query: what Reindex would compute)
+      const size_t n_idx = full_ws(d, q);
+      uint32_t* pkey = (uint32_t*)(w_full + n_idx);
+      if ((st = index_full(d, q, idx_q, idx_q_scales, idx_w, idx_k, idx_k_scales, fp4, pool_blocks, pool_count,
+                           nullptr, 0, w_full, n_idx, stream, dry, pages, pkey)))
+        return st;
+      if (!topk_pos || !topk_count) return fail(CSA2_ERR_INVALID_ARG, "required pointer is NULL");
+      if (!dry) {
+        TopkKeysArgs ta;
+        ta.pool_blocks = pool_blocks; ta.pool_count = pool_count;
+        ta.bscore = (const float*)(w_full + pool_ws(d, q)); ta.ld = full_ldb(d, q);
+        ta.pkey = pkey; ta.ld_pkey = full_ldpk(d, q);
+        ta.n_q = q->n_q; ta.pool = d->pool_blocks; ta.topk = d->topk;
+        ta.topk_pos = topk_pos; ta.topk_count = topk_count; ta.topk_scores = nullptr;
+        hipError_t e = launch_topk_keys(ta, (hipStream_t)stream);
+        if (e != hipSuccess) return hip_fail(e, "top-k launch");
+      }
+    }
+    if (mode == CSA2_LAYER_REINDEX &&
         (st = index_reindex(d, q, idx_q, idx_q_scales, idx_w, idx_k, idx_k_scales, fp4, pool_blocks, pool_count,
                             topk_pos, topk_count, nullptr, w_re, n_re, stream, dry, pages, counters)))
       return st;

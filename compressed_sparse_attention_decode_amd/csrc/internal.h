@@ -82,6 +82,21 @@ struct AttendArgs {
   int64_t rows;
 };
 
+// A Full layer's Top-K from the Full scan's own scores (the same indexer
+// query as the scan, so the same scores Reindex would compute).
+struct TopkKeysArgs {
+  const int32_t* pool_blocks;   // [n_q, pool] ascending, -1 past the count
+  const int32_t* pool_count;
+  const float* bscore;          // [n_q, ld] block scores written by the scan
+  int64_t ld;
+  const uint32_t* pkey;         // [n_q, ld_pkey] position keys written by the scan
+  int64_t ld_pkey;
+  int n_q, pool, topk;
+  int32_t* topk_pos;
+  int32_t* topk_count;
+  float* topk_scores;           // optional
+};
+
 hipError_t launch_encode(int64_t n, int group, const uint16_t* latent, const uint16_t* rope,
                          const int64_t* dst_row, uint8_t* codes, uint8_t* scales,
                          uint16_t* rope_out, hipStream_t s);
@@ -93,6 +108,7 @@ hipError_t launch_pool_select(const PoolArgs& a, hipStream_t s);
 int64_t pool_ws_words(int chunks, int mm_cap);   // workspace words per query
 hipError_t launch_reindex(const ReindexArgs& a, hipStream_t s);
 hipError_t launch_attend(const AttendArgs& a, hipStream_t s);
+hipError_t launch_topk_keys(const TopkKeysArgs& a, hipStream_t s);
 hipError_t launch_stream_read(const void* buf, int64_t bytes, uint32_t* sink, int cus, hipStream_t s);
 
 // Tiling constants the host needs for grids and workspace sizes.

@@ -88,9 +88,12 @@ struct TopkCut {
   uint32_t tt;
 };
 
-// All 512 threads call this with their 32 keys (slots past the valid range
-// already 0).  Contains barriers; K >= 1.
-__device__ __forceinline__ TopkCut radix_topk(uint32_t (&key)[kPer], int K) {
+// All 512 threads call this with their PER keys (PER <= 32; thread t holds
+// slots [PER t, PER (t + 1)); slots past the valid range already 0).
+// Contains barriers; K >= 1.  Each PER has its own LDS.
+template <int PER = kPer>
+__device__ __forceinline__ TopkCut radix_topk(uint32_t (&key)[PER], int K) {
+  static_assert(PER >= 1 && PER <= 32, "a 32-bit candidate mask per thread");
   __shared__ __align__(16) uint32_t s_hist[kTkBins + kTkEmpty];
   __shared__ uint64_t s_cand[kRankCap];
   __shared__ uint32_t s_red[2 * kTkWaves];
@@ -98,7 +101,7 @@ __device__ __forceinline__ TopkCut radix_topk(uint32_t (&key)[kPer], int K) {
 
   const int tid = threadIdx.x, lane = tid & 63;
 
-  const int s0 = tid * kPer;
+  const int s0 = tid * PER;
   *reinterpret_cast<v4u*>(s_hist + 4 * tid) = v4u{0u, 0u, 0u, 0u};
   if (tid < kTkEmpty / 4) *reinterpret_cast<v4u*>(s_hist + kTkBins + 4 * tid) = v4u{0u, 0u, 0u, 0u};
   if (tid == 0) s_misc[5] = 0;
@@ -106,7 +109,7 @@ __device__ __forceinline__ TopkCut radix_topk(uint32_t (&key)[kPer], int K) {
   // key range: key - 1 sends empty slots to the top for the minimum
   uint32_t lo = 0xFFFFFFFFu, hi = 0;
 #pragma unroll
-  for (int k = 0; k < kPer; ++k) {
+  for (int k = 0; k < PER; ++k) {
     lo = min(lo, key[k] - 1u);
     hi = max(hi, key[k]);
   }
@@ -120,7 +123,7 @@ __device__ __forceinline__ TopkCut radix_topk(uint32_t (&key)[kPer], int K) {
     const uint32_t d = kmax - kmin;
     int shift = d ? max(0, 21 - (int)__clz(d)) : 0;    // (d >> shift) < 2^11
 #pragma unroll
-    for (int k = 0; k < kPer; ++k) {
+    for (int k = 0; k < PER; ++k) {
       const uint32_t b = (key[k] - kmin) >> shift;
       atomicAdd(&s_hist[key[k] != 0 ? b : kTkBins + (lane & (kTkEmpty - 1))], 1u);
     }
@@ -140,7 +143,7 @@ __device__ __forceinline__ TopkCut radix_topk(uint32_t (&key)[kPer], int K) {
       *reinterpret_cast<v4u*>(s_hist + 4 * tid) = v4u{0u, 0u, 0u, 0u};
       __syncthreads();
 #pragma unroll
-      for (int k = 0; k < kPer; ++k) {
+      for (int k = 0; k < PER; ++k) {
         const uint32_t r = key[k] - blo;
         if ((r >> shift) == 0) atomicAdd(&s_hist[r >> sh2], 1u);
       }
@@ -163,7 +166,7 @@ __device__ __forceinline__ TopkCut radix_topk(uint32_t (&key)[kPer], int K) {
       const uint32_t bw = 1u << shift;
       uint32_t cm = 0;
 #pragma unroll
-      for (int k = 0; k < kPer; ++k) cm |= (uint32_t)(key[k] - blo < bw) << k;
+      for (int k = 0; k < PER; ++k) cm |= (uint32_t)(key[k] - blo < bw) << k;
       const uint32_t nc = __builtin_popcount(cm);
       const uint32_t incl = wave_incl_scan_u32(nc);
       uint32_t wbase = 0;
@@ -198,12 +201,12 @@ __device__ __forceinline__ TopkCut radix_topk(uint32_t (&key)[kPer], int K) {
       T = blo;
       uint32_t eq = 0;
 #pragma unroll
-      for (int k = 0; k < kPer; ++k) eq += key[k] == T;
+      for (int k = 0; k < PER; ++k) eq += key[k] == T;
       uint32_t total;
       uint32_t before = block_exclusive_scan<kTkThreads>(eq, s_red, &total);
       if (before < need && need <= before + eq) {
 #pragma unroll
-        for (int k = 0; k < kPer; ++k) {
+        for (int k = 0; k < PER; ++k) {
           before += key[k] == T;
           if (key[k] == T && before == need) s_misc[7] = (uint32_t)(s0 + k);
         }
@@ -217,9 +220,9 @@ __device__ __forceinline__ TopkCut radix_topk(uint32_t (&key)[kPer], int K) {
   // lie past ST compares against T + 1, the others against T; the one thread
   // that straddles ST first clears its keys equal to T past ST.
   const uint32_t Tt = s0 > ST ? T + 1u : T;
-  if (s0 <= ST && ST < s0 + kPer - 1) {
+  if (s0 <= ST && ST < s0 + PER - 1) {
 #pragma unroll
-    for (int k = 0; k < kPer; ++k) key[k] = (key[k] == T && s0 + k > ST) ? 0u : key[k];
+    for (int k = 0; k < PER; ++k) key[k] = (key[k] == T && s0 + k > ST) ? 0u : key[k];
   }
   return TopkCut{keff, Tt};
 }

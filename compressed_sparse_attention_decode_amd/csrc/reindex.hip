@@ -105,14 +105,16 @@ __device__ __forceinline__ void score_part(const ReindexArgs& a, int q, int part
   uint32_t ksw[SPW];                               // FP4: the dword holding the lane's two scales
 #pragma unroll
   for (int u = 0; u < SPW; ++u) {
-    const uint32_t off = row[u] == kNoKeyRow ? kNoKeyOff : row[u] * RB + gq * LB;
+    // the Full scan's byte -> k-slot map (for d = 128 fp8 rows: chunks gq
+    // and 4 + gq of 16 bytes), so both compute the same fp32 scores
+    const uint32_t off = row[u] == kNoKeyRow ? kNoKeyOff : row[u] * RB + gq * (LB == 32 ? 16 : LB);
     const v4u x = buf_load16(rk, off);
     kb[u][0] = x[0]; kb[u][1] = x[1]; kb[u][2] = x[2]; kb[u][3] = x[3];
     if constexpr (F4) {
       ksw[u] = __builtin_amdgcn_raw_buffer_load_b32(
           rks, row[u] == kNoKeyRow ? kNoKeyOff : row[u] * SB + (gq >> 1) * 4, 0, 0);
     } else if constexpr (LB == 32) {
-      const v4u y = buf_load16(rk, off + 16);
+      const v4u y = buf_load16(rk, off + 64);
       kb[u][4] = y[0]; kb[u][5] = y[1]; kb[u][6] = y[2]; kb[u][7] = y[3];
     }
   }
@@ -134,7 +136,8 @@ __device__ __forceinline__ void score_part(const ReindexArgs& a, int q, int part
     } else {
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc) {
-        const v2u x = *reinterpret_cast<const v2u*>(qp + (int64_t)hc * D + gq * LB + kc * 8);
+        const int qb = D == 128 ? (kc >> 1) * 64 + gq * 16 + (kc & 1) * 8 : gq * 16 + kc * 8;
+        const v2u x = *reinterpret_cast<const v2u*>(qp + (int64_t)hc * D + qb);
         qraw[t][kc][0] = x[0];
         qraw[t][kc][1] = x[1];
       }
@@ -177,16 +180,18 @@ __device__ __forceinline__ void score_part(const ReindexArgs& a, int q, int part
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc) kf[kc] = fp8x8_to_v8h(kb[u][2 * kc], kb[u][2 * kc + 1]);
     }
-    float sum = 0.0f;
+    // the Full scan's summation order: four partial sums over the head
+    // tiles, then the lane groups
+    float pp[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int t = 0; t < HT; ++t) {
       v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc) acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(qf[t][kc], kf[kc], acc, 0, 0, 0);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sum += wv[t][i] * fmaxf(acc[i], 0.0f);
+      for (int i = 0; i < 4; ++i) pp[i] += wv[t][i] * fmaxf(acc[i], 0.0f);
     }
-    sum = sum_rows4(sum);
+    const float sum = sum_rows4((pp[0] + pp[1]) + (pp[2] + pp[3]));
     // order-preserving key; 0 marks a slot with no candidate position
     if (gq == 0 && i < i_end) ks[i * kBlock + (col & 7)] = pos[u] < c ? order_key(sum) : 0u;
   }
@@ -318,7 +323,114 @@ hipError_t launch_d(const ReindexArgs& a, hipStream_t s) {
   return launch_db<D, F4, kReindexBlocks>(a, s);
 }
 
+// ---------------------------------------------------------------- Full layer
+// A Full layer's Top-K from the Full scan's own scores ("DeepSeek-V4.1-Flash
+// 梗概" §3.2: the Full layer takes its index set with the query that scored
+// the whole context, so its Top-K inside the pool is Reindex with that same
+// query).  The scan left every candidate position's score (as an order key)
+// and every block's maximum; one workgroup per query then selects, with no
+// key read and no re-scoring:
+//  1. the K best blocks of the pool (by (block score desc, block id asc)).
+//     Every one of the K best positions of the pool lies in them: a block
+//     ranked above the block B of such a position p contributes its maximum
+//     position, which ranks above p, so fewer than K blocks rank above B;
+//  2. the K best positions of those blocks (by (score desc, position asc)),
+//     written in ascending order, as Reindex writes them.
+// Scores and ties are those of k_reindex (same contraction and summation
+// order), so the result is the same set.
+template <int BPT>
+__global__ __launch_bounds__(kTkThreads) void k_topk_keys(TopkKeysArgs a) {
+  constexpr int PB = 2048 / kTkThreads;             // pool slots per thread (P <= 2048)
+  constexpr int PP = BPT * kBlock;                  // position slots per thread
+  __shared__ int32_t s_blk[kTkThreads * BPT];
+  __shared__ uint32_t s_scan[kTkWaves];
+  const int q = blockIdx.x, tid = threadIdx.x;
+  const int P = a.pool, K = a.topk;
+  const int32_t* pool = a.pool_blocks + (int64_t)q * P;
+  const int pcnt = min(load_uniform(a.pool_count + q), P);
+
+  // 1. the pool's block scores (slots past the count: key 0)
+  int32_t blk[PB];
+#pragma unroll
+  for (int k = 0; k < PB; ++k) blk[k] = pool[min(tid * PB + k, P - 1)];
+#pragma unroll
+  for (int k = 0; k < PB; ++k) asm volatile("" : "+v"(blk[k]));
+  const float* bs = a.bscore + (int64_t)q * a.ld;
+  float bv[PB];
+#pragma unroll
+  for (int k = 0; k < PB; ++k) bv[k] = bs[tid * PB + k < pcnt ? max(blk[k], 0) : 0];
+  uint32_t bkey[PB];
+#pragma unroll
+  for (int k = 0; k < PB; ++k) bkey[k] = tid * PB + k < pcnt ? order_key(bv[k]) : 0u;
+  const TopkCut bc = radix_topk<PB>(bkey, K);
+  uint32_t flags = 0;
+#pragma unroll
+  for (int k = 0; k < PB; ++k) flags |= (uint32_t)(bkey[k] >= bc.tt) << k;
+  uint32_t nsel;
+  uint32_t before = block_exclusive_scan<kTkThreads>(__builtin_popcount(flags), s_scan, &nsel);
+#pragma unroll
+  for (int k = 0; k < PB; ++k)
+    if (flags >> k & 1u) s_blk[before++] = blk[k];     // ascending: the pool is ascending
+  __syncthreads();
+
+  // 2. the positions of the selected blocks: thread t takes blocks
+  // [BPT t, BPT (t + 1)) of them, 8 position keys each (0 past c)
+  const uint32_t* pk = a.pkey + (int64_t)q * a.ld_pkey;
+  uint32_t key[PP];
+  int32_t mb[BPT];
+  // (slots past the selection load block 0's keys, a valid row, and clear them)
+#pragma unroll
+  for (int b = 0; b < BPT; ++b) mb[b] = tid * BPT + b < (int)nsel ? s_blk[tid * BPT + b] : 0;
+  v4u x0[BPT], x1[BPT];
+#pragma unroll
+  for (int b = 0; b < BPT; ++b) {
+    x0[b] = *reinterpret_cast<const v4u*>(pk + (int64_t)mb[b] * kBlock);
+    x1[b] = *reinterpret_cast<const v4u*>(pk + (int64_t)mb[b] * kBlock + 4);
+  }
+#pragma unroll
+  for (int b = 0; b < BPT; ++b) {
+    const bool live = tid * BPT + b < (int)nsel;
+    key[8 * b + 0] = live ? x0[b][0] : 0u; key[8 * b + 1] = live ? x0[b][1] : 0u;
+    key[8 * b + 2] = live ? x0[b][2] : 0u; key[8 * b + 3] = live ? x0[b][3] : 0u;
+    key[8 * b + 4] = live ? x1[b][0] : 0u; key[8 * b + 5] = live ? x1[b][1] : 0u;
+    key[8 * b + 6] = live ? x1[b][2] : 0u; key[8 * b + 7] = live ? x1[b][3] : 0u;
+  }
+  const TopkCut cut = radix_topk<PP>(key, K);
+  uint32_t pflags = 0;
+#pragma unroll
+  for (int k = 0; k < PP; ++k) pflags |= (uint32_t)(key[k] >= cut.tt) << k;
+  uint32_t total;
+  uint32_t pos_before = block_exclusive_scan<kTkThreads>(__builtin_popcount(pflags), s_scan, &total);
+  int32_t* out = a.topk_pos + (int64_t)q * K;
+  float* out_s = a.topk_scores ? a.topk_scores + (int64_t)q * K : nullptr;
+#pragma unroll
+  for (int k = 0; k < PP; ++k) {
+    if (pflags >> k & 1u) {
+      if (pos_before < (uint32_t)K) {
+        out[pos_before] = mb[k >> 3] * kBlock + (k & 7);
+        if (out_s) out_s[pos_before] = key_float(key[k]);
+      }
+      ++pos_before;
+    }
+  }
+  for (int t = (int)cut.keff + tid; t < K; t += kTkThreads) {
+    out[t] = -1;
+    if (out_s) out_s[t] = 0.0f;
+  }
+  if (tid == 0) a.topk_count[q] = (int32_t)cut.keff;
+}
+
 }  // namespace
+
+hipError_t launch_topk_keys(const TopkKeysArgs& a, hipStream_t s) {
+  // blocks per thread for the K best blocks: K <= 512 -> 1, <= 1024 -> 2, else 4
+  const dim3 grid((unsigned)a.n_q), block(kTkThreads);
+  if (a.pool > 2048 || a.topk > 2048) return hipErrorInvalidValue;
+  if (a.topk <= kTkThreads) hipLaunchKernelGGL(k_topk_keys<1>, grid, block, 0, s, a);
+  else if (a.topk <= 2 * kTkThreads) hipLaunchKernelGGL(k_topk_keys<2>, grid, block, 0, s, a);
+  else hipLaunchKernelGGL(k_topk_keys<4>, grid, block, 0, s, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_reindex(const ReindexArgs& a, hipStream_t s) {
   if (a.idx_k_scales) {

@@ -67,7 +67,7 @@ constexpr int kMaxTilePos = 4096;
 
 constexpr uint32_t kOob = 0xFFFFFF00u;   // a buffer offset past any row: reads zero
 
-template <int D, int HT, int R, int NW, bool F4, bool PG>
+template <int D, int HT, int R, int NW, bool F4, bool PG, bool PS>
 __global__ __launch_bounds__(64 * NW) void k_scan(ScanArgs a) {
   static_assert(!F4 || D == 128, "FP4 rows are 128 channels wide");
   constexpr int NT = 64 * NW;
@@ -82,6 +82,7 @@ __global__ __launch_bounds__(64 * NW) void k_scan(ScanArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t s_q[64 * D];
   __shared__ __attribute__((aligned(16))) float s_w[64];
   __shared__ int32_t s_pg[PG ? kMaxTilePos / 16 + 1 : 1];   // paged: the tile's page ids
+  __shared__ __attribute__((aligned(16))) uint32_t s_ps[PS ? kMaxTilePos : 4];   // position keys of the tile
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int gq = lane >> 4, col = lane & 15;
 
@@ -250,6 +251,10 @@ __global__ __launch_bounds__(64 * NW) void k_scan(ScanArgs a) {
     // positions >= c (only in a wave's last step) score -inf
     float v = part;
     if (last) v = p0 + col < c ? part : -__builtin_inff();
+    // every lane group holds the same 16 sums: group 0 keeps the position keys
+    // (key 0, which no score has, for positions >= c)
+    if constexpr (PS)
+      if (gq == 0) s_ps[s * 16 + col] = !last || p0 + col < c ? order_key(part) : 0u;
     v = max_lanes8(v);
     if (lane < 16 && (lane & 7) == 0) s_bs[s * 2 + (lane >> 3)] = v;
   };
@@ -364,6 +369,13 @@ __global__ __launch_bounds__(64 * NW) void k_scan(ScanArgs a) {
   stream_done:;
   }
   __syncthreads();
+  if constexpr (PS) {
+    // the tile's position keys, one coalesced store (whole steps: the row
+    // stride covers c rounded up to 32)
+    uint32_t* pk = a.pkey + (int64_t)q * a.ld_pkey + p_begin;
+    for (int i = tid * 4; i < nsteps * 16; i += NT * 4)
+      *reinterpret_cast<v4u*>(pk + i) = *reinterpret_cast<const v4u*>(&s_ps[i]);
+  }
   // block scores of the tile, one coalesced store
   float* bs = a.bscore + (int64_t)q * a.ld + (p_begin >> 3);
   const int nblk = (p_end - p_begin + 7) >> 3;
@@ -397,23 +409,26 @@ __global__ __launch_bounds__(64 * NW) void k_scan(ScanArgs a) {
   }
 }
 
-template <int D, int R, int NW, bool F4, bool PG = false>
+template <int D, int R, int NW, bool F4, bool PG = false, bool PS = false>
 hipError_t launch_drw(const ScanArgs& a, hipStream_t s) {
   const int ht = (a.hi + 15) / 16;
   const int units = ((a.n_q / a.g) * a.tiles + 7) / 8 * 8;
   const dim3 grid((unsigned)(units * a.g)), block(64 * NW);
   switch (ht) {
-    case 1: hipLaunchKernelGGL((k_scan<D, 1, R, NW, F4, PG>), grid, block, 0, s, a); break;
-    case 2: hipLaunchKernelGGL((k_scan<D, 2, R, NW, F4, PG>), grid, block, 0, s, a); break;
-    case 3: hipLaunchKernelGGL((k_scan<D, 3, R, NW, F4, PG>), grid, block, 0, s, a); break;
-    default: hipLaunchKernelGGL((k_scan<D, 4, R, NW, F4, PG>), grid, block, 0, s, a); break;
+    case 1: hipLaunchKernelGGL((k_scan<D, 1, R, NW, F4, PG, PS>), grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((k_scan<D, 2, R, NW, F4, PG, PS>), grid, block, 0, s, a); break;
+    case 3: hipLaunchKernelGGL((k_scan<D, 3, R, NW, F4, PG, PS>), grid, block, 0, s, a); break;
+    default: hipLaunchKernelGGL((k_scan<D, 4, R, NW, F4, PG, PS>), grid, block, 0, s, a); break;
   }
   return hipGetLastError();
 }
 
 template <int D, bool F4>
 hipError_t launch_d(const ScanArgs& a, hipStream_t s) {
-  // paged keys: the default ring and wave count only
+  // position keys, paged keys: the default ring and wave count only
+  if (a.pkey)
+    return a.pages ? launch_drw<D, kScanPrefetch, kScanWaves, F4, true, true>(a, s)
+                   : launch_drw<D, kScanPrefetch, kScanWaves, F4, false, true>(a, s);
   if (a.pages) return launch_drw<D, kScanPrefetch, kScanWaves, F4, true>(a, s);
   // LDS ring slots per wave (steps in flight + 1) and waves per workgroup
   if (a.waves == 8) {
@@ -428,6 +443,7 @@ hipError_t launch_d(const ScanArgs& a, hipStream_t s) {
 
 hipError_t launch_scan(const ScanArgs& a, hipStream_t s) {
   if (a.tiles == 0) return hipSuccess;
+  if (a.pkey && (a.ld_pkey % 32 || ((uintptr_t)a.pkey & 15))) return hipErrorInvalidValue;
   if (a.tile_pos > kMaxTilePos || a.tile_pos % 64) return hipErrorInvalidValue;
   if (a.pages && (a.tile_extra % 16 || a.page_shift < 4 || a.page_shift > 16 || a.rows * (a.d / (a.idx_k_scales ? 2 : 1)) > 0xFFFFFF00LL))
     return hipErrorInvalidValue;

@@ -37,6 +37,12 @@ struct ScanArgs {
   const int32_t* pages;
   int page_shift;
   int64_t rows;
+  // optional (nullptr: not written): every candidate position's score as an
+  // order key, [n_q, ld_pkey] (position p of query q at q * ld_pkey + p; 0
+  // for the positions past c in a query's last step), so that a Full layer's
+  // Top-K can be selected without scoring the pool again
+  uint32_t* pkey;
+  int64_t ld_pkey;
 };
 
 hipError_t launch_scan(const ScanArgs& a, hipStream_t s);

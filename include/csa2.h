@@ -236,6 +236,43 @@ csa2_status csa2_index_scan_fp4(const csa2_dims* dims, const csa2_queries* q,
                                 float* block_scores, int64_t ld_block_scores,
                                 void* pool_ws, size_t pool_ws_bytes, void* stream);
 
+/* csa2_index_scan that also keeps every candidate position's score, for a
+ * Full layer's own Top-K ([atlas] §3.2 mode table: the Full layer takes a new
+ * index set with the query that scored the whole context, so its Top-K in the
+ * pool is Reindex with that same query, whose scores the scan has already
+ * computed).  FP4 indexer rows when idx_q_scales and idx_k_scales are both
+ * given, fp8 when both are NULL; pages NULL for contiguous keys (else as in
+ * csa2_index_scan_paged).  Same block scores and pool-workspace preparation
+ * as csa2_index_scan, plus:
+ *   pos_keys     uint32 [n_q, ld_pos_keys]: position p of query q at
+ *                q * ld_pos_keys + p holds the order key of s_p (a uint32
+ *                that orders like the score, never 0) for p < c, and 0 for
+ *                the positions from c up to c rounded up to 16;
+ *                ld_pos_keys a multiple of 32 >= 8 * ceil((max_visible - W)
+ *                / 8) rounded up to 32; 16-byte aligned.
+ * The scores are bit-identical to csa2_index_reindex's for the same query. */
+csa2_status csa2_index_scan_keys(const csa2_dims* dims, const csa2_queries* q, const csa2_pages* pages,
+                                 const uint8_t* idx_q, const uint8_t* idx_q_scales, const float* idx_w,
+                                 const uint8_t* idx_k, const uint8_t* idx_k_scales,
+                                 float* block_scores, int64_t ld_block_scores,
+                                 uint32_t* pos_keys, int64_t ld_pos_keys,
+                                 void* pool_ws, size_t pool_ws_bytes, void* stream);
+
+/* A Full layer's Top-K from csa2_index_scan_keys's scores: the same output as
+ * csa2_index_reindex called with the scan's indexer query on this pool
+ * ([atlas] §3.2), without reading a key.  One kernel, one workgroup per
+ * query: the K best pool blocks by (block score desc, block id asc), which
+ * hold every one of the K best pool positions (a block ranked above such a
+ * position's block brings its own maximum position, ranked above it), then
+ * the K best of their positions by (score desc, position asc), ascending.
+ *   pool_blocks, pool_count  as written by csa2_index_pool on those scores
+ *   block_scores, pos_keys   as written by csa2_index_scan_keys
+ *   topk_pos, topk_count, topk_scores  as in csa2_index_reindex. */
+csa2_status csa2_index_topk_keys(const csa2_dims* dims, const csa2_queries* q, const int32_t* pool_blocks,
+                                 const int32_t* pool_count, const float* block_scores, int64_t ld_block_scores,
+                                 const uint32_t* pos_keys, int64_t ld_pos_keys,
+                                 int32_t* topk_pos, int32_t* topk_count, float* topk_scores, void* stream);
+
 /* csa2_index_pool flag: the workspace was passed to the csa2_index_scan call
  * that wrote these block scores, and since then it was used only by
  * csa2_index_pool calls on the same block scores. */
@@ -422,17 +459,18 @@ csa2_status csa2_page_rows(const csa2_pages* pages, int64_t n, const int64_t* ta
  * re-scores the inherited pool with its own indexer query, a Reuse layer
  * only attends over the inherited index set with its own main Q).  The call
  * checks every stage's arguments, then enqueues, on `stream`:
- *   CSA2_LAYER_FULL     csa2_index_full (pool_blocks, pool_count written),
- *                       csa2_index_reindex with the same indexer query
- *                       (topk_pos, topk_count written), csa2_attend;
+ *   CSA2_LAYER_FULL     csa2_index_scan_keys + csa2_index_pool
+ *                       (pool_blocks, pool_count written), then
+ *                       csa2_index_topk_keys (topk_pos, topk_count written:
+ *                       the same set as csa2_index_reindex with the same
+ *                       indexer query), csa2_attend;
  *   CSA2_LAYER_REINDEX  csa2_index_reindex on the given pool, csa2_attend;
  *   CSA2_LAYER_REUSE    csa2_attend on the given topk_pos / topk_count
  *                       (the idx_* arguments may be NULL).
  * The indexer rows are fp8 when idx_q_scales and idx_k_scales are NULL and
  * FP4 (as the *_fp4 calls) when both are given.  Every other argument is as
- * in the stage calls.  No kernel is fused: the chain is the stages' own
- * launches (5 kernels for a Full layer at batch 8), which a caller can also
- * capture into a HIP graph (no memset or allocation is enqueued).
+ * in the stage calls.  The chain is the stages' own launches, which a caller
+ * can also capture into a HIP graph (no memset or allocation is enqueued).
  *   ws, ws_bytes  csa2_decode_step_workspace_size bytes, 256-byte aligned,
  *               zero-filled before its first use (it holds the Reindex
  *               completion counters, which every call leaves at zero);

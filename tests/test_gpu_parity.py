@@ -257,6 +257,40 @@ def test_attention_on_oracle_topk(case):
         check_attention(out[qi], lse[qi], refs[qi][0], refs[qi][1], f"{name} q{qi}")
 
 
+def test_full_topk_from_scan_keys_matches_reindex(case):
+    """A Full layer's Top-K selected from the scan's own position scores
+    (csa2_index_scan_keys + csa2_index_topk_keys) is csa2_index_reindex with
+    the same query, bit for bit: the same positions, counts and scores; and
+    the scan's block scores are unchanged by keeping the position scores."""
+    name, g, lay = case
+    csa2, w = g.csa2, g.w
+    q, wt = g.iq(0)
+    idx_k = g.planes[0][0]
+    ld = csa2.block_scores_ld(g.dims, g.batch)
+    bs = torch.full((w.n_q, ld), float("nan"), dtype=torch.float32, device="cuda")
+    pk = torch.full((w.n_q, csa2.pos_keys_ld(g.dims, g.batch)), -1, dtype=torch.int32, device="cuda")
+    pws = torch.empty(csa2.workspace_pool(g.dims, g.batch) + 256, dtype=torch.uint8, device="cuda")
+    csa2.index_scan(g.dims, g.batch, q, wt, idx_k, bs, pool_ws=pws, pos_keys=pk)
+    pool, cnt = csa2.index_pool(g.dims, g.batch, bs, ws=pws, from_scan=True)
+    ts = torch.empty(w.n_q, w.dims.topk, dtype=torch.float32, device="cuda")
+    tk, tc = csa2.index_topk_keys(g.dims, g.batch, pool, cnt, bs, pk, topk_scores=ts)
+    ts2 = torch.empty_like(ts)
+    tk2, tc2 = csa2.index_reindex(g.dims, g.batch, q, wt, idx_k, pool, cnt, topk_scores=ts2)
+    bs2 = torch.full_like(bs, float("nan"))
+    csa2.index_scan(g.dims, g.batch, q, wt, idx_k, bs2)
+    torch.cuda.synchronize()
+    assert torch.equal(tc, tc2), f"{name}: Top-K counts differ from Reindex"
+    for qi in range(w.n_q):
+        k = int(tc[qi])
+        assert torch.equal(tk[qi, :k], tk2[qi, :k]), f"{name} q{qi}: Top-K differs from Reindex"
+        assert torch.equal(ts[qi, :k].view(torch.int32), ts2[qi, :k].view(torch.int32)), \
+            f"{name} q{qi}: Top-K scores differ from Reindex"
+        assert bool((tk[qi, k:] == -1).all())
+        nb = -(-max(0, lay.q_visible[qi] - w.dims.swa) // 8)
+        assert torch.equal(bs[qi, :nb].view(torch.int32), bs2[qi, :nb].view(torch.int32)), \
+            f"{name} q{qi}: block scores differ with position keys kept"
+
+
 def test_pipeline_end_to_end_and_deterministic(case):
     name, g, lay = case
     w = g.w

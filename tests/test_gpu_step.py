@@ -125,10 +125,13 @@ def test_step_modes_match_stage_calls(name):
     for qi in range(n_q):
         ro, rl = oqs[qi].attention(2, keep1[qi])
         check_attention(bufs["out"][qi].cpu().numpy(), bufs["lse"][qi].cpu().numpy(), ro, rl, f"{name} q{qi} reuse")
-    # the step leaves the Reindex counters (after the Full index's part of
-    # the workspace) at zero for the next call
-    off = (-ws.data_ptr()) % 256 + csa2.workspace_full(g.dims, g.batch)
-    assert int(ws[off:off + 4 * n_q].count_nonzero()) == 0, f"{name}: Reindex counters not left at zero"
+    # the step leaves the Reindex completion counters in its workspace at
+    # zero: a second Reindex layer on the same workspace selects the same set
+    # (with a counter left nonzero no workgroup would see itself last)
+    _step(g, csa2.LAYER_REINDEX, 1, bufs, ws)
+    torch.cuda.synchronize()
+    _same(bufs["topk_pos"], tk1, f"{name} reindex again topk")
+    _same(bufs["topk_count"], tc1, f"{name} reindex again count")
 
 
 @pytest.mark.parametrize("name", ["ragged_b3", "fp4_ragged_b3"])
