@@ -197,7 +197,7 @@ class Step:
         self.lse = torch.empty(len(self.layers), n_q, w.dims.n_heads, dtype=torch.float32, device=dev)
         self.ws_p = torch.empty(csa2.workspace_pool(st.dims, st.batch) + 256, dtype=torch.uint8, device=dev)
         self.ws_r = torch.zeros(csa2.workspace_reindex(st.dims, st.batch) + 256, dtype=torch.uint8, device=dev)
-        self.ws_a = torch.empty(csa2.workspace_attend(st.dims, st.batch) + 256, dtype=torch.uint8, device=dev)
+        self.ws_a = torch.zeros(csa2.workspace_attend(st.dims, st.batch) + 256, dtype=torch.uint8, device=dev)
         # a Full layer's Top-K comes from the scan's own scores (same query):
         # the scan keeps every position's score as an order key
         self.full_topk = not w.fresh_q_per_layer

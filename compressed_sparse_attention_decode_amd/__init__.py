@@ -268,7 +268,7 @@ def _workspace(nbytes: int, device, ws: Optional[torch.Tensor]) -> Optional[torc
     if nbytes == 0:
         return ws
     if ws is None or ws.numel() * ws.element_size() < nbytes:
-        # zero-filled: the Reindex workspace starts with counters that must
+        # zero-filled: the Reindex and attention workspaces start with counters that must
         # read zero on first use (each call leaves them so)
         ws = torch.zeros(nbytes + 256, dtype=torch.uint8, device=device)
     return ws

@@ -229,34 +229,36 @@ int pool_mark_wgs(const csa2_queries* q, int chunks) {
   return wpq < chunks ? wpq : chunks;
 }
 
-struct AttendPlan { int hg, splits, split_entries; };
+struct AttendPlan { int hg, splits, split_tiles; };
 
-// A small batch is spread over more workgroups by splitting each query's
-// entry list (each split costs one fp32 partial output, H x 512, merged by a
-// second kernel); a split keeps at least two tiles so that the gather of one
-// tile overlaps the contraction of the other.
+// Workgroups of 32 heads; a query's tiles (the window's, then the kept
+// entries', 64 each) are split so that the grid holds about one workgroup
+// per CU of the 256-CU part (one tile per split when a batch has few
+// queries); a second kernel merges the splits' partials.  The plan depends
+// only on the sizes, so the workspace size does too.  CSA2_ATTEND_SPLITS
+// overrides (1..16).
 AttendPlan attend_plan(const csa2_dims* d, const csa2_queries* q) {
   AttendPlan p;
-  p.hg = (d->n_heads + 16 * kAttendWaves - 1) / (16 * kAttendWaves);
-  const int emax = d->topk + d->swa;
-  const int tiles = (emax + kAttendTile - 1) / kAttendTile;
-  int want = (256 + q->n_q * p.hg - 1) / (q->n_q * p.hg);
-  int cap = tiles / 2;
-  if (const char* env = getenv("CSA2_ATTEND_SPLITS")) { want = atoi(env); cap = tiles; }
-  if (cap > kAttendMaxSplits) cap = kAttendMaxSplits;
-  if (cap < 1) cap = 1;
-  const int s = want < 1 ? 1 : (want > cap ? cap : want);
-  const int tps = (tiles + s - 1) / s;
-  p.split_entries = tps * kAttendTile;
-  p.splits = (emax + p.split_entries - 1) / p.split_entries;
-  if (p.splits < 1) p.splits = 1;
+  p.hg = (d->n_heads + kAttendHeads - 1) / kAttendHeads;
+  const int tiles = (d->swa + kAttendTile - 1) / kAttendTile + (d->topk + kAttendTile - 1) / kAttendTile;
+  const int64_t units = (int64_t)q->n_q * p.hg;
+  int s = (int)((256 + units - 1) / units);
+  if (const char* env = getenv("CSA2_ATTEND_SPLITS")) s = atoi(env);
+  const int cap = tiles < kAttendMaxSplits ? tiles : kAttendMaxSplits;
+  s = s < 1 ? 1 : (s > cap ? cap : s);
+  p.split_tiles = (tiles + s - 1) / s;
+  // a split holds at most kAttendMaxTiles tiles (every query's whole list
+  // fits: 1024 / 64 + 2048 / 64 = 48)
+  if (p.split_tiles > kAttendMaxTiles) p.split_tiles = kAttendMaxTiles;
+  p.splits = (tiles + p.split_tiles - 1) / p.split_tiles;
   return p;
 }
 
+// Attention workspace (splits > 1): the splits' partials
 size_t attend_ws(const csa2_dims* d, const csa2_queries* q) {
   const AttendPlan p = attend_plan(d, q);
   if (p.splits == 1) return 0;
-  const size_t rows = (size_t)q->n_q * p.splits * ((d->n_heads + 15) / 16 * 16);   // heads padded to 16
+  const size_t rows = (size_t)q->n_q * p.splits * p.hg * kAttendHeads;
   return align256(rows * 512 * 4) + align256(rows * 2 * 4);
 }
 
@@ -712,18 +714,16 @@ static csa2_status attend(const csa2_dims* d, const csa2_queries* q, const uint1
   aa.topk_pos = topk_pos; aa.topk_count = topk_count; aa.swa_kv = swa_kv; aa.swa_base = swa_base;
   aa.seq_base = q->seq_base; aa.n_visible = q->n_visible;
   aa.n_q = q->n_q; aa.heads = d->n_heads; aa.topk = d->topk; aa.swa = d->swa;
-  aa.head_groups = p.hg; aa.splits = p.splits; aa.split_entries = p.split_entries;
+  aa.head_groups = p.hg; aa.splits = p.splits; aa.split_tiles = p.split_tiles;
   aa.out = out; aa.lse = lse;
   aa.pages = pages ? pages->table : nullptr;
   aa.page_shift = pages ? page_shift(pages) : 0;
   aa.rows = pages ? pages->rows : 0;
+  aa.part_o = nullptr; aa.part_ml = nullptr;
   if (p.splits > 1) {
-    const size_t rows = (size_t)q->n_q * p.splits * ((d->n_heads + 15) / 16 * 16);
+    const size_t rows = (size_t)q->n_q * p.splits * p.hg * kAttendHeads;
     aa.part_o = (float*)ws;
     aa.part_ml = (float*)((char*)ws + align256(rows * 512 * 4));
-  } else {
-    aa.part_o = nullptr;
-    aa.part_ml = nullptr;
   }
   hipError_t e = launch_attend(aa, (hipStream_t)stream);
   return e == hipSuccess ? CSA2_OK : hip_fail(e, "attend launch");

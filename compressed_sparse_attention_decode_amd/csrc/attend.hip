@@ -8,44 +8,88 @@
 // of a sparse entry is [dequantised latent (512) || bf16 rope (64)] and its
 // value is the dequantised latent; a window row supplies both from bf16.
 // The FP4 scales cover 16 channels, or 32 in the group-32 codec variant (the
-// akhunji.com page, "Microscopic FP4 (E2M1) Cache Compression"): a gathered
-// 16-channel item then reads the scale byte of its 32-channel group.
+// akhunji.com page, "Microscopic FP4 (E2M1) Cache Compression"): a 16-channel
+// item then reads the scale byte of its 32-channel group.
 //
-// Mapping (gfx950): a workgroup = 4 waves = one query x up to 64 heads (one
-// wave per 16 heads; waves past the last head only help gather) x one split
-// of the entry list.  Entries stream in tiles of 32:
-//  * the split's cache rows are resolved into LDS once; each tile's raw
-//    bytes (FP4 codes + E4M3 scale, or bf16 window values, and the rope) are
-//    loaded into registers one tile ahead, so the gather of tile t+1 is in
-//    flight while tile t is contracted;
-//  * the raw tile is dequantised into one row-major f16 image in LDS (FP4 x
-//    E4M3 values are exact in f16; bf16 window / rope / query values are exact
-//    in f16 inside its normal range, the reason for the |x| < 65504 bound);
-//  * Q.K^T: v_mfma_f32_16x16x32_f16 with the tile as A (rows = entries) and
-//    the wave's 16 query heads as B (held in registers), giving S^T whose lane
-//    layout is exactly the A layout P.V needs, so P never leaves registers;
-//  * online softmax in the exp2 domain, P rounded to f16 (bf16 would cost
-//    about 2^-9 relative per weight); P.V with v_mfma_f32_16x16x32_f16 whose
-//    value operand is read from the same row-major image with the gfx950 LDS
-//    transpose read (ds_read_b64_tr_b16), into 32 accumulator tiles
-//    (16 heads x 512 dims);
-//  * with several splits per query, unnormalised partials (o, m, l) are
-//    merged by k_attend_combine with a log-sum-exp rescale.
+// Mapping (gfx950): a workgroup = 8 waves = one query x 32 heads x one split
+// of the query's tile list.  Waves 0-3 serve heads 0-15 of the 32, waves 4-7
+// heads 16-31; within a group, wave w (quarter w & 3) takes entries
+// 16w .. 16w+15 of each tile in Q.K^T and output dims 128w .. 128w+127 in
+// P.V, so the 64-entry tile image and the query are read once per head group
+// instead of once per wave.  The window's positions [c, n) come first (tiles
+// of 64 window rows, known before any index arrives), then the kept entries
+// (tiles of 64 of topk_pos); a tile never mixes the two.
+//  * gathers go straight from HBM into LDS (buffer loads with the LDS
+//    destination, 16 bytes per lane), with the wait counts kept by hand: a
+//    kept-entry tile's codes, scales and rope are loaded two tiles ahead into
+//    one of two staging slots, so two tiles' gathers are in flight while one
+//    is contracted; a window tile's rows land directly in the image (its
+//    rope in a staging slot), the first one before the loop;
+//  * the image is f16 (FP4 x E4M3 values are exact in f16, bf16 window values
+//    are exact inside the f16 normal range, the reason for |x| < 65504):
+//    kept entries are dequantised from their staging slot, window rows are
+//    converted in place;
+//  * Q.K^T: v_mfma_f32_16x16x32_f16 over the 512 latent dims with 16 entries
+//    of the image as A and the wave's 16 query heads as B (held in
+//    registers), and v_mfma_f32_16x16x32_bf16 over the 64 rope dims straight
+//    from the staged bf16 rope (the query's rope stays bf16: exact);
+//  * online softmax in the exp2 domain: the tile maximum per head is shared
+//    through LDS by the group's four waves, P is rounded to f16 (bf16 would
+//    cost about 2^-9 relative per weight) and written to LDS as [head][entry];
+//  * P.V: v_mfma_f32_16x16x32_f16 with P from LDS as A and the image's values
+//    read with the gfx950 transpose read (ds_read_b64_tr_b16) as B, into 8
+//    accumulator tiles (16 heads x 128 dims) per wave;
+//  * the result goes through LDS so that every output row (512 floats of one
+//    head) is written with whole 16-byte stores;
+//  * with several splits per (query, head group), each split writes its
+//    unnormalised partial (o, m, l) per head and k_attend_combine merges them
+//    with a log-sum-exp rescale.  The splits are sized so that the grid fills
+//    the chip about once: for a decode batch of a few queries each split is
+//    one tile, so a query's work is spread over tens of CUs.
 #include "common.h"
 #include "internal.h"
 
 namespace csa2 {
 namespace {
 
-constexpr int kTile = kAttendTile;        // 32 entries
-constexpr int kNW = kAttendWaves;         // waves per workgroup, 16 heads each
-constexpr int kNT = 64 * kNW;
-constexpr int kKS = kKeyDim + 8;          // f16 row stride of the tile image
-constexpr int kMaxSplit = 2048 + 1024;    // entries of one split (topk + swa bounds)
-constexpr int kRowPer = (kMaxSplit + kNT - 1) / kNT;   // kept positions per thread
+constexpr int kTE = kAttendTile;              // 64 entries per tile
+constexpr int kNW = kAttendWaves;             // 8 waves
+constexpr int kNT = 64 * kNW;                 // 512 threads
+constexpr int kLS = kLatent + 8;              // f16 row stride of the latent image
+constexpr int kPS = kTE + 4;                  // f16 row stride of the P tile (rows on distinct banks)
+constexpr int kOS = kLatent + 16;             // f32 row stride of the output rows in LDS
+constexpr int kMaxRows = kAttendMaxTiles * kTE;          // rows of one split, at most
+constexpr int kRowPer = kMaxRows / kNT;                  // rows resolved per thread
+constexpr int kItems = kTE * 32 / kNT;        // (entry, 16-channel group) items per thread
+constexpr int kWinRow = kKeyDim * 2;          // bytes of a window row
+constexpr uint32_t kOob = 0xFFFFFF00u;        // a buffer offset past any row: reads zero
+constexpr int32_t kNoRow = 0x7FFFFFFF;
+
+// LDS layout (bytes): the latent image, two rope slots, two staging slots
+// (codes, then the tile's scale block), the split's row codes, P, and the
+// per-head maxima, rescales and sums.  At the end the output rows reuse the
+// image and rope slots.
+constexpr int kOffLat = 0;
+constexpr int kOffRope = kOffLat + kTE * kLS * 2;
+constexpr int kRopeSlot = kTE * kRope * 2;
+constexpr int kOffStage = kOffRope + 2 * kRopeSlot;
+constexpr int kCodeStage = kTE * kCodeBytes;
+constexpr int kStageSlot = kCodeStage + kNW * 256;
+constexpr int kOffRow = kOffStage + 2 * kStageSlot;
+constexpr int kOffP = kOffRow + kMaxRows * 4;
+constexpr int kOffMx = kOffP + 2 * 16 * kPS * 2;
+constexpr int kOffAl = kOffMx + 2 * 4 * 16 * 4;
+constexpr int kOffLw = kOffAl + 2 * 16 * 4;
+constexpr int kLdsBytes = kOffLw + 2 * 4 * 16 * 4;
+static_assert(kTE * 8 == kNT, "one rope chunk per thread");
+static_assert(kTE * kScaleBytes <= kNW * 256, "a tile's scale block: one 256-byte load per wave");
+static_assert(kAttendHeads * kOS * 4 <= kOffStage, "output rows fit in the image and rope slots");
+static_assert(kLdsBytes <= 160 * 1024, "LDS per workgroup");
 
 typedef short v4s __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4s lds_v4s;
+typedef __attribute__((address_space(3))) void lds_void;
+typedef _Float16 v4h_t __attribute__((ext_vector_type(4)));
 
 // bf16 pair -> f16 pair.  Exact for values inside the f16 range (the ABI's
 // |x| < 65504 precondition); round-toward-zero only matters outside it.
@@ -63,191 +107,108 @@ __device__ __forceinline__ uint32_t fp4_byte_h2(uint32_t word, v2h s2) {
   return __builtin_bit_cast(uint32_t, x * s2);
 }
 
-constexpr int kItems = kTile * 32 / kNT;      // (entry, 16-channel group) items per thread
-constexpr int kRopeItems = kTile * 8 / kNT;   // (entry, 8-channel rope chunk) items per thread
+__device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)(lds_void*)p; }
 
-// One tile's raw bytes held by a thread, loaded a tile ahead: an item keeps
-// its 8 code bytes in c.xy and the aligned word holding its scale byte in
-// c.z; a rope chunk comes from the cache (r) or a window row (rw), the other
-// reading zeros.  Window items' latent values (at most W rows per query,
-// bf16) are read when the tile is stored.
-struct RawTile {
-  v4u c[kItems];
-  v4u r[kRopeItems];
-  v4u rw[kRopeItems];
-};
-
-// The query's sources as buffer resources over exactly its rows, so that a
-// load at offset kOob returns zeros: every load below is issued for every
-// item, masked by its offset instead of a branch (a load inside a divergent
-// branch waits for itself, and for everything issued before it), and no
-// loaded value is touched before the tile is stored.
-constexpr uint32_t kOob = 0xFFFFFF00u;
-struct TileSrc {
-  __amdgpu_buffer_rsrc_t codes, scales, rope, win;
-  uint32_t sbytes;           // scale bytes per entry (32, or 16 with 32-channel groups)
-  int gshift;                // 16-channel item -> its scale byte: item >> gshift
-};
-
-__device__ __forceinline__ TileSrc tile_src(const AttendArgs& a, int64_t seq_base, int64_t swa_base, int n, int w) {
-  TileSrc s;
-  s.codes = make_rsrc(a.kv_codes + seq_base * kCodeBytes, (uint32_t)n * kCodeBytes);
-  s.gshift = a.kv_gshift;
-  s.sbytes = (uint32_t)kScaleBytes >> a.kv_gshift;
-  s.scales = make_rsrc(a.kv_scales + seq_base * s.sbytes, (uint32_t)n * s.sbytes);
-  s.rope = make_rsrc(a.kv_rope + seq_base * kRope, (uint32_t)n * kRope * 2);
-  s.win = make_rsrc(a.swa_kv + swa_base * kKeyDim, (uint32_t)w * kKeyDim * 2);
-  return s;
+// Buffer resource (as four SGPRs) over [base, base + bytes): loads past the
+// end return zeros.
+__device__ __forceinline__ v4u rsrc_of(const void* base, uint32_t bytes) {
+  const uint64_t b = (uint64_t)(uintptr_t)base;
+  return v4u{(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b),
+             (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32)) & 0xFFFFu,
+             (uint32_t)__builtin_amdgcn_readfirstlane((int)bytes), 0x00020000u};
 }
 
-// The row ids of a thread's items in a tile of ne entries: rows[e] >= 0
-// is a sparse entry at position rows[e] (cache row seq_base + pos), rows[e]
-// < 0 the window row swa_base + (-1 - rows[e]); entries e >= ne read as
-// kNoRow.  All LDS reads first, then the selects.
-constexpr int32_t kNoRow = 0x7FFFFFFF;
-struct TileRows {
-  int32_t it[kItems];
-  int32_t rp[kRopeItems];
-};
-
-__device__ __forceinline__ TileRows tile_rows(const int32_t* rows, int ne, int tid) {
-  TileRows t;
-#pragma unroll
-  for (int k = 0; k < kItems; ++k) t.it[k] = rows[max(0, min((tid + k * kNT) >> 5, ne - 1))];
-#pragma unroll
-  for (int k = 0; k < kRopeItems; ++k) t.rp[k] = rows[max(0, min((tid + k * kNT) >> 3, ne - 1))];
-#pragma unroll
-  for (int k = 0; k < kItems; ++k) asm volatile("" : "+v"(t.it[k]));
-#pragma unroll
-  for (int k = 0; k < kRopeItems; ++k) asm volatile("" : "+v"(t.rp[k]));
-#pragma unroll
-  for (int k = 0; k < kItems; ++k) t.it[k] = ((tid + k * kNT) >> 5) < ne ? t.it[k] : kNoRow;
-#pragma unroll
-  for (int k = 0; k < kRopeItems; ++k) t.rp[k] = ((tid + k * kNT) >> 3) < ne ? t.rp[k] : kNoRow;
-  return t;
+// Buffer loads with the LDS as destination: lane l's 16 (or 4) bytes land at
+// the wave-uniform LDS address `lds` + 16 l (+ 4 l).  They count in vmcnt like
+// any load; the compiler does not see them, so every wait for them is written
+// out (wait_vmcnt below).
+__device__ __forceinline__ void dma16(uint32_t lds, uint32_t off, v4u rsrc) {
+  const uint32_t m0 = (uint32_t)__builtin_amdgcn_readfirstlane((int)lds);
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :: "s"(m0), "v"(off), "s"(rsrc) : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(uint32_t lds, uint32_t off, v4u rsrc) {
+  const uint32_t m0 = (uint32_t)__builtin_amdgcn_readfirstlane((int)lds);
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+               :: "s"(m0), "v"(off), "s"(rsrc) : "memory", "m0");
 }
 
-__device__ __forceinline__ void load_tile(const TileSrc& src, const int32_t* rows, int ne, int tid, RawTile& t) {
-  const TileRows tr = tile_rows(rows, ne, tid);
-#pragma unroll
-  for (int k = 0; k < kItems; ++k) {
-    const int grp = (tid + k * kNT) & 31;
-    const int32_t r = tr.it[k];
-    const bool sp = r >= 0 && r != kNoRow;
-    const v2u cw = __builtin_amdgcn_raw_buffer_load_b64(src.codes, sp ? (uint32_t)r * kCodeBytes + grp * 8 : kOob, 0, 0);
-    const uint32_t sw = __builtin_amdgcn_raw_buffer_load_b32(
-        src.scales, sp ? ((uint32_t)r * src.sbytes + (grp >> src.gshift)) & ~3u : kOob, 0, 0);
-    t.c[k] = v4u{cw[0], cw[1], sw, 0u};
-  }
-#pragma unroll
-  for (int k = 0; k < kRopeItems; ++k) {
-    const int ch = (tid + k * kNT) & 7;
-    const int32_t r = tr.rp[k];
-    const uint32_t osp = r >= 0 && r != kNoRow ? (uint32_t)r * (kRope * 2) + ch * 16 : kOob;
-    const uint32_t ow = r < 0 ? (uint32_t)(-1 - r) * (kKeyDim * 2) + kLatent * 2 + ch * 16 : kOob;
-    t.r[k] = buf_load16(src.rope, osp);
-    t.rw[k] = buf_load16(src.win, ow);
-  }
+// s_waitcnt vmcnt(N) (gfx9 layout: vmcnt[3:0] and [15:14], expcnt[6:4],
+// lgkmcnt[11:8]; the fields not named are left at "no wait").  Loads retire
+// in order, so vmcnt(N) means: all but the N youngest loads have landed.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+// The loads issued ahead for one tile, per wave: a kept-entry tile 4 (two
+// code loads, one scale load, one rope load), a window tile 1 (its rope).
+constexpr int kAheadSparse = 4;
+constexpr int kAheadWindow = 1;
+__device__ __forceinline__ void wait_ahead(int n) {
+  if (n == kAheadSparse) wait_vmcnt<kAheadSparse>();
+  else if (n == kAheadWindow) wait_vmcnt<kAheadWindow>();
+  else wait_vmcnt<0>();
 }
 
-// Dequantise a tile into the f16 image (rows past the tile's end are 0).  The
-// window rows' bf16 values are loaded here, all items at once.
-__device__ __forceinline__ void store_tile(const TileSrc& src, const int32_t* rows, int ne, bool has_win,
-                                           const RawTile& t, int tid, _Float16* s_k) {
-  const TileRows tr = tile_rows(rows, ne, tid);
-  v4u w0[kItems], w1[kItems];
-  if (has_win) {
-    // a tile that reaches into the window (uniform): every item's window
-    // load is issued before the first is used
-#pragma unroll
-    for (int k = 0; k < kItems; ++k) {
-      const int grp = (tid + k * kNT) & 31;
-      const uint32_t ow = tr.it[k] < 0 ? (uint32_t)(-1 - tr.it[k]) * (kKeyDim * 2) + grp * 32 : kOob;
-      w0[k] = buf_load16(src.win, ow);
-      w1[k] = buf_load16(src.win, ow + 16);
-    }
-#pragma unroll
-    for (int k = 0; k < kItems; ++k) asm volatile("" : "+v"(w0[k]), "+v"(w1[k]));
-  } else {
-#pragma unroll
-    for (int k = 0; k < kItems; ++k) { w0[k] = v4u{0u, 0u, 0u, 0u}; w1[k] = w0[k]; }
-  }
-#pragma unroll
-  for (int k = 0; k < kItems; ++k) {
-    const int it = tid + k * kNT, e = it >> 5, grp = it & 31;
-    v4u h0, h1;
-    if (tr.it[k] < 0) {
-      h0 = v4u{bf16x2_to_h2(w0[k][0]), bf16x2_to_h2(w0[k][1]), bf16x2_to_h2(w0[k][2]), bf16x2_to_h2(w0[k][3])};
-      h1 = v4u{bf16x2_to_h2(w1[k][0]), bf16x2_to_h2(w1[k][1]), bf16x2_to_h2(w1[k][2]), bf16x2_to_h2(w1[k][3])};
-    } else {
-      const _Float16 sh = (_Float16)e4m3_to_float((t.c[k][2] >> (8 * ((grp >> src.gshift) & 3))) & 0xFFu);  // exact
-      const v2h s2 = {sh, sh};
-      const uint32_t c0 = t.c[k][0], c1 = t.c[k][1];
-      h0 = v4u{fp4_byte_h2<0>(c0, s2), fp4_byte_h2<1>(c0, s2), fp4_byte_h2<2>(c0, s2), fp4_byte_h2<3>(c0, s2)};
-      h1 = v4u{fp4_byte_h2<0>(c1, s2), fp4_byte_h2<1>(c1, s2), fp4_byte_h2<2>(c1, s2), fp4_byte_h2<3>(c1, s2)};
-    }
-    v4u* dk = reinterpret_cast<v4u*>(s_k + e * kKS + grp * 16);
-    dk[0] = h0;
-    dk[1] = h1;
-  }
-#pragma unroll
-  for (int k = 0; k < kRopeItems; ++k) {
-    const int it = tid + k * kNT, e = it >> 3, ch = it & 7;
-    const v4u r = t.r[k] | t.rw[k];
-    *reinterpret_cast<v4u*>(s_k + e * kKS + kLatent + ch * 8) =
-        v4u{bf16x2_to_h2(r[0]), bf16x2_to_h2(r[1]), bf16x2_to_h2(r[2]), bf16x2_to_h2(r[3])};
-  }
+// Maximum over the four 16-lane rows of a wave (lanes l, l^16, l^32, l^48).
+__device__ __forceinline__ float max_rows4(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
 __global__ __launch_bounds__(kNT) void k_attend(AttendArgs a) {
-  __shared__ __attribute__((aligned(16))) _Float16 s_k[kTile * kKS];
-  __shared__ __attribute__((aligned(16))) _Float16 s_q[kNW * 16 * kKS];   // per wave: 16 heads x 576
-  __shared__ int32_t s_row[kMaxSplit];
+  __shared__ __attribute__((aligned(16))) unsigned char s_mem[kLdsBytes];
+  _Float16* s_lat = reinterpret_cast<_Float16*>(s_mem + kOffLat);   // [64][kLS]
+  int32_t* s_row = reinterpret_cast<int32_t*>(s_mem + kOffRow);     // [kMaxRows]
+  _Float16* s_p = reinterpret_cast<_Float16*>(s_mem + kOffP);       // [2 groups][16 heads * kPS]
+  float* s_mx = reinterpret_cast<float*>(s_mem + kOffMx);           // [2][4 quarters][16]: tile maximum per head
+  float* s_al = reinterpret_cast<float*>(s_mem + kOffAl);           // [2][16]: this tile's rescale per head
+  float* s_lw = reinterpret_cast<float*>(s_mem + kOffLw);           // [2][4][16]: row sums per head
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int gq = lane >> 4, col = lane & 15;
+  const int hgl = wave >> 2, qw = wave & 3;       // head group (of 16) in the workgroup, quarter
   const int S = a.splits, HG = a.head_groups;
   const int q = blockIdx.x / (HG * S);
   const int hg = (blockIdx.x / S) % HG;
   const int sp = blockIdx.x % S;
-  const int H = a.heads;
-  const int head0 = (hg * kNW + wave) * 16;
-  const bool active = head0 < H;           // wave-uniform
+  const int H = a.heads, K = a.topk;
+  const int head0 = hg * kAttendHeads + hgl * 16;  // the wave's 16 heads: head0 .. head0 + 15
+  const int nwt = (a.swa + kTE - 1) / kTE;        // window tiles (of the plan: W rows)
+  const int t_begin = sp * a.split_tiles;
+  const int t_end = min(nwt + (K + kTE - 1) / kTE, t_begin + a.split_tiles);
+  const int ntl = max(0, t_end - t_begin);
 
-  const int e_begin = sp * a.split_entries;
-  const int32_t* tk = a.topk_pos + (int64_t)q * a.topk;
+  // the split's kept positions (the row always holds K entries), then the
+  // wave's 16 query heads: both in flight together
+  const int32_t* tk = a.topk_pos + (int64_t)q * K;
   int32_t tkv[kRowPer];
-  {
-    const int e_lim = min(a.topk, e_begin + a.split_entries);
 #pragma unroll
-    for (int j = 0; j < kRowPer; ++j) {
-      const int e = e_begin + tid + j * kNT;
-      const int32_t v = tk[min(e, a.topk - 1)];      // the row always holds topk entries
-      tkv[j] = e < e_lim ? v : 0;
-    }
+  for (int j = 0; j < kRowPer; ++j) {
+    const int idx = tid + j * kNT;
+    const int jj = (t_begin + idx / kTE - nwt) * kTE + idx % kTE;   // index in topk_pos (sparse tiles)
+    tkv[j] = tk[min(max(jj, 0), K - 1)];
   }
-  // the wave's 16 query heads as f16 rows [head][576] (the B operand of
-  // Q.K^T): all 18 loads per lane issued before the first use
-  constexpr int kQv = 16 * (kKeyDim / 8) / 64;
-  v4u rq[kQv];
-  if (active) {
+  // lane (col, gq) holds head head0 + col, dims 32 ks + 8 gq .. + 8
+  v4u rq[kKeyDim / 32];
+  {
+    const int64_t qh = (int64_t)q * H + min(head0 + col, H - 1);
 #pragma unroll
-    for (int j = 0; j < kQv; ++j) {
-      const int i = lane + 64 * j, hh = i / (kKeyDim / 8), d = (i % (kKeyDim / 8)) * 8;
-      // heads past H (H a multiple of 8, not 16) read as zero rows
-      const int64_t qh = (int64_t)q * H + min(head0 + hh, H - 1);
-      const uint16_t* src = d < kLatent ? a.q_lat + qh * kLatent + d : a.q_rope + qh * kRope + (d - kLatent);
-      rq[j] = *reinterpret_cast<const v4u*>(src);
-      if (head0 + hh >= H) rq[j] = v4u{0u, 0u, 0u, 0u};
+    for (int ks = 0; ks < kKeyDim / 32; ++ks) {
+      const int d = ks * 32 + gq * 8;
+      rq[ks] = *reinterpret_cast<const v4u*>(d < kLatent ? a.q_lat + qh * kLatent + d : a.q_rope + qh * kRope + (d - kLatent));
     }
   }
   const int n = load_uniform(a.n_visible + q);
   const int c = max(0, n - a.swa);
-  const int Es = min(load_uniform(a.topk_count + q), a.topk);
-  const int E = Es + (n - c);
-  const int e_end = min(E, e_begin + a.split_entries);
+  const int Ew = n - c;                           // window rows [c, n)
+  const int Es = min(load_uniform(a.topk_count + q), K);
   const int64_t sbase = load_uniform(a.seq_base + q);
+  const int64_t wbase = load_uniform(a.swa_base + q);
   // paged main KV: the kept positions become rows of the whole planes (one
   // page id per position, loaded unconditionally from a clamped slot)
   const bool paged = a.pages != nullptr;
@@ -261,206 +222,334 @@ __global__ __launch_bounds__(kNT) void k_attend(AttendArgs a) {
     for (int j = 0; j < kRowPer; ++j)
       tkv[j] = (int32_t)(((uint32_t)pg[j] << a.page_shift) | ((uint32_t)tkv[j] & ((1u << a.page_shift) - 1u)));
   }
-  const TileSrc src = tile_src(a, paged ? 0 : sbase, load_uniform(a.swa_base + q), paged ? (int)a.rows : n, n - c);
-
-  {
-    // the split's kept positions: the row always holds `topk` entries, so
-    // these loads were issued before the counts (a.n_visible, a.topk_count)
-    // they are filtered by arrived
+  // the query's sources, each over exactly its rows
+  const int64_t kbase = paged ? 0 : sbase;
+  const uint32_t krows = paged ? (uint32_t)a.rows : (uint32_t)n;
+  const int gshift = a.kv_gshift;
+  const uint32_t sbytes = (uint32_t)kScaleBytes >> gshift;
+  const v4u rs_codes = rsrc_of(a.kv_codes + kbase * kCodeBytes, krows * kCodeBytes);
+  const v4u rs_scales = rsrc_of(a.kv_scales + kbase * sbytes, krows * sbytes);
+  const v4u rs_rope = rsrc_of(a.kv_rope + kbase * kRope, krows * (kRope * 2));
+  const v4u rs_win = rsrc_of(a.swa_kv + wbase * kKeyDim, (uint32_t)Ew * kWinRow);
+  // row codes of the split's tiles (>= 0: cache row, < 0: window row -1 - code)
 #pragma unroll
-    for (int j = 0; j < kRowPer; ++j) {
-      const int e = e_begin + tid + j * kNT;
-      if (e < e_end) s_row[e - e_begin] = e < Es ? tkv[j] : -1 - (e - Es);
+  for (int j = 0; j < kRowPer; ++j) {
+    const int idx = tid + j * kNT;
+    if (idx < ntl * kTE) {
+      const int t = t_begin + idx / kTE, e = idx % kTE;
+      int32_t code = kNoRow;
+      if (t < nwt) {
+        const int ge = t * kTE + e;
+        if (ge < Ew) code = -1 - ge;
+      } else if ((t - nwt) * kTE + e < Es) {
+        code = tkv[j];
+      }
+      s_row[idx] = code;
     }
   }
   __syncthreads();
-  // raw tiles two deep: tiles t and t+1 are in flight while t-1 is contracted
-  RawTile ra, rb;
-  // (unconditional: a tile past the split's end loads zeros)
-  load_tile(src, s_row, min(kTile, e_end - e_begin), tid, ra);
-  load_tile(src, s_row + kTile, min(kTile, e_end - e_begin - kTile), tid, rb);
-  // the query into LDS while the first tiles are in flight (read after the
-  // first tile's barriers)
-  if (active) {
-    _Float16* sq = s_q + wave * 16 * kKS;
-#pragma unroll
-    for (int j = 0; j < kQv; ++j) {
-      const int i = lane + 64 * j, hh = i / (kKeyDim / 8), d = (i % (kKeyDim / 8)) * 8;
-      *reinterpret_cast<v4u*>(sq + hh * kKS + d) =
-          v4u{bf16x2_to_h2(rq[j][0]), bf16x2_to_h2(rq[j][1]), bf16x2_to_h2(rq[j][2]), bf16x2_to_h2(rq[j][3])};
-    }
-  }
-  const _Float16* sqw = s_q + (wave * 16 + col) * kKS + gq * 8;
+  auto tile_entries = [&](int t) {
+    return t < nwt ? min(kTE, max(0, Ew - t * kTE)) : min(kTE, max(0, Es - (t - nwt) * kTE));
+  };
 
-  float m = -__builtin_inff(), l = 0.0f;
-  v4f o[kLatent / 16];
+  // ---- gathers.  Rope: rows 8 wave .. +8, lane l -> row 8 wave + l / 8 and
+  // source chunk (l % 8) ^ (l / 8), so a row's chunk j sits at position
+  // j ^ (row % 8) and the Q.K^T reads of 8 rows fall on distinct banks.
+  auto issue_rope = [&](int ti, bool win) {
+    const int32_t* rows = s_row + ti * kTE;
+    const int ne = tile_entries(t_begin + ti);
+    const int r = 8 * wave + (lane >> 3);
+    const int32_t code = rows[r];
+    const uint32_t ch = (uint32_t)(((lane & 7) ^ (lane >> 3)) * 16);
+    const uint32_t dst = lds_addr(s_mem + kOffRope + (ti & 1) * kRopeSlot + 8 * wave * (kRope * 2));
+    if (win) dma16(dst, r < ne ? (uint32_t)(-1 - code) * kWinRow + kLatent * 2 + ch : kOob, rs_win);
+    else dma16(dst, r < ne ? (uint32_t)code * (kRope * 2) + ch : kOob, rs_rope);
+  };
+  // a kept-entry tile: codes (rows 8 wave .. +8, two KiB loads of 4 rows),
+  // the wave's 256 bytes of the tile's scale block, the rope
+  auto issue_sparse = [&](int ti) {
+    const int32_t* rows = s_row + ti * kTE;
+    const int ne = tile_entries(t_begin + ti);
+    unsigned char* st = s_mem + kOffStage + (ti & 1) * kStageSlot;
 #pragma unroll
-  for (int nt = 0; nt < kLatent / 16; ++nt) o[nt] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-
-  auto tile = [&](RawTile& raw, int e0) {
-    const int ne = min(kTile, e_end - e0);
-    __syncthreads();                         // the previous tile's reads of s_k are done
-    store_tile(src, s_row + (e0 - e_begin), ne, e0 + ne > Es, raw, tid, s_k);
-    const int e2 = e0 + 2 * kTile;           // this register set's next tile
-    if (e2 < e_end) load_tile(src, s_row + (e2 - e_begin), min(kTile, e_end - e2), tid, raw);
-    __syncthreads();
-    if (!active) return;
-
-    // ---- S^T = K_tile . Q^T  (rows: entries, cols: heads)
-    v4f s0 = {0.0f, 0.0f, 0.0f, 0.0f}, s1 = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int ks = 0; ks < kKeyDim / 32; ++ks) {
-      const v8h k0 = __builtin_bit_cast(v8h, *reinterpret_cast<const v4u*>(s_k + col * kKS + ks * 32 + gq * 8));
-      const v8h k1 = __builtin_bit_cast(v8h, *reinterpret_cast<const v4u*>(s_k + (16 + col) * kKS + ks * 32 + gq * 8));
-      const v8h qb = __builtin_bit_cast(v8h, *reinterpret_cast<const v4u*>(sqw + ks * 32));
-      s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(k0, qb, s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(k1, qb, s1, 0, 0, 0);
+    for (int h = 0; h < 2; ++h) {
+      const int r = 8 * wave + 4 * h + (lane >> 4);
+      dma16(lds_addr(st + (8 * wave + 4 * h) * kCodeBytes),
+            r < ne ? (uint32_t)rows[r] * kCodeBytes + (lane & 15) * 16 : kOob, rs_codes);
     }
-    // lane holds entries 4gq+i (s0) and 16+4gq+i (s1) for head `col`
-    float sv[8];
+    const int b = wave * 256 + lane * 4;          // byte of the [64][sbytes] scale block
+    const int r = b >> (5 - gshift);
+    dma4(lds_addr(st + kCodeStage + wave * 256),
+         r < ne ? (uint32_t)rows[min(r, kTE - 1)] * sbytes + ((uint32_t)b & (sbytes - 1)) : kOob, rs_scales);
+    issue_rope(ti, false);
+  };
+  // a window tile's latent rows, straight into the image (bf16 for now)
+  auto issue_window_rows = [&](int ti) {
+    const int32_t* rows = s_row + ti * kTE;
+    const int ne = tile_entries(t_begin + ti);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      sv[i] = (4 * gq + i < ne) ? s0[i] * a.scale_log2 : -__builtin_inff();
-      sv[4 + i] = (16 + 4 * gq + i < ne) ? s1[i] * a.scale_log2 : -__builtin_inff();
-    }
-    float mt = sv[0];
-#pragma unroll
-    for (int i = 1; i < 8; ++i) mt = fmaxf(mt, sv[i]);
-    mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
-    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-    const float m_new = fmaxf(m, mt);                 // finite: the tile has an entry
-    const float alpha = exp2f(m - m_new);
-    v8h pf;
-    float ls = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float p = exp2f(sv[i] - m_new);
-      ls += p;
-      pf[i] = (_Float16)p;
-    }
-    ls += __shfl_xor(ls, 16, 64);
-    ls += __shfl_xor(ls, 32, 64);
-    l = l * alpha + ls;
-    m = m_new;
-    // rescale accumulator rows (heads 4gq+i) by their alpha
-    float ar[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) ar[i] = __shfl(alpha, 4 * gq + i, 64);
-#pragma unroll
-    for (int nt = 0; nt < kLatent / 16; ++nt) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) o[nt][i] *= ar[i];
-    }
-    // ---- O += P . V   (k-slots: entries 4gq..4gq+3, then 16+4gq..16+4gq+3;
-    //      the transpose read hands lane `col` four entries of dim 16nt+col)
-    const int ra = 4 * gq + (col >> 2), cb = 4 * (col & 3);
-#pragma unroll
-    for (int nt = 0; nt < kLatent / 16; ++nt) {
-      const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(s_k + ra * kKS + nt * 16 + cb));
-      const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(s_k + (16 + ra) * kKS + nt * 16 + cb));
-      const v8h vb = __builtin_bit_cast(v8h, (v4u{__builtin_bit_cast(v2u, lo)[0], __builtin_bit_cast(v2u, lo)[1],
-                                                  __builtin_bit_cast(v2u, hi)[0], __builtin_bit_cast(v2u, hi)[1]}));
-      o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pf, vb, o[nt], 0, 0, 0);
+    for (int j = 0; j < 8; ++j) {
+      const int r = 8 * wave + j;
+      const int32_t code = rows[r];
+      dma16(lds_addr(s_lat + r * kLS), r < ne ? (uint32_t)(-1 - code) * kWinRow + lane * 16 : kOob, rs_win);
     }
   };
-  for (int e0 = e_begin; e0 < e_end; e0 += 2 * kTile) {
-    tile(ra, e0);
-    if (e0 + kTile < e_end) tile(rb, e0 + kTile);
+  auto is_window = [&](int ti) { return t_begin + ti < nwt; };
+  auto ahead_count = [&](int ti) { return ti >= ntl ? 0 : (is_window(ti) ? kAheadWindow : kAheadSparse); };
+  auto issue_ahead = [&](int ti) {
+    if (ti >= ntl) return;
+    if (is_window(ti)) issue_rope(ti, true);
+    else issue_sparse(ti);
+  };
+
+  if (ntl > 0) {
+    issue_ahead(0);
+    if (is_window(0)) issue_window_rows(0);
+  }
+  issue_ahead(1);
+
+  // the query as MFMA operands: latent dims in f16, rope dims in bf16 (the
+  // empty asm keeps the wait for the query loads here, after the gathers are
+  // issued)
+#pragma unroll
+  for (int ks = 0; ks < kKeyDim / 32; ++ks) asm volatile("" : "+v"(rq[ks]));
+  v8h qf[kLatent / 32];
+  v8bf qr[kRope / 32];
+  {
+    const bool live = head0 + col < H;
+#pragma unroll
+    for (int ks = 0; ks < kLatent / 32; ++ks) {
+      const v4u x = live ? rq[ks] : v4u{0u, 0u, 0u, 0u};
+      qf[ks] = __builtin_bit_cast(v8h, (v4u{bf16x2_to_h2(x[0]), bf16x2_to_h2(x[1]), bf16x2_to_h2(x[2]), bf16x2_to_h2(x[3])}));
+    }
+#pragma unroll
+    for (int j = 0; j < kRope / 32; ++j)
+      qr[j] = __builtin_bit_cast(v8bf, live ? rq[kLatent / 32 + j] : v4u{0u, 0u, 0u, 0u});
   }
 
-  if (!active) return;
+  float m = -__builtin_inff(), l = 0.0f;         // per head (lanes of column col), this lane's entries' sum
+  v4f o[8];
+#pragma unroll
+  for (int nt = 0; nt < 8; ++nt) o[nt] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
-  // ---- epilogue: lane holds O[head 4gq+i][dim 16nt+col]
-  if (S == 1) {
-    float inv[4];
+  for (int ti = 0; ti < ntl; ++ti) {
+    const int t = t_begin + ti;
+    const int ne = tile_entries(t);
+    const bool win = t < nwt;
+    const unsigned char* rope = s_mem + kOffRope + (ti & 1) * kRopeSlot;
+    if (win && ti > 0) {
+      __syncthreads();                            // the previous tile's reads of the image are done
+      issue_window_rows(ti);
+      wait_vmcnt<0>();
+    } else {
+      wait_ahead(ahead_count(ti + 1));            // this tile's loads have landed (the next tile's in flight)
+    }
+    __syncthreads();                              // every wave's loads have landed; the previous P.V is done
+    if (ne > 0) {
+      if (win) {
+        // window rows in place: bf16 -> f16
+#pragma unroll
+        for (int j = 0; j < kTE * (kLatent / 8) / kNT; ++j) {
+          const int idx = j * kNT + tid, r = idx >> 6, ch = idx & 63;
+          v4u* p = reinterpret_cast<v4u*>(s_lat + r * kLS + ch * 8);
+          const v4u x = *p;
+          *p = v4u{bf16x2_to_h2(x[0]), bf16x2_to_h2(x[1]), bf16x2_to_h2(x[2]), bf16x2_to_h2(x[3])};
+        }
+      } else {
+        // kept entries: codes x scale from the staging slot
+        const unsigned char* st = s_mem + kOffStage + (ti & 1) * kStageSlot;
+#pragma unroll
+        for (int k = 0; k < kItems; ++k) {
+          const int it = tid + k * kNT, e = it >> 5, grp = it & 31;
+          const v2u cw = *reinterpret_cast<const v2u*>(st + e * kCodeBytes + grp * 8);
+          const _Float16 sh = (_Float16)e4m3_to_float(st[kCodeStage + e * sbytes + (grp >> gshift)]);   // exact
+          const v2h s2 = {sh, sh};
+          v4u* dk = reinterpret_cast<v4u*>(s_lat + e * kLS + grp * 16);
+          dk[0] = v4u{fp4_byte_h2<0>(cw[0], s2), fp4_byte_h2<1>(cw[0], s2), fp4_byte_h2<2>(cw[0], s2), fp4_byte_h2<3>(cw[0], s2)};
+          dk[1] = v4u{fp4_byte_h2<0>(cw[1], s2), fp4_byte_h2<1>(cw[1], s2), fp4_byte_h2<2>(cw[1], s2), fp4_byte_h2<3>(cw[1], s2)};
+        }
+      }
+    }
+    __syncthreads();                              // the image is complete
+
+    // ---- S^T = K . Q^T for entries 16 qw .. +16 (two accumulator chains)
+    float sv[4];
+    if (ne > 0) {
+      v4f s0 = {0.0f, 0.0f, 0.0f, 0.0f}, s1 = {0.0f, 0.0f, 0.0f, 0.0f};
+      const int er = 16 * qw + col;
+      const _Float16* kr = s_lat + er * kLS + gq * 8;
+#pragma unroll
+      for (int ks = 0; ks < kLatent / 32; ks += 2) {
+        const v8h k0 = __builtin_bit_cast(v8h, *reinterpret_cast<const v4u*>(kr + ks * 32));
+        const v8h k1 = __builtin_bit_cast(v8h, *reinterpret_cast<const v4u*>(kr + ks * 32 + 32));
+        s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(k0, qf[ks], s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(k1, qf[ks + 1], s1, 0, 0, 0);
+      }
+      {
+        const unsigned char* rr = rope + er * (kRope * 2);
+        const v8bf r0 = __builtin_bit_cast(v8bf, *reinterpret_cast<const v4u*>(rr + ((gq ^ (er & 7)) * 16)));
+        const v8bf r1 = __builtin_bit_cast(v8bf, *reinterpret_cast<const v4u*>(rr + (((4 + gq) ^ (er & 7)) * 16)));
+        s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(r0, qr[0], s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(r1, qr[1], s1, 0, 0, 0);
+      }
+      // lane holds entries 16 qw + 4 gq + i for head col
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sv[i] = 16 * qw + 4 * gq + i < ne ? (s0[i] + s1[i]) * a.scale_log2 : -__builtin_inff();
+      const float wmax = max_rows4(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])));
+      if (gq == 0) s_mx[(hgl * 4 + qw) * 16 + col] = wmax;
+    }
+    __syncthreads();                              // maxima written; every wave is past its Q.K^T
+    issue_ahead(ti + 2);                          // into the slots this tile has finished with
+    if (ne == 0) continue;
+
+    const float* mx = s_mx + hgl * 64;
+    const float tmax = fmaxf(fmaxf(mx[col], mx[16 + col]), fmaxf(mx[32 + col], mx[48 + col]));
+    const float m_new = fmaxf(m, tmax);           // finite: the tile has an entry
+    const float alpha = exp2f(m - m_new);
+    float ps = 0.0f;
+    _Float16 ph[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float li = __shfl(l, 4 * gq + i, 64);
-      inv[i] = li > 0.0f ? 1.0f / li : 0.0f;
+      const float p = exp2f(sv[i] - m_new);
+      ps += p;
+      ph[i] = (_Float16)p;
     }
+    l = l * alpha + ps;
+    m = m_new;
+    _Float16* pg = s_p + hgl * 16 * kPS;
+    *reinterpret_cast<v4s*>(&pg[col * kPS + 16 * qw + 4 * gq]) = __builtin_bit_cast(v4s, (v4h_t{ph[0], ph[1], ph[2], ph[3]}));
+    if (qw == 0 && gq == 0) s_al[hgl * 16 + col] = alpha;
+    __syncthreads();
+
+    // ---- O[heads][dims 128 qw ..] = alpha O + P . V
+    const v4f ar = *reinterpret_cast<const v4f*>(&s_al[hgl * 16 + 4 * gq]);    // alpha of heads 4 gq + i
+    const bool same = ar[0] == 1.0f && ar[1] == 1.0f && ar[2] == 1.0f && ar[3] == 1.0f;
+    if (__builtin_amdgcn_ballot_w64(!same) != 0) {      // (uniform) some head's maximum moved
 #pragma unroll
-    for (int nt = 0; nt < kLatent / 16; ++nt) {
+      for (int nt = 0; nt < 8; ++nt) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (head0 + 4 * gq + i < H)
-          a.out[((int64_t)q * H + head0 + 4 * gq + i) * kLatent + nt * 16 + col] = o[nt][i] * inv[i];
+        for (int i = 0; i < 4; ++i) o[nt][i] *= ar[i];
+      }
     }
-    if (a.lse && gq == 0 && head0 + col < H)
-      a.lse[(int64_t)q * H + head0 + col] = l > 0.0f ? (m + log2f(l)) * 0.69314718055994531f : -__builtin_inff();
-  } else {
-    // partial o of the wave's 16 heads in the accumulators' own layout
-    // [nt][lane][4] (one 1 KiB coalesced store per nt); k_attend_combine
-    // reads it back in the same layout
-    // (partials cover the heads padded to a multiple of 16)
-    const int HB = (H + 15) / 16;
-    float* po = a.part_o + (((int64_t)q * S + sp) * HB + head0 / 16) * (kLatent * 16);
+    const int ra_ = 4 * gq + (col >> 2), cb = 4 * (col & 3);
 #pragma unroll
-    for (int nt = 0; nt < kLatent / 16; ++nt)
-      *reinterpret_cast<v4f*>(po + (nt * 64 + lane) * 4) = o[nt];
-    if (gq == 0) {
-      float* pm = a.part_ml + (((int64_t)q * S + sp) * (HB * 16) + head0 + col) * 2;
-      pm[0] = m;
-      pm[1] = l;
+    for (int kk = 0; kk < kTE / 32; ++kk) {
+      // k-slots: entries 32 kk + 4 gq .. +4, then 32 kk + 16 + 4 gq .. +4 (the
+      // transpose read hands lane col the same entries of dim 16 nt + col)
+      const v2u plo = *reinterpret_cast<const v2u*>(&pg[col * kPS + 32 * kk + 4 * gq]);
+      const v2u phi = *reinterpret_cast<const v2u*>(&pg[col * kPS + 32 * kk + 16 + 4 * gq]);
+      const v8h pa = __builtin_bit_cast(v8h, (v4u{plo[0], plo[1], phi[0], phi[1]}));
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt) {
+        const int d = 128 * qw + nt * 16 + cb;
+        const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(s_lat + (32 * kk + ra_) * kLS + d));
+        const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(s_lat + (32 * kk + 16 + ra_) * kLS + d));
+        const v8h vb = __builtin_bit_cast(v8h, (v4u{__builtin_bit_cast(v2u, lo)[0], __builtin_bit_cast(v2u, lo)[1],
+                                                    __builtin_bit_cast(v2u, hi)[0], __builtin_bit_cast(v2u, hi)[1]}));
+        o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, vb, o[nt], 0, 0, 0);
+      }
+    }
+  }
+
+  // ---- row sums per head: this lane's entries, the four lane groups, the
+  // group's four waves
+  const float lw = sum_rows4(l);
+  if (gq == 0) s_lw[(hgl * 4 + qw) * 16 + col] = lw;
+  __syncthreads();                                // also: every wave is past its last P.V
+  const float* lwg = s_lw + hgl * 64;
+  const float l_head = (lwg[col] + lwg[16 + col]) + (lwg[32 + col] + lwg[48 + col]);
+  // lane holds O[head 4 gq + i][dim 128 qw + 16 nt + col]
+  float li[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int hh = 4 * gq + i;
+    li[i] = (lwg[hh] + lwg[16 + hh]) + (lwg[32 + hh] + lwg[48 + hh]);
+  }
+
+  // ---- the 32 rows (normalised, or this split's unnormalised partial)
+  // through LDS, then whole 16-byte stores
+  const bool fin = S == 1;
+  float* s_o = reinterpret_cast<float*>(s_mem);  // [32 heads][kOS]
+#pragma unroll
+  for (int nt = 0; nt < 8; ++nt) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      s_o[(hgl * 16 + 4 * gq + i) * kOS + 128 * qw + nt * 16 + col] =
+          fin ? (li[i] > 0.0f ? o[nt][i] / li[i] : 0.0f) : o[nt][i];
+  }
+  __syncthreads();
+  const int HP = HG * kAttendHeads;
+  float* dst = fin ? a.out + ((int64_t)q * H + hg * kAttendHeads) * kLatent
+                   : a.part_o + (((int64_t)q * S + sp) * HP + hg * kAttendHeads) * kLatent;
+#pragma unroll
+  for (int j = 0; j < kAttendHeads * (kLatent / 4) / kNT; ++j) {
+    const int idx = j * kNT + tid, hr = idx >> 7, c4 = (idx & 127) * 4;
+    if (hg * kAttendHeads + hr < H)
+      *reinterpret_cast<v4f*>(dst + hr * kLatent + c4) = *reinterpret_cast<const v4f*>(s_o + hr * kOS + c4);
+  }
+  if (qw == 0 && gq == 0 && head0 + col < H) {
+    if (fin) {
+      if (a.lse)
+        a.lse[(int64_t)q * H + head0 + col] = l_head > 0.0f ? (m + log2f(l_head)) * 0.69314718055994531f : -__builtin_inff();
+    } else {
+      *reinterpret_cast<v2f*>(a.part_ml + (((int64_t)q * S + sp) * HP + head0 + col) * 2) = v2f{m, l_head};
     }
   }
 }
 
-// Merge split partials: out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s.
-// A workgroup takes one query's 16-head block and 4 of its 32 accumulator
-// tiles; a thread owns one accumulator slot (4 heads x 1 dim) and issues all
-// of its partial loads (every split) before the first use.
-__global__ __launch_bounds__(256) void k_attend_combine(AttendArgs a) {
-  const int S = a.splits, H = a.heads, HB = (H + 15) / 16;
-  const int q = blockIdx.x / (HB * 8), hb = (blockIdx.x / 8) % HB, ntg = blockIdx.x % 8;
-  const int lane = threadIdx.x & 63, nt = ntg * 4 + (threadIdx.x >> 6);
-  const int gq = lane >> 4, col = lane & 15;
-  const int h0 = hb * 16 + 4 * gq;
+// Merge split partials: out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s,
+// lse = M + log2(sum_s 2^(m_s - M) l_s) (in the exp2 domain, then as a
+// natural log).  A thread owns four dims of one head and issues every
+// split's loads before the first use: one round trip.
+constexpr int kCombineThreads = 256;     // two heads x 128 threads of 4 dims
+__global__ __launch_bounds__(kCombineThreads) void k_attend_combine(AttendArgs a) {
+  const int S = a.splits, H = a.heads, HP = a.head_groups * kAttendHeads;
+  const int q = blockIdx.x / (HP / 2);
+  const int h = (blockIdx.x % (HP / 2)) * 2 + (threadIdx.x >> 7);
+  const int d = (threadIdx.x & 127) * 4;
+  if (h >= H) return;
+  v2f ml[kAttendMaxSplits];
   v4f os[kAttendMaxSplits];
-  float ms[kAttendMaxSplits][4], ls[kAttendMaxSplits][4];
 #pragma unroll
   for (int s = 0; s < kAttendMaxSplits; ++s) {
-    os[s] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) { ms[s][i] = -__builtin_inff(); ls[s][i] = 0.0f; }
-    if (s < S) {
-      os[s] = *reinterpret_cast<const v4f*>(a.part_o + (((int64_t)q * S + s) * HB + hb) * (kLatent * 16) +
-                                            (nt * 64 + lane) * 4);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const v2f ml = *reinterpret_cast<const v2f*>(a.part_ml + (((int64_t)q * S + s) * (HB * 16) + h0 + i) * 2);
-        ms[s][i] = ml[0];
-        ls[s][i] = ml[1];
-      }
-    }
+    const int64_t r = ((int64_t)q * S + min(s, S - 1)) * HP + h;
+    ml[s] = *reinterpret_cast<const v2f*>(a.part_ml + r * 2);
+    os[s] = *reinterpret_cast<const v4f*>(a.part_o + r * kLatent + d);
   }
+  float M = -__builtin_inff();
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    float M = ms[0][i];
+  for (int s = 0; s < kAttendMaxSplits; ++s)
+    if (s < S && ml[s][1] > 0.0f) M = fmaxf(M, ml[s][0]);
+  float den = 0.0f;
+  v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int s = 1; s < kAttendMaxSplits; ++s) M = fmaxf(M, ms[s][i]);
-    float den = 0.0f, acc = 0.0f;
-    if (M != -__builtin_inff()) {
+  for (int s = 0; s < kAttendMaxSplits; ++s) {
+    const float w = s < S && ml[s][1] > 0.0f ? exp2f(ml[s][0] - M) : 0.0f;
+    den += w * ml[s][1];
 #pragma unroll
-      for (int s = 0; s < kAttendMaxSplits; ++s) {
-        const float wgt = ls[s][i] > 0.0f ? exp2f(ms[s][i] - M) : 0.0f;
-        den += wgt * ls[s][i];
-        acc += wgt * os[s][i];
-      }
-    }
-    if (h0 + i >= H) continue;               // padding heads (H a multiple of 8)
-    a.out[((int64_t)q * H + h0 + i) * kLatent + nt * 16 + col] = den > 0.0f ? acc / den : 0.0f;
-    if (a.lse && nt == 0 && col == 0)
-      a.lse[(int64_t)q * H + h0 + i] = den > 0.0f ? (M + log2f(den)) * 0.69314718055994531f : -__builtin_inff();
+    for (int i = 0; i < 4; ++i) acc[i] += w * os[s][i];
   }
+  v4f r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r[i] = den > 0.0f ? acc[i] / den : 0.0f;
+  *reinterpret_cast<v4f*>(a.out + ((int64_t)q * H + h) * kLatent + d) = r;
+  if (a.lse && d == 0)
+    a.lse[(int64_t)q * H + h] = den > 0.0f ? (M + log2f(den)) * 0.69314718055994531f : -__builtin_inff();
 }
 
 }  // namespace
 
 hipError_t launch_attend(const AttendArgs& a, hipStream_t s) {
+  if (a.split_tiles * kTE > kMaxRows || a.splits < 1 || a.splits > kAttendMaxSplits ||
+      (a.splits > 1 && (!a.part_o || !a.part_ml)))
+    return hipErrorInvalidValue;
   hipLaunchKernelGGL(k_attend, dim3((unsigned)(a.n_q * a.head_groups * a.splits)), dim3(kNT), 0, s, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || a.splits == 1) return e;
-  hipLaunchKernelGGL(k_attend_combine, dim3((unsigned)(a.n_q * ((a.heads + 15) / 16) * 8)), dim3(256), 0, s, a);
+  if (a.splits > 1) {
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_attend_combine, dim3((unsigned)(a.n_q * a.head_groups * kAttendHeads / 2)),
+                       dim3(kCombineThreads), 0, s, a);
+  }
   return hipGetLastError();
 }
 

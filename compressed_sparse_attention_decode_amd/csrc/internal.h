@@ -70,13 +70,13 @@ struct AttendArgs {
   const int64_t* seq_base;
   const int32_t* n_visible;
   int n_q, heads, topk, swa;
-  int head_groups;           // workgroups across heads per query
-  int splits;                // workgroups across entries per query
-  int split_entries;         // entries per split (multiple of the tile)
+  int head_groups;           // workgroups across heads per query (32 heads each)
+  int splits;                // workgroups across the tile list per query and head group
+  int split_tiles;           // tiles per split (the window's tiles first, then the kept entries')
   float* out;                // [n_q, H, 512]
   float* lse;                // optional [n_q, H]
-  float* part_o;             // [n_q, splits, H, 512] when splits > 1
-  float* part_ml;            // [n_q, splits, H, 2]
+  float* part_o;             // splits > 1: [n_q][splits][head_groups * 32][512] unnormalised o
+  float* part_ml;            // splits > 1: [n_q][splits][head_groups * 32][2] (m in the exp2 domain, l)
   const int32_t* pages;      // paged main-KV planes (as ReindexArgs; the window stays apart)
   int page_shift;
   int64_t rows;
@@ -115,9 +115,11 @@ hipError_t launch_stream_read(const void* buf, int64_t bytes, uint32_t* sink, in
 constexpr int kPoolChunk = 4096;       // blocks per pool-select chunk workgroup
 constexpr int kPoolChunkCand = 1024;   // candidate slots per chunk
 constexpr int kPoolSmallBlocks = 16384;   // blocks a one-workgroup pool selection holds
-constexpr int kAttendTile = 32;        // entries per attention tile
-constexpr int kAttendWaves = 4;        // waves per attention workgroup (16 heads each)
-constexpr int kAttendMaxSplits = 16;   // entry-list splits per query, at most
+constexpr int kAttendTile = 64;        // entries per attention tile
+constexpr int kAttendWaves = 8;        // waves per attention workgroup (two groups of 16 heads, 4 waves each)
+constexpr int kAttendHeads = 32;       // heads per attention workgroup
+constexpr int kAttendMaxSplits = 16;   // tile-list splits per query and head group, at most
+constexpr int kAttendMaxTiles = 48;    // tiles of one query: 1024 / 64 window + 2048 / 64 kept
 constexpr int kReindexBlocks = 64;     // pool blocks per Reindex scoring workgroup (one-round grids)
 constexpr int kReindexBlocksWide = 128;   // ... when 64-block workgroups would exceed two per CU
 constexpr int kReindexBlocksNarrow = 32;  // ... when 32-block workgroups fit in one per CU

@@ -366,7 +366,11 @@ csa2_status csa2_index_reindex_fp4(const csa2_dims* dims, const csa2_queries* q,
                                    int32_t* topk_pos, int32_t* topk_count, float* topk_scores,
                                    void* ws, size_t ws_bytes, void* stream);
 
-/* Workspace bytes for csa2_attend. */
+/* Workspace bytes for csa2_attend: 0 when each (query, 32-head group) is one
+ * workgroup, else the partials of its splits (2 KiB + 8 B per split and
+ * head, heads padded to a multiple of 32).  The split count depends only on
+ * n_q, n_heads, topk and swa: one split per 64-entry tile for a batch of a
+ * few queries, one per (query, head group) once n_q * ceil(H / 32) >= 256. */
 csa2_status csa2_attend_workspace_size(const csa2_dims* dims, const csa2_queries* q,
                                        size_t* bytes);
 
@@ -389,6 +393,11 @@ csa2_status csa2_attend_workspace_size(const csa2_dims* dims, const csa2_queries
  *   topk_pos, topk_count          as produced by csa2_index_reindex
  *   swa_kv bf16 [swa_rows, 576]   swa_base int64 [n_q] (device)
  *   out    float [n_q, H, 512]    lse float [n_q, H] or NULL
+ *   ws, ws_bytes  csa2_attend_workspace_size bytes (NULL when that is 0),
+ *          256-byte aligned, no initial contents; calls sharing it must be
+ *          ordered on one stream.
+ * One kernel, or two when the plan splits a query's entries (the second
+ * merges the splits with a log-sum-exp rescale).
  * Window values are converted to fp16 for the value product: |v| must stay
  * below 65504. */
 csa2_status csa2_attend(const csa2_dims* dims, const csa2_queries* q,
@@ -510,9 +519,10 @@ csa2_status csa2_decode_step(const csa2_dims* dims, const csa2_queries* q, int32
  * one array of 64 MiB that the library holds on each GPU it runs on until the
  * process ends.  The call allocates nothing.
  *   Limits: at most 65,536 queries, and a batch whose workspace
- *   (csa2_decode_step_workspace_size) fits in 64 MiB minus 256 KiB: batch 8
- *   at 128K and batch 1 at 1M context take about 12 MB, 32 queries of up to
- *   256K about 40 MB.  Larger batches get CSA2_ERR_WORKSPACE, enqueuing
+ *   (csa2_decode_step_workspace_size) fits in 64 MiB minus 256 KiB: batch 1
+ *   at 1M context takes about 6 MiB, batch 8 at 128K about 16 MiB, 32
+ *   queries of up to 256K about 56 MiB.  Larger batches get
+ *   CSA2_ERR_WORKSPACE, enqueuing
  *   nothing.
  *   Every call on one GPU uses that GPU's array: calls that may overlap on
  *   one GPU (different streams, or a graph replayed while another call runs)
