@@ -228,11 +228,16 @@ class Step:
             # separately to time each
             seq.append(("scan", csa2.index_scan(st.dims, st.batch, q0, w0, idx_k, self.bs, pool_ws=self.ws_p,
                                                 prepare=True, pages=st.pages, pos_keys=self.pk)))
-            seq.append(("pool", csa2.index_pool(st.dims, st.batch, self.bs, self.pool, self.pcnt, ws=self.ws_p,
-                                                from_scan=True, prepare=True)))
             if self.full_topk:
-                seq.append(("topk", csa2.index_topk_keys(st.dims, st.batch, self.pool, self.pcnt, self.bs, self.pk,
-                                                         topk_pos=self.tk[0], topk_count=self.tc[0], prepare=True)))
+                # the pool and the Full layer's Top-K from the scan's keys
+                # (one kernel for pools of up to 16,384 blocks)
+                seq.append(("pool_topk", csa2.index_pool_topk(st.dims, st.batch, self.bs, self.pk, self.pool,
+                                                              self.pcnt, self.tk[0], self.tc[0], ws=self.ws_p,
+                                                              from_scan=True, prepare=True)))
+            else:
+                seq.append(("pool", csa2.index_pool(st.dims, st.batch, self.bs, self.pool, self.pcnt, ws=self.ws_p,
+                                                    from_scan=True, prepare=True)))
+            if self.full_topk:
                 ql, qr = st.mq(0)
                 seq.append(("attend", csa2.attend(st.dims, st.batch, ql, qr, 1.0, codes, scales, kv_rope,
                                                   self.tk[0], self.tc[0], swa_kv, st.swa_base, out=self.out[0],

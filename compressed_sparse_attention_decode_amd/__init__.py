@@ -100,6 +100,7 @@ def lib() -> ctypes.CDLL:
             "csa2_stream_read": (I32, [P, I64, P, P]),
             "csa2_index_scan_keys": (I32, [PD, PQ, PP, P, P, P, P, P, P, I64, P, I64, P, SZ, P]),
             "csa2_index_topk_keys": (I32, [PD, PQ, P, P, P, I64, P, I64, P, P, P, P]),
+            "csa2_index_pool_topk": (I32, [PD, PQ, P, I64, P, I64, P, P, P, P, P, SZ, I32, P]),
             "csa2_decode_step_noalloc": (I32, [PD, PQ, I32, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_float,
                                                P, P, P, P, P, P, P, P]),
         }
@@ -486,6 +487,40 @@ def index_pool(dims: Dims, b: Batch, block_scores: torch.Tensor,
             POOL_WS_FROM_SCAN if from_scan else 0, _stream(dev))
     call = _issue(lib().csa2_index_pool, args, (d, q, ws), prepare)
     return call if prepare else (pool_blocks, pool_count)
+
+
+def index_pool_topk(dims: Dims, b: Batch, block_scores: torch.Tensor, pos_keys: torch.Tensor,
+                    pool_blocks: Optional[torch.Tensor] = None, pool_count: Optional[torch.Tensor] = None,
+                    topk_pos: Optional[torch.Tensor] = None, topk_count: Optional[torch.Tensor] = None,
+                    ws: Optional[torch.Tensor] = None, from_scan: bool = False, prepare: bool = False):
+    """index_pool then index_topk_keys in one call (csa2_index_pool_topk; one
+    kernel for pools of up to 16,384 blocks).  Returns (pool_blocks,
+    pool_count, topk_pos, topk_count)."""
+    if from_scan and ws is None:
+        raise ValueError("from_scan needs the workspace that index_scan prepared")
+    dev = block_scores.device
+    _dev(block_scores, pos_keys, pool_blocks, pool_count, topk_pos, topk_count, ws)
+    n_q = b.n_q
+    if block_scores.dtype != torch.float32 or block_scores.dim() != 2 or block_scores.shape[0] != n_q:
+        raise ValueError("block_scores must be float32 [n_q, ld]")
+    if pos_keys.dim() != 2 or pos_keys.shape[0] != n_q or pos_keys.element_size() != 4:
+        raise ValueError("pos_keys must be 32-bit [n_q, ld]")
+    if pool_blocks is None:
+        pool_blocks = torch.empty(n_q, dims.pool_blocks, dtype=torch.int32, device=dev)
+    if pool_count is None:
+        pool_count = torch.empty(n_q, dtype=torch.int32, device=dev)
+    if topk_pos is None:
+        topk_pos = torch.empty(n_q, dims.topk, dtype=torch.int32, device=dev)
+    if topk_count is None:
+        topk_count = torch.empty(n_q, dtype=torch.int32, device=dev)
+    ws = _workspace(workspace_pool(dims, b), dev, ws)
+    wp, wn = _ws_ptr(ws)
+    d, q = dims.c(), b.c()
+    args = (ctypes.byref(d), ctypes.byref(q), block_scores.data_ptr(), block_scores.shape[1], pos_keys.data_ptr(),
+            pos_keys.shape[1], pool_blocks.data_ptr(), pool_count.data_ptr(), topk_pos.data_ptr(),
+            topk_count.data_ptr(), wp, wn, POOL_WS_FROM_SCAN if from_scan else 0, _stream(dev))
+    call = _issue(lib().csa2_index_pool_topk, args, (d, q, ws), prepare)
+    return call if prepare else (pool_blocks, pool_count, topk_pos, topk_count)
 
 
 def index_reindex(dims: Dims, b: Batch, idx_q, idx_w: torch.Tensor, idx_k,

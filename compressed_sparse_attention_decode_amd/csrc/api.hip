@@ -395,8 +395,13 @@ static csa2_status run_scan(const csa2_dims* d, const csa2_queries* q, const uin
   return e == hipSuccess ? CSA2_OK : hip_fail(e, "scan launch");
 }
 
+// With topk_pos, the Full layer's Top-K from the scan's position keys follows
+// the pool: inside the selecting workgroup for small pools, else by
+// k_topk_keys after the chunked kernels.
 static csa2_status run_pool(const csa2_dims* d, const csa2_queries* q, const float* block_scores, int64_t ld_block_scores,
-                            int32_t* pool_blocks, int32_t* pool_count, void* ws, bool after_scan, void* stream) {
+                            int32_t* pool_blocks, int32_t* pool_count, void* ws, bool after_scan, void* stream,
+                            const uint32_t* pkey = nullptr, int64_t ld_pkey = 0, int32_t* topk_pos = nullptr,
+                            int32_t* topk_count = nullptr) {
   PoolArgs pa;
   pa.bscore = block_scores; pa.ld = ld_block_scores; pa.n_visible = q->n_visible;
   pa.n_q = q->n_q; pa.swa = d->swa; pa.pool = d->pool_blocks;
@@ -424,8 +429,22 @@ static csa2_status run_pool(const csa2_dims* d, const csa2_queries* q, const flo
     pa.mm_span1 = pa.mm_span;
   }
   pa.pool_blocks = pool_blocks; pa.pool_count = pool_count;
+  const bool fused = topk_pos && pa.small;
+  pa.pkey = fused ? pkey : nullptr; pa.ld_pkey = ld_pkey; pa.topk = d->topk;
+  pa.topk_pos = fused ? topk_pos : nullptr; pa.topk_count = fused ? topk_count : nullptr;
   hipError_t e = launch_pool_select(pa, (hipStream_t)stream);
-  return e == hipSuccess ? CSA2_OK : hip_fail(e, "pool select launch");
+  if (e != hipSuccess) return hip_fail(e, "pool select launch");
+  if (topk_pos && !fused) {
+    TopkKeysArgs ta;
+    ta.pool_blocks = pool_blocks; ta.pool_count = pool_count;
+    ta.bscore = block_scores; ta.ld = ld_block_scores;
+    ta.pkey = pkey; ta.ld_pkey = ld_pkey;
+    ta.n_q = q->n_q; ta.pool = d->pool_blocks; ta.topk = d->topk;
+    ta.topk_pos = topk_pos; ta.topk_count = topk_count; ta.topk_scores = nullptr;
+    e = launch_topk_keys(ta, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "top-k launch");
+  }
+  return CSA2_OK;
 }
 
 // The indexer rows of a call: fp8 (no scale planes) or FP4 (both planes).
@@ -546,11 +565,30 @@ csa2_status csa2_index_pool(const csa2_dims* d, const csa2_queries* q, const flo
                   (flags & CSA2_POOL_WS_FROM_SCAN) != 0, stream);
 }
 
+csa2_status csa2_index_pool_topk(const csa2_dims* d, const csa2_queries* q, const float* block_scores,
+                                 int64_t ld_block_scores, const uint32_t* pos_keys, int64_t ld_pos_keys,
+                                 int32_t* pool_blocks, int32_t* pool_count, int32_t* topk_pos, int32_t* topk_count,
+                                 void* ws, size_t ws_bytes, int32_t flags, void* stream) {
+  csa2_status st = check_dims(d);
+  if (st) return st;
+  if ((st = check_queries(q))) return st;
+  if (!block_scores || !pool_blocks || !pool_count || !pos_keys || !topk_pos || !topk_count)
+    return fail(CSA2_ERR_INVALID_ARG, "required pointer is NULL");
+  if (flags & ~CSA2_POOL_WS_FROM_SCAN) return fail(CSA2_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
+  if ((st = check_block_scores(d, q, block_scores, ld_block_scores))) return st;
+  if ((st = check_pos_keys(d, q, pos_keys, ld_pos_keys))) return st;
+  if ((st = check_ws(ws, ws_bytes, pool_ws(d, q)))) return st;
+  if ((st = check_device())) return st;
+  return run_pool(d, q, block_scores, ld_block_scores, pool_blocks, pool_count, ws,
+                  (flags & CSA2_POOL_WS_FROM_SCAN) != 0, stream, pos_keys, ld_pos_keys, topk_pos, topk_count);
+}
+
 static csa2_status index_full(const csa2_dims* d, const csa2_queries* q, const uint8_t* idx_q, const uint8_t* q_scales,
                               const float* idx_w, const uint8_t* idx_k, const uint8_t* k_scales, bool fp4,
                               int32_t* pool_blocks, int32_t* pool_count, float* block_scores, int64_t ld_block_scores,
                               void* ws, size_t ws_bytes, void* stream, bool dry = false,
-                              const csa2_pages* pages = nullptr, uint32_t* pkey = nullptr) {
+                              const csa2_pages* pages = nullptr, uint32_t* pkey = nullptr,
+                              int32_t* topk_pos = nullptr, int32_t* topk_count = nullptr) {
   csa2_status st = check_dims(d);
   if (st) return st;
   if ((st = check_queries(q))) return st;
@@ -571,7 +609,8 @@ static csa2_status index_full(const csa2_dims* d, const csa2_queries* q, const u
   if ((st = run_scan(d, q, idx_q, fp4 ? q_scales : nullptr, idx_w, idx_k, fp4 ? k_scales : nullptr, bs, ld,
                      (uint32_t*)ws, stream, pages, pkey, pkey ? full_ldpk(d, q) : 0)))
     return st;
-  return run_pool(d, q, bs, ld, pool_blocks, pool_count, ws, true, stream);
+  return run_pool(d, q, bs, ld, pool_blocks, pool_count, ws, true, stream, pkey, pkey ? full_ldpk(d, q) : 0,
+                  pkey ? topk_pos : nullptr, pkey ? topk_count : nullptr);
 }
 
 csa2_status csa2_index_full(const csa2_dims* d, const csa2_queries* q, const uint8_t* idx_q, const float* idx_w,
@@ -840,20 +879,10 @@ static csa2_status decode_step(const csa2_dims* d, const csa2_queries* q, int32_
       // from those scores (the layer's own query: what Reindex would compute)
       const size_t n_idx = full_ws(d, q);
       uint32_t* pkey = (uint32_t*)(w_full + n_idx);
-      if ((st = index_full(d, q, idx_q, idx_q_scales, idx_w, idx_k, idx_k_scales, fp4, pool_blocks, pool_count,
-                           nullptr, 0, w_full, n_idx, stream, dry, pages, pkey)))
-        return st;
       if (!topk_pos || !topk_count) return fail(CSA2_ERR_INVALID_ARG, "required pointer is NULL");
-      if (!dry) {
-        TopkKeysArgs ta;
-        ta.pool_blocks = pool_blocks; ta.pool_count = pool_count;
-        ta.bscore = (const float*)(w_full + pool_ws(d, q)); ta.ld = full_ldb(d, q);
-        ta.pkey = pkey; ta.ld_pkey = full_ldpk(d, q);
-        ta.n_q = q->n_q; ta.pool = d->pool_blocks; ta.topk = d->topk;
-        ta.topk_pos = topk_pos; ta.topk_count = topk_count; ta.topk_scores = nullptr;
-        hipError_t e = launch_topk_keys(ta, (hipStream_t)stream);
-        if (e != hipSuccess) return hip_fail(e, "top-k launch");
-      }
+      if ((st = index_full(d, q, idx_q, idx_q_scales, idx_w, idx_k, idx_k_scales, fp4, pool_blocks, pool_count,
+                           nullptr, 0, w_full, n_idx, stream, dry, pages, pkey, topk_pos, topk_count)))
+        return st;
     }
     if (mode == CSA2_LAYER_REINDEX &&
         (st = index_reindex(d, q, idx_q, idx_q_scales, idx_w, idx_k, idx_k_scales, fp4, pool_blocks, pool_count,

@@ -27,6 +27,13 @@ struct PoolArgs {
   bool small;                // every query has <= kPoolSmallBlocks blocks: one-workgroup selection
   int32_t* pool_blocks;      // [n_q, pool]
   int32_t* pool_count;
+  // optional (topk_pos != nullptr, small pools only): the Full layer's
+  // Top-K from the scan's position keys, in the selecting workgroup
+  const uint32_t* pkey;      // [n_q, ld_pkey]
+  int64_t ld_pkey;
+  int topk;
+  int32_t* topk_pos;         // [n_q, topk]
+  int32_t* topk_count;
 };
 
 struct ReindexArgs {

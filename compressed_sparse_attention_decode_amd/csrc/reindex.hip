@@ -28,6 +28,7 @@
 #include "internal.h"
 #include "radix_topk.h"
 #include "select_common.h"
+#include "topk_positions.h"
 
 namespace csa2 {
 namespace {
@@ -373,51 +374,9 @@ __global__ __launch_bounds__(kTkThreads) void k_topk_keys(TopkKeysArgs a) {
     if (flags >> k & 1u) s_blk[before++] = blk[k];     // ascending: the pool is ascending
   __syncthreads();
 
-  // 2. the positions of the selected blocks: thread t takes blocks
-  // [BPT t, BPT (t + 1)) of them, 8 position keys each (0 past c)
-  const uint32_t* pk = a.pkey + (int64_t)q * a.ld_pkey;
-  uint32_t key[PP];
-  int32_t mb[BPT];
-  // (slots past the selection load block 0's keys, a valid row, and clear them)
-#pragma unroll
-  for (int b = 0; b < BPT; ++b) mb[b] = tid * BPT + b < (int)nsel ? s_blk[tid * BPT + b] : 0;
-  v4u x0[BPT], x1[BPT];
-#pragma unroll
-  for (int b = 0; b < BPT; ++b) {
-    x0[b] = *reinterpret_cast<const v4u*>(pk + (int64_t)mb[b] * kBlock);
-    x1[b] = *reinterpret_cast<const v4u*>(pk + (int64_t)mb[b] * kBlock + 4);
-  }
-#pragma unroll
-  for (int b = 0; b < BPT; ++b) {
-    const bool live = tid * BPT + b < (int)nsel;
-    key[8 * b + 0] = live ? x0[b][0] : 0u; key[8 * b + 1] = live ? x0[b][1] : 0u;
-    key[8 * b + 2] = live ? x0[b][2] : 0u; key[8 * b + 3] = live ? x0[b][3] : 0u;
-    key[8 * b + 4] = live ? x1[b][0] : 0u; key[8 * b + 5] = live ? x1[b][1] : 0u;
-    key[8 * b + 6] = live ? x1[b][2] : 0u; key[8 * b + 7] = live ? x1[b][3] : 0u;
-  }
-  const TopkCut cut = radix_topk<PP>(key, K);
-  uint32_t pflags = 0;
-#pragma unroll
-  for (int k = 0; k < PP; ++k) pflags |= (uint32_t)(key[k] >= cut.tt) << k;
-  uint32_t total;
-  uint32_t pos_before = block_exclusive_scan<kTkThreads>(__builtin_popcount(pflags), s_scan, &total);
-  int32_t* out = a.topk_pos + (int64_t)q * K;
-  float* out_s = a.topk_scores ? a.topk_scores + (int64_t)q * K : nullptr;
-#pragma unroll
-  for (int k = 0; k < PP; ++k) {
-    if (pflags >> k & 1u) {
-      if (pos_before < (uint32_t)K) {
-        out[pos_before] = mb[k >> 3] * kBlock + (k & 7);
-        if (out_s) out_s[pos_before] = key_float(key[k]);
-      }
-      ++pos_before;
-    }
-  }
-  for (int t = (int)cut.keff + tid; t < K; t += kTkThreads) {
-    out[t] = -1;
-    if (out_s) out_s[t] = 0.0f;
-  }
-  if (tid == 0) a.topk_count[q] = (int32_t)cut.keff;
+  // 2. the K best positions of those blocks
+  topk_positions<BPT>(s_blk, nsel, a.pkey + (int64_t)q * a.ld_pkey, K, a.topk_pos + (int64_t)q * K,
+                      a.topk_scores ? a.topk_scores + (int64_t)q * K : nullptr, a.topk_count + q, s_scan);
 }
 
 }  // namespace

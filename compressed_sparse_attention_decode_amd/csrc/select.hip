@@ -37,6 +37,7 @@
 #include "internal.h"
 #include "radix_topk.h"
 #include "select_common.h"
+#include "topk_positions.h"
 
 namespace csa2 {
 namespace {
@@ -603,10 +604,17 @@ __global__ __launch_bounds__(kCT) void k_pool_mark(PoolArgs a) {
 // block keys in registers and runs the radix Top-K of radix_topk.h: one
 // launch instead of the histogram and marking kernels.  Same result: the
 // min(P, nb) largest blocks, ties to the lower id, written in ascending order.
+// With BPT > 0 the same workgroup then takes the Full layer's Top-K from the
+// scan's position keys (topk_positions.h): the K best blocks of the pool
+// come from the keys still in its registers (those outside the pool
+// cleared), then the K best of their positions.  BPT = blocks per thread of
+// that step.
 static_assert(kPoolSmallBlocks == kMaxCand, "one key per register slot");
 
+template <int BPT>
 __global__ __launch_bounds__(kTkThreads) void k_pool_small(PoolArgs a) {
   __shared__ uint32_t s_scan[kTkWaves];
+  __shared__ int32_t s_blk[BPT > 0 ? kTkThreads * BPT : 1];
   const int q = blockIdx.x, tid = threadIdx.x;
   const int P = a.pool;
   const float* bs = a.bscore + (int64_t)q * a.ld;
@@ -646,6 +654,29 @@ __global__ __launch_bounds__(kTkThreads) void k_pool_small(PoolArgs a) {
   }
   for (int t = (int)cut.keff + tid; t < P; t += kTkThreads) out[t] = -1;
   if (tid == 0) a.pool_count[q] = (int32_t)cut.keff;
+
+  if constexpr (BPT > 0) {
+    // the K best blocks of the pool (all of it when K exceeds its count):
+    // the keys outside it are cleared first
+    const int K = a.topk;
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) key[k] = key[k] >= cut.tt ? key[k] : 0u;
+    const TopkCut bc = radix_topk(key, K);
+    uint32_t bflags = 0;
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) bflags |= (uint32_t)(key[k] >= bc.tt) << k;
+    uint32_t nsel;
+    uint32_t bb = block_exclusive_scan<kTkThreads>(__builtin_popcount(bflags), s_scan, &nsel);
+    while (bflags) {
+      const int k = __builtin_ctz(bflags);
+      bflags &= bflags - 1;
+      if (bb < (uint32_t)(kTkThreads * BPT)) s_blk[bb] = s0 + k;   // ascending block ids
+      ++bb;
+    }
+    __syncthreads();
+    topk_positions<BPT>(s_blk, min(nsel, (uint32_t)(kTkThreads * BPT)), a.pkey + (int64_t)q * a.ld_pkey, K,
+                        a.topk_pos + (int64_t)q * K, nullptr, a.topk_count + q, s_scan);
+  }
 }
 
 }  // namespace
@@ -660,9 +691,14 @@ size_t pool_final_lds(int nw_cap) { return ((size_t)2 * nw_cap + 2 * kCandCap) *
 
 hipError_t launch_pool_select(const PoolArgs& a, hipStream_t s) {
   if (a.small) {
-    hipLaunchKernelGGL(k_pool_small, dim3((unsigned)a.n_q), dim3(kTkThreads), 0, s, a);
+    const dim3 grid((unsigned)a.n_q), block(kTkThreads);
+    if (!a.topk_pos) hipLaunchKernelGGL(k_pool_small<0>, grid, block, 0, s, a);
+    else if (a.topk <= kTkThreads) hipLaunchKernelGGL(k_pool_small<1>, grid, block, 0, s, a);
+    else if (a.topk <= 2 * kTkThreads) hipLaunchKernelGGL(k_pool_small<2>, grid, block, 0, s, a);
+    else hipLaunchKernelGGL(k_pool_small<4>, grid, block, 0, s, a);
     return hipGetLastError();
   }
+  if (a.topk_pos) return hipErrorInvalidValue;   // the chunked path leaves the Top-K to k_topk_keys
   const dim3 grid((unsigned)(a.n_q * a.chunks));
   const dim3 mgrid((unsigned)(a.n_q * a.mark_wgs));
   const size_t lds = pool_final_lds(a.nw_cap);

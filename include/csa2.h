@@ -273,6 +273,22 @@ csa2_status csa2_index_topk_keys(const csa2_dims* dims, const csa2_queries* q, c
                                  const uint32_t* pos_keys, int64_t ld_pos_keys,
                                  int32_t* topk_pos, int32_t* topk_count, float* topk_scores, void* stream);
 
+/* csa2_index_pool followed by csa2_index_topk_keys on its result, in one
+ * call: the pool (pool_blocks, pool_count) and the Full layer's Top-K
+ * (topk_pos, topk_count) from csa2_index_scan_keys's block scores and
+ * position keys, both as those two calls write them.  When every query has
+ * at most 16,384 blocks (contexts up to about 131K positions) this is one
+ * kernel: the workgroup that selects a query's pool takes its Top-K next,
+ * the K best blocks straight from the keys it holds.  Otherwise the chunked
+ * pool kernels run, then csa2_index_topk_keys's kernel.
+ *   block_scores, pos_keys   as written by csa2_index_scan_keys
+ *   ws, flags                as in csa2_index_pool
+ * Errors as csa2_index_pool and csa2_index_topk_keys. */
+csa2_status csa2_index_pool_topk(const csa2_dims* dims, const csa2_queries* q, const float* block_scores,
+                                 int64_t ld_block_scores, const uint32_t* pos_keys, int64_t ld_pos_keys,
+                                 int32_t* pool_blocks, int32_t* pool_count, int32_t* topk_pos,
+                                 int32_t* topk_count, void* ws, size_t ws_bytes, int32_t flags, void* stream);
+
 /* csa2_index_pool flag: the workspace was passed to the csa2_index_scan call
  * that wrote these block scores, and since then it was used only by
  * csa2_index_pool calls on the same block scores. */
@@ -468,9 +484,8 @@ csa2_status csa2_page_rows(const csa2_pages* pages, int64_t n, const int64_t* ta
  * re-scores the inherited pool with its own indexer query, a Reuse layer
  * only attends over the inherited index set with its own main Q).  The call
  * checks every stage's arguments, then enqueues, on `stream`:
- *   CSA2_LAYER_FULL     csa2_index_scan_keys + csa2_index_pool
- *                       (pool_blocks, pool_count written), then
- *                       csa2_index_topk_keys (topk_pos, topk_count written:
+ *   CSA2_LAYER_FULL     csa2_index_scan_keys + csa2_index_pool_topk
+ *                       (pool_blocks, pool_count, and topk_pos, topk_count:
  *                       the same set as csa2_index_reindex with the same
  *                       indexer query), csa2_attend;
  *   CSA2_LAYER_REINDEX  csa2_index_reindex on the given pool, csa2_attend;

@@ -291,6 +291,37 @@ def test_full_topk_from_scan_keys_matches_reindex(case):
             f"{name} q{qi}: block scores differ with position keys kept"
 
 
+@pytest.mark.parametrize("small", ["1", "0"])
+def test_pool_topk_matches_separate_calls(case, small, monkeypatch):
+    """csa2_index_pool_topk (the pool and the Full layer's Top-K in one call:
+    one kernel for small pools, the chunked kernels then the Top-K kernel
+    otherwise, here forced with CSA2_POOL_SMALL=0) writes the same pool and
+    the same Top-K as csa2_index_pool followed by csa2_index_topk_keys."""
+    name, g, lay = case
+    monkeypatch.setenv("CSA2_POOL_SMALL", small)
+    csa2, w = g.csa2, g.w
+    q, wt = g.iq(0)
+    idx_k = g.planes[0][0]
+    ld = csa2.block_scores_ld(g.dims, g.batch)
+    bs = torch.empty(w.n_q, ld, dtype=torch.float32, device="cuda")
+    pk = torch.empty(w.n_q, csa2.pos_keys_ld(g.dims, g.batch), dtype=torch.int32, device="cuda")
+    pws = torch.zeros(csa2.workspace_pool(g.dims, g.batch) + 256, dtype=torch.uint8, device="cuda")
+    csa2.index_scan(g.dims, g.batch, q, wt, idx_k, bs, pool_ws=pws, pos_keys=pk)
+    pool, cnt = csa2.index_pool(g.dims, g.batch, bs, ws=pws, from_scan=True)
+    tk, tc = csa2.index_topk_keys(g.dims, g.batch, pool, cnt, bs, pk)
+    fill = lambda shape: torch.full(shape, 7, dtype=torch.int32, device="cuda")
+    pool2, cnt2 = fill((w.n_q, w.dims.pool_blocks)), fill((w.n_q,))
+    tk2, tc2 = fill((w.n_q, w.dims.topk)), fill((w.n_q,))
+    csa2.index_pool_topk(g.dims, g.batch, bs, pk, pool2, cnt2, tk2, tc2, ws=pws, from_scan=True)
+    torch.cuda.synchronize()
+    assert torch.equal(cnt, cnt2), f"{name}: pool counts differ"
+    assert torch.equal(tc, tc2), f"{name}: Top-K counts differ"
+    assert torch.equal(tk, tk2), f"{name}: Top-K differs"
+    for qi in range(w.n_q):
+        k = int(cnt[qi])
+        assert torch.equal(pool[qi, :k], pool2[qi, :k]), f"{name} q{qi}: pool differs"
+
+
 def test_pipeline_end_to_end_and_deterministic(case):
     name, g, lay = case
     w = g.w
