@@ -36,6 +36,7 @@ import workloads as wl  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 F16_PEAK_TFLOPS = 2500.0       # MI355X dense fp16 / bf16 matrix, published
+FP8_PEAK_TFLOPS = 5000.0       # MI355X dense fp8 matrix, published
 SCAN_SOURCES = ["compressed_sparse_attention_decode_amd/csrc/scan.hip",
                 "compressed_sparse_attention_decode_amd/csrc/common.h",
                 "compressed_sparse_attention_decode_amd/csrc/scan_args.h"]
@@ -407,7 +408,7 @@ def measure(w: wl.Workload, steps: int, warmup: int, replicas: int):
         "scan": {"bytes_per_launch": per_step, "avg_us": round(scan_us, 3),
                  "achieved_gbs": round(achieved, 1), "frac": round(achieved / HBM_PEAK_GBS, 4),
                  "mfma_tflops": round(scan_flops(w) / (scan_us * 1e-6) / 1e12, 1),
-                 "mfma_frac": round(scan_flops(w) / (scan_us * 1e-6) / 1e12 / F16_PEAK_TFLOPS, 4)},
+                 "mfma_frac": round(scan_flops(w) / (scan_us * 1e-6) / 1e12 / scan_peak_tflops(w), 4)},
         "step_bytes": step_bytes(w),
     }
     res["step_gbs"] = round(res["step_bytes"] / (ms * 1e-3) / 1e9, 1)
@@ -626,13 +627,24 @@ def read_ceiling(steps: int) -> dict:
 
 
 # ---------------------------------------------------------------- records
+def scan_peak_tflops(w: wl.Workload) -> float:
+    """The scan's matrix-core peak: fp8 rows run the fp8 MFMA (5 PFLOP/s
+    dense), FP4 rows the f16 one on exactly converted values (2.5)."""
+    return F16_PEAK_TFLOPS if w.idx_fp4 else FP8_PEAK_TFLOPS
+
+
+def scan_mfma_dtype(w: wl.Workload) -> str:
+    return ("f16 (FP4 rows converted exactly)" if w.idx_fp4
+            else "fp8 e4m3 (v_mfma_scale_f32_16x16x128_f8f6f4, unit scales)")
+
+
 def _is_mfma_bound(w: wl.Workload) -> bool:
     """Tokens of one sequence share each key: the scan does g * 2 H_i d_i
-    flops per key of key_bytes bytes, bound by the f16 matrix cores once that
-    exceeds their ridge, 2.5 PFLOP/s / 8 TB/s = 312.5 flops per byte (one
-    token at d_i = 128: 128)."""
+    flops per key of key_bytes bytes, bound by the matrix cores once that
+    exceeds their ridge, peak / 8 TB/s (fp8 rows: 625 flops per byte; FP4
+    rows on the f16 MFMA: 2.5 PFLOP/s over 72 bytes per key)."""
     per_byte = w.tokens_per_seq * 2 * w.dims.idx_heads * w.dims.idx_dim / key_bytes(w)
-    return per_byte > F16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    return per_byte > scan_peak_tflops(w) * 1e12 / (HBM_PEAK_GBS * 1e9)
 
 
 def record(w: wl.Workload, res: dict) -> dict:
@@ -642,14 +654,15 @@ def record(w: wl.Workload, res: dict) -> dict:
     unit = "query-tokens/s" if w.tokens_per_seq > 1 else "queries/s"
     sc = res["scan"]
     if _is_mfma_bound(w):
-        scan_rl = {"bound": "mfma", "achieved": sc["mfma_tflops"], "peak": F16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                   "frac": sc["mfma_frac"], "dtype": "f16 (exact fp8 / FP4 conversions)",
+        scan_rl = {"bound": "mfma", "achieved": sc["mfma_tflops"], "peak": scan_peak_tflops(w), "unit": "TFLOP/s",
+                   "frac": sc["mfma_frac"], "dtype": scan_mfma_dtype(w),
                    "flops_per_launch": scan_flops(w), "avg_us": sc["avg_us"],
                    "hbm_gbs": sc["achieved_gbs"], "hbm_frac": sc["frac"]}
     else:
         scan_rl = {"bound": "hbm", "achieved": sc["achieved_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                    "frac": sc["frac"], "bytes_per_launch": sc["bytes_per_launch"], "avg_us": sc["avg_us"],
-                   "traffic": measured_traffic(w.name)}
+                   "traffic": measured_traffic(w.name), "mfma_frac": sc["mfma_frac"],
+                   "mfma_dtype": scan_mfma_dtype(w)}
     step_gbs = res["step_bytes"] / (res["ms_per_step"] * 1e-3) / 1e9
     ceiling = w.n_q / (res["step_bytes"] / (HBM_PEAK_GBS * 1e9))
     return {"workload": w.name, "metric": "decode " + unit, "value": round(res["value"], 2), "unit": unit,
@@ -753,8 +766,10 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16",
-        "dtype_detail": "e4m3 indexer keys and E2M1/E4M3 KV, converted exactly to f16 for the MFMAs; fp32 accumulate",
+        "dtype": "fp8+f16",
+        "dtype_detail": ("indexer: e4m3 keys and queries on the fp8 MFMA (exact products, the instruction's own "
+                         "accumulation), fp32 ReLU-weighted head sums; attention: E2M1 x E4M3 KV and bf16 window "
+                         "converted exactly to f16 for the MFMAs, fp32 accumulate and softmax, f16 P"),
         "data": "synthetic (seeded N(0,1) fp8 keys and queries, bf16 latents FP4-encoded, U(0,1) weights)",
         "config": {"workload": w.name, "batch": w.n_seq, "tokens_per_seq": w.tokens_per_seq,
                    "ctx": list(w.ctx), "heads": d.n_heads, "idx_heads": d.idx_heads, "idx_dim": d.idx_dim,

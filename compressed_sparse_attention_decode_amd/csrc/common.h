@@ -14,6 +14,7 @@ typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
 typedef unsigned v2u __attribute__((ext_vector_type(2)));
 
 constexpr int kLatent = 512;           // latent width shared across heads
@@ -74,6 +75,21 @@ __device__ __forceinline__ v8h fp8x8_to_v8h(uint32_t a, uint32_t b) {
   r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
   r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
   return r;
+}
+
+// D += A B^T over 128 E4M3 k-slots with unit block scales (gfx950
+// v_mfma_scale_f32_16x16x128_f8f6f4, E8M0 scale 127 = 1.0): A row = lane
+// & 15, B column = lane & 15, 32 bytes of k-slots per lane; any byte -> k-slot
+// map that A and B share gives the same dot products.  The products are exact
+// (E4M3 x E4M3); the instruction's internal accumulation keeps fewer bits
+// than fp32 (measured: scores within about 3e-5 relative on N(0,1) keys).
+__device__ __forceinline__ v4f mfma_fp8_k128(v8i a, v8i b, v4f c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0x7f7f7f7f, 0, 0x7f7f7f7f);
+}
+
+// Two 16-byte halves as one 32-byte MFMA operand.
+__device__ __forceinline__ v8i cat_v8i(v4u lo, v4u hi) {
+  return __builtin_bit_cast(v8i, (__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7)));
 }
 
 // Eight E2M1 codes (one dword, low nibble = lower channel) times their

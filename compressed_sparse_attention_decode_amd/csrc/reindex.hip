@@ -10,7 +10,9 @@
 // One kernel, k_reindex, with 512-thread workgroups:
 //  * scoring: one workgroup per 64 pool blocks of a query; a wave step
 //    scores two pool blocks (16 positions, two contiguous key runs) with the
-//    same f16-MFMA contraction as the Full scan.  Every key load of the
+//    same contraction as the Full scan (fp8 rows: one fp8 MFMA per 16 heads
+//    on the raw bytes; FP4 rows: f16 MFMAs), so the scores are the scan's
+//    bit for bit.  Every key load of the
 //    workgroup is issued before the first contraction (the work is short and
 //    latency-bound).  Scores are written as order-preserving uint32 keys, 0
 //    marking a slot that holds no candidate position;
@@ -160,8 +162,14 @@ __device__ __forceinline__ void score_part(const ReindexArgs& a, int q, int part
         qf[t][kc] = fp4x8_to_v8h(live ? qraw[t][kc][0] : 0u, v2h{s, s});
       }
     } else {
-#pragma unroll
-      for (int kc = 0; kc < KC; ++kc) qf[t][kc] = fp8x8_to_v8h(live ? qraw[t][kc][0] : 0u, live ? qraw[t][kc][1] : 0u);
+      // raw E4M3 bytes in the keys' byte -> k-slot map (qf[t][0], qf[t][1];
+      // d = 64: the second half zero)
+      const v4u lo = live ? v4u{qraw[t][0][0], qraw[t][0][1], qraw[t][1][0], qraw[t][1][1]} : v4u{0u, 0u, 0u, 0u};
+      v4u hi = {0u, 0u, 0u, 0u};
+      if constexpr (KC == 4)
+        if (live) hi = v4u{qraw[t][2][0], qraw[t][2][1], qraw[t][3][0], qraw[t][3][1]};
+      qf[t][0] = __builtin_bit_cast(v8h, lo);
+      qf[t][1] = __builtin_bit_cast(v8h, hi);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) wv[t][i] = t * 16 + gq * 4 + i < a.hi ? wv[t][i] : 0.0f;
@@ -171,24 +179,33 @@ __device__ __forceinline__ void score_part(const ReindexArgs& a, int q, int part
 #pragma unroll
   for (int u = 0; u < SPW; ++u) {
     const int i = i_begin + 2 * (wave + NW * u) + (col >> 3);
-    v8h kf[KC];
+    // the key operand: f16 fragments (FP4 rows), or the raw E4M3 bytes
+    // (d = 64: the second half zero)
+    v8h kf[F4 ? KC : 1];
+    v8i kr8 = {0, 0, 0, 0, 0, 0, 0, 0};
     if constexpr (F4) {
       const v2h sc = fp4_pair_scales(ksw[u], gq & 1);
       const v2h s0 = {sc[0], sc[0]}, s1 = {sc[1], sc[1]};
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc) kf[kc] = fp4x8_to_v8h(kb[u][kc], kc < 2 ? s0 : s1);
+    } else if constexpr (LB == 32) {
+      kr8 = cat_v8i(v4u{kb[u][0], kb[u][1], kb[u][2], kb[u][3]}, v4u{kb[u][4], kb[u][5], kb[u][6], kb[u][7]});
     } else {
-#pragma unroll
-      for (int kc = 0; kc < KC; ++kc) kf[kc] = fp8x8_to_v8h(kb[u][2 * kc], kb[u][2 * kc + 1]);
+      kr8 = cat_v8i(v4u{kb[u][0], kb[u][1], kb[u][2], kb[u][3]}, v4u{0u, 0u, 0u, 0u});
     }
-    // the Full scan's summation order: four partial sums over the head
-    // tiles, then the lane groups
+    // the Full scan's contraction and summation order: one fp8 MFMA per head
+    // tile (fp8 rows) or four f16 ones (FP4 rows), four partial sums over the
+    // head tiles, then the lane groups
     float pp[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int t = 0; t < HT; ++t) {
       v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
+      if constexpr (F4) {
 #pragma unroll
-      for (int kc = 0; kc < KC; ++kc) acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(qf[t][kc], kf[kc], acc, 0, 0, 0);
+        for (int kc = 0; kc < KC; ++kc) acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(qf[t][kc], kf[kc], acc, 0, 0, 0);
+      } else {
+        acc = mfma_fp8_k128(cat_v8i(__builtin_bit_cast(v4u, qf[t][0]), __builtin_bit_cast(v4u, qf[t][1])), kr8, acc);
+      }
 #pragma unroll
       for (int i = 0; i < 4; ++i) pp[i] += wv[t][i] * fmaxf(acc[i], 0.0f);
     }

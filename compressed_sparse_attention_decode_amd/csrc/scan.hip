@@ -12,18 +12,22 @@
 //  * a wave step covers 16 positions: lane l holds d/4 bytes of key row
 //    (l & 15).  Keys stream with direct-to-LDS raw buffer loads (rows >= c
 //    read as zero, so the tail needs no branches) through a ring of R LDS
-//    slots per wave, R - 1 steps in flight, which costs no VGPRs (the f16
-//    query fragments already hold 64 per lane).  Each load instruction covers
-//    whole 128-byte lines with the nontemporal hint: the keys are read once,
-//    and a line split over two instructions would be fetched twice;
-//  * fp8 keys and queries are converted to f16 in registers (exact) and
-//    contracted with v_mfma_f32_16x16x32_f16: A = 16 query heads, B = 16
-//    positions, K = 32 dims per instruction.  Every product is exact and the
-//    dot products accumulate in fp32 (measured: scores within 2.4e-7 relative
-//    of the exact ones).  The gfx950 fp8 MFMAs (16x16x32 and 16x16x128) keep
-//    fewer bits in their sums: measured score errors up to 3.4e-5 relative on
-//    N(0,1) e4m3 inputs and 1.1e-4 on wide-range ones, above the 1e-5 band
-//    within which selections may differ, so they are not used;
+//    slots per wave, R - 1 steps in flight, which costs no VGPRs.  Each load
+//    instruction covers whole 128-byte lines with the nontemporal hint: the
+//    keys are read once, and a line split over two instructions would be
+//    fetched twice;
+//  * fp8 rows: the raw e4m3 bytes go straight into the gfx950 fp8 MFMA,
+//    v_mfma_scale_f32_16x16x128_f8f6f4 with unit scales (A = 16 query heads,
+//    B = 16 positions, K = 128 dims: one instruction per 16 heads and step;
+//    d = 64 pads K with zeros), so no conversion runs in the loop.  The
+//    products are exact; the instruction's internal accumulation keeps fewer
+//    bits than fp32.  Measured against the exact scores: within 3.4e-5
+//    relative on N(0,1) e4m3 inputs at 128K and 1M positions (1.1e-4 on
+//    wide-range ones), and over 48 queries x 131,072 positions every pool
+//    and Top-512 set either matched the exact one or differed only inside
+//    the 1e-5 band (largest gap of a differing index 3.8e-6 relative).  The
+//    f16 MFMA on exactly converted values (products exact, fp32 sums) stays
+//    within 2.4e-7 but needs 16 conversions and 4x the MFMA issues per step;
 //  * the epilogue applies ReLU and the head weights, reduces over the four
 //    lane groups, masks p >= c, takes the max over 8 lanes (one block), and
 //    one lane per block writes the block score to LDS; the tile's scores
@@ -35,8 +39,9 @@
 // E2M1 codes plus 8 E4M3 scale bytes (one per 16 channels), the query the
 // same per head.  A wave step then moves 1 KiB of codes (lane l: row l & 15,
 // channels 32 (l >> 4) .. +32) and the step's 128 scale bytes into the ring;
-// codes times scale are exact in f16 and feed the same MFMAs.  72 bytes per
-// position.
+// codes times scale are exact in f16 and feed v_mfma_f32_16x16x32_f16 (the
+// fp8f6f4 MFMA takes power-of-two block scales over 32 values, not E4M3
+// scales over 16).  72 bytes per position.
 #include "common.h"
 #include "scan_args.h"
 
@@ -216,23 +221,28 @@ __global__ __launch_bounds__(64 * NW) void k_scan(ScanArgs a) {
       kf[2] = fp4x8_to_v8h(x[2], s1);
       kf[3] = fp4x8_to_v8h(x[3], s1);
     } else {
-      uint32_t kb[4 * NH];
+      // the lane's raw E4M3 bytes (d = 64: 16 of them, the rest zero) in
+      // kf[0], kf[1]; the other fragments are unused
 #pragma unroll
-      for (int h = 0; h < NH; ++h) {
-        const v4u x = *reinterpret_cast<const v4u*>(slot + rd_pos[h] * 16);
-        kb[4 * h + 0] = x[0]; kb[4 * h + 1] = x[1]; kb[4 * h + 2] = x[2]; kb[4 * h + 3] = x[3];
-      }
-#pragma unroll
-      for (int kc = 0; kc < KC; ++kc) kf[kc] = fp8x8_to_v8h(kb[2 * kc], kb[2 * kc + 1]);
+      for (int h = 0; h < NH; ++h)
+        kf[h] = __builtin_bit_cast(v8h, *reinterpret_cast<const v4u*>(slot + rd_pos[h] * 16));
+      if constexpr (NH == 1) kf[1] = __builtin_bit_cast(v8h, (v4u{0u, 0u, 0u, 0u}));
     }
   };
   auto contract = [&](const v8h* kf, v4f* acc) {
 #pragma unroll
     for (int t = 0; t < HT; ++t) acc[t] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    if constexpr (F4) {
 #pragma unroll
-    for (int kc = 0; kc < KC; ++kc) {
+      for (int kc = 0; kc < KC; ++kc) {
 #pragma unroll
-      for (int t = 0; t < HT; ++t) acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qf[t][kc], kf[kc], acc[t], 0, 0, 0);
+        for (int t = 0; t < HT; ++t) acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qf[t][kc], kf[kc], acc[t], 0, 0, 0);
+      }
+    } else {
+      const v8i kb = cat_v8i(__builtin_bit_cast(v4u, kf[0]), __builtin_bit_cast(v4u, kf[1]));
+#pragma unroll
+      for (int t = 0; t < HT; ++t)
+        acc[t] = mfma_fp8_k128(cat_v8i(__builtin_bit_cast(v4u, qf[t][0]), __builtin_bit_cast(v4u, qf[t][1])), kb, acc[t]);
     }
   };
   // last: the wave's final step, the only one that can reach past c (the
@@ -260,8 +270,8 @@ __global__ __launch_bounds__(64 * NW) void k_scan(ScanArgs a) {
   };
 
   // software pipeline: the MFMAs of step k run while the VALU finishes
-  // step k - 1 (epilogue) and prepares step k + 1 (LDS read, fp8 -> f16),
-  // none of which depends on the MFMAs in flight
+  // step k - 1 (epilogue) and prepares step k + 1 (LDS read; FP4: the
+  // conversion to f16), none of which depends on the MFMAs in flight
   // The query (H_i x d fp8, one contiguous block) and the head weights come
   // in by direct-to-LDS loads issued before the first key loads, so they land
   // first: the explicit wait below covers them while the keys stay in flight
@@ -336,12 +346,15 @@ __global__ __launch_bounds__(64 * NW) void k_scan(ScanArgs a) {
         const _Float16 s = kc < 2 ? qsc[0] : qsc[1];
         qf[t][kc] = fp4x8_to_v8h(live ? qx[kc] : 0u, v2h{s, s});
       } else {
-        const v2u x = *reinterpret_cast<const v2u*>(&s_q[min(h, a.hi - 1) * D + key_chunk<D>(gq, kc >> 1) + (kc & 1) * 8]);
-        qf[t][kc] = fp8x8_to_v8h(live ? x[0] : 0u, live ? x[1] : 0u);
+        // raw E4M3 bytes, the keys' byte -> k-slot map: chunk gq (and, for
+        // d = 128, chunk 4 + gq) of 16 bytes in qf[t][0], qf[t][1]
+        v4u x = {0u, 0u, 0u, 0u};
+        if (kc < NH && live) x = *reinterpret_cast<const v4u*>(&s_q[h * D + key_chunk<D>(gq, kc)]);
+        qf[t][kc] = __builtin_bit_cast(v8h, x);
       }
       // keep the converted fragments resident: without this the compiler
       // re-converts them inside the loop to save registers
-      asm volatile("" : "+v"(qf[t][kc]));
+      if (F4 || kc < 2) asm volatile("" : "+v"(qf[t][kc]));
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) wv[t][i] = s_w[t * 16 + gq * 4 + i];

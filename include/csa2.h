@@ -66,8 +66,9 @@ typedef enum csa2_status {
  *   d_latent          512 (the latent shared across heads; [stamatios])
  *   d_rope            64  (the bf16 RoPE key part)
  *   idx_heads    H_i  indexer heads, 1..64 (the scan keeps the query of all
- *                     heads resident in registers as f16 MFMA operands: 64
- *                     VGPRs per lane at 64 heads x 128 dims)
+ *                     heads resident in registers as MFMA operands, 32 VGPRs
+ *                     per lane at 64 heads x 128 dims for fp8 rows and 64
+ *                     for FP4 rows, beside the accumulators)
  *   idx_dim      d_i  indexer key / query width, 64 or 128
  *   block             8   (indexer block size; [atlas] §3.2)
  *   pool_blocks  P    blocks kept by the Full indexer, 1..2048
@@ -199,8 +200,11 @@ csa2_status csa2_encode_fp4(int64_t n, int32_t width, const uint16_t* src, const
 /* Full-mode indexer, stage 1 of 2: the scan ([atlas] §3.2 hierarchical
  * sparse indexer and mode table; [newsaint] §3: the Full layer scores every
  * causally visible position).  For every query:
- *   s_p = sum_h w_h * max(0, q_h . k_p)  for p in [0, c)   (fp8 inputs: the
- *         products exact, the dot products and the weighted sum in fp32)
+ *   s_p = sum_h w_h * max(0, q_h . k_p)  for p in [0, c)   (fp8 inputs on
+ *         the fp8 MFMA: the products exact, each 128-long dot product
+ *         accumulated inside the instruction, which keeps fewer bits than
+ *         fp32 (measured within 3.4e-5 relative of the exact scores on
+ *         N(0,1) e4m3 inputs); the weighted sum over heads in fp32)
  *   b_j = max of s_p over p in [8j, min(8j+8, c)),  j < nb = ceil(c / 8)
  *   idx_q        fp8 [n_q, H_i, d_i]      idx_w  float [n_q, H_i]
  *   idx_k        fp8 [rows, d_i]  (one key per position, shared by heads)
@@ -228,8 +232,9 @@ csa2_status csa2_index_scan(const csa2_dims* dims, const csa2_queries* q,
  *   q_codes  uint8 [n_q, H_i, d_i / 2]   q_scales uint8 [n_q, H_i, d_i / 16]
  *   k_codes  uint8 [rows, d_i / 2]       k_scales uint8 [rows, d_i / 16]
  * Code planes 16-byte aligned, scale planes 8-byte aligned; d_i must be 128
- * (CSA2_ERR_INVALID_ARG otherwise).  The products are exact and the sums
- * fp32, as for fp8 rows. */
+ * (CSA2_ERR_INVALID_ARG otherwise).  Codes times scales are exact in f16 and
+ * run the f16 MFMA: the products exact, the sums fp32 (scores within about
+ * 2.4e-7 relative of the exact ones). */
 csa2_status csa2_index_scan_fp4(const csa2_dims* dims, const csa2_queries* q,
                                 const uint8_t* q_codes, const uint8_t* q_scales, const float* idx_w,
                                 const uint8_t* k_codes, const uint8_t* k_scales,
