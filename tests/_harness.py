@@ -161,3 +161,21 @@ def with_oracle_rows(tk: torch.Tensor, tc: torch.Tensor, rows: dict):
             tk2[qi, :len(keep)] = torch.as_tensor(np.asarray(keep, dtype=np.int32), device=tk.device)
         tc2[qi] = len(keep)
     return tk2, tc2
+
+
+def with_oracle_pool(pool: torch.Tensor, cnt: torch.Tensor, rows: dict):
+    """Copies of the library's pool_blocks / pool_count in which the queries
+    in `rows` (query -> oracle pool, ascending block ids) carry the oracle's
+    own pool.  When the library's pool differs from the oracle's inside the
+    selection band, a later layer's Reindex on the two pools can differ by
+    more than the band (its query is not the one that ranked the blocks), so
+    its Top-K is compared with the oracle's by running the library's Reindex
+    on the oracle's pool (oracle outputs feed the library, never the other
+    way round)."""
+    p2, c2 = pool.clone(), cnt.clone()
+    for qi, rp in rows.items():
+        p2[qi].fill_(-1)
+        if len(rp):
+            p2[qi, :len(rp)] = torch.as_tensor(np.asarray(rp, dtype=np.int32), device=pool.device)
+        c2[qi] = len(rp)
+    return p2, c2

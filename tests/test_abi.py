@@ -107,14 +107,19 @@ def test_documented_dims_accepted(good):
         assert st == OK, L.csa2_last_error()
 
 
-def test_attention_workspace_pads_heads_to_16():
-    """Attention partials are laid out in 16-head blocks: 24 heads take as
-    much workspace as 32."""
+def test_attention_workspace_pads_heads_to_32():
+    """Attention partials are laid out in 32-head workgroup blocks: 8, 24 and
+    32 heads take the same workspace, 40 heads that of 64; a batch that fills
+    the chip with one workgroup per (query, head group) needs none."""
     L = csa2.lib()
-    st, w24 = _call_ws(L.csa2_attend_workspace_size, _dims(n_heads=24), _batch(n_q=1))
-    assert st == OK
-    st, w32 = _call_ws(L.csa2_attend_workspace_size, _dims(n_heads=32), _batch(n_q=1))
-    assert st == OK and w24 == w32 > 0
+    sizes = {}
+    for h in (8, 24, 32, 40, 64):
+        st, sizes[h] = _call_ws(L.csa2_attend_workspace_size, _dims(n_heads=h), _batch(n_q=1))
+        assert st == OK
+    assert sizes[8] == sizes[24] == sizes[32] > 0
+    assert sizes[40] == sizes[64] > sizes[32]
+    st, big = _call_ws(L.csa2_attend_workspace_size, _dims(n_heads=64), _batch(n_q=128))
+    assert st == OK and big == 0
 
 
 def test_block_score_stride_at_least_four():

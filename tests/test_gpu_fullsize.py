@@ -20,7 +20,8 @@ import torch
 
 import oracle
 import workloads as wl
-from tests._harness import OracleQuery, check_attention, check_set, lib, u8, u16, with_oracle_rows
+from tests._harness import (OracleQuery, check_attention, check_set, lib, u8, u16, with_oracle_pool,
+                            with_oracle_rows)
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
@@ -64,12 +65,20 @@ def test_full_size_step(name):
         got_pool = pool[qi, :pcnt[qi]]
         check_set(got_pool, rpool, lambda j: rb[j], f"{name} q{qi} pool")
         assert np.all(pool[qi, pcnt[qi]:] == -1)
+        same_pool = np.array_equal(got_pool, rpool)
         for i, layer in enumerate(step.layers):
             keep, _, _ = oq.reindex(layer, rpool)
             got = tk[i, qi, :tc[i, qi]]
+            if not same_pool:
+                # the pools differ inside the band: this layer's Top-K from the
+                # library's Reindex (this layer's query) on the oracle's pool
+                p2, c2 = with_oracle_pool(step.pool, step.pcnt, {qi: rpool})
+                tk_o, tc_o, _ = st.reindex(layer, p2, c2)
+                torch.cuda.synchronize()
+                got = tk_o[qi, :int(tc_o[qi])].cpu().numpy()
             check_set(got, keep, lambda p: oq.scores_at(layer, p), f"{name} q{qi} layer {layer} topk")
             ro, rl = oq.attention(layer, keep)
-            if np.array_equal(got, keep):
+            if same_pool and np.array_equal(got, keep):
                 o_q, l_q = out[i, qi], lse[i, qi]
             else:
                 # the same attention call on the oracle's own Top-K

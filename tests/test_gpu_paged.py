@@ -10,7 +10,7 @@ import pytest
 import torch
 
 import workloads as wl
-from tests._harness import GpuCase, OracleQuery, check_attention, check_set, with_oracle_rows
+from tests._harness import GpuCase, OracleQuery, check_attention, check_set, with_oracle_pool, with_oracle_rows
 from tests.test_gpu_parity import BIG, small
 
 pytestmark = pytest.mark.gpu
@@ -109,9 +109,16 @@ def test_paged_reindex_and_attention_match_contiguous(case):
     check_set(pool.cpu().numpy()[qi, :int(cnt[qi])], rpool, lambda j: rb[j], f"{name} pool")
     keep, _, _ = oq.reindex(0, rpool)
     got = tk2.cpu().numpy()[qi, :int(tc2[qi])]
+    same_pool = np.array_equal(pool.cpu().numpy()[qi, :int(cnt[qi])], rpool)
+    if not same_pool:
+        # pools that differ inside the band: the paged Reindex on the oracle's pool
+        p3, c3 = with_oracle_pool(pool, cnt, {qi: rpool})
+        tk2, tc2 = csa2.index_reindex(g.dims, pg.batch, q, wt, pg.idx_k, p3, c3, pages=pg.pages)
+        torch.cuda.synchronize()
+        got = tk2.cpu().numpy()[qi, :int(tc2[qi])]
     check_set(got, keep, lambda x: oq.scores_at(0, x), f"{name} paged topk")
     ref_o, ref_l = oq.attention(0, keep)
-    if not np.array_equal(got, keep):
+    if not same_pool or not np.array_equal(got, keep):
         # the paged attention on the oracle's own Top-K
         tk3, tc3 = with_oracle_rows(tk2, tc2, {qi: keep})
         out2, lse2 = csa2.attend(g.dims, pg.batch, ql, qr, 1.0, pg.codes, pg.scales, pg.kv_rope, tk3, tc3, swa_kv,

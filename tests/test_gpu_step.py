@@ -11,7 +11,7 @@ import pytest
 import torch
 
 import workloads as wl
-from tests._harness import GpuCase, OracleQuery, check_attention, check_set, lib, with_oracle_rows
+from tests._harness import GpuCase, OracleQuery, check_attention, check_set, lib, with_oracle_pool, with_oracle_rows
 from tests.test_gpu_parity import CASES
 
 pytestmark = pytest.mark.gpu
@@ -82,6 +82,13 @@ def test_step_modes_match_stage_calls(name):
         check_set(bufs["pool_blocks"][qi, :int(cnt[qi])].cpu().numpy(), rpool, lambda j: rb[j], f"{name} q{qi} step pool")
         keep, _, _ = oq.reindex(0, rpool)
         got = bufs["topk_pos"][qi, :int(tc[qi])].cpu().numpy()
+        if not np.array_equal(bufs["pool_blocks"][qi, :int(cnt[qi])].cpu().numpy(), rpool):
+            # pools that differ inside the band: the Top-K of the library's
+            # Reindex (this layer's query) on the oracle's pool
+            p2, c2 = with_oracle_pool(pool, cnt, {qi: rpool})
+            tk_o, tc_o, _ = g.reindex(0, p2, c2)
+            torch.cuda.synchronize()
+            got = tk_o[qi, :int(tc_o[qi])].cpu().numpy()
         check_set(got, keep, lambda p, oq=oq: oq.scores_at(0, p), f"{name} q{qi} step topk")
         ro, rl = oq.attention(0, keep)
         if np.array_equal(got, keep):
