@@ -35,10 +35,11 @@ static_assert(kTkBins == 4 * kTkThreads, "one 16-byte histogram clear per thread
 // need = min(want, total).  Writes out[0] = the bin where the count from the
 // top first reaches need, out[1] = keys in higher bins, out[2] = keys in that
 // bin (out[0..2] only if need > 0), out[3] = need, out[4] = total.  Each lane
-// owns 32 consecutive bins, read with 16-byte LDS loads.  Called by wave 0.
+// owns 32 consecutive bins, read with 16-byte LDS loads.  Called by one whole
+// wave.
 __device__ __forceinline__ void crossing_2048(const uint32_t* hist, uint32_t want, uint32_t* out) {
   constexpr int kPB = kTkBins / 64;
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63;
   const int first = kTkBins - kPB * (lane + 1);     // lane 0 holds the highest bins
   uint32_t c[kPB];
 #pragma unroll
@@ -83,21 +84,29 @@ __device__ __forceinline__ void crossing_2048(const uint32_t* hist, uint32_t wan
 // What the caller needs to emit the selection: keff = min(K, valid keys),
 // and each thread's selected keys are exactly those with key[k] >= tt (the
 // thread straddling the tie cut has had its excluded equal keys cleared).
+// With a second rank K2 > 0, lb2 is a lower bound of the K2-th largest key
+// read off the first histogram (the lower edge of its bin; every key when
+// K2 covers them all), and n2 counts the keys >= lb2, so n2 >= min(K2, valid
+// keys).  Without one, lb2 = 0 and n2 = 0.
 struct TopkCut {
   uint32_t keff;
   uint32_t tt;
+  uint32_t lb2;
+  uint32_t n2;
 };
 
 // All 512 threads call this with their PER keys (PER <= 32; thread t holds
 // slots [PER t, PER (t + 1)); slots past the valid range already 0).
-// Contains barriers; K >= 1.  Each PER has its own LDS.
+// Contains barriers; K >= 1, K2 >= 0 (0: no second rank).  Each PER has its
+// own LDS.
 template <int PER = kPer>
-__device__ __forceinline__ TopkCut radix_topk(uint32_t (&key)[PER], int K) {
+__device__ __forceinline__ TopkCut radix_topk(uint32_t (&key)[PER], int K, int K2 = 0) {
   static_assert(PER >= 1 && PER <= 32, "a 32-bit candidate mask per thread");
   __shared__ __align__(16) uint32_t s_hist[kTkBins + kTkEmpty];
   __shared__ uint64_t s_cand[kRankCap];
   __shared__ uint32_t s_red[2 * kTkWaves];
   __shared__ uint32_t s_misc[8];
+  __shared__ uint32_t s_misc2[5];
 
   const int tid = threadIdx.x, lane = tid & 63;
 
@@ -116,7 +125,7 @@ __device__ __forceinline__ TopkCut radix_topk(uint32_t (&key)[PER], int K) {
   block_minmax_u32<kTkThreads>(&lo, &hi, s_red);   // its barriers also order the clears
   const uint32_t kmin = lo + 1u, kmax = hi;
 
-  uint32_t keff = 0;
+  uint32_t keff = 0, lb2 = 0, n2 = 0;
   uint32_t T = 0xFFFFFFFFu;                  // threshold key (no finite score has it)
   int ST = 0x7FFFFFFF;                       // keys == T at slots <= ST are selected
   if (kmax != 0) {
@@ -129,8 +138,13 @@ __device__ __forceinline__ TopkCut radix_topk(uint32_t (&key)[PER], int K) {
     }
     __syncthreads();
     if (tid < 64) crossing_2048(s_hist, (uint32_t)K, s_misc);
+    else if (tid < 128 && K2 > 0) crossing_2048(s_hist, (uint32_t)K2, s_misc2);
     __syncthreads();
     keff = s_misc[3];
+    if (K2 > 0 && s_misc2[3] > 0) {
+      lb2 = kmin + (s_misc2[0] << shift);
+      n2 = s_misc2[1] + s_misc2[2];
+    }
     uint32_t need = keff - s_misc[1];         // keys still to take from the crossing bin
     uint32_t cand = s_misc[2];
     uint32_t blo = kmin + (s_misc[0] << shift);    // the crossing bin is [blo, blo + 2^shift)
@@ -224,7 +238,7 @@ __device__ __forceinline__ TopkCut radix_topk(uint32_t (&key)[PER], int K) {
 #pragma unroll
     for (int k = 0; k < PER; ++k) key[k] = (key[k] == T && s0 + k > ST) ? 0u : key[k];
   }
-  return TopkCut{keff, Tt};
+  return TopkCut{keff, Tt, lb2, n2};
 }
 
 }  // namespace csa2

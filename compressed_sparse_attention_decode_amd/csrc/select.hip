@@ -605,16 +605,21 @@ __global__ __launch_bounds__(kCT) void k_pool_mark(PoolArgs a) {
 // launch instead of the histogram and marking kernels.  Same result: the
 // min(P, nb) largest blocks, ties to the lower id, written in ascending order.
 // With BPT > 0 the same workgroup then takes the Full layer's Top-K from the
-// scan's position keys (topk_positions.h): the K best blocks of the pool
-// come from the keys still in its registers (those outside the pool
-// cleared), then the K best of their positions.  BPT = blocks per thread of
-// that step.
+// scan's position keys (topk_positions.h).  Its candidate blocks are the
+// pool's blocks at or above the lower edge of the first histogram's bin that
+// holds the K-th best block: a superset of the K best blocks (ties to the
+// lower id), so their positions hold the K best positions, and kept in
+// ascending order so that slot order is position order for the ties.  Only
+// when that bin is so crowded that the candidates exceed the BPT blocks per
+// thread of the positions step does a second radix select pick exactly the
+// K best blocks of the pool (the keys outside it cleared first).
 static_assert(kPoolSmallBlocks == kMaxCand, "one key per register slot");
 
 template <int BPT>
 __global__ __launch_bounds__(kTkThreads) void k_pool_small(PoolArgs a) {
   __shared__ uint32_t s_scan[kTkWaves];
   __shared__ int32_t s_blk[BPT > 0 ? kTkThreads * BPT : 1];
+  constexpr uint32_t kCap = kTkThreads * BPT;       // candidate blocks of the positions step
   const int q = blockIdx.x, tid = threadIdx.x;
   const int P = a.pool;
   const float* bs = a.bscore + (int64_t)q * a.ld;
@@ -639,13 +644,22 @@ __global__ __launch_bounds__(kTkThreads) void k_pool_small(PoolArgs a) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) key[4 * v + e] = s0 + 4 * v + e < nb ? order_key(x[v][e]) : 0u;
   }
-  const TopkCut cut = radix_topk(key, P);
+  const int K = a.topk;
+  const TopkCut cut = radix_topk(key, P, BPT > 0 ? K : 0);
 
-  uint32_t flags = 0;
+  // pool members, and (BPT > 0) the candidate blocks of the Top-K: both
+  // offsets from one block scan (16-bit fields: at most 16,384 of each)
+  uint32_t flags = 0, cflags = 0;
 #pragma unroll
-  for (int k = 0; k < kPer; ++k) flags |= (uint32_t)(key[k] >= cut.tt) << k;
+  for (int k = 0; k < kPer; ++k) {
+    const bool in = key[k] >= cut.tt;
+    flags |= (uint32_t)in << k;
+    if constexpr (BPT > 0) cflags |= (uint32_t)(in && key[k] >= cut.lb2) << k;
+  }
   uint32_t total;
-  uint32_t before = block_exclusive_scan<kTkThreads>(__builtin_popcount(flags), s_scan, &total);
+  const uint32_t packed = block_exclusive_scan<kTkThreads>(
+      __builtin_popcount(flags) | (uint32_t)__builtin_popcount(cflags) << 16, s_scan, &total);
+  uint32_t before = packed & 0xFFFFu;
   while (flags) {
     const int k = __builtin_ctz(flags);
     flags &= flags - 1;
@@ -656,26 +670,37 @@ __global__ __launch_bounds__(kTkThreads) void k_pool_small(PoolArgs a) {
   if (tid == 0) a.pool_count[q] = (int32_t)cut.keff;
 
   if constexpr (BPT > 0) {
-    // the K best blocks of the pool (all of it when K exceeds its count):
-    // the keys outside it are cleared first
-    const int K = a.topk;
-#pragma unroll
-    for (int k = 0; k < kPer; ++k) key[k] = key[k] >= cut.tt ? key[k] : 0u;
-    const TopkCut bc = radix_topk(key, K);
-    uint32_t bflags = 0;
-#pragma unroll
-    for (int k = 0; k < kPer; ++k) bflags |= (uint32_t)(key[k] >= bc.tt) << k;
+    const uint32_t ncand = total >> 16;
     uint32_t nsel;
-    uint32_t bb = block_exclusive_scan<kTkThreads>(__builtin_popcount(bflags), s_scan, &nsel);
-    while (bflags) {
-      const int k = __builtin_ctz(bflags);
-      bflags &= bflags - 1;
-      if (bb < (uint32_t)(kTkThreads * BPT)) s_blk[bb] = s0 + k;   // ascending block ids
-      ++bb;
+    if (ncand <= kCap) {
+      uint32_t cb = packed >> 16;
+      while (cflags) {
+        const int k = __builtin_ctz(cflags);
+        cflags &= cflags - 1;
+        s_blk[cb++] = s0 + k;                      // ascending block ids
+      }
+      nsel = ncand;
+    } else {
+      // the exact K best blocks of the pool (all of it when K exceeds its
+      // count)
+#pragma unroll
+      for (int k = 0; k < kPer; ++k) key[k] = key[k] >= cut.tt ? key[k] : 0u;
+      const TopkCut bc = radix_topk(key, K);
+      uint32_t bflags = 0;
+#pragma unroll
+      for (int k = 0; k < kPer; ++k) bflags |= (uint32_t)(key[k] >= bc.tt) << k;
+      uint32_t bb = block_exclusive_scan<kTkThreads>(__builtin_popcount(bflags), s_scan, &nsel);
+      while (bflags) {
+        const int k = __builtin_ctz(bflags);
+        bflags &= bflags - 1;
+        if (bb < kCap) s_blk[bb] = s0 + k;         // ascending block ids
+        ++bb;
+      }
+      nsel = min(nsel, kCap);
     }
     __syncthreads();
-    topk_positions<BPT>(s_blk, min(nsel, (uint32_t)(kTkThreads * BPT)), a.pkey + (int64_t)q * a.ld_pkey, K,
-                        a.topk_pos + (int64_t)q * K, nullptr, a.topk_count + q, s_scan);
+    topk_positions<BPT>(s_blk, nsel, a.pkey + (int64_t)q * a.ld_pkey, K, a.topk_pos + (int64_t)q * K, nullptr,
+                        a.topk_count + q, s_scan);
   }
 }
 
@@ -692,9 +717,10 @@ size_t pool_final_lds(int nw_cap) { return ((size_t)2 * nw_cap + 2 * kCandCap) *
 hipError_t launch_pool_select(const PoolArgs& a, hipStream_t s) {
   if (a.small) {
     const dim3 grid((unsigned)a.n_q), block(kTkThreads);
+    // twice K's blocks where K allows: room for the crossing bin's extra
+    // candidates (K <= 2048 = kTkThreads * 4 in any case)
     if (!a.topk_pos) hipLaunchKernelGGL(k_pool_small<0>, grid, block, 0, s, a);
-    else if (a.topk <= kTkThreads) hipLaunchKernelGGL(k_pool_small<1>, grid, block, 0, s, a);
-    else if (a.topk <= 2 * kTkThreads) hipLaunchKernelGGL(k_pool_small<2>, grid, block, 0, s, a);
+    else if (a.topk <= kTkThreads) hipLaunchKernelGGL(k_pool_small<2>, grid, block, 0, s, a);
     else hipLaunchKernelGGL(k_pool_small<4>, grid, block, 0, s, a);
     return hipGetLastError();
   }

@@ -450,6 +450,61 @@ def test_outlier_score_narrows_the_range(pool_path):
         check_set(tk.cpu().numpy()[0, :tc.item()], keep, lambda p: oq.scores_at(0, p), "outlier topk")
 
 
+def _full_topk(g):
+    """csa2_index_scan keeping the position keys, then csa2_index_pool_topk:
+    the pool and a Full layer's Top-K of query 0."""
+    csa2, w = g.csa2, g.w
+    q, wt = g.iq(0)
+    bs = torch.empty(w.n_q, csa2.block_scores_ld(g.dims, g.batch), dtype=torch.float32, device="cuda")
+    pk = torch.empty(w.n_q, csa2.pos_keys_ld(g.dims, g.batch), dtype=torch.int32, device="cuda")
+    pws = torch.zeros(csa2.workspace_pool(g.dims, g.batch) + 256, dtype=torch.uint8, device="cuda")
+    csa2.index_scan(g.dims, g.batch, q, wt, g.planes[0][0], bs, pool_ws=pws, pos_keys=pk)
+    pool, cnt, tk, tc = csa2.index_pool_topk(g.dims, g.batch, bs, pk, ws=pws, from_scan=True)
+    torch.cuda.synchronize()
+    return pool.cpu().numpy()[0, :cnt.item()], tk.cpu().numpy()[0, :tc.item()]
+
+
+@pytest.mark.parametrize("pool_blocks,topk", [(256, 512), (2048, 512), (2048, 1024)])
+def test_pool_topk_all_scores_equal(pool_blocks, topk, pool_path):
+    """Every score ties: the first histogram's crossing bin holds every block,
+    so the Full layer's Top-K candidates are the whole pool.  With a pool
+    larger than the positions step takes (2048 blocks against 1024 or 2048
+    slots) the exact second block selection runs; the Top-K is then the
+    lowest K positions of the lowest blocks, as the oracle's."""
+    dims = wl.Dims(n_heads=16, idx_heads=16, idx_dim=128, pool_blocks=pool_blocks, topk=topk)
+    w = small(113, dims, [40000])
+    g = GpuCase(w)
+    oq = OracleQuery(w, wl.layout(w), 0)
+    _set_key_rows(oq, g, slice(None), oq.keys[5].copy())
+    rpool, _, _ = oq.full(0)
+    keep, _, _ = oq.reindex(0, rpool)
+    assert np.array_equal(keep, np.arange(topk))
+    pool, tk = _full_topk(g)
+    assert np.array_equal(pool, rpool)
+    assert np.array_equal(tk, keep)
+
+
+def test_pool_topk_outlier(pool_path):
+    """One far outlier stretches the block-score range, so the first
+    histogram's bins are coarse: the Full layer's Top-K candidates (the
+    pool's blocks from the K-th best block's bin up) are a strict superset of
+    the K best blocks (513 for K = 512 on this input)."""
+    dims = wl.Dims(n_heads=16, idx_heads=64, idx_dim=128, pool_blocks=2048, topk=512)
+    w = small(112, dims, [40000])
+    g = GpuCase(w)
+    oq = OracleQuery(w, wl.layout(w), 0)
+    q, wt = oq.iq(0)
+    qs = (wt[:, None] * oracle.e4m3_decode(q)).sum(0)
+    _set_key_rows(oq, g, 777, np.where(qs >= 0, 0x7E, 0xFE).astype(np.uint8))
+    _set_key_rows(oq, g, 776, np.zeros(128, np.uint8))
+    rpool, rb, _ = oq.full(0)
+    pool, tk = _full_topk(g)
+    check_set(pool, rpool, lambda j: rb[j], "outlier pool")
+    if np.array_equal(pool, rpool):
+        keep, _, _ = oq.reindex(0, rpool)
+        check_set(tk, keep, lambda p: oq.scores_at(0, p), "outlier full topk")
+
+
 def test_pool_paths_agree(case):
     """csa2_index_full (scan-prepared pool workspace), csa2_index_scan +
     csa2_index_pool (the pool's own key-range pass), repeated pool calls on
