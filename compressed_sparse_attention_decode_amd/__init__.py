@@ -101,6 +101,8 @@ def lib() -> ctypes.CDLL:
             "csa2_index_scan_keys": (I32, [PD, PQ, PP, P, P, P, P, P, P, I64, P, I64, P, SZ, P]),
             "csa2_index_topk_keys": (I32, [PD, PQ, P, P, P, I64, P, I64, P, P, P, P]),
             "csa2_index_pool_topk": (I32, [PD, PQ, P, I64, P, I64, P, P, P, P, P, SZ, I32, P]),
+            "csa2_pool_topk_attend": (I32, [PD, PQ, P, I64, P, I64, P, P, P, P, P, P, ctypes.c_float, P, P, P,
+                                            P, P, P, P, P, SZ, P]),
             "csa2_decode_step_noalloc": (I32, [PD, PQ, I32, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_float,
                                                P, P, P, P, P, P, P, P]),
         }
@@ -603,6 +605,60 @@ def attend(dims: Dims, b: Batch, q_lat: torch.Tensor, q_rope: torch.Tensor, soft
         return call if prepare else (out, lse)
     call = _issue(lib().csa2_attend, args, (d, q, ws), prepare)
     return call if prepare else (out, lse)
+
+
+def pool_topk_attend(dims: Dims, b: Batch, block_scores: torch.Tensor, pos_keys: torch.Tensor,
+                     q_lat: torch.Tensor, q_rope: torch.Tensor, softmax_scale: float,
+                     kv_codes: torch.Tensor, kv_scales: torch.Tensor, kv_rope: torch.Tensor,
+                     swa_kv: torch.Tensor, swa_base: torch.Tensor,
+                     pool_blocks: Optional[torch.Tensor] = None, pool_count: Optional[torch.Tensor] = None,
+                     topk_pos: Optional[torch.Tensor] = None, topk_count: Optional[torch.Tensor] = None,
+                     out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                     ws: Optional[torch.Tensor] = None, want_lse: bool = True, prepare: bool = False):
+    """The pool, the Full layer's Top-K and the attention on it, the
+    selection inside the attention kernel (csa2_pool_topk_attend; queries of
+    at most 16,384 blocks).  Returns (pool_blocks, pool_count, topk_pos,
+    topk_count, out, lse)."""
+    dev = q_lat.device
+    _dev(block_scores, pos_keys, q_lat, q_rope, kv_codes, kv_scales, kv_rope, swa_kv, swa_base, pool_blocks,
+         pool_count, topk_pos, topk_count, out, lse)
+    n_q, H = b.n_q, dims.n_heads
+    if block_scores.dtype != torch.float32 or block_scores.dim() != 2 or block_scores.shape[0] != n_q:
+        raise ValueError("block_scores must be float32 [n_q, ld]")
+    if pos_keys.dim() != 2 or pos_keys.shape[0] != n_q or pos_keys.element_size() != 4:
+        raise ValueError("pos_keys must be 32-bit [n_q, ld]")
+    if q_lat.shape != (n_q, H, 512) or q_rope.shape != (n_q, H, 64):
+        raise ValueError("q_lat / q_rope shape mismatch")
+    if q_lat.dtype != torch.bfloat16 or q_rope.dtype != torch.bfloat16 or swa_kv.dtype != torch.bfloat16:
+        raise TypeError("q_lat, q_rope and swa_kv must be bfloat16")
+    if swa_base.dtype != torch.int64 or swa_base.shape != (n_q,):
+        raise ValueError("swa_base must be int64 [n_q]")
+    if swa_kv.dim() != 2 or swa_kv.shape[1] != 576:
+        raise ValueError("swa_kv must be [rows, 576]")
+    if pool_blocks is None:
+        pool_blocks = torch.empty(n_q, dims.pool_blocks, dtype=torch.int32, device=dev)
+    if pool_count is None:
+        pool_count = torch.empty(n_q, dtype=torch.int32, device=dev)
+    if topk_pos is None:
+        topk_pos = torch.empty(n_q, dims.topk, dtype=torch.int32, device=dev)
+    if topk_count is None:
+        topk_count = torch.empty(n_q, dtype=torch.int32, device=dev)
+    if pool_blocks.shape != (n_q, dims.pool_blocks) or topk_pos.shape != (n_q, dims.topk):
+        raise ValueError("pool_blocks / topk_pos shape mismatch")
+    if out is None:
+        out = torch.empty(n_q, H, 512, dtype=torch.float32, device=dev)
+    if lse is None and want_lse:
+        lse = torch.empty(n_q, H, dtype=torch.float32, device=dev)
+    ws = _workspace(workspace_attend(dims, b), dev, ws)
+    wp, wn = _ws_ptr(ws)
+    d, q = dims.c(), b.c()
+    args = (ctypes.byref(d), ctypes.byref(q), block_scores.data_ptr(), block_scores.shape[1], pos_keys.data_ptr(),
+            pos_keys.shape[1], pool_blocks.data_ptr(), pool_count.data_ptr(), topk_pos.data_ptr(),
+            topk_count.data_ptr(), q_lat.data_ptr(), q_rope.data_ptr(), float(softmax_scale), kv_codes.data_ptr(),
+            kv_scales.data_ptr(), kv_rope.data_ptr(), swa_kv.data_ptr(), swa_base.data_ptr(), out.data_ptr(),
+            _ptr(lse), wp, wn, _stream(dev))
+    call = _issue(lib().csa2_pool_topk_attend, args, (d, q, ws), prepare)
+    return call if prepare else (pool_blocks, pool_count, topk_pos, topk_count, out, lse)
 
 
 LAYER_FULL, LAYER_REINDEX, LAYER_REUSE = 0, 1, 2

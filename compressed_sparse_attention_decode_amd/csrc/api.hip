@@ -588,7 +588,7 @@ static csa2_status index_full(const csa2_dims* d, const csa2_queries* q, const u
                               int32_t* pool_blocks, int32_t* pool_count, float* block_scores, int64_t ld_block_scores,
                               void* ws, size_t ws_bytes, void* stream, bool dry = false,
                               const csa2_pages* pages = nullptr, uint32_t* pkey = nullptr,
-                              int32_t* topk_pos = nullptr, int32_t* topk_count = nullptr) {
+                              int32_t* topk_pos = nullptr, int32_t* topk_count = nullptr, bool scan_only = false) {
   csa2_status st = check_dims(d);
   if (st) return st;
   if ((st = check_queries(q))) return st;
@@ -609,6 +609,7 @@ static csa2_status index_full(const csa2_dims* d, const csa2_queries* q, const u
   if ((st = run_scan(d, q, idx_q, fp4 ? q_scales : nullptr, idx_w, idx_k, fp4 ? k_scales : nullptr, bs, ld,
                      (uint32_t*)ws, stream, pages, pkey, pkey ? full_ldpk(d, q) : 0)))
     return st;
+  if (scan_only) return CSA2_OK;
   return run_pool(d, q, bs, ld, pool_blocks, pool_count, ws, true, stream, pkey, pkey ? full_ldpk(d, q) : 0,
                   pkey ? topk_pos : nullptr, pkey ? topk_count : nullptr);
 }
@@ -725,15 +726,45 @@ csa2_status csa2_attend_workspace_size(const csa2_dims* d, const csa2_queries* q
   return CSA2_OK;
 }
 
+// The pool and the Full layer's Top-K selected inside the attention kernel
+// (csa2_pool_topk_attend): the scan's scores in, the selection out.
+struct AttendSel {
+  const float* block_scores;
+  int64_t ld_block_scores;
+  const uint32_t* pos_keys;
+  int64_t ld_pos_keys;
+  int32_t* pool_blocks;
+  int32_t* pool_count;
+};
+
+// Whether every query's pool fits one selecting workgroup (and the
+// chunked kernels are not forced with CSA2_POOL_SMALL=0).
+static bool pool_small(const csa2_dims* d, const csa2_queries* q) {
+  bool small = max_blocks(d, q) <= kPoolSmallBlocks;
+  if (const char* env = getenv("CSA2_POOL_SMALL")) small = small && atoi(env) != 0;
+  return small;
+}
+
 static csa2_status attend(const csa2_dims* d, const csa2_queries* q, const uint16_t* q_lat, const uint16_t* q_rope,
                           float softmax_scale, const uint8_t* kv_codes, const uint8_t* kv_scales,
                           const uint16_t* kv_rope, const int32_t* topk_pos, const int32_t* topk_count,
                           const uint16_t* swa_kv, const int64_t* swa_base, float* out, float* lse, void* ws,
-                          size_t ws_bytes, void* stream, bool dry = false, const csa2_pages* pages = nullptr) {
+                          size_t ws_bytes, void* stream, bool dry = false, const csa2_pages* pages = nullptr,
+                          const AttendSel* sel = nullptr) {
   csa2_status st = check_dims(d);
   if (st) return st;
   if ((st = check_queries(q))) return st;
   if (pages && (st = check_pages(pages, 256))) return st;   // kv_codes: the widest plane
+  if (sel) {
+    if (pages) return fail(CSA2_ERR_UNSUPPORTED, "the in-kernel selection takes unpaged planes");
+    if (!pool_small(d, q))
+      return fail(CSA2_ERR_UNSUPPORTED, "the in-kernel selection takes at most %d blocks per query (max_visible %lld)",
+                  kPoolSmallBlocks, (long long)q->max_visible);
+    if (!sel->block_scores || !sel->pos_keys || !sel->pool_blocks || !sel->pool_count)
+      return fail(CSA2_ERR_INVALID_ARG, "required pointer is NULL");
+    if ((st = check_block_scores(d, q, sel->block_scores, sel->ld_block_scores))) return st;
+    if ((st = check_pos_keys(d, q, sel->pos_keys, sel->ld_pos_keys))) return st;
+  }
   if (!q_lat || !q_rope || !kv_codes || !kv_scales || !kv_rope || !topk_pos || !topk_count || !swa_base || !out)
     return fail(CSA2_ERR_INVALID_ARG, "required pointer is NULL");
   if (!swa_kv && d->swa > 0) return fail(CSA2_ERR_INVALID_ARG, "swa_kv is NULL");
@@ -759,6 +790,15 @@ static csa2_status attend(const csa2_dims* d, const csa2_queries* q, const uint1
   aa.page_shift = pages ? page_shift(pages) : 0;
   aa.rows = pages ? pages->rows : 0;
   aa.part_o = nullptr; aa.part_ml = nullptr;
+  aa.bscore = nullptr; aa.ld_bs = 0; aa.pkey = nullptr; aa.ld_pkey = 0; aa.pool = d->pool_blocks;
+  aa.pool_blocks = nullptr; aa.pool_count = nullptr; aa.topk_out = nullptr; aa.topk_count_out = nullptr;
+  if (sel) {
+    aa.bscore = sel->block_scores; aa.ld_bs = sel->ld_block_scores;
+    aa.pkey = sel->pos_keys; aa.ld_pkey = sel->ld_pos_keys;
+    aa.pool_blocks = sel->pool_blocks; aa.pool_count = sel->pool_count;
+    aa.topk_out = const_cast<int32_t*>(topk_pos); aa.topk_count_out = const_cast<int32_t*>(topk_count);
+    aa.topk_pos = nullptr; aa.topk_count = nullptr;
+  }
   if (p.splits > 1) {
     const size_t rows = (size_t)q->n_q * p.splits * p.hg * kAttendHeads;
     aa.part_o = (float*)ws;
@@ -786,6 +826,18 @@ csa2_status csa2_attend_paged(const csa2_dims* d, const csa2_queries* q, const c
   if (!pages) return fail(CSA2_ERR_INVALID_ARG, "pages is NULL");
   return attend(d, q, q_lat, q_rope, softmax_scale, kv_codes, kv_scales, kv_rope, topk_pos, topk_count, swa_kv,
                 swa_base, out, lse, ws, ws_bytes, stream, false, pages);
+}
+
+csa2_status csa2_pool_topk_attend(const csa2_dims* d, const csa2_queries* q, const float* block_scores,
+                                  int64_t ld_block_scores, const uint32_t* pos_keys, int64_t ld_pos_keys,
+                                  int32_t* pool_blocks, int32_t* pool_count, int32_t* topk_pos, int32_t* topk_count,
+                                  const uint16_t* q_lat, const uint16_t* q_rope, float softmax_scale,
+                                  const uint8_t* kv_codes, const uint8_t* kv_scales, const uint16_t* kv_rope,
+                                  const uint16_t* swa_kv, const int64_t* swa_base, float* out, float* lse, void* ws,
+                                  size_t ws_bytes, void* stream) {
+  const AttendSel sel{block_scores, ld_block_scores, pos_keys, ld_pos_keys, pool_blocks, pool_count};
+  return attend(d, q, q_lat, q_rope, softmax_scale, kv_codes, kv_scales, kv_rope, topk_pos, topk_count, swa_kv,
+                swa_base, out, lse, ws, ws_bytes, stream, false, nullptr, &sel);
 }
 
 csa2_status csa2_page_rows(const csa2_pages* pages, int64_t n, const int64_t* table_off, const int32_t* pos,
@@ -874,6 +926,9 @@ static csa2_status decode_step(const csa2_dims* d, const csa2_queries* q, int32_
   // every stage's arguments are checked before the first launch
   for (int pass = 0; pass < 2; ++pass) {
     const bool dry = pass == 0;
+    // a Full layer with small pools selects them inside the attention kernel
+    const bool fused = mode == CSA2_LAYER_FULL && !pages && pool_small(d, q);
+    AttendSel sel{};
     if (mode == CSA2_LAYER_FULL) {
       // the scan also keeps every position's score; the Top-K then comes
       // from those scores (the layer's own query: what Reindex would compute)
@@ -881,15 +936,18 @@ static csa2_status decode_step(const csa2_dims* d, const csa2_queries* q, int32_
       uint32_t* pkey = (uint32_t*)(w_full + n_idx);
       if (!topk_pos || !topk_count) return fail(CSA2_ERR_INVALID_ARG, "required pointer is NULL");
       if ((st = index_full(d, q, idx_q, idx_q_scales, idx_w, idx_k, idx_k_scales, fp4, pool_blocks, pool_count,
-                           nullptr, 0, w_full, n_idx, stream, dry, pages, pkey, topk_pos, topk_count)))
+                           nullptr, 0, w_full, n_idx, stream, dry, pages, pkey, topk_pos, topk_count, fused)))
         return st;
+      sel = AttendSel{(const float*)(w_full + pool_ws(d, q)), full_ldb(d, q), pkey, full_ldpk(d, q), pool_blocks,
+                      pool_count};
     }
     if (mode == CSA2_LAYER_REINDEX &&
         (st = index_reindex(d, q, idx_q, idx_q_scales, idx_w, idx_k, idx_k_scales, fp4, pool_blocks, pool_count,
                             topk_pos, topk_count, nullptr, w_re, n_re, stream, dry, pages, counters)))
       return st;
     if ((st = attend(d, q, q_lat, q_rope, softmax_scale, kv_codes, kv_scales, kv_rope, topk_pos, topk_count, swa_kv,
-                     swa_base, out, lse, attend_ws(d, q) ? w_att : nullptr, n_att, stream, dry, pages)))
+                     swa_base, out, lse, attend_ws(d, q) ? w_att : nullptr, n_att, stream, dry, pages,
+                     fused ? &sel : nullptr)))
       return st;
   }
   return CSA2_OK;

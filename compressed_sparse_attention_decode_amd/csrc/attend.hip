@@ -48,6 +48,7 @@
 //    one tile, so a query's work is spread over tens of CUs.
 #include "common.h"
 #include "internal.h"
+#include "pool_topk.h"
 
 namespace csa2 {
 namespace {
@@ -81,6 +82,12 @@ constexpr int kOffMx = kOffP + 2 * 16 * kPS * 2;
 constexpr int kOffAl = kOffMx + 2 * 4 * 16 * 4;
 constexpr int kOffLw = kOffAl + 2 * 16 * 4;
 constexpr int kLdsBytes = kOffLw + 2 * 4 * 16 * 4;
+// A selecting split's query latents (32 rows of 512 bf16, padded so that the
+// 16 rows one read instruction spans fall on distinct banks), in the image
+// after the selection's own LDS; read into registers before the first gather.
+constexpr int kQS = (kLatent + 8) * 2;
+constexpr int kOffQ = 18 * 1024;
+static_assert(kOffQ + kAttendHeads * kQS <= kTE * kLS * 2, "query latents fit in the image");
 static_assert(kTE * 8 == kNT, "one rope chunk per thread");
 static_assert(kTE * kScaleBytes <= kNW * 256, "a tile's scale block: one 256-byte load per wave");
 static_assert(kAttendHeads * kOS * 4 <= kOffStage, "output rows fit in the image and rope slots");
@@ -159,6 +166,14 @@ __device__ __forceinline__ float max_rows4(float x) {
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
+// SEL > 0: the splits with kept-entry tiles select the query's pool and
+// Full-layer Top-K themselves (pool_topk.h, SEL blocks per thread in its
+// positions step) from the scan's scores instead of reading topk_pos: the
+// selection is repeated by each such split, which costs a few microseconds
+// of one CU each, against a launch and a round trip for the positions; the
+// split holding the first kept-entry tile of head group 0 writes the pool
+// and the Top-K out.
+template <int SEL>
 __global__ __launch_bounds__(kNT) void k_attend(AttendArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char s_mem[kLdsBytes];
   _Float16* s_lat = reinterpret_cast<_Float16*>(s_mem + kOffLat);   // [64][kLS]
@@ -182,36 +197,60 @@ __global__ __launch_bounds__(kNT) void k_attend(AttendArgs a) {
   const int t_begin = sp * a.split_tiles;
   const int t_end = min(nwt + (K + kTE - 1) / kTE, t_begin + a.split_tiles);
   const int ntl = max(0, t_end - t_begin);
+  // the query's sizes and bases: scalar loads issued together, one round
+  // trip (a use between them would wait for the first alone)
+  const int n = load_uniform(a.n_visible + q);
+  const int tcount = SEL ? 0 : load_uniform(a.topk_count + q);
+  const int64_t sbase = load_uniform(a.seq_base + q);
+  const int64_t wbase = load_uniform(a.swa_base + q);
 
   // the split's kept positions (the row always holds K entries), then the
   // wave's 16 query heads: both in flight together
-  const int32_t* tk = a.topk_pos + (int64_t)q * K;
   int32_t tkv[kRowPer];
+  if constexpr (SEL == 0) {
+    const int32_t* tk = a.topk_pos + (int64_t)q * K;
 #pragma unroll
-  for (int j = 0; j < kRowPer; ++j) {
-    const int idx = tid + j * kNT;
-    const int jj = (t_begin + idx / kTE - nwt) * kTE + idx % kTE;   // index in topk_pos (sparse tiles)
-    tkv[j] = tk[min(max(jj, 0), K - 1)];
+    for (int j = 0; j < kRowPer; ++j) {
+      const int idx = tid + j * kNT;
+      const int jj = (t_begin + idx / kTE - nwt) * kTE + idx % kTE;   // index in topk_pos (sparse tiles)
+      tkv[j] = tk[min(max(jj, 0), K - 1)];
+    }
   }
-  // lane (col, gq) holds head head0 + col, dims 32 ks + 8 gq .. + 8
+  // lane (col, gq) holds head head0 + col, dims 32 ks + 8 gq .. + 8 (a
+  // selecting split issues these after its block-score loads)
   v4u rq[kKeyDim / 32];
-  {
+  auto load_q = [&]() {
     const int64_t qh = (int64_t)q * H + min(head0 + col, H - 1);
 #pragma unroll
     for (int ks = 0; ks < kKeyDim / 32; ++ks) {
       const int d = ks * 32 + gq * 8;
       rq[ks] = *reinterpret_cast<const v4u*>(d < kLatent ? a.q_lat + qh * kLatent + d : a.q_rope + qh * kRope + (d - kLatent));
     }
-  }
-  const int n = load_uniform(a.n_visible + q);
+  };
+  const bool selects = SEL > 0 && t_end > nwt;
+  if (!selects) load_q();
+  // a selecting split: the latent dims into the LDS (one 1 KiB row per
+  // instruction instead of every wave loading its group's 16 heads), the
+  // rope dims into registers, both issued once the block keys are in
+  auto load_q_sel = [&]() {
+    const v4u rs_q = rsrc_of(a.q_lat + (int64_t)q * H * kLatent, (uint32_t)H * (kLatent * 2));
+#pragma unroll
+    for (int j = 0; j < kAttendHeads / kNW; ++j) {
+      const int h = (kAttendHeads / kNW) * wave + j;
+      dma16(lds_addr(s_mem + kOffQ + h * kQS), (uint32_t)min(hg * kAttendHeads + h, H - 1) * (kLatent * 2) + lane * 16,
+            rs_q);
+    }
+    const int64_t qh = (int64_t)q * H + min(head0 + col, H - 1);
+#pragma unroll
+    for (int j = 0; j < kRope / 32; ++j)
+      rq[kLatent / 32 + j] = *reinterpret_cast<const v4u*>(a.q_rope + qh * kRope + j * 32 + gq * 8);
+  };
   const int c = max(0, n - a.swa);
   const int Ew = n - c;                           // window rows [c, n)
-  const int Es = min(load_uniform(a.topk_count + q), K);
-  const int64_t sbase = load_uniform(a.seq_base + q);
-  const int64_t wbase = load_uniform(a.swa_base + q);
+  int Es = min(tcount, K);
   // paged main KV: the kept positions become rows of the whole planes (one
   // page id per position, loaded unconditionally from a clamped slot)
-  const bool paged = a.pages != nullptr;
+  const bool paged = SEL == 0 && a.pages != nullptr;
   if (paged && c > 0) {
     int32_t pg[kRowPer];
 #pragma unroll
@@ -232,6 +271,7 @@ __global__ __launch_bounds__(kNT) void k_attend(AttendArgs a) {
   const v4u rs_rope = rsrc_of(a.kv_rope + kbase * kRope, krows * (kRope * 2));
   const v4u rs_win = rsrc_of(a.swa_kv + wbase * kKeyDim, (uint32_t)Ew * kWinRow);
   // row codes of the split's tiles (>= 0: cache row, < 0: window row -1 - code)
+  asm volatile("" ::"s"(n), "s"(tcount), "s"(sbase), "s"(wbase));
 #pragma unroll
   for (int j = 0; j < kRowPer; ++j) {
     const int idx = tid + j * kNT;
@@ -241,13 +281,42 @@ __global__ __launch_bounds__(kNT) void k_attend(AttendArgs a) {
       if (t < nwt) {
         const int ge = t * kTE + e;
         if (ge < Ew) code = -1 - ge;
-      } else if ((t - nwt) * kTE + e < Es) {
+      } else if (SEL == 0 && (t - nwt) * kTE + e < Es) {
         code = tkv[j];
       }
       s_row[idx] = code;
     }
   }
+  if constexpr (SEL > 0) {
+    if (selects) {
+      // this split's kept positions (ranks r0 .. r1 of the Top-K) straight
+      // into its row codes; the selection's LDS is the image's, unused until
+      // the first gather (its first barrier orders the row codes above)
+      static_assert(sizeof(PoolTopkLds<SEL>) <= kOffQ, "selection LDS fits in the image before the query");
+      const int s_first = max(t_begin, nwt);
+      const bool lead = hg == 0 && t_begin <= nwt;  // holds the first kept-entry tile
+      PoolTopkOut o;
+      o.pool = lead ? a.pool_blocks + (int64_t)q * a.pool : nullptr;
+      o.pool_count = lead ? a.pool_count + q : nullptr;
+      o.topk = lead ? a.topk_out + (int64_t)q * K : nullptr;
+      o.topk_count = lead ? a.topk_count_out + q : nullptr;
+      o.rows = s_row + (s_first - t_begin) * kTE;
+      o.r0 = (s_first - nwt) * kTE;
+      o.r1 = (t_end - nwt) * kTE;
+      Es = min((int)pool_topk_select<SEL>(a.bscore + (int64_t)q * a.ld_bs, (int)a.ld_bs, (c + 7) >> 3, a.pool, K,
+                                          a.pkey + (int64_t)q * a.ld_pkey, o,
+                                          *reinterpret_cast<PoolTopkLds<SEL>*>(s_mem + kOffLat), load_q_sel),
+               K);
+      wait_vmcnt<0>();                             // this wave's query rows have landed
+    }
+  }
   __syncthreads();
+  if (selects) {
+#pragma unroll
+    for (int ks = 0; ks < kLatent / 32; ++ks)
+      rq[ks] = *reinterpret_cast<const v4u*>(s_mem + kOffQ + (hgl * 16 + col) * kQS + (ks * 32 + gq * 8) * 2);
+    __syncthreads();                              // read before any gather lands in the image
+  }
   auto tile_entries = [&](int t) {
     return t < nwt ? min(kTE, max(0, Ew - t * kTE)) : min(kTE, max(0, Es - (t - nwt) * kTE));
   };
@@ -543,7 +612,18 @@ hipError_t launch_attend(const AttendArgs& a, hipStream_t s) {
   if (a.split_tiles * kTE > kMaxRows || a.splits < 1 || a.splits > kAttendMaxSplits ||
       (a.splits > 1 && (!a.part_o || !a.part_ml)))
     return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_attend, dim3((unsigned)(a.n_q * a.head_groups * a.splits)), dim3(kNT), 0, s, a);
+  const dim3 grid((unsigned)(a.n_q * a.head_groups * a.splits));
+  if (!a.bscore) {
+    hipLaunchKernelGGL(k_attend<0>, grid, dim3(kNT), 0, s, a);
+  } else {
+    // (a query of at most kMaxCand blocks, pool and Top-K within 2048, no
+    // page table: checked by the caller)
+    if (a.pages || a.pool > 2048 || a.topk > 2048 || !a.pkey || !a.pool_blocks || !a.pool_count || !a.topk_out ||
+        !a.topk_count_out)
+      return hipErrorInvalidValue;
+    if (a.topk <= kTkThreads) hipLaunchKernelGGL(k_attend<2>, grid, dim3(kNT), 0, s, a);
+    else hipLaunchKernelGGL(k_attend<4>, grid, dim3(kNT), 0, s, a);
+  }
   if (a.splits > 1) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

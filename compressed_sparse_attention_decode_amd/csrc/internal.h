@@ -87,6 +87,18 @@ struct AttendArgs {
   const int32_t* pages;      // paged main-KV planes (as ReindexArgs; the window stays apart)
   int page_shift;
   int64_t rows;
+  // the pool and the Full layer's Top-K selected in the attention kernel
+  // (bscore != nullptr; then topk_pos / topk_count are not read): the scan's
+  // block scores and position keys, and where the selection goes
+  const float* bscore;
+  int64_t ld_bs;
+  const uint32_t* pkey;
+  int64_t ld_pkey;
+  int pool;
+  int32_t* pool_blocks;
+  int32_t* pool_count;
+  int32_t* topk_out;         // [n_q, topk]
+  int32_t* topk_count_out;
 };
 
 // A Full layer's Top-K from the Full scan's own scores (the same indexer

@@ -1,0 +1,143 @@
+// The pool of a query with at most kMaxCand blocks, and optionally its Full
+// layer's Top-K, selected by one 512-thread workgroup that holds all of the
+// query's block keys in registers.
+//
+// Pool ("DeepSeek-V4.1-Flash 梗概" §3.1, the Full indexer keeps the P best
+// blocks by block maximum): the radix Top-K of radix_topk.h over the block
+// keys, ties to the lower block id, written in ascending order.
+//
+// Top-K (same page, §3.2: a Full layer's index set comes from the query that
+// scored the whole context): the K best positions of the pool by (score
+// desc, position asc), from the scan's position keys (topk_positions.h).
+// Its candidate blocks are the pool's blocks at or above the lower edge of
+// the first histogram's bin that holds the K-th best block: a superset of
+// the K best blocks (ties to the lower id), so their positions hold the K
+// best positions, and kept in ascending order so that slot order is
+// position order for the ties.  Only when that bin is so crowded that the
+// candidates exceed the BPT blocks per thread of the positions step does a
+// second radix select pick exactly the K best blocks of the pool (the keys
+// outside it cleared first).
+#pragma once
+
+#include "common.h"
+#include "radix_topk.h"
+#include "select_common.h"
+#include "topk_positions.h"
+
+namespace csa2 {
+
+// Where the selection goes; every pointer is optional.
+struct PoolTopkOut {
+  int32_t* pool;         // [P] block ids ascending, -1 past the count
+  int32_t* pool_count;
+  int32_t* topk;         // [K] positions ascending, -1 past the count
+  int32_t* topk_count;
+  int32_t* rows;         // LDS: Top-K ranks [r0, r1) to rows[rank - r0]
+  int r0, r1;
+};
+
+// The LDS of one selection (s_blk: BPT blocks per thread).
+template <int BPT>
+struct PoolTopkLds {
+  RadixLds radix;
+  int32_t blk[BPT > 0 ? kTkThreads * BPT : 1];
+  uint32_t scan[kTkWaves];
+};
+
+// Called by all kTkThreads threads.  bs: the query's block scores (row
+// stride ld, a multiple of 4 floats, >= 4), nb <= kMaxCand of them valid;
+// pk: its position keys (BPT > 0).  after_keys() runs once the block keys
+// are in registers, before the first selection (a caller's own loads then
+// land while it runs without delaying the keys).  Returns the Top-K count
+// (BPT > 0) or the pool count.  Contains barriers.
+template <int BPT, typename AfterKeys>
+__device__ __forceinline__ uint32_t pool_topk_select(const float* bs, int ld, int nb, int P, int K,
+                                                     const uint32_t* pk, const PoolTopkOut& o,
+                                                     PoolTopkLds<BPT>& L, AfterKeys&& after_keys) {
+  constexpr uint32_t kCap = kTkThreads * BPT;       // candidate blocks of the positions step
+  const int tid = threadIdx.x;
+  // thread t holds blocks [kPer t, kPer (t + 1)); the loads are bounded by
+  // the row stride only, so they need not wait for the block count, which
+  // masks them afterwards.  Every load is issued, clamped into the row, and
+  // masked after it: a load under a condition would be waited for at once,
+  // which made four round trips of the eight.
+  const int s0 = tid * kPer;
+  v4f x[kPer / 4];
+#pragma unroll
+  for (int v = 0; v < kPer / 4; ++v) x[v] = *reinterpret_cast<const v4f*>(bs + min(s0 + 4 * v, ld - 4));
+#pragma unroll
+  for (int v = 0; v < kPer / 4; ++v) {
+    if (s0 + 4 * v >= ld) x[v] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+  }
+  uint32_t key[kPer];
+#pragma unroll
+  for (int v = 0; v < kPer / 4; ++v) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) key[4 * v + e] = s0 + 4 * v + e < nb ? order_key(x[v][e]) : 0u;
+  }
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) asm volatile("" : "+v"(key[k]));   // the keys are complete here
+  after_keys();
+  const TopkCut cut = radix_topk<kPer>(key, P, BPT > 0 ? K : 0, L.radix);
+
+  // pool members, and (BPT > 0) the candidate blocks of the Top-K: both
+  // offsets from one block scan (16-bit fields: at most 16,384 of each)
+  uint32_t flags = 0, cflags = 0;
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    const bool in = key[k] >= cut.tt;
+    flags |= (uint32_t)in << k;
+    if constexpr (BPT > 0) cflags |= (uint32_t)(in && key[k] >= cut.lb2) << k;
+  }
+  uint32_t total;
+  const uint32_t packed = block_exclusive_scan<kTkThreads>(
+      __builtin_popcount(flags) | (uint32_t)__builtin_popcount(cflags) << 16, L.scan, &total);
+  if (o.pool) {
+    uint32_t before = packed & 0xFFFFu;
+    while (flags) {
+      const int k = __builtin_ctz(flags);
+      flags &= flags - 1;
+      if (before < (uint32_t)P) o.pool[before] = s0 + k;
+      ++before;
+    }
+    for (int t = (int)cut.keff + tid; t < P; t += kTkThreads) o.pool[t] = -1;
+  }
+  if (o.pool_count && tid == 0) *o.pool_count = (int32_t)cut.keff;
+  if constexpr (BPT == 0) {
+    return cut.keff;
+  } else {
+    const uint32_t ncand = total >> 16;
+    uint32_t nsel;
+    if (ncand <= kCap) {
+      uint32_t cb = packed >> 16;
+      while (cflags) {
+        const int k = __builtin_ctz(cflags);
+        cflags &= cflags - 1;
+        L.blk[cb++] = s0 + k;                      // ascending block ids
+      }
+      nsel = ncand;
+    } else {
+      // the exact K best blocks of the pool (all of it when K exceeds its
+      // count)
+#pragma unroll
+      for (int k = 0; k < kPer; ++k) key[k] = key[k] >= cut.tt ? key[k] : 0u;
+      const TopkCut bc = radix_topk<kPer>(key, K, 0, L.radix);
+      uint32_t bflags = 0;
+#pragma unroll
+      for (int k = 0; k < kPer; ++k) bflags |= (uint32_t)(key[k] >= bc.tt) << k;
+      uint32_t bb = block_exclusive_scan<kTkThreads>(__builtin_popcount(bflags), L.scan, &nsel);
+      while (bflags) {
+        const int k = __builtin_ctz(bflags);
+        bflags &= bflags - 1;
+        if (bb < kCap) L.blk[bb] = s0 + k;         // ascending block ids
+        ++bb;
+      }
+      nsel = min(nsel, kCap);
+    }
+    __syncthreads();
+    return topk_positions<BPT>(L.blk, nsel, pk, K, o.topk, nullptr, o.topk_count, L.scan, L.radix, o.rows, o.r0,
+                               o.r1);
+  }
+}
+
+}  // namespace csa2

@@ -95,18 +95,27 @@ struct TopkCut {
   uint32_t n2;
 };
 
+// The selection's LDS.  Calls may share one (a barrier always separates one
+// call's last read from the next call's first write).
+struct __align__(16) RadixLds {
+  uint32_t hist[kTkBins + kTkEmpty];
+  uint64_t cand[kRankCap];
+  uint32_t red[2 * kTkWaves];
+  uint32_t misc[8];
+  uint32_t misc2[8];
+};
+
 // All 512 threads call this with their PER keys (PER <= 32; thread t holds
 // slots [PER t, PER (t + 1)); slots past the valid range already 0).
-// Contains barriers; K >= 1, K2 >= 0 (0: no second rank).  Each PER has its
-// own LDS.
-template <int PER = kPer>
-__device__ __forceinline__ TopkCut radix_topk(uint32_t (&key)[PER], int K, int K2 = 0) {
+// Contains barriers; K >= 1, K2 >= 0 (0: no second rank).
+template <int PER>
+__device__ __forceinline__ TopkCut radix_topk(uint32_t (&key)[PER], int K, int K2, RadixLds& L) {
   static_assert(PER >= 1 && PER <= 32, "a 32-bit candidate mask per thread");
-  __shared__ __align__(16) uint32_t s_hist[kTkBins + kTkEmpty];
-  __shared__ uint64_t s_cand[kRankCap];
-  __shared__ uint32_t s_red[2 * kTkWaves];
-  __shared__ uint32_t s_misc[8];
-  __shared__ uint32_t s_misc2[5];
+  uint32_t* s_hist = L.hist;
+  uint64_t* s_cand = L.cand;
+  uint32_t* s_red = L.red;
+  uint32_t* s_misc = L.misc;
+  uint32_t* s_misc2 = L.misc2;
 
   const int tid = threadIdx.x, lane = tid & 63;
 
@@ -239,6 +248,13 @@ __device__ __forceinline__ TopkCut radix_topk(uint32_t (&key)[PER], int K, int K
     for (int k = 0; k < PER; ++k) key[k] = (key[k] == T && s0 + k > ST) ? 0u : key[k];
   }
   return TopkCut{keff, Tt, lb2, n2};
+}
+
+// The same with LDS of its own (one per PER).
+template <int PER = kPer>
+__device__ __forceinline__ TopkCut radix_topk(uint32_t (&key)[PER], int K, int K2 = 0) {
+  __shared__ RadixLds s_radix;
+  return radix_topk<PER>(key, K, K2, s_radix);
 }
 
 }  // namespace csa2

@@ -56,7 +56,9 @@ __device__ __forceinline__ void score_part(const ReindexArgs& a, int q, int part
   const int gq = lane >> 4, col = lane & 15;
   const int i_begin = part * BPW;
   const int i_end = min(a.pool, i_begin + BPW);
+  // scalar loads issued together: one round trip
   const int n = load_uniform(a.n_visible + q);
+  const int64_t sbase = load_uniform(a.seq_base + q);
   const int c = max(0, n - a.swa);
   const int32_t* pool = a.pool_blocks + (int64_t)q * a.pool;
 
@@ -67,7 +69,9 @@ __device__ __forceinline__ void score_part(const ReindexArgs& a, int q, int part
   for (int u = 0; u < SPW; ++u) pos[u] = pool[min(i_begin + 2 * (wave + NW * u) + (col >> 3), a.pool - 1)];
   // the empty asm uses every loaded id, so the loads stay unconditional and
   // all in flight together (a load the compiler sinks into the masked
-  // branch below waits on its own)
+  // branch below waits on its own); the sequence base is waited for here
+  // too, so its load is issued with the others
+  asm volatile("" ::"s"(sbase));
 #pragma unroll
   for (int u = 0; u < SPW; ++u) asm volatile("" : "+v"(pos[u]));
 #pragma unroll
@@ -76,7 +80,6 @@ __device__ __forceinline__ void score_part(const ReindexArgs& a, int q, int part
     pos[u] = i < i_end ? pos[u] * kBlock + (col & 7) : c;
   }
   // every key load in flight at once (a position >= c reads zeros)
-  const int64_t sbase = load_uniform(a.seq_base + q);
 #pragma unroll
   for (int u = 0; u < SPW; ++u) {
     if (pos[u] > c || pos[u] < 0) pos[u] = c;
@@ -392,8 +395,9 @@ __global__ __launch_bounds__(kTkThreads) void k_topk_keys(TopkKeysArgs a) {
   __syncthreads();
 
   // 2. the K best positions of those blocks
+  __shared__ RadixLds s_radix;
   topk_positions<BPT>(s_blk, nsel, a.pkey + (int64_t)q * a.ld_pkey, K, a.topk_pos + (int64_t)q * K,
-                      a.topk_scores ? a.topk_scores + (int64_t)q * K : nullptr, a.topk_count + q, s_scan);
+                      a.topk_scores ? a.topk_scores + (int64_t)q * K : nullptr, a.topk_count + q, s_scan, s_radix);
 }
 
 }  // namespace

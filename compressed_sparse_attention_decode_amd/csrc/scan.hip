@@ -102,7 +102,11 @@ __global__ __launch_bounds__(64 * NW) void k_scan(ScanArgs a) {
   if (tile >= a.tiles) return;
   const int q = group * g + j;
 
+  // the query's visible length and sequence base: scalar loads waited for
+  // together (one round trip before the first key load)
   const int n = a.n_visible[q];
+  const int64_t sbase = a.seq_base[q];
+  asm volatile("" ::"s"(n), "s"(sbase));
   const int c = max(0, n - a.swa);
   // with two workgroups per CU, the one dispatched first (the first half of
   // the tile indices) streams faster, so it gets the longer tile
@@ -120,7 +124,6 @@ __global__ __launch_bounds__(64 * NW) void k_scan(ScanArgs a) {
   // buffer descriptor over this sequence's candidate keys, built from
   // wave-uniform scalars (rows >= c read as zero)
   // (paged: over the whole plane; rows >= c are then masked per lane)
-  const int64_t sbase = a.seq_base[q];
   const int64_t kbase = PG ? 0 : sbase;
   const uint32_t krows = PG ? (uint32_t)a.rows : (uint32_t)c;
   const uint64_t kaddr = (uint64_t)(uintptr_t)(a.idx_k + kbase * RB);

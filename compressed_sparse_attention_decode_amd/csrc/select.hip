@@ -36,6 +36,7 @@
 #include "common.h"
 #include "internal.h"
 #include "radix_topk.h"
+#include "pool_topk.h"
 #include "select_common.h"
 #include "topk_positions.h"
 
@@ -600,108 +601,25 @@ __global__ __launch_bounds__(kCT) void k_pool_mark(PoolArgs a) {
 
 // ---------------------------------------------------------------- small pools
 // A query with at most kPoolSmallBlocks blocks (contexts up to 131,200
-// positions) is selected by one 512-thread workgroup that holds all of its
-// block keys in registers and runs the radix Top-K of radix_topk.h: one
-// launch instead of the histogram and marking kernels.  Same result: the
-// min(P, nb) largest blocks, ties to the lower id, written in ascending order.
-// With BPT > 0 the same workgroup then takes the Full layer's Top-K from the
-// scan's position keys (topk_positions.h).  Its candidate blocks are the
-// pool's blocks at or above the lower edge of the first histogram's bin that
-// holds the K-th best block: a superset of the K best blocks (ties to the
-// lower id), so their positions hold the K best positions, and kept in
-// ascending order so that slot order is position order for the ties.  Only
-// when that bin is so crowded that the candidates exceed the BPT blocks per
-// thread of the positions step does a second radix select pick exactly the
-// K best blocks of the pool (the keys outside it cleared first).
+// positions) is selected by one 512-thread workgroup (pool_topk.h): one
+// launch instead of the histogram and marking kernels, with the same
+// result.  With BPT > 0 the same workgroup then takes the Full layer's
+// Top-K from the scan's position keys.
 static_assert(kPoolSmallBlocks == kMaxCand, "one key per register slot");
 
 template <int BPT>
 __global__ __launch_bounds__(kTkThreads) void k_pool_small(PoolArgs a) {
-  __shared__ uint32_t s_scan[kTkWaves];
-  __shared__ int32_t s_blk[BPT > 0 ? kTkThreads * BPT : 1];
-  constexpr uint32_t kCap = kTkThreads * BPT;       // candidate blocks of the positions step
-  const int q = blockIdx.x, tid = threadIdx.x;
-  const int P = a.pool;
-  const float* bs = a.bscore + (int64_t)q * a.ld;
-  int32_t* out = a.pool_blocks + (int64_t)q * P;
-  // thread t holds blocks [kPer t, kPer (t + 1)); the loads are bounded by
-  // the row stride (a multiple of 4 floats) only, so they need not wait for
-  // the block count, which masks them afterwards.  Every load is issued,
-  // clamped into the row, and masked after it: a load under a condition
-  // would be waited for at once, which made four round trips of the eight.
-  const int s0 = tid * kPer;
-  v4f x[kPer / 4];
-#pragma unroll
-  for (int v = 0; v < kPer / 4; ++v) x[v] = *reinterpret_cast<const v4f*>(bs + min(s0 + 4 * v, (int)a.ld - 4));
-#pragma unroll
-  for (int v = 0; v < kPer / 4; ++v) {
-    if (s0 + 4 * v >= a.ld) x[v] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-  }
-  const int nb = query_blocks(a, q);
-  uint32_t key[kPer];
-#pragma unroll
-  for (int v = 0; v < kPer / 4; ++v) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) key[4 * v + e] = s0 + 4 * v + e < nb ? order_key(x[v][e]) : 0u;
-  }
-  const int K = a.topk;
-  const TopkCut cut = radix_topk(key, P, BPT > 0 ? K : 0);
-
-  // pool members, and (BPT > 0) the candidate blocks of the Top-K: both
-  // offsets from one block scan (16-bit fields: at most 16,384 of each)
-  uint32_t flags = 0, cflags = 0;
-#pragma unroll
-  for (int k = 0; k < kPer; ++k) {
-    const bool in = key[k] >= cut.tt;
-    flags |= (uint32_t)in << k;
-    if constexpr (BPT > 0) cflags |= (uint32_t)(in && key[k] >= cut.lb2) << k;
-  }
-  uint32_t total;
-  const uint32_t packed = block_exclusive_scan<kTkThreads>(
-      __builtin_popcount(flags) | (uint32_t)__builtin_popcount(cflags) << 16, s_scan, &total);
-  uint32_t before = packed & 0xFFFFu;
-  while (flags) {
-    const int k = __builtin_ctz(flags);
-    flags &= flags - 1;
-    if (before < (uint32_t)P) out[before] = s0 + k;
-    ++before;
-  }
-  for (int t = (int)cut.keff + tid; t < P; t += kTkThreads) out[t] = -1;
-  if (tid == 0) a.pool_count[q] = (int32_t)cut.keff;
-
-  if constexpr (BPT > 0) {
-    const uint32_t ncand = total >> 16;
-    uint32_t nsel;
-    if (ncand <= kCap) {
-      uint32_t cb = packed >> 16;
-      while (cflags) {
-        const int k = __builtin_ctz(cflags);
-        cflags &= cflags - 1;
-        s_blk[cb++] = s0 + k;                      // ascending block ids
-      }
-      nsel = ncand;
-    } else {
-      // the exact K best blocks of the pool (all of it when K exceeds its
-      // count)
-#pragma unroll
-      for (int k = 0; k < kPer; ++k) key[k] = key[k] >= cut.tt ? key[k] : 0u;
-      const TopkCut bc = radix_topk(key, K);
-      uint32_t bflags = 0;
-#pragma unroll
-      for (int k = 0; k < kPer; ++k) bflags |= (uint32_t)(key[k] >= bc.tt) << k;
-      uint32_t bb = block_exclusive_scan<kTkThreads>(__builtin_popcount(bflags), s_scan, &nsel);
-      while (bflags) {
-        const int k = __builtin_ctz(bflags);
-        bflags &= bflags - 1;
-        if (bb < kCap) s_blk[bb] = s0 + k;         // ascending block ids
-        ++bb;
-      }
-      nsel = min(nsel, kCap);
-    }
-    __syncthreads();
-    topk_positions<BPT>(s_blk, nsel, a.pkey + (int64_t)q * a.ld_pkey, K, a.topk_pos + (int64_t)q * K, nullptr,
-                        a.topk_count + q, s_scan);
-  }
+  __shared__ PoolTopkLds<BPT> s_sel;
+  const int q = blockIdx.x;
+  PoolTopkOut o;
+  o.pool = a.pool_blocks + (int64_t)q * a.pool;
+  o.pool_count = a.pool_count + q;
+  o.topk = BPT > 0 ? a.topk_pos + (int64_t)q * a.topk : nullptr;
+  o.topk_count = BPT > 0 ? a.topk_count + q : nullptr;
+  o.rows = nullptr;
+  o.r0 = o.r1 = 0;
+  pool_topk_select<BPT>(a.bscore + (int64_t)q * a.ld, (int)a.ld, query_blocks(a, q), a.pool, a.topk,
+                        BPT > 0 ? a.pkey + (int64_t)q * a.ld_pkey : nullptr, o, s_sel, [] {});
 }
 
 }  // namespace

@@ -19,10 +19,13 @@ namespace csa2 {
 // keys, 0 for positions past the candidates), 8 per block; thread t takes
 // blocks [BPT t, BPT (t + 1)) of the selection (nsel <= BPT * kTkThreads).
 // Writes out[0 .. K) (ascending positions, -1 past the count), out_s (the
-// scores, optional) and *count.
+// scores) and *count, each optional, and the positions of ranks [r0, r1) to
+// rows[rank - r0] (LDS, optional; ranks past the count are not written).
+// Returns the count.
 template <int BPT>
-__device__ __forceinline__ void topk_positions(const int32_t* s_blk, uint32_t nsel, const uint32_t* pk, int K,
-                                               int32_t* out, float* out_s, int32_t* count, uint32_t* s_scan) {
+__device__ __forceinline__ uint32_t topk_positions(const int32_t* s_blk, uint32_t nsel, const uint32_t* pk, int K,
+                                                   int32_t* out, float* out_s, int32_t* count, uint32_t* s_scan,
+                                                   RadixLds& L, int32_t* rows = nullptr, int r0 = 0, int r1 = 0) {
   constexpr int PP = BPT * kBlock;                  // position slots per thread
   const int tid = threadIdx.x;
   uint32_t key[PP];
@@ -44,7 +47,7 @@ __device__ __forceinline__ void topk_positions(const int32_t* s_blk, uint32_t ns
     key[8 * b + 4] = live ? x1[b][0] : 0u; key[8 * b + 5] = live ? x1[b][1] : 0u;
     key[8 * b + 6] = live ? x1[b][2] : 0u; key[8 * b + 7] = live ? x1[b][3] : 0u;
   }
-  const TopkCut cut = radix_topk<PP>(key, K);
+  const TopkCut cut = radix_topk<PP>(key, K, 0, L);
   uint32_t pflags = 0;
 #pragma unroll
   for (int k = 0; k < PP; ++k) pflags |= (uint32_t)(key[k] >= cut.tt) << k;
@@ -54,17 +57,22 @@ __device__ __forceinline__ void topk_positions(const int32_t* s_blk, uint32_t ns
   for (int k = 0; k < PP; ++k) {
     if (pflags >> k & 1u) {
       if (pos_before < (uint32_t)K) {
-        out[pos_before] = mb[k >> 3] * kBlock + (k & 7);
+        const int32_t p = mb[k >> 3] * kBlock + (k & 7);
+        if (out) out[pos_before] = p;
         if (out_s) out_s[pos_before] = key_float(key[k]);
+        if (rows && (int)pos_before >= r0 && (int)pos_before < r1) rows[pos_before - r0] = p;
       }
       ++pos_before;
     }
   }
-  for (int t = (int)cut.keff + tid; t < K; t += kTkThreads) {
-    out[t] = -1;
-    if (out_s) out_s[t] = 0.0f;
+  if (out) {
+    for (int t = (int)cut.keff + tid; t < K; t += kTkThreads) {
+      out[t] = -1;
+      if (out_s) out_s[t] = 0.0f;
+    }
   }
-  if (tid == 0) *count = (int32_t)cut.keff;
+  if (count && tid == 0) *count = (int32_t)cut.keff;
+  return cut.keff;
 }
 
 }  // namespace csa2

@@ -322,6 +322,42 @@ def test_pool_topk_matches_separate_calls(case, small, monkeypatch):
         assert torch.equal(pool[qi, :k], pool2[qi, :k]), f"{name} q{qi}: pool differs"
 
 
+def test_pool_topk_attend_matches_separate_calls(case):
+    """csa2_pool_topk_attend (the pool and the Full layer's Top-K selected
+    inside the attention kernel, by every workgroup with kept-entry tiles)
+    writes the same pool, Top-K, output and log-sum-exp, bit for bit, as
+    csa2_index_pool_topk followed by csa2_attend."""
+    name, g, lay = case
+    csa2, w = g.csa2, g.w
+    q, wt = g.iq(0)
+    idx_k, codes, scales, kv_rope, swa_kv = g.planes[0]
+    ld = csa2.block_scores_ld(g.dims, g.batch)
+    bs = torch.empty(w.n_q, ld, dtype=torch.float32, device="cuda")
+    pk = torch.empty(w.n_q, csa2.pos_keys_ld(g.dims, g.batch), dtype=torch.int32, device="cuda")
+    pws = torch.zeros(csa2.workspace_pool(g.dims, g.batch) + 256, dtype=torch.uint8, device="cuda")
+    csa2.index_scan(g.dims, g.batch, q, wt, idx_k, bs, pool_ws=pws, pos_keys=pk)
+    pool, cnt, tk, tc = csa2.index_pool_topk(g.dims, g.batch, bs, pk, ws=pws, from_scan=True)
+    ql, qr = g.mq(0)
+    out, lse = csa2.attend(g.dims, g.batch, ql, qr, 1.0, codes, scales, kv_rope, tk, tc, swa_kv, g.swa_base)
+    fill = lambda shape, dt=torch.int32: torch.full(shape, 7, dtype=dt, device="cuda")
+    pool2, cnt2 = fill((w.n_q, w.dims.pool_blocks)), fill((w.n_q,))
+    tk2, tc2 = fill((w.n_q, w.dims.topk)), fill((w.n_q,))
+    out2 = fill((w.n_q, w.dims.n_heads, 512), torch.float32)
+    lse2 = fill((w.n_q, w.dims.n_heads), torch.float32)
+    csa2.pool_topk_attend(g.dims, g.batch, bs, pk, ql, qr, 1.0, codes, scales, kv_rope, swa_kv, g.swa_base,
+                          pool2, cnt2, tk2, tc2, out2, lse2)
+    torch.cuda.synchronize()
+    assert torch.equal(cnt, cnt2), f"{name}: pool counts differ"
+    for qi in range(w.n_q):
+        k = int(cnt[qi])
+        assert torch.equal(pool[qi, :k], pool2[qi, :k]), f"{name} q{qi}: pool differs"
+        assert bool((pool2[qi, k:] == -1).all()), f"{name} q{qi}: pool tail"
+    assert torch.equal(tc, tc2), f"{name}: Top-K counts differ"
+    assert torch.equal(tk, tk2), f"{name}: Top-K differs"
+    assert torch.equal(out.view(torch.int32), out2.view(torch.int32)), f"{name}: attention output differs"
+    assert torch.equal(lse.view(torch.int32), lse2.view(torch.int32)), f"{name}: log-sum-exp differs"
+
+
 def test_pipeline_end_to_end_and_deterministic(case):
     name, g, lay = case
     w = g.w
@@ -460,6 +496,15 @@ def _full_topk(g):
     pws = torch.zeros(csa2.workspace_pool(g.dims, g.batch) + 256, dtype=torch.uint8, device="cuda")
     csa2.index_scan(g.dims, g.batch, q, wt, g.planes[0][0], bs, pool_ws=pws, pos_keys=pk)
     pool, cnt, tk, tc = csa2.index_pool_topk(g.dims, g.batch, bs, pk, ws=pws, from_scan=True)
+    if os.environ.get("CSA2_POOL_SMALL") != "0":
+        # the selection inside the attention kernel: the same pool and Top-K
+        idx_k, codes, scales, kv_rope, swa_kv = g.planes[0]
+        ql, qr = g.mq(0)
+        pool2, cnt2, tk2, tc2, _, _ = csa2.pool_topk_attend(g.dims, g.batch, bs, pk, ql, qr, 1.0, codes, scales,
+                                                             kv_rope, swa_kv, g.swa_base)
+        torch.cuda.synchronize()
+        assert torch.equal(cnt, cnt2) and torch.equal(tc, tc2) and torch.equal(tk, tk2)
+        assert torch.equal(pool[0, :cnt.item()], pool2[0, :cnt.item()])
     torch.cuda.synchronize()
     return pool.cpu().numpy()[0, :cnt.item()], tk.cpu().numpy()[0, :tc.item()]
 
