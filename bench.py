@@ -204,9 +204,9 @@ class Step:
         self.full_topk = not w.fresh_q_per_layer
         self.pk = torch.empty(n_q, csa2.pos_keys_ld(st.dims, st.batch), dtype=torch.int32, device=dev) \
             if self.full_topk else None
-        # small unpaged pools: the selection runs inside the attention kernel
-        self.fused = self.full_topk and st.pages is None and csa2.n_blocks(st.dims, st.batch) <= 16384 and \
-            os.environ.get("CSA2_POOL_SMALL") != "0"
+        # unpaged planes: the Top-K (and a small pool) is selected inside the
+        # attention kernel
+        self.fused = self.full_topk and st.pages is None
         for layer in [0] + self.layers:
             st.iq(layer)
             st.mq(layer)
@@ -234,13 +234,13 @@ class Step:
                                                 prepare=True, pages=st.pages, pos_keys=self.pk)))
             if self.fused:
                 # the pool, the Full layer's Top-K and the attention, the
-                # selection inside the attention kernel (pools of up to
-                # 16,384 blocks, unpaged: csa2_decode_step's Full chain)
+                # Top-K (and a pool of up to 16,384 blocks) selected inside
+                # the attention kernel: csa2_decode_step's Full chain
                 ql, qr = st.mq(0)
                 seq.append(("pool_topk_attend", csa2.pool_topk_attend(
                     st.dims, st.batch, self.bs, self.pk, ql, qr, 1.0, codes, scales, kv_rope, swa_kv, st.swa_base,
                     self.pool, self.pcnt, self.tk[0], self.tc[0], out=self.out[0], lse=self.lse[0], ws=self.ws_a,
-                    prepare=True)))
+                    pool_ws=self.ws_p, from_scan=True, prepare=True)))
             elif self.full_topk:
                 # the pool and the Full layer's Top-K from the scan's keys
                 # (one kernel for pools of up to 16,384 blocks)

@@ -102,7 +102,7 @@ def lib() -> ctypes.CDLL:
             "csa2_index_topk_keys": (I32, [PD, PQ, P, P, P, I64, P, I64, P, P, P, P]),
             "csa2_index_pool_topk": (I32, [PD, PQ, P, I64, P, I64, P, P, P, P, P, SZ, I32, P]),
             "csa2_pool_topk_attend": (I32, [PD, PQ, P, I64, P, I64, P, P, P, P, P, P, ctypes.c_float, P, P, P,
-                                            P, P, P, P, P, SZ, P]),
+                                            P, P, P, P, P, SZ, I32, P, SZ, P]),
             "csa2_decode_step_noalloc": (I32, [PD, PQ, I32, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_float,
                                                P, P, P, P, P, P, P, P]),
         }
@@ -614,10 +614,13 @@ def pool_topk_attend(dims: Dims, b: Batch, block_scores: torch.Tensor, pos_keys:
                      pool_blocks: Optional[torch.Tensor] = None, pool_count: Optional[torch.Tensor] = None,
                      topk_pos: Optional[torch.Tensor] = None, topk_count: Optional[torch.Tensor] = None,
                      out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-                     ws: Optional[torch.Tensor] = None, want_lse: bool = True, prepare: bool = False):
-    """The pool, the Full layer's Top-K and the attention on it, the
-    selection inside the attention kernel (csa2_pool_topk_attend; queries of
-    at most 16,384 blocks).  Returns (pool_blocks, pool_count, topk_pos,
+                     ws: Optional[torch.Tensor] = None, pool_ws: Optional[torch.Tensor] = None,
+                     from_scan: bool = False, want_lse: bool = True, prepare: bool = False):
+    """The pool, the Full layer's Top-K and the attention on it, the Top-K
+    (and, for queries of at most 16,384 blocks, the pool) selected inside the
+    attention kernel (csa2_pool_topk_attend).  `pool_ws`, `from_scan` as
+    index_pool's `ws`, `from_scan` (used by the chunked pool kernels of
+    longer queries).  Returns (pool_blocks, pool_count, topk_pos,
     topk_count, out, lse)."""
     dev = q_lat.device
     _dev(block_scores, pos_keys, q_lat, q_rope, kv_codes, kv_scales, kv_rope, swa_kv, swa_base, pool_blocks,
@@ -649,15 +652,20 @@ def pool_topk_attend(dims: Dims, b: Batch, block_scores: torch.Tensor, pos_keys:
         out = torch.empty(n_q, H, 512, dtype=torch.float32, device=dev)
     if lse is None and want_lse:
         lse = torch.empty(n_q, H, dtype=torch.float32, device=dev)
+    if from_scan and pool_ws is None:
+        raise ValueError("from_scan needs the workspace that index_scan prepared")
     ws = _workspace(workspace_attend(dims, b), dev, ws)
     wp, wn = _ws_ptr(ws)
+    if n_blocks(dims, b) > 16384 or os.environ.get("CSA2_POOL_SMALL") == "0":
+        pool_ws = _workspace(workspace_pool(dims, b), dev, pool_ws)
+    pp, pn = _ws_ptr(pool_ws) if pool_ws is not None else (None, 0)
     d, q = dims.c(), b.c()
     args = (ctypes.byref(d), ctypes.byref(q), block_scores.data_ptr(), block_scores.shape[1], pos_keys.data_ptr(),
             pos_keys.shape[1], pool_blocks.data_ptr(), pool_count.data_ptr(), topk_pos.data_ptr(),
             topk_count.data_ptr(), q_lat.data_ptr(), q_rope.data_ptr(), float(softmax_scale), kv_codes.data_ptr(),
             kv_scales.data_ptr(), kv_rope.data_ptr(), swa_kv.data_ptr(), swa_base.data_ptr(), out.data_ptr(),
-            _ptr(lse), wp, wn, _stream(dev))
-    call = _issue(lib().csa2_pool_topk_attend, args, (d, q, ws), prepare)
+            _ptr(lse), pp, pn, POOL_WS_FROM_SCAN if from_scan else 0, wp, wn, _stream(dev))
+    call = _issue(lib().csa2_pool_topk_attend, args, (d, q, ws, pool_ws), prepare)
     return call if prepare else (pool_blocks, pool_count, topk_pos, topk_count, out, lse)
 
 

@@ -735,6 +735,7 @@ struct AttendSel {
   int64_t ld_pos_keys;
   int32_t* pool_blocks;
   int32_t* pool_count;
+  bool from_pool;            // the pool is selected before (chunked kernels): only the Top-K in the kernel
 };
 
 // Whether every query's pool fits one selecting workgroup (and the
@@ -757,7 +758,7 @@ static csa2_status attend(const csa2_dims* d, const csa2_queries* q, const uint1
   if (pages && (st = check_pages(pages, 256))) return st;   // kv_codes: the widest plane
   if (sel) {
     if (pages) return fail(CSA2_ERR_UNSUPPORTED, "the in-kernel selection takes unpaged planes");
-    if (!pool_small(d, q))
+    if (!sel->from_pool && !pool_small(d, q))
       return fail(CSA2_ERR_UNSUPPORTED, "the in-kernel selection takes at most %d blocks per query (max_visible %lld)",
                   kPoolSmallBlocks, (long long)q->max_visible);
     if (!sel->block_scores || !sel->pos_keys || !sel->pool_blocks || !sel->pool_count)
@@ -792,7 +793,9 @@ static csa2_status attend(const csa2_dims* d, const csa2_queries* q, const uint1
   aa.part_o = nullptr; aa.part_ml = nullptr;
   aa.bscore = nullptr; aa.ld_bs = 0; aa.pkey = nullptr; aa.ld_pkey = 0; aa.pool = d->pool_blocks;
   aa.pool_blocks = nullptr; aa.pool_count = nullptr; aa.topk_out = nullptr; aa.topk_count_out = nullptr;
+  aa.sel_from_pool = 0;
   if (sel) {
+    aa.sel_from_pool = sel->from_pool ? 1 : 0;
     aa.bscore = sel->block_scores; aa.ld_bs = sel->ld_block_scores;
     aa.pkey = sel->pos_keys; aa.ld_pkey = sel->ld_pos_keys;
     aa.pool_blocks = sel->pool_blocks; aa.pool_count = sel->pool_count;
@@ -828,16 +831,55 @@ csa2_status csa2_attend_paged(const csa2_dims* d, const csa2_queries* q, const c
                 swa_base, out, lse, ws, ws_bytes, stream, false, pages);
 }
 
+// The pool and the Full layer's Top-K with the attention on it: for small
+// pools one attention launch that selects both; otherwise the chunked pool
+// kernels, then the attention launch that selects the Top-K of that pool.
+static csa2_status pool_topk_attend(const csa2_dims* d, const csa2_queries* q, const float* block_scores,
+                                    int64_t ld_block_scores, const uint32_t* pos_keys, int64_t ld_pos_keys,
+                                    int32_t* pool_blocks, int32_t* pool_count, int32_t* topk_pos, int32_t* topk_count,
+                                    const uint16_t* q_lat, const uint16_t* q_rope, float softmax_scale,
+                                    const uint8_t* kv_codes, const uint8_t* kv_scales, const uint16_t* kv_rope,
+                                    const uint16_t* swa_kv, const int64_t* swa_base, float* out, float* lse,
+                                    void* pool_wsp, size_t pool_ws_bytes, int32_t flags, void* ws, size_t ws_bytes,
+                                    void* stream, bool dry = false) {
+  csa2_status st = check_dims(d);
+  if (st) return st;
+  if ((st = check_queries(q))) return st;
+  if (flags & ~CSA2_POOL_WS_FROM_SCAN) return fail(CSA2_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
+  const bool small = pool_small(d, q);
+  if (!small && (st = check_ws(pool_wsp, pool_ws_bytes, pool_ws(d, q)))) return st;
+  // a Top-K of more than 1024 positions from a given pool is selected apart
+  // (k_topk_keys): its positions step does not fit beside the attention
+  const bool apart = !small && d->topk > 1024;
+  if (!block_scores || !pos_keys) return fail(CSA2_ERR_INVALID_ARG, "required pointer is NULL");
+  if (apart && ((st = check_block_scores(d, q, block_scores, ld_block_scores)) ||
+                (st = check_pos_keys(d, q, pos_keys, ld_pos_keys))))
+    return st;
+  const AttendSel sel{block_scores, ld_block_scores, pos_keys, ld_pos_keys, pool_blocks, pool_count, !small};
+  // every argument is checked before the first launch
+  if ((st = attend(d, q, q_lat, q_rope, softmax_scale, kv_codes, kv_scales, kv_rope, topk_pos, topk_count, swa_kv,
+                   swa_base, out, lse, ws, ws_bytes, stream, true, nullptr, apart ? nullptr : &sel)))
+    return st;
+  if (dry) return CSA2_OK;
+  if (!small && (st = run_pool(d, q, block_scores, ld_block_scores, pool_blocks, pool_count, pool_wsp,
+                               (flags & CSA2_POOL_WS_FROM_SCAN) != 0, stream, pos_keys, ld_pos_keys,
+                               apart ? topk_pos : nullptr, apart ? topk_count : nullptr)))
+    return st;
+  return attend(d, q, q_lat, q_rope, softmax_scale, kv_codes, kv_scales, kv_rope, topk_pos, topk_count, swa_kv,
+                swa_base, out, lse, ws, ws_bytes, stream, false, nullptr, apart ? nullptr : &sel);
+}
+
 csa2_status csa2_pool_topk_attend(const csa2_dims* d, const csa2_queries* q, const float* block_scores,
                                   int64_t ld_block_scores, const uint32_t* pos_keys, int64_t ld_pos_keys,
                                   int32_t* pool_blocks, int32_t* pool_count, int32_t* topk_pos, int32_t* topk_count,
                                   const uint16_t* q_lat, const uint16_t* q_rope, float softmax_scale,
                                   const uint8_t* kv_codes, const uint8_t* kv_scales, const uint16_t* kv_rope,
-                                  const uint16_t* swa_kv, const int64_t* swa_base, float* out, float* lse, void* ws,
-                                  size_t ws_bytes, void* stream) {
-  const AttendSel sel{block_scores, ld_block_scores, pos_keys, ld_pos_keys, pool_blocks, pool_count};
-  return attend(d, q, q_lat, q_rope, softmax_scale, kv_codes, kv_scales, kv_rope, topk_pos, topk_count, swa_kv,
-                swa_base, out, lse, ws, ws_bytes, stream, false, nullptr, &sel);
+                                  const uint16_t* swa_kv, const int64_t* swa_base, float* out, float* lse,
+                                  void* pool_ws, size_t pool_ws_bytes, int32_t flags, void* ws, size_t ws_bytes,
+                                  void* stream) {
+  return pool_topk_attend(d, q, block_scores, ld_block_scores, pos_keys, ld_pos_keys, pool_blocks, pool_count,
+                          topk_pos, topk_count, q_lat, q_rope, softmax_scale, kv_codes, kv_scales, kv_rope, swa_kv,
+                          swa_base, out, lse, pool_ws, pool_ws_bytes, flags, ws, ws_bytes, stream);
 }
 
 csa2_status csa2_page_rows(const csa2_pages* pages, int64_t n, const int64_t* table_off, const int32_t* pos,
@@ -926,9 +968,9 @@ static csa2_status decode_step(const csa2_dims* d, const csa2_queries* q, int32_
   // every stage's arguments are checked before the first launch
   for (int pass = 0; pass < 2; ++pass) {
     const bool dry = pass == 0;
-    // a Full layer with small pools selects them inside the attention kernel
-    const bool fused = mode == CSA2_LAYER_FULL && !pages && pool_small(d, q);
-    AttendSel sel{};
+    // a Full layer of unpaged planes selects its Top-K (and a small pool)
+    // inside the attention kernel
+    const bool fused = mode == CSA2_LAYER_FULL && !pages;
     if (mode == CSA2_LAYER_FULL) {
       // the scan also keeps every position's score; the Top-K then comes
       // from those scores (the layer's own query: what Reindex would compute)
@@ -938,16 +980,22 @@ static csa2_status decode_step(const csa2_dims* d, const csa2_queries* q, int32_
       if ((st = index_full(d, q, idx_q, idx_q_scales, idx_w, idx_k, idx_k_scales, fp4, pool_blocks, pool_count,
                            nullptr, 0, w_full, n_idx, stream, dry, pages, pkey, topk_pos, topk_count, fused)))
         return st;
-      sel = AttendSel{(const float*)(w_full + pool_ws(d, q)), full_ldb(d, q), pkey, full_ldpk(d, q), pool_blocks,
-                      pool_count};
+      if (fused) {
+        if ((st = pool_topk_attend(d, q, (const float*)(w_full + pool_ws(d, q)), full_ldb(d, q), pkey,
+                                   full_ldpk(d, q), pool_blocks, pool_count, topk_pos, topk_count, q_lat, q_rope,
+                                   softmax_scale, kv_codes, kv_scales, kv_rope, swa_kv, swa_base, out, lse, w_full,
+                                   pool_ws(d, q), CSA2_POOL_WS_FROM_SCAN, attend_ws(d, q) ? w_att : nullptr, n_att,
+                                   stream, dry)))
+          return st;
+        continue;
+      }
     }
     if (mode == CSA2_LAYER_REINDEX &&
         (st = index_reindex(d, q, idx_q, idx_q_scales, idx_w, idx_k, idx_k_scales, fp4, pool_blocks, pool_count,
                             topk_pos, topk_count, nullptr, w_re, n_re, stream, dry, pages, counters)))
       return st;
     if ((st = attend(d, q, q_lat, q_rope, softmax_scale, kv_codes, kv_scales, kv_rope, topk_pos, topk_count, swa_kv,
-                     swa_base, out, lse, attend_ws(d, q) ? w_att : nullptr, n_att, stream, dry, pages,
-                     fused ? &sel : nullptr)))
+                     swa_base, out, lse, attend_ws(d, q) ? w_att : nullptr, n_att, stream, dry, pages)))
       return st;
   }
   return CSA2_OK;

@@ -58,10 +58,11 @@ constexpr int kNW = kAttendWaves;             // 8 waves
 constexpr int kNT = 64 * kNW;                 // 512 threads
 constexpr int kLS = kLatent + 8;              // f16 row stride of the latent image
 constexpr int kPS = kTE + 4;                  // f16 row stride of the P tile (rows on distinct banks)
-constexpr int kOS = kLatent + 16;             // f32 row stride of the output rows in LDS
+constexpr int kOS = kLatent + 4;              // f32 row stride of the output rows in LDS (a lane group's
+                                              // rows 4 gq + i then fall on distinct banks)
 constexpr int kMaxRows = kAttendMaxTiles * kTE;          // rows of one split, at most
 constexpr int kRowPer = kMaxRows / kNT;                  // rows resolved per thread
-constexpr int kItems = kTE * 32 / kNT;        // (entry, 16-channel group) items per thread
+constexpr int kItems = kTE * 64 / kNT;        // (entry, 8-channel half group) items per thread
 constexpr int kWinRow = kKeyDim * 2;          // bytes of a window row
 constexpr uint32_t kOob = 0xFFFFFF00u;        // a buffer offset past any row: reads zero
 constexpr int32_t kNoRow = 0x7FFFFFFF;
@@ -172,8 +173,9 @@ __device__ __forceinline__ float max_rows4(float x) {
 // selection is repeated by each such split, which costs a few microseconds
 // of one CU each, against a launch and a round trip for the positions; the
 // split holding the first kept-entry tile of head group 0 writes the pool
-// and the Top-K out.
-template <int SEL>
+// and the Top-K out.  FROM_POOL: the pool is given (a query too long for
+// one workgroup's selection), the splits select only its Top-K.
+template <int SEL, bool FROM_POOL>
 __global__ __launch_bounds__(kNT) void k_attend(AttendArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char s_mem[kLdsBytes];
   _Float16* s_lat = reinterpret_cast<_Float16*>(s_mem + kOffLat);   // [64][kLS]
@@ -201,6 +203,7 @@ __global__ __launch_bounds__(kNT) void k_attend(AttendArgs a) {
   // trip (a use between them would wait for the first alone)
   const int n = load_uniform(a.n_visible + q);
   const int tcount = SEL ? 0 : load_uniform(a.topk_count + q);
+  const int pcount = FROM_POOL ? load_uniform(a.pool_count + q) : 0;
   const int64_t sbase = load_uniform(a.seq_base + q);
   const int64_t wbase = load_uniform(a.swa_base + q);
 
@@ -271,7 +274,7 @@ __global__ __launch_bounds__(kNT) void k_attend(AttendArgs a) {
   const v4u rs_rope = rsrc_of(a.kv_rope + kbase * kRope, krows * (kRope * 2));
   const v4u rs_win = rsrc_of(a.swa_kv + wbase * kKeyDim, (uint32_t)Ew * kWinRow);
   // row codes of the split's tiles (>= 0: cache row, < 0: window row -1 - code)
-  asm volatile("" ::"s"(n), "s"(tcount), "s"(sbase), "s"(wbase));
+  asm volatile("" ::"s"(n), "s"(tcount), "s"(pcount), "s"(sbase), "s"(wbase));
 #pragma unroll
   for (int j = 0; j < kRowPer; ++j) {
     const int idx = tid + j * kNT;
@@ -296,17 +299,23 @@ __global__ __launch_bounds__(kNT) void k_attend(AttendArgs a) {
       const int s_first = max(t_begin, nwt);
       const bool lead = hg == 0 && t_begin <= nwt;  // holds the first kept-entry tile
       PoolTopkOut o;
-      o.pool = lead ? a.pool_blocks + (int64_t)q * a.pool : nullptr;
-      o.pool_count = lead ? a.pool_count + q : nullptr;
+      o.pool = lead && !FROM_POOL ? a.pool_blocks + (int64_t)q * a.pool : nullptr;
+      o.pool_count = lead && !FROM_POOL ? a.pool_count + q : nullptr;
       o.topk = lead ? a.topk_out + (int64_t)q * K : nullptr;
       o.topk_count = lead ? a.topk_count_out + q : nullptr;
       o.rows = s_row + (s_first - t_begin) * kTE;
       o.r0 = (s_first - nwt) * kTE;
       o.r1 = (t_end - nwt) * kTE;
-      Es = min((int)pool_topk_select<SEL>(a.bscore + (int64_t)q * a.ld_bs, (int)a.ld_bs, (c + 7) >> 3, a.pool, K,
-                                          a.pkey + (int64_t)q * a.ld_pkey, o,
-                                          *reinterpret_cast<PoolTopkLds<SEL>*>(s_mem + kOffLat), load_q_sel),
-               K);
+      PoolTopkLds<SEL>& sl = *reinterpret_cast<PoolTopkLds<SEL>*>(s_mem + kOffLat);
+      uint32_t kept;
+      if constexpr (FROM_POOL)
+        kept = topk_from_pool<SEL>(a.pool_blocks + (int64_t)q * a.pool, min(pcount, a.pool), a.pool,
+                                   a.bscore + (int64_t)q * a.ld_bs, a.pkey + (int64_t)q * a.ld_pkey, K, o, nullptr,
+                                   sl, load_q_sel);
+      else
+        kept = pool_topk_select<SEL>(a.bscore + (int64_t)q * a.ld_bs, (int)a.ld_bs, (c + 7) >> 3, a.pool, K,
+                                     a.pkey + (int64_t)q * a.ld_pkey, o, sl, load_q_sel);
+      Es = min((int)kept, K);
       wait_vmcnt<0>();                             // this wave's query rows have landed
     }
   }
@@ -425,17 +434,17 @@ __global__ __launch_bounds__(kNT) void k_attend(AttendArgs a) {
           *p = v4u{bf16x2_to_h2(x[0]), bf16x2_to_h2(x[1]), bf16x2_to_h2(x[2]), bf16x2_to_h2(x[3])};
         }
       } else {
-        // kept entries: codes x scale from the staging slot
+        // kept entries: codes x scale from the staging slot (a lane writes
+        // 16 consecutive bytes of the image, so a wave's writes are whole rows)
         const unsigned char* st = s_mem + kOffStage + (ti & 1) * kStageSlot;
 #pragma unroll
         for (int k = 0; k < kItems; ++k) {
-          const int it = tid + k * kNT, e = it >> 5, grp = it & 31;
-          const v2u cw = *reinterpret_cast<const v2u*>(st + e * kCodeBytes + grp * 8);
-          const _Float16 sh = (_Float16)e4m3_to_float(st[kCodeStage + e * sbytes + (grp >> gshift)]);   // exact
+          const int it = tid + k * kNT, e = it >> 6, hg8 = it & 63;
+          const uint32_t cw = *reinterpret_cast<const uint32_t*>(st + e * kCodeBytes + hg8 * 4);
+          const _Float16 sh = (_Float16)e4m3_to_float(st[kCodeStage + e * sbytes + ((hg8 >> 1) >> gshift)]);   // exact
           const v2h s2 = {sh, sh};
-          v4u* dk = reinterpret_cast<v4u*>(s_lat + e * kLS + grp * 16);
-          dk[0] = v4u{fp4_byte_h2<0>(cw[0], s2), fp4_byte_h2<1>(cw[0], s2), fp4_byte_h2<2>(cw[0], s2), fp4_byte_h2<3>(cw[0], s2)};
-          dk[1] = v4u{fp4_byte_h2<0>(cw[1], s2), fp4_byte_h2<1>(cw[1], s2), fp4_byte_h2<2>(cw[1], s2), fp4_byte_h2<3>(cw[1], s2)};
+          *reinterpret_cast<v4u*>(s_lat + e * kLS + hg8 * 8) =
+              v4u{fp4_byte_h2<0>(cw, s2), fp4_byte_h2<1>(cw, s2), fp4_byte_h2<2>(cw, s2), fp4_byte_h2<3>(cw, s2)};
         }
       }
     }
@@ -614,15 +623,24 @@ hipError_t launch_attend(const AttendArgs& a, hipStream_t s) {
     return hipErrorInvalidValue;
   const dim3 grid((unsigned)(a.n_q * a.head_groups * a.splits));
   if (!a.bscore) {
-    hipLaunchKernelGGL(k_attend<0>, grid, dim3(kNT), 0, s, a);
+    hipLaunchKernelGGL((k_attend<0, false>), grid, dim3(kNT), 0, s, a);
   } else {
-    // (a query of at most kMaxCand blocks, pool and Top-K within 2048, no
-    // page table: checked by the caller)
+    // (without a given pool: a query of at most kMaxCand blocks; pool and
+    // Top-K within 2048, no page table: checked by the caller)
     if (a.pages || a.pool > 2048 || a.topk > 2048 || !a.pkey || !a.pool_blocks || !a.pool_count || !a.topk_out ||
         !a.topk_count_out)
       return hipErrorInvalidValue;
-    if (a.topk <= kTkThreads) hipLaunchKernelGGL(k_attend<2>, grid, dim3(kNT), 0, s, a);
-    else hipLaunchKernelGGL(k_attend<4>, grid, dim3(kNT), 0, s, a);
+    if (a.sel_from_pool) {
+      // (K <= 1024: the positions step of a larger K does not fit the
+      // registers beside the attention's; the caller selects it apart)
+      if (a.topk <= kTkThreads) hipLaunchKernelGGL((k_attend<1, true>), grid, dim3(kNT), 0, s, a);
+      else if (a.topk <= 2 * kTkThreads) hipLaunchKernelGGL((k_attend<2, true>), grid, dim3(kNT), 0, s, a);
+      else return hipErrorInvalidValue;
+    } else if (a.topk <= kTkThreads) {
+      hipLaunchKernelGGL((k_attend<2, false>), grid, dim3(kNT), 0, s, a);
+    } else {
+      hipLaunchKernelGGL((k_attend<4, false>), grid, dim3(kNT), 0, s, a);
+    }
   }
   if (a.splits > 1) {
     hipError_t e = hipGetLastError();

@@ -99,6 +99,7 @@ struct AttendArgs {
   int32_t* pool_count;
   int32_t* topk_out;         // [n_q, topk]
   int32_t* topk_count_out;
+  int sel_from_pool;         // 1: the pool is given (pool_blocks, pool_count are read), only the Top-K is selected
 };
 
 // A Full layer's Top-K from the Full scan's own scores (the same indexer

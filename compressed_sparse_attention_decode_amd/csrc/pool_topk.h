@@ -140,4 +140,45 @@ __device__ __forceinline__ uint32_t pool_topk_select(const float* bs, int ld, in
   }
 }
 
+// A Full layer's Top-K of a pool selected before (csa2_index_pool's
+// output): the K best blocks of the pool by (block score desc, block id asc),
+// then the K best of their positions (topk_positions.h).  The blocks suffice
+// for the same reason as above.  Called by all kTkThreads threads; pool: the
+// query's P block ids ascending, pcnt valid; bs: its block scores; pk: its
+// position keys.  o.pool / o.pool_count are not written; out_s (optional)
+// receives the kept positions' scores.  Returns the Top-K count.
+template <int BPT, typename AfterKeys>
+__device__ __forceinline__ uint32_t topk_from_pool(const int32_t* pool, int pcnt, int P, const float* bs,
+                                                   const uint32_t* pk, int K, const PoolTopkOut& o, float* out_s,
+                                                   PoolTopkLds<BPT>& L, AfterKeys&& after_keys) {
+  constexpr int PB = 2048 / kTkThreads;             // pool slots per thread (P <= 2048)
+  const int tid = threadIdx.x;
+  int32_t blk[PB];
+#pragma unroll
+  for (int k = 0; k < PB; ++k) blk[k] = pool[min(tid * PB + k, P - 1)];
+#pragma unroll
+  for (int k = 0; k < PB; ++k) asm volatile("" : "+v"(blk[k]));
+  float bv[PB];
+#pragma unroll
+  for (int k = 0; k < PB; ++k) bv[k] = bs[tid * PB + k < pcnt ? max(blk[k], 0) : 0];
+  uint32_t bkey[PB];
+#pragma unroll
+  for (int k = 0; k < PB; ++k) bkey[k] = tid * PB + k < pcnt ? order_key(bv[k]) : 0u;
+#pragma unroll
+  for (int k = 0; k < PB; ++k) asm volatile("" : "+v"(bkey[k]));   // the keys are complete here
+  after_keys();
+  const TopkCut bc = radix_topk<PB>(bkey, K, 0, L.radix);
+  uint32_t flags = 0;
+#pragma unroll
+  for (int k = 0; k < PB; ++k) flags |= (uint32_t)(bkey[k] >= bc.tt) << k;
+  uint32_t nsel;
+  uint32_t before = block_exclusive_scan<kTkThreads>(__builtin_popcount(flags), L.scan, &nsel);
+#pragma unroll
+  for (int k = 0; k < PB; ++k)
+    if (flags >> k & 1u) L.blk[before++] = blk[k];   // ascending: the pool is ascending
+  __syncthreads();
+  return topk_positions<BPT>(L.blk, nsel, pk, K, o.topk, out_s, o.topk_count, L.scan, L.radix, o.rows, o.r0,
+                             o.r1);
+}
+
 }  // namespace csa2

@@ -31,6 +31,7 @@
 #include "radix_topk.h"
 #include "select_common.h"
 #include "topk_positions.h"
+#include "pool_topk.h"
 
 namespace csa2 {
 namespace {
@@ -361,43 +362,19 @@ hipError_t launch_d(const ReindexArgs& a, hipStream_t s) {
 // order), so the result is the same set.
 template <int BPT>
 __global__ __launch_bounds__(kTkThreads) void k_topk_keys(TopkKeysArgs a) {
-  constexpr int PB = 2048 / kTkThreads;             // pool slots per thread (P <= 2048)
-  constexpr int PP = BPT * kBlock;                  // position slots per thread
-  __shared__ int32_t s_blk[kTkThreads * BPT];
-  __shared__ uint32_t s_scan[kTkWaves];
-  const int q = blockIdx.x, tid = threadIdx.x;
+  __shared__ PoolTopkLds<BPT> s_sel;
+  const int q = blockIdx.x;
   const int P = a.pool, K = a.topk;
-  const int32_t* pool = a.pool_blocks + (int64_t)q * P;
-  const int pcnt = min(load_uniform(a.pool_count + q), P);
-
-  // 1. the pool's block scores (slots past the count: key 0)
-  int32_t blk[PB];
-#pragma unroll
-  for (int k = 0; k < PB; ++k) blk[k] = pool[min(tid * PB + k, P - 1)];
-#pragma unroll
-  for (int k = 0; k < PB; ++k) asm volatile("" : "+v"(blk[k]));
-  const float* bs = a.bscore + (int64_t)q * a.ld;
-  float bv[PB];
-#pragma unroll
-  for (int k = 0; k < PB; ++k) bv[k] = bs[tid * PB + k < pcnt ? max(blk[k], 0) : 0];
-  uint32_t bkey[PB];
-#pragma unroll
-  for (int k = 0; k < PB; ++k) bkey[k] = tid * PB + k < pcnt ? order_key(bv[k]) : 0u;
-  const TopkCut bc = radix_topk<PB>(bkey, K);
-  uint32_t flags = 0;
-#pragma unroll
-  for (int k = 0; k < PB; ++k) flags |= (uint32_t)(bkey[k] >= bc.tt) << k;
-  uint32_t nsel;
-  uint32_t before = block_exclusive_scan<kTkThreads>(__builtin_popcount(flags), s_scan, &nsel);
-#pragma unroll
-  for (int k = 0; k < PB; ++k)
-    if (flags >> k & 1u) s_blk[before++] = blk[k];     // ascending: the pool is ascending
-  __syncthreads();
-
-  // 2. the K best positions of those blocks
-  __shared__ RadixLds s_radix;
-  topk_positions<BPT>(s_blk, nsel, a.pkey + (int64_t)q * a.ld_pkey, K, a.topk_pos + (int64_t)q * K,
-                      a.topk_scores ? a.topk_scores + (int64_t)q * K : nullptr, a.topk_count + q, s_scan, s_radix);
+  PoolTopkOut o;
+  o.pool = nullptr;
+  o.pool_count = nullptr;
+  o.topk = a.topk_pos + (int64_t)q * K;
+  o.topk_count = a.topk_count + q;
+  o.rows = nullptr;
+  o.r0 = o.r1 = 0;
+  topk_from_pool<BPT>(a.pool_blocks + (int64_t)q * P, min(load_uniform(a.pool_count + q), P), P,
+                      a.bscore + (int64_t)q * a.ld, a.pkey + (int64_t)q * a.ld_pkey, K, o,
+                      a.topk_scores ? a.topk_scores + (int64_t)q * K : nullptr, s_sel, [] {});
 }
 
 }  // namespace

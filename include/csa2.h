@@ -474,30 +474,37 @@ csa2_status csa2_attend_paged(const csa2_dims* dims, const csa2_queries* q, cons
                               const uint16_t* swa_kv, const int64_t* swa_base,
                               float* out, float* lse, void* ws, size_t ws_bytes, void* stream);
 
-/* csa2_index_pool_topk followed by csa2_attend on its Top-K, in one launch
- * sequence for queries of at most 16,384 blocks (contexts up to about 131K
- * positions): every attention workgroup that holds kept-entry tiles selects
- * its query's pool and Full-layer Top-K itself from the scan's scores (the
- * same selection as csa2_index_pool_topk's one-workgroup kernel, repeated by
- * each such workgroup) and gathers its tiles' entries at once, so no launch
- * and no round trip for the positions sit between the selection and the
- * gathers.  The workgroup holding head group 0's first kept-entry tile
- * writes pool_blocks, pool_count, topk_pos and topk_count, as
- * csa2_index_pool_topk writes them; out and lse are csa2_attend's on that
- * Top-K.
+/* csa2_index_pool_topk followed by csa2_attend on its Top-K, with the Top-K
+ * selected inside the attention kernel: every attention workgroup that
+ * holds kept-entry tiles selects its query's Top-K itself from the scan's
+ * scores and gathers its tiles' entries at once, so no launch and no round
+ * trip for the positions sit between the selection and the gathers.  When
+ * every query has at most 16,384 blocks (contexts up to about 131K
+ * positions) the pool is selected there too (the same selection as
+ * csa2_index_pool_topk's one-workgroup kernel, repeated by each such
+ * workgroup): one attention launch for the whole chain.  Otherwise the
+ * chunked pool kernels run first and the attention workgroups select the
+ * Top-K of that pool (as csa2_index_topk_keys).  The workgroup holding head
+ * group 0's first kept-entry tile writes pool_blocks, pool_count (small
+ * pools), topk_pos and topk_count, as csa2_index_pool_topk writes them; out
+ * and lse are csa2_attend's on that Top-K.
  *   block_scores, pos_keys   as written by csa2_index_scan_keys
  *   q_lat ... lse            as in csa2_attend (topk_pos, topk_count are
  *                            outputs here)
+ *   pool_ws, pool_ws_bytes, flags  as ws, ws_bytes, flags of
+ *                            csa2_index_pool (read only for the chunked
+ *                            kernels; NULL and 0 are accepted for small
+ *                            pools)
  *   ws, ws_bytes             csa2_attend_workspace_size bytes, as in csa2_attend
- * Errors: CSA2_ERR_UNSUPPORTED when max_visible allows more than 16,384
- * blocks per query (or CSA2_POOL_SMALL=0 forces the chunked pool kernels):
- * call csa2_index_pool_topk and csa2_attend instead; otherwise as those. */
+ * Errors: CSA2_ERR_UNSUPPORTED for paged planes (call csa2_index_pool_topk
+ * and csa2_attend_paged); otherwise as those calls. */
 csa2_status csa2_pool_topk_attend(const csa2_dims* dims, const csa2_queries* q, const float* block_scores,
                                   int64_t ld_block_scores, const uint32_t* pos_keys, int64_t ld_pos_keys,
                                   int32_t* pool_blocks, int32_t* pool_count, int32_t* topk_pos, int32_t* topk_count,
                                   const uint16_t* q_lat, const uint16_t* q_rope, float softmax_scale,
                                   const uint8_t* kv_codes, const uint8_t* kv_scales, const uint16_t* kv_rope,
                                   const uint16_t* swa_kv, const int64_t* swa_base, float* out, float* lse,
+                                  void* pool_ws, size_t pool_ws_bytes, int32_t flags,
                                   void* ws, size_t ws_bytes, void* stream);
 
 /* Rows of paged positions, so that csa2_encode_kv (through dst_row) appends
@@ -516,10 +523,10 @@ csa2_status csa2_page_rows(const csa2_pages* pages, int64_t n, const int64_t* ta
  * only attends over the inherited index set with its own main Q).  The call
  * checks every stage's arguments, then enqueues, on `stream`:
  *   CSA2_LAYER_FULL     csa2_index_scan_keys, then csa2_pool_topk_attend
- *                       (unpaged planes, at most 16,384 blocks per query)
- *                       or csa2_index_pool_topk + csa2_attend (pool_blocks,
- *                       pool_count, and topk_pos, topk_count: the same set
- *                       as csa2_index_reindex with the same indexer query);
+ *                       (unpaged planes) or csa2_index_pool_topk +
+ *                       csa2_attend_paged (pool_blocks, pool_count, and
+ *                       topk_pos, topk_count: the same set as
+ *                       csa2_index_reindex with the same indexer query);
  *   CSA2_LAYER_REINDEX  csa2_index_reindex on the given pool, csa2_attend;
  *   CSA2_LAYER_REUSE    csa2_attend on the given topk_pos / topk_count
  *                       (the idx_* arguments may be NULL).

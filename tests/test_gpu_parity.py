@@ -322,12 +322,17 @@ def test_pool_topk_matches_separate_calls(case, small, monkeypatch):
         assert torch.equal(pool[qi, :k], pool2[qi, :k]), f"{name} q{qi}: pool differs"
 
 
-def test_pool_topk_attend_matches_separate_calls(case):
-    """csa2_pool_topk_attend (the pool and the Full layer's Top-K selected
-    inside the attention kernel, by every workgroup with kept-entry tiles)
-    writes the same pool, Top-K, output and log-sum-exp, bit for bit, as
-    csa2_index_pool_topk followed by csa2_attend."""
+@pytest.mark.parametrize("small", ["1", "0"])
+def test_pool_topk_attend_matches_separate_calls(case, small, monkeypatch):
+    """csa2_pool_topk_attend (the Full layer's Top-K, and for small pools the
+    pool too, selected inside the attention kernel by every workgroup with
+    kept-entry tiles; with CSA2_POOL_SMALL=0 the chunked pool kernels run
+    first and the attention selects the Top-K of their pool, or for K above
+    1024 the Top-K kernel does) writes the same pool, Top-K, output and
+    log-sum-exp, bit for bit, as csa2_index_pool_topk followed by
+    csa2_attend."""
     name, g, lay = case
+    monkeypatch.setenv("CSA2_POOL_SMALL", small)
     csa2, w = g.csa2, g.w
     q, wt = g.iq(0)
     idx_k, codes, scales, kv_rope, swa_kv = g.planes[0]
@@ -345,7 +350,7 @@ def test_pool_topk_attend_matches_separate_calls(case):
     out2 = fill((w.n_q, w.dims.n_heads, 512), torch.float32)
     lse2 = fill((w.n_q, w.dims.n_heads), torch.float32)
     csa2.pool_topk_attend(g.dims, g.batch, bs, pk, ql, qr, 1.0, codes, scales, kv_rope, swa_kv, g.swa_base,
-                          pool2, cnt2, tk2, tc2, out2, lse2)
+                          pool2, cnt2, tk2, tc2, out2, lse2, pool_ws=pws, from_scan=True)
     torch.cuda.synchronize()
     assert torch.equal(cnt, cnt2), f"{name}: pool counts differ"
     for qi in range(w.n_q):
@@ -496,15 +501,14 @@ def _full_topk(g):
     pws = torch.zeros(csa2.workspace_pool(g.dims, g.batch) + 256, dtype=torch.uint8, device="cuda")
     csa2.index_scan(g.dims, g.batch, q, wt, g.planes[0][0], bs, pool_ws=pws, pos_keys=pk)
     pool, cnt, tk, tc = csa2.index_pool_topk(g.dims, g.batch, bs, pk, ws=pws, from_scan=True)
-    if os.environ.get("CSA2_POOL_SMALL") != "0":
-        # the selection inside the attention kernel: the same pool and Top-K
-        idx_k, codes, scales, kv_rope, swa_kv = g.planes[0]
-        ql, qr = g.mq(0)
-        pool2, cnt2, tk2, tc2, _, _ = csa2.pool_topk_attend(g.dims, g.batch, bs, pk, ql, qr, 1.0, codes, scales,
-                                                             kv_rope, swa_kv, g.swa_base)
-        torch.cuda.synchronize()
-        assert torch.equal(cnt, cnt2) and torch.equal(tc, tc2) and torch.equal(tk, tk2)
-        assert torch.equal(pool[0, :cnt.item()], pool2[0, :cnt.item()])
+    # the selection inside the attention kernel: the same pool and Top-K
+    idx_k, codes, scales, kv_rope, swa_kv = g.planes[0]
+    ql, qr = g.mq(0)
+    pool2, cnt2, tk2, tc2, _, _ = csa2.pool_topk_attend(g.dims, g.batch, bs, pk, ql, qr, 1.0, codes, scales,
+                                                         kv_rope, swa_kv, g.swa_base, pool_ws=pws, from_scan=True)
+    torch.cuda.synchronize()
+    assert torch.equal(cnt, cnt2) and torch.equal(tc, tc2) and torch.equal(tk, tk2)
+    assert torch.equal(pool[0, :cnt.item()], pool2[0, :cnt.item()])
     torch.cuda.synchronize()
     return pool.cpu().numpy()[0, :cnt.item()], tk.cpu().numpy()[0, :tc.item()]
 
