@@ -456,13 +456,28 @@ __global__ __launch_bounds__(kNT) void k_attend(AttendArgs a) {
       v4f s0 = {0.0f, 0.0f, 0.0f, 0.0f}, s1 = {0.0f, 0.0f, 0.0f, 0.0f};
       const int er = 16 * qw + col;
       const _Float16* kr = s_lat + er * kLS + gq * 8;
+      // eight K fragments in flight: each read's LDS latency hides behind
+      // the MFMAs of the seven before it
+      constexpr int kKF = 8;
+      v4u kf[kKF];
 #pragma unroll
-      for (int ks = 0; ks < kLatent / 32; ks += 2) {
-        const v8h k0 = __builtin_bit_cast(v8h, *reinterpret_cast<const v4u*>(kr + ks * 32));
-        const v8h k1 = __builtin_bit_cast(v8h, *reinterpret_cast<const v4u*>(kr + ks * 32 + 32));
-        s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(k0, qf[ks], s0, 0, 0, 0);
-        s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(k1, qf[ks + 1], s1, 0, 0, 0);
+      for (int j = 0; j < kKF; ++j) kf[j] = *reinterpret_cast<const v4u*>(kr + j * 32);
+#pragma unroll
+      for (int ks = 0; ks < kLatent / 32; ++ks) {
+        const v8h k = __builtin_bit_cast(v8h, kf[ks % kKF]);
+        if (ks + kKF < kLatent / 32) kf[ks % kKF] = *reinterpret_cast<const v4u*>(kr + (ks + kKF) * 32);
+        if (ks & 1) s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(k, qf[ks], s1, 0, 0, 0);
+        else s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(k, qf[ks], s0, 0, 0, 0);
       }
+      // keep that order: the scheduler otherwise trades the reads in flight
+      // for registers and waits out every read's latency
+      __builtin_amdgcn_sched_group_barrier(0x100, kKF, 0);
+#pragma unroll
+      for (int j = 0; j < kLatent / 32 - kKF; ++j) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, kKF, 0);
       {
         const unsigned char* rr = rope + er * (kRope * 2);
         const v8bf r0 = __builtin_bit_cast(v8bf, *reinterpret_cast<const v4u*>(rr + ((gq ^ (er & 7)) * 16)));

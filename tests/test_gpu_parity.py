@@ -322,17 +322,20 @@ def test_pool_topk_matches_separate_calls(case, small, monkeypatch):
         assert torch.equal(pool[qi, :k], pool2[qi, :k]), f"{name} q{qi}: pool differs"
 
 
-@pytest.mark.parametrize("small", ["1", "0"])
-def test_pool_topk_attend_matches_separate_calls(case, small, monkeypatch):
+@pytest.mark.parametrize("small,splits", [("1", ""), ("0", ""), ("1", "1"), ("1", "3"), ("0", "2")])
+def test_pool_topk_attend_matches_separate_calls(case, small, splits, monkeypatch):
     """csa2_pool_topk_attend (the Full layer's Top-K, and for small pools the
     pool too, selected inside the attention kernel by every workgroup with
     kept-entry tiles; with CSA2_POOL_SMALL=0 the chunked pool kernels run
     first and the attention selects the Top-K of their pool, or for K above
     1024 the Top-K kernel does) writes the same pool, Top-K, output and
     log-sum-exp, bit for bit, as csa2_index_pool_topk followed by
-    csa2_attend."""
+    csa2_attend.  CSA2_ATTEND_SPLITS forces splits of several tiles, so that
+    window and kept-entry tiles share a workgroup (as at large batch)."""
     name, g, lay = case
     monkeypatch.setenv("CSA2_POOL_SMALL", small)
+    if splits:
+        monkeypatch.setenv("CSA2_ATTEND_SPLITS", splits)
     csa2, w = g.csa2, g.w
     q, wt = g.iq(0)
     idx_k, codes, scales, kv_rope, swa_kv = g.planes[0]
