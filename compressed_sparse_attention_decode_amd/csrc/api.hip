@@ -186,11 +186,13 @@ size_t reindex_ws(const csa2_dims* d, const csa2_queries* q) {
 
 // Pool blocks per Reindex scoring workgroup: 32 when 32-block workgroups
 // fit in one per CU (a batch of a few queries: more of them share the
-// scoring), 64 when 64-block workgroups fit in two per CU, else 128 (the
-// grid takes several rounds, and fewer, longer workgroups are faster).
+// scoring), 64 when 64-block workgroups fit in two per CU, 128 when 128-block
+// ones fit in one per CU (their registers allow one), else 256 (one round of
+// one workgroup per CU, where 128-block ones would take two).
 // Measured per Reindex call: 1 query 14.4 / 15.4 us (32 / 64), 8 queries
 // 19.2 / 25.8 us (64 / 32), 32 queries 42.5 / 56.9 us (128 / 64).
-// CSA2_REINDEX_BLOCKS (32, 64 or 128) overrides.  Called after check_device.
+// CSA2_REINDEX_BLOCKS (32, 64, 128 or 256) overrides.  Called after
+// check_device.
 int reindex_blocks_per_wg(const csa2_dims* d, const csa2_queries* q) {
   int dev = 0;
   int bpw = kReindexBlocks;
@@ -198,11 +200,14 @@ int reindex_blocks_per_wg(const csa2_dims* d, const csa2_queries* q) {
     const int64_t cus = g_cus[dev];
     const int64_t wgs32 = (int64_t)q->n_q * ((d->pool_blocks + kReindexBlocksNarrow - 1) / kReindexBlocksNarrow);
     const int64_t wgs64 = (int64_t)q->n_q * ((d->pool_blocks + kReindexBlocks - 1) / kReindexBlocks);
-    bpw = wgs32 <= cus ? kReindexBlocksNarrow : wgs64 <= 2 * cus ? kReindexBlocks : kReindexBlocksWide;
+    const int64_t wgs128 = (int64_t)q->n_q * ((d->pool_blocks + kReindexBlocksWide - 1) / kReindexBlocksWide);
+    bpw = wgs32 <= cus ? kReindexBlocksNarrow
+        : wgs64 <= 2 * cus ? kReindexBlocks
+        : wgs128 <= cus ? kReindexBlocksWide : kReindexBlocksHuge;
   }
   if (const char* env = getenv("CSA2_REINDEX_BLOCKS")) {
     const int v = atoi(env);
-    if (v == kReindexBlocks || v == kReindexBlocksWide || v == kReindexBlocksNarrow) bpw = v;
+    if (v == kReindexBlocks || v == kReindexBlocksWide || v == kReindexBlocksNarrow || v == kReindexBlocksHuge) bpw = v;
   }
   return bpw;
 }

@@ -143,6 +143,7 @@ constexpr int kAttendMaxTiles = 48;    // tiles of one query: 1024 / 64 window +
 constexpr int kReindexBlocks = 64;     // pool blocks per Reindex scoring workgroup (one-round grids)
 constexpr int kReindexBlocksWide = 128;   // ... when 64-block workgroups would exceed two per CU
 constexpr int kReindexBlocksNarrow = 32;  // ... when 32-block workgroups fit in one per CU
+constexpr int kReindexBlocksHuge = 256;   // ... when 128-block workgroups would exceed one per CU
 constexpr int kMaxVisible = 1 << 21;   // bound of n_visible
 constexpr int kMaxTokensPerSeq = 64;   // query tokens of one sequence sharing its key stream
 constexpr int kMaxBlocks = kMaxVisible / 8;

@@ -340,6 +340,7 @@ hipError_t launch_db(const ReindexArgs& a, hipStream_t s) {
 
 template <int D, bool F4>
 hipError_t launch_d(const ReindexArgs& a, hipStream_t s) {
+  if (a.blocks_per_wg == kReindexBlocksHuge) return launch_db<D, F4, kReindexBlocksHuge>(a, s);
   if (a.blocks_per_wg == kReindexBlocksWide) return launch_db<D, F4, kReindexBlocksWide>(a, s);
   if (a.blocks_per_wg == kReindexBlocksNarrow) return launch_db<D, F4, kReindexBlocksNarrow>(a, s);
   return launch_db<D, F4, kReindexBlocks>(a, s);

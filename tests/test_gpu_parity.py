@@ -600,16 +600,16 @@ def test_pool_paths_agree(case):
 
 
 def test_reindex_workgroup_sizes_agree(case):
-    """Reindex scored by 32-, 64- and 128-block workgroups (the library picks
-    by batch size) selects the same Top-K with bit-identical scores: the
-    per-position arithmetic does not depend on how the pool is split."""
+    """Reindex scored by 32-, 64-, 128- and 256-block workgroups (the library
+    picks by batch size) selects the same Top-K with bit-identical scores:
+    the per-position arithmetic does not depend on how the pool is split."""
     name, g, lay = case
     csa2 = g.csa2
     pool, cnt, _ = g.full(0)
     q, wt = g.iq(0)
     idx_k = g.planes[0][0]
     outs = []
-    for bpw in ("64", "128", "32"):
+    for bpw in ("64", "128", "32", "256"):
         os.environ["CSA2_REINDEX_BLOCKS"] = bpw
         try:
             ts = torch.empty(g.w.n_q, g.w.dims.topk, dtype=torch.float32, device="cuda")
