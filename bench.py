@@ -257,10 +257,18 @@ class Step:
                                                   lse=self.lse[0], ws=self.ws_a, prepare=True, pages=st.pages)))
             for i, layer in enumerate(self.layers if not self.full_topk else []):
                 q, wt = st.iq(layer)
+                ql, qr = st.mq(layer)
+                if st.pages is None:
+                    # the Reindex keys, the Top-K selected inside the
+                    # attention kernel: csa2_decode_step's Reindex chain
+                    seq.append(("reindex_attend", csa2.reindex_attend(
+                        st.dims, st.batch, q, wt, idx_k, self.pool, self.pcnt, ql, qr, 1.0, codes, scales, kv_rope,
+                        swa_kv, st.swa_base, self.tk[i], self.tc[i], out=self.out[i], lse=self.lse[i],
+                        reindex_ws=self.ws_r, ws=self.ws_a, prepare=True)))
+                    continue
                 seq.append(("reindex", csa2.index_reindex(st.dims, st.batch, q, wt, idx_k, self.pool, self.pcnt,
                                                           topk_pos=self.tk[i], topk_count=self.tc[i],
                                                           ws=self.ws_r, prepare=True, pages=st.pages)))
-                ql, qr = st.mq(layer)
                 seq.append(("attend", csa2.attend(st.dims, st.batch, ql, qr, 1.0, codes, scales, kv_rope,
                                                   self.tk[i], self.tc[i], swa_kv, st.swa_base, out=self.out[i],
                                                   lse=self.lse[i], ws=self.ws_a, prepare=True, pages=st.pages)))

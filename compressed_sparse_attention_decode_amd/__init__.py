@@ -103,6 +103,8 @@ def lib() -> ctypes.CDLL:
             "csa2_index_pool_topk": (I32, [PD, PQ, P, I64, P, I64, P, P, P, P, P, SZ, I32, P]),
             "csa2_pool_topk_attend": (I32, [PD, PQ, P, I64, P, I64, P, P, P, P, P, P, ctypes.c_float, P, P, P,
                                             P, P, P, P, P, SZ, I32, P, SZ, P]),
+            "csa2_reindex_attend": (I32, [PD, PQ, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_float, P, P, P, P, P,
+                                          P, P, P, SZ, P, SZ, P]),
             "csa2_decode_step_noalloc": (I32, [PD, PQ, I32, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_float,
                                                P, P, P, P, P, P, P, P]),
         }
@@ -667,6 +669,57 @@ def pool_topk_attend(dims: Dims, b: Batch, block_scores: torch.Tensor, pos_keys:
             _ptr(lse), pp, pn, POOL_WS_FROM_SCAN if from_scan else 0, wp, wn, _stream(dev))
     call = _issue(lib().csa2_pool_topk_attend, args, (d, q, ws, pool_ws), prepare)
     return call if prepare else (pool_blocks, pool_count, topk_pos, topk_count, out, lse)
+
+
+def reindex_attend(dims: Dims, b: Batch, idx_q, idx_w: torch.Tensor, idx_k,
+                   pool_blocks: torch.Tensor, pool_count: torch.Tensor,
+                   q_lat: torch.Tensor, q_rope: torch.Tensor, softmax_scale: float,
+                   kv_codes: torch.Tensor, kv_scales: torch.Tensor, kv_rope: torch.Tensor,
+                   swa_kv: torch.Tensor, swa_base: torch.Tensor,
+                   topk_pos: Optional[torch.Tensor] = None, topk_count: Optional[torch.Tensor] = None,
+                   out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                   reindex_ws: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None,
+                   want_lse: bool = True, prepare: bool = False):
+    """A Reindex layer with the Top-K selected inside the attention kernel
+    (csa2_reindex_attend).  idx_q / idx_k as in index_reindex (a
+    (codes, scales) pair each for FP4 rows).  Returns (topk_pos, topk_count,
+    out, lse)."""
+    dev = q_lat.device
+    _dev(pool_blocks, pool_count, q_lat, q_rope, kv_codes, kv_scales, kv_rope, swa_kv, swa_base, topk_pos,
+         topk_count, out, lse)
+    fp4, qp, kp = _check_idx(dims, b, idx_q, idx_w, idx_k)
+    (qc, qs), (kc, ksc) = (qp, kp) if fp4 else ((qp[0], None), (kp[0], None))
+    n_q, H = b.n_q, dims.n_heads
+    if q_lat.shape != (n_q, H, 512) or q_rope.shape != (n_q, H, 64):
+        raise ValueError("q_lat / q_rope shape mismatch")
+    if q_lat.dtype != torch.bfloat16 or q_rope.dtype != torch.bfloat16 or swa_kv.dtype != torch.bfloat16:
+        raise TypeError("q_lat, q_rope and swa_kv must be bfloat16")
+    if swa_base.dtype != torch.int64 or swa_base.shape != (n_q,):
+        raise ValueError("swa_base must be int64 [n_q]")
+    if pool_blocks.shape != (n_q, dims.pool_blocks):
+        raise ValueError("pool_blocks shape mismatch")
+    if topk_pos is None:
+        topk_pos = torch.empty(n_q, dims.topk, dtype=torch.int32, device=dev)
+    if topk_count is None:
+        topk_count = torch.empty(n_q, dtype=torch.int32, device=dev)
+    if topk_pos.shape != (n_q, dims.topk):
+        raise ValueError("topk_pos shape mismatch")
+    if out is None:
+        out = torch.empty(n_q, H, 512, dtype=torch.float32, device=dev)
+    if lse is None and want_lse:
+        lse = torch.empty(n_q, H, dtype=torch.float32, device=dev)
+    reindex_ws = _workspace(workspace_reindex(dims, b), dev, reindex_ws)
+    ws = _workspace(workspace_attend(dims, b), dev, ws)
+    rp, rn = _ws_ptr(reindex_ws)
+    wp, wn = _ws_ptr(ws)
+    d, q = dims.c(), b.c()
+    args = (ctypes.byref(d), ctypes.byref(q), qc, qs, idx_w.data_ptr(), kc, ksc,
+            pool_blocks.data_ptr(), pool_count.data_ptr(), topk_pos.data_ptr(), topk_count.data_ptr(),
+            q_lat.data_ptr(), q_rope.data_ptr(), float(softmax_scale), kv_codes.data_ptr(), kv_scales.data_ptr(),
+            kv_rope.data_ptr(), swa_kv.data_ptr(), swa_base.data_ptr(), out.data_ptr(), _ptr(lse), rp, rn, wp, wn,
+            _stream(dev))
+    call = _issue(lib().csa2_reindex_attend, args, (d, q, ws, reindex_ws), prepare)
+    return call if prepare else (topk_pos, topk_count, out, lse)
 
 
 LAYER_FULL, LAYER_REINDEX, LAYER_REUSE = 0, 1, 2

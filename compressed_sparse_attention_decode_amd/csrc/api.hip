@@ -662,7 +662,8 @@ static csa2_status index_reindex(const csa2_dims* d, const csa2_queries* q, cons
                                  const float* idx_w, const uint8_t* idx_k, const uint8_t* k_scales, bool fp4,
                                  const int32_t* pool_blocks, const int32_t* pool_count, int32_t* topk_pos,
                                  int32_t* topk_count, float* topk_scores, void* ws, size_t ws_bytes, void* stream,
-                                 bool dry = false, const csa2_pages* pages = nullptr, uint32_t* counters = nullptr) {
+                                 bool dry = false, const csa2_pages* pages = nullptr, uint32_t* counters = nullptr,
+                                 bool score_only = false) {
   csa2_status st = check_dims(d);
   if (st) return st;
   if ((st = check_queries(q))) return st;
@@ -686,6 +687,7 @@ static csa2_status index_reindex(const csa2_dims* d, const csa2_queries* q, cons
   ra.done = counters ? counters : (uint32_t*)ws;
   ra.keys = counters ? (uint32_t*)ws : (uint32_t*)((char*)ws + align256((size_t)q->n_q * 4));
   ra.topk_pos = topk_pos; ra.topk_count = topk_count; ra.topk_scores = topk_scores;
+  ra.score_only = score_only ? 1 : 0;
   ra.pages = pages ? pages->table : nullptr;
   ra.page_shift = pages ? page_shift(pages) : 0;
   ra.rows = pages ? pages->rows : 0;
@@ -741,6 +743,7 @@ struct AttendSel {
   int32_t* pool_blocks;
   int32_t* pool_count;
   bool from_pool;            // the pool is selected before (chunked kernels): only the Top-K in the kernel
+  const uint32_t* rkeys;     // Reindex order keys: the Top-K from them (block_scores, pos_keys unused)
 };
 
 // Whether every query's pool fits one selecting workgroup (and the
@@ -761,7 +764,10 @@ static csa2_status attend(const csa2_dims* d, const csa2_queries* q, const uint1
   if (st) return st;
   if ((st = check_queries(q))) return st;
   if (pages && (st = check_pages(pages, 256))) return st;   // kv_codes: the widest plane
-  if (sel) {
+  if (sel && sel->rkeys) {
+    if (pages) return fail(CSA2_ERR_UNSUPPORTED, "the in-kernel selection takes unpaged planes");
+    if (!sel->pool_blocks || !sel->pool_count) return fail(CSA2_ERR_INVALID_ARG, "required pointer is NULL");
+  } else if (sel) {
     if (pages) return fail(CSA2_ERR_UNSUPPORTED, "the in-kernel selection takes unpaged planes");
     if (!sel->from_pool && !pool_small(d, q))
       return fail(CSA2_ERR_UNSUPPORTED, "the in-kernel selection takes at most %d blocks per query (max_visible %lld)",
@@ -799,8 +805,10 @@ static csa2_status attend(const csa2_dims* d, const csa2_queries* q, const uint1
   aa.bscore = nullptr; aa.ld_bs = 0; aa.pkey = nullptr; aa.ld_pkey = 0; aa.pool = d->pool_blocks;
   aa.pool_blocks = nullptr; aa.pool_count = nullptr; aa.topk_out = nullptr; aa.topk_count_out = nullptr;
   aa.sel_from_pool = 0;
+  aa.rkeys = nullptr;
   if (sel) {
     aa.sel_from_pool = sel->from_pool ? 1 : 0;
+    aa.rkeys = sel->rkeys;
     aa.bscore = sel->block_scores; aa.ld_bs = sel->ld_block_scores;
     aa.pkey = sel->pos_keys; aa.ld_pkey = sel->ld_pos_keys;
     aa.pool_blocks = sel->pool_blocks; aa.pool_count = sel->pool_count;
@@ -860,7 +868,7 @@ static csa2_status pool_topk_attend(const csa2_dims* d, const csa2_queries* q, c
   if (apart && ((st = check_block_scores(d, q, block_scores, ld_block_scores)) ||
                 (st = check_pos_keys(d, q, pos_keys, ld_pos_keys))))
     return st;
-  const AttendSel sel{block_scores, ld_block_scores, pos_keys, ld_pos_keys, pool_blocks, pool_count, !small};
+  const AttendSel sel{block_scores, ld_block_scores, pos_keys, ld_pos_keys, pool_blocks, pool_count, !small, nullptr};
   // every argument is checked before the first launch
   if ((st = attend(d, q, q_lat, q_rope, softmax_scale, kv_codes, kv_scales, kv_rope, topk_pos, topk_count, swa_kv,
                    swa_base, out, lse, ws, ws_bytes, stream, true, nullptr, apart ? nullptr : &sel)))
@@ -885,6 +893,56 @@ csa2_status csa2_pool_topk_attend(const csa2_dims* d, const csa2_queries* q, con
   return pool_topk_attend(d, q, block_scores, ld_block_scores, pos_keys, ld_pos_keys, pool_blocks, pool_count,
                           topk_pos, topk_count, q_lat, q_rope, softmax_scale, kv_codes, kv_scales, kv_rope, swa_kv,
                           swa_base, out, lse, pool_ws, pool_ws_bytes, flags, ws, ws_bytes, stream);
+}
+
+// A Reindex layer: the scoring kernel writes the order keys only, and the
+// attention workgroups select the Top-K from them.
+static csa2_status reindex_attend(const csa2_dims* d, const csa2_queries* q, const uint8_t* idx_q,
+                                  const uint8_t* idx_q_scales, const float* idx_w, const uint8_t* idx_k,
+                                  const uint8_t* idx_k_scales, const int32_t* pool_blocks, const int32_t* pool_count,
+                                  int32_t* topk_pos, int32_t* topk_count, const uint16_t* q_lat,
+                                  const uint16_t* q_rope, float softmax_scale, const uint8_t* kv_codes,
+                                  const uint8_t* kv_scales, const uint16_t* kv_rope, const uint16_t* swa_kv,
+                                  const int64_t* swa_base, float* out, float* lse, void* reindex_wsp,
+                                  size_t reindex_ws_bytes, void* ws, size_t ws_bytes, void* stream, bool dry = false,
+                                  uint32_t* counters = nullptr) {
+  if ((idx_q_scales == nullptr) != (idx_k_scales == nullptr))
+    return fail(CSA2_ERR_INVALID_ARG, "idx_q_scales and idx_k_scales must both be given (FP4 rows) or both NULL");
+  const bool fp4 = idx_q_scales != nullptr;
+  csa2_status st;
+  if ((st = index_reindex(d, q, idx_q, idx_q_scales, idx_w, idx_k, idx_k_scales, fp4, pool_blocks, pool_count,
+                          topk_pos, topk_count, nullptr, reindex_wsp, reindex_ws_bytes, stream, true, nullptr,
+                          counters, true)))
+    return st;
+  // the keys sit after the completion counters (or at the start, with
+  // external counters)
+  const uint32_t* rkeys = counters ? (const uint32_t*)reindex_wsp
+                                   : (const uint32_t*)((const char*)reindex_wsp + align256((size_t)q->n_q * 4));
+  const AttendSel sel{nullptr, 0, nullptr, 0, const_cast<int32_t*>(pool_blocks), const_cast<int32_t*>(pool_count),
+                      true, rkeys};
+  if ((st = attend(d, q, q_lat, q_rope, softmax_scale, kv_codes, kv_scales, kv_rope, topk_pos, topk_count, swa_kv,
+                   swa_base, out, lse, ws, ws_bytes, stream, true, nullptr, &sel)))
+    return st;
+  if (dry) return CSA2_OK;
+  if ((st = index_reindex(d, q, idx_q, idx_q_scales, idx_w, idx_k, idx_k_scales, fp4, pool_blocks, pool_count,
+                          topk_pos, topk_count, nullptr, reindex_wsp, reindex_ws_bytes, stream, false, nullptr,
+                          counters, true)))
+    return st;
+  return attend(d, q, q_lat, q_rope, softmax_scale, kv_codes, kv_scales, kv_rope, topk_pos, topk_count, swa_kv,
+                swa_base, out, lse, ws, ws_bytes, stream, false, nullptr, &sel);
+}
+
+csa2_status csa2_reindex_attend(const csa2_dims* d, const csa2_queries* q, const uint8_t* idx_q,
+                                const uint8_t* idx_q_scales, const float* idx_w, const uint8_t* idx_k,
+                                const uint8_t* idx_k_scales, const int32_t* pool_blocks, const int32_t* pool_count,
+                                int32_t* topk_pos, int32_t* topk_count, const uint16_t* q_lat, const uint16_t* q_rope,
+                                float softmax_scale, const uint8_t* kv_codes, const uint8_t* kv_scales,
+                                const uint16_t* kv_rope, const uint16_t* swa_kv, const int64_t* swa_base, float* out,
+                                float* lse, void* reindex_ws, size_t reindex_ws_bytes, void* ws, size_t ws_bytes,
+                                void* stream) {
+  return reindex_attend(d, q, idx_q, idx_q_scales, idx_w, idx_k, idx_k_scales, pool_blocks, pool_count, topk_pos,
+                        topk_count, q_lat, q_rope, softmax_scale, kv_codes, kv_scales, kv_rope, swa_kv, swa_base, out,
+                        lse, reindex_ws, reindex_ws_bytes, ws, ws_bytes, stream);
 }
 
 csa2_status csa2_page_rows(const csa2_pages* pages, int64_t n, const int64_t* table_off, const int32_t* pos,
@@ -994,6 +1052,16 @@ static csa2_status decode_step(const csa2_dims* d, const csa2_queries* q, int32_
           return st;
         continue;
       }
+    }
+    if (mode == CSA2_LAYER_REINDEX && !pages) {
+      // unpaged planes: the attention workgroups select the Top-K from the
+      // Reindex keys
+      if ((st = reindex_attend(d, q, idx_q, idx_q_scales, idx_w, idx_k, idx_k_scales, pool_blocks, pool_count,
+                               topk_pos, topk_count, q_lat, q_rope, softmax_scale, kv_codes, kv_scales, kv_rope,
+                               swa_kv, swa_base, out, lse, w_re, n_re, attend_ws(d, q) ? w_att : nullptr, n_att,
+                               stream, dry, counters)))
+        return st;
+      continue;
     }
     if (mode == CSA2_LAYER_REINDEX &&
         (st = index_reindex(d, q, idx_q, idx_q_scales, idx_w, idx_k, idx_k_scales, fp4, pool_blocks, pool_count,

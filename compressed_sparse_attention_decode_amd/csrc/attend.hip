@@ -173,9 +173,13 @@ __device__ __forceinline__ float max_rows4(float x) {
 // selection is repeated by each such split, which costs a few microseconds
 // of one CU each, against a launch and a round trip for the positions; the
 // split holding the first kept-entry tile of head group 0 writes the pool
-// and the Top-K out.  FROM_POOL: the pool is given (a query too long for
-// one workgroup's selection), the splits select only its Top-K.
-template <int SEL, bool FROM_POOL>
+// and the Top-K out.  SRC: where the selection starts.  kSrcScan: the scan's
+// block scores and position keys (pool and Top-K); kSrcPool: the pool is
+// given (a query too long for one workgroup's selection), the splits select
+// only its Top-K; kSrcReindex: a Reindex layer's Top-K from the order keys
+// its scoring kernel wrote (csa2_reindex_attend).
+constexpr int kSrcScan = 0, kSrcPool = 1, kSrcReindex = 2;
+template <int SEL, int SRC>
 __global__ __launch_bounds__(kNT) void k_attend(AttendArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char s_mem[kLdsBytes];
   _Float16* s_lat = reinterpret_cast<_Float16*>(s_mem + kOffLat);   // [64][kLS]
@@ -203,7 +207,7 @@ __global__ __launch_bounds__(kNT) void k_attend(AttendArgs a) {
   // trip (a use between them would wait for the first alone)
   const int n = load_uniform(a.n_visible + q);
   const int tcount = SEL ? 0 : load_uniform(a.topk_count + q);
-  const int pcount = FROM_POOL ? load_uniform(a.pool_count + q) : 0;
+  const int pcount = SRC != kSrcScan ? load_uniform(a.pool_count + q) : 0;
   const int64_t sbase = load_uniform(a.seq_base + q);
   const int64_t wbase = load_uniform(a.swa_base + q);
 
@@ -299,8 +303,8 @@ __global__ __launch_bounds__(kNT) void k_attend(AttendArgs a) {
       const int s_first = max(t_begin, nwt);
       const bool lead = hg == 0 && t_begin <= nwt;  // holds the first kept-entry tile
       PoolTopkOut o;
-      o.pool = lead && !FROM_POOL ? a.pool_blocks + (int64_t)q * a.pool : nullptr;
-      o.pool_count = lead && !FROM_POOL ? a.pool_count + q : nullptr;
+      o.pool = lead && SRC == kSrcScan ? a.pool_blocks + (int64_t)q * a.pool : nullptr;
+      o.pool_count = lead && SRC == kSrcScan ? a.pool_count + q : nullptr;
       o.topk = lead ? a.topk_out + (int64_t)q * K : nullptr;
       o.topk_count = lead ? a.topk_count_out + q : nullptr;
       o.rows = s_row + (s_first - t_begin) * kTE;
@@ -308,7 +312,10 @@ __global__ __launch_bounds__(kNT) void k_attend(AttendArgs a) {
       o.r1 = (t_end - nwt) * kTE;
       PoolTopkLds<SEL>& sl = *reinterpret_cast<PoolTopkLds<SEL>*>(s_mem + kOffLat);
       uint32_t kept;
-      if constexpr (FROM_POOL)
+      if constexpr (SRC == kSrcReindex)
+        kept = topk_from_keys(a.rkeys + (int64_t)q * a.pool * kBlock, a.pool_blocks + (int64_t)q * a.pool,
+                              min(pcount, a.pool), a.pool, K, o, sl.radix, sl.scan, load_q_sel);
+      else if constexpr (SRC == kSrcPool)
         kept = topk_from_pool<SEL>(a.pool_blocks + (int64_t)q * a.pool, min(pcount, a.pool), a.pool,
                                    a.bscore + (int64_t)q * a.ld_bs, a.pkey + (int64_t)q * a.ld_pkey, K, o, nullptr,
                                    sl, load_q_sel);
@@ -637,8 +644,13 @@ hipError_t launch_attend(const AttendArgs& a, hipStream_t s) {
       (a.splits > 1 && (!a.part_o || !a.part_ml)))
     return hipErrorInvalidValue;
   const dim3 grid((unsigned)(a.n_q * a.head_groups * a.splits));
-  if (!a.bscore) {
-    hipLaunchKernelGGL((k_attend<0, false>), grid, dim3(kNT), 0, s, a);
+  if (a.rkeys) {
+    if (a.pages || a.pool > 2048 || a.topk > 2048 || !a.pool_blocks || !a.pool_count || !a.topk_out ||
+        !a.topk_count_out)
+      return hipErrorInvalidValue;
+    hipLaunchKernelGGL((k_attend<1, kSrcReindex>), grid, dim3(kNT), 0, s, a);
+  } else if (!a.bscore) {
+    hipLaunchKernelGGL((k_attend<0, kSrcScan>), grid, dim3(kNT), 0, s, a);
   } else {
     // (without a given pool: a query of at most kMaxCand blocks; pool and
     // Top-K within 2048, no page table: checked by the caller)
@@ -648,13 +660,13 @@ hipError_t launch_attend(const AttendArgs& a, hipStream_t s) {
     if (a.sel_from_pool) {
       // (K <= 1024: the positions step of a larger K does not fit the
       // registers beside the attention's; the caller selects it apart)
-      if (a.topk <= kTkThreads) hipLaunchKernelGGL((k_attend<1, true>), grid, dim3(kNT), 0, s, a);
-      else if (a.topk <= 2 * kTkThreads) hipLaunchKernelGGL((k_attend<2, true>), grid, dim3(kNT), 0, s, a);
+      if (a.topk <= kTkThreads) hipLaunchKernelGGL((k_attend<1, kSrcPool>), grid, dim3(kNT), 0, s, a);
+      else if (a.topk <= 2 * kTkThreads) hipLaunchKernelGGL((k_attend<2, kSrcPool>), grid, dim3(kNT), 0, s, a);
       else return hipErrorInvalidValue;
     } else if (a.topk <= kTkThreads) {
-      hipLaunchKernelGGL((k_attend<2, false>), grid, dim3(kNT), 0, s, a);
+      hipLaunchKernelGGL((k_attend<2, kSrcScan>), grid, dim3(kNT), 0, s, a);
     } else {
-      hipLaunchKernelGGL((k_attend<4, false>), grid, dim3(kNT), 0, s, a);
+      hipLaunchKernelGGL((k_attend<4, kSrcScan>), grid, dim3(kNT), 0, s, a);
     }
   }
   if (a.splits > 1) {

@@ -54,6 +54,7 @@ struct ReindexArgs {
   int32_t* topk_pos;
   int32_t* topk_count;
   float* topk_scores;        // optional
+  int score_only;            // 1: only the keys (the attention kernel selects from them)
   // paged caches (nullptr: position p of query q's sequence is row
   // seq_base[q] + p): it is row (pages[seq_base[q] + (p >> page_shift)] <<
   // page_shift) + (p mod 2^page_shift) of planes of `rows` rows
@@ -100,6 +101,7 @@ struct AttendArgs {
   int32_t* topk_out;         // [n_q, topk]
   int32_t* topk_count_out;
   int sel_from_pool;         // 1: the pool is given (pool_blocks, pool_count are read), only the Top-K is selected
+  const uint32_t* rkeys;     // Reindex order keys [n_q, 8 * pool] (csa2_reindex_attend): the Top-K from them
 };
 
 // A Full layer's Top-K from the Full scan's own scores (the same indexer

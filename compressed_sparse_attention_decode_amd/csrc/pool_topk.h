@@ -181,4 +181,60 @@ __device__ __forceinline__ uint32_t topk_from_pool(const int32_t* pool, int pcnt
                              o.r1);
 }
 
+// A Reindex layer's Top-K from the order keys its scoring kernel wrote (one
+// per pool position, 0 = no candidate; "DeepSeek-V4.1-Flash 梗概" §3.2:
+// Reindex re-scores the inherited pool with the layer's own indexer query
+// and keeps the K best positions): the K best by (key desc, slot asc), slot
+// order being ascending position order, written in ascending order.  The
+// same selection as k_reindex's last workgroup.  Called by all kTkThreads
+// threads; ks: the query's 8 P keys; pool: its P block ids, pcnt valid.
+// o.pool / o.pool_count are not written.  Returns the Top-K count.
+template <typename AfterKeys>
+__device__ __forceinline__ uint32_t topk_from_keys(const uint32_t* ks, const int32_t* pool, int pcnt, int P, int K,
+                                                   const PoolTopkOut& o, RadixLds& L, uint32_t* s_scan,
+                                                   AfterKeys&& after_keys) {
+  constexpr int kBP = kPer / kBlock;                // pool blocks per thread
+  const int tid = threadIdx.x;
+  int32_t blk[kBP];
+#pragma unroll
+  for (int j = 0; j < kBP; ++j) blk[j] = pool[min(tid * kBP + j, P - 1)];
+  const int s0 = tid * kPer;
+  const bool mine = s0 < P * kBlock;
+  uint32_t key[kPer];
+#pragma unroll
+  for (int v = 0; v < kPer / 4; ++v) {
+    const v4u x = *reinterpret_cast<const v4u*>(ks + min(s0 + v * 4, P * kBlock - 4));
+    key[4 * v] = x[0]; key[4 * v + 1] = x[1]; key[4 * v + 2] = x[2]; key[4 * v + 3] = x[3];
+  }
+  const int nh = mine ? pcnt * kBlock - s0 : 0;    // slots of this thread inside the pool count
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) key[k] = k < nh ? key[k] : 0u;
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) asm volatile("" : "+v"(key[k]));   // the keys are complete here
+  after_keys();
+  const TopkCut cut = radix_topk<kPer>(key, K, 0, L);
+  uint32_t flags = 0;
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) flags |= (uint32_t)(key[k] >= cut.tt) << k;
+  uint32_t total;
+  uint32_t before = block_exclusive_scan<kTkThreads>(__builtin_popcount(flags), s_scan, &total);
+  while (flags) {
+    const int k = __builtin_ctz(flags);
+    flags &= flags - 1;
+    int32_t b = blk[0];
+#pragma unroll
+    for (int j = 1; j < kBP; ++j) b = (k >> 3) == j ? blk[j] : b;
+    const int32_t p = b * kBlock + (k & 7);
+    if (before < (uint32_t)K) {
+      if (o.topk) o.topk[before] = p;
+      if (o.rows && (int)before >= o.r0 && (int)before < o.r1) o.rows[before - o.r0] = p;
+    }
+    ++before;
+  }
+  if (o.topk)
+    for (int t = (int)cut.keff + tid; t < K; t += kTkThreads) o.topk[t] = -1;
+  if (o.topk_count && tid == 0) *o.topk_count = (int32_t)cut.keff;
+  return cut.keff;
+}
+
 }  // namespace csa2

@@ -306,6 +306,7 @@ __global__ __launch_bounds__(kTkThreads) void k_reindex(ReindexArgs a) {
   const int32_t b2 = pool[min(j0 + 2, a.pool - 1)], b3 = pool[min(j0 + 3, a.pool - 1)];
   const int pcnt = load_uniform(a.pool_count + q);
   score_part<D, HT, kTkWaves, F4, BPW>(a, q, part);
+  if (a.score_only) return;             // the next kernel selects (its launch orders the keys)
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's key stores have reached L2
   __syncthreads();
   if (threadIdx.x == 0) {

@@ -507,6 +507,32 @@ csa2_status csa2_pool_topk_attend(const csa2_dims* dims, const csa2_queries* q, 
                                   void* pool_ws, size_t pool_ws_bytes, int32_t flags,
                                   void* ws, size_t ws_bytes, void* stream);
 
+/* csa2_index_reindex followed by csa2_attend on its Top-K, with the Top-K
+ * selected inside the attention kernel: the Reindex kernel only scores the
+ * pool's positions (order keys into reindex_ws), and every attention
+ * workgroup that holds kept-entry tiles selects the K best of them itself
+ * (the same selection as csa2_index_reindex's) and gathers its tiles'
+ * entries at once.  The workgroup holding head group 0's first kept-entry
+ * tile writes topk_pos and topk_count, as csa2_index_reindex writes them
+ * ([atlas] §3.2: a Reindex layer re-scores the inherited pool with its own
+ * indexer query, then attends over the kept positions with its main Q).
+ * FP4 indexer rows when idx_q_scales and idx_k_scales are both given.
+ *   idx_q ... pool_count          as in csa2_index_reindex
+ *   q_lat ... lse                 as in csa2_attend (topk_pos, topk_count
+ *                                 are outputs here)
+ *   reindex_ws, reindex_ws_bytes  csa2_index_reindex_workspace_size bytes
+ *                                 (its completion counters are not used)
+ *   ws, ws_bytes                  csa2_attend_workspace_size bytes
+ * Unpaged planes only.  Errors as those two calls. */
+csa2_status csa2_reindex_attend(const csa2_dims* dims, const csa2_queries* q, const uint8_t* idx_q,
+                                const uint8_t* idx_q_scales, const float* idx_w, const uint8_t* idx_k,
+                                const uint8_t* idx_k_scales, const int32_t* pool_blocks, const int32_t* pool_count,
+                                int32_t* topk_pos, int32_t* topk_count, const uint16_t* q_lat, const uint16_t* q_rope,
+                                float softmax_scale, const uint8_t* kv_codes, const uint8_t* kv_scales,
+                                const uint16_t* kv_rope, const uint16_t* swa_kv, const int64_t* swa_base,
+                                float* out, float* lse, void* reindex_ws, size_t reindex_ws_bytes,
+                                void* ws, size_t ws_bytes, void* stream);
+
 /* Rows of paged positions, so that csa2_encode_kv (through dst_row) appends
  * new entries into their pages:
  *   dst_row[i] = table[table_off[i] + pos[i] / page_size] * page_size
@@ -527,7 +553,8 @@ csa2_status csa2_page_rows(const csa2_pages* pages, int64_t n, const int64_t* ta
  *                       csa2_attend_paged (pool_blocks, pool_count, and
  *                       topk_pos, topk_count: the same set as
  *                       csa2_index_reindex with the same indexer query);
- *   CSA2_LAYER_REINDEX  csa2_index_reindex on the given pool, csa2_attend;
+ *   CSA2_LAYER_REINDEX  csa2_reindex_attend on the given pool (unpaged
+ *                       planes), or csa2_index_reindex + csa2_attend_paged;
  *   CSA2_LAYER_REUSE    csa2_attend on the given topk_pos / topk_count
  *                       (the idx_* arguments may be NULL).
  * The indexer rows are fp8 when idx_q_scales and idx_k_scales are NULL and

@@ -366,6 +366,37 @@ def test_pool_topk_attend_matches_separate_calls(case, small, splits, monkeypatc
     assert torch.equal(lse.view(torch.int32), lse2.view(torch.int32)), f"{name}: log-sum-exp differs"
 
 
+@pytest.mark.parametrize("splits", ["", "1", "3"])
+def test_reindex_attend_matches_separate_calls(case, splits, monkeypatch):
+    """csa2_reindex_attend (the Reindex kernel writes its order keys only and
+    every attention workgroup with kept-entry tiles selects the Top-K from
+    them) writes the same Top-K, output and log-sum-exp, bit for bit, as
+    csa2_index_reindex followed by csa2_attend; also with splits of several
+    tiles forced (CSA2_ATTEND_SPLITS)."""
+    name, g, lay = case
+    if splits:
+        monkeypatch.setenv("CSA2_ATTEND_SPLITS", splits)
+    csa2, w = g.csa2, g.w
+    pool, cnt, _ = g.full(0)
+    layer = 1
+    tk, tc, _ = g.reindex(layer, pool, cnt)
+    out, lse = g.attend(layer, tk, tc)
+    q, wt = g.iq(layer)
+    ql, qr = g.mq(layer)
+    idx_k, codes, scales, kv_rope, swa_kv = g.planes[0]
+    fill = lambda shape, dt=torch.int32: torch.full(shape, 7, dtype=dt, device="cuda")
+    tk2, tc2 = fill((w.n_q, w.dims.topk)), fill((w.n_q,))
+    out2 = fill((w.n_q, w.dims.n_heads, 512), torch.float32)
+    lse2 = fill((w.n_q, w.dims.n_heads), torch.float32)
+    csa2.reindex_attend(g.dims, g.batch, q, wt, idx_k, pool, cnt, ql, qr, 1.0, codes, scales, kv_rope, swa_kv,
+                        g.swa_base, tk2, tc2, out2, lse2)
+    torch.cuda.synchronize()
+    assert torch.equal(tc, tc2), f"{name}: Top-K counts differ"
+    assert torch.equal(tk, tk2), f"{name}: Top-K differs"
+    assert torch.equal(out.view(torch.int32), out2.view(torch.int32)), f"{name}: attention output differs"
+    assert torch.equal(lse.view(torch.int32), lse2.view(torch.int32)), f"{name}: log-sum-exp differs"
+
+
 def test_pipeline_end_to_end_and_deterministic(case):
     name, g, lay = case
     w = g.w
