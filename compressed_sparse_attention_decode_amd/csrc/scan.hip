@@ -87,7 +87,6 @@ __global__ __launch_bounds__(64 * NW) void k_scan(ScanArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t s_q[64 * D];
   __shared__ __attribute__((aligned(16))) float s_w[64];
   __shared__ int32_t s_pg[PG ? kMaxTilePos / 16 + 1 : 1];   // paged: the tile's page ids
-  __shared__ __attribute__((aligned(16))) uint32_t s_ps[PS ? kMaxTilePos : 4];   // position keys of the tile
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int gq = lane >> 4, col = lane & 15;
 
@@ -264,10 +263,12 @@ __global__ __launch_bounds__(64 * NW) void k_scan(ScanArgs a) {
     // positions >= c (only in a wave's last step) score -inf
     float v = part;
     if (last) v = p0 + col < c ? part : -__builtin_inff();
-    // every lane group holds the same 16 sums: group 0 keeps the position keys
-    // (key 0, which no score has, for positions >= c)
+    // every lane group holds the same 16 sums: group 0 writes the position
+    // keys (key 0, which no score has, for positions >= c) straight to the
+    // row (64 bytes per step; staging them in LDS cost a third workgroup per
+    // CU, which the compute-bound many-token scans need)
     if constexpr (PS)
-      if (gq == 0) s_ps[s * 16 + col] = !last || p0 + col < c ? order_key(part) : 0u;
+      if (gq == 0) a.pkey[(int64_t)q * a.ld_pkey + p0 + col] = !last || p0 + col < c ? order_key(part) : 0u;
     v = max_lanes8(v);
     if (lane < 16 && (lane & 7) == 0) s_bs[s * 2 + (lane >> 3)] = v;
   };
@@ -385,13 +386,6 @@ __global__ __launch_bounds__(64 * NW) void k_scan(ScanArgs a) {
   stream_done:;
   }
   __syncthreads();
-  if constexpr (PS) {
-    // the tile's position keys, one coalesced store (whole steps: the row
-    // stride covers c rounded up to 32)
-    uint32_t* pk = a.pkey + (int64_t)q * a.ld_pkey + p_begin;
-    for (int i = tid * 4; i < nsteps * 16; i += NT * 4)
-      *reinterpret_cast<v4u*>(pk + i) = *reinterpret_cast<const v4u*>(&s_ps[i]);
-  }
   // block scores of the tile, one coalesced store
   float* bs = a.bscore + (int64_t)q * a.ld + (p_begin >> 3);
   const int nblk = (p_end - p_begin + 7) >> 3;
