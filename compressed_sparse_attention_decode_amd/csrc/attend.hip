@@ -167,17 +167,19 @@ __device__ __forceinline__ float max_rows4(float x) {
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
-// SEL > 0: the splits with kept-entry tiles select the query's pool and
-// Full-layer Top-K themselves (pool_topk.h, SEL blocks per thread in its
-// positions step) from the scan's scores instead of reading topk_pos: the
-// selection is repeated by each such split, which costs a few microseconds
-// of one CU each, against a launch and a round trip for the positions; the
-// split holding the first kept-entry tile of head group 0 writes the pool
-// and the Top-K out.  SRC: where the selection starts.  kSrcScan: the scan's
-// block scores and position keys (pool and Top-K); kSrcPool: the pool is
-// given (a query too long for one workgroup's selection), the splits select
-// only its Top-K; kSrcReindex: a Reindex layer's Top-K from the order keys
-// its scoring kernel wrote (csa2_reindex_attend).
+// SEL > 0: the splits with kept-entry tiles select the query's Full-layer
+// Top-K themselves (pool_topk.h, SEL blocks per thread in its positions
+// step) instead of reading topk_pos: the selection is repeated by each such
+// split, which costs a few microseconds of one CU each, against a launch and
+// a round trip for the positions; the split holding the first kept-entry
+// tile of head group 0 writes the Top-K out.  SRC: where the selection
+// starts.  kSrcScan: the scan's block scores and position keys; one extra
+// workgroup per query (past the attention grid) selects and writes the pool,
+// so the attention splits need only the Top-K's candidate blocks (those at
+// or above the first histogram's bound for the K-th block); kSrcPool: the
+// pool is given (a query too long for one workgroup's selection), the splits
+// select only its Top-K; kSrcReindex: a Reindex layer's Top-K from the order
+// keys its scoring kernel wrote (csa2_reindex_attend).
 constexpr int kSrcScan = 0, kSrcPool = 1, kSrcReindex = 2;
 template <int SEL, int SRC>
 __global__ __launch_bounds__(kNT) void k_attend(AttendArgs a) {
@@ -194,6 +196,25 @@ __global__ __launch_bounds__(kNT) void k_attend(AttendArgs a) {
   const int gq = lane >> 4, col = lane & 15;
   const int hgl = wave >> 2, qw = wave & 3;       // head group (of 16) in the workgroup, quarter
   const int S = a.splits, HG = a.head_groups;
+  if constexpr (SEL > 0 && SRC == kSrcScan) {
+    // one workgroup per query past the attention grid selects and writes the
+    // pool (the attention workgroups then need only the Top-K's candidates)
+    const int main_grid = a.n_q * HG * S;
+    if ((int)blockIdx.x >= main_grid) {
+      const int qp = (int)blockIdx.x - main_grid;
+      const int cp = max(0, load_uniform(a.n_visible + qp) - a.swa);
+      PoolTopkOut o;
+      o.pool = a.pool_blocks + (int64_t)qp * a.pool;
+      o.pool_count = a.pool_count + qp;
+      o.topk = nullptr;
+      o.topk_count = nullptr;
+      o.rows = nullptr;
+      o.r0 = o.r1 = 0;
+      pool_topk_select<0>(a.bscore + (int64_t)qp * a.ld_bs, (int)a.ld_bs, (cp + 7) >> 3, a.pool, a.topk, nullptr, o,
+                          *reinterpret_cast<PoolTopkLds<0>*>(s_mem + kOffLat), [] {});
+      return;
+    }
+  }
   const int q = blockIdx.x / (HG * S);
   const int hg = (blockIdx.x / S) % HG;
   const int sp = blockIdx.x % S;
@@ -303,8 +324,8 @@ __global__ __launch_bounds__(kNT) void k_attend(AttendArgs a) {
       const int s_first = max(t_begin, nwt);
       const bool lead = hg == 0 && t_begin <= nwt;  // holds the first kept-entry tile
       PoolTopkOut o;
-      o.pool = lead && SRC == kSrcScan ? a.pool_blocks + (int64_t)q * a.pool : nullptr;
-      o.pool_count = lead && SRC == kSrcScan ? a.pool_count + q : nullptr;
+      o.pool = nullptr;                           // (written by the pool workgroups, or given)
+      o.pool_count = nullptr;
       o.topk = lead ? a.topk_out + (int64_t)q * K : nullptr;
       o.topk_count = lead ? a.topk_count_out + q : nullptr;
       o.rows = s_row + (s_first - t_begin) * kTE;
@@ -666,10 +687,11 @@ hipError_t launch_attend(const AttendArgs& a, hipStream_t s) {
       if (a.topk <= kTkThreads) hipLaunchKernelGGL((k_attend<1, kSrcPool>), grid, dim3(kNT), 0, s, a);
       else if (a.topk <= 2 * kTkThreads) hipLaunchKernelGGL((k_attend<2, kSrcPool>), grid, dim3(kNT), 0, s, a);
       else return hipErrorInvalidValue;
-    } else if (a.topk <= kTkThreads) {
-      hipLaunchKernelGGL((k_attend<2, kSrcScan>), grid, dim3(kNT), 0, s, a);
     } else {
-      hipLaunchKernelGGL((k_attend<4, kSrcScan>), grid, dim3(kNT), 0, s, a);
+      // plus one pool workgroup per query
+      const dim3 gp((unsigned)(a.n_q * a.head_groups * a.splits + a.n_q));
+      if (a.topk <= kTkThreads) hipLaunchKernelGGL((k_attend<2, kSrcScan>), gp, dim3(kNT), 0, s, a);
+      else hipLaunchKernelGGL((k_attend<4, kSrcScan>), gp, dim3(kNT), 0, s, a);
     }
   }
   if (a.splits > 1) {

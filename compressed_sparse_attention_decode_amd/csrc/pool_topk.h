@@ -48,8 +48,11 @@ struct PoolTopkLds {
 // stride ld, a multiple of 4 floats, >= 4), nb <= kMaxCand of them valid;
 // pk: its position keys (BPT > 0).  after_keys() runs once the block keys
 // are in registers, before the first selection (a caller's own loads then
-// land while it runs without delaying the keys).  Returns the Top-K count
-// (BPT > 0) or the pool count.  Contains barriers.
+// land while it runs without delaying the keys).  Without o.pool (the pool
+// is written elsewhere) and with K <= P the Top-K needs no exact pool: the K
+// best blocks lie in the pool, and the blocks at or above the first
+// histogram's bound for the K-th block (radix_bound) are its candidates.
+// Returns the Top-K count (BPT > 0) or the pool count.  Contains barriers.
 template <int BPT, typename AfterKeys>
 __device__ __forceinline__ uint32_t pool_topk_select(const float* bs, int ld, int nb, int P, int K,
                                                      const uint32_t* pk, const PoolTopkOut& o,
@@ -78,6 +81,27 @@ __device__ __forceinline__ uint32_t pool_topk_select(const float* bs, int ld, in
 #pragma unroll
   for (int k = 0; k < kPer; ++k) asm volatile("" : "+v"(key[k]));   // the keys are complete here
   after_keys();
+  if constexpr (BPT > 0) {
+    if (!o.pool && !o.pool_count && K <= P) {
+      const TopkBound bd = radix_bound<kPer>(key, K, L.radix);
+      uint32_t cflags = 0;
+#pragma unroll
+      for (int k = 0; k < kPer; ++k) cflags |= (uint32_t)(key[k] >= bd.lb) << k;
+      uint32_t ncand;
+      uint32_t cb = block_exclusive_scan<kTkThreads>(__builtin_popcount(cflags), L.scan, &ncand);
+      if (ncand <= kCap) {
+        while (cflags) {
+          const int k = __builtin_ctz(cflags);
+          cflags &= cflags - 1;
+          L.blk[cb++] = s0 + k;                    // ascending block ids
+        }
+        __syncthreads();
+        return topk_positions<BPT>(L.blk, ncand, pk, K, o.topk, nullptr, o.topk_count, L.scan, L.radix, o.rows,
+                                   o.r0, o.r1);
+      }
+      // (a crowded bin: the exact path below)
+    }
+  }
   const TopkCut cut = radix_topk<kPer>(key, P, BPT > 0 ? K : 0, L.radix);
 
   // pool members, and (BPT > 0) the candidate blocks of the Top-K: both

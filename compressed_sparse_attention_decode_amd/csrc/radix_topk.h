@@ -250,6 +250,47 @@ __device__ __forceinline__ TopkCut radix_topk(uint32_t (&key)[PER], int K, int K
   return TopkCut{keff, Tt, lb2, n2};
 }
 
+// The first pass of radix_topk alone: a lower bound lb of the K-th largest
+// key (the lower edge of the first histogram's bin that holds it; every key
+// when K covers them all) and n, the number of keys >= lb (n >= min(K,
+// valid keys)).  No key is left out of {key >= lb} that the exact K largest
+// hold.  With no valid key lb = 0xFFFFFFFF, n = 0.  Called by all kTkThreads
+// threads; contains barriers.
+struct TopkBound {
+  uint32_t lb;
+  uint32_t n;
+};
+template <int PER>
+__device__ __forceinline__ TopkBound radix_bound(const uint32_t (&key)[PER], int K, RadixLds& L) {
+  static_assert(PER >= 1 && PER <= 32, "PER keys per thread");
+  uint32_t* s_hist = L.hist;
+  const int tid = threadIdx.x, lane = tid & 63;
+  *reinterpret_cast<v4u*>(s_hist + 4 * tid) = v4u{0u, 0u, 0u, 0u};
+  if (tid < kTkEmpty / 4) *reinterpret_cast<v4u*>(s_hist + kTkBins + 4 * tid) = v4u{0u, 0u, 0u, 0u};
+  uint32_t lo = 0xFFFFFFFFu, hi = 0;
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    lo = min(lo, key[k] - 1u);
+    hi = max(hi, key[k]);
+  }
+  block_minmax_u32<kTkThreads>(&lo, &hi, L.red);   // its barriers also order the clears
+  const uint32_t kmin = lo + 1u, kmax = hi;
+  if (kmax == 0) return TopkBound{0xFFFFFFFFu, 0u};
+  const uint32_t d = kmax - kmin;
+  const int shift = d ? max(0, 21 - (int)__clz(d)) : 0;   // (d >> shift) < 2^11, as radix_topk
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const uint32_t b = (key[k] - kmin) >> shift;
+    atomicAdd(&s_hist[key[k] != 0 ? b : kTkBins + (lane & (kTkEmpty - 1))], 1u);
+  }
+  __syncthreads();
+  if (tid < 64) crossing_2048(s_hist, (uint32_t)K, L.misc2);
+  __syncthreads();
+  const TopkBound r{kmin + (L.misc2[0] << shift), L.misc2[1] + L.misc2[2]};
+  __syncthreads();                                   // (the next selection may reuse L at once)
+  return r;
+}
+
 // The same with LDS of its own (one per PER).
 template <int PER = kPer>
 __device__ __forceinline__ TopkCut radix_topk(uint32_t (&key)[PER], int K, int K2 = 0) {
