@@ -158,6 +158,18 @@ int pool_mm_cap(const csa2_dims* d, const csa2_queries* q) {
   return t > g ? t : g;
 }
 
+// The scan writes group keys (the largest block key of each kGroupBlocks
+// blocks) into the pool workspace when its tiles start at group boundaries:
+// always, unless CSA2_SCAN_TILE / CSA2_SCAN_SPLIT move them off.
+static bool scan_groups_ok(const csa2_dims* d, const csa2_queries* q) {
+  const int tile = scan_tile(), tiles = scan_tiles(d, q, tile);
+  const int extra = scan_tile_extra(d, q, tile, tiles);
+  return tile % (8 * kGroupBlocks) == 0 && extra % (8 * kGroupBlocks) == 0;
+}
+
+// Words of a query's group keys in the pool workspace.
+static int pool_gcap(const csa2_dims* d, const csa2_queries* q) { return pool_chunks(d, q) * (kPoolChunk / kGroupBlocks); }
+
 size_t pool_ws(const csa2_dims* d, const csa2_queries* q) {
   return align256((size_t)q->n_q * pool_ws_words(pool_chunks(d, q), pool_mm_cap(d, q)) * 4);
 }
@@ -396,6 +408,12 @@ static csa2_status run_scan(const csa2_dims* d, const csa2_queries* q, const uin
   sa.rows = pages ? pages->rows : 0;
   sa.pkey = pkey;
   sa.ld_pkey = ld_pkey;
+  sa.gkey = nullptr;
+  sa.ld_gkey = 0;
+  if (pool_ws_ptr && scan_groups_ok(d, q)) {
+    sa.gkey = pool_ws_ptr + pool_gkey_off(pool_chunks(d, q), pool_mm_cap(d, q));
+    sa.ld_gkey = sa.pool_ws_stride;
+  }
   hipError_t e = launch_scan(sa, (hipStream_t)stream);
   return e == hipSuccess ? CSA2_OK : hip_fail(e, "scan launch");
 }
@@ -744,6 +762,9 @@ struct AttendSel {
   int32_t* pool_count;
   bool from_pool;            // the pool is selected before (chunked kernels): only the Top-K in the kernel
   const uint32_t* rkeys;     // Reindex order keys: the Top-K from them (block_scores, pos_keys unused)
+  const uint32_t* gkeys;     // the scan's group keys: queries past kPoolSmallBlocks blocks select from them
+  int64_t ld_gkeys;
+  int gcap;
 };
 
 // Whether every query's pool fits one selecting workgroup (and the
@@ -769,9 +790,12 @@ static csa2_status attend(const csa2_dims* d, const csa2_queries* q, const uint1
     if (!sel->pool_blocks || !sel->pool_count) return fail(CSA2_ERR_INVALID_ARG, "required pointer is NULL");
   } else if (sel) {
     if (pages) return fail(CSA2_ERR_UNSUPPORTED, "the in-kernel selection takes unpaged planes");
-    if (!sel->from_pool && !pool_small(d, q))
+    if (!sel->from_pool && !sel->gkeys && !pool_small(d, q))
       return fail(CSA2_ERR_UNSUPPORTED, "the in-kernel selection takes at most %d blocks per query (max_visible %lld)",
                   kPoolSmallBlocks, (long long)q->max_visible);
+    if (sel->gkeys && (max_blocks(d, q) > (int64_t)kPoolGroupsMax * kGroupBlocks || d->topk > 1024))
+      return fail(CSA2_ERR_UNSUPPORTED, "the group-key selection takes at most %d blocks per query and a Top-K of 1024",
+                  kPoolGroupsMax * kGroupBlocks);
     if (!sel->block_scores || !sel->pos_keys || !sel->pool_blocks || !sel->pool_count)
       return fail(CSA2_ERR_INVALID_ARG, "required pointer is NULL");
     if ((st = check_block_scores(d, q, sel->block_scores, sel->ld_block_scores))) return st;
@@ -806,9 +830,11 @@ static csa2_status attend(const csa2_dims* d, const csa2_queries* q, const uint1
   aa.pool_blocks = nullptr; aa.pool_count = nullptr; aa.topk_out = nullptr; aa.topk_count_out = nullptr;
   aa.sel_from_pool = 0;
   aa.rkeys = nullptr;
+  aa.gkey = nullptr; aa.ld_gkey = 0; aa.gcap = 0;
   if (sel) {
     aa.sel_from_pool = sel->from_pool ? 1 : 0;
     aa.rkeys = sel->rkeys;
+    aa.gkey = sel->gkeys; aa.ld_gkey = sel->ld_gkeys; aa.gcap = sel->gcap;
     aa.bscore = sel->block_scores; aa.ld_bs = sel->ld_block_scores;
     aa.pkey = sel->pos_keys; aa.ld_pkey = sel->ld_pos_keys;
     aa.pool_blocks = sel->pool_blocks; aa.pool_count = sel->pool_count;
@@ -861,20 +887,32 @@ static csa2_status pool_topk_attend(const csa2_dims* d, const csa2_queries* q, c
   if (flags & ~CSA2_POOL_WS_FROM_SCAN) return fail(CSA2_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
   const bool small = pool_small(d, q);
   if (!small && (st = check_ws(pool_wsp, pool_ws_bytes, pool_ws(d, q)))) return st;
+  if ((st = check_device())) return st;          // (the scan's tile shape reads the device)
+  // a long query after the scan: pool and Top-K from the scan's group keys
+  // in the attention launch (CSA2_POOL_GROUPS=0: the chunked pool kernels)
+  bool groups = !small && (flags & CSA2_POOL_WS_FROM_SCAN) && scan_groups_ok(d, q) &&
+                max_blocks(d, q) <= (int64_t)kPoolGroupsMax * kGroupBlocks && d->topk <= 1024;
+  if (const char* env = getenv("CSA2_POOL_GROUPS")) groups = groups && atoi(env) != 0;
   // a Top-K of more than 1024 positions from a given pool is selected apart
   // (k_topk_keys): its positions step does not fit beside the attention
-  const bool apart = !small && d->topk > 1024;
+  const bool apart = !small && !groups && d->topk > 1024;
   if (!block_scores || !pos_keys) return fail(CSA2_ERR_INVALID_ARG, "required pointer is NULL");
   if (apart && ((st = check_block_scores(d, q, block_scores, ld_block_scores)) ||
                 (st = check_pos_keys(d, q, pos_keys, ld_pos_keys))))
     return st;
-  const AttendSel sel{block_scores, ld_block_scores, pos_keys, ld_pos_keys, pool_blocks, pool_count, !small, nullptr};
+  AttendSel sel{block_scores, ld_block_scores, pos_keys, ld_pos_keys, pool_blocks, pool_count, !small && !groups,
+                nullptr, nullptr, 0, 0};
+  if (groups) {
+    sel.gkeys = (const uint32_t*)pool_wsp + pool_gkey_off(pool_chunks(d, q), pool_mm_cap(d, q));
+    sel.ld_gkeys = pool_ws_words(pool_chunks(d, q), pool_mm_cap(d, q));
+    sel.gcap = pool_gcap(d, q);
+  }
   // every argument is checked before the first launch
   if ((st = attend(d, q, q_lat, q_rope, softmax_scale, kv_codes, kv_scales, kv_rope, topk_pos, topk_count, swa_kv,
                    swa_base, out, lse, ws, ws_bytes, stream, true, nullptr, apart ? nullptr : &sel)))
     return st;
   if (dry) return CSA2_OK;
-  if (!small && (st = run_pool(d, q, block_scores, ld_block_scores, pool_blocks, pool_count, pool_wsp,
+  if (!small && !groups && (st = run_pool(d, q, block_scores, ld_block_scores, pool_blocks, pool_count, pool_wsp,
                                (flags & CSA2_POOL_WS_FROM_SCAN) != 0, stream, pos_keys, ld_pos_keys,
                                apart ? topk_pos : nullptr, apart ? topk_count : nullptr)))
     return st;

@@ -48,6 +48,7 @@
 //    one tile, so a query's work is spread over tens of CUs.
 #include "common.h"
 #include "internal.h"
+#include "group_topk.h"
 #include "pool_topk.h"
 
 namespace csa2 {
@@ -89,6 +90,12 @@ constexpr int kLdsBytes = kOffLw + 2 * 4 * 16 * 4;
 constexpr int kQS = (kLatent + 8) * 2;
 constexpr int kOffQ = 18 * 1024;
 static_assert(kOffQ + kAttendHeads * kQS <= kTE * kLS * 2, "query latents fit in the image");
+// a selecting split's candidate groups (long queries), in the image after the
+// query latents
+constexpr int kOffGrp = kOffQ + kAttendHeads * kQS;
+static_assert(kOffGrp % 16 == 0 && kOffGrp + 4 * 4 * kTkThreads <= kTE * kLS * 2, "candidate groups fit in the image");
+static_assert(sizeof(PoolGroupLds) <= kLdsBytes, "a pool selection fits the workgroup's LDS");
+static_assert(kMaxGroups == kPoolGroupsMax, "the host's bound of the group keys");
 static_assert(kTE * 8 == kNT, "one rope chunk per thread");
 static_assert(kTE * kScaleBytes <= kNW * 256, "a tile's scale block: one 256-byte load per wave");
 static_assert(kAttendHeads * kOS * 4 <= kOffStage, "output rows fit in the image and rope slots");
@@ -179,8 +186,10 @@ __device__ __forceinline__ float max_rows4(float x) {
 // or above the first histogram's bound for the K-th block); kSrcPool: the
 // pool is given (a query too long for one workgroup's selection), the splits
 // select only its Top-K; kSrcReindex: a Reindex layer's Top-K from the order
-// keys its scoring kernel wrote (csa2_reindex_attend).
-constexpr int kSrcScan = 0, kSrcPool = 1, kSrcReindex = 2;
+// keys its scoring kernel wrote (csa2_reindex_attend); kSrcGroups: as
+// kSrcScan, and a query longer than one workgroup's registers hold
+// (kMaxCand blocks) selects from the scan's group keys (group_topk.h).
+constexpr int kSrcScan = 0, kSrcPool = 1, kSrcReindex = 2, kSrcGroups = 3;
 template <int SEL, int SRC>
 __global__ __launch_bounds__(kNT) void k_attend(AttendArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char s_mem[kLdsBytes];
@@ -196,7 +205,7 @@ __global__ __launch_bounds__(kNT) void k_attend(AttendArgs a) {
   const int gq = lane >> 4, col = lane & 15;
   const int hgl = wave >> 2, qw = wave & 3;       // head group (of 16) in the workgroup, quarter
   const int S = a.splits, HG = a.head_groups;
-  if constexpr (SEL > 0 && SRC == kSrcScan) {
+  if constexpr (SEL > 0 && (SRC == kSrcScan || SRC == kSrcGroups)) {
     // one workgroup per query past the attention grid selects and writes the
     // pool (the attention workgroups then need only the Top-K's candidates)
     const int main_grid = a.n_q * HG * S;
@@ -210,8 +219,13 @@ __global__ __launch_bounds__(kNT) void k_attend(AttendArgs a) {
       o.topk_count = nullptr;
       o.rows = nullptr;
       o.r0 = o.r1 = 0;
-      pool_topk_select<0>(a.bscore + (int64_t)qp * a.ld_bs, (int)a.ld_bs, (cp + 7) >> 3, a.pool, a.topk, nullptr, o,
-                          *reinterpret_cast<PoolTopkLds<0>*>(s_mem + kOffLat), [] {});
+      const int nbq = (cp + 7) >> 3;
+      if (SRC == kSrcGroups && nbq > kMaxCand)
+        pool_from_groups(a.gkey + (int64_t)qp * a.ld_gkey, a.gcap, a.bscore + (int64_t)qp * a.ld_bs, a.ld_bs, nbq,
+                         a.pool, o.pool, o.pool_count, *reinterpret_cast<PoolGroupLds*>(s_mem));
+      else
+        pool_topk_select<0>(a.bscore + (int64_t)qp * a.ld_bs, (int)a.ld_bs, nbq, a.pool, a.topk, nullptr, o,
+                            *reinterpret_cast<PoolTopkLds<0>*>(s_mem + kOffLat), [] {});
       return;
     }
   }
@@ -340,6 +354,10 @@ __global__ __launch_bounds__(kNT) void k_attend(AttendArgs a) {
         kept = topk_from_pool<SEL>(a.pool_blocks + (int64_t)q * a.pool, min(pcount, a.pool), a.pool,
                                    a.bscore + (int64_t)q * a.ld_bs, a.pkey + (int64_t)q * a.ld_pkey, K, o, nullptr,
                                    sl, load_q_sel);
+      else if (SRC == kSrcGroups && ((c + 7) >> 3) > kMaxCand)
+        kept = topk_from_groups<SEL>(a.gkey + (int64_t)q * a.ld_gkey, a.gcap, a.bscore + (int64_t)q * a.ld_bs, a.ld_bs,
+                                     (c + 7) >> 3, a.pkey + (int64_t)q * a.ld_pkey, K, o, sl,
+                                     reinterpret_cast<int32_t*>(s_mem + kOffGrp), load_q_sel);
       else
         kept = pool_topk_select<SEL>(a.bscore + (int64_t)q * a.ld_bs, (int)a.ld_bs, (c + 7) >> 3, a.pool, K,
                                      a.pkey + (int64_t)q * a.ld_pkey, o, sl, load_q_sel);
@@ -690,8 +708,19 @@ hipError_t launch_attend(const AttendArgs& a, hipStream_t s) {
     } else {
       // plus one pool workgroup per query
       const dim3 gp((unsigned)(a.n_q * a.head_groups * a.splits + a.n_q));
-      if (a.topk <= kTkThreads) hipLaunchKernelGGL((k_attend<2, kSrcScan>), gp, dim3(kNT), 0, s, a);
-      else hipLaunchKernelGGL((k_attend<4, kSrcScan>), gp, dim3(kNT), 0, s, a);
+      if (a.gkey) {
+        // long queries from the group keys: Top-K within 1024 (candidate
+        // groups, 512 SEL of them), pool within half the candidate groups
+        if (a.topk > 2 * kTkThreads || 2 * a.pool > kPoolGroupCap || a.gcap < 4 || a.gcap % 4 ||
+            a.gcap > kMaxGroups || a.ld_gkey < a.gcap)
+          return hipErrorInvalidValue;
+        if (a.topk <= kTkThreads) hipLaunchKernelGGL((k_attend<2, kSrcGroups>), gp, dim3(kNT), 0, s, a);
+        else hipLaunchKernelGGL((k_attend<4, kSrcGroups>), gp, dim3(kNT), 0, s, a);
+      } else if (a.topk <= kTkThreads) {
+        hipLaunchKernelGGL((k_attend<2, kSrcScan>), gp, dim3(kNT), 0, s, a);
+      } else {
+        hipLaunchKernelGGL((k_attend<4, kSrcScan>), gp, dim3(kNT), 0, s, a);
+      }
     }
   }
   if (a.splits > 1) {

@@ -102,6 +102,11 @@ struct AttendArgs {
   int32_t* topk_count_out;
   int sel_from_pool;         // 1: the pool is given (pool_blocks, pool_count are read), only the Top-K is selected
   const uint32_t* rkeys;     // Reindex order keys [n_q, 8 * pool] (csa2_reindex_attend): the Top-K from them
+  // the scan's group keys (nullptr: none): a query of more than kMaxCand
+  // blocks selects from them, query q's at gkey + q * ld_gkey, gcap words
+  const uint32_t* gkey;
+  int64_t ld_gkey;
+  int gcap;
 };
 
 // A Full layer's Top-K from the Full scan's own scores (the same indexer
@@ -128,6 +133,7 @@ hipError_t launch_page_rows(int64_t n, const int32_t* pages, int page_shift, con
                             const int32_t* pos, int64_t* dst_row, hipStream_t s);
 hipError_t launch_pool_select(const PoolArgs& a, hipStream_t s);
 int64_t pool_ws_words(int chunks, int mm_cap);   // workspace words per query
+int64_t pool_gkey_off(int chunks, int mm_cap);   // word offset of the group keys in a query's workspace
 hipError_t launch_reindex(const ReindexArgs& a, hipStream_t s);
 hipError_t launch_attend(const AttendArgs& a, hipStream_t s);
 hipError_t launch_topk_keys(const TopkKeysArgs& a, hipStream_t s);
@@ -137,6 +143,7 @@ hipError_t launch_stream_read(const void* buf, int64_t bytes, uint32_t* sink, in
 constexpr int kPoolChunk = 4096;       // blocks per pool-select chunk workgroup
 constexpr int kPoolChunkCand = 1024;   // candidate slots per chunk
 constexpr int kPoolSmallBlocks = 16384;   // blocks a one-workgroup pool selection holds
+constexpr int kPoolGroupsMax = 8192;      // group keys an in-kernel selection holds (131,072 blocks)
 constexpr int kAttendTile = 64;        // entries per attention tile
 constexpr int kAttendWaves = 8;        // waves per attention workgroup (two groups of 16 heads, 4 waves each)
 constexpr int kAttendHeads = 32;       // heads per attention workgroup

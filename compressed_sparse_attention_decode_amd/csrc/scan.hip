@@ -390,11 +390,32 @@ __global__ __launch_bounds__(64 * NW) void k_scan(ScanArgs a) {
   float* bs = a.bscore + (int64_t)q * a.ld + (p_begin >> 3);
   const int nblk = (p_end - p_begin + 7) >> 3;
   uint32_t lo = 0xFFFFFFFFu, hi = 0;
-  for (int i = tid; i < nblk; i += NT) {
-    const float v = s_bs[i];
-    bs[i] = v;
-    lo = min(lo, order_key(v));
-    hi = max(hi, order_key(v));
+  if (a.gkey) {
+    // and the group keys: 16 lanes hold one group's blocks (the tile starts
+    // at a group boundary; a partial last group reads 0 past the tile)
+    uint32_t* gk = a.gkey + (int64_t)q * a.ld_gkey + (p_begin >> 7);
+    const int nblk16 = (nblk + kGroupBlocks - 1) & ~(kGroupBlocks - 1);
+    for (int i = tid; i < nblk16; i += NT) {
+      const bool live = i < nblk;
+      const float v = s_bs[min(i, nblk - 1)];
+      const uint32_t k = live ? order_key(v) : 0u;
+      if (live) {
+        bs[i] = v;
+        lo = min(lo, k);
+        hi = max(hi, k);
+      }
+      uint32_t m = k;
+#pragma unroll
+      for (int d = 1; d < kGroupBlocks; d <<= 1) m = max(m, (uint32_t)__shfl_xor(m, d, 64));
+      if ((i & (kGroupBlocks - 1)) == 0) gk[i >> 4] = m;
+    }
+  } else {
+    for (int i = tid; i < nblk; i += NT) {
+      const float v = s_bs[i];
+      bs[i] = v;
+      lo = min(lo, order_key(v));
+      hi = max(hi, order_key(v));
+    }
   }
   if (a.pool_ws) {
     // the tile's key range for the pool select, and (tile 0) its histogram cleared
@@ -459,6 +480,8 @@ hipError_t launch_scan(const ScanArgs& a, hipStream_t s) {
     return hipErrorInvalidValue;
   if (a.tile_extra < 0 || a.tile_extra % 8 || a.tile_extra >= a.tile_pos ||
       a.tile_pos + a.tile_extra > kMaxTilePos || (a.tile_extra && (a.tiles & 1)))
+    return hipErrorInvalidValue;
+  if (a.gkey && (a.tile_pos % (8 * kGroupBlocks) || a.tile_extra % (8 * kGroupBlocks) || a.ld_gkey < 4))
     return hipErrorInvalidValue;
   if (a.idx_k_scales) {
     if (a.d != 128 || !a.idx_q_scales) return hipErrorInvalidValue;

@@ -43,6 +43,12 @@ struct ScanArgs {
   // Top-K can be selected without scoring the pool again
   uint32_t* pkey;
   int64_t ld_pkey;
+  // optional (nullptr: not written): per group of kGroupBlocks consecutive
+  // blocks of a query (128 positions), the largest of their block scores'
+  // order keys, group i of query q at gkey[q * ld_gkey + i]; every tile then
+  // starts at a multiple of 128 positions
+  uint32_t* gkey;
+  int64_t ld_gkey;
 };
 
 hipError_t launch_scan(const ScanArgs& a, hipStream_t s);
@@ -52,5 +58,6 @@ constexpr int kScanTile = 2048;        // default positions per scan workgroup
 constexpr int kScanPrefetch = 4;       // default LDS ring slots per wave
 constexpr int kScanWaves = 4;          // default waves per scan workgroup
 constexpr int kScanTileExtra = 512;    // uneven-tile shift when the grid is one round of two per CU
+constexpr int kGroupBlocks = 16;       // blocks per group key
 
 }  // namespace csa2

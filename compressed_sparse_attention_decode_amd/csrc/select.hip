@@ -624,9 +624,16 @@ __global__ __launch_bounds__(kTkThreads) void k_pool_small(PoolArgs a) {
 
 }  // namespace
 
-int64_t pool_ws_words(int chunks, int mm_cap) {
+// After the chunked selection's words: the scan's group keys (one per
+// kGroupBlocks blocks, for the in-kernel selections of long queries).
+int64_t pool_gkey_off(int chunks, int mm_cap) {
   const int64_t words = kHistBins + 2 * (int64_t)mm_cap + chunks + 1 + (int64_t)chunks * (kPoolChunk / 32) +
                         2 * (int64_t)chunks * kPoolChunkCand;
+  return (words + 3) / 4 * 4;
+}
+
+int64_t pool_ws_words(int chunks, int mm_cap) {
+  const int64_t words = pool_gkey_off(chunks, mm_cap) + (int64_t)chunks * (kPoolChunk / kGroupBlocks);
   return (words + 63) / 64 * 64;
 }
 
