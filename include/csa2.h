@@ -218,7 +218,9 @@ csa2_status csa2_encode_fp4(int64_t n, int32_t width, const uint16_t* src, const
  *                computes (each tile's smallest and largest block score, and
  *                a cleared histogram), so that the following csa2_index_pool
  *                call on these block scores, passed the same workspace and
- *                CSA2_POOL_WS_FROM_SCAN, skips that pass.
+ *                CSA2_POOL_WS_FROM_SCAN, skips that pass; and, per 16 blocks,
+ *                the largest block score (as an order key), from which
+ *                csa2_pool_topk_attend selects long queries.
  * One kernel.  Queries with n <= W write no block scores. */
 csa2_status csa2_index_scan(const csa2_dims* dims, const csa2_queries* q,
                             const uint8_t* idx_q, const float* idx_w, const uint8_t* idx_k,
@@ -482,19 +484,27 @@ csa2_status csa2_attend_paged(const csa2_dims* dims, const csa2_queries* q, cons
  * every query has at most 16,384 blocks (contexts up to about 131K
  * positions) the pool is selected there too (the same selection as
  * csa2_index_pool_topk's one-workgroup kernel, repeated by each such
- * workgroup): one attention launch for the whole chain.  Otherwise the
- * chunked pool kernels run first and the attention workgroups select the
- * Top-K of that pool (as csa2_index_topk_keys).  The workgroup holding head
- * group 0's first kept-entry tile writes pool_blocks, pool_count (small
- * pools), topk_pos and topk_count, as csa2_index_pool_topk writes them; out
- * and lse are csa2_attend's on that Top-K.
+ * workgroup): one attention launch for the whole chain.  Longer queries
+ * (up to 131,072 blocks, contexts up to about 1M positions) after a scan
+ * that prepared pool_ws (flags CSA2_POOL_WS_FROM_SCAN) are selected in the
+ * same launch from the scan's group keys (the largest block score of every
+ * 16 blocks, which pool_ws holds): one extra workgroup per query writes the
+ * pool, and the attention workgroups take the Top-K's candidates from the
+ * groups at or above a bound of the K-th group key; the result is exact
+ * (candidates that overflow their room fall back to an exact selection that
+ * streams every block score).  Otherwise the chunked pool kernels run first
+ * and the attention workgroups select the Top-K of that pool (as
+ * csa2_index_topk_keys).  pool_blocks and pool_count are written as
+ * csa2_index_pool_topk writes them, and the workgroup holding head group 0's
+ * first kept-entry tile writes topk_pos and topk_count; out and lse are
+ * csa2_attend's on that Top-K.
  *   block_scores, pos_keys   as written by csa2_index_scan_keys
  *   q_lat ... lse            as in csa2_attend (topk_pos, topk_count are
  *                            outputs here)
  *   pool_ws, pool_ws_bytes, flags  as ws, ws_bytes, flags of
- *                            csa2_index_pool (read only for the chunked
- *                            kernels; NULL and 0 are accepted for small
- *                            pools)
+ *                            csa2_index_pool (read only for queries past
+ *                            16,384 blocks; NULL and 0 are accepted for
+ *                            small pools)
  *   ws, ws_bytes             csa2_attend_workspace_size bytes, as in csa2_attend
  * Errors: CSA2_ERR_UNSUPPORTED for paged planes (call csa2_index_pool_topk
  * and csa2_attend_paged); otherwise as those calls. */
