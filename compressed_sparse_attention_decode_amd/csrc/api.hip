@@ -1,5 +1,6 @@
 // C ABI of the CSA2 decode-path library: argument checks, workspace layout and
 // kernel launches.  Declarations and contracts are in include/csa2.h.
+#include <algorithm>
 #include <mutex>
 #include <stdlib.h>
 #include <stdarg.h>
@@ -765,6 +766,7 @@ struct AttendSel {
   const uint32_t* gkeys;     // the scan's group keys: queries past kPoolSmallBlocks blocks select from them
   int64_t ld_gkeys;
   int gcap;
+  int group_min;             // (and the Top-K of queries past this many blocks)
 };
 
 // Whether every query's pool fits one selecting workgroup (and the
@@ -830,11 +832,11 @@ static csa2_status attend(const csa2_dims* d, const csa2_queries* q, const uint1
   aa.pool_blocks = nullptr; aa.pool_count = nullptr; aa.topk_out = nullptr; aa.topk_count_out = nullptr;
   aa.sel_from_pool = 0;
   aa.rkeys = nullptr;
-  aa.gkey = nullptr; aa.ld_gkey = 0; aa.gcap = 0;
+  aa.gkey = nullptr; aa.ld_gkey = 0; aa.gcap = 0; aa.group_min = kPoolSmallBlocks;
   if (sel) {
     aa.sel_from_pool = sel->from_pool ? 1 : 0;
     aa.rkeys = sel->rkeys;
-    aa.gkey = sel->gkeys; aa.ld_gkey = sel->ld_gkeys; aa.gcap = sel->gcap;
+    aa.gkey = sel->gkeys; aa.ld_gkey = sel->ld_gkeys; aa.gcap = sel->gcap; aa.group_min = sel->group_min;
     aa.bscore = sel->block_scores; aa.ld_bs = sel->ld_block_scores;
     aa.pkey = sel->pos_keys; aa.ld_pkey = sel->ld_pos_keys;
     aa.pool_blocks = sel->pool_blocks; aa.pool_count = sel->pool_count;
@@ -886,13 +888,18 @@ static csa2_status pool_topk_attend(const csa2_dims* d, const csa2_queries* q, c
   if ((st = check_queries(q))) return st;
   if (flags & ~CSA2_POOL_WS_FROM_SCAN) return fail(CSA2_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
   const bool small = pool_small(d, q);
-  if (!small && (st = check_ws(pool_wsp, pool_ws_bytes, pool_ws(d, q)))) return st;
   if ((st = check_device())) return st;          // (the scan's tile shape reads the device)
   // a long query after the scan: pool and Top-K from the scan's group keys
   // in the attention launch (CSA2_POOL_GROUPS=0: the chunked pool kernels)
-  bool groups = !small && (flags & CSA2_POOL_WS_FROM_SCAN) && scan_groups_ok(d, q) &&
-                max_blocks(d, q) <= (int64_t)kPoolGroupsMax * kGroupBlocks && d->topk <= 1024;
+  // (CSA2_GROUP_MIN: the Top-K of queries past that many blocks from the
+  // group keys too, small pools included; for tuning)
+  int group_min = kPoolSmallBlocks;
+  if (const char* env = getenv("CSA2_GROUP_MIN")) group_min = std::min(std::max(atoi(env), 0), kPoolSmallBlocks);
+  bool groups = (!small || (group_min < kPoolSmallBlocks && pool_wsp)) && (flags & CSA2_POOL_WS_FROM_SCAN) &&
+                scan_groups_ok(d, q) && max_blocks(d, q) <= (int64_t)kPoolGroupsMax * kGroupBlocks &&
+                d->topk <= 1024 && 2 * d->pool_blocks <= 4096;
   if (const char* env = getenv("CSA2_POOL_GROUPS")) groups = groups && atoi(env) != 0;
+  if ((!small || groups) && (st = check_ws(pool_wsp, pool_ws_bytes, pool_ws(d, q)))) return st;
   // a Top-K of more than 1024 positions from a given pool is selected apart
   // (k_topk_keys): its positions step does not fit beside the attention
   const bool apart = !small && !groups && d->topk > 1024;
@@ -901,7 +908,7 @@ static csa2_status pool_topk_attend(const csa2_dims* d, const csa2_queries* q, c
                 (st = check_pos_keys(d, q, pos_keys, ld_pos_keys))))
     return st;
   AttendSel sel{block_scores, ld_block_scores, pos_keys, ld_pos_keys, pool_blocks, pool_count, !small && !groups,
-                nullptr, nullptr, 0, 0};
+                nullptr, nullptr, 0, 0, group_min};
   if (groups) {
     sel.gkeys = (const uint32_t*)pool_wsp + pool_gkey_off(pool_chunks(d, q), pool_mm_cap(d, q));
     sel.ld_gkeys = pool_ws_words(pool_chunks(d, q), pool_mm_cap(d, q));

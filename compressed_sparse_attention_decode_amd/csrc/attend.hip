@@ -354,7 +354,7 @@ __global__ __launch_bounds__(kNT) void k_attend(AttendArgs a) {
         kept = topk_from_pool<SEL>(a.pool_blocks + (int64_t)q * a.pool, min(pcount, a.pool), a.pool,
                                    a.bscore + (int64_t)q * a.ld_bs, a.pkey + (int64_t)q * a.ld_pkey, K, o, nullptr,
                                    sl, load_q_sel);
-      else if (SRC == kSrcGroups && ((c + 7) >> 3) > kMaxCand)
+      else if (SRC == kSrcGroups && ((c + 7) >> 3) > a.group_min)
         kept = topk_from_groups<SEL>(a.gkey + (int64_t)q * a.ld_gkey, a.gcap, a.bscore + (int64_t)q * a.ld_bs, a.ld_bs,
                                      (c + 7) >> 3, a.pkey + (int64_t)q * a.ld_pkey, K, o, sl,
                                      reinterpret_cast<int32_t*>(s_mem + kOffGrp), load_q_sel);
@@ -712,7 +712,7 @@ hipError_t launch_attend(const AttendArgs& a, hipStream_t s) {
         // long queries from the group keys: Top-K within 1024 (candidate
         // groups, 512 SEL of them), pool within half the candidate groups
         if (a.topk > 2 * kTkThreads || 2 * a.pool > kPoolGroupCap || a.gcap < 4 || a.gcap % 4 ||
-            a.gcap > kMaxGroups || a.ld_gkey < a.gcap)
+            a.gcap > kMaxGroups || a.ld_gkey < a.gcap || a.group_min < 0 || a.group_min > kMaxCand)
           return hipErrorInvalidValue;
         if (a.topk <= kTkThreads) hipLaunchKernelGGL((k_attend<2, kSrcGroups>), gp, dim3(kNT), 0, s, a);
         else hipLaunchKernelGGL((k_attend<4, kSrcGroups>), gp, dim3(kNT), 0, s, a);

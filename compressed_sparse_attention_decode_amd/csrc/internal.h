@@ -107,6 +107,7 @@ struct AttendArgs {
   const uint32_t* gkey;
   int64_t ld_gkey;
   int gcap;
+  int group_min;             // queries of more blocks take the Top-K from the group keys (<= kMaxCand)
 };
 
 // A Full layer's Top-K from the Full scan's own scores (the same indexer

@@ -242,22 +242,26 @@ __device__ __forceinline__ uint32_t topk_from_keys(const uint32_t* ks, const int
   for (int k = 0; k < kPer; ++k) flags |= (uint32_t)(key[k] >= cut.tt) << k;
   uint32_t total;
   uint32_t before = block_exclusive_scan<kTkThreads>(__builtin_popcount(flags), s_scan, &total);
+  // the positions by rank into LDS (the histogram's words, free once the
+  // selection is made), then whole-row writes of the Top-K and of the rows
+  uint32_t* s_tk = L.hist;
   while (flags) {
     const int k = __builtin_ctz(flags);
     flags &= flags - 1;
     int32_t b = blk[0];
 #pragma unroll
     for (int j = 1; j < kBP; ++j) b = (k >> 3) == j ? blk[j] : b;
-    const int32_t p = b * kBlock + (k & 7);
-    if (before < (uint32_t)K) {
-      if (o.topk) o.topk[before] = p;
-      if (o.rows && (int)before >= o.r0 && (int)before < o.r1) o.rows[before - o.r0] = p;
-    }
+    if (before < (uint32_t)K) s_tk[before] = (uint32_t)(b * kBlock + (k & 7));
     ++before;
   }
+  __syncthreads();
+  const int keff = (int)cut.keff;
   if (o.topk)
-    for (int t = (int)cut.keff + tid; t < K; t += kTkThreads) o.topk[t] = -1;
+    for (int t = tid; t < K; t += kTkThreads) o.topk[t] = t < keff ? (int32_t)s_tk[t] : -1;
+  if (o.rows)
+    for (int t = o.r0 + tid; t < min(o.r1, keff); t += kTkThreads) o.rows[t - o.r0] = (int32_t)s_tk[t];
   if (o.topk_count && tid == 0) *o.topk_count = (int32_t)cut.keff;
+  __syncthreads();                                   // (s_tk read before the caller reuses L)
   return cut.keff;
 }
 

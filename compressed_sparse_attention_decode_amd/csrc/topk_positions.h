@@ -53,25 +53,40 @@ __device__ __forceinline__ uint32_t topk_positions(const int32_t* s_blk, uint32_
   for (int k = 0; k < PP; ++k) pflags |= (uint32_t)(key[k] >= cut.tt) << k;
   uint32_t total;
   uint32_t pos_before = block_exclusive_scan<kTkThreads>(__builtin_popcount(pflags), s_scan, &total);
+  if (out_s) {
 #pragma unroll
-  for (int k = 0; k < PP; ++k) {
-    if (pflags >> k & 1u) {
-      if (pos_before < (uint32_t)K) {
-        const int32_t p = mb[k >> 3] * kBlock + (k & 7);
-        if (out) out[pos_before] = p;
-        if (out_s) out_s[pos_before] = key_float(key[k]);
-        if (rows && (int)pos_before >= r0 && (int)pos_before < r1) rows[pos_before - r0] = p;
+    for (int k = 0; k < PP; ++k) {
+      if (pflags >> k & 1u) {
+        if (pos_before + __builtin_popcount(pflags & ((1u << k) - 1u)) < (uint32_t)K)
+          out_s[pos_before + __builtin_popcount(pflags & ((1u << k) - 1u))] = key_float(key[k]);
       }
-      ++pos_before;
     }
   }
-  if (out) {
-    for (int t = (int)cut.keff + tid; t < K; t += kTkThreads) {
-      out[t] = -1;
-      if (out_s) out_s[t] = 0.0f;
-    }
+  // the positions by rank into LDS (the histogram's words: free once the
+  // selection is made), one short loop over this thread's selected slots;
+  // then whole-row writes of the Top-K and of the rows [r0, r1)
+  static_assert(kTkBins + kTkEmpty >= 2048, "a Top-K of up to 2048 positions staged in the histogram");
+  uint32_t* s_tk = L.hist;
+  uint32_t f = pflags;
+  while (f) {
+    const int k = __builtin_ctz(f);
+    f &= f - 1;
+    int32_t b = mb[0];
+#pragma unroll
+    for (int j = 1; j < BPT; ++j) b = (k >> 3) == j ? mb[j] : b;
+    if (pos_before < (uint32_t)K) s_tk[pos_before] = (uint32_t)(b * kBlock + (k & 7));
+    ++pos_before;
   }
+  __syncthreads();
+  const int keff = (int)cut.keff;
+  if (out)
+    for (int t = tid; t < K; t += kTkThreads) out[t] = t < keff ? (int32_t)s_tk[t] : -1;
+  if (out_s)
+    for (int t = keff + tid; t < K; t += kTkThreads) out_s[t] = 0.0f;
+  if (rows)
+    for (int t = r0 + tid; t < min(r1, keff); t += kTkThreads) rows[t - r0] = (int32_t)s_tk[t];
   if (count && tid == 0) *count = (int32_t)cut.keff;
+  __syncthreads();                                   // (s_tk read before the caller reuses L)
   return cut.keff;
 }
 
