@@ -92,12 +92,24 @@ __global__ __launch_bounds__(64 * NW) void k_scan(ScanArgs a) {
 
   // block -> (query, tile); the g tokens of one sequence and the same tile
   // land on the same XCD (block ids equal mod 8) so their key reads share L2.
+  // Eight or more sequences: XCD x takes sequences x, x + 8, ... whole.
+  // One, two or four sequences of single tokens: each sequence's XCDs take
+  // contiguous runs of its tiles, a run of long tiles (dispatched first)
+  // and a run of short ones, instead of every eighth tile (measured: 0.6 us
+  // less for one sequence of 1M positions).
   const int g = a.g;
   const int bid = blockIdx.x;
   const int unit = (bid / (8 * g)) * 8 + (bid & 7);
   const int j = (bid >> 3) % g;
   const int n_groups = a.n_q / g;
-  const int group = unit % n_groups, tile = unit / n_groups;
+  int group = unit % n_groups, tile = unit / n_groups;
+  if (g == 1 && n_groups < 8 && 8 % n_groups == 0 && a.tiles % (16 / n_groups) == 0) {
+    const int X = 8 / n_groups;                   // XCDs per sequence
+    const int per = a.tiles / (2 * X);            // long (and short) tiles per XCD run
+    const int xcd = bid & 7, jj = bid >> 3;
+    group = xcd / X;
+    tile = jj < per ? per * (xcd % X) + jj : (a.tiles >> 1) + per * (xcd % X) + (jj - per);
+  }
   if (tile >= a.tiles) return;
   const int q = group * g + j;
 

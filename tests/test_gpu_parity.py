@@ -54,6 +54,10 @@ CASES = {
                        [3000], fp4=True),
     # 16 query tokens of one sequence (a chunk scored against one key stream)
     "chunk_g16": small(141, BIG, [9000], g=16),
+    # two and four sequences whose scan tiles (2048 positions) split evenly
+    # over their XCDs: each XCD takes contiguous runs of one sequence's tiles
+    "xcd_runs_b2": small(151, BIG, [65536 + 128, 30000]),
+    "xcd_runs_b4": small(152, BIG, [32768 + 128, 20000, 5001, 32768 + 100]),
     # the group-32 main-KV codec (one E4M3 scale per 32 latent channels)
     "kvg32_ragged_b3": small(131, dataclasses.replace(BIG, kv_group=32), [20005, 9003, 4099]),
     "kvg32_edge_short": small(132, wl.Dims(n_heads=16, idx_heads=16, idx_dim=128, pool_blocks=4, topk=16,
