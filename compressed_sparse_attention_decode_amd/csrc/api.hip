@@ -897,7 +897,7 @@ static csa2_status pool_topk_attend(const csa2_dims* d, const csa2_queries* q, c
   if (const char* env = getenv("CSA2_GROUP_MIN")) group_min = std::min(std::max(atoi(env), 0), kPoolSmallBlocks);
   bool groups = (!small || (group_min < kPoolSmallBlocks && pool_wsp)) && (flags & CSA2_POOL_WS_FROM_SCAN) &&
                 scan_groups_ok(d, q) && max_blocks(d, q) <= (int64_t)kPoolGroupsMax * kGroupBlocks &&
-                d->topk <= 1024 && 2 * d->pool_blocks <= 4096;
+                d->topk <= 1024 && d->topk <= d->pool_blocks && 2 * d->pool_blocks <= 4096;   // (K > P: the exact pool decides)
   if (const char* env = getenv("CSA2_POOL_GROUPS")) groups = groups && atoi(env) != 0;
   if ((!small || groups) && (st = check_ws(pool_wsp, pool_ws_bytes, pool_ws(d, q)))) return st;
   // a Top-K of more than 1024 positions from a given pool is selected apart

@@ -358,6 +358,10 @@ __global__ __launch_bounds__(kNT) void k_attend(AttendArgs a) {
         kept = topk_from_groups<SEL>(a.gkey + (int64_t)q * a.ld_gkey, a.gcap, a.bscore + (int64_t)q * a.ld_bs, a.ld_bs,
                                      (c + 7) >> 3, a.pkey + (int64_t)q * a.ld_pkey, K, o, sl,
                                      reinterpret_cast<int32_t*>(s_mem + kOffGrp), load_q_sel);
+      else if (K <= a.pool)                       // (the K best blocks lie in the pool)
+        kept = topk_from_blocks<SEL>(a.bscore + (int64_t)q * a.ld_bs, (int)a.ld_bs, (c + 7) >> 3,
+                                     a.pkey + (int64_t)q * a.ld_pkey, K, o, sl,
+                                     reinterpret_cast<uint32_t*>(s_mem + kOffGrp), load_q_sel);
       else
         kept = pool_topk_select<SEL>(a.bscore + (int64_t)q * a.ld_bs, (int)a.ld_bs, (c + 7) >> 3, a.pool, K,
                                      a.pkey + (int64_t)q * a.ld_pkey, o, sl, load_q_sel);

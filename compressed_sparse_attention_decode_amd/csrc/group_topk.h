@@ -170,7 +170,8 @@ __device__ __forceinline__ uint32_t topk_from_groups(const uint32_t* gk, int gca
   uint32_t key[kGroupPer];
   load_group_keys(gk, ng, gcap, key);
   after_keys();
-  const TopkBound bd = radix_bound<kGroupPer>(key, K, L.radix);
+  const TopkBound bd = K <= kTkThreads ? radix_bound_top<kGroupPer>(key, K, L.radix)
+                                       : radix_bound<kGroupPer>(key, K, L.radix);
   const uint32_t lb = ng >= K ? bd.lb : 1u;               // too few groups: every block
   uint32_t gflags = 0;
 #pragma unroll
@@ -226,6 +227,73 @@ __device__ __forceinline__ uint32_t topk_from_groups(const uint32_t* gk, int gca
   if (cut.keff) stream_emit(bs, nb, cut, L.scan, [&](uint32_t r, int i) { L.blk[r] = i; });
   __syncthreads();
   return topk_positions<BPT>(L.blk, cut.keff, pk, K, o.topk, nullptr, o.topk_count, L.scan, L.radix, o.rows, o.r0,
+                             o.r1);
+}
+
+// ------------------------------------------------------------ Top-K, short queries
+// The Full layer's Top-K of a query of nb <= kMaxCand blocks for an
+// attention workgroup (the pool is written elsewhere, K <= P): the blocks at
+// or above the first histogram's bound for the K-th block key, in ascending
+// order, then the K best of their positions.  The block scores are read
+// coalesced (thread t takes blocks 4 (512 v + t) .. + 3, v < 8: each load
+// instruction covers whole lines once; 32 consecutive blocks per thread made
+// every instruction touch 64 lines and fetch each line eight times), so slot
+// order is not block order: the candidates are marked in an LDS bitmap
+// (s_bits, 512 words) and compacted in ascending order from it.  A crowded
+// bin takes the exact streaming selection.  Returns the Top-K count.
+template <int BPT, typename AfterKeys>
+__device__ __forceinline__ uint32_t topk_from_blocks(const float* bs, int ld, int nb, const uint32_t* pk, int K,
+                                                     const PoolTopkOut& o, PoolTopkLds<BPT>& L, uint32_t* s_bits,
+                                                     AfterKeys&& after_keys) {
+  constexpr uint32_t kCap = kTkThreads * BPT;
+  constexpr int NV = kPer / 4;                       // 16-byte loads per thread
+  const int tid = threadIdx.x;
+  v4f x[NV];
+#pragma unroll
+  for (int v = 0; v < NV; ++v) x[v] = *reinterpret_cast<const v4f*>(bs + min(4 * (kTkThreads * v + tid), ld - 4));
+  uint32_t key[kPer];
+#pragma unroll
+  for (int v = 0; v < NV; ++v) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) key[4 * v + e] = 4 * (kTkThreads * v + tid) + e < nb ? order_key(x[v][e]) : 0u;
+  }
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) asm volatile("" : "+v"(key[k]));   // the keys are complete here
+  after_keys();
+  s_bits[tid] = 0u;                                  // (ordered by the bound's barriers)
+  const TopkBound bd = K <= kTkThreads ? radix_bound_top<kPer>(key, K, L.radix) : radix_bound<kPer>(key, K, L.radix);
+  uint32_t nmine = 0;
+#pragma unroll
+  for (int v = 0; v < NV; ++v) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (key[4 * v + e] >= bd.lb) {
+        const int b = 4 * (kTkThreads * v + tid) + e;
+        atomicOr(&s_bits[b >> 5], 1u << (b & 31));
+        ++nmine;
+      }
+    }
+  }
+  uint32_t ncand;
+  block_exclusive_scan<kTkThreads>(nmine, L.scan, &ncand);   // (its barriers complete the marks)
+  uint32_t nsel;
+  if (ncand <= kCap) {
+    // thread t: the bitmap word of blocks [32 t, 32 t + 32)
+    uint32_t w = s_bits[tid];
+    uint32_t cb = block_exclusive_scan<kTkThreads>((uint32_t)__builtin_popcount(w), L.scan, &nsel);
+    while (w) {
+      const int k = __builtin_ctz(w);
+      w &= w - 1;
+      L.blk[cb++] = tid * 32 + k;                    // ascending block ids
+    }
+  } else {
+    // crowded: the exact K best blocks (K <= kCap), ascending
+    const StreamCut cut = stream_cut(bs, nb, K, L.radix);
+    if (cut.keff) stream_emit(bs, nb, cut, L.scan, [&](uint32_t r, int i) { L.blk[r] = i; });
+    nsel = cut.keff;
+  }
+  __syncthreads();
+  return topk_positions<BPT>(L.blk, nsel, pk, K, o.topk, nullptr, o.topk_count, L.scan, L.radix, o.rows, o.r0,
                              o.r1);
 }
 

@@ -291,6 +291,55 @@ __device__ __forceinline__ TopkBound radix_bound(const uint32_t (&key)[PER], int
   return r;
 }
 
+// radix_bound for K <= kTkThreads, with a prefilter: the smallest of the
+// threads' own largest keys, t0, is at most the K-th largest key (the
+// threads' largest keys are kTkThreads >= K distinct keys at or above it),
+// so only the keys at or above t0 enter the histogram, whose bins then span
+// [t0, max]: a few thousand LDS atomics instead of one per key, and finer
+// bins where the bound falls.  (A thread without keys makes t0 = 0: every
+// key enters, as in radix_bound.)  Same result contract as radix_bound.
+template <int PER>
+__device__ __forceinline__ TopkBound radix_bound_top(const uint32_t (&key)[PER], int K, RadixLds& L) {
+  static_assert(PER >= 1 && PER <= 32, "PER keys per thread");
+  constexpr int NW = kTkWaves;
+  uint32_t* s_hist = L.hist;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  *reinterpret_cast<v4u*>(s_hist + 4 * tid) = v4u{0u, 0u, 0u, 0u};
+  uint32_t lo = 0xFFFFFFFFu, hi = 0;
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    lo = min(lo, key[k] - 1u);
+    hi = max(hi, key[k]);
+  }
+  // block minimum of (key - 1), maximum of the keys, minimum of the threads'
+  // maxima: one barrier pair (its barriers also order the clear)
+  uint32_t t0 = hi;
+  lo = wave_reduce_u32(lo, [](uint32_t x, uint32_t y) { return min(x, y); });
+  t0 = wave_reduce_u32(t0, [](uint32_t x, uint32_t y) { return min(x, y); });
+  hi = wave_reduce_u32(hi, [](uint32_t x, uint32_t y) { return max(x, y); });
+  if (lane == 0) { L.red[wave] = lo; L.red[NW + wave] = hi; L.misc[wave & 7] = t0; }
+  static_assert(NW <= 8, "one misc word per wave");
+  __syncthreads();
+  uint32_t rl = 0xFFFFFFFFu, rh = 0, rt = 0xFFFFFFFFu;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) { rl = min(rl, L.red[w]); rh = max(rh, L.red[NW + w]); rt = min(rt, L.misc[w]); }
+  __syncthreads();
+  const uint32_t kmin = rl + 1u, kmax = rh;
+  if (kmax == 0) return TopkBound{0xFFFFFFFFu, 0u};
+  const uint32_t base = K <= kTkThreads ? max(kmin, rt) : kmin;
+  const uint32_t d = kmax - base;
+  const int shift = d ? max(0, 21 - (int)__clz(d)) : 0;   // (d >> shift) < 2^11
+#pragma unroll
+  for (int k = 0; k < PER; ++k)
+    if (key[k] >= base) atomicAdd(&s_hist[(key[k] - base) >> shift], 1u);
+  __syncthreads();
+  if (tid < 64) crossing_2048(s_hist, (uint32_t)K, L.misc2);
+  __syncthreads();
+  const TopkBound r{base + (L.misc2[0] << shift), L.misc2[1] + L.misc2[2]};
+  __syncthreads();                                   // (the next selection may reuse L at once)
+  return r;
+}
+
 // The same with LDS of its own (one per PER).
 template <int PER = kPer>
 __device__ __forceinline__ TopkCut radix_topk(uint32_t (&key)[PER], int K, int K2 = 0) {

@@ -50,6 +50,10 @@ LONG = {
     # a small pool and Top-K, the largest context the group keys take (131,072 blocks)
     "p256_max": _long(203, wl.Dims(n_heads=16, idx_heads=8, idx_dim=64, pool_blocks=256, topk=128),
                       [131072 * 8 + 128]),
+    # K > P: the Top-K is taken from exactly the pool, so the chunked pool
+    # kernels run (no group path), and the short query selects its exact pool
+    "k_above_p": _long(205, wl.Dims(n_heads=16, idx_heads=8, idx_dim=64, pool_blocks=64, topk=128),
+                       [200000, 3000]),
 }
 
 
