@@ -93,7 +93,9 @@ static_assert(kOffQ + kAttendHeads * kQS <= kTE * kLS * 2, "query latents fit in
 // a selecting split's candidate groups (long queries), in the image after the
 // query latents
 constexpr int kOffGrp = kOffQ + kAttendHeads * kQS;
-static_assert(kOffGrp % 16 == 0 && kOffGrp + 4 * 4 * kTkThreads <= kTE * kLS * 2, "candidate groups fit in the image");
+constexpr int kOffGrpBits = kOffGrp + 4 * 4 * kTkThreads;   // their bitmap
+static_assert(kOffGrp % 16 == 0 && kOffGrpBits + 4 * kMaxGroups / 32 <= kTE * kLS * 2,
+              "candidate groups and their bitmap fit in the image");
 static_assert(sizeof(PoolGroupLds) <= kLdsBytes, "a pool selection fits the workgroup's LDS");
 static_assert(kMaxGroups == kPoolGroupsMax, "the host's bound of the group keys");
 static_assert(kTE * 8 == kNT, "one rope chunk per thread");
@@ -357,7 +359,8 @@ __global__ __launch_bounds__(kNT) void k_attend(AttendArgs a) {
       else if (SRC == kSrcGroups && ((c + 7) >> 3) > a.group_min)
         kept = topk_from_groups<SEL>(a.gkey + (int64_t)q * a.ld_gkey, a.gcap, a.bscore + (int64_t)q * a.ld_bs, a.ld_bs,
                                      (c + 7) >> 3, a.pkey + (int64_t)q * a.ld_pkey, K, o, sl,
-                                     reinterpret_cast<int32_t*>(s_mem + kOffGrp), load_q_sel);
+                                     reinterpret_cast<int32_t*>(s_mem + kOffGrp),
+                                     reinterpret_cast<uint32_t*>(s_mem + kOffGrpBits), load_q_sel);
       else if (K <= a.pool)                       // (the K best blocks lie in the pool)
         kept = topk_from_blocks<SEL>(a.bscore + (int64_t)q * a.ld_bs, (int)a.ld_bs, (c + 7) >> 3,
                                      a.pkey + (int64_t)q * a.ld_pkey, K, o, sl,

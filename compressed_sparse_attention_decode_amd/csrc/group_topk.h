@@ -35,20 +35,54 @@ constexpr int kPoolCandCap = kTkThreads * kGroupPer;       // candidate blocks o
 constexpr int kPoolGpt = 2;                                // candidate groups per thread and round
 static_assert(kGroupBlocks == 16, "a group's blocks are four 16-byte loads");
 
-// Thread t's group keys [16 t, 16 t + 16), 0 past ng.  gk: the query's row of
-// gcap words (a multiple of 4, >= 4); loads are clamped into the row.
-__device__ __forceinline__ void load_group_keys(const uint32_t* gk, int ng, int gcap, uint32_t (&key)[kGroupPer]) {
-  const int s0 = threadIdx.x * kGroupPer;
+// Thread t's group keys, read coalesced: groups 4 (512 v + t) + e (v, e < 4;
+// every load instruction covers whole lines once), 0 past ng.  Slot order is
+// not group order: callers mark candidates in an LDS bitmap and compact it.
+__device__ __forceinline__ int group_of(int v, int e) { return 4 * (kTkThreads * v + (int)threadIdx.x) + e; }
+
+__device__ __forceinline__ void load_group_keys_c(const uint32_t* gk, int ng, int gcap, uint32_t (&key)[kGroupPer]) {
   v4u x[kGroupPer / 4];
 #pragma unroll
-  for (int v = 0; v < kGroupPer / 4; ++v) x[v] = *reinterpret_cast<const v4u*>(gk + min(s0 + 4 * v, gcap - 4));
+  for (int v = 0; v < kGroupPer / 4; ++v) x[v] = *reinterpret_cast<const v4u*>(gk + min(group_of(v, 0), gcap - 4));
 #pragma unroll
   for (int v = 0; v < kGroupPer / 4; ++v) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) key[4 * v + e] = s0 + 4 * v + e < ng ? x[v][e] : 0u;
+    for (int e = 0; e < 4; ++e) key[4 * v + e] = group_of(v, e) < ng ? x[v][e] : 0u;
   }
 #pragma unroll
   for (int k = 0; k < kGroupPer; ++k) asm volatile("" : "+v"(key[k]));   // the keys are complete here
+}
+
+// Marks this thread's groups with key >= lb in s_bits (kMaxGroups / 32
+// words, cleared before the caller's last barrier) and returns how many.
+__device__ __forceinline__ uint32_t mark_groups(const uint32_t (&key)[kGroupPer], uint32_t lb, uint32_t* s_bits) {
+  uint32_t n = 0;
+#pragma unroll
+  for (int v = 0; v < kGroupPer / 4; ++v) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (key[4 * v + e] >= lb && key[4 * v + e] != 0u) {
+        const int g = group_of(v, e);
+        atomicOr(&s_bits[g >> 5], 1u << (g & 31));
+        ++n;
+      }
+    }
+  }
+  return n;
+}
+
+// The marked groups in ascending order into out[0 ..): threads t <
+// kMaxGroups / 32 take bitmap word t.  Contains barriers (a block scan).
+__device__ __forceinline__ void compact_groups(const uint32_t* s_bits, int32_t* out, uint32_t* s_scan) {
+  const int tid = threadIdx.x;
+  uint32_t w = tid < kMaxGroups / 32 ? s_bits[tid] : 0u;
+  uint32_t total;
+  uint32_t at = block_exclusive_scan<kTkThreads>((uint32_t)__builtin_popcount(w), s_scan, &total);
+  while (w) {
+    const int k = __builtin_ctz(w);
+    w &= w - 1;
+    out[at++] = tid * 32 + k;
+  }
 }
 
 // The 16 block scores of group g (rows of stride ld, 16-byte aligned; blocks
@@ -162,28 +196,23 @@ __device__ __forceinline__ void stream_emit(const float* bs, int n, const Stream
 template <int BPT, typename AfterKeys>
 __device__ __forceinline__ uint32_t topk_from_groups(const uint32_t* gk, int gcap, const float* bs, int64_t ld,
                                                      int nb, const uint32_t* pk, int K, const PoolTopkOut& o,
-                                                     PoolTopkLds<BPT>& L, int32_t* s_grp, AfterKeys&& after_keys) {
+                                                     PoolTopkLds<BPT>& L, int32_t* s_grp, uint32_t* s_bits,
+                                                     AfterKeys&& after_keys) {
   static_assert(BPT >= 1 && BPT <= 4, "16 BPT block flags per thread in 64 bits");
   constexpr uint32_t kCap = kTkThreads * BPT;
   const int tid = threadIdx.x;
   const int ng = (nb + kGroupBlocks - 1) / kGroupBlocks;
   uint32_t key[kGroupPer];
-  load_group_keys(gk, ng, gcap, key);
+  load_group_keys_c(gk, ng, gcap, key);
   after_keys();
+  if (tid < kMaxGroups / 32) s_bits[tid] = 0u;           // (ordered by the bound's barriers)
   const TopkBound bd = K <= kTkThreads ? radix_bound_top<kGroupPer>(key, K, L.radix)
                                        : radix_bound<kGroupPer>(key, K, L.radix);
   const uint32_t lb = ng >= K ? bd.lb : 1u;               // too few groups: every block
-  uint32_t gflags = 0;
-#pragma unroll
-  for (int k = 0; k < kGroupPer; ++k) gflags |= (uint32_t)(key[k] >= lb && key[k] != 0u) << k;
   uint32_t ngc;
-  uint32_t gb = block_exclusive_scan<kTkThreads>((uint32_t)__builtin_popcount(gflags), L.scan, &ngc);
+  block_exclusive_scan<kTkThreads>(mark_groups(key, lb, s_bits), L.scan, &ngc);   // (completes the marks)
   if (ngc <= kCap) {
-    while (gflags) {
-      const int k = __builtin_ctz(gflags);
-      gflags &= gflags - 1;
-      s_grp[gb++] = tid * kGroupPer + k;                  // ascending group ids
-    }
+    compact_groups(s_bits, s_grp, L.scan);                // ascending group ids
     __syncthreads();
     // thread t: candidate groups [BPT t, BPT (t + 1)), every load issued first
     int gid[BPT];
@@ -262,7 +291,6 @@ __device__ __forceinline__ uint32_t topk_from_blocks(const float* bs, int ld, in
   after_keys();
   s_bits[tid] = 0u;                                  // (ordered by the bound's barriers)
   const TopkBound bd = K <= kTkThreads ? radix_bound_top<kPer>(key, K, L.radix) : radix_bound<kPer>(key, K, L.radix);
-  uint32_t nmine = 0;
 #pragma unroll
   for (int v = 0; v < NV; ++v) {
 #pragma unroll
@@ -270,17 +298,16 @@ __device__ __forceinline__ uint32_t topk_from_blocks(const float* bs, int ld, in
       if (key[4 * v + e] >= bd.lb) {
         const int b = 4 * (kTkThreads * v + tid) + e;
         atomicOr(&s_bits[b >> 5], 1u << (b & 31));
-        ++nmine;
       }
     }
   }
-  uint32_t ncand;
-  block_exclusive_scan<kTkThreads>(nmine, L.scan, &ncand);   // (its barriers complete the marks)
+  __syncthreads();
+  // thread t: the bitmap word of blocks [32 t, 32 t + 32), compacted in
+  // ascending order (only while within the room; the total decides)
+  uint32_t w = s_bits[tid];
   uint32_t nsel;
-  if (ncand <= kCap) {
-    // thread t: the bitmap word of blocks [32 t, 32 t + 32)
-    uint32_t w = s_bits[tid];
-    uint32_t cb = block_exclusive_scan<kTkThreads>((uint32_t)__builtin_popcount(w), L.scan, &nsel);
+  uint32_t cb = block_exclusive_scan<kTkThreads>((uint32_t)__builtin_popcount(w), L.scan, &nsel);
+  if (nsel <= kCap) {
     while (w) {
       const int k = __builtin_ctz(w);
       w &= w - 1;
@@ -302,6 +329,7 @@ __device__ __forceinline__ uint32_t topk_from_blocks(const float* bs, int ld, in
 struct PoolGroupLds {
   RadixLds radix;
   uint32_t scan[kTkWaves];
+  uint32_t bits[kMaxGroups / 32];
   int32_t grp[kPoolGroupCap];
   uint32_t ckey[kPoolCandCap];
   int32_t cblk[kPoolCandCap];
@@ -319,22 +347,16 @@ __device__ __forceinline__ uint32_t pool_from_groups(const uint32_t* gk, int gca
   const int tid = threadIdx.x;
   const int ng = (nb + kGroupBlocks - 1) / kGroupBlocks;
   uint32_t key[kGroupPer];
-  load_group_keys(gk, ng, gcap, key);
+  load_group_keys_c(gk, ng, gcap, key);
+  if (tid < kMaxGroups / 32) L.bits[tid] = 0u;          // (ordered by the bound's barriers)
   const TopkBound bd = radix_bound<kGroupPer>(key, P, L.radix);
   const uint32_t lb = ng >= P ? bd.lb : 1u;
-  uint32_t gflags = 0;
-#pragma unroll
-  for (int k = 0; k < kGroupPer; ++k) gflags |= (uint32_t)(key[k] >= lb && key[k] != 0u) << k;
   uint32_t ngc;
-  uint32_t gb = block_exclusive_scan<kTkThreads>((uint32_t)__builtin_popcount(gflags), L.scan, &ngc);
+  block_exclusive_scan<kTkThreads>(mark_groups(key, lb, L.bits), L.scan, &ngc);   // (completes the marks)
   uint32_t ncand = 0;
   bool fast = ngc <= (uint32_t)kPoolGroupCap;
   if (fast) {
-    while (gflags) {
-      const int k = __builtin_ctz(gflags);
-      gflags &= gflags - 1;
-      L.grp[gb++] = tid * kGroupPer + k;                  // ascending group ids
-    }
+    compact_groups(L.bits, L.grp, L.scan);               // ascending group ids
     __syncthreads();
 #pragma unroll 1
     for (int r0 = 0; r0 < (int)ngc; r0 += kPoolGpt * kTkThreads) {
