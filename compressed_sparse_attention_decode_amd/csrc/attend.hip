@@ -96,6 +96,7 @@ constexpr int kOffGrp = kOffQ + kAttendHeads * kQS;
 constexpr int kOffGrpBits = kOffGrp + 4 * 4 * kTkThreads;   // their bitmap
 static_assert(kOffGrp % 16 == 0 && kOffGrpBits + 4 * kMaxGroups / 32 <= kTE * kLS * 2,
               "candidate groups and their bitmap fit in the image");
+static_assert(kOffGrp + 4 * kMaxCand <= kOffRow, "a Reindex selection's staged keys fit before the row codes");
 static_assert(sizeof(PoolGroupLds) <= kLdsBytes, "a pool selection fits the workgroup's LDS");
 static_assert(kMaxGroups == kPoolGroupsMax, "the host's bound of the group keys");
 static_assert(kTE * 8 == kNT, "one rope chunk per thread");
@@ -351,7 +352,8 @@ __global__ __launch_bounds__(kNT) void k_attend(AttendArgs a) {
       uint32_t kept;
       if constexpr (SRC == kSrcReindex)
         kept = topk_from_keys(a.rkeys + (int64_t)q * a.pool * kBlock, a.pool_blocks + (int64_t)q * a.pool,
-                              min(pcount, a.pool), a.pool, K, o, sl.radix, sl.scan, load_q_sel);
+                              min(pcount, a.pool), a.pool, K, o, sl.radix, sl.scan,
+                              reinterpret_cast<uint32_t*>(s_mem + kOffGrp), load_q_sel);
       else if constexpr (SRC == kSrcPool)
         kept = topk_from_pool<SEL>(a.pool_blocks + (int64_t)q * a.pool, min(pcount, a.pool), a.pool,
                                    a.bscore + (int64_t)q * a.ld_bs, a.pkey + (int64_t)q * a.ld_pkey, K, o, nullptr,

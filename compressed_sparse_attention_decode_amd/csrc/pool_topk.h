@@ -213,22 +213,39 @@ __device__ __forceinline__ uint32_t topk_from_pool(const int32_t* pool, int pcnt
 // same selection as k_reindex's last workgroup.  Called by all kTkThreads
 // threads; ks: the query's 8 P keys; pool: its P block ids, pcnt valid.
 // o.pool / o.pool_count are not written.  Returns the Top-K count.
+// s_stage: LDS for the 8 P keys (<= kMaxCand words): they are read with
+// 16-byte loads that cover whole lines (thread t takes chunks 512 v + t) into
+// 128-byte rows whose chunks are XOR-swizzled by the row, then each thread
+// reads its own 32 consecutive keys back (slot order stays position order).
 template <typename AfterKeys>
 __device__ __forceinline__ uint32_t topk_from_keys(const uint32_t* ks, const int32_t* pool, int pcnt, int P, int K,
                                                    const PoolTopkOut& o, RadixLds& L, uint32_t* s_scan,
-                                                   AfterKeys&& after_keys) {
+                                                   uint32_t* s_stage, AfterKeys&& after_keys) {
   constexpr int kBP = kPer / kBlock;                // pool blocks per thread
+  static_assert(kPer == 32, "a thread's keys are one 128-byte row of the staging");
   const int tid = threadIdx.x;
   int32_t blk[kBP];
 #pragma unroll
   for (int j = 0; j < kBP; ++j) blk[j] = pool[min(tid * kBP + j, P - 1)];
   const int s0 = tid * kPer;
   const bool mine = s0 < P * kBlock;
+  {
+    v4u x[kPer / 4];
+#pragma unroll
+    for (int v = 0; v < kPer / 4; ++v)
+      x[v] = *reinterpret_cast<const v4u*>(ks + min(4 * (kTkThreads * v + tid), P * kBlock - 4));
+#pragma unroll
+    for (int v = 0; v < kPer / 4; ++v) {
+      const int i = kTkThreads * v + tid, r = i >> 3, c = i & 7;   // row r, chunk c
+      *reinterpret_cast<v4u*>(s_stage + r * kPer + ((c ^ (r & 7)) << 2)) = x[v];
+    }
+  }
+  __syncthreads();
   uint32_t key[kPer];
 #pragma unroll
-  for (int v = 0; v < kPer / 4; ++v) {
-    const v4u x = *reinterpret_cast<const v4u*>(ks + min(s0 + v * 4, P * kBlock - 4));
-    key[4 * v] = x[0]; key[4 * v + 1] = x[1]; key[4 * v + 2] = x[2]; key[4 * v + 3] = x[3];
+  for (int c = 0; c < kPer / 4; ++c) {
+    const v4u x = *reinterpret_cast<const v4u*>(s_stage + tid * kPer + ((c ^ (tid & 7)) << 2));
+    key[4 * c] = x[0]; key[4 * c + 1] = x[1]; key[4 * c + 2] = x[2]; key[4 * c + 3] = x[3];
   }
   const int nh = mine ? pcnt * kBlock - s0 : 0;    // slots of this thread inside the pool count
 #pragma unroll
