@@ -652,29 +652,32 @@ __global__ __launch_bounds__(kNT) void k_attend(AttendArgs a) {
 // lse = M + log2(sum_s 2^(m_s - M) l_s) (in the exp2 domain, then as a
 // natural log).  A thread owns four dims of one head and issues every
 // split's loads before the first use: one round trip.
+// SM: a bound of the split count (2, 4, 8 or 16), so that only the splits
+// that exist are loaded.
 constexpr int kCombineThreads = 256;     // two heads x 128 threads of 4 dims
+template <int SM>
 __global__ __launch_bounds__(kCombineThreads) void k_attend_combine(AttendArgs a) {
   const int S = a.splits, H = a.heads, HP = a.head_groups * kAttendHeads;
   const int q = blockIdx.x / (HP / 2);
   const int h = (blockIdx.x % (HP / 2)) * 2 + (threadIdx.x >> 7);
   const int d = (threadIdx.x & 127) * 4;
   if (h >= H) return;
-  v2f ml[kAttendMaxSplits];
-  v4f os[kAttendMaxSplits];
+  v2f ml[SM];
+  v4f os[SM];
 #pragma unroll
-  for (int s = 0; s < kAttendMaxSplits; ++s) {
+  for (int s = 0; s < SM; ++s) {
     const int64_t r = ((int64_t)q * S + min(s, S - 1)) * HP + h;
     ml[s] = *reinterpret_cast<const v2f*>(a.part_ml + r * 2);
     os[s] = *reinterpret_cast<const v4f*>(a.part_o + r * kLatent + d);
   }
   float M = -__builtin_inff();
 #pragma unroll
-  for (int s = 0; s < kAttendMaxSplits; ++s)
+  for (int s = 0; s < SM; ++s)
     if (s < S && ml[s][1] > 0.0f) M = fmaxf(M, ml[s][0]);
   float den = 0.0f;
   v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-  for (int s = 0; s < kAttendMaxSplits; ++s) {
+  for (int s = 0; s < SM; ++s) {
     const float w = s < S && ml[s][1] > 0.0f ? exp2f(ml[s][0] - M) : 0.0f;
     den += w * ml[s][1];
 #pragma unroll
@@ -735,8 +738,11 @@ hipError_t launch_attend(const AttendArgs& a, hipStream_t s) {
   if (a.splits > 1) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_attend_combine, dim3((unsigned)(a.n_q * a.head_groups * kAttendHeads / 2)),
-                       dim3(kCombineThreads), 0, s, a);
+    const dim3 cg((unsigned)(a.n_q * a.head_groups * kAttendHeads / 2));
+    if (a.splits <= 2) hipLaunchKernelGGL(k_attend_combine<2>, cg, dim3(kCombineThreads), 0, s, a);
+    else if (a.splits <= 4) hipLaunchKernelGGL(k_attend_combine<4>, cg, dim3(kCombineThreads), 0, s, a);
+    else if (a.splits <= 8) hipLaunchKernelGGL(k_attend_combine<8>, cg, dim3(kCombineThreads), 0, s, a);
+    else hipLaunchKernelGGL(k_attend_combine<kAttendMaxSplits>, cg, dim3(kCombineThreads), 0, s, a);
   }
   return hipGetLastError();
 }
