@@ -652,8 +652,8 @@ __global__ __launch_bounds__(kNT) void k_attend(AttendArgs a) {
 // lse = M + log2(sum_s 2^(m_s - M) l_s) (in the exp2 domain, then as a
 // natural log).  A thread owns four dims of one head and issues every
 // split's loads before the first use: one round trip.
-// SM: a bound of the split count (2, 4, 8 or 16), so that only the splits
-// that exist are loaded.
+// SM: a bound of the split count (2, 4, 8, 10, 12 or 16), so that only the
+// splits that exist are loaded.
 constexpr int kCombineThreads = 256;     // two heads x 128 threads of 4 dims
 template <int SM>
 __global__ __launch_bounds__(kCombineThreads) void k_attend_combine(AttendArgs a) {
@@ -742,6 +742,8 @@ hipError_t launch_attend(const AttendArgs& a, hipStream_t s) {
     if (a.splits <= 2) hipLaunchKernelGGL(k_attend_combine<2>, cg, dim3(kCombineThreads), 0, s, a);
     else if (a.splits <= 4) hipLaunchKernelGGL(k_attend_combine<4>, cg, dim3(kCombineThreads), 0, s, a);
     else if (a.splits <= 8) hipLaunchKernelGGL(k_attend_combine<8>, cg, dim3(kCombineThreads), 0, s, a);
+    else if (a.splits <= 10) hipLaunchKernelGGL(k_attend_combine<10>, cg, dim3(kCombineThreads), 0, s, a);
+    else if (a.splits <= 12) hipLaunchKernelGGL(k_attend_combine<12>, cg, dim3(kCombineThreads), 0, s, a);
     else hipLaunchKernelGGL(k_attend_combine<kAttendMaxSplits>, cg, dim3(kCombineThreads), 0, s, a);
   }
   return hipGetLastError();
