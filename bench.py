@@ -204,9 +204,8 @@ class Step:
         self.full_topk = not w.fresh_q_per_layer
         self.pk = torch.empty(n_q, csa2.pos_keys_ld(st.dims, st.batch), dtype=torch.int32, device=dev) \
             if self.full_topk else None
-        # unpaged planes: the Top-K (and a small pool) is selected inside the
-        # attention kernel
-        self.fused = self.full_topk and st.pages is None
+        # the pool and the Top-K are selected inside the attention kernel
+        self.fused = self.full_topk
         for layer in [0] + self.layers:
             st.iq(layer)
             st.mq(layer)
@@ -233,45 +232,26 @@ class Step:
             seq.append(("scan", csa2.index_scan(st.dims, st.batch, q0, w0, idx_k, self.bs, pool_ws=self.ws_p,
                                                 prepare=True, pages=st.pages, pos_keys=self.pk)))
             if self.fused:
-                # the pool, the Full layer's Top-K and the attention, the
-                # Top-K (and a pool of up to 16,384 blocks) selected inside
-                # the attention kernel: csa2_decode_step's Full chain
+                # the pool, the Full layer's Top-K and the attention, both
+                # selected inside the attention kernel: csa2_decode_step's
+                # Full chain
                 ql, qr = st.mq(0)
                 seq.append(("pool_topk_attend", csa2.pool_topk_attend(
                     st.dims, st.batch, self.bs, self.pk, ql, qr, 1.0, codes, scales, kv_rope, swa_kv, st.swa_base,
                     self.pool, self.pcnt, self.tk[0], self.tc[0], out=self.out[0], lse=self.lse[0], ws=self.ws_a,
-                    pool_ws=self.ws_p, from_scan=True, prepare=True)))
-            elif self.full_topk:
-                # the pool and the Full layer's Top-K from the scan's keys
-                # (one kernel for pools of up to 16,384 blocks)
-                seq.append(("pool_topk", csa2.index_pool_topk(st.dims, st.batch, self.bs, self.pk, self.pool,
-                                                              self.pcnt, self.tk[0], self.tc[0], ws=self.ws_p,
-                                                              from_scan=True, prepare=True)))
+                    pool_ws=self.ws_p, from_scan=True, prepare=True, pages=st.pages)))
             else:
                 seq.append(("pool", csa2.index_pool(st.dims, st.batch, self.bs, self.pool, self.pcnt, ws=self.ws_p,
                                                     from_scan=True, prepare=True)))
-            if self.full_topk and not self.fused:
-                ql, qr = st.mq(0)
-                seq.append(("attend", csa2.attend(st.dims, st.batch, ql, qr, 1.0, codes, scales, kv_rope,
-                                                  self.tk[0], self.tc[0], swa_kv, st.swa_base, out=self.out[0],
-                                                  lse=self.lse[0], ws=self.ws_a, prepare=True, pages=st.pages)))
             for i, layer in enumerate(self.layers if not self.full_topk else []):
                 q, wt = st.iq(layer)
                 ql, qr = st.mq(layer)
-                if st.pages is None:
-                    # the Reindex keys, the Top-K selected inside the
-                    # attention kernel: csa2_decode_step's Reindex chain
-                    seq.append(("reindex_attend", csa2.reindex_attend(
-                        st.dims, st.batch, q, wt, idx_k, self.pool, self.pcnt, ql, qr, 1.0, codes, scales, kv_rope,
-                        swa_kv, st.swa_base, self.tk[i], self.tc[i], out=self.out[i], lse=self.lse[i],
-                        reindex_ws=self.ws_r, ws=self.ws_a, prepare=True)))
-                    continue
-                seq.append(("reindex", csa2.index_reindex(st.dims, st.batch, q, wt, idx_k, self.pool, self.pcnt,
-                                                          topk_pos=self.tk[i], topk_count=self.tc[i],
-                                                          ws=self.ws_r, prepare=True, pages=st.pages)))
-                seq.append(("attend", csa2.attend(st.dims, st.batch, ql, qr, 1.0, codes, scales, kv_rope,
-                                                  self.tk[i], self.tc[i], swa_kv, st.swa_base, out=self.out[i],
-                                                  lse=self.lse[i], ws=self.ws_a, prepare=True, pages=st.pages)))
+                # the Reindex keys, the Top-K selected inside the attention
+                # kernel: csa2_decode_step's Reindex chain
+                seq.append(("reindex_attend", csa2.reindex_attend(
+                    st.dims, st.batch, q, wt, idx_k, self.pool, self.pcnt, ql, qr, 1.0, codes, scales, kv_rope,
+                    swa_kv, st.swa_base, self.tk[i], self.tc[i], out=self.out[i], lse=self.lse[i],
+                    reindex_ws=self.ws_r, ws=self.ws_a, prepare=True, pages=st.pages)))
             self.calls.append(seq)
 
     def run(self, r: int):

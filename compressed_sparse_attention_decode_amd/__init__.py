@@ -105,6 +105,10 @@ def lib() -> ctypes.CDLL:
                                             P, P, P, P, P, SZ, I32, P, SZ, P]),
             "csa2_reindex_attend": (I32, [PD, PQ, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_float, P, P, P, P, P,
                                           P, P, P, SZ, P, SZ, P]),
+            "csa2_pool_topk_attend_paged": (I32, [PD, PQ, PP, P, I64, P, I64, P, P, P, P, P, P, ctypes.c_float, P,
+                                                  P, P, P, P, P, P, P, SZ, I32, P, SZ, P]),
+            "csa2_reindex_attend_paged": (I32, [PD, PQ, PP, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_float, P, P,
+                                                P, P, P, P, P, P, SZ, P, SZ, P]),
             "csa2_decode_step_noalloc": (I32, [PD, PQ, I32, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_float,
                                                P, P, P, P, P, P, P, P]),
         }
@@ -617,13 +621,13 @@ def pool_topk_attend(dims: Dims, b: Batch, block_scores: torch.Tensor, pos_keys:
                      topk_pos: Optional[torch.Tensor] = None, topk_count: Optional[torch.Tensor] = None,
                      out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
                      ws: Optional[torch.Tensor] = None, pool_ws: Optional[torch.Tensor] = None,
-                     from_scan: bool = False, want_lse: bool = True, prepare: bool = False):
-    """The pool, the Full layer's Top-K and the attention on it, the Top-K
-    (and, for queries of at most 16,384 blocks, the pool) selected inside the
-    attention kernel (csa2_pool_topk_attend).  `pool_ws`, `from_scan` as
-    index_pool's `ws`, `from_scan` (used by the chunked pool kernels of
-    longer queries).  Returns (pool_blocks, pool_count, topk_pos,
-    topk_count, out, lse)."""
+                     from_scan: bool = False, want_lse: bool = True, prepare: bool = False,
+                     pages: Optional[Pages] = None):
+    """The pool, the Full layer's Top-K and the attention on it, selected
+    inside the attention kernel (csa2_pool_topk_attend; with `pages`,
+    csa2_pool_topk_attend_paged).  `pool_ws`, `from_scan` as index_pool's
+    `ws`, `from_scan` (read by the selection of queries past 16,384 blocks).
+    Returns (pool_blocks, pool_count, topk_pos, topk_count, out, lse)."""
     dev = q_lat.device
     _dev(block_scores, pos_keys, q_lat, q_rope, kv_codes, kv_scales, kv_rope, swa_kv, swa_base, pool_blocks,
          pool_count, topk_pos, topk_count, out, lse)
@@ -667,7 +671,14 @@ def pool_topk_attend(dims: Dims, b: Batch, block_scores: torch.Tensor, pos_keys:
             topk_count.data_ptr(), q_lat.data_ptr(), q_rope.data_ptr(), float(softmax_scale), kv_codes.data_ptr(),
             kv_scales.data_ptr(), kv_rope.data_ptr(), swa_kv.data_ptr(), swa_base.data_ptr(), out.data_ptr(),
             _ptr(lse), pp, pn, POOL_WS_FROM_SCAN if from_scan else 0, wp, wn, _stream(dev))
-    call = _issue(lib().csa2_pool_topk_attend, args, (d, q, ws, pool_ws), prepare)
+    if pages is not None:
+        if pages.rows > min(kv_codes.shape[0], kv_scales.shape[0], kv_rope.shape[0]):
+            raise ValueError(f"pages.rows ({pages.rows}) exceeds the main-KV planes' rows")
+        pg = pages.c()
+        call = _issue(lib().csa2_pool_topk_attend_paged, args[:2] + (ctypes.byref(pg),) + args[2:],
+                      (d, q, pg, ws, pool_ws, pages.table), prepare)
+    else:
+        call = _issue(lib().csa2_pool_topk_attend, args, (d, q, ws, pool_ws), prepare)
     return call if prepare else (pool_blocks, pool_count, topk_pos, topk_count, out, lse)
 
 
@@ -679,11 +690,11 @@ def reindex_attend(dims: Dims, b: Batch, idx_q, idx_w: torch.Tensor, idx_k,
                    topk_pos: Optional[torch.Tensor] = None, topk_count: Optional[torch.Tensor] = None,
                    out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
                    reindex_ws: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None,
-                   want_lse: bool = True, prepare: bool = False):
+                   want_lse: bool = True, prepare: bool = False, pages: Optional[Pages] = None):
     """A Reindex layer with the Top-K selected inside the attention kernel
-    (csa2_reindex_attend).  idx_q / idx_k as in index_reindex (a
-    (codes, scales) pair each for FP4 rows).  Returns (topk_pos, topk_count,
-    out, lse)."""
+    (csa2_reindex_attend; with `pages`, csa2_reindex_attend_paged).  idx_q /
+    idx_k as in index_reindex (a (codes, scales) pair each for FP4 rows).
+    Returns (topk_pos, topk_count, out, lse)."""
     dev = q_lat.device
     _dev(pool_blocks, pool_count, q_lat, q_rope, kv_codes, kv_scales, kv_rope, swa_kv, swa_base, topk_pos,
          topk_count, out, lse)
@@ -718,7 +729,14 @@ def reindex_attend(dims: Dims, b: Batch, idx_q, idx_w: torch.Tensor, idx_k,
             q_lat.data_ptr(), q_rope.data_ptr(), float(softmax_scale), kv_codes.data_ptr(), kv_scales.data_ptr(),
             kv_rope.data_ptr(), swa_kv.data_ptr(), swa_base.data_ptr(), out.data_ptr(), _ptr(lse), rp, rn, wp, wn,
             _stream(dev))
-    call = _issue(lib().csa2_reindex_attend, args, (d, q, ws, reindex_ws), prepare)
+    if pages is not None:
+        if pages.rows > min(kv_codes.shape[0], kv_scales.shape[0], kv_rope.shape[0]):
+            raise ValueError(f"pages.rows ({pages.rows}) exceeds the main-KV planes' rows")
+        pg = pages.c()
+        call = _issue(lib().csa2_reindex_attend_paged, args[:2] + (ctypes.byref(pg),) + args[2:],
+                      (d, q, pg, ws, reindex_ws, pages.table), prepare)
+    else:
+        call = _issue(lib().csa2_reindex_attend, args, (d, q, ws, reindex_ws), prepare)
     return call if prepare else (topk_pos, topk_count, out, lse)
 
 

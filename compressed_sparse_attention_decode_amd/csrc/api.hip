@@ -788,10 +788,8 @@ static csa2_status attend(const csa2_dims* d, const csa2_queries* q, const uint1
   if ((st = check_queries(q))) return st;
   if (pages && (st = check_pages(pages, 256))) return st;   // kv_codes: the widest plane
   if (sel && sel->rkeys) {
-    if (pages) return fail(CSA2_ERR_UNSUPPORTED, "the in-kernel selection takes unpaged planes");
     if (!sel->pool_blocks || !sel->pool_count) return fail(CSA2_ERR_INVALID_ARG, "required pointer is NULL");
   } else if (sel) {
-    if (pages) return fail(CSA2_ERR_UNSUPPORTED, "the in-kernel selection takes unpaged planes");
     if (!sel->from_pool && !sel->gkeys && !pool_small(d, q))
       return fail(CSA2_ERR_UNSUPPORTED, "the in-kernel selection takes at most %d blocks per query (max_visible %lld)",
                   kPoolSmallBlocks, (long long)q->max_visible);
@@ -882,7 +880,7 @@ static csa2_status pool_topk_attend(const csa2_dims* d, const csa2_queries* q, c
                                     const uint8_t* kv_codes, const uint8_t* kv_scales, const uint16_t* kv_rope,
                                     const uint16_t* swa_kv, const int64_t* swa_base, float* out, float* lse,
                                     void* pool_wsp, size_t pool_ws_bytes, int32_t flags, void* ws, size_t ws_bytes,
-                                    void* stream, bool dry = false) {
+                                    void* stream, bool dry = false, const csa2_pages* pages = nullptr) {
   csa2_status st = check_dims(d);
   if (st) return st;
   if ((st = check_queries(q))) return st;
@@ -916,7 +914,7 @@ static csa2_status pool_topk_attend(const csa2_dims* d, const csa2_queries* q, c
   }
   // every argument is checked before the first launch
   if ((st = attend(d, q, q_lat, q_rope, softmax_scale, kv_codes, kv_scales, kv_rope, topk_pos, topk_count, swa_kv,
-                   swa_base, out, lse, ws, ws_bytes, stream, true, nullptr, apart ? nullptr : &sel)))
+                   swa_base, out, lse, ws, ws_bytes, stream, true, pages, apart ? nullptr : &sel)))
     return st;
   if (dry) return CSA2_OK;
   if (!small && !groups && (st = run_pool(d, q, block_scores, ld_block_scores, pool_blocks, pool_count, pool_wsp,
@@ -924,7 +922,7 @@ static csa2_status pool_topk_attend(const csa2_dims* d, const csa2_queries* q, c
                                apart ? topk_pos : nullptr, apart ? topk_count : nullptr)))
     return st;
   return attend(d, q, q_lat, q_rope, softmax_scale, kv_codes, kv_scales, kv_rope, topk_pos, topk_count, swa_kv,
-                swa_base, out, lse, ws, ws_bytes, stream, false, nullptr, apart ? nullptr : &sel);
+                swa_base, out, lse, ws, ws_bytes, stream, false, pages, apart ? nullptr : &sel);
 }
 
 csa2_status csa2_pool_topk_attend(const csa2_dims* d, const csa2_queries* q, const float* block_scores,
@@ -940,6 +938,21 @@ csa2_status csa2_pool_topk_attend(const csa2_dims* d, const csa2_queries* q, con
                           swa_base, out, lse, pool_ws, pool_ws_bytes, flags, ws, ws_bytes, stream);
 }
 
+csa2_status csa2_pool_topk_attend_paged(const csa2_dims* d, const csa2_queries* q, const csa2_pages* pages,
+                                        const float* block_scores, int64_t ld_block_scores, const uint32_t* pos_keys,
+                                        int64_t ld_pos_keys, int32_t* pool_blocks, int32_t* pool_count,
+                                        int32_t* topk_pos, int32_t* topk_count, const uint16_t* q_lat,
+                                        const uint16_t* q_rope, float softmax_scale, const uint8_t* kv_codes,
+                                        const uint8_t* kv_scales, const uint16_t* kv_rope, const uint16_t* swa_kv,
+                                        const int64_t* swa_base, float* out, float* lse, void* pool_ws,
+                                        size_t pool_ws_bytes, int32_t flags, void* ws, size_t ws_bytes,
+                                        void* stream) {
+  if (!pages) return fail(CSA2_ERR_INVALID_ARG, "pages is NULL");
+  return pool_topk_attend(d, q, block_scores, ld_block_scores, pos_keys, ld_pos_keys, pool_blocks, pool_count,
+                          topk_pos, topk_count, q_lat, q_rope, softmax_scale, kv_codes, kv_scales, kv_rope, swa_kv,
+                          swa_base, out, lse, pool_ws, pool_ws_bytes, flags, ws, ws_bytes, stream, false, pages);
+}
+
 // A Reindex layer: the scoring kernel writes the order keys only, and the
 // attention workgroups select the Top-K from them.
 static csa2_status reindex_attend(const csa2_dims* d, const csa2_queries* q, const uint8_t* idx_q,
@@ -950,13 +963,13 @@ static csa2_status reindex_attend(const csa2_dims* d, const csa2_queries* q, con
                                   const uint8_t* kv_scales, const uint16_t* kv_rope, const uint16_t* swa_kv,
                                   const int64_t* swa_base, float* out, float* lse, void* reindex_wsp,
                                   size_t reindex_ws_bytes, void* ws, size_t ws_bytes, void* stream, bool dry = false,
-                                  uint32_t* counters = nullptr) {
+                                  uint32_t* counters = nullptr, const csa2_pages* pages = nullptr) {
   if ((idx_q_scales == nullptr) != (idx_k_scales == nullptr))
     return fail(CSA2_ERR_INVALID_ARG, "idx_q_scales and idx_k_scales must both be given (FP4 rows) or both NULL");
   const bool fp4 = idx_q_scales != nullptr;
   csa2_status st;
   if ((st = index_reindex(d, q, idx_q, idx_q_scales, idx_w, idx_k, idx_k_scales, fp4, pool_blocks, pool_count,
-                          topk_pos, topk_count, nullptr, reindex_wsp, reindex_ws_bytes, stream, true, nullptr,
+                          topk_pos, topk_count, nullptr, reindex_wsp, reindex_ws_bytes, stream, true, pages,
                           counters, true)))
     return st;
   // the keys sit after the completion counters (or at the start, with
@@ -966,15 +979,15 @@ static csa2_status reindex_attend(const csa2_dims* d, const csa2_queries* q, con
   const AttendSel sel{nullptr, 0, nullptr, 0, const_cast<int32_t*>(pool_blocks), const_cast<int32_t*>(pool_count),
                       true, rkeys};
   if ((st = attend(d, q, q_lat, q_rope, softmax_scale, kv_codes, kv_scales, kv_rope, topk_pos, topk_count, swa_kv,
-                   swa_base, out, lse, ws, ws_bytes, stream, true, nullptr, &sel)))
+                   swa_base, out, lse, ws, ws_bytes, stream, true, pages, &sel)))
     return st;
   if (dry) return CSA2_OK;
   if ((st = index_reindex(d, q, idx_q, idx_q_scales, idx_w, idx_k, idx_k_scales, fp4, pool_blocks, pool_count,
-                          topk_pos, topk_count, nullptr, reindex_wsp, reindex_ws_bytes, stream, false, nullptr,
+                          topk_pos, topk_count, nullptr, reindex_wsp, reindex_ws_bytes, stream, false, pages,
                           counters, true)))
     return st;
   return attend(d, q, q_lat, q_rope, softmax_scale, kv_codes, kv_scales, kv_rope, topk_pos, topk_count, swa_kv,
-                swa_base, out, lse, ws, ws_bytes, stream, false, nullptr, &sel);
+                swa_base, out, lse, ws, ws_bytes, stream, false, pages, &sel);
 }
 
 csa2_status csa2_reindex_attend(const csa2_dims* d, const csa2_queries* q, const uint8_t* idx_q,
@@ -988,6 +1001,21 @@ csa2_status csa2_reindex_attend(const csa2_dims* d, const csa2_queries* q, const
   return reindex_attend(d, q, idx_q, idx_q_scales, idx_w, idx_k, idx_k_scales, pool_blocks, pool_count, topk_pos,
                         topk_count, q_lat, q_rope, softmax_scale, kv_codes, kv_scales, kv_rope, swa_kv, swa_base, out,
                         lse, reindex_ws, reindex_ws_bytes, ws, ws_bytes, stream);
+}
+
+csa2_status csa2_reindex_attend_paged(const csa2_dims* d, const csa2_queries* q, const csa2_pages* pages,
+                                      const uint8_t* idx_q, const uint8_t* idx_q_scales, const float* idx_w,
+                                      const uint8_t* idx_k, const uint8_t* idx_k_scales, const int32_t* pool_blocks,
+                                      const int32_t* pool_count, int32_t* topk_pos, int32_t* topk_count,
+                                      const uint16_t* q_lat, const uint16_t* q_rope, float softmax_scale,
+                                      const uint8_t* kv_codes, const uint8_t* kv_scales, const uint16_t* kv_rope,
+                                      const uint16_t* swa_kv, const int64_t* swa_base, float* out, float* lse,
+                                      void* reindex_ws, size_t reindex_ws_bytes, void* ws, size_t ws_bytes,
+                                      void* stream) {
+  if (!pages) return fail(CSA2_ERR_INVALID_ARG, "pages is NULL");
+  return reindex_attend(d, q, idx_q, idx_q_scales, idx_w, idx_k, idx_k_scales, pool_blocks, pool_count, topk_pos,
+                        topk_count, q_lat, q_rope, softmax_scale, kv_codes, kv_scales, kv_rope, swa_kv, swa_base, out,
+                        lse, reindex_ws, reindex_ws_bytes, ws, ws_bytes, stream, false, nullptr, pages);
 }
 
 csa2_status csa2_page_rows(const csa2_pages* pages, int64_t n, const int64_t* table_off, const int32_t* pos,
@@ -1076,42 +1104,34 @@ static csa2_status decode_step(const csa2_dims* d, const csa2_queries* q, int32_
   // every stage's arguments are checked before the first launch
   for (int pass = 0; pass < 2; ++pass) {
     const bool dry = pass == 0;
-    // a Full layer of unpaged planes selects its Top-K (and a small pool)
-    // inside the attention kernel
-    const bool fused = mode == CSA2_LAYER_FULL && !pages;
     if (mode == CSA2_LAYER_FULL) {
-      // the scan also keeps every position's score; the Top-K then comes
-      // from those scores (the layer's own query: what Reindex would compute)
+      // the scan also keeps every position's score; the pool and the Top-K
+      // (the layer's own query: what Reindex would compute) are then
+      // selected inside the attention kernel
       const size_t n_idx = full_ws(d, q);
       uint32_t* pkey = (uint32_t*)(w_full + n_idx);
       if (!topk_pos || !topk_count) return fail(CSA2_ERR_INVALID_ARG, "required pointer is NULL");
       if ((st = index_full(d, q, idx_q, idx_q_scales, idx_w, idx_k, idx_k_scales, fp4, pool_blocks, pool_count,
-                           nullptr, 0, w_full, n_idx, stream, dry, pages, pkey, topk_pos, topk_count, fused)))
+                           nullptr, 0, w_full, n_idx, stream, dry, pages, pkey, topk_pos, topk_count, true)))
         return st;
-      if (fused) {
-        if ((st = pool_topk_attend(d, q, (const float*)(w_full + pool_ws(d, q)), full_ldb(d, q), pkey,
-                                   full_ldpk(d, q), pool_blocks, pool_count, topk_pos, topk_count, q_lat, q_rope,
-                                   softmax_scale, kv_codes, kv_scales, kv_rope, swa_kv, swa_base, out, lse, w_full,
-                                   pool_ws(d, q), CSA2_POOL_WS_FROM_SCAN, attend_ws(d, q) ? w_att : nullptr, n_att,
-                                   stream, dry)))
-          return st;
-        continue;
-      }
-    }
-    if (mode == CSA2_LAYER_REINDEX && !pages) {
-      // unpaged planes: the attention workgroups select the Top-K from the
-      // Reindex keys
-      if ((st = reindex_attend(d, q, idx_q, idx_q_scales, idx_w, idx_k, idx_k_scales, pool_blocks, pool_count,
-                               topk_pos, topk_count, q_lat, q_rope, softmax_scale, kv_codes, kv_scales, kv_rope,
-                               swa_kv, swa_base, out, lse, w_re, n_re, attend_ws(d, q) ? w_att : nullptr, n_att,
-                               stream, dry, counters)))
+      if ((st = pool_topk_attend(d, q, (const float*)(w_full + pool_ws(d, q)), full_ldb(d, q), pkey, full_ldpk(d, q),
+                                 pool_blocks, pool_count, topk_pos, topk_count, q_lat, q_rope, softmax_scale,
+                                 kv_codes, kv_scales, kv_rope, swa_kv, swa_base, out, lse, w_full, pool_ws(d, q),
+                                 CSA2_POOL_WS_FROM_SCAN, attend_ws(d, q) ? w_att : nullptr, n_att, stream, dry,
+                                 pages)))
         return st;
       continue;
     }
-    if (mode == CSA2_LAYER_REINDEX &&
-        (st = index_reindex(d, q, idx_q, idx_q_scales, idx_w, idx_k, idx_k_scales, fp4, pool_blocks, pool_count,
-                            topk_pos, topk_count, nullptr, w_re, n_re, stream, dry, pages, counters)))
-      return st;
+    if (mode == CSA2_LAYER_REINDEX) {
+      // the attention workgroups select the Top-K from the Reindex keys
+      if ((st = reindex_attend(d, q, idx_q, idx_q_scales, idx_w, idx_k, idx_k_scales, pool_blocks, pool_count,
+                               topk_pos, topk_count, q_lat, q_rope, softmax_scale, kv_codes, kv_scales, kv_rope,
+                               swa_kv, swa_base, out, lse, w_re, n_re, attend_ws(d, q) ? w_att : nullptr, n_att,
+                               stream, dry, counters, pages)))
+        return st;
+      continue;
+    }
+    // a Reuse layer: attention on the inherited Top-K
     if ((st = attend(d, q, q_lat, q_rope, softmax_scale, kv_codes, kv_scales, kv_rope, topk_pos, topk_count, swa_kv,
                      swa_base, out, lse, attend_ws(d, q) ? w_att : nullptr, n_att, stream, dry, pages)))
       return st;

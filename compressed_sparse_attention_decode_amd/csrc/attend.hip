@@ -100,6 +100,7 @@ static_assert(kOffGrp + 4 * kMaxCand <= kOffRow, "a Reindex selection's staged k
 static_assert(sizeof(PoolGroupLds) <= kLdsBytes, "a pool selection fits the workgroup's LDS");
 static_assert(kMaxGroups == kPoolGroupsMax, "the host's bound of the group keys");
 static_assert(kTE * 8 == kNT, "one rope chunk per thread");
+static_assert(kRowPer % 2 == 0, "rows resolved per thread in two halves");
 static_assert(kTE * kScaleBytes <= kNW * 256, "a tile's scale block: one 256-byte load per wave");
 static_assert(kAttendHeads * kOS * 4 <= kOffStage, "output rows fit in the image and rope slots");
 static_assert(kLdsBytes <= 160 * 1024, "LDS per workgroup");
@@ -193,7 +194,9 @@ __device__ __forceinline__ float max_rows4(float x) {
 // kSrcScan, and a query longer than one workgroup's registers hold
 // (kMaxCand blocks) selects from the scan's group keys (group_topk.h).
 constexpr int kSrcScan = 0, kSrcPool = 1, kSrcReindex = 2, kSrcGroups = 3;
-template <int SEL, int SRC>
+// PGD (SEL > 0): paged main-KV planes; the selected positions become rows
+// through the page table before the gathers.  (SEL == 0 reads a.pages.)
+template <int SEL, int SRC, bool PGD = false>
 __global__ __launch_bounds__(kNT) void k_attend(AttendArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char s_mem[kLdsBytes];
   _Float16* s_lat = reinterpret_cast<_Float16*>(s_mem + kOffLat);   // [64][kLS]
@@ -295,8 +298,8 @@ __global__ __launch_bounds__(kNT) void k_attend(AttendArgs a) {
   int Es = min(tcount, K);
   // paged main KV: the kept positions become rows of the whole planes (one
   // page id per position, loaded unconditionally from a clamped slot)
-  const bool paged = SEL == 0 && a.pages != nullptr;
-  if (paged && c > 0) {
+  const bool paged = SEL == 0 ? a.pages != nullptr : PGD;
+  if (SEL == 0 && paged && c > 0) {
     int32_t pg[kRowPer];
 #pragma unroll
     for (int j = 0; j < kRowPer; ++j) pg[j] = a.pages[sbase + (min(max(tkv[j], 0), c - 1) >> a.page_shift)];
@@ -371,6 +374,31 @@ __global__ __launch_bounds__(kNT) void k_attend(AttendArgs a) {
         kept = pool_topk_select<SEL>(a.bscore + (int64_t)q * a.ld_bs, (int)a.ld_bs, (c + 7) >> 3, a.pool, K,
                                      a.pkey + (int64_t)q * a.ld_pkey, o, sl, load_q_sel);
       Es = min((int)kept, K);
+      if (PGD && c > 0) {
+        // paged main KV: this split's kept positions (written by the
+        // selection, whose last barrier made them visible) become rows of
+        // the whole planes, one page id each; a half of the thread's rows at
+        // a time with its loads issued together (the second half only for
+        // splits of more than 3 kNT rows: fewer live registers)
+        constexpr int kHalf = kRowPer / 2;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          if (h == 1 && ntl * kTE <= kHalf * kNT) break;
+          int32_t pos[kHalf], pg[kHalf];
+#pragma unroll
+          for (int j = 0; j < kHalf; ++j) {
+            const int idx = tid + (h * kHalf + j) * kNT;
+            pos[j] = idx < ntl * kTE ? s_row[idx] : kNoRow;
+            pg[j] = a.pages[sbase + (min(max(pos[j], 0), c - 1) >> a.page_shift)];
+          }
+#pragma unroll
+          for (int j = 0; j < kHalf; ++j) {
+            const int idx = tid + (h * kHalf + j) * kNT;
+            if (pos[j] >= 0 && pos[j] != kNoRow)
+              s_row[idx] = (int32_t)(((uint32_t)pg[j] << a.page_shift) | ((uint32_t)pos[j] & ((1u << a.page_shift) - 1u)));
+          }
+        }
+      }
       wait_vmcnt<0>();                             // this wave's query rows have landed
     }
   }
@@ -691,6 +719,13 @@ __global__ __launch_bounds__(kCombineThreads) void k_attend_combine(AttendArgs a
     a.lse[(int64_t)q * H + h] = den > 0.0f ? (M + log2f(den)) * 0.69314718055994531f : -__builtin_inff();
 }
 
+// A selecting attention launch: the paged instance when the planes are paged.
+template <int SEL, int SRC>
+void launch_sel(const AttendArgs& a, dim3 grid, hipStream_t s) {
+  if (a.pages) hipLaunchKernelGGL((k_attend<SEL, SRC, true>), grid, dim3(kNT), 0, s, a);
+  else hipLaunchKernelGGL((k_attend<SEL, SRC>), grid, dim3(kNT), 0, s, a);
+}
+
 }  // namespace
 
 hipError_t launch_attend(const AttendArgs& a, hipStream_t s) {
@@ -699,23 +734,23 @@ hipError_t launch_attend(const AttendArgs& a, hipStream_t s) {
     return hipErrorInvalidValue;
   const dim3 grid((unsigned)(a.n_q * a.head_groups * a.splits));
   if (a.rkeys) {
-    if (a.pages || a.pool > 2048 || a.topk > 2048 || !a.pool_blocks || !a.pool_count || !a.topk_out ||
+    if (a.pool > 2048 || a.topk > 2048 || !a.pool_blocks || !a.pool_count || !a.topk_out ||
         !a.topk_count_out)
       return hipErrorInvalidValue;
-    hipLaunchKernelGGL((k_attend<1, kSrcReindex>), grid, dim3(kNT), 0, s, a);
+    launch_sel<1, kSrcReindex>(a, grid, s);
   } else if (!a.bscore) {
     hipLaunchKernelGGL((k_attend<0, kSrcScan>), grid, dim3(kNT), 0, s, a);
   } else {
-    // (without a given pool: a query of at most kMaxCand blocks; pool and
-    // Top-K within 2048, no page table: checked by the caller)
-    if (a.pages || a.pool > 2048 || a.topk > 2048 || !a.pkey || !a.pool_blocks || !a.pool_count || !a.topk_out ||
+    // (without a given pool: a query of at most kMaxCand blocks, or the
+    // group keys; pool and Top-K within 2048: checked by the caller)
+    if (a.pool > 2048 || a.topk > 2048 || !a.pkey || !a.pool_blocks || !a.pool_count || !a.topk_out ||
         !a.topk_count_out)
       return hipErrorInvalidValue;
     if (a.sel_from_pool) {
       // (K <= 1024: the positions step of a larger K does not fit the
       // registers beside the attention's; the caller selects it apart)
-      if (a.topk <= kTkThreads) hipLaunchKernelGGL((k_attend<1, kSrcPool>), grid, dim3(kNT), 0, s, a);
-      else if (a.topk <= 2 * kTkThreads) hipLaunchKernelGGL((k_attend<2, kSrcPool>), grid, dim3(kNT), 0, s, a);
+      if (a.topk <= kTkThreads) launch_sel<1, kSrcPool>(a, grid, s);
+      else if (a.topk <= 2 * kTkThreads) launch_sel<2, kSrcPool>(a, grid, s);
       else return hipErrorInvalidValue;
     } else {
       // plus one pool workgroup per query
@@ -726,12 +761,12 @@ hipError_t launch_attend(const AttendArgs& a, hipStream_t s) {
         if (a.topk > 2 * kTkThreads || 2 * a.pool > kPoolGroupCap || a.gcap < 4 || a.gcap % 4 ||
             a.gcap > kMaxGroups || a.ld_gkey < a.gcap || a.group_min < 0 || a.group_min > kMaxCand)
           return hipErrorInvalidValue;
-        if (a.topk <= kTkThreads) hipLaunchKernelGGL((k_attend<2, kSrcGroups>), gp, dim3(kNT), 0, s, a);
-        else hipLaunchKernelGGL((k_attend<4, kSrcGroups>), gp, dim3(kNT), 0, s, a);
+        if (a.topk <= kTkThreads) launch_sel<2, kSrcGroups>(a, gp, s);
+        else launch_sel<4, kSrcGroups>(a, gp, s);
       } else if (a.topk <= kTkThreads) {
-        hipLaunchKernelGGL((k_attend<2, kSrcScan>), gp, dim3(kNT), 0, s, a);
+        launch_sel<2, kSrcScan>(a, gp, s);
       } else {
-        hipLaunchKernelGGL((k_attend<4, kSrcScan>), gp, dim3(kNT), 0, s, a);
+        launch_sel<4, kSrcScan>(a, gp, s);
       }
     }
   }

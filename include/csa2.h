@@ -506,8 +506,7 @@ csa2_status csa2_attend_paged(const csa2_dims* dims, const csa2_queries* q, cons
  *                            16,384 blocks; NULL and 0 are accepted for
  *                            small pools)
  *   ws, ws_bytes             csa2_attend_workspace_size bytes, as in csa2_attend
- * Errors: CSA2_ERR_UNSUPPORTED for paged planes (call csa2_index_pool_topk
- * and csa2_attend_paged); otherwise as those calls. */
+ * Errors as csa2_index_pool_topk and csa2_attend. */
 csa2_status csa2_pool_topk_attend(const csa2_dims* dims, const csa2_queries* q, const float* block_scores,
                                   int64_t ld_block_scores, const uint32_t* pos_keys, int64_t ld_pos_keys,
                                   int32_t* pool_blocks, int32_t* pool_count, int32_t* topk_pos, int32_t* topk_count,
@@ -516,6 +515,23 @@ csa2_status csa2_pool_topk_attend(const csa2_dims* dims, const csa2_queries* q, 
                                   const uint16_t* swa_kv, const int64_t* swa_base, float* out, float* lse,
                                   void* pool_ws, size_t pool_ws_bytes, int32_t flags,
                                   void* ws, size_t ws_bytes, void* stream);
+
+/* csa2_pool_topk_attend over paged main-KV planes (see csa2_pages; NEXT-3
+ * paged caches): the same selection from the same block scores and position
+ * keys (as csa2_index_scan_keys writes them with pages), after which each
+ * selecting workgroup turns its kept positions into rows of the planes with
+ * one page-id load each before its gathers; pool_blocks, pool_count,
+ * topk_pos and topk_count hold positions, as in the unpaged call.  Same
+ * arguments otherwise; errors as csa2_attend_paged for the pages. */
+csa2_status csa2_pool_topk_attend_paged(const csa2_dims* dims, const csa2_queries* q, const csa2_pages* pages,
+                                        const float* block_scores, int64_t ld_block_scores, const uint32_t* pos_keys,
+                                        int64_t ld_pos_keys, int32_t* pool_blocks, int32_t* pool_count,
+                                        int32_t* topk_pos, int32_t* topk_count, const uint16_t* q_lat,
+                                        const uint16_t* q_rope, float softmax_scale, const uint8_t* kv_codes,
+                                        const uint8_t* kv_scales, const uint16_t* kv_rope, const uint16_t* swa_kv,
+                                        const int64_t* swa_base, float* out, float* lse, void* pool_ws,
+                                        size_t pool_ws_bytes, int32_t flags, void* ws, size_t ws_bytes,
+                                        void* stream);
 
 /* csa2_index_reindex followed by csa2_attend on its Top-K, with the Top-K
  * selected inside the attention kernel: the Reindex kernel only scores the
@@ -533,7 +549,7 @@ csa2_status csa2_pool_topk_attend(const csa2_dims* dims, const csa2_queries* q, 
  *   reindex_ws, reindex_ws_bytes  csa2_index_reindex_workspace_size bytes
  *                                 (its completion counters are not used)
  *   ws, ws_bytes                  csa2_attend_workspace_size bytes
- * Unpaged planes only.  Errors as those two calls. */
+ * Errors as those two calls. */
 csa2_status csa2_reindex_attend(const csa2_dims* dims, const csa2_queries* q, const uint8_t* idx_q,
                                 const uint8_t* idx_q_scales, const float* idx_w, const uint8_t* idx_k,
                                 const uint8_t* idx_k_scales, const int32_t* pool_blocks, const int32_t* pool_count,
@@ -542,6 +558,21 @@ csa2_status csa2_reindex_attend(const csa2_dims* dims, const csa2_queries* q, co
                                 const uint16_t* kv_rope, const uint16_t* swa_kv, const int64_t* swa_base,
                                 float* out, float* lse, void* reindex_ws, size_t reindex_ws_bytes,
                                 void* ws, size_t ws_bytes, void* stream);
+
+/* csa2_reindex_attend over paged planes (see csa2_pages): the Reindex
+ * scoring reads the pool's keys through the page table (as
+ * csa2_index_reindex_paged) and each selecting attention workgroup turns its
+ * kept positions into rows with one page-id load each before its gathers.
+ * Same arguments and outputs (positions) otherwise. */
+csa2_status csa2_reindex_attend_paged(const csa2_dims* dims, const csa2_queries* q, const csa2_pages* pages,
+                                      const uint8_t* idx_q, const uint8_t* idx_q_scales, const float* idx_w,
+                                      const uint8_t* idx_k, const uint8_t* idx_k_scales, const int32_t* pool_blocks,
+                                      const int32_t* pool_count, int32_t* topk_pos, int32_t* topk_count,
+                                      const uint16_t* q_lat, const uint16_t* q_rope, float softmax_scale,
+                                      const uint8_t* kv_codes, const uint8_t* kv_scales, const uint16_t* kv_rope,
+                                      const uint16_t* swa_kv, const int64_t* swa_base, float* out, float* lse,
+                                      void* reindex_ws, size_t reindex_ws_bytes, void* ws, size_t ws_bytes,
+                                      void* stream);
 
 /* Rows of paged positions, so that csa2_encode_kv (through dst_row) appends
  * new entries into their pages:
@@ -559,12 +590,10 @@ csa2_status csa2_page_rows(const csa2_pages* pages, int64_t n, const int64_t* ta
  * only attends over the inherited index set with its own main Q).  The call
  * checks every stage's arguments, then enqueues, on `stream`:
  *   CSA2_LAYER_FULL     csa2_index_scan_keys, then csa2_pool_topk_attend
- *                       (unpaged planes) or csa2_index_pool_topk +
- *                       csa2_attend_paged (pool_blocks, pool_count, and
- *                       topk_pos, topk_count: the same set as
- *                       csa2_index_reindex with the same indexer query);
- *   CSA2_LAYER_REINDEX  csa2_reindex_attend on the given pool (unpaged
- *                       planes), or csa2_index_reindex + csa2_attend_paged;
+ *                       (pool_blocks, pool_count, and topk_pos,
+ *                       topk_count: the same set as csa2_index_reindex
+ *                       with the same indexer query);
+ *   CSA2_LAYER_REINDEX  csa2_reindex_attend on the given pool;
  *   CSA2_LAYER_REUSE    csa2_attend on the given topk_pos / topk_count
  *                       (the idx_* arguments may be NULL).
  * The indexer rows are fp8 when idx_q_scales and idx_k_scales are NULL and
@@ -582,8 +611,9 @@ csa2_status csa2_page_rows(const csa2_pages* pages, int64_t n, const int64_t* ta
 csa2_status csa2_decode_step_workspace_size(const csa2_dims* dims, const csa2_queries* q, size_t* bytes);
 
 /* csa2_decode_step with every per-position plane paged (see csa2_pages):
- * the stages' paged calls (csa2_index_full_paged, csa2_index_reindex_paged,
- * csa2_attend_paged) in the same order and with the same workspace. */
+ * the stages' paged calls (csa2_index_scan_keys with pages,
+ * csa2_pool_topk_attend_paged, csa2_reindex_attend_paged, csa2_attend_paged)
+ * in the same order and with the same workspace. */
 csa2_status csa2_decode_step_paged(const csa2_dims* dims, const csa2_queries* q, const csa2_pages* pages,
                                    int32_t mode, const uint8_t* idx_q, const uint8_t* idx_q_scales,
                                    const float* idx_w, const uint8_t* idx_k, const uint8_t* idx_k_scales,

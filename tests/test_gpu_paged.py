@@ -21,6 +21,9 @@ CASES = {
     "edge_short_p16": (small(203, wl.Dims(n_heads=16, idx_heads=16, idx_dim=128, pool_blocks=4, topk=16),
                              [0, 1, 100, 128, 129, 136, 137, 160]), 16),
     "g4_p128": (small(204, BIG, [6001, 12345], g=4), 128),
+    # a long query (the group-key selection) beside a short one
+    "long_p64": (small(206, wl.Dims(n_heads=16, idx_heads=16, idx_dim=128, pool_blocks=2048, topk=512),
+                       [300000, 5000]), 64),
     "kvg32_p32": (small(205, wl.Dims(n_heads=32, idx_heads=8, idx_dim=64, pool_blocks=64, topk=128, kv_group=32),
                         [7777, 3000]), 32),
 }
@@ -229,6 +232,46 @@ def test_paged_decode_step_matches_contiguous(case):
         assert torch.equal(b["topk_pos"][qi, :k], a["topk_pos"][qi, :k]), f"{name} q{qi}: step Top-K differs"
     assert torch.equal(b["out"].view(torch.int32), a["out"].view(torch.int32)), f"{name}: step output differs"
     assert torch.equal(b["lse"].view(torch.int32), a["lse"].view(torch.int32)), f"{name}: step LSE differs"
+
+
+def test_paged_reindex_step_matches_contiguous(case):
+    """csa2_decode_step_paged in Reindex mode (the Reindex keys scored
+    through the page table, the Top-K selected inside the attention kernel)
+    writes the contiguous Reindex step's Top-K, outputs and LSE bit for bit,
+    on the pool of a contiguous Full step."""
+    name, g, pg = case
+    csa2, w, d = g.csa2, g.w, g.w.dims
+    n_q = w.n_q
+    q, wt = g.iq(0)
+    ql, qr = g.mq(0)
+    _, codes, scales, kv_rope, swa_kv = g.planes[0]
+
+    def bufs():
+        return dict(topk_pos=torch.empty(n_q, d.topk, dtype=torch.int32, device="cuda"),
+                    topk_count=torch.empty(n_q, dtype=torch.int32, device="cuda"),
+                    out=torch.empty(n_q, d.n_heads, 512, dtype=torch.float32, device="cuda"),
+                    lse=torch.empty(n_q, d.n_heads, dtype=torch.float32, device="cuda"))
+
+    pool = torch.empty(n_q, d.pool_blocks, dtype=torch.int32, device="cuda")
+    cnt = torch.empty(n_q, dtype=torch.int32, device="cuda")
+    f = bufs()
+    csa2.decode_step(g.dims, g.batch, csa2.LAYER_FULL, q, wt, g.planes[0][0], pool, cnt, f["topk_pos"],
+                     f["topk_count"], ql, qr, 1.0, codes, scales, kv_rope, swa_kv, g.swa_base, f["out"], f["lse"])
+    q1, w1 = g.iq(1)
+    ql1, qr1 = g.mq(1)
+    a, b = bufs(), bufs()
+    csa2.decode_step(g.dims, g.batch, csa2.LAYER_REINDEX, q1, w1, g.planes[0][0], pool, cnt, a["topk_pos"],
+                     a["topk_count"], ql1, qr1, 1.0, codes, scales, kv_rope, swa_kv, g.swa_base, a["out"], a["lse"])
+    csa2.decode_step(g.dims, pg.batch, csa2.LAYER_REINDEX, q1, w1, pg.idx_k, pool, cnt, b["topk_pos"],
+                     b["topk_count"], ql1, qr1, 1.0, pg.codes, pg.scales, pg.kv_rope, swa_kv, g.swa_base,
+                     b["out"], b["lse"], pages=pg.pages)
+    torch.cuda.synchronize()
+    assert torch.equal(b["topk_count"], a["topk_count"]), f"{name}: Reindex Top-K counts differ"
+    for qi in range(n_q):
+        k = int(a["topk_count"][qi])
+        assert torch.equal(b["topk_pos"][qi, :k], a["topk_pos"][qi, :k]), f"{name} q{qi}: Reindex Top-K differs"
+    assert torch.equal(b["out"].view(torch.int32), a["out"].view(torch.int32)), f"{name}: Reindex output differs"
+    assert torch.equal(b["lse"].view(torch.int32), a["lse"].view(torch.int32)), f"{name}: Reindex LSE differs"
 
 
 def test_paged_step_graph_replays(case):
