@@ -359,12 +359,25 @@ def _timed(launch, n: int, spin_s_per_cycle: float, issue_s: float) -> float:
     return t0.elapsed_time(t1)
 
 
+WARM_S = 0.3   # seconds of steps before each workload's timing
+
+
 def measure(w: wl.Workload, steps: int, warmup: int, replicas: int):
     per_step = scan_bytes(w)
     if replicas <= 0:
         replicas = max(1, min(8, math.ceil(1.0e9 / max(per_step, 1))))
     st = DeviceState(w, replicas=replicas)
     step = Step(st)
+    # steady state: the GPU idles while the host builds inputs or runs the
+    # oracle between workloads, and a few warm-up steps do not bring it back
+    # to speed, so steps run for WARM_S of wall time first, then the warm-up
+    t_warm = time.perf_counter() + WARM_S
+    i = 0
+    while time.perf_counter() < t_warm:
+        step.run(i % replicas)
+        i += 1
+        if i % 64 == 0:
+            torch.cuda.synchronize()
     for i in range(warmup):
         step.run(i % replicas)
     torch.cuda.synchronize()
