@@ -460,9 +460,27 @@ def measure(w: wl.Workload, steps: int, warmup: int, replicas: int):
             graphs[i % replicas].replay()
         torch.cuda.synchronize()
         graph_ms = _timed(lambda i: graphs[i % replicas].replay(), steps, rate, issue_s)
-        res["layer_step_us"] = {"stage_calls": round(ms * 1e3, 2), "decode_step": round(call_ms / steps * 1e3, 2),
-                                "graph_replay": round(graph_ms / steps * 1e3, 2)}
         del graphs
+        # ten consecutive layer calls (rotating replicas) in one graph, as a
+        # model step would capture its layers: the graph launch's fixed cost
+        # spread over ten layers
+        G = 10
+        graphs = []
+        for r in range(replicas):
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gr):
+                for j in range(G):
+                    layer((r + j) % replicas)
+            graphs.append(gr)
+        for i in range(max(1, warmup // G)):
+            graphs[i % replicas].replay()
+        torch.cuda.synchronize()
+        n10 = max(1, steps // G)
+        graph10_ms = _timed(lambda i: graphs[i % replicas].replay(), n10, rate, issue_s)
+        del graphs
+        res["layer_step_us"] = {"stage_calls": round(ms * 1e3, 2), "decode_step": round(call_ms / steps * 1e3, 2),
+                                "graph_replay": round(graph_ms / steps * 1e3, 2),
+                                "graph_replay_10_layers": round(graph10_ms / (n10 * G) * 1e3, 2)}
     # spread of the step time: 20 short blocks of 5 steps, one event pair each
     import numpy as np
     blocks = []
