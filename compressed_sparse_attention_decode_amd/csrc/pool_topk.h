@@ -253,7 +253,7 @@ __device__ __forceinline__ uint32_t topk_from_keys(const uint32_t* ks, const int
 #pragma unroll
   for (int k = 0; k < kPer; ++k) asm volatile("" : "+v"(key[k]));   // the keys are complete here
   after_keys();
-  const TopkCut cut = radix_topk<kPer>(key, K, 0, L);
+  const TopkCut cut = radix_topk<kPer, true>(key, K, 0, L);
   uint32_t flags = 0;
 #pragma unroll
   for (int k = 0; k < kPer; ++k) flags |= (uint32_t)(key[k] >= cut.tt) << k;

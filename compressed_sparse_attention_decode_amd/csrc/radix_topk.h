@@ -107,8 +107,14 @@ struct __align__(16) RadixLds {
 
 // All 512 threads call this with their PER keys (PER <= 32; thread t holds
 // slots [PER t, PER (t + 1)); slots past the valid range already 0).
-// Contains barriers; K >= 1, K2 >= 0 (0: no second rank).
-template <int PER>
+// Contains barriers; K >= 1, K2 >= 0 (0: no second rank).  TOP (with K2 =
+// 0): when K <= kTkThreads, only the keys at or above t0, the smallest of
+// the threads' own largest keys, enter the histogram: t0 is at most the
+// K-th largest key (the threads' largest keys are kTkThreads >= K distinct
+// keys at or above it), and every later pass works inside the crossing bin,
+// so the result is the same with far fewer LDS atomics.  (A thread without
+// keys makes t0 = 0: every key enters.)
+template <int PER, bool TOP = false>
 __device__ __forceinline__ TopkCut radix_topk(uint32_t (&key)[PER], int K, int K2, RadixLds& L) {
   static_assert(PER >= 1 && PER <= 32, "a 32-bit candidate mask per thread");
   uint32_t* s_hist = L.hist;
@@ -131,19 +137,38 @@ __device__ __forceinline__ TopkCut radix_topk(uint32_t (&key)[PER], int K, int K
     lo = min(lo, key[k] - 1u);
     hi = max(hi, key[k]);
   }
+  if constexpr (TOP) {
+    // the waves' smallest thread maxima (read after the reduction's barriers)
+    const uint32_t tm = wave_reduce_u32(hi, [](uint32_t x, uint32_t y) { return min(x, y); });
+    if (lane == 0) s_misc2[tid >> 6] = tm;
+    static_assert(kTkWaves <= 8, "one word per wave");
+  }
   block_minmax_u32<kTkThreads>(&lo, &hi, s_red);   // its barriers also order the clears
   const uint32_t kmin = lo + 1u, kmax = hi;
+  uint32_t base = kmin;                      // the histogram's lowest key
+  if constexpr (TOP) {
+    uint32_t t0 = 0xFFFFFFFFu;
+#pragma unroll
+    for (int w = 0; w < kTkWaves; ++w) t0 = min(t0, s_misc2[w]);
+    if (K <= kTkThreads) base = max(kmin, t0);
+  }
 
   uint32_t keff = 0, lb2 = 0, n2 = 0;
   uint32_t T = 0xFFFFFFFFu;                  // threshold key (no finite score has it)
   int ST = 0x7FFFFFFF;                       // keys == T at slots <= ST are selected
   if (kmax != 0) {
-    const uint32_t d = kmax - kmin;
+    const uint32_t d = kmax - base;
     int shift = d ? max(0, 21 - (int)__clz(d)) : 0;    // (d >> shift) < 2^11
+    if constexpr (TOP) {
 #pragma unroll
-    for (int k = 0; k < PER; ++k) {
-      const uint32_t b = (key[k] - kmin) >> shift;
-      atomicAdd(&s_hist[key[k] != 0 ? b : kTkBins + (lane & (kTkEmpty - 1))], 1u);
+      for (int k = 0; k < PER; ++k)
+        if (key[k] >= base) atomicAdd(&s_hist[(key[k] - base) >> shift], 1u);
+    } else {
+#pragma unroll
+      for (int k = 0; k < PER; ++k) {
+        const uint32_t b = (key[k] - base) >> shift;
+        atomicAdd(&s_hist[key[k] != 0 ? b : kTkBins + (lane & (kTkEmpty - 1))], 1u);
+      }
     }
     __syncthreads();
     if (tid < 64) crossing_2048(s_hist, (uint32_t)K, s_misc);
@@ -151,12 +176,12 @@ __device__ __forceinline__ TopkCut radix_topk(uint32_t (&key)[PER], int K, int K
     __syncthreads();
     keff = s_misc[3];
     if (K2 > 0 && s_misc2[3] > 0) {
-      lb2 = kmin + (s_misc2[0] << shift);
+      lb2 = base + (s_misc2[0] << shift);
       n2 = s_misc2[1] + s_misc2[2];
     }
     uint32_t need = keff - s_misc[1];         // keys still to take from the crossing bin
     uint32_t cand = s_misc[2];
-    uint32_t blo = kmin + (s_misc[0] << shift);    // the crossing bin is [blo, blo + 2^shift)
+    uint32_t blo = base + (s_misc[0] << shift);    // the crossing bin is [blo, blo + 2^shift)
 
     // Rare: a crossing bin with more than kRankCap keys (clustered or equal
     // scores).  Further digits of (key - blo) narrow it.
