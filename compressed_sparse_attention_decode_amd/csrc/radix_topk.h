@@ -366,10 +366,10 @@ __device__ __forceinline__ TopkBound radix_bound_top(const uint32_t (&key)[PER],
 }
 
 // The same with LDS of its own (one per PER).
-template <int PER = kPer>
+template <int PER = kPer, bool TOP = false>
 __device__ __forceinline__ TopkCut radix_topk(uint32_t (&key)[PER], int K, int K2 = 0) {
   __shared__ RadixLds s_radix;
-  return radix_topk<PER>(key, K, K2, s_radix);
+  return radix_topk<PER, TOP>(key, K, K2, s_radix);
 }
 
 }  // namespace csa2

@@ -250,7 +250,7 @@ __device__ __forceinline__ void topk_select(const ReindexArgs& a, int q, int32_t
 #pragma unroll
     for (int k = 0; k < kPer; ++k) key[k] = k < nh ? key[k] : 0u;
   }
-  const TopkCut cut = radix_topk(key, K);
+  const TopkCut cut = radix_topk<kPer, true>(key, K);
 
   uint32_t flags = 0;
 #pragma unroll
