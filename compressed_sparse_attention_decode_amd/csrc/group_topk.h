@@ -247,16 +247,16 @@ __device__ __forceinline__ uint32_t topk_from_groups(const uint32_t* gk, int gca
         }
       }
       __syncthreads();
-      return topk_positions<BPT>(L.blk, ncand, pk, K, o.topk, nullptr, o.topk_count, L.scan, L.radix, o.rows, o.r0,
-                                 o.r1);
+      return topk_positions<BPT>(L.blk, ncand, pk, K, o.topk, nullptr, o.topk_count, L.scan, L.radix, lb, o.rows,
+                                 o.r0, o.r1);
     }
   }
   // crowded: the exact K best blocks (K <= kCap), then their positions
   const StreamCut cut = stream_cut(bs, nb, K, L.radix);
   if (cut.keff) stream_emit(bs, nb, cut, L.scan, [&](uint32_t r, int i) { L.blk[r] = i; });
   __syncthreads();
-  return topk_positions<BPT>(L.blk, cut.keff, pk, K, o.topk, nullptr, o.topk_count, L.scan, L.radix, o.rows, o.r0,
-                             o.r1);
+  return topk_positions<BPT>(L.blk, cut.keff, pk, K, o.topk, nullptr, o.topk_count, L.scan, L.radix, lb, o.rows,
+                             o.r0, o.r1);
 }
 
 // ------------------------------------------------------------ Top-K, short queries
@@ -320,8 +320,8 @@ __device__ __forceinline__ uint32_t topk_from_blocks(const float* bs, int ld, in
     nsel = cut.keff;
   }
   __syncthreads();
-  return topk_positions<BPT>(L.blk, nsel, pk, K, o.topk, nullptr, o.topk_count, L.scan, L.radix, o.rows, o.r0,
-                             o.r1);
+  return topk_positions<BPT>(L.blk, nsel, pk, K, o.topk, nullptr, o.topk_count, L.scan, L.radix, bd.lb, o.rows,
+                             o.r0, o.r1);
 }
 
 // ------------------------------------------------------------ pool

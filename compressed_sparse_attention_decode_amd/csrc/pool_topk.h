@@ -96,8 +96,8 @@ __device__ __forceinline__ uint32_t pool_topk_select(const float* bs, int ld, in
           L.blk[cb++] = s0 + k;                    // ascending block ids
         }
         __syncthreads();
-        return topk_positions<BPT>(L.blk, ncand, pk, K, o.topk, nullptr, o.topk_count, L.scan, L.radix, o.rows,
-                                   o.r0, o.r1);
+        return topk_positions<BPT>(L.blk, ncand, pk, K, o.topk, nullptr, o.topk_count, L.scan, L.radix, bd.lb,
+                                   o.rows, o.r0, o.r1);
       }
       // (a crowded bin: the exact path below)
     }
@@ -159,8 +159,8 @@ __device__ __forceinline__ uint32_t pool_topk_select(const float* bs, int ld, in
       nsel = min(nsel, kCap);
     }
     __syncthreads();
-    return topk_positions<BPT>(L.blk, nsel, pk, K, o.topk, nullptr, o.topk_count, L.scan, L.radix, o.rows, o.r0,
-                               o.r1);
+    return topk_positions<BPT>(L.blk, nsel, pk, K, o.topk, nullptr, o.topk_count, L.scan, L.radix, cut.lb2, o.rows,
+                               o.r0, o.r1);
   }
 }
 
@@ -201,7 +201,7 @@ __device__ __forceinline__ uint32_t topk_from_pool(const int32_t* pool, int pcnt
   for (int k = 0; k < PB; ++k)
     if (flags >> k & 1u) L.blk[before++] = blk[k];   // ascending: the pool is ascending
   __syncthreads();
-  return topk_positions<BPT>(L.blk, nsel, pk, K, o.topk, out_s, o.topk_count, L.scan, L.radix, o.rows, o.r0,
+  return topk_positions<BPT>(L.blk, nsel, pk, K, o.topk, out_s, o.topk_count, L.scan, L.radix, 0u, o.rows, o.r0,
                              o.r1);
 }
 

@@ -113,9 +113,12 @@ struct __align__(16) RadixLds {
 // K-th largest key (the threads' largest keys are kTkThreads >= K distinct
 // keys at or above it), and every later pass works inside the crossing bin,
 // so the result is the same with far fewer LDS atomics.  (A thread without
-// keys makes t0 = 0: every key enters.)
+// keys makes t0 = 0: every key enters.)  floor (TOP only, uniform): a lower
+// bound of the K-th largest key that the caller knows; the keys below it
+// stay out of the histogram as well.
 template <int PER, bool TOP = false>
-__device__ __forceinline__ TopkCut radix_topk(uint32_t (&key)[PER], int K, int K2, RadixLds& L) {
+__device__ __forceinline__ TopkCut radix_topk(uint32_t (&key)[PER], int K, int K2, RadixLds& L,
+                                              uint32_t floor = 0u) {
   static_assert(PER >= 1 && PER <= 32, "a 32-bit candidate mask per thread");
   uint32_t* s_hist = L.hist;
   uint64_t* s_cand = L.cand;
@@ -151,6 +154,7 @@ __device__ __forceinline__ TopkCut radix_topk(uint32_t (&key)[PER], int K, int K
 #pragma unroll
     for (int w = 0; w < kTkWaves; ++w) t0 = min(t0, s_misc2[w]);
     if (K <= kTkThreads) base = max(kmin, t0);
+    base = max(base, floor);
   }
 
   uint32_t keff = 0, lb2 = 0, n2 = 0;

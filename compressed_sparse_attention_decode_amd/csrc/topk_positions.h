@@ -25,7 +25,8 @@ namespace csa2 {
 template <int BPT>
 __device__ __forceinline__ uint32_t topk_positions(const int32_t* s_blk, uint32_t nsel, const uint32_t* pk, int K,
                                                    int32_t* out, float* out_s, int32_t* count, uint32_t* s_scan,
-                                                   RadixLds& L, int32_t* rows = nullptr, int r0 = 0, int r1 = 0) {
+                                                   RadixLds& L, uint32_t floor, int32_t* rows = nullptr, int r0 = 0,
+                                                   int r1 = 0) {
   constexpr int PP = BPT * kBlock;                  // position slots per thread
   const int tid = threadIdx.x;
   uint32_t key[PP];
@@ -47,7 +48,11 @@ __device__ __forceinline__ uint32_t topk_positions(const int32_t* s_blk, uint32_
     key[8 * b + 4] = live ? x1[b][0] : 0u; key[8 * b + 5] = live ? x1[b][1] : 0u;
     key[8 * b + 6] = live ? x1[b][2] : 0u; key[8 * b + 7] = live ? x1[b][3] : 0u;
   }
-  const TopkCut cut = radix_topk<PP>(key, K, 0, L);
+  // floor bounds the K-th best candidate block's key from below; that
+  // block and the K - 1 above it each bring their best position, K distinct
+  // keys at or above it, so the K-th best position key is too (with fewer
+  // than K blocks no such bound holds)
+  const TopkCut cut = radix_topk<PP, true>(key, K, 0, L, nsel >= (uint32_t)K ? floor : 0u);
   uint32_t pflags = 0;
 #pragma unroll
   for (int k = 0; k < PP; ++k) pflags |= (uint32_t)(key[k] >= cut.tt) << k;
