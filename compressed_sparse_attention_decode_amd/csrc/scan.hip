@@ -92,7 +92,13 @@ __global__ __launch_bounds__(64 * NW) void k_scan(ScanArgs a) {
 
   // block -> (query, tile); the g tokens of one sequence and the same tile
   // land on the same XCD (block ids equal mod 8) so their key reads share L2.
-  // Eight or more sequences: XCD x takes sequences x, x + 8, ... whole.
+  // Eight sequences or fewer: XCD x takes sequences x, x + 8, ... whole.
+  // More: the sequences rotate across tiles (tile t of sequence s is unit
+  // t n_groups + (s - t) mod n_groups), so each XCD takes an equal share of
+  // every sequence's tiles.  Whole sequences left the XCDs up to 1.46x apart
+  // in work on a batch of 32 contexts drawn from [32K, 256K] (the kernel
+  // waits for the busiest XCD); for 8 equal sequences the rotation measured
+  // 0.6 us slower.
   // One, two or four sequences of single tokens: each sequence's XCDs take
   // contiguous runs of its tiles, a run of long tiles (dispatched first)
   // and a run of short ones, instead of every eighth tile (measured: 0.6 us
@@ -102,7 +108,8 @@ __global__ __launch_bounds__(64 * NW) void k_scan(ScanArgs a) {
   const int unit = (bid / (8 * g)) * 8 + (bid & 7);
   const int j = (bid >> 3) % g;
   const int n_groups = a.n_q / g;
-  int group = unit % n_groups, tile = unit / n_groups;
+  int tile = unit / n_groups, group = unit % n_groups;
+  if (n_groups > 8) group = (group + tile) % n_groups;
   if (g == 1 && n_groups < 8 && 8 % n_groups == 0 && a.tiles % (16 / n_groups) == 0) {
     const int X = 8 / n_groups;                   // XCDs per sequence
     const int per = a.tiles / (2 * X);            // long (and short) tiles per XCD run
