@@ -270,17 +270,15 @@ __device__ __forceinline__ uint32_t topk_from_groups(const uint32_t* gk, int gca
 // order is not block order: the candidates are marked in an LDS bitmap
 // (s_bits, 512 words) and compacted in ascending order from it.  A crowded
 // bin takes the exact streaming selection.  Returns the Top-K count.
-template <int BPT, typename AfterKeys>
-__device__ __forceinline__ uint32_t topk_from_blocks(const float* bs, int ld, int nb, const uint32_t* pk, int K,
-                                                     const PoolTopkOut& o, PoolTopkLds<BPT>& L, uint32_t* s_bits,
-                                                     AfterKeys&& after_keys) {
-  constexpr uint32_t kCap = kTkThreads * BPT;
+// Thread t's keys of blocks 4 (512 v + t) + e (v < 8, e < 4) of a row of
+// ld >= 4 block scores, 0 at or past nb: whole lines per load instruction.
+__device__ __forceinline__ void load_block_keys_c(const float* bs, int64_t ld, int nb, uint32_t (&key)[kPer]) {
   constexpr int NV = kPer / 4;                       // 16-byte loads per thread
   const int tid = threadIdx.x;
   v4f x[NV];
 #pragma unroll
-  for (int v = 0; v < NV; ++v) x[v] = *reinterpret_cast<const v4f*>(bs + min(4 * (kTkThreads * v + tid), ld - 4));
-  uint32_t key[kPer];
+  for (int v = 0; v < NV; ++v)
+    x[v] = *reinterpret_cast<const v4f*>(bs + min((int64_t)(4 * (kTkThreads * v + tid)), ld - 4));
 #pragma unroll
   for (int v = 0; v < NV; ++v) {
 #pragma unroll
@@ -288,6 +286,17 @@ __device__ __forceinline__ uint32_t topk_from_blocks(const float* bs, int ld, in
   }
 #pragma unroll
   for (int k = 0; k < kPer; ++k) asm volatile("" : "+v"(key[k]));   // the keys are complete here
+}
+
+template <int BPT, typename AfterKeys>
+__device__ __forceinline__ uint32_t topk_from_blocks(const float* bs, int ld, int nb, const uint32_t* pk, int K,
+                                                     const PoolTopkOut& o, PoolTopkLds<BPT>& L, uint32_t* s_bits,
+                                                     AfterKeys&& after_keys) {
+  constexpr uint32_t kCap = kTkThreads * BPT;
+  constexpr int NV = kPer / 4;                       // 16-byte loads per thread
+  const int tid = threadIdx.x;
+  uint32_t key[kPer];
+  load_block_keys_c(bs, ld, nb, key);
   after_keys();
   s_bits[tid] = 0u;                                  // (ordered by the bound's barriers)
   const TopkBound bd = K <= kTkThreads ? radix_bound_top<kPer>(key, K, L.radix) : radix_bound<kPer>(key, K, L.radix);
@@ -340,8 +349,12 @@ struct PoolGroupLds {
 // block asc), written ascending to pool[0 .. P) (-1 past the count) with the
 // count.  The candidate groups at or above the bound of the P-th group are
 // read kPoolGpt per thread at a time; their blocks at or above the bound are
-// listed in ascending order and ranked by radix_topk.  Returns the count.
-// Contains barriers.
+// listed in ascending order and ranked by radix_topk.  With fewer groups
+// than P (nb < 16 P) the bound comes from the first kMaxCand blocks' keys
+// instead: the P-th best key of any kMaxCand >= P of the blocks is at most
+// the P-th best of all, and at nb <= 2 kMaxCand about 2P blocks reach it
+// (every block was a candidate before, and the exact streaming selection
+// over all of them ran).  Returns the count.  Contains barriers.
 __device__ __forceinline__ uint32_t pool_from_groups(const uint32_t* gk, int gcap, const float* bs, int64_t ld, int nb,
                                                      int P, int32_t* pool, int32_t* pool_count, PoolGroupLds& L) {
   const int tid = threadIdx.x;
@@ -349,8 +362,14 @@ __device__ __forceinline__ uint32_t pool_from_groups(const uint32_t* gk, int gca
   uint32_t key[kGroupPer];
   load_group_keys_c(gk, ng, gcap, key);
   if (tid < kMaxGroups / 32) L.bits[tid] = 0u;          // (ordered by the bound's barriers)
-  const TopkBound bd = radix_bound<kGroupPer>(key, P, L.radix);
-  const uint32_t lb = ng >= P ? bd.lb : 1u;
+  uint32_t lb;
+  if (ng >= P) {
+    lb = radix_bound<kGroupPer>(key, P, L.radix).lb;
+  } else {
+    uint32_t bk[kPer];
+    load_block_keys_c(bs, ld, kMaxCand, bk);             // nb > kMaxCand: every slot valid
+    lb = radix_bound<kPer>(bk, P, L.radix).lb;
+  }
   uint32_t ngc;
   block_exclusive_scan<kTkThreads>(mark_groups(key, lb, L.bits), L.scan, &ngc);   // (completes the marks)
   uint32_t ncand = 0;
