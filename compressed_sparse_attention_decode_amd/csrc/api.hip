@@ -125,9 +125,16 @@ int pool_chunks(const csa2_dims* d, const csa2_queries* q) {
   return g > 0 ? (int)g : 1;
 }
 
-// Positions per Full-scan workgroup (CSA2_SCAN_TILE overrides for tuning).
-int scan_tile() {
+// Positions per Full-scan workgroup: kScanTile, halved (down to 256) while
+// the launch would hold fewer than kScanSmallGrid workgroups, so that a few
+// short queries spread over more CUs instead of each wave walking a long run
+// of positions alone.  A function of the sizes only, so the scan, the pool
+// that reads its key ranges and the workspace sizes agree
+// (CSA2_SCAN_TILE overrides for tuning).
+int scan_tile(const csa2_dims* d, const csa2_queries* q) {
   int tile = kScanTile;
+  const int64_t pos = max_blocks(d, q) * 8;
+  while (tile > kScanTileMin && (int64_t)q->n_q * ((pos + tile - 1) / tile) < kScanSmallGrid) tile /= 2;
   if (const char* env = getenv("CSA2_SCAN_TILE")) tile = atoi(env);
   if (tile < 64 || tile % 64 || tile > 4096) tile = kScanTile;
   return tile;
@@ -155,7 +162,7 @@ int scan_tile_extra(const csa2_dims* d, const csa2_queries* q, int tile, int til
 
 // (min, max) key pairs per query: one per pool chunk or one per scan tile
 int pool_mm_cap(const csa2_dims* d, const csa2_queries* q) {
-  const int t = scan_tiles(d, q, scan_tile()), g = pool_chunks(d, q);
+  const int t = scan_tiles(d, q, scan_tile(d, q)), g = pool_chunks(d, q);
   return t > g ? t : g;
 }
 
@@ -163,7 +170,7 @@ int pool_mm_cap(const csa2_dims* d, const csa2_queries* q) {
 // blocks) into the pool workspace when its tiles start at group boundaries:
 // always, unless CSA2_SCAN_TILE / CSA2_SCAN_SPLIT move them off.
 static bool scan_groups_ok(const csa2_dims* d, const csa2_queries* q) {
-  const int tile = scan_tile(), tiles = scan_tiles(d, q, tile);
+  const int tile = scan_tile(d, q), tiles = scan_tiles(d, q, tile);
   const int extra = scan_tile_extra(d, q, tile, tiles);
   return tile % (8 * kGroupBlocks) == 0 && extra % (8 * kGroupBlocks) == 0;
 }
@@ -395,7 +402,7 @@ static csa2_status run_scan(const csa2_dims* d, const csa2_queries* q, const uin
   if (const char* env = getenv("CSA2_SCAN_WAVES")) nw = atoi(env);
   if (pf != 4 && pf != 6 && pf != 8) pf = kScanPrefetch;
   if (nw != 4 && nw != 8) nw = kScanWaves;
-  sa.tile_pos = scan_tile();
+  sa.tile_pos = scan_tile(d, q);
   sa.prefetch = pf;
   sa.waves = nw;
   sa.tiles = scan_tiles(d, q, sa.tile_pos);
@@ -439,10 +446,10 @@ static csa2_status run_pool(const csa2_dims* d, const csa2_queries* q, const flo
   pa.ws_stride = pool_ws_words(pa.chunks, pa.mm_cap);
   pa.have_minmax = after_scan;
   pa.mm_half = 0;
-  pa.mm_span = after_scan ? scan_tile() / 8 : kPoolChunk;
+  pa.mm_span = after_scan ? scan_tile(d, q) / 8 : kPoolChunk;
   if (after_scan) {
     // the scan's tiles: the first half longer when it split them unevenly
-    const int tile = scan_tile(), tiles = scan_tiles(d, q, tile);
+    const int tile = scan_tile(d, q), tiles = scan_tiles(d, q, tile);
     const int extra = scan_tile_extra(d, q, tile, tiles);
     if (extra) {
       pa.mm_half = tiles / 2;
