@@ -125,7 +125,7 @@ int pool_chunks(const csa2_dims* d, const csa2_queries* q) {
   return g > 0 ? (int)g : 1;
 }
 
-// Positions per Full-scan workgroup: kScanTile, halved (down to 256) while
+// Positions per Full-scan workgroup: kScanTile, halved (down to 128) while
 // the launch would hold fewer than kScanSmallGrid workgroups, so that a few
 // short queries spread over more CUs instead of each wave walking a long run
 // of positions alone.  A function of the sizes only, so the scan, the pool

@@ -55,7 +55,7 @@ hipError_t launch_scan(const ScanArgs& a, hipStream_t s);
 
 constexpr int kHistBins = 4096;        // pool histogram bins, cleared by the scan's tile 0
 constexpr int kScanTile = 2048;        // default positions per scan workgroup
-constexpr int kScanTileMin = 256;      // the smallest tile a small launch takes
+constexpr int kScanTileMin = 128;      // the smallest tile a small launch takes
 constexpr int kScanSmallGrid = 64;     // launches of fewer workgroups take smaller tiles
 constexpr int kScanPrefetch = 4;       // default LDS ring slots per wave
 constexpr int kScanWaves = 4;          // default waves per scan workgroup
