@@ -295,6 +295,41 @@ def test_full_topk_from_scan_keys_matches_reindex(case):
             f"{name} q{qi}: block scores differ with position keys kept"
 
 
+@pytest.mark.parametrize("tile", ["2048", "128"])
+def test_scan_tile_independent(case, tile, monkeypatch):
+    """The scan's tile (2048 positions, halved down to 128 for launches of
+    few workgroups; forced here with CSA2_SCAN_TILE) changes neither the block
+    scores, the position keys, nor the pool selected after the scan from its
+    key ranges: each position's score is the same contraction whatever tile
+    holds it."""
+    name, g, lay = case
+    csa2, w = g.csa2, g.w
+    q, wt = g.iq(0)
+    idx_k = g.planes[0][0]
+
+    def run():
+        bs = torch.zeros(w.n_q, csa2.block_scores_ld(g.dims, g.batch), dtype=torch.float32, device="cuda")
+        pk = torch.zeros(w.n_q, csa2.pos_keys_ld(g.dims, g.batch), dtype=torch.int32, device="cuda")
+        pws = torch.zeros(csa2.workspace_pool(g.dims, g.batch) + 256, dtype=torch.uint8, device="cuda")
+        csa2.index_scan(g.dims, g.batch, q, wt, idx_k, bs, pool_ws=pws, pos_keys=pk)
+        pool, cnt = csa2.index_pool(g.dims, g.batch, bs, ws=pws, from_scan=True)
+        torch.cuda.synchronize()
+        return bs.cpu(), pk.cpu(), pool.cpu(), cnt.cpu()
+
+    bs, pk, pool, cnt = run()
+    monkeypatch.setenv("CSA2_SCAN_TILE", tile)
+    bs2, pk2, pool2, cnt2 = run()
+    assert torch.equal(cnt, cnt2), f"{name}: pool counts differ with tile {tile}"
+    for qi in range(w.n_q):
+        c = max(0, lay.q_visible[qi] - w.dims.swa)
+        nb = -(-c // 8)
+        assert torch.equal(bs[qi, :nb].view(torch.int32), bs2[qi, :nb].view(torch.int32)), \
+            f"{name} q{qi}: block scores differ with tile {tile}"
+        assert torch.equal(pk[qi, :c], pk2[qi, :c]), f"{name} q{qi}: position keys differ with tile {tile}"
+        k = int(cnt[qi])
+        assert torch.equal(pool[qi, :k], pool2[qi, :k]), f"{name} q{qi}: pool differs with tile {tile}"
+
+
 @pytest.mark.parametrize("small", ["1", "0"])
 def test_pool_topk_matches_separate_calls(case, small, monkeypatch):
     """csa2_index_pool_topk (the pool and the Full layer's Top-K in one call:
